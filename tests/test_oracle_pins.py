@@ -1,0 +1,540 @@
+"""Pins of the CPU oracle against what the pages and mathematics fix.
+
+Each test is chosen so that a plausible slip in the oracle (a dropped term,
+a wrong sign or index, a transposed operand, a missing normalisation) fails
+at least one of them.  None of these tests retypes the oracle's own formula:
+they check identities, closed forms, brute force on tiny sizes, library
+routines in special cases, and the constants the pages print.
+"""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from conftest import golden
+
+D = 128
+
+
+@pytest.fixture(scope="module")
+def tiny_cal():
+    w = synth.WORKLOADS["tiny"]
+    q, k, v = synth.calib_layer(w)
+    return w, q, k, v, O.calibrate_layer(q, k, v)
+
+
+def _rand_orth(rng, d):
+    a = rng.standard_normal((d, d))
+    qm, r = np.linalg.qr(a)
+    return qm * np.sign(np.diag(r))
+
+
+# --- P1: R^T R = I ---------------------------------------------------------
+
+def test_p1_rotation_orthogonal(tiny_cal):
+    w, q, k, v, cal = tiny_cal
+    lam, u = O.eig_desc(O.query_covariance(q[:, 0:1, :]))
+    r64 = O.composite_rotation(u)
+    assert np.abs(r64.T @ r64 - np.eye(D)).max() < 1e-12
+    for r in (cal.r_k[0], cal.r_v[0]):
+        r = r.astype(np.float64)
+        assert np.abs(r.T @ r - np.eye(D)).max() < 2e-6
+
+
+# --- P2: Lemma 1 and its composite form ------------------------------------
+
+@pytest.mark.parametrize("d", [8, 32, 128])
+def test_p2_lemma1_hadamard_equalises(d):
+    rng = np.random.default_rng(d)
+    lam = np.diag(rng.exponential(size=d))
+    h = O.hadamard(d)
+    assert np.allclose(h @ h.T, np.eye(d), atol=1e-14)
+    dg = np.diag(h.T @ lam @ h)
+    assert np.abs(dg - np.trace(lam) / d).max() < 1e-12
+
+
+def test_p2_composite_equalises_error_weight(tiny_cal):
+    w, q, k, v, cal = tiny_cal
+    cq = O.query_covariance(q[:, 0:1, :])
+    cs = O.score_weighted_value_covariance(q[:, 0:1, :], k[:, 0], v[:, 0])
+    for c in (cq, cs):
+        lam, u = O.eig_desc(c)
+        r = O.composite_rotation(u)
+        dg = np.diag(r.T @ c @ r)
+        assert np.abs(dg - np.trace(c) / D).max() < 1e-12 * np.trace(c)
+        # without the Hadamard factor the weights are the (unequal) eigenvalues
+        assert np.allclose(np.diag(u.T @ c @ u), lam, rtol=1e-10, atol=1e-14)
+        assert lam[0] > 10 * lam[-1]
+
+
+# --- P3: bit reversal strata ------------------------------------------------
+
+def test_p3_bitrev_strata_and_algebra():
+    for d in (8, 64, 128):
+        p = O.bitrev_perm(d)
+        assert np.array_equal(p, p.T) and np.array_equal(p @ p, np.eye(d))
+        h = O.hadamard(d)
+        assert np.abs(h @ p - p @ h).max() < 1e-15
+        src = (np.arange(d)[None, :] @ p).ravel().astype(int)   # (x P)[j] = x[src[j]]
+        assert src[1] == d // 2 and src[d // 2] == 1 and src[d - 1] == d - 1
+        g = 2
+        while g <= d:
+            for gamma in range(d // g):
+                strata = sorted(src[gamma * g:(gamma + 1) * g] // (d // g))
+                assert strata == list(range(g)), (d, g, gamma)
+            g *= 2
+
+
+def test_p3_bit_reverse_small_cases():
+    assert [O.bit_reverse(j, 3) for j in range(8)] == [0, 4, 2, 6, 1, 5, 3, 7]
+
+
+# --- P4: logit-error identity, tying rotate / dequantise / unrotate ---------
+
+def test_p4_logit_error_identity(tiny_cal):
+    w, q, k, v, cal = tiny_cal
+    rng = np.random.default_rng(4)
+    x = O.bf16_to_f64(synth.f32_to_bf16_bits(k[:512, 0]))
+    # the identity needs an exactly orthogonal R: use the fp64 composite
+    r = O.composite_rotation(O.eig_desc(O.query_covariance(q[:, 0:1, :]))[1])
+    codes, s, z, _ = O.quantize(x, r, cal.tau_k, 32)
+    deq = O.dequantize(codes, s, z, 32)
+    k_hat = O.unrotate(deq, r)
+    qm = rng.standard_normal((300, D))
+    lhs = np.linalg.norm(qm @ x.T - qm @ k_hat.T) ** 2
+    d_rot = x @ r - deq                       # error seen in the rotated basis
+    rhs = np.trace(d_rot @ (r.T @ qm.T @ qm @ r) @ d_rot.T)
+    assert abs(lhs - rhs) <= 1e-10 * rhs
+    # the same identity written with the original-basis error
+    dk = x - k_hat
+    assert abs(lhs - np.trace(dk @ qm.T @ qm @ dk.T)) <= 1e-10 * rhs
+
+
+# --- P5: eigen solution ------------------------------------------------------
+
+def test_p5_eigensolution_and_convention(tiny_cal):
+    w, q, k, v, cal = tiny_cal
+    c = O.query_covariance(q[:, 0:1, :])
+    lam, u = O.eig_desc(c)
+    assert np.linalg.norm(c @ u - u * lam) <= 1e-12 * np.linalg.norm(c)
+    assert np.abs(u.T @ u - np.eye(D)).max() < 1e-12
+    assert np.all(np.diff(lam) <= 0)
+    idx = np.argmax(np.abs(u), axis=0)
+    assert np.all(u[idx, np.arange(D)] > 0)
+    # statistical: the sample spectrum tracks the generator's geometric law
+    spec = np.geomspace(1.0, 1e-3, D)
+    assert abs(lam.sum() / spec.sum() - 1) < 0.1
+    assert np.all(np.abs(lam[:16] / spec[:16] - 1) < 0.35)
+    assert np.allclose(cal.eig_k[0], lam)
+
+
+def test_p5_eigh_agrees_with_svd():
+    rng = np.random.default_rng(5)
+    a = rng.standard_normal((64, 16))
+    c = a.T @ a
+    lam, u = O.eig_desc(c)
+    sv = np.linalg.svd(a, compute_uv=False) ** 2
+    assert np.allclose(lam, sv, rtol=1e-12)
+
+
+# --- P6: C_S two ways; causal scores -----------------------------------------
+
+def test_p6_score_weighted_covariance(tiny_cal):
+    w, q, k, v, cal = tiny_cal
+    n = 256
+    qh, kh, vh = q[:n, 0:1, :], k[:n, 0], v[:n, 0]
+    cs = O.score_weighted_value_covariance(qh, kh, vh)
+    s = O.causal_scores(qh[:, 0], kh)
+    assert np.allclose(s.sum(axis=1), 1.0, atol=1e-14)
+    assert np.all(s[np.triu_indices(n, 1)] == 0)
+    sv = s @ vh.astype(np.float64)
+    assert np.abs(cs - sv.T @ sv / n).max() <= 1e-12 * np.abs(cs).max()
+    # library route: C_S = O^T O / N with O the causal attention output
+    o = torch.nn.functional.scaled_dot_product_attention(
+        torch.tensor(qh[:, 0], dtype=torch.float64)[None, None],
+        torch.tensor(kh, dtype=torch.float64)[None, None],
+        torch.tensor(vh, dtype=torch.float64)[None, None], is_causal=True)[0, 0].numpy()
+    assert np.abs(cs - o.T @ o / n).max() <= 1e-10 * np.abs(cs).max()
+
+
+def test_p6_causal_scores_brute_force():
+    rng = np.random.default_rng(6)
+    n, d = 7, 4
+    q, k = rng.standard_normal((n, d)), rng.standard_normal((n, d))
+    s = O.causal_scores(q, k)
+    for i in range(n):
+        e = [math.exp(sum(q[i, a] * k[j, a] for a in range(d)) / math.sqrt(d)) for j in range(i + 1)]
+        for j in range(n):
+            ref = e[j] / sum(e) if j <= i else 0.0
+            assert abs(s[i, j] - ref) < 1e-14
+
+
+def test_p6_gqa_pooling_is_mean_over_heads():
+    rng = np.random.default_rng(61)
+    q = rng.standard_normal((32, 3, 8))
+    c = O.query_covariance(q)
+    ref = sum(O.query_covariance(q[:, h:h + 1]) for h in range(3)) / 3
+    assert np.allclose(c, ref, rtol=1e-13)
+
+
+# --- P7: quantiser brute force on tiny d; fp16 rounding; packing -------------
+
+def _exact_f16_round(x: float) -> float:
+    """Correct nearest-even rounding to binary16 with exact rationals."""
+    fx = Fraction(x)
+    if fx == 0:
+        return 0.0
+    sign = -1 if fx < 0 else 1
+    a = abs(fx)
+    e = math.floor(math.log2(a))
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    e = max(e, -14)
+    ulp = Fraction(2) ** (e - 10)
+    m = a / ulp
+    lo = math.floor(m)
+    rem = m - lo
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and lo % 2 == 1):
+        lo += 1
+    val = lo * ulp
+    if val > 65504:
+        return sign * math.inf
+    return sign * float(val)
+
+
+def test_p7_fp16_rounding_is_single_correct_rounding():
+    rng = np.random.default_rng(7)
+    xs = list(rng.standard_normal(2000) * 10.0 ** rng.integers(-9, 5, 2000))
+    # exact midpoints between fp16 neighbours, and values a hair off them
+    for _ in range(300):
+        h = np.float16(rng.standard_normal() * 100)
+        nxt = np.nextafter(h, np.float16(np.inf))
+        mid = (float(h) + float(nxt)) / 2
+        xs += [mid, np.nextafter(mid, np.inf), np.nextafter(mid, -np.inf)]
+    got = O.to_f16(np.array(xs))
+    for x, g in zip(xs, got):
+        assert float(g) == _exact_f16_round(float(x)), x
+
+
+@pytest.mark.parametrize("d,group", [(4, 2), (8, 4), (8, 2), (16, 8)])
+def test_p7_codes_are_nearest_level(d, group):
+    rng = np.random.default_rng(d * 10 + group)
+    r = _rand_orth(rng, d)
+    x = rng.standard_normal((400, d)) * 3
+    tau = 3.0
+    codes, s, z, xr = O.quantize(x, r, tau, group)
+    ng = d // group
+    for n in range(x.shape[0]):
+        rot = [sum(x[n, i] * r[i, j] for i in range(d)) for j in range(d)]
+        rot = [min(max(val, -tau), tau) for val in rot]
+        for gm in range(ng):
+            vals = rot[gm * group:(gm + 1) * group]
+            mn, mx = min(vals), max(vals)
+            assert float(s[n, gm]) == _exact_f16_round((mx - mn) / 3.0)
+            assert float(z[n, gm]) == _exact_f16_round(mn)
+            sv, zv = float(s[n, gm]), float(z[n, gm])
+            if sv == 0:
+                assert np.all(codes[n, gm * group:(gm + 1) * group] == 0)
+                continue
+            for jj, val in enumerate(vals):
+                dist = [abs(val - (zv + c * sv)) for c in range(4)]
+                best = int(np.argmin(dist))
+                t = (val - zv) / sv
+                if abs(t - math.floor(t) - 0.5) < 1e-9:
+                    continue            # tie band
+                assert codes[n, gm * group + jj] == best
+
+
+def test_p7_textbook_grid_assignment_with_identity_rotation():
+    """R = I, no clip: codes equal the interval index of x among the midpoints
+    of the 4-level grid (np.searchsorted), i.e. plain per-token min/max INT2."""
+    rng = np.random.default_rng(71)
+    d, group = 128, 32
+    x = rng.standard_normal((300, d))
+    codes, s, z, _ = O.quantize(x, np.eye(d), np.inf, group)
+    for n in range(x.shape[0]):
+        for gm in range(d // group):
+            sv, zv = float(s[n, gm]), float(z[n, gm])
+            mids = zv + (np.arange(3) + 0.5) * sv
+            ref = np.searchsorted(mids, x[n, gm * group:(gm + 1) * group], side="left")
+            tt = (x[n, gm * group:(gm + 1) * group] - zv) / sv
+            ok = np.abs(tt - np.floor(tt) - 0.5) > 1e-9
+            assert np.array_equal(codes[n, gm * group:(gm + 1) * group][ok], ref[ok])
+
+
+def test_p7_degenerate_groups_and_nan():
+    d, group = 8, 4
+    x = np.zeros((3, d))
+    x[1, :4] = 2.0                       # constant group -> s = 0, codes 0, z = value
+    x[2, 0] = np.nan
+    codes, s, z, _ = O.quantize(x, np.eye(d), 10.0, group)
+    assert np.all(codes[0] == 0) and np.all(s[0] == 0) and np.all(z[0] == 0)
+    assert s[1, 0] == 0 and z[1, 0] == 2.0 and np.all(codes[1, :4] == 0)
+    assert np.isnan(s[2, 0]) and np.isnan(z[2, 0]) and np.all(codes[2, :4] == 0)
+    assert np.all(np.isnan(s[2])) and np.all(codes[2] == 0)   # NaN * 0 = NaN: the rotation spreads it
+
+
+def test_p7_clip_bounds_dequantised_values():
+    rng = np.random.default_rng(72)
+    r = _rand_orth(rng, 16)
+    x = rng.standard_normal((200, 16)) * 5
+    codes, s, z, xr = O.quantize(x, r, 1.5, 8)
+    assert np.all(np.abs(xr) <= 1.5)
+    deq = O.dequantize(codes, s, z, 8)
+    err = np.abs(deq - xr).reshape(200, 2, 8).max(axis=2)
+    assert np.all(err <= s.astype(np.float64) / 2 + 2e-3 * 1.5)
+
+
+def test_p7_int2_block_layout_by_hand():
+    d, group = 128, 32
+    kc = np.tile(np.arange(d) % 4, (16, 1)).astype(np.uint8)        # channel j -> code j%4
+    vc = np.zeros((16, d), np.uint8)
+    vc[3, 5] = 3                                                     # token 3, channel 5
+    vc[9, 127] = 2                                                   # token 9, channel 127
+    ks = np.full((16, 4), np.float16(0.5))
+    kz = np.full((16, 4), np.float16(-1.0))
+    blk = O.pack_int2_block(kc, ks, kz, vc, ks, kz)
+    assert blk.size == O.int2_block_bytes(d, group) == 1536
+    assert np.all(blk[:512] == 0xE4)                                 # 0b11_10_01_00
+    sz = blk[512:768].view(np.float16).reshape(4, 16, 2)
+    assert np.all(sz[:, :, 0] == 0.5) and np.all(sz[:, :, 1] == -1.0)
+    vw = blk[768:1280].view(np.uint16).reshape(2, d)
+    assert vw[0, 5] == 3 << 6 and vw[1, 127] == 2 << 2
+    assert np.count_nonzero(vw) == 2
+    back = O.unpack_int2_block(blk, d, group)
+    for a, b in zip(back, (kc, ks, kz, vc, ks, kz)):
+        assert np.array_equal(a, b)
+
+
+def test_p7_int2_block_roundtrip_all_bytes():
+    rng = np.random.default_rng(73)
+    for group in (32, 64):
+        ng = 128 // group
+        kc, vc = rng.integers(0, 4, (2, 16, 128)).astype(np.uint8)
+        ks, kz, vs, vz = (rng.standard_normal((4, 16, ng)) * 4).astype(np.float16)
+        blk = O.pack_int2_block(kc, ks, kz, vc, vs, vz)
+        assert blk.size == O.int2_block_bytes(128, group)
+        for a, b in zip(O.unpack_int2_block(blk, 128, group), (kc, ks, kz, vc, vs, vz)):
+            assert np.array_equal(a, b)
+    # every byte value decodes to four 2-bit fields and re-encodes to itself
+    allb = np.arange(256, dtype=np.uint8)
+    blk = np.zeros(1536, np.uint8)
+    blk[:256] = allb
+    blk[256:512] = allb[::-1]
+    kc = O.unpack_int2_block(blk, 128, 32)[0]
+    for b in range(256):
+        t, j0 = divmod(b, 32)
+        assert [int(kc[t, 4 * j0 + i]) for i in range(4)] == [(b >> (2 * i)) & 3 for i in range(4)]
+
+
+def test_bf16_block_layout():
+    rng = np.random.default_rng(8)
+    k, v = rng.integers(0, 65535, (2, 16, 128)).astype(np.uint16)
+    blk = O.pack_bf16_block(k, v)
+    assert blk.size == O.bf16_block_bytes(128) == 8192
+    assert np.array_equal(blk[:4096].view(np.uint16).reshape(16, 128), k)
+    assert blk[4096:].view(np.uint16)[7 * 16 + 3] == v[3, 7]
+
+
+# --- P8: the pages' accounting ---------------------------------------------
+
+def test_p8_bits_per_element_matches_printed_values():
+    gc = golden("pages_constants.txt")
+    s0, w = int(gc["sink_tokens"]), int(gc["recent_tokens"])
+    hist = O.int2_history_bits(int(gc["group_k"]), 8, 8)        # 2.25 bits: G=64 with 8-bit scale and zero
+    assert hist == 2.25
+    bpe_main = O.bits_per_element(int(gc["main_context"]), s0, w, hist)
+    bpe_aime = O.bits_per_element(int(gc["aime_generation"]), s0, w, hist)
+    assert round(bpe_main, 2) == gc["bpe_main"] and abs(bpe_main - 2.2836) < 1e-4
+    assert round(bpe_aime, 2) == gc["bpe_aime_qwen3_8b"] and abs(bpe_aime - 2.3843) < 1e-4
+    reg = O.regions(int(gc["main_context"]), s0, w)
+    share = 100.0 * np.count_nonzero(reg != O.REGION_INT2) / reg.size
+    assert round(share, 2) == gc["bf16_share_128k_pct"]
+    assert O.int2_history_bits(32) == 3.0 and O.int2_history_bits(64) == 2.5
+    # block sizes agree with the accounting: (codes + s/z) bytes per token and head
+    assert O.int2_block_bytes(128, 32) * 8 == 16 * 2 * 128 * O.int2_history_bits(32)
+
+
+def test_regions_small_cases():
+    assert list(O.regions(10, 2, 3)) == [0, 0, 1, 1, 1, 1, 1, 2, 2, 2]
+    assert list(O.regions(5, 2, 3)) == [0, 0, 2, 2, 2]
+    assert list(O.regions(3, 4, 3)) == [0, 0, 0]
+    assert list(O.regions(6, 0, 0)) == [1] * 6
+
+
+# --- P9: special cases reducing to library routines --------------------------
+
+def _sdpa(q, k, v):
+    hq, d = q.shape
+    hkv = k.shape[1]
+    kk = torch.tensor(np.repeat(k.transpose(1, 0, 2), hq // hkv, axis=0))
+    vv = torch.tensor(np.repeat(v.transpose(1, 0, 2), hq // hkv, axis=0))
+    return torch.nn.functional.scaled_dot_product_attention(
+        torch.tensor(q)[:, None, :], kk, vv)[:, 0, :].numpy()
+
+
+def test_p9_all_bf16_equals_sdpa(tiny_cal):
+    w, q, k, v, cal = tiny_cal
+    rng = np.random.default_rng(9)
+    t, hkv, hq = 100, 2, 6
+    kb = synth.f32_to_bf16_bits(rng.standard_normal((t, hkv, D)).astype(np.float32))
+    vb = synth.f32_to_bf16_bits(rng.standard_normal((t, hkv, D)).astype(np.float32))
+    qb = synth.f32_to_bf16_bits(rng.standard_normal((hq, D)).astype(np.float32))
+    cal2 = O.LayerCalibration(np.stack([cal.r_k[0]] * hkv), np.stack([cal.r_v[0]] * hkv),
+                              None, None, cal.tau_k, cal.tau_v)
+    st = O.store_request(kb, vb, cal2, 32, 4, 128)            # t <= S0 + W: all bf16
+    assert np.all(st.region != O.REGION_INT2)
+    out = O.decode_attention(qb, st, cal2, 32)
+    ref = _sdpa(O.bf16_to_f64(qb), O.bf16_to_f64(kb), O.bf16_to_f64(vb))
+    assert np.abs(out - ref).max() < 1e-12
+
+
+def test_p9_grid_exact_int2_equals_sdpa():
+    """Values on the 4-level grid with a signed-permutation rotation are stored
+    exactly, so INT2 attention equals plain fp64 attention."""
+    rng = np.random.default_rng(91)
+    t, hkv, hq, group = 64, 1, 2, 32
+    perm = rng.permutation(D)
+    r = np.zeros((D, D), np.float32)
+    r[np.arange(D), perm] = rng.choice([-1.0, 1.0], D)
+    levels = np.array([-1.5, -1.0, -0.5, 0.0])
+    c = rng.integers(0, 4, (t, hkv, D))
+    c[:, :, ::group] = 0
+    c[:, :, 1::group] = 3                                      # every group spans the full grid
+    x_rot = levels[c]
+    x = np.einsum("thj,ij->thi", x_rot, r.astype(np.float64))  # x = x_rot R^T exactly
+    kb = synth.f32_to_bf16_bits(x.astype(np.float32))
+    vb = kb.copy()
+    assert np.array_equal(O.bf16_to_f64(kb), x)
+    cal = O.LayerCalibration(r[None], r[None], None, None, np.float32(2.0), np.float32(2.0))
+    st = O.store_request(kb, vb, cal, group, 0, 0)
+    assert np.all(st.region == O.REGION_INT2)
+    assert np.array_equal(st.k_codes, c.astype(np.uint8))
+    qb = synth.f32_to_bf16_bits(rng.standard_normal((hq, D)).astype(np.float32))
+    out = O.decode_attention(qb, st, cal, group)
+    ref = _sdpa(O.bf16_to_f64(qb), x, x)
+    assert np.abs(out - ref).max() < 1e-12
+
+
+# --- P10: tiny brute force end to end; algebraic undo ------------------------
+
+def _loop_quant(x, r, tau, group):
+    n, d = len(x), len(x[0])
+    codes, ss, zz, deq = [], [], [], []
+    for row in x:
+        rot = [min(max(sum(row[i] * r[i][j] for i in range(d)), -tau), tau) for j in range(d)]
+        crow, srow, zrow, drow = [], [], [], []
+        for gm in range(d // group):
+            vals = rot[gm * group:(gm + 1) * group]
+            s = _exact_f16_round((max(vals) - min(vals)) / 3.0)
+            z = _exact_f16_round(min(vals))
+            for val in vals:
+                c = 0 if s == 0 else min(3, max(0, round((val - z) / s)))
+                crow.append(c)
+                drow.append(z + c * s)
+            srow.append(s)
+            zrow.append(z)
+        codes.append(crow), ss.append(srow), zz.append(zrow), deq.append(drow)
+    return codes, ss, zz, deq
+
+
+@pytest.mark.parametrize("d", [4, 8, 16])
+def test_p10_brute_force_end_to_end(d):
+    rng = np.random.default_rng(100 + d)
+    n_cal, t, g, group, s0, w = 24, 40, 2, d // 2, 2, 5
+    qc = rng.standard_normal((n_cal, g, d))
+    kc = rng.standard_normal((n_cal, d))
+    vc = rng.standard_normal((n_cal, d))
+    # covariances by loops
+    cq = [[sum(qc[n, h, a] * qc[n, h, b] for n in range(n_cal) for h in range(g)) / (n_cal * g)
+           for b in range(d)] for a in range(d)]
+    assert np.abs(O.query_covariance(qc) - np.array(cq)).max() < 1e-12
+    cs = np.zeros((d, d))
+    for h in range(g):
+        for i in range(n_cal):
+            e = [math.exp(sum(qc[i, h, a] * kc[j, a] for a in range(d)) / math.sqrt(d)) for j in range(i + 1)]
+            o = [sum(e[j] / sum(e) * vc[j, b] for j in range(i + 1)) for b in range(d)]
+            cs += np.outer(o, o)
+    cs /= n_cal * g
+    assert np.abs(O.score_weighted_value_covariance(qc, kc, vc) - cs).max() < 1e-12
+    # quantisation by loops
+    r = _rand_orth(rng, d).astype(np.float32).astype(np.float64)
+    x = O.bf16_to_f64(synth.f32_to_bf16_bits((rng.standard_normal((t, d)) * 2).astype(np.float32)))
+    codes, s, z, xr = O.quantize(x, r, 2.5, group)
+    lc, ls, lz, ld = _loop_quant(x.tolist(), r.tolist(), 2.5, group)
+    assert np.array_equal(codes, np.array(lc)) and np.array_equal(s.astype(float), np.array(ls))
+    assert np.array_equal(z.astype(float), np.array(lz))
+    # attention by loops over the stored representation (explicit inverse rotation)
+    reg = O.regions(t, s0, w)
+    cal = O.LayerCalibration(r.astype(np.float32)[None], r.astype(np.float32)[None], None, None,
+                             np.float32(2.5), np.float32(2.5))
+    kb = synth.f32_to_bf16_bits(x.astype(np.float32))[:, None, :]
+    vb = synth.f32_to_bf16_bits((x[::-1] * 0.5).astype(np.float32).copy())[:, None, :]
+    st = O.store_request(kb, vb, cal, group, s0, w)
+    qv = rng.standard_normal(d)
+    qb = synth.f32_to_bf16_bits(qv.astype(np.float32))[None]
+    qf = O.bf16_to_f64(qb)[0]
+    kv_rows = []
+    _, _, _, kdeq = _loop_quant(O.bf16_to_f64(kb[:, 0]).tolist(), r.tolist(), 2.5, group)
+    _, _, _, vdeq = _loop_quant(O.bf16_to_f64(vb[:, 0]).tolist(), r.tolist(), 2.5, group)
+    for p in range(t):
+        if reg[p] == O.REGION_INT2:
+            kr = [sum(kdeq[p][j] * r[i][j] for j in range(d)) for i in range(d)]
+            vr = [sum(vdeq[p][j] * r[i][j] for j in range(d)) for i in range(d)]
+        else:
+            kr = list(O.bf16_to_f64(kb[p, 0]))
+            vr = list(O.bf16_to_f64(vb[p, 0]))
+        kv_rows.append((kr, vr))
+    lg = [sum(qf[a] * kr[a] for a in range(d)) / math.sqrt(d) for kr, _ in kv_rows]
+    mx = max(lg)
+    e = [math.exp(x_ - mx) for x_ in lg]
+    ref = [sum(e[p] / sum(e) * kv_rows[p][1][b] for p in range(t)) for b in range(d)]
+    out = O.decode_attention(qb, st, cal, group)[0]
+    assert np.abs(out - np.array(ref)).max() < 1e-12
+    # algebraic undo: (q R) . x_rot for keys, R^T applied once to the summed values
+    int2 = reg == O.REGION_INT2
+    kd = O.dequantize(st.k_codes[:, 0], st.k_s[:, 0], st.k_z[:, 0], group)
+    vd = O.dequantize(st.v_codes[:, 0], st.v_s[:, 0], st.v_z[:, 0], group)
+    qr = qf @ r
+    lg2 = np.where(int2, kd @ qr, O.bf16_to_f64(kb[:, 0]) @ qf) / math.sqrt(d)
+    p2 = np.exp(lg2 - lg2.max())
+    p2 /= p2.sum()
+    o2 = (p2[int2] @ vd[int2]) @ r.T + p2[~int2] @ O.bf16_to_f64(vb[~int2, 0])
+    assert np.abs(out - o2).max() < 1e-12
+
+
+# --- region planner reference model ------------------------------------------
+
+@pytest.mark.parametrize("s0,w", [(4, 128), (64, 256), (0, 16), (3, 5), (4, 0)])
+def test_plan_append_replays_to_region_rule(s0, w):
+    rng = np.random.default_rng(s0 * 1000 + w)
+    t_final = 700
+    ring = {}
+    int2 = {}
+    t = 0
+    while t < t_final:
+        n = int(min(t_final - t, rng.choice([1, 1, 2, 7, 16, 33, 150])))
+        i2, bf, age = O.plan_append(t, n, s0, w)
+        for src, dst in age:                       # age-out reads before new writes
+            int2[dst] = ring.pop(src)
+        for i in range(n):
+            p = t + i
+            if i2[i] >= 0:
+                assert i2[i] == p
+                int2[p] = p
+            else:
+                assert bf[i] not in ring
+                ring[bf[i]] = p
+        t += n
+        reg = O.regions(t, s0, w)
+        assert sorted(int2) == list(np.nonzero(reg == O.REGION_INT2)[0])
+        assert all(int2[p] == p for p in int2)
+        assert sorted(ring.values()) == list(np.nonzero(reg != O.REGION_INT2)[0])
+        for slot, p in ring.items():
+            assert slot == O.bf16_logical_slot(p, s0, w)
