@@ -1,0 +1,243 @@
+/*
+ * oscar.h -- C ABI of the OSCAR 2-bit KV-cache hot path for MI355X (gfx950).
+ *
+ * OSCAR ("Offline Spectral Covariance-Aware Rotation", arXiv 2605.17757) stores
+ * the history of the KV cache as per-token INT2 after a fixed, calibrated
+ * rotation, and keeps sink and recent tokens in bf16.  Sources, cited by page
+ * title and section:
+ *   [IT] gist.science, Italian technical summary of arXiv 2605.17757, sections
+ *        2.2.A (offline calibration) and 2.2.B (online serving).
+ *   [ES] 7minutos.es article on OSCAR, sections "Lo que OSCAR hace diferente"
+ *        (covariances, composite rotations, Lemma 1, bit reversal) and "El
+ *        sistema de servicio: diseno de cache de precision mixta" (regions,
+ *        write path, read path).
+ *   [JA] gist.science, Japanese technical summary, sections 2.2.A and 2.2.B.
+ *
+ * Conventions
+ *   - Every call returns oscar_status: OSCAR_OK (0) or a negative code.  No C++
+ *     exception crosses this boundary.  oscar_last_error() returns a message for
+ *     the last failing call on the calling thread.
+ *   - "device" pointers are GPU memory owned by the caller; "host" pointers are
+ *     CPU memory owned by the caller.  The library never allocates device memory.
+ *   - Kernels are enqueued on the caller's HIP stream (hipStream_t passed as
+ *     void*; NULL = the null stream) and run asynchronously.  A GPU fault shows
+ *     up at the caller's next synchronisation.  Argument errors are detected on
+ *     the host before anything is enqueued.
+ *   - Row-vector convention: a head vector x (d channels) is rotated as
+ *     x_rot = x R, with R stored row-major [d][d] in fp32.
+ *   - A pool (oscar_pool) holds host bookkeeping only (free lists, reference
+ *     counts, sequences); it is not thread-safe: callers serialise calls that
+ *     take the same pool.  Launch functions keep no state and are reentrant.
+ *   - Slots: a physical slot is page_id * page_size + slot_in_page (int32).
+ *
+ * Storage format of one (page, KV head) block, d channels, G channels per
+ * group, NG = d / G, page_size = 16 tokens:
+ *   INT2 block (2*(4*d + 64*NG) bytes: 1536 for d=128,G=32; 1280 for G=64):
+ *     K codes  [16][d/4] bytes, token-major; channel j of token t sits in byte
+ *              t*d/4 + j/4 at bits 2*(j%4).
+ *     K scale/zero  fp16 [NG][16][2] = (s, z) per group and token.
+ *     V codes  16-bit words [2][d]: word [a][j] holds channel j of tokens
+ *              8a..8a+7, token 8a+i at bits 2*i.
+ *     V scale/zero  as for K.
+ *   BF16 block (4*16*d bytes): K as bf16 [16][d] (token-major), then V as
+ *   bf16 [d][16] (channel-major).
+ *   A layer's INT2 storage is [n_int2_pages][n_kv_heads][INT2 block]; its bf16
+ *   storage is [n_bf16_pages][n_kv_heads][BF16 block].
+ *
+ * Regions of a request of length T ([ES] serving section; [IT] 2.2.B):
+ *   positions [0, sink) are bf16 "sink" tokens, the last `recent` positions are
+ *   bf16 "recent" tokens, everything between is INT2 history.  INT2 position p
+ *   lives in INT2 logical page p/16, slot p%16.  Sink position p lives in bf16
+ *   logical page p/16; recent position p lives in a ring of `recent` slots
+ *   after the sink pages: bf16 logical slot 16*ceil(sink/16) + (p-sink)%recent.
+ */
+#ifndef OSCAR_H
+#define OSCAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t oscar_status;
+#define OSCAR_OK 0
+#define OSCAR_EINVAL (-1)        /* bad argument (null pointer, size, alignment, range) */
+#define OSCAR_ENOMEM (-2)        /* a pool ran out of pages (host bookkeeping only) */
+#define OSCAR_EHIP (-3)          /* the HIP runtime reported an error at launch */
+#define OSCAR_EUNSUPPORTED (-4)  /* shape outside what the kernels are built for */
+
+/* Shape of one attention layer and of the cache layout.
+ * Supported: head_dim 128, page_size 16, group 32 or 64, n_q_heads a multiple
+ * of n_kv_heads with n_q_heads / n_kv_heads * (head_dim / group) <= 48,
+ * sink >= 0, recent >= 0 (recent a multiple of page_size or 0). */
+typedef struct oscar_shape {
+  int32_t head_dim;    /* d */
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t group;       /* G: channels per quantisation group ([ES] write path; default there 64) */
+  int32_t sink;        /* S0 ([ES] serving section; 64 there) */
+  int32_t recent;      /* W  ([ES] serving section; 256 there) */
+  int32_t page_size;   /* tokens per page */
+} oscar_shape;
+
+/* Calibration state of one layer ([IT] 2.2.A: fixed rotations and clip
+ * thresholds).  r_k / r_v: device fp32 [n_kv_heads][d][d]. */
+typedef struct oscar_layer {
+  const float* r_k;
+  const float* r_v;
+  float tau_k;         /* clip threshold for rotated keys (x_rot clamped to [-tau, tau]) */
+  float tau_v;
+} oscar_layer;
+
+/* Device storage of one layer (caller-owned; 256-byte aligned). */
+typedef struct oscar_cache {
+  void* int2_pages;
+  int64_t n_int2_pages;
+  void* bf16_pages;
+  int64_t n_bf16_pages;
+} oscar_cache;
+
+typedef struct oscar_pool oscar_pool;
+typedef struct oscar_seq oscar_seq;
+
+const char* oscar_last_error(void);
+
+/* Bytes of one (page, KV head) block. */
+int64_t oscar_int2_block_bytes(const oscar_shape* shape);
+int64_t oscar_bf16_block_bytes(const oscar_shape* shape);
+
+/* ---- Offline calibration ([IT] 2.2.A; [ES] "Lo que OSCAR hace diferente") ----
+ * Inputs (host, fp32): q [n][n_q_heads][d], k and v [n][n_kv_heads][d]: one
+ * calibration sequence of n tokens.  For each KV head (its g = Hq/Hkv query
+ * heads pooled): C_Q = sum q^T q / (n g); C_S = sum_h V^T S_h^T S_h V / (n g)
+ * with S_h the causal softmax(Q_h K^T / sqrt(d)); eigenbases sorted by
+ * decreasing eigenvalue, each eigenvector signed so its largest-magnitude entry
+ * is positive; R_K = U_Q H P_br, R_V = U_S H P_br (H: orthonormal Sylvester
+ * Walsh-Hadamard in natural order; P_br: bit-reversal permutation).  tau_k and
+ * tau_v: the clip_pct_k / clip_pct_v quantile (linear interpolation) of
+ * |x R| over all calibration tokens, KV heads and channels, using the fp32 R.
+ * Computed in fp64 on the host; outputs (host): r_k_out, r_v_out fp32
+ * [n_kv][d][d]; eig_k_out, eig_v_out fp64 [n_kv][d] (may be NULL); tau outputs.
+ * Errors: OSCAR_EINVAL for null pointers, n < 1, bad shape or a quantile
+ * outside (0, 1]. */
+oscar_status oscar_calibrate_host(const oscar_shape* shape, int64_t n, const float* q, const float* k,
+                                  const float* v, double clip_pct_k, double clip_pct_v, float* r_k_out,
+                                  float* r_v_out, double* eig_k_out, double* eig_v_out, float* tau_k_out,
+                                  float* tau_v_out);
+
+/* ---- Page pools and sequences (host bookkeeping; [IT] 2.2.B paged cache with
+ * prefix caching; [ES] serving section) ---- */
+oscar_status oscar_pool_create(const oscar_shape* shape, int64_t n_int2_pages, int64_t n_bf16_pages,
+                               oscar_pool** out);
+oscar_status oscar_pool_destroy(oscar_pool* pool);
+/* Free pages left in each pool (either pointer may be NULL). */
+oscar_status oscar_pool_free_pages(const oscar_pool* pool, int64_t* int2_free, int64_t* bf16_free);
+
+oscar_status oscar_seq_create(oscar_pool* pool, oscar_seq** out);
+/* Drops the sequence's page references; pages whose count reaches zero return
+ * to the free lists. */
+oscar_status oscar_seq_release(oscar_pool* pool, oscar_seq* seq);
+int64_t oscar_seq_length(const oscar_seq* seq);
+
+/* Plan the growth of `seq` by n_new tokens (positions T .. T+n_new-1), allocating
+ * pages as needed.  Outputs (host arrays):
+ *   int2_slots[n_new]  physical INT2 slot of each new token that goes straight to
+ *                      the INT2 history, else -1;
+ *   bf16_slots[n_new]  physical bf16 slot of each new sink/recent token, else -1;
+ *   age_src[], age_dst[] (capacity n_new + recent): tokens that leave the recent
+ *                      window: physical bf16 slot -> physical INT2 slot; *n_age
+ *                      receives their count.
+ * Execution order on the device: oscar_requant_from_bf16 (age-out) first, then
+ * oscar_quant_write and oscar_bf16_write for the new tokens (a new recent token
+ * may reuse the ring slot of a token that ages out).  On OSCAR_ENOMEM nothing is
+ * changed. */
+oscar_status oscar_seq_plan_append(oscar_pool* pool, oscar_seq* seq, int64_t n_new, int32_t* int2_slots,
+                                   int32_t* bf16_slots, int32_t* age_src, int32_t* age_dst, int64_t* n_age);
+
+/* New sequence equal to `parent` as it stands (prefix caching).  Sink pages and
+ * full INT2 pages are shared by reference count; pages the child will write into
+ * (the partly filled last INT2 page and the recent ring) are fresh copies.  The
+ * caller must run the copies with oscar_copy_pages before writing to either
+ * sequence: copy_src/copy_dst (host, capacity 64 + recent/16 each) receive
+ * physical page ids and copy_kind 0 (INT2) or 1 (bf16); *n_copies their count. */
+oscar_status oscar_seq_fork(oscar_pool* pool, const oscar_seq* parent, oscar_seq** child, int32_t* copy_src,
+                            int32_t* copy_dst, int32_t* copy_kind, int64_t* n_copies);
+
+/* Block tables for a batch (host outputs): int2_bt [n][max_int2_pages] and
+ * bf16_bt [n][max_bf16_pages] physical page ids (-1 past the end), ctx_lens[n].
+ * Errors: OSCAR_EINVAL if a sequence needs more pages than the row width. */
+oscar_status oscar_block_tables(const oscar_pool* pool, const oscar_seq* const* seqs, int32_t n,
+                                int32_t* int2_bt, int32_t max_int2_pages, int32_t* bf16_bt,
+                                int32_t max_bf16_pages, int32_t* ctx_lens);
+
+/* ---- Write path ([ES] serving section, write path; [IT] 2.2.B) ----
+ * For each token i < n with int2_slots[i] >= 0 and each KV head h:
+ *   x_rot = x R (fp64 accumulation of the exact bf16 x fp32 products);
+ *   clamp to [-tau, tau]; per group of G channels: mn, mx,
+ *   s = fp16((mx-mn)/3), z = fp16(mn) (fp64 arithmetic, one rounding to fp16,
+ *   nearest-even); code = clamp(rint((x_rot - z)/s), 0, 3) (fp64, half-even),
+ *   code = 0 where s == 0; a group holding NaN stores s = z = NaN, codes 0;
+ * packed into the slot's INT2 block.  Inputs: k_bf16, v_bf16 device bf16
+ * [n][n_kv_heads][d]; int2_slots device int32 [n].  Slots must be distinct
+ * within one call.  n == 0 is a no-op. */
+oscar_status oscar_quant_write(const oscar_shape* shape, const oscar_layer* layer, const oscar_cache* cache,
+                               const void* k_bf16, const void* v_bf16, const int32_t* int2_slots, int64_t n,
+                               void* stream);
+
+/* Same quantisation for tokens already held in bf16 slots (tokens leaving the
+ * recent window): src_bf16_slots / dst_int2_slots device int32 [n]. */
+oscar_status oscar_requant_from_bf16(const oscar_shape* shape, const oscar_layer* layer,
+                                     const oscar_cache* cache, const int32_t* src_bf16_slots,
+                                     const int32_t* dst_int2_slots, int64_t n, void* stream);
+
+/* Copy bf16 K/V (unrotated) of tokens with bf16_slots[i] >= 0 into bf16 blocks
+ * (sink and recent tokens).  k_bf16, v_bf16: device [n][n_kv_heads][d]. */
+oscar_status oscar_bf16_write(const oscar_shape* shape, const oscar_cache* cache, const void* k_bf16,
+                              const void* v_bf16, const int32_t* bf16_slots, int64_t n, void* stream);
+
+/* Copy whole pages (all KV heads): kind 0 = INT2 storage, 1 = bf16 storage.
+ * src, dst: device int32 [n] physical page ids. */
+oscar_status oscar_copy_pages(const oscar_shape* shape, const oscar_cache* cache, int32_t kind,
+                              const int32_t* src_pages, const int32_t* dst_pages, int64_t n, void* stream);
+
+/* ---- Read path: mixed-precision paged decode attention ([ES] serving
+ * section, read path; [IT] 2.2.B) ----
+ * For each request b and query head h (KV head h / (Hq/Hkv)), over the T =
+ * ctx_lens[b] positions of the request:
+ *   o = sum_t softmax_t(q.k_t / sqrt(d)) v_t, with k_t, v_t the stored bf16
+ *   values for sink/recent positions and (z + c s) R^T for INT2 positions.
+ * The rotation is undone algebraically: logits of INT2 tokens use q R_K, and the
+ * INT2 part of the value sum is multiplied by R_V^T once.  Split-K partials
+ * (log-sum-exp) are merged by a second kernel.
+ * Inputs (device): q bf16 [batch][n_q_heads][d]; int2_bt int32
+ * [batch][max_int2_pages]; bf16_bt int32 [batch][max_bf16_pages]; ctx_lens
+ * int32 [batch].  Output (device): out fp32 [batch][n_q_heads][d].
+ * splits_int2 / splits_bf16: work items per (request, KV head) for the INT2 and
+ * bf16 regions (0 = choose).  workspace: device, >= oscar_decode_workspace_bytes
+ * with the same arguments, 256-byte aligned.  T = 0 gives a zero row. */
+size_t oscar_decode_workspace_bytes(const oscar_shape* shape, int32_t batch, int32_t splits_int2,
+                                    int32_t splits_bf16);
+oscar_status oscar_decode_attn(const oscar_shape* shape, const oscar_layer* layer, const oscar_cache* cache,
+                               const void* q, int32_t batch, const int32_t* int2_bt, int32_t max_int2_pages,
+                               const int32_t* bf16_bt, int32_t max_bf16_pages, const int32_t* ctx_lens,
+                               int32_t splits_int2, int32_t splits_bf16, float* out, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/* The same decode kernels over an all-bf16 cache (the comparison baseline):
+ * position p of request b lives in bf16 logical page p/16 (bf16_bt row b),
+ * slot p%16; sink/recent/INT2 regions are not used. */
+oscar_status oscar_decode_attn_bf16_baseline(const oscar_shape* shape, const oscar_cache* cache, const void* q,
+                                             int32_t batch, const int32_t* bf16_bt, int32_t max_bf16_pages,
+                                             const int32_t* ctx_lens, int32_t splits, float* out,
+                                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Splits chosen when 0 is passed (deterministic in the arguments). */
+int32_t oscar_decode_auto_splits(const oscar_shape* shape, int32_t batch, int32_t max_int2_pages);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OSCAR_H */

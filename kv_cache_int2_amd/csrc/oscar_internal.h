@@ -1,0 +1,75 @@
+// Internal declarations shared by the host library and the HIP kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace oscar {
+
+constexpr int kHeadDim = 128;
+constexpr int kPage = 16;
+
+// Byte offsets inside an INT2 (page, KV head) block; ng = head_dim / group.
+struct Int2Layout {
+  int ng;
+  __host__ __device__ constexpr int k_codes() const { return 0; }
+  __host__ __device__ constexpr int k_sz() const { return kPage * kHeadDim / 4; }
+  __host__ __device__ constexpr int v_codes() const { return k_sz() + kPage * ng * 4; }
+  __host__ __device__ constexpr int v_sz() const { return v_codes() + kPage * kHeadDim / 4; }
+  __host__ __device__ constexpr int bytes() const { return v_sz() + kPage * ng * 4; }
+};
+constexpr int kBf16BlockBytes = 4 * kPage * kHeadDim;
+
+struct QuantParams {
+  const uint16_t* k_src;      // dense bf16 [n][n_kv][d]            (mode 0)
+  const uint16_t* v_src;
+  const uint8_t* bf16_pages;  // bf16 storage for requantisation    (mode 1)
+  int64_t n_bf16_pages;
+  const int32_t* src_slots;   // bf16 physical slots                (mode 1)
+  const int32_t* dst_slots;   // INT2 physical slots
+  uint8_t* int2_pages;
+  int64_t n_int2_pages;
+  const float* r_k;           // [n_kv][d][d]
+  const float* r_v;
+  double tau_k, tau_v;
+  int64_t n;
+  int n_kv;
+  int group;
+};
+
+struct DecodeParams {
+  const uint8_t* int2_pages;
+  int64_t n_int2_pages;
+  const uint8_t* bf16_pages;
+  int64_t n_bf16_pages;
+  const uint16_t* q;          // bf16 [B][Hq][d]
+  const float* r_k;           // [n_kv][d][d]
+  const float* r_v;
+  const int32_t* int2_bt;
+  int max_int2_pages;
+  const int32_t* bf16_bt;
+  int max_bf16_pages;
+  const int32_t* ctx_lens;
+  int batch, n_q, n_kv, g, ng, ct;
+  int sink, recent;           // region rule (baseline: sink huge, recent 0)
+  int splits_int2, splits_bf16;
+  float p_scale_exp;          // P' is scaled by 2^p_scale_exp before fp16 rounding
+  // workspace carve-up
+  uint32_t* qb;               // [B*n_kv][ct][2][4][64][4] fp16x2 words (q R_K hi/lo operands)
+  float* qaux;                // [B*n_kv][1 + 16*ct]: logit factor, then scaled group sums
+  float* partial;             // [B][Hq][splits][2 + d]: m (log2), l, acc
+  float* out;                 // [B][Hq][d]
+};
+
+hipError_t launch_quant_write(const QuantParams& p, int mode, hipStream_t stream);
+hipError_t launch_bf16_write(const uint16_t* k, const uint16_t* v, const int32_t* slots, int64_t n, int n_kv,
+                             uint8_t* bf16_pages, int64_t n_pages, hipStream_t stream);
+hipError_t launch_copy_pages(uint8_t* base, int64_t block_bytes_all_heads, int64_t n_pages, const int32_t* src,
+                             const int32_t* dst, int64_t n, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
+
+// Workspace bytes for the decode path (each region 256-byte aligned).
+size_t decode_workspace_bytes(int batch, int n_q, int n_kv, int ct, int splits_total);
+void decode_workspace_carve(DecodeParams& p, void* ws);
+
+}  // namespace oscar

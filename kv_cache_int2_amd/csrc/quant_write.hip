@@ -1,0 +1,304 @@
+// OSCAR write path for gfx950: rotate, clip, per-token asymmetric INT2 per
+// channel group, pack into the paged INT2 blocks.
+//
+// [ES] "El sistema de servicio", write path: each token is rotated by the fixed
+// calibrated rotation, clipped at the calibrated percentile threshold, and
+// quantised to asymmetric INT2 per token with a group of channels sharing a
+// scale and zero point.  [IT] 2.2.B: the history lives in INT2 after the fixed
+// rotation and clip.
+//
+// One wavefront handles 16 tokens of one KV head and one of K / V:
+//   x_rot[16][128] = X[16][128] R[128][128]   on v_mfma_f64_16x16x4_f64.
+// X holds bf16 values and R fp32 values; both are exact in fp64 and so are
+// their products, and the sums are fp64.  The quantiser's decisions (fp16
+// rounding of scale and zero, the code of each element) are therefore taken on
+// an fp64 rotated value, the same precision a double-precision reference uses.
+// Per group: mn, mx; s = fp16((mx - mn) / 3), z = fp16(mn), one rounding from
+// fp64, nearest-even; code = clamp(rint((x - z) / s), 0, 3) in fp64 (IEEE
+// division, rint = nearest-even).
+//
+// Storage (per (page, KV head) block): K codes token-major (a token's 32 bytes
+// are its own), V codes channel-major 16-bit words [2][128] (8 tokens of one
+// channel per word).  V words are written whole when this wavefront holds all
+// 8 tokens of that half page, else merged with 32-bit atomic and/or, so tokens
+// of one page may be written by different wavefronts or launches.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "oscar_internal.h"
+
+namespace oscar {
+namespace {
+
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+// IEEE binary64 -> binary16, round to nearest even (single rounding).
+__device__ __forceinline__ uint16_t f64_to_f16_bits(double x) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint16_t sign = (uint16_t)((u >> 48) & 0x8000u);
+  const uint64_t a = u & 0x7fffffffffffffffull;
+  if (a >= 0x7ff0000000000000ull) return sign | (a > 0x7ff0000000000000ull ? 0x7e00u : 0x7c00u);
+  if (a == 0) return sign;
+  int e = (int)(a >> 52) - 1023;
+  uint64_t m = a & 0x000fffffffffffffull;
+  if (e == -1023) {
+    return sign;  // binary64 subnormal: far below half the smallest binary16 subnormal
+  }
+  m |= 1ull << 52;
+  if (e >= -14) {
+    uint64_t mant = m >> 42;
+    const uint64_t rem = m & ((1ull << 42) - 1);
+    const uint64_t half = 1ull << 41;
+    if (rem > half || (rem == half && (mant & 1))) ++mant;
+    if (mant == 2048) {
+      mant = 1024;
+      ++e;
+    }
+    if (e > 15) return sign | 0x7c00u;
+    return sign | (uint16_t)((e + 15) << 10) | (uint16_t)(mant & 0x3ffu);
+  }
+  const int shift = 28 - e;  // >= 43
+  if (shift >= 64) return sign;
+  uint64_t mant = m >> shift;
+  const uint64_t rem = m & ((1ull << shift) - 1);
+  const uint64_t half = 1ull << (shift - 1);
+  if (rem > half || (rem == half && (mant & 1))) ++mant;
+  return sign | (uint16_t)mant;
+}
+
+__device__ __forceinline__ double f16_bits_to_f64(uint16_t h) {
+  return (double)__builtin_bit_cast(_Float16, h);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __builtin_bit_cast(float, (uint32_t)b << 16); }
+
+template <int MODE, int NG>
+__global__ __launch_bounds__(64) void quant_write_kernel(QuantParams p) {
+  constexpr int G = kHeadDim / NG;
+  constexpr Int2Layout L{NG};
+  const int lane = threadIdx.x;
+  const int64_t t0 = (int64_t)blockIdx.x * 16;
+  const int kv = blockIdx.y;
+  const int isv = blockIdx.z;
+  __shared__ float xin[16][kHeadDim + 1];
+  __shared__ double xr[16][kHeadDim + 1];
+  __shared__ uint8_t codes[16][kHeadDim];
+  __shared__ uint32_t szs[16][NG];
+  __shared__ int32_t dst[16];
+
+  if (lane < 16) {
+    const int64_t t = t0 + lane;
+    dst[lane] = (t < p.n) ? p.dst_slots[t] : -1;
+    if (dst[lane] >= 0 && (int64_t)(dst[lane] / kPage) >= p.n_int2_pages) dst[lane] = -1;
+  }
+  __syncthreads();
+  // ---- stage inputs (bf16 values) ----
+  for (int idx = lane; idx < 16 * kHeadDim; idx += 64) {
+    const int t = idx / kHeadDim, j = idx % kHeadDim;
+    float v = 0.f;
+    if (dst[t] >= 0) {
+      if constexpr (MODE == 0) {
+        const uint16_t* src = isv ? p.v_src : p.k_src;
+        v = bf16_to_f32(src[((t0 + t) * p.n_kv + kv) * kHeadDim + j]);
+      } else {
+        const int32_t ss = p.src_slots[t0 + t];
+        const int64_t page = ss / kPage;
+        const int slot = ss % kPage;
+        if (ss >= 0 && page < p.n_bf16_pages) {
+          const uint16_t* blk = (const uint16_t*)(p.bf16_pages + (page * p.n_kv + kv) * (int64_t)kBf16BlockBytes);
+          v = bf16_to_f32(isv ? blk[kPage * kHeadDim + j * kPage + slot] : blk[slot * kHeadDim + j]);
+        }
+      }
+    }
+    xin[t][j] = v;
+  }
+  __syncthreads();
+  // ---- x_rot = X R in fp64 on MFMA ----
+  // f64 16x16x4 operands: A lane l -> A[l%16][l/16]; B lane l -> B[l/16][l%16];
+  // C lane l, element r -> C[4r + l/16][l%16].
+  const float* R = (isv ? p.r_v : p.r_k) + (int64_t)kv * kHeadDim * kHeadDim;
+  const int ln = lane & 15, qd = lane >> 4;
+  f64x4 acc[8];
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) acc[nt] = f64x4{0.0, 0.0, 0.0, 0.0};
+  for (int ks = 0; ks < kHeadDim / 4; ++ks) {
+    const int k = 4 * ks + qd;
+    const double av = (double)xin[ln][k];
+    const float* rrow = R + k * kHeadDim + ln;
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+      const double bv = (double)rrow[16 * nt];
+      acc[nt] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc[nt], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) xr[4 * r + qd][16 * nt + ln] = acc[nt][r];
+  __syncthreads();
+  // ---- clip, group statistics, codes (one lane per (token, group)) ----
+  if (lane < 16 * NG) {
+    const int t = lane / NG, gm = lane % NG;
+    if (dst[t] >= 0) {
+      const double tau = isv ? p.tau_v : p.tau_k;
+      double mn = 0.0, mx = 0.0;
+      bool nan = false;
+      for (int j = gm * G; j < (gm + 1) * G; ++j) {
+        double v = xr[t][j];
+        v = (v < -tau) ? -tau : ((v > tau) ? tau : v);
+        xr[t][j] = v;
+        nan |= (v != v);
+        if (j == gm * G) {
+          mn = v;
+          mx = v;
+        } else {
+          mn = v < mn ? v : mn;
+          mx = v > mx ? v : mx;
+        }
+      }
+      uint16_t sb, zb;
+      if (nan) {
+        sb = zb = 0x7e00u;
+        for (int j = gm * G; j < (gm + 1) * G; ++j) codes[t][j] = 0;
+      } else {
+        sb = f64_to_f16_bits((mx - mn) / 3.0);
+        zb = f64_to_f16_bits(mn);
+        const double sd = f16_bits_to_f64(sb), zd = f16_bits_to_f64(zb);
+        for (int j = gm * G; j < (gm + 1) * G; ++j) {
+          double c = 0.0;
+          if (sd != 0.0) {
+            c = __builtin_rint((xr[t][j] - zd) / sd);
+            c = c < 0.0 ? 0.0 : (c > 3.0 ? 3.0 : c);
+          }
+          codes[t][j] = (uint8_t)c;
+        }
+      }
+      szs[t][gm] = (uint32_t)sb | ((uint32_t)zb << 16);
+    }
+  }
+  __syncthreads();
+  // ---- stores ----
+  uint8_t* pages = p.int2_pages;
+  const int64_t blk_bytes = L.bytes();
+  // scale / zero: (t, gamma) pairs
+  if (lane < 16 * NG) {
+    const int t = lane / NG, gm = lane % NG;
+    if (dst[t] >= 0) {
+      const int64_t page = dst[t] / kPage;
+      const int slot = dst[t] % kPage;
+      uint8_t* blk = pages + (page * p.n_kv + kv) * blk_bytes;
+      *(uint32_t*)(blk + (isv ? L.v_sz() : L.k_sz()) + (gm * kPage + slot) * 4) = szs[t][gm];
+    }
+  }
+  if (!isv) {
+    // K codes: lane -> (token lane/4, bytes 8*(lane%4) .. +7)
+    const int t = lane >> 2, part = lane & 3;
+    if (dst[t] >= 0) {
+      const int64_t page = dst[t] / kPage;
+      const int slot = dst[t] % kPage;
+      uint8_t* blk = pages + (page * p.n_kv + kv) * blk_bytes;
+      uint32_t w[2] = {0u, 0u};
+#pragma unroll
+      for (int j = 0; j < 32; ++j) w[j >> 4] |= (uint32_t)codes[t][32 * part + j] << (2 * (j & 15));
+      *(uint2*)(blk + L.k_codes() + slot * 32 + 8 * part) = make_uint2(w[0], w[1]);
+    }
+  } else {
+    // V codes: lane -> channel pair (2*lane, 2*lane+1); runs of tokens sharing
+    // a (page, half) are merged into one 32-bit word per lane.
+    const int jp = lane;
+    int64_t key = -1;
+    uint32_t mask = 0u, bits = 0u;
+    auto flush = [&](int64_t k, uint32_t msk, uint32_t bts) {
+      if (k < 0 || msk == 0u) return;
+      const int64_t page = k >> 1;
+      const int a = (int)(k & 1);
+      uint8_t* blk = pages + (page * p.n_kv + kv) * blk_bytes;
+      uint32_t* word = (uint32_t*)(blk + L.v_codes() + (a * kHeadDim + 2 * jp) * 2);
+      if (msk == 0xffffffffu) {
+        *word = bts;
+      } else {
+        atomicAnd(word, ~msk);
+        atomicOr(word, bts);
+      }
+    };
+    for (int t = 0; t < 16; ++t) {
+      const int32_t sl = dst[t];
+      if (sl < 0) continue;
+      const int64_t k = (int64_t)(sl / kPage) * 2 + ((sl % kPage) >> 3);
+      if (k != key) {
+        flush(key, mask, bits);
+        key = k;
+        mask = 0u;
+        bits = 0u;
+      }
+      const int i = sl & 7;
+      mask |= (3u << (2 * i)) | (3u << (16 + 2 * i));
+      bits |= ((uint32_t)codes[t][2 * jp] << (2 * i)) | ((uint32_t)codes[t][2 * jp + 1] << (16 + 2 * i));
+    }
+    flush(key, mask, bits);
+  }
+}
+
+// bf16 append: K row-major, V channel-major inside the bf16 block.
+__global__ __launch_bounds__(64) void bf16_write_kernel(const uint16_t* k, const uint16_t* v, const int32_t* slots,
+                                                        int n_kv, uint8_t* pages, int64_t n_pages) {
+  const int64_t i = blockIdx.x;
+  const int kv = blockIdx.y;
+  const int lane = threadIdx.x;
+  const int32_t sl = slots[i];
+  if (sl < 0) return;
+  const int64_t page = sl / kPage;
+  const int slot = sl % kPage;
+  if (page >= n_pages) return;
+  uint16_t* blk = (uint16_t*)(pages + (page * n_kv + kv) * (int64_t)kBf16BlockBytes);
+  const uint32_t kk = *(const uint32_t*)(k + (i * n_kv + kv) * kHeadDim + 2 * lane);
+  const uint32_t vv = *(const uint32_t*)(v + (i * n_kv + kv) * kHeadDim + 2 * lane);
+  *(uint32_t*)(blk + slot * kHeadDim + 2 * lane) = kk;
+  blk[kPage * kHeadDim + (2 * lane) * kPage + slot] = (uint16_t)(vv & 0xffffu);
+  blk[kPage * kHeadDim + (2 * lane + 1) * kPage + slot] = (uint16_t)(vv >> 16);
+}
+
+__global__ __launch_bounds__(256) void copy_pages_kernel(uint8_t* base, int64_t page_bytes, int64_t n_pages,
+                                                         const int32_t* src, const int32_t* dst) {
+  const int64_t i = blockIdx.x;
+  const int32_t s = src[i], d = dst[i];
+  if (s < 0 || d < 0 || s >= n_pages || d >= n_pages || s == d) return;
+  const uint4* from = (const uint4*)(base + s * page_bytes);
+  uint4* to = (uint4*)(base + d * page_bytes);
+  for (int64_t w = threadIdx.x; w < page_bytes / 16; w += 256) to[w] = from[w];
+}
+
+template <int MODE>
+hipError_t launch_qw(const QuantParams& p, hipStream_t stream) {
+  const dim3 grid((unsigned)((p.n + 15) / 16), (unsigned)p.n_kv, 2);
+  if (p.group == 32)
+    hipLaunchKernelGGL((quant_write_kernel<MODE, 4>), grid, dim3(64), 0, stream, p);
+  else
+    hipLaunchKernelGGL((quant_write_kernel<MODE, 2>), grid, dim3(64), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quant_write(const QuantParams& p, int mode, hipStream_t stream) {
+  if (p.n == 0) return hipSuccess;
+  return mode == 0 ? launch_qw<0>(p, stream) : launch_qw<1>(p, stream);
+}
+
+hipError_t launch_bf16_write(const uint16_t* k, const uint16_t* v, const int32_t* slots, int64_t n, int n_kv,
+                             uint8_t* bf16_pages, int64_t n_pages, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(bf16_write_kernel, dim3((unsigned)n, (unsigned)n_kv), dim3(64), 0, stream, k, v, slots, n_kv,
+                     bf16_pages, n_pages);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_pages(uint8_t* base, int64_t block_bytes_all_heads, int64_t n_pages, const int32_t* src,
+                             const int32_t* dst, int64_t n, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(copy_pages_kernel, dim3((unsigned)n), dim3(256), 0, stream, base, block_bytes_all_heads,
+                     n_pages, src, dst);
+  return hipGetLastError();
+}
+
+}  // namespace oscar

@@ -1,0 +1,298 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+  * stored pages: INT2 codes, fp16 scale/zero and bf16 blocks bit-exact;
+  * decode attention: max-abs <= 2e-3 and relative-L2 <= 1e-3 against exact
+    fp64 attention over the identical stored cache;
+  * the all-bf16 baseline decode against exact fp64 attention.
+Inputs are the seeded synthetic workloads; the calibration (R, tau) fed to
+both sides is the oracle's.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_int2_amd as K
+import oracle as O
+import synth
+from gpu_cache import BaselineCache, DeviceCache
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS, REL_L2 = 2e-3, 1e-3
+
+
+def _flush(msg):
+    print(msg, flush=True)
+
+
+def _check_close(out, ref, label):
+    out = np.asarray(out, np.float64)
+    err = np.abs(out - ref).max()
+    rel = np.linalg.norm(out - ref) / max(np.linalg.norm(ref), 1e-30)
+    _flush(f"{label}: max_abs={err:.3e} rel_l2={rel:.3e}")
+    assert np.all(np.isfinite(out)), label
+    assert err <= MAX_ABS and rel <= REL_L2, (label, err, rel)
+
+
+def _calibrate(w, hkv=None):
+    q, k, v = synth.calib_layer(w)
+    if hkv is not None:
+        q, k, v = q[:, :hkv * w.gqa], k[:, :hkv], v[:, :hkv]
+    return O.calibrate_layer(q, k, v)
+
+
+def _expected_int2_block(st, lp, h, group):
+    t = st.region.shape[0]
+    kc = np.zeros((16, 128), np.uint8)
+    vc = np.zeros_like(kc)
+    ng = 128 // group
+    ks, kz, vs, vz = (np.zeros((16, ng), np.float16) for _ in range(4))
+    for s in range(16):
+        p = lp * 16 + s
+        if p < t and st.region[p] == O.REGION_INT2:
+            kc[s], ks[s], kz[s] = st.k_codes[p, h], st.k_s[p, h], st.k_z[p, h]
+            vc[s], vs[s], vz[s] = st.v_codes[p, h], st.v_s[p, h], st.v_z[p, h]
+    return O.pack_int2_block(kc, ks, kz, vc, vs, vz)
+
+
+def _expected_bf16_block(st, lp, h, sink, recent):
+    t = st.region.shape[0]
+    sp = -(-sink // 16)
+    kb = np.zeros((16, 128), np.uint16)
+    vb = np.zeros_like(kb)
+    for s in range(16):
+        pos = None
+        if lp < sp:
+            if lp * 16 + s < min(sink, t):
+                pos = lp * 16 + s
+        else:
+            r = (lp - sp) * 16 + s
+            live = [p for p in range(max(sink, t - recent), t) if (p - sink) % recent == r]
+            pos = live[0] if live else None
+        if pos is not None:
+            kb[s], vb[s] = st.k_bf16[pos, h], st.v_bf16[pos, h]
+    return O.pack_bf16_block(kb, vb)
+
+
+def _check_pages(dc, seq, st, w, label, heads=None):
+    i2, bf, ctx = dc.tables([seq])
+    heads = range(w.n_kv_heads) if heads is None else heads
+    t = int(ctx[0])
+    n_int2_pages = 0
+    mism = 0
+    for lp in range(i2.shape[1]):
+        if i2[0, lp] < 0:
+            continue
+        n_int2_pages += 1
+        for h in heads:
+            got = dc.int2_block_bytes_of(int(i2[0, lp]), h)
+            exp = _expected_int2_block(st, lp, h, w.group)
+            if not np.array_equal(got, exp):
+                mism += 1
+                if mism < 4:
+                    bad = np.nonzero(got != exp)[0]
+                    _flush(f"{label}: INT2 page {lp} head {h}: {bad.size} bytes differ, first at {bad[:8]}")
+    for lp in range(bf.shape[1]):
+        if bf[0, lp] < 0:
+            continue
+        for h in heads:
+            got = dc.bf16_block_bytes_of(int(bf[0, lp]), h)
+            exp = _expected_bf16_block(st, lp, h, w.sink, w.recent)
+            if not np.array_equal(got, exp):
+                mism += 1
+                _flush(f"{label}: bf16 page {lp} head {h} differs")
+    _flush(f"{label}: T={t} int2 pages={n_int2_pages} mismatching blocks={mism}")
+    assert mism == 0
+
+
+def _fill(dc, seq, kb, vb, plan):
+    """plan: list of chunk sizes summing to len(kb)."""
+    t = 0
+    for n in plan:
+        dc.append(seq, kb[t:t + n], vb[t:t + n])
+        t += n
+    assert t == kb.shape[0]
+
+
+# ---------------------------------------------------------------------------
+
+def test_tiny_write_pages_and_decode():
+    w = synth.WORKLOADS["tiny"]
+    _flush("case tiny: T=4096 Hq=Hkv=1 G=32")
+    cal = _calibrate(w)
+    sh = K.make_shape(n_q_heads=1, n_kv_heads=1, group=32, sink=w.sink, recent=w.recent)
+    dc = DeviceCache(sh, cal.r_k, cal.r_v, cal.tau_k, cal.tau_v, 300, 16)
+    kb, vb = synth.kv_request_bf16(w, 0, 0, w.context)
+    seq = dc.new_seq()
+    # prefill in uneven chunks, then single-token decode steps (ring age-out path)
+    _fill(dc, seq, kb, vb, [1000, 1, 2000, 77, 999] + [1] * 19)
+    st = O.store_request(kb, vb, cal, w.group, w.sink, w.recent)
+    _check_pages(dc, seq, st, w, "tiny")
+    q = synth.q_decode_bf16(w, 0)[None]
+    out = dc.decode([seq], q).cpu().numpy()
+    ref = O.decode_attention(q[0], st, cal, w.group)[None]
+    _check_close(out, ref, "tiny decode")
+    for si in (1, 3, 7, 64):
+        out = dc.decode([seq], q, splits_int2=si).cpu().numpy()
+        _check_close(out, ref, f"tiny decode splits={si}")
+
+
+def test_qwen3_8b_layer_32k():
+    w = synth.WORKLOADS["qwen3_8b_32k"]
+    _flush("case qwen3_8b_32k: T=32768 Hq=32 Hkv=8 G=32")
+    cal = _calibrate(w)
+    sh = K.make_shape(n_q_heads=32, n_kv_heads=8, group=32, sink=w.sink, recent=w.recent)
+    dc = DeviceCache(sh, cal.r_k, cal.r_v, cal.tau_k, cal.tau_v, 2100, 16)
+    kb, vb = synth.kv_request_bf16(w, 0, 0, w.context)
+    seq = dc.new_seq()
+    _fill(dc, seq, kb, vb, [8192, 8192, 8192, 8190, 1, 1])
+    st = O.store_request(kb, vb, cal, w.group, w.sink, w.recent)
+    _check_pages(dc, seq, st, w, "qwen3_8b_32k")
+    q = synth.q_decode_bf16(w, 0)[None]
+    ref = O.decode_attention(q[0], st, cal, w.group)[None]
+    for si in (0, 5, 16):
+        out = dc.decode([seq], q, splits_int2=si).cpu().numpy()
+        _check_close(out, ref, f"qwen3_8b_32k decode splits={si}")
+
+
+@pytest.mark.parametrize("hq,hkv,group", [(4, 1, 32), (8, 1, 32), (12, 1, 32), (12, 1, 64), (4, 2, 64), (16, 1, 64)])
+def test_ragged_batch_gqa_groups(hq, hkv, group):
+    """Mixed lengths (all-bf16, exactly sink+recent, one INT2 token, odd page
+    counts) in one batch, for several GQA widths and both group sizes."""
+    w = synth.Workload("ragged", 10 + hq + group, hq, hkv, 128, 1, 0, group=group, sink=4, recent=32,
+                       outlier_scale=(40.0, 40.0), calib_tokens=512)
+    _flush(f"case ragged hq={hq} hkv={hkv} G={group}")
+    cal = _calibrate(w)
+    sh = K.make_shape(n_q_heads=hq, n_kv_heads=hkv, group=group, sink=4, recent=32)
+    dc = DeviceCache(sh, cal.r_k, cal.r_v, cal.tau_k, cal.tau_v, 600, 64)
+    lens = [1, 5, 36, 37, 53, 100, 515, 1000, 2049, 3001]
+    seqs, stores, qs = [], [], []
+    for r, t in enumerate(lens):
+        kb, vb = synth.kv_request_bf16(w, r, 0, t)
+        seq = dc.new_seq()
+        _fill(dc, seq, kb, vb, [t] if t < 200 else [t - 7] + [1] * 7)
+        seqs.append(seq)
+        stores.append(O.store_request(kb, vb, cal, group, 4, 32))
+        qs.append(synth.q_decode_bf16(w, r))
+    for r in (0, 6, 9):
+        _check_pages(dc, seqs[r], stores[r], w, f"ragged len={lens[r]}")
+    q = np.stack(qs)
+    ref = np.stack([O.decode_attention(q[r], stores[r], cal, group) for r in range(len(lens))])
+    for si in (0, 1, 4):
+        out = dc.decode(seqs, q, splits_int2=si).cpu().numpy()
+        for r in range(len(lens)):
+            _check_close(out[r], ref[r], f"ragged hq={hq} G={group} len={lens[r]} splits={si}")
+
+
+def test_empty_context_gives_zero_rows():
+    w = synth.WORKLOADS["tiny"]
+    cal = _calibrate(w)
+    sh = K.make_shape(n_q_heads=1, n_kv_heads=1, group=32)
+    dc = DeviceCache(sh, cal.r_k, cal.r_v, cal.tau_k, cal.tau_v, 8, 16)
+    empty = dc.new_seq()
+    full = dc.new_seq()
+    kb, vb = synth.kv_request_bf16(w, 0, 0, 200)
+    dc.append(full, kb, vb)
+    q = np.stack([synth.q_decode_bf16(w, 0), synth.q_decode_bf16(w, 1)])
+    out = dc.decode([empty, full], q).cpu().numpy()
+    assert np.all(out[0] == 0)
+    st = O.store_request(kb, vb, cal, 32, w.sink, w.recent)
+    _check_close(out[1], O.decode_attention(q[1], st, cal, 32), "after empty row")
+
+
+def test_quant_write_scattered_slots_and_nan_group():
+    """Tokens written in shuffled order into scattered slots (V words merged by
+    atomics across wavefronts) and a NaN input row."""
+    w = synth.WORKLOADS["qwen3_8b_32k"]
+    cal = _calibrate(w)
+    sh = K.make_shape(n_q_heads=32, n_kv_heads=8, group=32, sink=0, recent=0)
+    dc = DeviceCache(sh, cal.r_k, cal.r_v, cal.tau_k, cal.tau_v, 64, 1)
+    n = 37 * 16
+    kb, vb = synth.kv_request_bf16(w, 3, 0, n)
+    kb[100, 2, 5] = 0x7FC0                       # bf16 NaN in K of token 100, head 2
+    rng = np.random.default_rng(0)
+    slots = rng.permutation(64 * 16)[:n].astype(np.int32)
+    order = rng.permutation(n)
+    from gpu_cache import to_dev_bits, to_dev_i32
+    K.oscar_quant_write(sh, dc.layer, dc.cache, to_dev_bits(kb[order]), to_dev_bits(vb[order]),
+                        to_dev_i32(slots[order]))
+    torch.cuda.synchronize()
+    pool = dc.int2.cpu().numpy().reshape(64, 8, -1)
+    for h in (0, 2, 7):
+        xk = O.bf16_to_f64(kb[:, h])
+        xv = O.bf16_to_f64(vb[:, h])
+        ck, sk, zk, _ = O.quantize(xk, cal.r_k[h], cal.tau_k, 32)
+        cv, sv, zv, _ = O.quantize(xv, cal.r_v[h], cal.tau_v, 32)
+        for i in range(n):
+            page, s = divmod(int(slots[i]), 16)
+            blk = O.unpack_int2_block(pool[page, h], 128, 32)
+            assert np.array_equal(blk[0][s], ck[i]), (h, i)
+            assert np.array_equal(blk[3][s], cv[i]), (h, i)
+            if h == 2 and i == 100:
+                assert np.all(np.isnan(blk[1][s])) and np.all(np.isnan(blk[2][s]))
+                continue
+            assert np.array_equal(blk[1][s].view(np.uint16), sk[i].view(np.uint16))
+            assert np.array_equal(blk[2][s].view(np.uint16), zk[i].view(np.uint16))
+            assert np.array_equal(blk[4][s].view(np.uint16), sv[i].view(np.uint16))
+            assert np.array_equal(blk[5][s].view(np.uint16), zv[i].view(np.uint16))
+
+
+def test_shared_prefix_fork():
+    """Prefix caching: children forked from one parent share its complete pages
+    (same physical ids) and decode like independent requests."""
+    w = synth.Workload("prefix", 42, 8, 1, 128, 1, 0, sink=4, recent=32, shared_prefix=4096, calib_tokens=512)
+    _flush("case shared prefix fork")
+    cal = _calibrate(w)
+    sh = K.make_shape(n_q_heads=8, n_kv_heads=1, group=32, sink=4, recent=32)
+    dc = DeviceCache(sh, cal.r_k, cal.r_v, cal.tau_k, cal.tau_v, 2000, 64)
+    parent = dc.new_seq()
+    pk, pv = synth.kv_request_bf16(w, 0, 0, 4096)   # shared prefix (generator's shared id)
+    dc.append(parent, pk, pv)
+    kids, stores, qs = [], [], []
+    for r in range(4):
+        c = dc.fork(parent)
+        own_k, own_v = synth.kv_request_bf16(w, r + 1, 4096, 4096 + 700 + 13 * r)
+        dc.append(c, own_k[:500], own_v[:500])
+        for i in range(500, own_k.shape[0]):
+            dc.append(c, own_k[i:i + 1], own_v[i:i + 1])
+        kb = np.concatenate([pk, own_k])
+        vb = np.concatenate([pv, own_v])
+        kids.append(c)
+        stores.append(O.store_request(kb, vb, cal, 32, 4, 32))
+        qs.append(synth.q_decode_bf16(w, r))
+    tabs = dc.tables(kids)
+    shared = (4096 - 32) // 16                      # complete INT2 pages at fork time
+    for r in range(1, 4):
+        assert np.array_equal(tabs[0][r, :shared], tabs[0][0, :shared])
+        assert tabs[0][r, shared] != tabs[0][0, shared]
+    for r in range(4):
+        _check_pages(dc, kids[r], stores[r], w, f"fork child {r}")
+    q = np.stack(qs)
+    out = dc.decode(kids, q).cpu().numpy()
+    for r in range(4):
+        _check_close(out[r], O.decode_attention(q[r], stores[r], cal, 32), f"fork child {r} decode")
+
+
+@pytest.mark.parametrize("hq,hkv", [(1, 1), (32, 8), (12, 1)])
+def test_bf16_baseline_decode(hq, hkv):
+    w = synth.Workload("base", 50 + hq, hq, hkv, 128, 1, 0, calib_tokens=256)
+    _flush(f"case bf16 baseline hq={hq} hkv={hkv}")
+    sh = K.make_shape(n_q_heads=hq, n_kv_heads=hkv)
+    bc = BaselineCache(sh, 1200, 5000)
+    lens = [1, 17, 300, 4999]
+    seqs, ks, vs = [], [], []
+    for r, t in enumerate(lens):
+        kb, vb = synth.kv_request_bf16(w, r, 0, t)
+        s = bc.new_seq()
+        bc.append(s, kb, vb)
+        seqs.append(s)
+        ks.append(kb)
+        vs.append(vb)
+    q = np.stack([synth.q_decode_bf16(w, r) for r in range(len(lens))])
+    for sp in (0, 1, 5):
+        out = bc.decode(seqs, q, splits=sp).cpu().numpy()
+        for r in range(len(lens)):
+            ref = O.attend(O.bf16_to_f64(q[r]), O.bf16_to_f64(ks[r]), O.bf16_to_f64(vs[r]))
+            _check_close(out[r], ref, f"baseline hq={hq} len={lens[r]} splits={sp}")

@@ -1,0 +1,206 @@
+"""Host-side checks of liboscar.so that need no GPU: the exported C ABI,
+argument validation, offline calibration against the oracle, and the page
+pool / region planner against the oracle's reference model of the region rule."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import kv_cache_int2_amd as K
+import oracle as O
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(K.LIB_PATH):
+        pytest.fail("liboscar.so not built (run __graft_entry__.build())")
+    return K.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    hdr = open(os.path.join(ROOT, "include", "oscar.h")).read()
+    hdr = re.sub(r"/\*.*?\*/", "", hdr, flags=re.S)
+    declared = set(re.findall(r"\b(oscar_[a-z0-9_]+)\s*\(", hdr))
+    assert len(declared) >= 20
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert declared == set(K.EXPORTED), declared ^ set(K.EXPORTED)
+
+
+def test_block_sizes(lib):
+    assert K.oscar_int2_block_bytes(K.make_shape(group=32)) == O.int2_block_bytes(128, 32) == 1536
+    assert K.oscar_int2_block_bytes(K.make_shape(group=64)) == O.int2_block_bytes(128, 64) == 1280
+    assert K.oscar_bf16_block_bytes(K.make_shape()) == O.bf16_block_bytes(128) == 8192
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=64), K.OSCAR_EUNSUPPORTED),
+    (dict(group=16), K.OSCAR_EUNSUPPORTED),
+    (dict(page_size=32), K.OSCAR_EUNSUPPORTED),
+    (dict(n_q_heads=3, n_kv_heads=2), K.OSCAR_EINVAL),
+    (dict(n_q_heads=64, n_kv_heads=2), K.OSCAR_EUNSUPPORTED),
+    (dict(recent=100), K.OSCAR_EUNSUPPORTED),
+    (dict(sink=-1), K.OSCAR_EINVAL),
+])
+def test_shape_validation(lib, kw, code):
+    sh = K.make_shape(**kw)
+    h = C.c_void_p()
+    assert lib.oscar_pool_create(C.byref(sh), 4, 4, C.byref(h)) == code
+    assert lib.oscar_last_error()
+
+
+def test_launch_argument_errors_before_any_gpu_call(lib):
+    sh = K.make_shape()
+    cache = K.make_cache()
+    lay = K.Layer(None, None, 1.0, 1.0)
+    # n == 0 is a no-op even without storage
+    assert lib.oscar_quant_write(C.byref(sh), C.byref(lay), C.byref(cache), None, None, None, 0, None) == K.OSCAR_OK
+    assert lib.oscar_quant_write(C.byref(sh), C.byref(lay), C.byref(cache), None, None, None, 5, None) == K.OSCAR_EINVAL
+    assert lib.oscar_quant_write(C.byref(sh), C.byref(lay), C.byref(cache), None, None, None, -1, None) == K.OSCAR_EINVAL
+    assert lib.oscar_bf16_write(C.byref(sh), C.byref(cache), None, None, None, 3, None) == K.OSCAR_EINVAL
+    assert lib.oscar_copy_pages(C.byref(sh), C.byref(cache), 2, None, None, 1, None) == K.OSCAR_EINVAL
+    assert lib.oscar_decode_attn(C.byref(sh), C.byref(lay), C.byref(cache), None, 1, None, 1, None, 1, None, 0, 0,
+                                 None, None, 0, None) == K.OSCAR_EINVAL
+    assert lib.oscar_decode_attn(C.byref(sh), C.byref(lay), C.byref(cache), None, 0, None, 1, None, 1, None, 0, 0,
+                                 None, None, 0, None) == K.OSCAR_OK
+    # misaligned storage is refused
+    bad = K.Cache(0x1010, 4, 0x2000, 4)
+    good_layer = K.Layer(0x1000, 0x2000, 1.0, 1.0)
+    assert lib.oscar_quant_write(C.byref(sh), C.byref(good_layer), C.byref(bad), 0x10, 0x10, 0x10, 1,
+                                 None) == K.OSCAR_EINVAL
+    nan_layer = K.Layer(0x1000, 0x2000, float("nan"), 1.0)
+    ok_cache = K.Cache(0x1000, 4, 0x2000, 4)
+    assert lib.oscar_quant_write(C.byref(sh), C.byref(nan_layer), C.byref(ok_cache), 0x10, 0x10, 0x10, 1,
+                                 None) == K.OSCAR_EINVAL
+
+
+def test_workspace_bytes_monotone(lib):
+    sh = K.make_shape(n_q_heads=32, n_kv_heads=8)
+    a = K.oscar_decode_workspace_bytes(sh, 28, 8, 1)
+    b = K.oscar_decode_workspace_bytes(sh, 28, 16, 1)
+    assert 0 < a < b and a % 256 == 0
+    assert K.oscar_decode_workspace_bytes(sh, 28, 0, 0) >= b
+    s = K.oscar_decode_auto_splits(sh, 28, 6300)
+    assert 1 <= s <= 64
+
+
+# ---------------------------------------------------------------------------
+# calibration vs oracle
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["tiny", "qwen3_8b_32k"])
+def test_calibration_matches_oracle(lib, name):
+    w = synth.WORKLOADS[name]
+    q, k, v = synth.calib_layer(w, n=1024 if name != "tiny" else None)
+    sh = K.make_shape(n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads, group=w.group)
+    rk, rv, ek, ev, tk, tv = K.oscar_calibrate_host(sh, q, k, v)
+    cal = O.calibrate_layer(q, k, v)
+    assert np.abs(ek / cal.eig_k - 1).max() < 1e-10
+    assert np.abs(ev / cal.eig_v - 1).max() < 1e-10
+    # same sign convention -> same rotation up to fp32 rounding of a 1e-13 difference
+    assert np.abs(rk - cal.r_k).max() < 1e-7 and np.abs(rv - cal.r_v).max() < 1e-7
+    assert np.count_nonzero(rk != cal.r_k) < 1e-3 * rk.size
+    assert abs(tk / cal.tau_k - 1) < 1e-6 and abs(tv / cal.tau_v - 1) < 1e-6
+
+
+def test_calibration_errors(lib):
+    sh = K.make_shape()
+    z = np.zeros((4, 1, 128), np.float32)
+    with pytest.raises(K.OscarError):
+        K.oscar_calibrate_host(sh, z, z, z, clip_pct_k=0.0)
+    with pytest.raises(K.OscarError):
+        K.oscar_calibrate_host(sh, z, z, z, clip_pct_v=1.5)
+
+
+# ---------------------------------------------------------------------------
+# pools, sequences, planner
+# ---------------------------------------------------------------------------
+
+def _phys_to_logical(seq_tables, slot, kind):
+    """Map a physical slot back to (logical page, slot) through a block table row."""
+    page, s = divmod(int(slot), 16)
+    row = seq_tables[kind]
+    lp = list(row).index(page)
+    return lp * 16 + s
+
+
+@pytest.mark.parametrize("s0,w", [(4, 128), (64, 256), (0, 16), (5, 32), (4, 0)])
+def test_planner_matches_region_model(lib, s0, w):
+    sh = K.make_shape(sink=s0, recent=w)
+    pool = K.Pool(sh, 400, 40)
+    seq = K.oscar_seq_create(pool)
+    rng = np.random.default_rng(s0 * 7 + w)
+    t = 0
+    while t < 1500:
+        n = int(min(1500 - t, rng.choice([1, 1, 3, 16, 40, 200])))
+        i2, bf, a_s, a_d = K.oscar_seq_plan_append(pool, seq, n)
+        r_i2, r_bf, r_age = O.plan_append(t, n, s0, w)
+        tables = K.oscar_block_tables(pool, [seq], 200, 40)
+        rows = (tables[0][0], tables[1][0])
+        assert tables[2][0] == t + n == K.oscar_seq_length(seq)
+        for j in range(n):
+            if r_i2[j] >= 0:
+                assert i2[j] >= 0 and bf[j] == -1
+                assert _phys_to_logical(rows, i2[j], 0) == r_i2[j]
+            else:
+                assert i2[j] == -1 and bf[j] >= 0
+                assert _phys_to_logical(rows, bf[j], 1) == r_bf[j]
+        assert len(a_s) == len(r_age)
+        for (src, dst), (rs, rd) in zip(zip(a_s, a_d), r_age):
+            assert _phys_to_logical(rows, src, 1) == rs
+            assert _phys_to_logical(rows, dst, 0) == rd
+        t += n
+    # pages were allocated once each and return on release
+    used = 400 - pool.free_pages()[0]
+    last_int2 = 1500 - w - 1                             # INT2 positions are [s0, T - w)
+    assert used == (last_int2 // 16 - s0 // 16 + 1 if last_int2 >= s0 else 0)
+    K.oscar_seq_release(pool, seq)
+    assert pool.free_pages() == (400, 40)
+
+
+def test_pool_exhaustion_leaves_state_unchanged(lib):
+    sh = K.make_shape(sink=4, recent=16)
+    pool = K.Pool(sh, 3, 2)
+    seq = K.oscar_seq_create(pool)
+    K.oscar_seq_plan_append(pool, seq, 40)
+    before = pool.free_pages()
+    with pytest.raises(K.OscarError) as e:
+        K.oscar_seq_plan_append(pool, seq, 200)
+    assert e.value.code == K.OSCAR_ENOMEM
+    assert pool.free_pages() == before and K.oscar_seq_length(seq) == 40
+    tables = K.oscar_block_tables(pool, [seq], 8, 8)
+    with pytest.raises(K.OscarError):
+        K.oscar_block_tables(pool, [seq], 1, 8)         # row too narrow
+    assert tables[2][0] == 40
+
+
+def test_fork_shares_complete_pages_and_copies_open_ones(lib):
+    s0, w = 4, 32
+    sh = K.make_shape(sink=s0, recent=w)
+    pool = K.Pool(sh, 100, 20)
+    parent = K.oscar_seq_create(pool)
+    K.oscar_seq_plan_append(pool, parent, 100)          # INT2 positions 4..67, ring holds 68..99
+    child, src, dst, kind = K.oscar_seq_fork(pool, parent)
+    assert K.oscar_seq_length(child) == 100
+    pt = K.oscar_block_tables(pool, [parent, child], 16, 8)
+    p_i2, c_i2 = pt[0][0], pt[0][1]
+    # INT2 pages 0..3 (positions 0..63) are complete -> shared; page 4 (64..79) is open -> copied
+    assert list(p_i2[:4]) == list(c_i2[:4])
+    assert p_i2[4] != c_i2[4] and p_i2[4] >= 0
+    p_bf, c_bf = pt[1][0], pt[1][1]
+    assert p_bf[0] == c_bf[0]                            # full sink page shared
+    assert p_bf[1] != c_bf[1] and p_bf[2] != c_bf[2]     # ring pages copied
+    assert sorted(zip(kind, src, dst)) == sorted(
+        [(0, p_i2[4], c_i2[4]), (1, p_bf[1], c_bf[1]), (1, p_bf[2], c_bf[2])])
+    # both sequences grow independently; releasing one keeps shared pages alive
+    K.oscar_seq_plan_append(pool, child, 50)
+    K.oscar_seq_release(pool, parent)
+    t = K.oscar_block_tables(pool, [child], 16, 8)
+    assert list(t[0][0][:4]) == list(c_i2[:4])
+    K.oscar_seq_release(pool, child)
+    assert pool.free_pages() == (100, 20)
