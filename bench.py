@@ -1,0 +1,327 @@
+"""Benchmark of the OSCAR INT2 KV-cache hot path on one MI355X.
+
+One step = one decode step for the whole batch: host region planning
+(oscar_plan_decode_step), re-quantisation of the tokens leaving the recent
+window, bf16 append of every request's new token, and mixed-precision paged
+decode attention (prologue, main kernel, split-K combine).  The cache is
+resident in HBM before the timed region; inputs of every step are generated
+and uploaded beforehand.
+
+Prints one JSON line.  value = KV tokens attended per second (summed context
+lengths of all requests and steps / wall time of the timed steps).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak
+FP64_PEAK_TFLOPS = 78.6        # MI355X fp64 (vector and matrix)
+PROFILE_PMC = os.path.join(ROOT, "profiles", "decode_main_long_28x100k_pmc.json")
+KERNEL_SRC = os.path.join(ROOT, "kv_cache_int2_amd", "csrc", "decode_attn.hip")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long_28x100k")
+    ap.add_argument("--group", type=int, default=0, help="override the workload's INT2 group size")
+    ap.add_argument("--splits", type=int, default=0, help="INT2 splits per (request, KV head); 0 = auto")
+    ap.add_argument("--no-baseline", action="store_true", help="skip the bf16 same-kernel baseline")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    return ap.parse_args()
+
+
+def algorithmic_bytes(ctx, hkv, hq, group, sink, recent):
+    """Bytes the method must move for one decode of the batch: INT2 codes +
+    fp16 scale/zero of history tokens, bf16 K/V of sink/recent tokens, the
+    bf16 query and the fp32 output."""
+    per_int2 = 2 * (128 // 4 + (128 // group) * 4)          # K and V, per token and KV head
+    per_bf16 = 2 * 128 * 2
+    tot = 0
+    for t in ctx:
+        n_bf = min(t, sink + recent)
+        tot += ((t - n_bf) * per_int2 + n_bf * per_bf16) * hkv
+    return tot + len(ctx) * hq * 128 * (2 + 4)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import kv_cache_int2_amd as K
+    import synth
+    from kv_cache_int2_amd.torch_cache import BaselineCache, DeviceCache, to_dev_bits, to_dev_i32
+
+    assert torch.cuda.is_available(), "bench needs a GPU"
+    torch.cuda.set_device(0)
+    w = synth.WORKLOADS[args.workload]
+    group = args.group or w.group
+    B, hq, hkv = w.batch, w.n_q_heads, w.n_kv_heads
+    n_steps = args.warmup + args.steps
+    T_final = w.context
+    T0 = T_final - n_steps                      # the last timed step attends T_final tokens
+    sh = K.make_shape(n_q_heads=hq, n_kv_heads=hkv, group=group, sink=w.sink, recent=w.recent)
+    log(f"workload {w.name}: B={B} T={T_final} Hq={hq} Hkv={hkv} G={group} sink={w.sink} recent={w.recent}")
+
+    # ---- calibration (offline, host C++) ----
+    t = time.time()
+    qc, kc, vc = synth.calib_layer(w)
+    r_k, r_v, _, _, tau_k, tau_v = K.oscar_calibrate_host(sh, qc, kc, vc)
+    log(f"calibration {time.time() - t:.1f}s tau_k={tau_k:.3f} tau_v={tau_v:.3f}")
+
+    pages_per_req = (T_final + 15) // 16 + 2
+    dc = DeviceCache(sh, r_k, r_v, tau_k, tau_v, B * pages_per_req + 8, B * (w.sink // 16 + 2 + w.recent // 16) + 8)
+    bc = None
+    if not args.no_baseline:
+        bc = BaselineCache(sh, B * pages_per_req + 8, T_final + 16)
+
+    # ---- fill the cache (prefill through the write path, timed per quant_write launch) ----
+    seqs, bseqs = [], []
+    qw_ms, qw_tokens = [], 0
+    chunk = 16384
+    t = time.time()
+    parent = None
+    if w.shared_prefix:
+        kb, vb = synth.kv_request_bf16(w, 0, 0, w.shared_prefix)
+        parent = dc.new_seq()
+        dc.append(parent, kb, vb)
+        pbk, pbv = kb, vb
+    for r in range(B):
+        start = 0
+        if parent is not None:
+            s = dc.fork(parent)
+            start = w.shared_prefix
+        else:
+            s = dc.new_seq()
+        kb_all, vb_all = synth.kv_request_bf16(w, r, start, T0)
+        if bc is not None:
+            bs = bc.new_seq()
+            if parent is not None:
+                bc.append(bs, pbk, pbv)
+        for c0 in range(0, T0 - start, chunk):
+            kb, vb = kb_all[c0:c0 + chunk], vb_all[c0:c0 + chunk]
+            i2, bf, a_s, a_d = K.oscar_seq_plan_append(dc.pool, s, kb.shape[0])
+            kd, vd = to_dev_bits(kb), to_dev_bits(vb)
+            if len(a_s):
+                K.oscar_requant_from_bf16(sh, dc.layer, dc.cache, to_dev_i32(a_s), to_dev_i32(a_d))
+            if np.any(i2 >= 0):
+                i2d = to_dev_i32(i2)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                K.oscar_quant_write(sh, dc.layer, dc.cache, kd, vd, i2d)
+                e1.record()
+                qw_ms.append((e0, e1))
+                qw_tokens += int(np.count_nonzero(i2 >= 0))
+            if np.any(bf >= 0):
+                K.oscar_bf16_write(sh, dc.cache, kd, vd, to_dev_i32(bf))
+            if bc is not None:
+                bc.append(bs, kb, vb)
+        seqs.append(s)
+        if bc is not None:
+            bseqs.append(bs)
+        del kb_all, vb_all
+        if r % 7 == 0:
+            log(f"filled request {r + 1}/{B} ({time.time() - t:.1f}s)")
+    torch.cuda.synchronize()
+    qw_time = sum(a.elapsed_time(b) for a, b in qw_ms) / 1e3
+    log(f"cache filled in {time.time() - t:.1f}s; quant_write {qw_tokens} tokens in {qw_time * 1e3:.1f} ms")
+
+    # ---- step inputs, resident before timing ----
+    new_k = np.empty((n_steps, B, hkv, 128), np.uint16)
+    new_v = np.empty_like(new_k)
+    qs = np.empty((n_steps, B, hq, 128), np.uint16)
+    for r in range(B):
+        kb, vb = synth.kv_request_bf16(w, r, T0, T_final, threads=1)
+        new_k[:, r], new_v[:, r] = kb, vb
+        for st in range(n_steps):
+            qs[st, r] = synth.q_decode_bf16(w, r, st + 1)
+    new_k_d, new_v_d, q_d = to_dev_bits(new_k), to_dev_bits(new_v), to_dev_bits(qs)
+    planner = K.DecodeStepPlanner(dc.pool, seqs)
+    host_small = torch.zeros((n_steps, 5, B), dtype=torch.int32).pin_memory()
+    dev_small = torch.zeros((n_steps, 5, B), dtype=torch.int32, device="cuda")
+    max_i2 = (T_final + 15) // 16
+    max_bf = w.sink // 16 + 1 + w.recent // 16
+    si = args.splits or K.oscar_decode_auto_splits(sh, B, max_i2)
+    ws = torch.empty(K.oscar_decode_workspace_bytes(sh, B, si, 1), dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, hq, 128), dtype=torch.float32, device="cuda")
+    i2_bt, bf_bt, ctx = dc.tables(seqs, max_i2, max_bf)
+    tables = [to_dev_i32(i2_bt), to_dev_i32(bf_bt)]
+    ctx_hist = []
+
+    def step(st):
+        n_age, changed = planner.step()
+        host_small[st].copy_(torch.from_numpy(planner.buf))
+        dev_small[st].copy_(host_small[st], non_blocking=True)
+        if changed:
+            i2_bt, bf_bt, _ = dc.tables(seqs, max_i2, max_bf)
+            tables[0] = to_dev_i32(i2_bt)
+            tables[1] = to_dev_i32(bf_bt)
+        d = dev_small[st]
+        if n_age:
+            K.oscar_requant_from_bf16(sh, dc.layer, dc.cache, d[2], d[3], n=n_age)
+        K.oscar_bf16_write(sh, dc.cache, new_k_d[st], new_v_d[st], d[1], n=B)
+        if np.any(planner.buf[0] >= 0):
+            K.oscar_quant_write(sh, dc.layer, dc.cache, new_k_d[st], new_v_d[st], d[0], n=B)
+        K.oscar_decode_attn(sh, dc.layer, dc.cache, q_d[st], tables[0], tables[1], d[4], out, ws, si, 1)
+        ctx_hist.append(planner.buf[4].astype(np.int64).copy())
+
+    for st in range(args.warmup):
+        step(st)
+    torch.cuda.synchronize()
+    ctx_hist.clear()
+    K.oscar_profile_enable(True)
+    t0 = time.perf_counter()
+    for st in range(args.warmup, n_steps):
+        step(st)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    K.oscar_profile_enable(False)
+    main_ms, launches = K.oscar_profile_read()
+    elapsed = t1 - t0
+    tokens = int(sum(c.sum() for c in ctx_hist))
+    value = tokens / elapsed
+    main_avg_ms = main_ms / max(launches, 1)
+    alg = np.mean([algorithmic_bytes(c, hkv, hq, group, w.sink, w.recent) for c in ctx_hist])
+    achieved = alg / (main_avg_ms * 1e-3) / 1e9
+    log(f"timed {args.steps} steps in {elapsed * 1e3:.2f} ms: {value / 1e9:.3f} G KV tok/s; "
+        f"decode_main avg {main_avg_ms * 1e3:.1f} us -> {achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS:.1%} of peak)")
+
+    # ---- parity sample on the timed cache: cheap invariant (finite output) ----
+    assert torch.isfinite(out).all(), "non-finite decode output"
+
+    # ---- HBM traffic from committed rocprofv3 counters (if they match this kernel source) ----
+    traffic = None
+    src_hash = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    if os.path.exists(PROFILE_PMC):
+        pm = json.load(open(PROFILE_PMC))
+        if pm.get("kernel_source_sha256") == src_hash and pm.get("workload") == w.name:
+            traffic = pm.get("hbm_bytes_per_launch")
+
+    # ---- bf16 same-kernel baseline ----
+    baseline = None
+    if bc is not None:
+        bq = q_d[n_steps - 1]
+        btab = bc.tables(bseqs)
+        bf_bt_d, bctx = to_dev_i32(btab[0]), to_dev_i32(btab[1])
+        sb = K.oscar_decode_auto_splits(bc.shape, B, btab[0].shape[1])
+        bws = torch.empty(K.oscar_decode_workspace_bytes(bc.shape, B, 1, sb), dtype=torch.uint8, device="cuda")
+        bout = torch.empty_like(out)
+        for _ in range(3):
+            K.oscar_decode_attn_bf16_baseline(bc.shape, bc.cache, bq, bf_bt_d, bctx, bout, bws, sb)
+        torch.cuda.synchronize()
+        K.oscar_profile_enable(True)
+        nb = max(5, args.steps // 2)
+        tb0 = time.perf_counter()
+        for _ in range(nb):
+            K.oscar_decode_attn_bf16_baseline(bc.shape, bc.cache, bq, bf_bt_d, bctx, bout, bws, sb)
+        torch.cuda.synchronize()
+        tb1 = time.perf_counter()
+        K.oscar_profile_enable(False)
+        bms, bl = K.oscar_profile_read()
+        bctx_np = btab[1].astype(np.int64)
+        b_alg = int(bctx_np.sum()) * hkv * 512 + B * hq * 128 * 6
+        b_main = bms / max(bl, 1)
+        baseline = {
+            "kv_tokens_per_s": float(bctx_np.sum() * nb / (tb1 - tb0)),
+            "decode_main_us": round(b_main * 1e3, 2),
+            "achieved_gbs": round(b_alg / (b_main * 1e-3) / 1e9, 1),
+            "frac": round(b_alg / (b_main * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "bytes_per_launch": b_alg,
+            "splits": sb,
+        }
+        # plain copy of a known size (1 GiB read + 1 GiB written), for scaling
+        # rocprofv3 FETCH_SIZE / WRITE_SIZE counters
+        page_bytes = hkv * 8192
+        n_copy = (1 << 30) // page_bytes
+        cbuf = torch.zeros(2 * n_copy * page_bytes, dtype=torch.uint8, device="cuda")
+        ccache = K.make_cache(None, 0, cbuf, 2 * n_copy)
+        src = torch.arange(n_copy, dtype=torch.int32, device="cuda")
+        K.oscar_copy_pages(bc.shape, ccache, 1, src, src + n_copy)
+        torch.cuda.synchronize()
+        del cbuf
+        log(f"copy calibration: {n_copy} pages x {page_bytes} B = {n_copy * page_bytes} B read and written")
+        log(f"bf16 baseline: decode_main {b_main * 1e3:.1f} us, {baseline['achieved_gbs']} GB/s; "
+            f"INT2/bf16 speedup {b_main / main_avg_ms:.2f}x")
+
+    # ---- CPU oracle baseline on a bounded sample ----
+    cpu = None
+    if not args.no_cpu:
+        import oracle as O
+        import threadpoolctl
+        cal = O.calibrate_layer(qc, kc, vc)
+        cores = len(os.sched_getaffinity(0))
+        blas = threadpoolctl.threadpool_info()
+        blas_threads = max([b.get("num_threads", 1) for b in blas] or [1])
+        done_tokens, spent, n_req = 0, 0.0, 0
+        T_s = T_final
+        while spent < args.cpu_seconds and n_req < B:
+            kb, vb = synth.kv_request_bf16(w, n_req, 0, T_s)
+            st_ = O.store_request(kb, vb, cal, group, w.sink, w.recent)
+            qb = synth.q_decode_bf16(w, n_req)
+            c0 = time.perf_counter()
+            O.decode_attention(qb, st_, cal, group)
+            spent += time.perf_counter() - c0
+            done_tokens += T_s
+            n_req += 1
+        cpu = {"value": done_tokens / spent, "unit": "KV tokens/s", "cores": min(cores, blas_threads),
+               "kind": "oracle",
+               "sample": f"{n_req} of {B} requests x {T_s} tokens, all {hq} query heads: fp64 numpy decode "
+                         f"attention over the stored INT2/bf16 cache ({spent:.1f} s)"}
+        log(f"cpu oracle: {cpu['value']:.3e} tok/s on {cpu['cores']} threads")
+
+    qw = None
+    if qw_tokens:
+        qw_flops = 2 * 2 * 128 * 128 * hkv * qw_tokens
+        qw = {"tokens_per_s": qw_tokens / qw_time, "ms_total": round(qw_time * 1e3, 3),
+              "fp64_mfma_util": round(qw_flops / qw_time / (FP64_PEAK_TFLOPS * 1e12), 4),
+              "gbs": round(qw_tokens * hkv * (2 * 128 * 2 + 2 * (32 + 4 * 128 // group)) / qw_time / 1e9, 1)}
+
+    res = {
+        "metric": "INT2 paged decode attention: KV tokens/s + achieved HBM GB/s (% of peak)",
+        "value": value,
+        "unit": "KV tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int2+bf16 storage, int8/fp16/bf16 MFMA, fp32 accumulate",
+        "data": "synthetic (seeded generator; calibration on synthetic activations)",
+        "config": {"workload": w.name, "batch": B, "context": T_final, "n_q_heads": hq, "n_kv_heads": hkv,
+                   "head_dim": 128, "group": group, "sink": w.sink, "recent": w.recent, "page_size": 16,
+                   "splits_int2": si},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "decode_main", "kernel_us": round(main_avg_ms * 1e3, 2),
+                     "algorithmic_bytes_per_launch": int(alg)},
+        "cpu_baseline": cpu,
+        "bf16_baseline": baseline,
+        "quant_write": qw,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

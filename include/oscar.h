@@ -236,6 +236,25 @@ oscar_status oscar_decode_attn_bf16_baseline(const oscar_shape* shape, const osc
 /* Splits chosen when 0 is passed (deterministic in the arguments). */
 int32_t oscar_decode_auto_splits(const oscar_shape* shape, int32_t batch, int32_t max_int2_pages);
 
+/* One decode step for a batch: grows each of the n sequences by one token
+ * (host bookkeeping, as oscar_seq_plan_append with n_new = 1 per sequence).
+ * Outputs (host, capacity n each): int2_slots / bf16_slots of the new tokens
+ * (-1 where not that region); age_src / age_dst: compacted bf16 -> INT2 moves
+ * of tokens leaving the recent window, *n_age their count; ctx_lens: the new
+ * lengths; *tables_changed = 1 if any sequence received a new page (its block
+ * table rows must be refreshed).  On OSCAR_ENOMEM no sequence is changed. */
+oscar_status oscar_plan_decode_step(oscar_pool* pool, oscar_seq* const* seqs, int32_t n, int32_t* int2_slots,
+                                    int32_t* bf16_slots, int32_t* age_src, int32_t* age_dst, int32_t* n_age,
+                                    int32_t* ctx_lens, int32_t* tables_changed);
+
+/* Instrumentation.  While enabled (on != 0), each decode launch made by the
+ * calling thread records a pair of HIP events on its stream around the main
+ * decode kernel (not the prologue or the combine).  oscar_profile_read waits
+ * for the recorded events, returns the summed milliseconds and the launch
+ * count, and clears them. */
+oscar_status oscar_profile_enable(int32_t on);
+oscar_status oscar_profile_read(double* main_ms, int64_t* launches);
+
 #ifdef __cplusplus
 }
 #endif

@@ -69,6 +69,9 @@ _SIGS = {
     "oscar_decode_attn_bf16_baseline": (C.c_int32, [C.POINTER(Shape), C.POINTER(Cache), P, C.c_int32, P,
                                                     C.c_int32, P, C.c_int32, P, P, C.c_size_t, P]),
     "oscar_decode_auto_splits": (C.c_int32, [C.POINTER(Shape), C.c_int32, C.c_int32]),
+    "oscar_plan_decode_step": (C.c_int32, [P, P, C.c_int32, P, P, P, P, P, P, P]),
+    "oscar_profile_enable": (C.c_int32, [C.c_int32]),
+    "oscar_profile_read": (C.c_int32, [C.POINTER(C.c_double), I64P]),
 }
 EXPORTED = tuple(_SIGS)
 
@@ -277,3 +280,34 @@ def oscar_decode_attn_bf16_baseline(shape, cache, q, bf16_bt, ctx_lens, out, wor
     _check(lib().oscar_decode_attn_bf16_baseline(C.byref(shape), C.byref(cache), _ptr(q), batch, _ptr(bf16_bt),
                                                  bf16_bt.shape[1], _ptr(ctx_lens), splits, _ptr(out), _ptr(workspace),
                                                  workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+class DecodeStepPlanner:
+    """oscar_plan_decode_step with reusable host arrays (pinned when torch
+    can provide them), one call per decode step for the whole batch."""
+
+    def __init__(self, pool: Pool, seqs):
+        import numpy as np
+        self.pool = pool
+        self.n = len(seqs)
+        self.arr = (P * max(self.n, 1))(*seqs)
+        self.buf = np.zeros((5, max(self.n, 1)), np.int32)   # int2, bf16, age_src, age_dst, ctx
+        self.n_age = C.c_int32()
+        self.changed = C.c_int32()
+
+    def step(self):
+        b = self.buf
+        _check(lib().oscar_plan_decode_step(self.pool.handle, self.arr, self.n, b[0].ctypes.data, b[1].ctypes.data,
+                                            b[2].ctypes.data, b[3].ctypes.data, C.byref(self.n_age),
+                                            b[4].ctypes.data, C.byref(self.changed)))
+        return self.n_age.value, bool(self.changed.value)
+
+
+def oscar_profile_enable(on: bool):
+    _check(lib().oscar_profile_enable(1 if on else 0))
+
+
+def oscar_profile_read():
+    ms, n = C.c_double(), C.c_int64()
+    _check(lib().oscar_profile_read(C.byref(ms), C.byref(n)))
+    return ms.value, n.value

@@ -682,7 +682,7 @@ __global__ __launch_bounds__(128) void decode_combine(DecodeParams p) {
 }
 
 template <int NG, int CT>
-hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream) {
+hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
   const int bkn = p.batch * p.n_kv;
   const int S = p.splits_int2 + p.splits_bf16;
   if (p.splits_int2 > 0) {
@@ -690,24 +690,32 @@ hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  if (ev_start) {
+    hipError_t e = hipEventRecord(ev_start, stream);
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL((decode_main<NG, CT>), dim3(bkn * S), dim3(64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (ev_stop) {
+    e = hipEventRecord(ev_stop, stream);
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(decode_combine, dim3(bkn), dim3(128), 0, stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
   if (p.ng == 4) {
-    if (p.ct == 1) return launch_decode_t<4, 1>(p, stream);
-    if (p.ct == 2) return launch_decode_t<4, 2>(p, stream);
-    if (p.ct == 3) return launch_decode_t<4, 3>(p, stream);
+    if (p.ct == 1) return launch_decode_t<4, 1>(p, stream, ev_start, ev_stop);
+    if (p.ct == 2) return launch_decode_t<4, 2>(p, stream, ev_start, ev_stop);
+    if (p.ct == 3) return launch_decode_t<4, 3>(p, stream, ev_start, ev_stop);
   } else if (p.ng == 2) {
-    if (p.ct == 1) return launch_decode_t<2, 1>(p, stream);
-    if (p.ct == 2) return launch_decode_t<2, 2>(p, stream);
-    if (p.ct == 3) return launch_decode_t<2, 3>(p, stream);
+    if (p.ct == 1) return launch_decode_t<2, 1>(p, stream, ev_start, ev_stop);
+    if (p.ct == 2) return launch_decode_t<2, 2>(p, stream, ev_start, ev_stop);
+    if (p.ct == 3) return launch_decode_t<2, 3>(p, stream, ev_start, ev_stop);
   }
   return hipErrorInvalidValue;
 }

@@ -22,6 +22,12 @@ namespace {
 
 thread_local std::string g_err;
 
+struct ProfileState {
+  bool on = false;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> events;
+};
+thread_local ProfileState g_prof;
+
 oscar_status fail(oscar_status code, const char* fmt, ...) {
   char buf[512];
   va_list ap;
@@ -572,6 +578,52 @@ oscar_status oscar_block_tables(const oscar_pool* pool, const oscar_seq* const* 
   return ok();
 }
 
+oscar_status oscar_plan_decode_step(oscar_pool* pool, oscar_seq* const* seqs, int32_t n, int32_t* int2_slots,
+                                    int32_t* bf16_slots, int32_t* age_src, int32_t* age_dst, int32_t* n_age,
+                                    int32_t* ctx_lens, int32_t* tables_changed) {
+  if (!pool || n < 0 || (n > 0 && (!seqs || !int2_slots || !bf16_slots || !age_src || !age_dst || !ctx_lens)) ||
+      !n_age || !tables_changed)
+    return fail(OSCAR_EINVAL, "NULL argument");
+  const oscar_shape& sh = pool->shape;
+  // page needs first, so that exhaustion changes nothing
+  int64_t need[2] = {0, 0};
+  for (int32_t i = 0; i < n; ++i) {
+    const oscar_seq* s = seqs[i];
+    if (!s) return fail(OSCAR_EINVAL, "sequence %d is NULL", i);
+    const int64_t t0 = s->len, t1 = t0 + 1;
+    if (sh.recent > 0 && t0 - sh.recent >= sh.sink) {
+      const int64_t p = t0 - sh.recent;  // leaves the window
+      const int64_t lp = p / kPage;
+      if (lp >= (int64_t)s->int2.size() || s->int2[(size_t)lp] < 0) ++need[0];
+    }
+    if (region(sh, t0, t1) == kInt2) {
+      const int64_t lp = t0 / kPage;
+      if (lp >= (int64_t)s->int2.size() || s->int2[(size_t)lp] < 0) ++need[0];
+    } else {
+      const int64_t lp = bf16_logical_slot(sh, t0) / kPage;
+      if (s->bf16[(size_t)lp] < 0) ++need[1];
+    }
+  }
+  if (need[0] > (int64_t)pool->free_[0].size() || need[1] > (int64_t)pool->free_[1].size())
+    return fail(OSCAR_ENOMEM, "pool exhausted in decode step");
+  int32_t na = 0;
+  *tables_changed = (need[0] + need[1]) > 0;
+  for (int32_t i = 0; i < n; ++i) {
+    int64_t n_age_i = 0;
+    int32_t src = -1, dst = -1;
+    oscar_status st = oscar_seq_plan_append(pool, seqs[i], 1, &int2_slots[i], &bf16_slots[i], &src, &dst, &n_age_i);
+    if (st) return st;
+    if (n_age_i) {
+      age_src[na] = src;
+      age_dst[na] = dst;
+      ++na;
+    }
+    ctx_lens[i] = (int32_t)seqs[i]->len;
+  }
+  *n_age = na;
+  return ok();
+}
+
 // ----------------------------------------------------------------------------
 // Launches
 // ----------------------------------------------------------------------------
@@ -756,7 +808,13 @@ static oscar_status decode_common(const oscar_shape* shape, const oscar_layer* l
   if (workspace_bytes < need) return fail(OSCAR_EINVAL, "workspace %zu bytes < %zu needed", workspace_bytes, need);
   decode_workspace_carve(p, workspace);
   p.out = out;
-  return hip_status(launch_decode(p, (hipStream_t)stream), "decode launch");
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  if (g_prof.on) {
+    if (hipEventCreate(&ev0) != hipSuccess || hipEventCreate(&ev1) != hipSuccess)
+      return fail(OSCAR_EHIP, "hipEventCreate failed");
+    g_prof.events.emplace_back(ev0, ev1);
+  }
+  return hip_status(launch_decode(p, (hipStream_t)stream, ev0, ev1), "decode launch");
 }
 
 oscar_status oscar_decode_attn(const oscar_shape* shape, const oscar_layer* layer, const oscar_cache* cache,
@@ -766,6 +824,28 @@ oscar_status oscar_decode_attn(const oscar_shape* shape, const oscar_layer* laye
                                size_t workspace_bytes, void* stream) {
   return decode_common(shape, layer, cache, q, batch, int2_bt, max_int2_pages, bf16_bt, max_bf16_pages, ctx_lens,
                        splits_int2, splits_bf16, out, workspace, workspace_bytes, stream, false);
+}
+
+oscar_status oscar_profile_enable(int32_t on) {
+  g_prof.on = on != 0;
+  return ok();
+}
+
+oscar_status oscar_profile_read(double* main_ms, int64_t* launches) {
+  if (!main_ms || !launches) return fail(OSCAR_EINVAL, "NULL argument");
+  double total = 0.0;
+  for (auto& pr : g_prof.events) {
+    float ms = 0.f;
+    if (hipEventSynchronize(pr.second) != hipSuccess || hipEventElapsedTime(&ms, pr.first, pr.second) != hipSuccess)
+      return fail(OSCAR_EHIP, "event timing failed");
+    total += ms;
+    (void)hipEventDestroy(pr.first);
+    (void)hipEventDestroy(pr.second);
+  }
+  *launches = (int64_t)g_prof.events.size();
+  g_prof.events.clear();
+  *main_ms = total;
+  return ok();
 }
 
 oscar_status oscar_decode_attn_bf16_baseline(const oscar_shape* shape, const oscar_cache* cache, const void* q,

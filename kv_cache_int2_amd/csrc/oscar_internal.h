@@ -66,7 +66,8 @@ hipError_t launch_bf16_write(const uint16_t* k, const uint16_t* v, const int32_t
                              uint8_t* bf16_pages, int64_t n_pages, hipStream_t stream);
 hipError_t launch_copy_pages(uint8_t* base, int64_t block_bytes_all_heads, int64_t n_pages, const int32_t* src,
                              const int32_t* dst, int64_t n, hipStream_t stream);
-hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
+// ev_start / ev_stop (may be null): recorded on `stream` around the main kernel.
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop);
 
 // Workspace bytes for the decode path (each region 256-byte aligned).
 size_t decode_workspace_bytes(int batch, int n_q, int n_kv, int ct, int splits_total);

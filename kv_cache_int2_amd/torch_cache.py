@@ -1,4 +1,4 @@
-"""Drive the product path (C ABI through the Python binding) for GPU tests,
+"""Torch-side driver of the C ABI: a paged cache held in torch device tensors,
 the smoke entry point and the benchmark.  Imports nothing from the oracle."""
 from __future__ import annotations
 

@@ -16,7 +16,7 @@ import torch
 import kv_cache_int2_amd as K
 import oracle as O
 import synth
-from gpu_cache import BaselineCache, DeviceCache
+from kv_cache_int2_amd.torch_cache import BaselineCache, DeviceCache
 
 pytestmark = pytest.mark.gpu
 
@@ -215,7 +215,7 @@ def test_quant_write_scattered_slots_and_nan_group():
     rng = np.random.default_rng(0)
     slots = rng.permutation(64 * 16)[:n].astype(np.int32)
     order = rng.permutation(n)
-    from gpu_cache import to_dev_bits, to_dev_i32
+    from kv_cache_int2_amd.torch_cache import to_dev_bits, to_dev_i32
     K.oscar_quant_write(sh, dc.layer, dc.cache, to_dev_bits(kb[order]), to_dev_bits(vb[order]),
                         to_dev_i32(slots[order]))
     torch.cuda.synchronize()
