@@ -35,10 +35,10 @@
  *   INT2 block (2*(4*d + 64*NG) bytes: 1536 for d=128,G=32; 1280 for G=64):
  *     K codes  [16][d/4] bytes, token-major; channel j of token t sits in byte
  *              t*d/4 + j/4 at bits 2*(j%4).
- *     K scale/zero  fp16 [NG][16][2] = (s, z) per group and token.
- *     V codes  16-bit words [2][d]: word [a][j] holds channel j of tokens
- *              8a..8a+7, token 8a+i at bits 2*i.
- *     V scale/zero  as for K.
+ *     K scale/zero  fp16 [16][NG][2] = (s, z) per token and group (token-major).
+ *     V codes  [4][d] bytes by token quad: byte q*d + j holds channel j of
+ *              tokens 4q..4q+3, token 4q+i at bits 2*i.
+ *     V scale/zero  fp16 [NG][16][2] = (s, z) per group and token (group-major).
  *   BF16 block (4*16*d bytes): K as bf16 [16][d] (token-major), then V as
  *   bf16 [d][16] (channel-major).
  *   A layer's INT2 storage is [n_int2_pages][n_kv_heads][INT2 block]; its bf16

@@ -12,29 +12,32 @@
 // Kernels
 //   decode_prologue  per (request, KV head): q R_K for the g query heads of the
 //                    group, turned into MFMA operands.
-//   decode_main      per (request, KV head, split): one wavefront streams its
-//                    share of pages, two pages (32 tokens) per iteration.
+//   decode_int2      per (request, KV head, split): one wavefront streams its
+//                    share of INT2 pages, two pages (32 tokens) per iteration.
+//   decode_bf16      the same for the bf16 pages (sink + recent tokens, or the
+//                    whole context in the all-bf16 baseline).
 //   decode_combine   per (request, KV head): log-sum-exp merge of the splits,
 //                    R_V^T on the INT2 part, normalisation.
 //
 // INT2 logits on MFMA (v_mfma_i32_16x16x64_i8, exact integer accumulation):
 //   q~ = (q R_K) log2(e)/sqrt(d) is held as the fixed-point integer
-//   Q = rint(q~ 2^sq) (|Q| < 2^22 per head), split into three balanced int8
-//   digits Q = d0 2^16 + d1 2^8 + d2.  A = the 2-bit codes as int8 bytes,
-//   B = the digits, block-diagonal over channel groups: column (h, gamma) only
-//   sees channels of group gamma, so C[t, (h, gamma)] = sum_{j in gamma} Q_hj c_tj
-//   exactly.  With the group sum Qbar = sum_{j in gamma} Q_hj,
-//     sum_j Q_j (z + c_j s) = (s/2) (2C - 3 Qbar) + (z + 1.5 s) Qbar,
-//   where 2C - 3 Qbar = sum_j Q_j (2 c_j - 3) is formed exactly in int32, so
-//   the large, nearly cancelling terms s C and z Qbar are never rounded.
-// INT2 values on MFMA:
-//   A = P'[(h, gamma), t] = p_ht s_t,gamma 2^sp 2^-2r (hi + lo fp16),
-//   B = centred V codes (2c - 3) 2^(2r-24) as exact fp16 subnormals
-//       (channel-major words make a lane's 8 tokens of one channel a single
-//       16-bit word; one packed fp16 fma centres them),
-//   acc[(h, gamma), j] for j in group gamma; the midpoint term
-//   sum_t p_ht (z + 1.5 s)_t,gamma is accumulated on the VALU.  Centring keeps
-//   both sums free of the large cancelling parts sum p z and sum p s c.
+//   Q = rint(q~ 2^sq) (|Q| <= 2^21 per (request, KV head)); 2Q is split into
+//   three balanced int8 digits.  A = the digits, block-diagonal over channel
+//   groups (row (h, gamma) only sees channels of group gamma), B = the 2-bit
+//   codes as int8 bytes (columns = tokens).  The digit chains feed each other
+//   (acc <- (acc << 8) + sum d c) and the last starts from -3 Qbar, so the
+//   accumulator ends holding, exactly,
+//     C2 = sum_{j in gamma} Q_j (2 c_j - 3),     Qbar = sum_{j in gamma} Q_j,
+//   and  sum_j Q_j (z + c_j s) = (s/2) C2 + (z + 1.5 s) Qbar.  The large, nearly
+//   cancelling terms s C and z Qbar of the direct form are never rounded.
+// INT2 values on MFMA (v_mfma_f32_16x16x32_f16):
+//   A = P'[(h, gamma), t] = p_ht s_t,gamma 2^sp 4^-r as fp16 hi + lo (about 22
+//   significant bits), B = centred codes (2c - 3) 4^r 2^-24, exact fp16
+//   subnormals built from the packed bytes with one mask and one packed fma.
+//   The accumulator row (h, gamma) is kept for the channels of group gamma.
+//   With the midpoint w = z + 1.5 s the value is w + (2c - 3) s / 2: the VALU
+//   sums p w, the MFMA sums p s (2c - 3), whose signs keep its accumulation
+//   unbiased.
 // bf16 tokens use v_mfma_f32_16x16x32_bf16 with the unrotated query (exact
 // products) and P split into bf16 hi + mid + lo.
 #include <hip/hip_runtime.h>
@@ -88,6 +91,17 @@ __device__ __forceinline__ uint32_t bf16_bits(float x) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 __device__ __forceinline__ float bf16_val(uint32_t b) { return __builtin_bit_cast(float, b << 16); }
+// x - (float)h for the low / high fp16 half of a packed pair, in one mixed-precision fma
+__device__ __forceinline__ float mix_sub_lo(float x, f16x2 h) {
+  float r;
+  asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(x));
+  return r;
+}
+__device__ __forceinline__ float mix_sub_hi(float x, f16x2 h) {
+  float r;
+  asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(x));
+  return r;
+}
 
 // butterfly sum over the NG lanes of a channel-group set (lanes differ in the low bits)
 template <int NG>
@@ -108,6 +122,25 @@ __device__ __forceinline__ float sum_across_quads(float x) {
   return x;
 }
 
+// exp2 without the denormal-range fix-up: softmax weights below 2^-126 are 0
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// all-reduce max / sum over the 16 lanes of a row
+__device__ __forceinline__ float row_max16(float x) {
+  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false)));
+  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false)));
+  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x124, 0xF, 0xF, false)));
+  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false)));
+  return x;
+}
+__device__ __forceinline__ float row_sum16(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x124, 0xF, 0xF, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false));
+  return x;
+}
+
 __device__ __forceinline__ const uint8_t* block_ptr(const uint8_t* base, int64_t page, int n_kv, int kv,
                                                     int bytes) {
   return base + ((page * n_kv + kv) * (int64_t)bytes);
@@ -116,9 +149,9 @@ __device__ __forceinline__ const uint8_t* block_ptr(const uint8_t* base, int64_t
 // ---------------------------------------------------------------------------
 // prologue: q R_K operands
 // ---------------------------------------------------------------------------
-// Words per (request, KV head): B digits ((((ct*3 + digit)*2 + kstep)*64 + lane)*4 + reg),
-// then aux floats [1 + 32*CT]: logit factor 2^-sq / 2, per column 2*Qbar (float),
-// per column -3*Qbar (int32 bits).
+// Words per (request, KV head): A digits of 2Q ((((ct*3 + digit)*2 + kstep)*64 + lane)*4 + reg),
+// then aux floats [1 + 32*CT]: logit factor 2^-sq / 2, per row 2*Qbar (float),
+// per row -3*Qbar (int32 bits).
 template <int NG, int CT>
 __global__ __launch_bounds__(128) void decode_prologue(DecodeParams p) {
   const int bk = blockIdx.x;
@@ -145,12 +178,13 @@ __global__ __launch_bounds__(128) void decode_prologue(DecodeParams p) {
   if ((j & 63) == 0) red[j >> 6] = mx;
   __syncthreads();
   mx = fmaxf(red[0], red[1]);
-  // 2^sq brings the largest |q~| to [2^21, 2^22)
+  // 2^sq brings the largest |q~| to [2^20, 2^21), so |2Q| <= 2^22 fits three
+  // balanced int8 digits
   int sq = 0;
   if (mx > 0.f && mx < __builtin_huge_valf()) {
     int e;
     frexpf(mx, &e);  // mx in [2^(e-1), 2^e)
-    sq = 22 - e;
+    sq = min(21 - e, 100);  // keeps the logit factor 2^-sq / 2 a normal float
   }
   for (int h = 0; h < g; ++h) qi[h][j] = (int)rintf(ldexpf(qt[h], sq));
   __syncthreads();
@@ -175,7 +209,7 @@ __global__ __launch_bounds__(128) void decode_prologue(DecodeParams p) {
       const int ch = 32 * qd + 16 * ks + 4 * byte + reg;
       int dv = 0;
       if (h < g && ch / G == gam) {
-        const int q = qi[h][ch];
+        const int q = 2 * qi[h][ch];
         const int d2 = ((q + 128) & 255) - 128;
         const int q1 = (q - d2) >> 8;
         const int d1 = ((q1 + 128) & 255) - 128;
@@ -190,198 +224,391 @@ __global__ __launch_bounds__(128) void decode_prologue(DecodeParams p) {
 
 // ---------------------------------------------------------------------------
 // main kernel: INT2 work item
+//
+// Per iteration one wavefront takes two pages (32 tokens) of one (request, KV
+// head).  Logits: C[(h, gamma), t] = sum_j 2Q_hj c_tj - 3 Qbar on the int8 MFMA
+// with A = digits of 2Q (rows (h, gamma)), B = codes (columns = the 16 tokens
+// of one page); the -3 Qbar enters as the initial accumulator of the low
+// digit.  Lane l then holds, for the head of its row group and token l%16, all
+// channel groups, so the group sum and the exp need no cross-lane traffic.
+// The running max is lazy: it moves, with a margin, only when a logit passes
+// it (one ballot per pair); only then are row maxima reduced and the
+// accumulators rescaled.  p moves through LDS to the value MFMA, whose A
+// operand is P'[(h, gamma), t] (rows again (h, gamma), k = tokens) and whose
+// accumulator rows match the logit rows, so rescaling is lane-local.
+//
+// Value k order: in lane quad qd, half-word 2r + e of the operand is token
+// 4qd + r of page e.  Both pages are then read at lane-uniform block
+// addresses, and one byte permute pairs a channel's codes of the two pages.
 // ---------------------------------------------------------------------------
-template <int NG, int CT, bool EDGE>
-__device__ __forceinline__ void int2_pair(const DecodeParams& p, const uint8_t* blk0, const uint8_t* blk1,
-                                          int lp0, int p_end, int lo, int hi, const u32x4 (&bq)[CT][3][2],
-                                          const float (&qbar2)[CT], const int (&qneg3)[CT], float kfac,
-                                          float pscale, float (&m_run)[CT],
-                                          float (&l_run)[CT], float (&zsum)[CT], f32x4 (&acc)[CT][8]) {
+constexpr float kMaxMargin = 4.f;  // log2 headroom added when the running max moves
+
+template <int NG, int CT>
+struct Int2State {
+  static constexpr int HPL = 4 / NG;  // heads per lane per row tile
+  // running max m (log2 units) kept as moff = log2(pfac) - m, so that the exp
+  // yields p pfac directly; l sums those scaled weights (per lane)
+  float moff[CT][HPL];
+  float mx_run[CT][HPL];  // m in raw logit units
+  float l_run[CT][HPL];
+  float zsum[CT][4];      // value-operand row 16ct + ln, token slot r; units pscale 4^-r
+  f32x4 acc[CT][8];
+};
+
+template <int NG, int CT>
+struct Int2Const {
+  u32x4 qa[CT][3][2];  // digits of 2Q: A operand, rows 16ct + ln
+  i32x4 qneg3[CT];     // -3 Qbar of the accumulator rows 16ct + 4qd + r
+  float qbar2[CT][4];  // 2 Qbar of those rows
+  float kfac, ikfac;   // raw logit -> log2 units, and its inverse (powers of two)
+  float lpf;           // log2(pscale 4^-(ln % 4)): P' factor of the token this lane writes
+};
+
+// one pair of INT2 blocks, as this lane reads them: the key part, read
+// before the logits, and the value part, read after the softmax
+template <int NG>
+struct Int2KData {
+  u32x2 kc[2];          // K codes: token ln, bytes 8qd..8qd+7
+  uint32_t ksz[2][NG];  // K (s, z): token ln, every group
+};
+template <int NG>
+struct Int2VData {
+  u32x2 vw[2];          // V codes: quad qd, channels 8ln..8ln+7
+  u32x4 vsz[2];         // V (s, z): group ln % NG, tokens 4qd..4qd+3
+};
+// a pair already in registers (the masked path)
+template <int NG>
+struct Int2Data {
+  Int2KData<NG> kd;
+  Int2VData<NG> vd;
+  __device__ __forceinline__ const Int2KData<NG>& k() const { return kd; }
+  __device__ __forceinline__ const Int2VData<NG>& v() const { return vd; }
+};
+
+struct Int2Offsets {
+  uint32_t kc, ksz, vw, vsz;
+};
+
+template <int NG>
+__device__ __forceinline__ Int2Offsets int2_offsets() {
   constexpr Int2Layout L{NG};
   const int lane = threadIdx.x, ln = lane & 15, qd = lane >> 4;
-  const int a = qd & 1, gam = ln % NG;
-  // A operand rows (tokens) of the two QK tiles
-  const uint8_t* bk = (ln >> 3) ? blk1 : blk0;
-  const int tokA = 8 * ((ln >> 2) & 1) + (ln & 3);
-  const u32x2 ka0 = *(const u32x2*)(bk + L.k_codes() + tokA * 32 + 8 * qd);
-  const u32x2 ka1 = *(const u32x2*)(bk + L.k_codes() + (tokA + 4) * 32 + 8 * qd);
-  // this lane's C rows / PV k-range: page qd>>1, tokens 8a + 4*tile + r
-  const uint8_t* bq_ = (qd >> 1) ? blk1 : blk0;
-  const u32x4 ksz0 = *(const u32x4*)(bq_ + L.k_sz() + (gam * 16 + 8 * a) * 4);
-  const u32x4 ksz1 = *(const u32x4*)(bq_ + L.k_sz() + (gam * 16 + 8 * a + 4) * 4);
-  const u32x4 vw = *(const u32x4*)(bq_ + L.v_codes() + (a * 128 + 8 * ln) * 2);
-  const u32x4 vsz0 = *(const u32x4*)(bq_ + L.v_sz() + (gam * 16 + 8 * a) * 4);
-  const u32x4 vsz1 = *(const u32x4*)(bq_ + L.v_sz() + (gam * 16 + 8 * a + 4) * 4);
+  return Int2Offsets{(uint32_t)(L.k_codes() + ln * 32 + 8 * qd), (uint32_t)(L.k_sz() + ln * NG * 4),
+                     (uint32_t)(L.v_codes() + qd * kHeadDim + 8 * ln),
+                     (uint32_t)(L.v_sz() + ((ln % NG) * kPage + 4 * qd) * 4)};
+}
 
-  // ---- QK: exact integer sums per (token, (h, gamma)) ----
-  // A register k of K-step ks holds, byte b, the code of channel 32qd + 16ks + 4b + k.
-  i32x4 c[2][CT];
-  const uint32_t kd[2][2] = {{ka0[0], ka0[1]}, {ka1[0], ka1[1]}};
+// Buffer descriptor of one block (gfx9 raw buffer: stride 0, bounds = the
+// block's bytes).  The block address is wavefront-uniform, so the descriptor
+// lives in SGPRs and each load is a per-lane 32-bit offset with no address math.
+constexpr int kBufferWord3 = 0x00020000;
+// s_waitcnt immediate for vmcnt(0) alone (expcnt and lgkmcnt at their maxima)
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+template <int NG>
+__device__ __forceinline__ Int2Data<NG> int2_load(const uint8_t* blk0, const uint8_t* blk1, const Int2Offsets& o) {
+  constexpr Int2Layout L{NG};
+  Int2Data<NG> d;
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    i32x4 cd[CT][3];
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(t ? blk1 : blk0), 0, L.bytes(), kBufferWord3);
+    d.kd.kc[t] = __builtin_amdgcn_raw_buffer_load_b64(rs, o.kc, 0, 0);
+    if constexpr (NG == 4) {
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, o.ksz, 0, 0);
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct)
+      for (int g = 0; g < 4; ++g) d.kd.ksz[t][g] = v[g];
+    } else {
+      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rs, o.ksz, 0, 0);
+      d.kd.ksz[t][0] = v[0];
+      d.kd.ksz[t][1] = v[1];
+    }
+    d.vd.vw[t] = __builtin_amdgcn_raw_buffer_load_b64(rs, o.vw, 0, 0);
+    d.vd.vsz[t] = __builtin_amdgcn_raw_buffer_load_b128(rs, o.vsz, 0, 0);
+  }
+  return d;
+}
+
+// Interior pairs are staged through LDS with buffer->LDS loads (a pair is two
+// blocks; each block is one full-wavefront 16-byte load plus one from the first
+// (bytes - 1024)/16 lanes).  Such a load writes LDS at M0 + its immediate
+// offset + 16 per lane, so the immediate stays 0 and the block offset travels
+// in the per-lane offset.  The loads are issued from inline assembly: the
+// compiler's wait insertion would otherwise put a full vmcnt(0) before every
+// LDS read, which serialises the prefetch; vm_wait below carries the exact
+// count instead (loads it does not know of can only lengthen its own waits).
+// Ordering: the staging loads and the waits are compiler memory barriers, so
+// no read of the staged bytes moves across them.
+__device__ __forceinline__ u32x4 block_rsrc(const void* p, uint32_t bytes) {
+  const uint64_t a = (uint64_t)p;
+  return u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+               (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu)), bytes,
+               (uint32_t)kBufferWord3};
+}
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+__device__ __forceinline__ void lds_dma16(const u32x4& rs, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(voff), "s"(rs)
+               : "memory", "m0");
+}
+
+// st: LDS byte address of a two-block slot
+template <int NG>
+__device__ __forceinline__ void int2_issue(const uint8_t* blk0, const uint8_t* blk1, uint32_t st) {
+  constexpr Int2Layout L{NG};
+  constexpr int kRest = (L.bytes() - 1024) / 16;
+  static_assert(L.bytes() > 1024 && L.bytes() <= 2048 && L.bytes() % 16 == 0, "block staging layout");
+  const int lane = threadIdx.x;
 #pragma unroll
-      for (int d = 0; d < 3; ++d) cd[ct][d] = i32x4{0, 0, 0, 0};
+  for (int t = 0; t < 2; ++t) {
+    const u32x4 rs = block_rsrc(t ? blk1 : blk0, L.bytes());
+    lds_dma16(rs, st + t * L.bytes(), 16 * lane);
+    if (lane < kRest) lds_dma16(rs, st + t * L.bytes() + 1024, 1024 + 16 * lane);
+  }
+}
+// Wait until at most N vector-memory operations of this wavefront are in
+// flight (the N most recent are the next pair's four staging loads).
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N == 0 || N == 4, "vm_wait");
+  if constexpr (N == 0)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+}
+
+// a pair staged in LDS: each part is read when the pair asks for it
+template <int NG>
+struct Int2Staged {
+  const uint8_t* st;
+  Int2Offsets o;
+  __device__ __forceinline__ Int2KData<NG> k() const {
+    constexpr Int2Layout L{NG};
+    Int2KData<NG> d;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const uint8_t* blk = st + t * L.bytes();
+      d.kc[t] = *(const u32x2*)(blk + o.kc);
+      if constexpr (NG == 4) {
+        const u32x4 v = *(const u32x4*)(blk + o.ksz);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) d.ksz[t][g] = v[g];
+      } else {
+        const u32x2 v = *(const u32x2*)(blk + o.ksz);
+        d.ksz[t][0] = v[0];
+        d.ksz[t][1] = v[1];
+      }
+    }
+    return d;
+  }
+  __device__ __forceinline__ Int2VData<NG> v() const {
+    constexpr Int2Layout L{NG};
+    Int2VData<NG> d;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const uint8_t* blk = st + t * L.bytes();
+      d.vw[t] = *(const u32x2*)(blk + o.vw);
+      d.vsz[t] = *(const u32x4*)(blk + o.vsz);
+    }
+    return d;
+  }
+};
+
+template <int NG, int CT, bool EDGE, class Src>
+__device__ __forceinline__ void int2_pair(const Src& src, int lp0, int p_end, int lo, int hi,
+                                          const Int2Const<NG, CT>& K, Int2State<NG, CT>& S, float* p_lds) {
+  constexpr int HPL = 4 / NG;
+  const int lane = threadIdx.x, ln = lane & 15, qd = lane >> 4;
+  // ---- logits ----
+  const Int2KData<NG> DK = src.k();
+  bool valid[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    if constexpr (EDGE) {
+      const int pos = (lp0 + t) * kPage + ln;
+      valid[t] = lp0 + t < p_end && pos >= lo && pos < hi;
+    } else {
+      valid[t] = true;
+    }
+  }
+  float lg[2][CT][HPL];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    u32x4 av[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const uint32_t x = kd[t][ks];
-      const u32x4 av = {x & 0x03030303u, (x >> 2) & 0x03030303u, (x >> 4) & 0x03030303u, (x >> 6) & 0x03030303u};
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-        for (int d = 0; d < 3; ++d) cd[ct][d] = mfma_i8(av, bq[ct][d][ks], cd[ct][d]);
+      const uint32_t x = DK.kc[t][ks];
+      av[ks] = u32x4{x & 0x03030303u, (x >> 2) & 0x03030303u, (x >> 4) & 0x03030303u, (x >> 6) & 0x03030303u};
     }
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct)
+    for (int ct = 0; ct < CT; ++ct) {
+      // digit chains feed each other: acc <- (acc << 8) + sum d_k c, the low
+      // digit's chain starting from (acc << 8) - 3 Qbar; every partial value is
+      // an exact integer below 2^31 in magnitude
+      i32x4 cd = i32x4{0, 0, 0, 0};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int cc = (cd[ct][0][r] * 256 + cd[ct][1][r]) * 256 + cd[ct][2][r];  // sum Q c
-        c[t][ct][r] = 2 * cc + qneg3[ct];                                           // sum Q (2c - 3)
+      for (int d = 0; d < 3; ++d) {
+        if (d == 1) cd = cd << 8;
+        if (d == 2) cd = (cd << 8) + K.qneg3[ct];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) cd = mfma_i8(K.qa[ct][d][ks], av[ks], cd);
       }
-  }
-  // ---- logits (log2 domain) ----
-  const int lp = lp0 + (qd >> 1);
-  const int pos0 = lp * kPage + 8 * a;
-  bool valid[2][4];
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+      for (int hh = 0; hh < HPL; ++hh) {
+        float x = 0.f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if constexpr (EDGE) {
-        const int pos = pos0 + 4 * t + r;
-        valid[t][r] = lp < p_end && pos >= lo && pos < hi;
-      } else {
-        valid[t][r] = true;
-      }
-    }
-  float lg[2][CT][4];
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const u32x4 sz = t ? ksz1 : ksz0;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float sv = half_lo(sz[r]), zv = half_hi(sz[r]);
-      if constexpr (EDGE) {
-        sv = valid[t][r] ? sv : 0.f;
-        zv = valid[t][r] ? zv : 0.f;
-      }
-      const float mid = fmaf(1.5f, sv, zv);   // group midpoint z + 1.5 s (exact)
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
-        float x = fmaf(sv, (float)c[t][ct][r], mid * qbar2[ct]);
-        x = group_sum<NG>(x) * kfac;
-        lg[t][ct][r] = valid[t][r] ? x : kNegInf;
+        for (int gg = 0; gg < NG; ++gg) {
+          const int r = hh * NG + gg;
+          const int c2 = cd[r];  // sum_j 2Q_j c_j - 3 Qbar = sum_j Q_j (2 c_j - 3)
+          const float sv = half_lo(DK.ksz[t][gg]), zv = half_hi(DK.ksz[t][gg]);
+          x = fmaf(sv, (float)c2, fmaf(fmaf(1.5f, sv, zv), K.qbar2[ct][r], x));
+        }
+        lg[t][ct][hh] = valid[t] ? x : kNegInf;
       }
     }
   }
-  // ---- online softmax ----
-  float pr[2][CT][4];
+  // ---- online softmax, lazy running max (per head: a 16-lane row) ----
+  float pr[2][CT][HPL];
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
-    float mt = kNegInf;
+    float mt[HPL];
+    bool grow = false;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int hh = 0; hh < HPL; ++hh) {
+      mt[hh] = fmaxf(lg[0][ct][hh], lg[1][ct][hh]);
+      grow |= mt[hh] > S.mx_run[ct][hh];
+    }
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(grow) != 0, 0)) {
+      float alpha[HPL];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) mt = fmaxf(mt, lg[t][ct][r]);
-    mt = max_across_quads(mt);
-    const float m_new = fmaxf(m_run[ct], mt);
-    if (__builtin_amdgcn_ballot_w64(m_new > m_run[ct])) {
-      const float alpha = (m_new == kNegInf) ? 1.f : exp2f(m_run[ct] - m_new);
-      l_run[ct] *= alpha;
-      zsum[ct] *= alpha;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float ar = __shfl(alpha, 4 * qd + r);
-#pragma unroll
-        for (int kt = 0; kt < 8; ++kt) acc[ct][kt][r] *= ar;
+      for (int hh = 0; hh < HPL; ++hh) {
+        const float rm = row_max16(mt[hh]);
+        alpha[hh] = 1.f;
+        if (rm > S.mx_run[ct][hh]) {
+          const float m_new = fmaf(rm, K.kfac, kMaxMargin);
+          const float moff = K.lpf - m_new;
+          alpha[hh] = fast_exp2(moff - S.moff[ct][hh]);  // 0 when there was no max yet
+          S.moff[ct][hh] = moff;
+          S.mx_run[ct][hh] = m_new * K.ikfac;
+          S.l_run[ct][hh] *= alpha[hh];
+        }
       }
-      m_run[ct] = m_new;
+#pragma unroll
+      for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S.acc[ct][kt][r] *= alpha[r / NG];
+      // value-operand row 16ct + ln belongs to head (16ct + ln) / NG, whose
+      // alpha is held by quad ln / 4, entry (ln % 4) / NG
+      float az = __shfl(alpha[0], 16 * (ln >> 2));
+      if constexpr (HPL == 2) {
+        const float az1 = __shfl(alpha[1], 16 * (ln >> 2));
+        az = ((ln >> 1) & 1) ? az1 : az;
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) S.zsum[ct][r] *= az;
     }
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float e = exp2f(lg[t][ct][r] - m_run[ct]);
-        pr[t][ct][r] = valid[t][r] ? e : 0.f;
-        l_run[ct] += pr[t][ct][r];
+      for (int hh = 0; hh < HPL; ++hh) {
+        const float e = fast_exp2(fmaf(lg[t][ct][hh], K.kfac, S.moff[ct][hh]));  // p pfac
+        pr[t][ct][hh] = valid[t] ? e : 0.f;
+        S.l_run[ct][hh] += pr[t][ct][hh];
       }
   }
-  // ---- P' operands and zero-point term ----
+  // ---- p' = p pscale 4^-(token % 4) to the value-operand layout: p_lds[h][page][16] ----
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+    for (int hh = 0; hh < HPL; ++hh) {
+      const int h = (16 * ct + 4 * qd + hh * NG) / NG;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) p_lds[(2 * h + t) * kPage + ln] = pr[t][ct][hh];
+    }
+  __builtin_amdgcn_wave_barrier();
+  const Int2VData<NG> DV = src.v();
   u32x4 pa[CT][2];
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
+    const int h = (16 * ct + ln) / NG;
+    const f32x4 pf0 = *(const f32x4*)(p_lds + (2 * h) * kPage + 4 * qd);
+    const f32x4 pf1 = *(const f32x4*)(p_lds + (2 * h + 1) * kPage + 4 * qd);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float s0 = half_lo(vsz0[r]), z0 = half_hi(vsz0[r]);
-      float s1 = half_lo(vsz1[r]), z1 = half_hi(vsz1[r]);
+      float s0 = half_lo(DV.vsz[0][r]), z0 = half_hi(DV.vsz[0][r]);
+      float s1 = half_lo(DV.vsz[1][r]), z1 = half_hi(DV.vsz[1][r]);
       if constexpr (EDGE) {
-        s0 = valid[0][r] ? s0 : 0.f;
-        z0 = valid[0][r] ? z0 : 0.f;
-        s1 = valid[1][r] ? s1 : 0.f;
-        z1 = valid[1][r] ? z1 : 0.f;
+        // unwritten slots may hold anything: zero their scale and zero point
+        const int pos0 = lp0 * kPage + 4 * qd + r, pos1 = pos0 + kPage;
+        const bool v0 = lp0 < p_end && pos0 >= lo && pos0 < hi;
+        const bool v1 = lp0 + 1 < p_end && pos1 >= lo && pos1 < hi;
+        s0 = v0 ? s0 : 0.f;
+        z0 = v0 ? z0 : 0.f;
+        s1 = v1 ? s1 : 0.f;
+        z1 = v1 ? z1 : 0.f;
       }
-      const float f = pscale * (1.0f / (float)(1 << (2 * r)));
-      const float x0 = pr[0][ct][r] * s0 * f;
-      const float x1 = pr[1][ct][r] * s1 * f;
-      const float h0 = (float)(_Float16)x0, h1 = (float)(_Float16)x1;
-      pa[ct][0][r] = pack_f16(h0, h1);
-      pa[ct][1][r] = pack_f16(x0 - h0, x1 - h1);
-      // value = (z + 1.5 s) + (c - 1.5) s: the midpoint part is summed here,
-      // the centred codes go through the MFMA
-      zsum[ct] = fmaf(pr[0][ct][r], fmaf(1.5f, s0, z0), zsum[ct]);
-      zsum[ct] = fmaf(pr[1][ct][r], fmaf(1.5f, s1, z1), zsum[ct]);
+      const float x0 = fmaf(pf0[r], s0, 0.f), x1 = fmaf(pf1[r], s1, 0.f);
+      // hi = x truncated to fp16, lo = the exact remainder, truncated again
+      const f16x2 hv = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(x0, x1));
+      pa[ct][0][r] = __builtin_bit_cast(uint32_t, hv);
+      pa[ct][1][r] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(mix_sub_lo(x0, hv), mix_sub_hi(x1, hv)));
+      // value = (z + 1.5 s) + (2c - 3) s / 2: the midpoint term here, the
+      // centred term on the MFMA, where its signs keep the accumulation unbiased
+      S.zsum[ct][r] = fmaf(pf0[r], fmaf(1.5f, s0, z0), S.zsum[ct][r]);
+      S.zsum[ct][r] = fmaf(pf1[r], fmaf(1.5f, s1, z1), S.zsum[ct][r]);
     }
   }
-  // ---- PV ----
+  // ---- values on MFMA ----
 #pragma unroll
   for (int kt = 0; kt < 8; ++kt) {
-    const uint32_t w = (kt & 1) ? (vw[kt >> 1] >> 16) : (vw[kt >> 1] & 0xffffu);
-    const uint32_t x = (w & 0xffu) | ((w & 0xff00u) << 8);
-    // centred codes (2c - 3) 2^(2r-24), exact fp16 subnormals: 2 * (c 2^(2r-24)) - 3 2^(2r-24)
+    // channel 8ln + kt: byte kt of this lane's quad, page 0 -> low half, page 1 -> high half
+    const uint32_t lo_src = DV.vw[0][kt >> 2], hi_src = DV.vw[1][kt >> 2];
+    const uint32_t sel = (uint32_t)(kt & 3) | 0x0c00u | ((uint32_t)(4 + (kt & 3)) << 16) | 0x0c000000u;
+    const uint32_t x = __builtin_amdgcn_perm(hi_src, lo_src, sel);
+    // code c at bits 2r of each half is the fp16 subnormal c 2^(2r-24); 2c - 3 is exact
     u32x4 bv;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const f16x2 cv = __builtin_bit_cast(f16x2, x & (0x00030003u << (2 * r)));
-      const _Float16 off = (_Float16)(-3.0f * (float)(1 << (2 * r)) * 5.9604644775390625e-08f);  // -3 2^(2r-24)
+      const _Float16 off = (_Float16)(-3.0f * (float)(1 << (2 * r)) * 0x1p-24f);
       bv[r] = __builtin_bit_cast(uint32_t, cv * (_Float16)2.0f + f16x2{off, off});
     }
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
-      acc[ct][kt] = mfma_f16(pa[ct][0], bv, acc[ct][kt]);
-      acc[ct][kt] = mfma_f16(pa[ct][1], bv, acc[ct][kt]);
+      S.acc[ct][kt] = mfma_f16(pa[ct][0], bv, S.acc[ct][kt]);
+      S.acc[ct][kt] = mfma_f16(pa[ct][1], bv, S.acc[ct][kt]);
     }
   }
 }
 
 template <int NG, int CT>
-__device__ void int2_item(const DecodeParams& p, int b, int kv, int split) {
+__device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float* p_lds, uint8_t* stage) {
   constexpr Int2Layout L{NG};
+  constexpr int HPL = 4 / NG;
   const int lane = threadIdx.x, ln = lane & 15, qd = lane >> 4;
   const int T = p.ctx_lens[b];
   const int lo = p.sink;
   const int hi = T - p.recent;
   const int bk = b * p.n_kv + kv;
-  float m_run[CT], l_run[CT], zsum[CT];
-  f32x4 acc[CT][8];
+  Int2State<NG, CT> S;
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
-    m_run[ct] = kNegInf;
-    l_run[ct] = 0.f;
-    zsum[ct] = 0.f;
 #pragma unroll
-    for (int kt = 0; kt < 8; ++kt) acc[ct][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int hh = 0; hh < HPL; ++hh) {
+      S.moff[ct][hh] = __builtin_huge_valf();
+      S.mx_run[ct][hh] = kNegInf;
+      S.l_run[ct][hh] = 0.f;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) S.zsum[ct][r] = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 8; ++kt) S.acc[ct][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const float* aux = p.qaux + (int64_t)bk * (1 + 32 * CT);
-  const float kfac = aux[0];
-  float qbar2[CT];
-  int qneg3[CT];
-#pragma unroll
-  for (int ct = 0; ct < CT; ++ct) {
-    qbar2[ct] = aux[1 + 16 * ct + ln];
-    qneg3[ct] = __builtin_bit_cast(int, aux[1 + 16 * CT + 16 * ct + ln]);
-  }
+  const float pscale = exp2f(p.p_scale_exp);
   if (hi > lo && lo >= 0) {
     const int first = lo / kPage, last = (hi - 1) / kPage;
     const int n_pages = last - first + 1;
@@ -390,50 +617,106 @@ __device__ void int2_item(const DecodeParams& p, int b, int kv, int split) {
     const int p_begin = first + split * pps;
     const int p_end = min(min(first + n_pages, p_begin + pps), p.max_int2_pages);
     if (p_begin < p_end) {
-      u32x4 bq[CT][3][2];
+      Int2Const<NG, CT> K;
       const u32x4* qb = (const u32x4*)(p.qb + (int64_t)bk * CT * 3 * 2 * 64 * 4);
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
+      for (int ct = 0; ct < CT; ++ct) {
 #pragma unroll
         for (int d = 0; d < 3; ++d)
 #pragma unroll
-          for (int ks = 0; ks < 2; ++ks) bq[ct][d][ks] = qb[((ct * 3 + d) * 2 + ks) * 64 + lane];
-      const float pscale = exp2f(p.p_scale_exp);
+          for (int ks = 0; ks < 2; ++ks) K.qa[ct][d][ks] = qb[((ct * 3 + d) * 2 + ks) * 64 + lane];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          K.qbar2[ct][r] = aux[1 + 16 * ct + 4 * qd + r];
+          K.qneg3[ct][r] = __builtin_bit_cast(int, aux[1 + 16 * CT + 16 * ct + 4 * qd + r]);
+        }
+      }
+      K.kfac = aux[0];
+      K.ikfac = 1.0f / K.kfac;
+      K.lpf = p.p_scale_exp - (float)(2 * (ln & 3));
       const int32_t* bt = p.int2_bt + (int64_t)b * p.max_int2_pages;
       const int64_t npg = p.n_int2_pages;
-      for (int lp0 = p_begin; lp0 < p_end; lp0 += 2) {
+      const uint8_t* base = p.int2_pages;
+      const int n_kv = p.n_kv;
+      const Int2Offsets off = int2_offsets<NG>();
+      auto blk = [&](int pg) { return base + ((int64_t)pg * n_kv + kv) * (int64_t)L.bytes(); };
+      auto ok = [&](int pg) { return pg >= 0 && pg < npg; };
+      // masked pair: partial pages at the region edges, odd tails, bad page ids
+      auto edge = [&](int lp0) {
         const bool has1 = lp0 + 1 < p_end;
         int pg0 = bt[lp0];
         int pg1 = has1 ? bt[lp0 + 1] : pg0;
-        const bool ok0 = pg0 >= 0 && pg0 < npg;
-        const bool ok1 = pg1 >= 0 && pg1 < npg;
+        const bool ok0 = ok(pg0), ok1 = ok(pg1);
         if (!ok0) pg0 = 0;
         if (!ok1) pg1 = pg0;
-        const uint8_t* blk0 = block_ptr(p.int2_pages, pg0, p.n_kv, kv, L.bytes());
-        const uint8_t* blk1 = block_ptr(p.int2_pages, pg1, p.n_kv, kv, L.bytes());
-        const bool interior = has1 && ok0 && ok1 && lp0 * kPage >= lo && (lp0 + 2) * kPage <= hi;
-        if (interior) {
-          int2_pair<NG, CT, false>(p, blk0, blk1, lp0, p_end, lo, hi, bq, qbar2, qneg3, kfac, pscale, m_run, l_run, zsum,
-                                   acc);
-        } else {
-          // pages with a bad id are masked out entirely
-          const int lo_e = lo, hi_e = hi;
-          const int pe = ok0 ? (ok1 ? p_end : lp0 + 1) : lp0;
-          int2_pair<NG, CT, true>(p, blk0, blk1, lp0, pe, lo_e, hi_e, bq, qbar2, qneg3, kfac, pscale, m_run, l_run, zsum,
-                                  acc);
-        }
+        const int pe = ok0 ? (ok1 ? p_end : lp0 + 1) : lp0;
+        const Int2Data<NG> D = int2_load<NG>(blk(pg0), blk(pg1), off);
+        int2_pair<NG, CT, true>(D, lp0, pe, lo, hi, K, S, p_lds);
+      };
+      int lp0 = p_begin;
+      if (lp0 * kPage < lo) {
+        edge(lp0);
+        lp0 += 2;
       }
+      // interior pairs (both pages fully inside [lo, hi)), staged in LDS one
+      // pair ahead: two slots, the loop unrolled by two so the slots are fixed.
+      // Page ids come 64 at a time, one per lane, and a pair takes its two ids
+      // with v_readlane: no memory access and no wait inside the pair loop.
+      // Each chunk ends with its staging loads drained.
+      const int main_end = min(p_end, hi / kPage);
+      uint8_t* const st0 = stage;
+      uint8_t* const st1 = stage + 2 * L.bytes();
+      const uint32_t a0 = lds_address(st0), a1 = lds_address(st1);
+      while (lp0 + 2 <= main_end) {
+        const int c0 = lp0;
+        const int cn = min(64, main_end - c0);
+        const int id = lane < cn ? bt[c0 + lane] : 0;
+        const uint64_t bad = __builtin_amdgcn_ballot_w64(lane < cn && !ok(id));
+        const int lim = bad ? c0 + (int)__builtin_ctzll(bad) : c0 + cn;  // pages [c0, lim) have good ids
+        if (lp0 + 2 > lim) break;
+        // every earlier vector load (operands, ids, edge pages) completes here,
+        // where the compiler sees it, so it adds no wait inside the pair loop
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        auto page = [&](int l) { return blk(__builtin_amdgcn_readlane(id, l - c0)); };
+        int2_issue<NG>(page(lp0), page(lp0 + 1), a0);
+        for (;;) {
+          bool nx = lp0 + 4 <= lim;
+          if (nx) {
+            int2_issue<NG>(page(lp0 + 2), page(lp0 + 3), a1);
+            vm_wait<4>();
+          } else {
+            vm_wait<0>();
+          }
+          int2_pair<NG, CT, false>(Int2Staged<NG>{st0, off}, lp0, p_end, lo, hi, K, S, p_lds);
+          lp0 += 2;
+          if (!nx) break;
+          nx = lp0 + 4 <= lim;
+          if (nx) {
+            int2_issue<NG>(page(lp0 + 2), page(lp0 + 3), a0);
+            vm_wait<4>();
+          } else {
+            vm_wait<0>();
+          }
+          int2_pair<NG, CT, false>(Int2Staged<NG>{st1, off}, lp0, p_end, lo, hi, K, S, p_lds);
+          lp0 += 2;
+          if (!nx) break;
+        }
+        if (lim < c0 + cn) break;  // a bad id: the rest goes through the masked path
+      }
+      for (; lp0 < p_end; lp0 += 2) edge(lp0);
     }
   }
-  // ---- finalize: reduce per-lane partials, undo scales, write partials ----
-  const int S = p.splits_int2 + p.splits_bf16;
+  // ---- finalize ----
+  const int Ssp = p.splits_int2 + p.splits_bf16;
   const float accscale = exp2f(23.f - p.p_scale_exp);  // MFMA sums p s (2c - 3) 2^(sp-24)
+  const float ipscale = 1.0f / pscale;
   constexpr int G = kHeadDim / NG;
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
-    const float l = sum_across_quads(l_run[ct]);
-    const float z = sum_across_quads(zsum[ct]);
-    // rows of this lane in the PV accumulator: (h, gamma) = 16ct + 4qd + r
+    float z = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) z = fmaf(S.zsum[ct][r], (float)(1 << (2 * r)) * ipscale, z);
+    z = sum_across_quads(z);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float zr = __shfl(z, 4 * qd + r);
@@ -443,16 +726,21 @@ __device__ void int2_item(const DecodeParams& p, int b, int kv, int split) {
       for (int kt = 0; kt < 8; ++kt) {
         const int ch = 8 * ln + kt;
         if (h < p.g && ch / G == gam_row) {
-          float* dst = p.partial + (((int64_t)b * p.n_q + kv * p.g + h) * S + split) * kPartialStride;
-          dst[2 + ch] = fmaf(acc[ct][kt][r], accscale, zr);
+          float* dst = p.partial + (((int64_t)b * p.n_q + kv * p.g + h) * Ssp + split) * kPartialStride;
+          dst[2 + ch] = fmaf(S.acc[ct][kt][r], accscale, zr);
         }
       }
     }
-    const int col = 16 * ct + ln, h = col / NG;
-    if (qd == 0 && col % NG == 0 && h < p.g) {
-      float* dst = p.partial + (((int64_t)b * p.n_q + kv * p.g + h) * S + split) * kPartialStride;
-      dst[0] = m_run[ct];
-      dst[1] = l;
+#pragma unroll
+    for (int hh = 0; hh < HPL; ++hh) {
+      const float lpf = p.p_scale_exp - (float)(2 * (ln & 3));
+      const float l = row_sum16(S.l_run[ct][hh] * exp2f(-lpf));
+      const int h = (16 * ct + 4 * qd + hh * NG) / NG;
+      if (ln == 0 && h < p.g) {
+        float* dst = p.partial + (((int64_t)b * p.n_q + kv * p.g + h) * Ssp + split) * kPartialStride;
+        dst[0] = lpf - S.moff[ct][hh];  // -inf when this split saw no token
+        dst[1] = l;
+      }
     }
   }
 }
@@ -617,17 +905,23 @@ __device__ void bf16_item(const DecodeParams& p, int b, int kv, int split) {
   }
 }
 
+// register budget: one row tile fits 4 wavefronts per SIMD; wider GQA groups need more
 template <int NG, int CT>
-__global__ __launch_bounds__(64) void decode_main(DecodeParams p) {
-  const int S = p.splits_int2 + p.splits_bf16;
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(CT == 1 ? 3 : (CT == 2 ? 2 : 1), 8))) void
+decode_int2(DecodeParams p) {
+  __shared__ __attribute__((aligned(16))) float p_lds[16 * 32];
+  __shared__ __attribute__((aligned(16))) uint8_t stage[4 * Int2Layout{NG}.bytes()];
   const int item = blockIdx.x;
-  const int split = item % S;
-  const int bk = item / S;
-  const int kv = bk % p.n_kv, b = bk / p.n_kv;
-  if (split < p.splits_int2)
-    int2_item<NG, CT>(p, b, kv, split);
-  else
-    bf16_item(p, b, kv, split);
+  const int split = item % p.splits_int2;
+  const int bk = item / p.splits_int2;
+  int2_item<NG, CT>(p, bk / p.n_kv, bk % p.n_kv, split, p_lds, stage);
+}
+
+__global__ __launch_bounds__(64) void decode_bf16(DecodeParams p) {
+  const int item = blockIdx.x;
+  const int sb = item % p.splits_bf16;
+  const int bk = item / p.splits_bf16;
+  bf16_item(p, bk / p.n_kv, bk % p.n_kv, p.splits_int2 + sb);
 }
 
 // ---------------------------------------------------------------------------
@@ -684,22 +978,26 @@ __global__ __launch_bounds__(128) void decode_combine(DecodeParams p) {
 template <int NG, int CT>
 hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
   const int bkn = p.batch * p.n_kv;
-  const int S = p.splits_int2 + p.splits_bf16;
-  if (p.splits_int2 > 0) {
+  // the event pair brackets the dominant kernel: the INT2 stream when there is
+  // one, else the bf16 stream
+  const bool int2 = p.splits_int2 > 0;
+  auto mark = [&](hipEvent_t ev) { return ev ? hipEventRecord(ev, stream) : hipSuccess; };
+  hipError_t e = hipSuccess;
+  if (int2) {
     hipLaunchKernelGGL((decode_prologue<NG, CT>), dim3(bkn), dim3(128), 0, stream, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if (ev_start) {
-    hipError_t e = hipEventRecord(ev_start, stream);
-    if (e != hipSuccess) return e;
+  if (p.splits_bf16 > 0) {
+    if (!int2 && (e = mark(ev_start)) != hipSuccess) return e;
+    hipLaunchKernelGGL(decode_bf16, dim3(bkn * p.splits_bf16), dim3(64), 0, stream, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (!int2 && (e = mark(ev_stop)) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((decode_main<NG, CT>), dim3(bkn * S), dim3(64), 0, stream, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (ev_stop) {
-    e = hipEventRecord(ev_stop, stream);
-    if (e != hipSuccess) return e;
+  if (int2) {
+    if ((e = mark(ev_start)) != hipSuccess) return e;
+    hipLaunchKernelGGL((decode_int2<NG, CT>), dim3(bkn * p.splits_int2), dim3(64), 0, stream, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = mark(ev_stop)) != hipSuccess) return e;
   }
   hipLaunchKernelGGL(decode_combine, dim3(bkn), dim3(128), 0, stream, p);
   return hipGetLastError();

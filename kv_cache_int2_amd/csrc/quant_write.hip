@@ -18,10 +18,12 @@
 // division, rint = nearest-even).
 //
 // Storage (per (page, KV head) block): K codes token-major (a token's 32 bytes
-// are its own), V codes channel-major 16-bit words [2][128] (8 tokens of one
-// channel per word).  V words are written whole when this wavefront holds all
-// 8 tokens of that half page, else merged with 32-bit atomic and/or, so tokens
-// of one page may be written by different wavefronts or launches.
+// are its own) with token-major scale/zero, V codes by token quad [4][128]
+// bytes (byte j of quad q: channel j of tokens 4q..4q+3) with group-major
+// scale/zero.  A V dword (4 channels of one quad) is written whole when this
+// wavefront holds all 4 tokens of the quad, else merged with 32-bit atomic
+// and/or, so tokens of one page may be written by different wavefronts or
+// launches.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -187,7 +189,8 @@ __global__ __launch_bounds__(64) void quant_write_kernel(QuantParams p) {
       const int64_t page = dst[t] / kPage;
       const int slot = dst[t] % kPage;
       uint8_t* blk = pages + (page * p.n_kv + kv) * blk_bytes;
-      *(uint32_t*)(blk + (isv ? L.v_sz() : L.k_sz()) + (gm * kPage + slot) * 4) = szs[t][gm];
+      const int idx = isv ? (gm * kPage + slot) : (slot * NG + gm);  // V group-major, K token-major
+      *(uint32_t*)(blk + (isv ? L.v_sz() : L.k_sz()) + idx * 4) = szs[t][gm];
     }
   }
   if (!isv) {
@@ -203,17 +206,17 @@ __global__ __launch_bounds__(64) void quant_write_kernel(QuantParams p) {
       *(uint2*)(blk + L.k_codes() + slot * 32 + 8 * part) = make_uint2(w[0], w[1]);
     }
   } else {
-    // V codes: lane -> channel pair (2*lane, 2*lane+1); runs of tokens sharing
-    // a (page, half) are merged into one 32-bit word per lane.
-    const int jp = lane;
+    // V codes: lane -> dword jd (channels 4jd..4jd+3) for the tokens of half th
+    // of the 16; runs of tokens sharing a (page, quad) merge into one word.
+    const int jd = lane & 31, th = lane >> 5;
     int64_t key = -1;
     uint32_t mask = 0u, bits = 0u;
     auto flush = [&](int64_t k, uint32_t msk, uint32_t bts) {
       if (k < 0 || msk == 0u) return;
-      const int64_t page = k >> 1;
-      const int a = (int)(k & 1);
+      const int64_t page = k >> 2;
+      const int q = (int)(k & 3);
       uint8_t* blk = pages + (page * p.n_kv + kv) * blk_bytes;
-      uint32_t* word = (uint32_t*)(blk + L.v_codes() + (a * kHeadDim + 2 * jp) * 2);
+      uint32_t* word = (uint32_t*)(blk + L.v_codes() + q * kHeadDim + 4 * jd);
       if (msk == 0xffffffffu) {
         *word = bts;
       } else {
@@ -221,19 +224,22 @@ __global__ __launch_bounds__(64) void quant_write_kernel(QuantParams p) {
         atomicOr(word, bts);
       }
     };
-    for (int t = 0; t < 16; ++t) {
+    for (int t = 8 * th; t < 8 * th + 8; ++t) {
       const int32_t sl = dst[t];
       if (sl < 0) continue;
-      const int64_t k = (int64_t)(sl / kPage) * 2 + ((sl % kPage) >> 3);
+      const int64_t k = (int64_t)(sl / kPage) * 4 + ((sl % kPage) >> 2);
       if (k != key) {
         flush(key, mask, bits);
         key = k;
         mask = 0u;
         bits = 0u;
       }
-      const int i = sl & 7;
-      mask |= (3u << (2 * i)) | (3u << (16 + 2 * i));
-      bits |= ((uint32_t)codes[t][2 * jp] << (2 * i)) | ((uint32_t)codes[t][2 * jp + 1] << (16 + 2 * i));
+      const int i = sl & 3;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        mask |= 3u << (8 * c + 2 * i);
+        bits |= (uint32_t)codes[t][4 * jd + c] << (8 * c + 2 * i);
+      }
     }
     flush(key, mask, bits);
   }

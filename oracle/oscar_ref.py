@@ -366,11 +366,11 @@ def decode_attention(q_bits: np.ndarray, st: StoredRequest, cal: LayerCalibratio
 # INT2 page block, d channels, NG = d / G groups, 16 tokens:
 #   [0, 16*d/4)          K codes, token-major: token t owns d/4 bytes;
 #                        channel j sits in byte j//4 at bits 2*(j%4).
-#   next 16*NG*4 bytes   K scale/zero as fp16 pairs [NG][16][(s, z)].
-#   next 16*d/4 bytes    V codes, channel-major 16-bit words [2][d]:
-#                        word [a][j] holds channel j of tokens 8a..8a+7,
-#                        token 8a+i at bits 2*i.
-#   next 16*NG*4 bytes   V scale/zero, same layout as K.
+#   next 16*NG*4 bytes   K scale/zero as fp16 pairs, token-major [16][NG][(s, z)].
+#   next 16*d/4 bytes    V codes, [4][d] bytes by token quad: byte [q][j]
+#                        holds channel j of tokens 4q..4q+3, token 4q+i at
+#                        bits 2*i.
+#   next 16*NG*4 bytes   V scale/zero as fp16 pairs, group-major [NG][16][(s, z)].
 # BF16 page block: K as [16][d] bf16 (token-major), then V as [d][16] bf16
 # (channel-major).
 # ---------------------------------------------------------------------------
@@ -383,10 +383,10 @@ def bf16_block_bytes(d: int) -> int:
     return 2 * PAGE * d * 2
 
 
-def _pack_sz(s: np.ndarray, z: np.ndarray) -> np.ndarray:
-    # s, z: [16, NG] float16 -> bytes of [NG][16][2] fp16
-    pair = np.stack([s.T, z.T], axis=-1).astype(np.float16)
-    return pair.view(np.uint8).ravel()
+def _pack_sz(s: np.ndarray, z: np.ndarray, token_major: bool) -> np.ndarray:
+    # s, z: [16, NG] float16 -> bytes of [16][NG][2] (token-major) or [NG][16][2] fp16
+    pair = np.stack([s, z] if token_major else [s.T, z.T], axis=-1).astype(np.float16)
+    return np.ascontiguousarray(pair).view(np.uint8).ravel()
 
 
 def pack_int2_block(kc, ks, kz, vc, vs, vz) -> np.ndarray:
@@ -398,11 +398,12 @@ def pack_int2_block(kc, ks, kz, vc, vs, vz) -> np.ndarray:
     kbytes = np.zeros((PAGE, d // 4), np.uint8)
     for i in range(4):
         kbytes |= (kc[:, i::4] << (2 * i)).astype(np.uint8)
-    vwords = np.zeros((2, d), np.uint16)
-    for a in range(2):
-        for i in range(8):
-            vwords[a] |= (vc[8 * a + i, :].astype(np.uint16) << (2 * i)).astype(np.uint16)
-    return np.concatenate([kbytes.ravel(), _pack_sz(ks, kz), vwords.view(np.uint8).ravel(), _pack_sz(vs, vz)])
+    vbytes = np.zeros((4, d), np.uint8)
+    for q in range(4):
+        for i in range(4):
+            vbytes[q] |= (vc[4 * q + i, :] << (2 * i)).astype(np.uint8)
+    return np.concatenate([kbytes.ravel(), _pack_sz(ks, kz, True), vbytes.ravel(),
+                           _pack_sz(vs, vz, False)])
 
 
 def unpack_int2_block(buf: np.ndarray, d: int, group: int):
@@ -416,13 +417,13 @@ def unpack_int2_block(buf: np.ndarray, d: int, group: int):
     for i in range(4):
         kc[:, i::4] = (kb >> (2 * i)) & 3
     o = nc
-    ksz = buf[o:o + nsz].copy().view(np.float16).reshape(ng, PAGE, 2)
+    ksz = buf[o:o + nsz].copy().view(np.float16).reshape(PAGE, ng, 2).transpose(1, 0, 2)
     o += nsz
-    vw = buf[o:o + nc].copy().view(np.uint16).reshape(2, d)
+    vb = buf[o:o + nc].reshape(4, d)
     vc = np.zeros((PAGE, d), np.uint8)
-    for a in range(2):
-        for i in range(8):
-            vc[8 * a + i] = (vw[a] >> (2 * i)) & 3
+    for q in range(4):
+        for i in range(4):
+            vc[4 * q + i] = (vb[q] >> (2 * i)) & 3
     o += nc
     vsz = buf[o:o + nsz].copy().view(np.float16).reshape(ng, PAGE, 2)
     return kc, ksz[:, :, 0].T, ksz[:, :, 1].T, vc, vsz[:, :, 0].T, vsz[:, :, 1].T

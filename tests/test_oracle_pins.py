@@ -299,16 +299,22 @@ def test_p7_int2_block_layout_by_hand():
     vc[9, 127] = 2                                                   # token 9, channel 127
     ks = np.full((16, 4), np.float16(0.5))
     kz = np.full((16, 4), np.float16(-1.0))
-    blk = O.pack_int2_block(kc, ks, kz, vc, ks, kz)
+    ks[7, 2] = np.float16(3.0)                                       # token 7, group 2
+    vs = np.full((16, 4), np.float16(0.25))
+    vs[7, 2] = np.float16(5.0)
+    blk = O.pack_int2_block(kc, ks, kz, vc, vs, kz)
     assert blk.size == O.int2_block_bytes(d, group) == 1536
     assert np.all(blk[:512] == 0xE4)                                 # 0b11_10_01_00
-    sz = blk[512:768].view(np.float16).reshape(4, 16, 2)
-    assert np.all(sz[:, :, 0] == 0.5) and np.all(sz[:, :, 1] == -1.0)
-    vw = blk[768:1280].view(np.uint16).reshape(2, d)
-    assert vw[0, 5] == 3 << 6 and vw[1, 127] == 2 << 2
-    assert np.count_nonzero(vw) == 2
+    ksz = blk[512:768].view(np.float16)                              # K: [token][group][(s, z)]
+    assert ksz[(7 * 4 + 2) * 2] == 3.0 and ksz[(7 * 4 + 2) * 2 + 1] == -1.0
+    assert np.count_nonzero(ksz[0::2] == 0.5) == 63
+    vsz = blk[1280:1536].view(np.float16)                            # V: [group][token][(s, z)]
+    assert vsz[(2 * 16 + 7) * 2] == 5.0 and np.count_nonzero(vsz[0::2] == 0.25) == 63
+    vb = blk[768:1280].reshape(4, d)                                 # V: [token quad][channel]
+    assert vb[0, 5] == 3 << 6 and vb[2, 127] == 2 << 2
+    assert np.count_nonzero(vb) == 2
     back = O.unpack_int2_block(blk, d, group)
-    for a, b in zip(back, (kc, ks, kz, vc, ks, kz)):
+    for a, b in zip(back, (kc, ks, kz, vc, vs, kz)):
         assert np.array_equal(a, b)
 
 
