@@ -146,6 +146,26 @@ __device__ __forceinline__ const uint8_t* block_ptr(const uint8_t* base, int64_t
   return base + ((page * n_kv + kv) * (int64_t)bytes);
 }
 
+// A 128 x 128 fp32 matrix to LDS by a block of 256 threads, row stride
+// `stride` floats: 16 independent 16-byte loads per thread, all issued before
+// the first store.
+template <int Stride>
+__device__ __forceinline__ void stage_matrix256(const float* src, float* lds) {
+  const float4* R = (const float4*)src;
+  float4 v[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) v[k] = R[threadIdx.x + 256 * k];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int e = threadIdx.x + 256 * k;
+    float* d = lds + (e >> 5) * Stride + 4 * (e & 31);
+    d[0] = v[k].x;
+    d[1] = v[k].y;
+    d[2] = v[k].z;
+    d[3] = v[k].w;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // prologue: q R_K operands
 // ---------------------------------------------------------------------------
@@ -153,31 +173,59 @@ __device__ __forceinline__ const uint8_t* block_ptr(const uint8_t* base, int64_t
 // then aux floats [1 + 32*CT]: logit factor 2^-sq / 2, per row 2*Qbar (float),
 // per row -3*Qbar (int32 bits).
 template <int NG, int CT>
-__global__ __launch_bounds__(128) void decode_prologue(DecodeParams p) {
+__global__ __launch_bounds__(256) void decode_prologue(DecodeParams p) {
   const int bk = blockIdx.x;
   const int b = bk / p.n_kv, kv = bk % p.n_kv;
-  const int j = threadIdx.x;
+  const int t = threadIdx.x, j = t & (kHeadDim - 1), hf = t >> 7;
   constexpr int G = kHeadDim / NG;
+  __shared__ float rk[kHeadDim * kHeadDim];
   __shared__ float qs[16][kHeadDim];
   __shared__ int qi[16][kHeadDim];
   __shared__ float red[4];
   const int g = p.g;
-  for (int h = 0; h < g; ++h)
-    qs[h][j] = bf16_val(p.q[((int64_t)b * p.n_q + kv * g + h) * kHeadDim + j]);
+  stage_matrix256<kHeadDim>(p.r_k + (int64_t)kv * kHeadDim * kHeadDim, rk);
+  for (int e = t; e < g * kHeadDim; e += 256)
+    qs[e >> 7][e & (kHeadDim - 1)] = bf16_val(p.q[((int64_t)b * p.n_q + kv * g) * kHeadDim + e]);
   __syncthreads();
-  const float* R = p.r_k + (int64_t)kv * kHeadDim * kHeadDim;
-  float qt[16];
-  float mx = 0.f;
-  for (int h = 0; h < g; ++h) {
-    float acc = 0.f;
-    for (int i = 0; i < kHeadDim; ++i) acc = fmaf(qs[h][i], R[i * kHeadDim + j], acc);
-    qt[h] = acc * kLog2eOverSqrtD;
-    mx = fmaxf(mx, fabsf(qt[h]));
+  // q~[h][j]: this thread sums inputs i in [64 hf, 64 hf + 64) for every head
+  // (q read four inputs at a time); the halves exchange partial sums through
+  // LDS and each thread keeps the heads h = hf, hf + 2, ...
+  float acc[16];
+#pragma unroll
+  for (int h = 0; h < 16; ++h) acc[h] = 0.f;
+  for (int i = 64 * hf; i < 64 * hf + 64; i += 4) {
+    const float r0 = rk[i * kHeadDim + j], r1 = rk[(i + 1) * kHeadDim + j];
+    const float r2 = rk[(i + 2) * kHeadDim + j], r3 = rk[(i + 3) * kHeadDim + j];
+#pragma unroll
+    for (int h = 0; h < 16; ++h) {
+      if (h < g) {
+        const float4 q4 = *(const float4*)&qs[h][i];
+        acc[h] = fmaf(q4.w, r3, fmaf(q4.z, r2, fmaf(q4.y, r1, fmaf(q4.x, r0, acc[h]))));
+      }
+    }
   }
-  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-  if ((j & 63) == 0) red[j >> 6] = mx;
+  __syncthreads();  // qs becomes the exchange: each half publishes the heads the other keeps
+#pragma unroll
+  for (int h = 0; h < 16; ++h)
+    if (h < g && (h & 1) != hf) qs[h][j] = acc[h];
   __syncthreads();
-  mx = fmaxf(red[0], red[1]);
+  float qt[8];
+  float mx = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int h = hf + 2 * k;
+    qt[k] = 0.f;
+    if (h < g) {
+      const float own = hf ? acc[2 * k + 1] : acc[2 * k];  // hf is uniform per wavefront
+      qt[k] = (own + qs[h][j]) * kLog2eOverSqrtD;
+      mx = fmaxf(mx, fabsf(qt[k]));
+    }
+  }
+
+  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  if ((t & 63) == 0) red[t >> 6] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   // 2^sq brings the largest |q~| to [2^20, 2^21), so |2Q| <= 2^22 fits three
   // balanced int8 digits
   int sq = 0;
@@ -186,20 +234,22 @@ __global__ __launch_bounds__(128) void decode_prologue(DecodeParams p) {
     frexpf(mx, &e);  // mx in [2^(e-1), 2^e)
     sq = min(21 - e, 100);  // keeps the logit factor 2^-sq / 2 a normal float
   }
-  for (int h = 0; h < g; ++h) qi[h][j] = (int)rintf(ldexpf(qt[h], sq));
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    if (hf + 2 * k < g) qi[hf + 2 * k][j] = (int)rintf(ldexpf(qt[k], sq));
   __syncthreads();
   float* aux = p.qaux + (int64_t)bk * (1 + 32 * CT);
-  if (j == 0) aux[0] = ldexpf(0.5f, -sq);
-  if (j < 16 * CT) {
-    const int h = j / NG, gam = j % NG;
+  if (t == 0) aux[0] = ldexpf(0.5f, -sq);
+  if (t < 16 * CT) {
+    const int h = t / NG, gam = t % NG;
     int sum = 0;
     if (h < g)
       for (int c = gam * G; c < (gam + 1) * G; ++c) sum += qi[h][c];
-    aux[1 + j] = 2.0f * (float)sum;
-    aux[1 + 16 * CT + j] = __builtin_bit_cast(float, -3 * sum);
+    aux[1 + t] = 2.0f * (float)sum;
+    aux[1 + 16 * CT + t] = __builtin_bit_cast(float, -3 * sum);
   }
   uint32_t* qb = p.qb + (int64_t)bk * CT * 3 * 2 * 64 * 4;
-  for (int w = j; w < CT * 3 * 2 * 64 * 4; w += 128) {
+  for (int w = t; w < CT * 3 * 2 * 64 * 4; w += 256) {
     const int reg = w & 3, lane = (w >> 2) & 63, ks = (w >> 8) & 1, rest = w >> 9;
     const int digit = rest % 3, ct = rest / 3;
     const int ln = lane & 15, qd = lane >> 4;
@@ -927,50 +977,107 @@ __global__ __launch_bounds__(64) void decode_bf16(DecodeParams p) {
 // ---------------------------------------------------------------------------
 // combine: LSE merge, R_V^T on the INT2 part, normalisation
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(128) void decode_combine(DecodeParams p) {
+// One block of 256 threads per (request, KV head).  R_V is staged once in LDS
+// with a row stride of 129 floats, so thread j reading row j at column i hits
+// bank (j + i) % 32: no conflicts.  Split weights are recomputed where used.
+constexpr int kRvStride = kHeadDim + 1;
+
+__device__ __forceinline__ float block_max256(float x, float* red) {
+  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  x = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  return x;
+}
+__device__ __forceinline__ float block_sum256(float x, float* red) {
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  x = (red[0] + red[1]) + (red[2] + red[3]);
+  __syncthreads();
+  return x;
+}
+
+__global__ __launch_bounds__(256) void decode_combine(DecodeParams p) {
+  __shared__ float rv[kHeadDim * kRvStride];
+  __shared__ float half_sum[3][2][kHeadDim];
+  __shared__ float aint[kHeadDim];
+  __shared__ float wts[256];
+  __shared__ float red[4];
   const int bk = blockIdx.x;
   const int b = bk / p.n_kv, kv = bk % p.n_kv;
-  const int j = threadIdx.x;
+  const int t = threadIdx.x, j = t & (kHeadDim - 1), hf = t >> 7;
   const int S = p.splits_int2 + p.splits_bf16;
-  __shared__ float ai[kHeadDim];
-  const float* R = p.r_v + (int64_t)kv * kHeadDim * kHeadDim;
+  if (p.splits_int2 > 0) stage_matrix256<kRvStride>(p.r_v + (int64_t)kv * kHeadDim * kHeadDim, rv);
+  __syncthreads();
   for (int h = 0; h < p.g; ++h) {
     const int hq = kv * p.g + h;
     const float* base = p.partial + ((int64_t)b * p.n_q + hq) * S * kPartialStride;
-    float M = kNegInf;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, base[s * kPartialStride]);
-    float o = 0.f;
-    float aint = 0.f, abf = 0.f, L = 0.f;
-    if (M != kNegInf) {
-      for (int s = 0; s < S; ++s) {
+    float m = kNegInf;
+    for (int s = t; s < S; s += 256) m = fmaxf(m, base[s * kPartialStride]);
+    const float M = block_max256(m, red);
+    float l = 0.f;
+    if (M != kNegInf)
+      for (int s = t; s < S; s += 256) {
         const float ms = base[s * kPartialStride];
-        const float w = (ms == kNegInf) ? 0.f : exp2f(ms - M);
-        L = fmaf(w, base[s * kPartialStride + 1], L);
-        const float v = w == 0.f ? 0.f : w * base[s * kPartialStride + 2 + j];
-        if (s < p.splits_int2)
-          aint += v;
-        else
-          abf += v;
+        if (ms != kNegInf) l = fmaf(exp2f(ms - M), base[s * kPartialStride + 1], l);
       }
-    }
-    ai[j] = aint;
-    __syncthreads();
+    const float L = block_sum256(l, red);
+    // weighted sums of the partial rows: this thread takes channel j of every
+    // other split (half hf), separately for the INT2 and the bf16 splits; the
+    // weights of 256 splits at a time go through LDS so the row loads are
+    // independent of each other
+    float ai = 0.f, ab = 0.f;
     if (M != kNegInf) {
-      float r = 0.f;
-      if (p.splits_int2 > 0) {
-        const float4* row = (const float4*)(R + j * kHeadDim);
-#pragma unroll 8
-        for (int i = 0; i < kHeadDim / 4; ++i) {
-          const float4 rv = row[i];
-          r = fmaf(ai[4 * i], rv.x, r);
-          r = fmaf(ai[4 * i + 1], rv.y, r);
-          r = fmaf(ai[4 * i + 2], rv.z, r);
-          r = fmaf(ai[4 * i + 3], rv.w, r);
+      for (int c0 = 0; c0 < S; c0 += 256) {
+        const int cn = min(256, S - c0);
+        if (t < cn) {
+          const float ms = base[(c0 + t) * kPartialStride];
+          wts[t] = ms == kNegInf ? 0.f : exp2f(ms - M);  // a split without tokens has zero rows
         }
+        __syncthreads();
+        const int si = max(0, min(cn, p.splits_int2 - c0));  // INT2 splits of this chunk
+        int s = hf;
+        for (; s + 6 < si; s += 8) {
+          float x[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) x[u] = base[(c0 + s + 2 * u) * kPartialStride + 2 + j];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) ai = fmaf(wts[s + 2 * u], x[u], ai);
+        }
+        for (; s < si; s += 2) ai = fmaf(wts[s], base[(c0 + s) * kPartialStride + 2 + j], ai);
+        for (; s + 6 < cn; s += 8) {
+          float x[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) x[u] = base[(c0 + s + 2 * u) * kPartialStride + 2 + j];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) ab = fmaf(wts[s + 2 * u], x[u], ab);
+        }
+        for (; s < cn; s += 2) ab = fmaf(wts[s], base[(c0 + s) * kPartialStride + 2 + j], ab);
+        __syncthreads();
       }
-      o = (r + abf) / L;
     }
-    p.out[((int64_t)b * p.n_q + hq) * kHeadDim + j] = o;
+    half_sum[0][hf][j] = ai;
+    half_sum[1][hf][j] = ab;
+    __syncthreads();
+    if (hf == 0) aint[j] = half_sum[0][0][j] + half_sum[0][1][j];
+    __syncthreads();
+    // R_V^T on the INT2 part: out_j = sum_i aint_i R_V[j][i], i split over the halves
+    float r = 0.f;
+    if (p.splits_int2 > 0) {
+      const float* row = rv + j * kRvStride + 64 * hf;
+      const float* a = aint + 64 * hf;
+#pragma unroll 16
+      for (int i = 0; i < 64; ++i) r = fmaf(a[i], row[i], r);
+    }
+    half_sum[2][hf][j] = r;
+    __syncthreads();
+    if (hf == 0) {
+      const float abf = half_sum[1][0][j] + half_sum[1][1][j];
+      const float o = (M == kNegInf) ? 0.f : ((half_sum[2][0][j] + half_sum[2][1][j]) + abf) / L;
+      p.out[((int64_t)b * p.n_q + hq) * kHeadDim + j] = o;
+    }
     __syncthreads();
   }
 }
@@ -984,7 +1091,7 @@ hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream, hipEvent_t
   auto mark = [&](hipEvent_t ev) { return ev ? hipEventRecord(ev, stream) : hipSuccess; };
   hipError_t e = hipSuccess;
   if (int2) {
-    hipLaunchKernelGGL((decode_prologue<NG, CT>), dim3(bkn), dim3(128), 0, stream, p);
+    hipLaunchKernelGGL((decode_prologue<NG, CT>), dim3(bkn), dim3(256), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (p.splits_bf16 > 0) {
@@ -999,7 +1106,7 @@ hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream, hipEvent_t
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = mark(ev_stop)) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(decode_combine, dim3(bkn), dim3(128), 0, stream, p);
+  hipLaunchKernelGGL(decode_combine, dim3(bkn), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

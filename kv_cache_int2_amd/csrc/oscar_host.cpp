@@ -733,10 +733,12 @@ static const int kAutoMaxSplits = 64;
 
 int32_t oscar_decode_auto_splits(const oscar_shape* shape, int32_t batch, int32_t max_int2_pages) {
   if (check_shape(shape) != OSCAR_OK || batch < 1) return 1;
+  // about 12 work items per SIMD (1024 SIMDs on 256 compute units: four rounds
+  // of three resident wavefronts), each split keeping at least 16 page pairs
   const int64_t pairs = (int64_t)batch * shape->n_kv_heads;
-  const int64_t target = 256 * 8;  // work items: 8 wavefronts per compute unit
+  const int64_t target = 1024 * 12;
   int64_t s = (target + pairs - 1) / pairs;
-  s = std::min<int64_t>(s, std::max<int64_t>(1, max_int2_pages / 8));
+  s = std::min<int64_t>(s, std::max<int64_t>(1, max_int2_pages / 32));
   s = std::max<int64_t>(1, std::min<int64_t>(s, kAutoMaxSplits));
   return (int32_t)s;
 }

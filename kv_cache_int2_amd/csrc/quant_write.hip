@@ -7,8 +7,12 @@
 // scale and zero point.  [IT] 2.2.B: the history lives in INT2 after the fixed
 // rotation and clip.
 //
-// One wavefront handles 16 tokens of one KV head and one of K / V:
-//   x_rot[16][128] = X[16][128] R[128][128]   on v_mfma_f64_16x16x4_f64.
+// One block of eight wavefronts handles 16 tokens of one KV head and one of
+// K / V:  x_rot[16][128] = X[16][128] R[128][128]  on v_mfma_f64_16x16x4_f64,
+// wavefront w producing columns 16w..16w+15 (its 32 values of R are loaded
+// together, so the block waits for memory once); then 8 (G=32) or 16 (G=64)
+// threads per (token, group) clip, reduce min/max with shuffles and code 4
+// channels each.
 // X holds bf16 values and R fp32 values; both are exact in fp64 and so are
 // their products, and the sums are fp64.  The quantiser's decisions (fp16
 // rounding of scale and zero, the code of each element) are therefore taken on
@@ -75,10 +79,12 @@ __device__ __forceinline__ double f16_bits_to_f64(uint16_t h) {
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __builtin_bit_cast(float, (uint32_t)b << 16); }
 
 template <int MODE, int NG>
-__global__ __launch_bounds__(64) void quant_write_kernel(QuantParams p) {
+__global__ __launch_bounds__(512) void quant_write_kernel(QuantParams p) {
   constexpr int G = kHeadDim / NG;
   constexpr Int2Layout L{NG};
-  const int lane = threadIdx.x;
+  constexpr int kTpg = 32 / NG;  // threads per (token, group), 4 channels each
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int64_t t0 = (int64_t)blockIdx.x * 16;
   const int kv = blockIdx.y;
   const int isv = blockIdx.z;
@@ -88,14 +94,14 @@ __global__ __launch_bounds__(64) void quant_write_kernel(QuantParams p) {
   __shared__ uint32_t szs[16][NG];
   __shared__ int32_t dst[16];
 
-  if (lane < 16) {
-    const int64_t t = t0 + lane;
-    dst[lane] = (t < p.n) ? p.dst_slots[t] : -1;
-    if (dst[lane] >= 0 && (int64_t)(dst[lane] / kPage) >= p.n_int2_pages) dst[lane] = -1;
+  if (tid < 16) {
+    const int64_t t = t0 + tid;
+    dst[tid] = (t < p.n) ? p.dst_slots[t] : -1;
+    if (dst[tid] >= 0 && (int64_t)(dst[tid] / kPage) >= p.n_int2_pages) dst[tid] = -1;
   }
   __syncthreads();
   // ---- stage inputs (bf16 values) ----
-  for (int idx = lane; idx < 16 * kHeadDim; idx += 64) {
+  for (int idx = tid; idx < 16 * kHeadDim; idx += 512) {
     const int t = idx / kHeadDim, j = idx % kHeadDim;
     float v = 0.f;
     if (dst[t] >= 0) {
@@ -114,71 +120,71 @@ __global__ __launch_bounds__(64) void quant_write_kernel(QuantParams p) {
     }
     xin[t][j] = v;
   }
-  __syncthreads();
-  // ---- x_rot = X R in fp64 on MFMA ----
+  // ---- x_rot = X R in fp64 on MFMA: wavefront w owns output columns 16w..16w+15 ----
   // f64 16x16x4 operands: A lane l -> A[l%16][l/16]; B lane l -> B[l/16][l%16];
   // C lane l, element r -> C[4r + l/16][l%16].
   const float* R = (isv ? p.r_v : p.r_k) + (int64_t)kv * kHeadDim * kHeadDim;
   const int ln = lane & 15, qd = lane >> 4;
-  f64x4 acc[8];
+  float rb[kHeadDim / 4];  // this lane's B values, loaded together
 #pragma unroll
-  for (int nt = 0; nt < 8; ++nt) acc[nt] = f64x4{0.0, 0.0, 0.0, 0.0};
-  for (int ks = 0; ks < kHeadDim / 4; ++ks) {
-    const int k = 4 * ks + qd;
-    const double av = (double)xin[ln][k];
-    const float* rrow = R + k * kHeadDim + ln;
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-      const double bv = (double)rrow[16 * nt];
-      acc[nt] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc[nt], 0, 0, 0);
-    }
-  }
-#pragma unroll
-  for (int nt = 0; nt < 8; ++nt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) xr[4 * r + qd][16 * nt + ln] = acc[nt][r];
+  for (int ks = 0; ks < kHeadDim / 4; ++ks) rb[ks] = R[(4 * ks + qd) * kHeadDim + 16 * wave + ln];
   __syncthreads();
-  // ---- clip, group statistics, codes (one lane per (token, group)) ----
-  if (lane < 16 * NG) {
-    const int t = lane / NG, gm = lane % NG;
-    if (dst[t] >= 0) {
-      const double tau = isv ? p.tau_v : p.tau_k;
-      double mn = 0.0, mx = 0.0;
-      bool nan = false;
-      for (int j = gm * G; j < (gm + 1) * G; ++j) {
-        double v = xr[t][j];
-        v = (v < -tau) ? -tau : ((v > tau) ? tau : v);
-        xr[t][j] = v;
-        nan |= (v != v);
-        if (j == gm * G) {
-          mn = v;
-          mx = v;
-        } else {
-          mn = v < mn ? v : mn;
-          mx = v > mx ? v : mx;
-        }
-      }
-      uint16_t sb, zb;
-      if (nan) {
-        sb = zb = 0x7e00u;
-        for (int j = gm * G; j < (gm + 1) * G; ++j) codes[t][j] = 0;
-      } else {
-        sb = f64_to_f16_bits((mx - mn) / 3.0);
-        zb = f64_to_f16_bits(mn);
-        const double sd = f16_bits_to_f64(sb), zd = f16_bits_to_f64(zb);
-        for (int j = gm * G; j < (gm + 1) * G; ++j) {
-          double c = 0.0;
-          if (sd != 0.0) {
-            c = __builtin_rint((xr[t][j] - zd) / sd);
-            c = c < 0.0 ? 0.0 : (c > 3.0 ? 3.0 : c);
-          }
-          codes[t][j] = (uint8_t)c;
-        }
-      }
-      szs[t][gm] = (uint32_t)sb | ((uint32_t)zb << 16);
+  f64x4 acc = f64x4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int ks = 0; ks < kHeadDim / 4; ++ks)
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xin[ln][4 * ks + qd], (double)rb[ks], acc, 0, 0, 0);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) xr[4 * r + qd][16 * wave + ln] = acc[r];
+  __syncthreads();
+  // ---- clip, group statistics, codes: kTpg threads per (token, group) ----
+  {
+    const int pair = tid / kTpg, sub = tid % kTpg;
+    const int t = pair / NG, gm = pair % NG;
+    const int j0 = gm * G + 4 * sub;
+    const double tau = isv ? p.tau_v : p.tau_k;
+    double v[4];
+    double mn = 0.0, mx = 0.0;
+    bool nan = false;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      double x = xr[t][j0 + e];
+      x = (x < -tau) ? -tau : ((x > tau) ? tau : x);
+      v[e] = x;
+      nan |= (x != x);
+      mn = e == 0 ? x : (x < mn ? x : mn);
+      mx = e == 0 ? x : (x > mx ? x : mx);
     }
+    // the kTpg threads of a (token, group) are consecutive lanes of one wavefront
+#pragma unroll
+    for (int off = 1; off < kTpg; off <<= 1) {
+      const double omn = __shfl_xor(mn, off), omx = __shfl_xor(mx, off);
+      mn = omn < mn ? omn : mn;
+      mx = omx > mx ? omx : mx;
+      nan |= __shfl_xor((int)nan, off) != 0;
+    }
+    uint16_t sb, zb;
+    if (nan) {
+      sb = zb = 0x7e00u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) codes[t][j0 + e] = 0;
+    } else {
+      sb = f64_to_f16_bits((mx - mn) / 3.0);
+      zb = f64_to_f16_bits(mn);
+      const double sd = f16_bits_to_f64(sb), zd = f16_bits_to_f64(zb);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        double c = 0.0;
+        if (sd != 0.0) {
+          c = __builtin_rint((v[e] - zd) / sd);
+          c = c < 0.0 ? 0.0 : (c > 3.0 ? 3.0 : c);
+        }
+        codes[t][j0 + e] = (uint8_t)c;
+      }
+    }
+    if (sub == 0) szs[t][gm] = (uint32_t)sb | ((uint32_t)zb << 16);
   }
   __syncthreads();
+  if (tid >= 64) return;
   // ---- stores ----
   uint8_t* pages = p.int2_pages;
   const int64_t blk_bytes = L.bytes();
@@ -278,9 +284,9 @@ template <int MODE>
 hipError_t launch_qw(const QuantParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)((p.n + 15) / 16), (unsigned)p.n_kv, 2);
   if (p.group == 32)
-    hipLaunchKernelGGL((quant_write_kernel<MODE, 4>), grid, dim3(64), 0, stream, p);
+    hipLaunchKernelGGL((quant_write_kernel<MODE, 4>), grid, dim3(512), 0, stream, p);
   else
-    hipLaunchKernelGGL((quant_write_kernel<MODE, 2>), grid, dim3(64), 0, stream, p);
+    hipLaunchKernelGGL((quant_write_kernel<MODE, 2>), grid, dim3(512), 0, stream, p);
   return hipGetLastError();
 }
 

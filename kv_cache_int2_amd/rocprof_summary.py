@@ -1,0 +1,98 @@
+"""Summaries of rocprofv3 result databases (SQLite) for the OSCAR kernels.
+
+    python -m kv_cache_int2_amd.rocprof_summary trace DB --command CMD
+        per-kernel dispatch statistics (count, average / min / max duration),
+        as a short markdown table.
+
+    python -m kv_cache_int2_amd.rocprof_summary pmc --fetch DB --write DB
+        --kernel NAME --copy NAME --copy-bytes N --workload W --source FILE
+        --algorithmic-bytes N --command CMD
+        HBM traffic per launch of one kernel from a FETCH_SIZE pass and a
+        WRITE_SIZE pass (KiB per dispatch), each scaled by what the same
+        counter reads for a plain copy kernel that moves a known number of
+        bytes in each direction.  Prints JSON; the source hash ties the figure
+        to the kernel source it was measured on.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import sqlite3
+import sys
+
+
+def _short(name: str) -> str:
+    n = name.replace("(anonymous namespace)::", "").replace("void ", "")
+    return n.split("(")[0][-60:]
+
+
+def kernel_stats(db: str):
+    con = sqlite3.connect(db)
+    rows = con.execute("select name, count(*), avg(duration), min(duration), max(duration), sum(duration) "
+                       "from kernels group by name order by sum(duration) desc").fetchall()
+    return [dict(name=_short(n), calls=c, avg_us=a / 1e3, min_us=lo / 1e3, max_us=hi / 1e3, total_ms=t / 1e6)
+            for n, c, a, lo, hi, t in rows]
+
+
+def counter_per_dispatch(db: str, counter: str, kernel: str):
+    """Per-dispatch values of a counter for kernels whose name contains `kernel`
+    (summed over the counter's hardware instances)."""
+    con = sqlite3.connect(db)
+    q = ("select k.dispatch_id, sum(p.counter_value) from pmc_events p join kernels k "
+         "on p.dispatch_id = k.dispatch_id where p.counter_name = ? and k.name like ? group by k.dispatch_id")
+    return [v for _, v in con.execute(q, (counter, f"%{kernel}%")).fetchall()]
+
+
+def cmd_trace(a):
+    rows = kernel_stats(a.db)
+    out = [f"# rocprofv3 kernel trace: {a.title}", "", "Command:", "", "```", a.command, "```", "",
+           "| kernel | calls | avg us | min us | max us | total ms |", "|---|---:|---:|---:|---:|---:|"]
+    for r in rows:
+        out.append(f"| {r['name']} | {r['calls']} | {r['avg_us']:.2f} | {r['min_us']:.2f} | {r['max_us']:.2f} "
+                   f"| {r['total_ms']:.3f} |")
+    print("\n".join(out))
+
+
+def cmd_pmc(a):
+    res = {"kernel": a.kernel, "workload": a.workload, "command": a.command}
+    with open(a.source, "rb") as f:
+        res["kernel_source_sha256"] = hashlib.sha256(f.read()).hexdigest()
+    total = 0.0
+    for counter, db in (("FETCH_SIZE", a.fetch), ("WRITE_SIZE", a.write)):
+        k = counter_per_dispatch(db, counter, a.kernel)
+        c = counter_per_dispatch(db, counter, a.copy)
+        if not k or not c:
+            sys.exit(f"no {counter} values for {a.kernel} or {a.copy} in {db}")
+        copy_kib = sum(c) / len(c)
+        factor = a.copy_bytes / (copy_kib * 1024.0)        # true bytes per counted byte
+        kern_kib = sum(k) / len(k)
+        bytes_ = kern_kib * 1024.0 * factor
+        res[counter.lower()] = {"kernel_kib_per_dispatch": kern_kib, "dispatches": len(k),
+                                "copy_kib_per_dispatch": copy_kib, "copy_true_bytes": a.copy_bytes,
+                                "scale": factor, "bytes_per_launch": bytes_}
+        total += bytes_
+    res["hbm_bytes_per_launch"] = total
+    res["algorithmic_bytes_per_launch"] = a.algorithmic_bytes
+    res["traffic_over_algorithmic"] = total / a.algorithmic_bytes if a.algorithmic_bytes else None
+    print(json.dumps(res, indent=1))
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("db")
+    t.add_argument("--command", required=True)
+    t.add_argument("--title", default="")
+    p = sub.add_parser("pmc")
+    for k in ("fetch", "write", "kernel", "copy", "workload", "source", "command"):
+        p.add_argument("--" + k, required=True)
+    p.add_argument("--copy-bytes", type=int, required=True)
+    p.add_argument("--algorithmic-bytes", type=int, default=0)
+    a = ap.parse_args(argv)
+    cmd_trace(a) if a.cmd == "trace" else cmd_pmc(a)
+
+
+if __name__ == "__main__":
+    main()

@@ -87,6 +87,9 @@ def test_workspace_bytes_monotone(lib):
     assert K.oscar_decode_workspace_bytes(sh, 28, 0, 0) >= b
     s = K.oscar_decode_auto_splits(sh, 28, 6300)
     assert 1 <= s <= 64
+    assert K.oscar_decode_auto_splits(sh, 1, 64) == 2          # at least 32 pages per split
+    assert K.oscar_decode_auto_splits(sh, 1, 40000) == 64      # capped
+    assert K.oscar_decode_auto_splits(sh, 28, 6300) == 55      # 12288 items over 224 (request, head)
 
 
 # ---------------------------------------------------------------------------
