@@ -48,6 +48,11 @@ def parse():
     return ap.parse_args()
 
 
+def int2_tokens(t, sink, recent):
+    """INT2 history tokens of a request of length t: positions [sink, t - recent)."""
+    return max(0, int(t) - sink - recent)
+
+
 def algorithmic_bytes(ctx, hkv, hq, group, sink, recent):
     """Bytes the method must move for one decode of the batch: INT2 codes +
     fp16 scale/zero of history tokens, bf16 K/V of sink/recent tokens, the
@@ -56,9 +61,17 @@ def algorithmic_bytes(ctx, hkv, hq, group, sink, recent):
     per_bf16 = 2 * 128 * 2
     tot = 0
     for t in ctx:
-        n_bf = min(t, sink + recent)
-        tot += ((t - n_bf) * per_int2 + n_bf * per_bf16) * hkv
+        n_i2 = int2_tokens(t, sink, recent)
+        tot += (n_i2 * per_int2 + (int(t) - n_i2) * per_bf16) * hkv
     return tot + len(ctx) * hq * 128 * (2 + 4)
+
+
+def int2_kernel_bytes(ctx, hkv, group, sink, recent):
+    """Algorithmic bytes of one launch of the INT2 kernel: 2 x (32 B of codes +
+    (128/G) x 4 B of fp16 scale/zero) per INT2 token and KV head (96 B at G=32,
+    80 B at G=64).  The bf16 tokens belong to the bf16 kernel."""
+    per_int2 = 2 * (128 // 4 + (128 // group) * 4)
+    return sum(int2_tokens(t, sink, recent) for t in ctx) * hkv * per_int2
 
 
 def main():
@@ -201,7 +214,8 @@ def main():
     tokens = int(sum(c.sum() for c in ctx_hist))
     value = tokens / elapsed
     main_avg_ms = main_ms / max(launches, 1)
-    alg = np.mean([algorithmic_bytes(c, hkv, hq, group, w.sink, w.recent) for c in ctx_hist])
+    alg_step = np.mean([algorithmic_bytes(c, hkv, hq, group, w.sink, w.recent) for c in ctx_hist])
+    alg = np.mean([int2_kernel_bytes(c, hkv, group, w.sink, w.recent) for c in ctx_hist])
     achieved = alg / (main_avg_ms * 1e-3) / 1e9
     log(f"timed {args.steps} steps in {elapsed * 1e3:.2f} ms: {value / 1e9:.3f} G KV tok/s; "
         f"decode_int2 avg {main_avg_ms * 1e3:.1f} us -> {achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS:.1%} of peak)")
@@ -316,7 +330,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "decode_int2", "kernel_us": round(main_avg_ms * 1e3, 2),
-                     "algorithmic_bytes_per_launch": int(alg)},
+                     "algorithmic_bytes_per_launch": int(alg),
+                     "algorithmic_bytes_per_step": int(alg_step)},
         "cpu_baseline": cpu,
         "bf16_baseline": baseline,
         "quant_write": qw,

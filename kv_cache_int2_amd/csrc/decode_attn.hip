@@ -301,7 +301,9 @@ struct Int2State {
   float moff[CT][HPL];
   float mx_run[CT][HPL];  // m in raw logit units
   float l_run[CT][HPL];
-  float zsum[CT][4];      // value-operand row 16ct + ln, token slot r; units pscale 4^-r
+  // value-operand row 16ct + ln, units pscale 4^-r: zz[r] = sum over token slot
+  // r of p z, plus 3 p s on the odd slots
+  float zz[CT][4];
   f32x4 acc[CT][8];
 };
 
@@ -558,7 +560,7 @@ __device__ __forceinline__ void int2_pair(const Src& src, int lp0, int p_end, in
         az = ((ln >> 1) & 1) ? az1 : az;
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) S.zsum[ct][r] *= az;
+      for (int r = 0; r < 4; ++r) S.zz[ct][r] *= az;
     }
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -600,15 +602,19 @@ __device__ __forceinline__ void int2_pair(const Src& src, int lp0, int p_end, in
         s1 = v1 ? s1 : 0.f;
         z1 = v1 ? z1 : 0.f;
       }
-      const float x0 = fmaf(pf0[r], s0, 0.f), x1 = fmaf(pf1[r], s1, 0.f);
+      // odd token slots enter with -P' against the complemented code 3 - c
+      const float sg = (r & 1) ? -1.f : 1.f;
+      const float x0 = fmaf(pf0[r], sg * s0, 0.f), x1 = fmaf(pf1[r], sg * s1, 0.f);
       // hi = x truncated to fp16, lo = the exact remainder, truncated again
       const f16x2 hv = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(x0, x1));
       pa[ct][0][r] = __builtin_bit_cast(uint32_t, hv);
       pa[ct][1][r] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(mix_sub_lo(x0, hv), mix_sub_hi(x1, hv)));
-      // value = (z + 1.5 s) + (2c - 3) s / 2: the midpoint term here, the
-      // centred term on the MFMA, where its signs keep the accumulation unbiased
-      S.zsum[ct][r] = fmaf(pf0[r], fmaf(1.5f, s0, z0), S.zsum[ct][r]);
-      S.zsum[ct][r] = fmaf(pf1[r], fmaf(1.5f, s1, z1), S.zsum[ct][r]);
+      S.zz[ct][r] = fmaf(pf0[r], z0, S.zz[ct][r]);
+      S.zz[ct][r] = fmaf(pf1[r], z1, S.zz[ct][r]);
+      if (r & 1) {  // x = -p s pscale 4^-r here
+        S.zz[ct][r] = fmaf(-3.f, x0, S.zz[ct][r]);
+        S.zz[ct][r] = fmaf(-3.f, x1, S.zz[ct][r]);
+      }
     }
   }
   // ---- values on MFMA ----
@@ -618,13 +624,13 @@ __device__ __forceinline__ void int2_pair(const Src& src, int lp0, int p_end, in
     const uint32_t lo_src = DV.vw[0][kt >> 2], hi_src = DV.vw[1][kt >> 2];
     const uint32_t sel = (uint32_t)(kt & 3) | 0x0c00u | ((uint32_t)(4 + (kt & 3)) << 16) | 0x0c000000u;
     const uint32_t x = __builtin_amdgcn_perm(hi_src, lo_src, sel);
-    // code c at bits 2r of each half is the fp16 subnormal c 2^(2r-24); 2c - 3 is exact
+    // code c at bits 2r of each half is the fp16 subnormal c 2^(2r-24); odd
+    // token slots take 3 - c = c ^ 3 (one and-xor)
     u32x4 bv;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const f16x2 cv = __builtin_bit_cast(f16x2, x & (0x00030003u << (2 * r)));
-      const _Float16 off = (_Float16)(-3.0f * (float)(1 << (2 * r)) * 0x1p-24f);
-      bv[r] = __builtin_bit_cast(uint32_t, cv * (_Float16)2.0f + f16x2{off, off});
+      const uint32_t m = 0x00030003u << (2 * r);
+      bv[r] = (r & 1) ? ((x & m) ^ m) : (x & m);
     }
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
@@ -653,7 +659,7 @@ __device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float
       S.l_run[ct][hh] = 0.f;
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) S.zsum[ct][r] = 0.f;
+    for (int r = 0; r < 4; ++r) S.zz[ct][r] = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 8; ++kt) S.acc[ct][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -758,14 +764,16 @@ __device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float
   }
   // ---- finalize ----
   const int Ssp = p.splits_int2 + p.splits_bf16;
-  const float accscale = exp2f(23.f - p.p_scale_exp);  // MFMA sums p s (2c - 3) 2^(sp-24)
+  // the MFMA sums 2^(sp-24) (sum_even p s c - sum_odd p s (3 - c))
+  const float accscale = exp2f(24.f - p.p_scale_exp);
   const float ipscale = 1.0f / pscale;
   constexpr int G = kHeadDim / NG;
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
+    // sum p z + 3 sum_odd p s
     float z = 0.f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) z = fmaf(S.zsum[ct][r], (float)(1 << (2 * r)) * ipscale, z);
+    for (int r = 0; r < 4; ++r) z = fmaf(S.zz[ct][r], (float)(1 << (2 * r)) * ipscale, z);
     z = sum_across_quads(z);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
