@@ -422,14 +422,16 @@ __device__ __forceinline__ void int2_issue(const uint8_t* blk0, const uint8_t* b
   }
 }
 // Wait until at most N vector-memory operations of this wavefront are in
-// flight (the N most recent are the next pair's four staging loads).
+// flight (the N most recent are the staging loads of the next one or two pairs).
 template <int N>
 __device__ __forceinline__ void vm_wait() {
-  static_assert(N == 0 || N == 4, "vm_wait");
+  static_assert(N == 0 || N == 4 || N == 8, "vm_wait");
   if constexpr (N == 0)
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  else
+  else if constexpr (N == 4)
     asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
 }
 
 // a pair staged in LDS: each part is read when the pair asks for it
@@ -714,15 +716,14 @@ __device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float
         edge(lp0);
         lp0 += 2;
       }
-      // interior pairs (both pages fully inside [lo, hi)), staged in LDS one
-      // pair ahead: two slots, the loop unrolled by two so the slots are fixed.
-      // Page ids come 64 at a time, one per lane, and a pair takes its two ids
-      // with v_readlane: no memory access and no wait inside the pair loop.
-      // Each chunk ends with its staging loads drained.
+      // interior pairs (both pages fully inside [lo, hi)), staged in LDS two
+      // pairs ahead in a ring of three slots.  Page ids come 64 at a time, one
+      // per lane, and a pair takes its two ids with v_readlane: no memory
+      // access and no wait inside the pair loop.  Each chunk ends with its
+      // staging loads drained.
       const int main_end = min(p_end, hi / kPage);
-      uint8_t* const st0 = stage;
-      uint8_t* const st1 = stage + 2 * L.bytes();
-      const uint32_t a0 = lds_address(st0), a1 = lds_address(st1);
+      constexpr int kSlot = 2 * L.bytes();
+      const uint32_t a0 = lds_address(stage);
       while (lp0 + 2 <= main_end) {
         const int c0 = lp0;
         const int cn = min(64, main_end - c0);
@@ -735,27 +736,24 @@ __device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         auto page = [&](int l) { return blk(__builtin_amdgcn_readlane(id, l - c0)); };
         int2_issue<NG>(page(lp0), page(lp0 + 1), a0);
+        if (lp0 + 4 <= lim) int2_issue<NG>(page(lp0 + 2), page(lp0 + 3), a0 + kSlot);
+        int cur = 0;  // slot of the pair at lp0 (wavefront-uniform)
         for (;;) {
-          bool nx = lp0 + 4 <= lim;
-          if (nx) {
-            int2_issue<NG>(page(lp0 + 2), page(lp0 + 3), a1);
+          // stage the pair two ahead into the slot the previous pair freed,
+          // then wait for this pair's bytes
+          const int nxt = cur == 0 ? 2 : cur - 1;
+          if (lp0 + 6 <= lim) {
+            int2_issue<NG>(page(lp0 + 4), page(lp0 + 5), a0 + nxt * kSlot);
+            vm_wait<8>();
+          } else if (lp0 + 4 <= lim) {
             vm_wait<4>();
           } else {
             vm_wait<0>();
           }
-          int2_pair<NG, CT, false>(Int2Staged<NG>{st0, off}, lp0, p_end, lo, hi, K, S, p_lds);
+          int2_pair<NG, CT, false>(Int2Staged<NG>{stage + cur * kSlot, off}, lp0, p_end, lo, hi, K, S, p_lds);
           lp0 += 2;
-          if (!nx) break;
-          nx = lp0 + 4 <= lim;
-          if (nx) {
-            int2_issue<NG>(page(lp0 + 2), page(lp0 + 3), a0);
-            vm_wait<4>();
-          } else {
-            vm_wait<0>();
-          }
-          int2_pair<NG, CT, false>(Int2Staged<NG>{st1, off}, lp0, p_end, lo, hi, K, S, p_lds);
-          lp0 += 2;
-          if (!nx) break;
+          if (lp0 + 2 > lim) break;
+          cur = cur == 2 ? 0 : cur + 1;
         }
         if (lim < c0 + cn) break;  // a bad id: the rest goes through the masked path
       }
@@ -963,12 +961,16 @@ __device__ void bf16_item(const DecodeParams& p, int b, int kv, int split) {
   }
 }
 
-// register budget: one row tile fits 4 wavefronts per SIMD; wider GQA groups need more
+// register budget: one row tile fits 4 wavefronts per SIMD (128 VGPRs; LDS
+// 9.5-10 KB per wavefront also fits 16 per compute unit); wider GQA groups
+// need more registers
 template <int NG, int CT>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(CT == 1 ? 3 : (CT == 2 ? 2 : 1), 8))) void
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(CT == 1 ? 4 : (CT == 2 ? 2 : 1), 8))) void
 decode_int2(DecodeParams p) {
-  __shared__ __attribute__((aligned(16))) float p_lds[16 * 32];
-  __shared__ __attribute__((aligned(16))) uint8_t stage[4 * Int2Layout{NG}.bytes()];
+  // p of the 16 CT / NG heads a wavefront covers, 2 pages x 16 tokens each;
+  // three staging slots of two blocks
+  __shared__ __attribute__((aligned(16))) float p_lds[(16 * CT / NG) * 32];
+  __shared__ __attribute__((aligned(16))) uint8_t stage[6 * Int2Layout{NG}.bytes()];
   const int item = blockIdx.x;
   const int split = item % p.splits_int2;
   const int bk = item / p.splits_int2;
