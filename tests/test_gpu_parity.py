@@ -296,3 +296,50 @@ def test_bf16_baseline_decode(hq, hkv):
         for r in range(len(lens)):
             ref = O.attend(O.bf16_to_f64(q[r]), O.bf16_to_f64(ks[r]), O.bf16_to_f64(vs[r]))
             _check_close(out[r], ref, f"baseline hq={hq} len={lens[r]} splits={sp}")
+
+
+def test_full_size_28x100k_sampled():
+    """The measured workload at full size, in the launch configuration the
+    bench times (whole batch, automatic split count): decode outputs of every
+    query head of two requests, and a spread of their page blocks, against the
+    oracle run on those two requests alone."""
+    w = synth.WORKLOADS["long_28x100k"]
+    B, T = w.batch, w.context
+    _flush(f"case long_28x100k: B={B} T={T} Hq={w.n_q_heads} Hkv={w.n_kv_heads} G={w.group}")
+    cal = _calibrate(w)
+    sh = K.make_shape(n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads, group=w.group, sink=w.sink,
+                      recent=w.recent)
+    ppr = (T + 15) // 16 + 2
+    dc = DeviceCache(sh, cal.r_k, cal.r_v, cal.tau_k, cal.tau_v, B * ppr + 8,
+                     B * (w.sink // 16 + 2 + w.recent // 16) + 8)
+    seqs = []
+    for r in range(B):
+        kb, vb = synth.kv_request_bf16(w, r, 0, T)
+        seq = dc.new_seq()
+        _fill(dc, seq, kb, vb, [16384] * (T // 16384) + [T % 16384])
+        seqs.append(seq)
+    _flush("filled")
+    q = np.stack([synth.q_decode_bf16(w, r, 1) for r in range(B)])
+    out = dc.decode(seqs, q).cpu().numpy()
+    assert np.all(np.isfinite(out))
+    i2, bf, _ = dc.tables(seqs)
+    for r in (0, B - 1):
+        kb, vb = synth.kv_request_bf16(w, r, 0, T)
+        st = O.store_request(kb, vb, cal, w.group, w.sink, w.recent)
+        _check_close(out[r], O.decode_attention(q[r], st, cal, w.group), f"long_28x100k request {r}")
+        # page blocks: the first INT2 pages, pages spread over the history, the last ones
+        n_lp = int(np.count_nonzero(i2[r] >= 0))
+        lps = sorted({0, 1, 2, n_lp // 3, n_lp // 2, 2 * n_lp // 3, n_lp - 2, n_lp - 1})
+        mism = 0
+        for lp in lps:
+            for h in range(w.n_kv_heads):
+                got = dc.int2_block_bytes_of(int(i2[r, lp]), h)
+                mism += not np.array_equal(got, _expected_int2_block(st, lp, h, w.group))
+            for lpb in range(bf.shape[1]):
+                if bf[r, lpb] >= 0 and lp == lps[0]:
+                    for h in range(w.n_kv_heads):
+                        got = dc.bf16_block_bytes_of(int(bf[r, lpb]), h)
+                        mism += not np.array_equal(got, _expected_bf16_block(st, lpb, h, w.sink, w.recent))
+        _flush(f"long_28x100k request {r}: {len(lps)} INT2 pages x {w.n_kv_heads} heads and the bf16 pages, "
+               f"mismatching blocks={mism}")
+        assert mism == 0
