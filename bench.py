@@ -37,8 +37,9 @@ def log(msg):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=2000,
+                    help="untimed steps first (about a second of decode, so clocks have settled)")
     ap.add_argument("--workload", default="long_28x100k")
     ap.add_argument("--group", type=int, default=0, help="override the workload's INT2 group size")
     ap.add_argument("--splits", type=int, default=0, help="INT2 splits per (request, KV head); 0 = auto")
@@ -159,14 +160,15 @@ def main():
     qw_time = sum(a.elapsed_time(b) for a, b in qw_ms) / 1e3
     log(f"cache filled in {time.time() - t:.1f}s; quant_write {qw_tokens} tokens in {qw_time * 1e3:.1f} ms")
 
-    # ---- step inputs, resident before timing ----
-    new_k = np.empty((n_steps, B, hkv, 128), np.uint16)
+    # ---- step inputs, resident before timing (n_in distinct sets, used in turn) ----
+    n_in = min(n_steps, 128)
+    new_k = np.empty((n_in, B, hkv, 128), np.uint16)
     new_v = np.empty_like(new_k)
-    qs = np.empty((n_steps, B, hq, 128), np.uint16)
+    qs = np.empty((n_in, B, hq, 128), np.uint16)
     for r in range(B):
-        kb, vb = synth.kv_request_bf16(w, r, T0, T_final, threads=1)
+        kb, vb = synth.kv_request_bf16(w, r, T0, T0 + n_in, threads=1)
         new_k[:, r], new_v[:, r] = kb, vb
-        for st in range(n_steps):
+        for st in range(n_in):
             qs[st, r] = synth.q_decode_bf16(w, r, st + 1)
     new_k_d, new_v_d, q_d = to_dev_bits(new_k), to_dev_bits(new_v), to_dev_bits(qs)
     planner = K.DecodeStepPlanner(dc.pool, seqs)
@@ -190,12 +192,13 @@ def main():
             tables[0] = to_dev_i32(i2_bt)
             tables[1] = to_dev_i32(bf_bt)
         d = dev_small[st]
+        si_ = st % n_in
         if n_age:
             K.oscar_requant_from_bf16(sh, dc.layer, dc.cache, d[2], d[3], n=n_age)
-        K.oscar_bf16_write(sh, dc.cache, new_k_d[st], new_v_d[st], d[1], n=B)
+        K.oscar_bf16_write(sh, dc.cache, new_k_d[si_], new_v_d[si_], d[1], n=B)
         if np.any(planner.buf[0] >= 0):
-            K.oscar_quant_write(sh, dc.layer, dc.cache, new_k_d[st], new_v_d[st], d[0], n=B)
-        K.oscar_decode_attn(sh, dc.layer, dc.cache, q_d[st], tables[0], tables[1], d[4], out, ws, si, 1)
+            K.oscar_quant_write(sh, dc.layer, dc.cache, new_k_d[si_], new_v_d[si_], d[0], n=B)
+        K.oscar_decode_attn(sh, dc.layer, dc.cache, q_d[si_], tables[0], tables[1], d[4], out, ws, si, 1)
         ctx_hist.append(planner.buf[4].astype(np.int64).copy())
 
     for st in range(args.warmup):
@@ -234,7 +237,7 @@ def main():
     # ---- bf16 same-kernel baseline ----
     baseline = None
     if bc is not None:
-        bq = q_d[n_steps - 1]
+        bq = q_d[(n_steps - 1) % n_in]
         btab = bc.tables(bseqs)
         bf_bt_d, bctx = to_dev_i32(btab[0]), to_dev_i32(btab[1])
         sb = K.oscar_decode_auto_splits(bc.shape, B, btab[0].shape[1])

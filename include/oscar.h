@@ -233,9 +233,9 @@ oscar_status oscar_decode_attn_bf16_baseline(const oscar_shape* shape, const osc
                                              const int32_t* ctx_lens, int32_t splits, float* out,
                                              void* workspace, size_t workspace_bytes, void* stream);
 
-/* Splits chosen when 0 is passed (deterministic in the arguments): enough
- * work items to fill the device several times over, at least 32 pages per
- * split, at most 64. */
+/* Splits chosen when 0 is passed: the count whose work items fill two whole
+ * rounds of the wavefronts the device runs at once, at most 64 and at least 32
+ * pages per split (deterministic for a given device). */
 int32_t oscar_decode_auto_splits(const oscar_shape* shape, int32_t batch, int32_t max_int2_pages);
 
 /* One decode step for a batch: grows each of the n sequences by one token

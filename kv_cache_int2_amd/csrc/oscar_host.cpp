@@ -731,16 +731,35 @@ oscar_status oscar_copy_pages(const oscar_shape* shape, const oscar_cache* cache
 
 static const int kAutoMaxSplits = 64;
 
+// compute units of the current device (256 on MI355X; also the answer when no
+// device can be queried, so the choice below is deterministic on a host)
+static int device_cus() {
+  static int cached = 0;
+  if (cached > 0) return cached;
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+      n > 0)
+    cached = n;
+  else
+    cached = 256;
+  (void)hipGetLastError();
+  return cached;
+}
+
 int32_t oscar_decode_auto_splits(const oscar_shape* shape, int32_t batch, int32_t max_int2_pages) {
   if (check_shape(shape) != OSCAR_OK || batch < 1) return 1;
-  // about 12 work items per SIMD (1024 SIMDs on 256 compute units: four rounds
-  // of three resident wavefronts), each split keeping at least 16 page pairs
+  // Work items run in rounds of the wavefronts that fit the device at once
+  // (4 SIMDs per compute unit; 4, 2 or 1 wavefronts per SIMD for 1, 2 or 3
+  // row tiles).  A count just above a whole number of rounds leaves a nearly
+  // empty last round that costs a full item time.  Take the count that fills
+  // two whole rounds (some slack for uneven requests, few partial results),
+  // within [1, 64] and at least 32 pages per split.
   const int64_t pairs = (int64_t)batch * shape->n_kv_heads;
-  const int64_t target = 1024 * 12;
-  int64_t s = (target + pairs - 1) / pairs;
-  s = std::min<int64_t>(s, std::max<int64_t>(1, max_int2_pages / 32));
-  s = std::max<int64_t>(1, std::min<int64_t>(s, kAutoMaxSplits));
-  return (int32_t)s;
+  const int ct = ct_of(shape);
+  const int64_t cap = (int64_t)device_cus() * 4 * (ct == 1 ? 4 : (ct == 2 ? 2 : 1));
+  const int64_t smax = std::max<int64_t>(1, std::min<int64_t>(kAutoMaxSplits, max_int2_pages / 32));
+  const int64_t s = 2 * cap / pairs;
+  return (int32_t)std::max<int64_t>(1, std::min<int64_t>(s, smax));
 }
 
 size_t oscar_decode_workspace_bytes(const oscar_shape* shape, int32_t batch, int32_t splits_int2,

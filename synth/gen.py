@@ -108,8 +108,22 @@ def head_profile(w: Workload, kv_head: int, layer: int = 0) -> HeadProfile:
     return HeadProfile(*out)
 
 
+_Q_FACTORS: dict = {}
+
+
 def q_factor(w: Workload, q_head: int, layer: int = 0) -> np.ndarray:
-    """Matrix F with rows q = z F, z ~ N(0, I), so Cov(q) = F^T F = O diag(lam) O^T."""
+    """Matrix F with rows q = z F, z ~ N(0, I), so Cov(q) = F^T F = O diag(lam) O^T.
+    Deterministic in (workload, head, layer); kept after the first call (read-only)."""
+    key = (w, q_head, layer)
+    f = _Q_FACTORS.get(key)
+    if f is None:
+        f = _q_factor(w, q_head, layer)
+        f.setflags(write=False)
+        _Q_FACTORS[key] = f
+    return f
+
+
+def _q_factor(w: Workload, q_head: int, layer: int) -> np.ndarray:
     d = w.head_dim
     g = _rng(w.index, KIND_Q, layer, q_head, 0xFFFF)
     a = g.standard_normal((d, d))

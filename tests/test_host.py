@@ -89,7 +89,8 @@ def test_workspace_bytes_monotone(lib):
     assert 1 <= s <= 64
     assert K.oscar_decode_auto_splits(sh, 1, 64) == 2          # at least 32 pages per split
     assert K.oscar_decode_auto_splits(sh, 1, 40000) == 64      # capped
-    assert K.oscar_decode_auto_splits(sh, 28, 6300) == 55      # 12288 items over 224 (request, head)
+    assert K.oscar_decode_auto_splits(sh, 28, 6300) == 36      # 2 rounds of 4096 wavefronts over 224 (request, head)
+    assert K.oscar_decode_auto_splits(sh, 4096, 6300) == 1     # more than two rounds of pairs
 
 
 # ---------------------------------------------------------------------------
