@@ -1,11 +1,14 @@
 """Benchmark of the OSCAR INT2 KV-cache hot path on one MI355X.
 
 One step = one decode step for the whole batch: host region planning
-(oscar_plan_decode_step), re-quantisation of the tokens leaving the recent
-window, bf16 append of every request's new token, and mixed-precision paged
-decode attention (prologue, main kernel, split-K combine).  The cache is
-resident in HBM before the timed region; inputs of every step are generated
-and uploaded beforehand.
+(oscar_plan_decode_step), then oscar_decode_step: re-quantisation of the
+tokens leaving the recent window and bf16 append of every request's new token
+(fused into the prologue kernel), and mixed-precision paged decode attention
+(prologue, INT2 kernel with the bf16-region kernel beside it on a second
+stream, split-K combine).  --unfused runs the same step as separate write
+calls and in-order kernels.  The cache is resident in HBM before the timed
+region; the inputs of the steps are generated and uploaded beforehand (128
+distinct sets, used in turn).
 
 Prints one JSON line.  value = KV tokens attended per second (summed context
 lengths of all requests and steps / wall time of the timed steps).
@@ -43,6 +46,8 @@ def parse():
     ap.add_argument("--workload", default="long_28x100k")
     ap.add_argument("--group", type=int, default=0, help="override the workload's INT2 group size")
     ap.add_argument("--splits", type=int, default=0, help="INT2 splits per (request, KV head); 0 = auto")
+    ap.add_argument("--unfused", action="store_true",
+                    help="separate write calls and in-order kernels instead of the fused decode step")
     ap.add_argument("--no-baseline", action="store_true", help="skip the bf16 same-kernel baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -193,12 +198,16 @@ def main():
             tables[1] = to_dev_i32(bf_bt)
         d = dev_small[st]
         si_ = st % n_in
-        if n_age:
-            K.oscar_requant_from_bf16(sh, dc.layer, dc.cache, d[2], d[3], n=n_age)
-        K.oscar_bf16_write(sh, dc.cache, new_k_d[si_], new_v_d[si_], d[1], n=B)
-        if np.any(planner.buf[0] >= 0):
-            K.oscar_quant_write(sh, dc.layer, dc.cache, new_k_d[si_], new_v_d[si_], d[0], n=B)
-        K.oscar_decode_attn(sh, dc.layer, dc.cache, q_d[si_], tables[0], tables[1], d[4], out, ws, si, 1)
+        if args.unfused:
+            if n_age:
+                K.oscar_requant_from_bf16(sh, dc.layer, dc.cache, d[2], d[3], n=B)
+            if np.any(planner.buf[0] >= 0):
+                K.oscar_quant_write(sh, dc.layer, dc.cache, new_k_d[si_], new_v_d[si_], d[0], n=B)
+            K.oscar_bf16_write(sh, dc.cache, new_k_d[si_], new_v_d[si_], d[1], n=B)
+            K.oscar_decode_attn(sh, dc.layer, dc.cache, q_d[si_], tables[0], tables[1], d[4], out, ws, si, 1)
+        else:
+            K.oscar_decode_step(sh, dc.layer, dc.cache, new_k_d[si_], new_v_d[si_], d[:4], q_d[si_], tables[0],
+                                tables[1], d[4], out, ws, si, 1)
         ctx_hist.append(planner.buf[4].astype(np.int64).copy())
 
     for st in range(args.warmup):
@@ -329,7 +338,7 @@ def main():
         "data": "synthetic (seeded generator; calibration on synthetic activations)",
         "config": {"workload": w.name, "batch": B, "context": T_final, "n_q_heads": hq, "n_kv_heads": hkv,
                    "head_dim": 128, "group": group, "sink": w.sink, "recent": w.recent, "page_size": 16,
-                   "splits_int2": si},
+                   "splits_int2": si, "step": "unfused" if args.unfused else "fused"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "decode_int2", "kernel_us": round(main_avg_ms * 1e3, 2),

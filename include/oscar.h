@@ -241,13 +241,44 @@ int32_t oscar_decode_auto_splits(const oscar_shape* shape, int32_t batch, int32_
 /* One decode step for a batch: grows each of the n sequences by one token
  * (host bookkeeping, as oscar_seq_plan_append with n_new = 1 per sequence).
  * Outputs (host, capacity n each): int2_slots / bf16_slots of the new tokens
- * (-1 where not that region); age_src / age_dst: compacted bf16 -> INT2 moves
- * of tokens leaving the recent window, *n_age their count; ctx_lens: the new
- * lengths; *tables_changed = 1 if any sequence received a new page (its block
- * table rows must be refreshed).  On OSCAR_ENOMEM no sequence is changed. */
+ * (-1 where not that region); age_src / age_dst: the bf16 -> INT2 move of the
+ * token of sequence i leaving the recent window (-1 if none), *n_age the number
+ * of moves; ctx_lens: the new lengths; *tables_changed = 1 if any sequence
+ * received a new page (its block table rows must be refreshed).  The four slot
+ * arrays laid out as rows of one int32 [4][n] array are the step_slots of
+ * oscar_decode_step.  On OSCAR_ENOMEM no sequence is changed. */
 oscar_status oscar_plan_decode_step(oscar_pool* pool, oscar_seq* const* seqs, int32_t n, int32_t* int2_slots,
                                     int32_t* bf16_slots, int32_t* age_src, int32_t* age_dst, int32_t* n_age,
                                     int32_t* ctx_lens, int32_t* tables_changed);
+
+/* One decode step, writes and attention in one call ([ES] serving section:
+ * the fused write and read kernels; [IT] 2.2.B).  Before the attention of
+ * oscar_decode_attn (same arguments, same result), and inside its first kernel,
+ * each request b of the batch stores this step's token, per KV head:
+ *   step_slots[3*batch + b] >= 0: the token in bf16 slot step_slots[2*batch + b]
+ *     (leaving the recent window) is quantised into that INT2 slot, exactly as
+ *     oscar_requant_from_bf16 does;
+ *   step_slots[b] >= 0: the new token (k_new, v_new row b) is quantised into
+ *     that INT2 slot, exactly as oscar_quant_write does;
+ *   step_slots[batch + b] >= 0: the new token is copied into that bf16 slot
+ *     (read after the leaving token, so the two may share a ring slot).
+ * Inputs (device): k_new, v_new bf16 [batch][n_kv_heads][d]; step_slots int32
+ * [4][batch] (-1 = nothing to do; out-of-range slots are skipped).  The
+ * block tables and ctx_lens must already include the new token (as
+ * oscar_plan_decode_step leaves them).  Errors as oscar_decode_attn. */
+oscar_status oscar_decode_step(const oscar_shape* shape, const oscar_layer* layer, const oscar_cache* cache,
+                               const void* k_new, const void* v_new, const int32_t* step_slots, const void* q,
+                               int32_t batch, const int32_t* int2_bt, int32_t max_int2_pages,
+                               const int32_t* bf16_bt, int32_t max_bf16_pages, const int32_t* ctx_lens,
+                               int32_t splits_int2, int32_t splits_bf16, float* out, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/* Whether oscar_decode_attn / oscar_decode_step run the bf16-region kernel on
+ * a second stream of the library's (default priority, one per device, created
+ * at first use) beside the INT2 kernel (on != 0, the default), or in order on
+ * the caller's stream.  The results are the same either way; calls that use
+ * the second stream are serialised by a lock while they enqueue. */
+oscar_status oscar_set_overlap(int32_t on);
 
 /* Instrumentation.  While enabled (on != 0), each decode launch made by the
  * calling thread records a pair of HIP events on its stream around the main

@@ -66,6 +66,10 @@ _SIGS = {
     "oscar_decode_workspace_bytes": (C.c_size_t, [C.POINTER(Shape), C.c_int32, C.c_int32, C.c_int32]),
     "oscar_decode_attn": (C.c_int32, [C.POINTER(Shape), C.POINTER(Layer), C.POINTER(Cache), P, C.c_int32, P,
                                       C.c_int32, P, C.c_int32, P, C.c_int32, C.c_int32, P, P, C.c_size_t, P]),
+    "oscar_decode_step": (C.c_int32, [C.POINTER(Shape), C.POINTER(Layer), C.POINTER(Cache), P, P, P, P,
+                                      C.c_int32, P, C.c_int32, P, C.c_int32, P, C.c_int32, C.c_int32, P, P,
+                                      C.c_size_t, P]),
+    "oscar_set_overlap": (C.c_int32, [C.c_int32]),
     "oscar_decode_attn_bf16_baseline": (C.c_int32, [C.POINTER(Shape), C.POINTER(Cache), P, C.c_int32, P,
                                                     C.c_int32, P, C.c_int32, P, P, C.c_size_t, P]),
     "oscar_decode_auto_splits": (C.c_int32, [C.POINTER(Shape), C.c_int32, C.c_int32]),
@@ -273,6 +277,21 @@ def oscar_decode_attn(shape, layer, cache, q, int2_bt, bf16_bt, ctx_lens, out, w
                                    int2_bt.shape[1], _ptr(bf16_bt), bf16_bt.shape[1], _ptr(ctx_lens), splits_int2,
                                    splits_bf16, _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                    _stream(stream)))
+
+
+def oscar_decode_step(shape, layer, cache, k_new, v_new, step_slots, q, int2_bt, bf16_bt, ctx_lens, out, workspace,
+                      splits_int2=0, splits_bf16=0, stream=None):
+    """Fused decode step: step_slots int32 [4][batch] rows = new token's INT2
+    slot, new token's bf16 slot, leaving token's bf16 source, its INT2 target."""
+    batch = q.shape[0]
+    _check(lib().oscar_decode_step(C.byref(shape), C.byref(layer), C.byref(cache), _ptr(k_new), _ptr(v_new),
+                                   _ptr(step_slots), _ptr(q), batch, _ptr(int2_bt), int2_bt.shape[1], _ptr(bf16_bt),
+                                   bf16_bt.shape[1], _ptr(ctx_lens), splits_int2, splits_bf16, _ptr(out),
+                                   _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def oscar_set_overlap(on: bool):
+    _check(lib().oscar_set_overlap(1 if on else 0))
 
 
 def oscar_decode_attn_bf16_baseline(shape, cache, q, bf16_bt, ctx_lens, out, workspace, splits=0, stream=None):

@@ -46,6 +46,7 @@
 #include <cmath>
 
 #include "oscar_internal.h"
+#include "quant_common.h"
 
 namespace oscar {
 namespace {
@@ -167,12 +168,132 @@ __device__ __forceinline__ void stage_matrix256(const float* src, float* lds) {
 }
 
 // ---------------------------------------------------------------------------
+// decode-step writes, fused into the prologue
+// ---------------------------------------------------------------------------
+// Per (request, KV head), by the prologue's 256 threads: the token leaving the
+// recent window is read from its bf16 slot and quantised into its INT2 slot; a
+// new token that goes straight to the INT2 history is quantised from the
+// input; a new sink/recent token is copied into its bf16 slot after the
+// leaving token has been read (the two may share a ring slot).  The quantiser
+// is the write path's: x R with exact bf16 x fp32 products summed in fp64,
+// clip, per group mn/mx, s = fp16((mx - mn)/3), z = fp16(mn), code =
+// clamp(rint((x - z)/s), 0, 3) in fp64, a group holding NaN stores NaN scale
+// and zero with codes 0.  Thread t handles channel t % 128 of K (t < 128) or V.
+struct StepScratch {
+  float x[2][2][kHeadDim];     // [token][K/V][channel] inputs (bf16 values)
+  uint8_t code[2][kHeadDim];   // [K/V][channel] codes of the token being stored
+  uint32_t sz[2][4];           // [K/V][group] fp16 scale | zero << 16
+};
+
+template <int NG>
+__device__ __forceinline__ void quantise_and_store(const DecodeParams& p, int kv, int tok, int32_t dst,
+                                                   const float* rk, const float* rv, StepScratch& sc) {
+  constexpr int G = kHeadDim / NG;
+  constexpr Int2Layout L{NG};
+  const int t = threadIdx.x, m = t >> 7, j = t & (kHeadDim - 1);
+  const float* R = m ? rv : rk;
+  const float* x = sc.x[tok][m];
+  double acc = 0.0;
+#pragma unroll 8
+  for (int i = 0; i < kHeadDim; i += 4) {
+    const float4 x4 = *(const float4*)&x[i];
+    acc = fma((double)x4.x, (double)R[i * kHeadDim + j], acc);
+    acc = fma((double)x4.y, (double)R[(i + 1) * kHeadDim + j], acc);
+    acc = fma((double)x4.z, (double)R[(i + 2) * kHeadDim + j], acc);
+    acc = fma((double)x4.w, (double)R[(i + 3) * kHeadDim + j], acc);
+  }
+  const double tau = m ? p.tau_v : p.tau_k;
+  const double v = acc < -tau ? -tau : (acc > tau ? tau : acc);
+  double mn = v, mx = v;
+  bool nan = v != v;
+  // the G channels of a group are consecutive lanes of one wavefront
+#pragma unroll
+  for (int off = 1; off < G; off <<= 1) {
+    const double omn = __shfl_xor(mn, off), omx = __shfl_xor(mx, off);
+    mn = omn < mn ? omn : mn;
+    mx = omx > mx ? omx : mx;
+    nan |= __shfl_xor((int)nan, off) != 0;
+  }
+  uint16_t sb = 0x7e00u, zb = 0x7e00u;
+  uint8_t c = 0;
+  if (!nan) {
+    sb = f64_to_f16_bits((mx - mn) / 3.0);
+    zb = f64_to_f16_bits(mn);
+    const double sd = f16_bits_to_f64(sb), zd = f16_bits_to_f64(zb);
+    if (sd != 0.0) {
+      double cd = __builtin_rint((v - zd) / sd);
+      cd = cd < 0.0 ? 0.0 : (cd > 3.0 ? 3.0 : cd);
+      c = (uint8_t)cd;
+    }
+  }
+  sc.code[m][j] = c;
+  if (j % G == 0) sc.sz[m][j / G] = (uint32_t)sb | ((uint32_t)zb << 16);
+  __syncthreads();
+  const int64_t page = dst / kPage;
+  const int slot = dst % kPage;
+  uint8_t* blk = p.int2_w + (page * p.n_kv + kv) * (int64_t)L.bytes();
+  if (t < 8) {
+    // K codes, token-major: 16 channels per word, channel 16t + e at bits 2e
+    uint32_t w = 0u;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) w |= (uint32_t)sc.code[0][16 * t + e] << (2 * e);
+    *(uint32_t*)(blk + L.k_codes() + slot * 32 + 4 * t) = w;
+  } else if (t >= 16 && t < 16 + NG) {
+    const int gm = t - 16;
+    *(uint32_t*)(blk + L.k_sz() + (slot * NG + gm) * 4) = sc.sz[0][gm];  // K: token-major
+  } else if (t >= 32 && t < 32 + NG) {
+    const int gm = t - 32;
+    *(uint32_t*)(blk + L.v_sz() + (gm * kPage + slot) * 4) = sc.sz[1][gm];  // V: group-major
+  } else if (t >= 64 && t < 96) {
+    // V codes by token quad: byte jc of quad slot/4 holds channel jc, this
+    // token at bits 2 (slot % 4); the other three tokens keep their bits
+    const int jd = t - 64, sh = 2 * (slot & 3);
+    uint32_t mask = 0u, bits = 0u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      mask |= 3u << (8 * e + sh);
+      bits |= (uint32_t)sc.code[1][4 * jd + e] << (8 * e + sh);
+    }
+    uint32_t* word = (uint32_t*)(blk + L.v_codes() + (slot >> 2) * kHeadDim + 4 * jd);
+    atomicAnd(word, ~mask);
+    atomicOr(word, bits);
+  }
+  __syncthreads();
+}
+
+template <int NG>
+__device__ void step_writes(const DecodeParams& p, int b, int kv, const float* rk, const float* rv,
+                            StepScratch& sc) {
+  const int t = threadIdx.x, m = t >> 7, j = t & (kHeadDim - 1);
+  const int32_t i2_new = p.step_slots[b], bf_new = p.step_slots[p.batch + b];
+  const int32_t age_src = p.step_slots[2 * p.batch + b], age_dst = p.step_slots[3 * p.batch + b];
+  const bool age = age_src >= 0 && age_dst >= 0 && age_src / kPage < p.n_bf16_pages &&
+                   age_dst / kPage < p.n_int2_pages;
+  const bool put_i2 = i2_new >= 0 && i2_new / kPage < p.n_int2_pages;
+  const bool put_bf = bf_new >= 0 && bf_new / kPage < p.n_bf16_pages;
+  const int64_t in = ((int64_t)b * p.n_kv + kv) * kHeadDim + j;
+  const uint16_t xn = (m ? p.v_new : p.k_new)[in];
+  // bf16 block: K [16][d] then V [d][16]
+  auto bf16_elem = [&](int32_t slot_id) {
+    uint16_t* blk = (uint16_t*)(p.bf16_w + ((int64_t)(slot_id / kPage) * p.n_kv + kv) * (int64_t)kBf16BlockBytes);
+    const int sl = slot_id % kPage;
+    return m ? blk + kPage * kHeadDim + j * kPage + sl : blk + sl * kHeadDim + j;
+  };
+  if (age) sc.x[0][m][j] = bf16_val(*bf16_elem(age_src));
+  if (put_i2) sc.x[1][m][j] = bf16_val(xn);
+  __syncthreads();  // the leaving token has been read before its ring slot is reused
+  if (put_bf) *bf16_elem(bf_new) = xn;
+  if (age) quantise_and_store<NG>(p, kv, 0, age_dst, rk, rv, sc);
+  if (put_i2) quantise_and_store<NG>(p, kv, 1, i2_new, rk, rv, sc);
+}
+
+// ---------------------------------------------------------------------------
 // prologue: q R_K operands
 // ---------------------------------------------------------------------------
 // Words per (request, KV head): A digits of 2Q ((((ct*3 + digit)*2 + kstep)*64 + lane)*4 + reg),
 // then aux floats [1 + 32*CT]: logit factor 2^-sq / 2, per row 2*Qbar (float),
-// per row -3*Qbar (int32 bits).
-template <int NG, int CT>
+// per row -3*Qbar (int32 bits).  WRITE: the decode-step writes come first.
+template <int NG, int CT, bool WRITE>
 __global__ __launch_bounds__(256) void decode_prologue(DecodeParams p) {
   const int bk = blockIdx.x;
   const int b = bk / p.n_kv, kv = bk % p.n_kv;
@@ -182,8 +303,17 @@ __global__ __launch_bounds__(256) void decode_prologue(DecodeParams p) {
   __shared__ float qs[16][kHeadDim];
   __shared__ int qi[16][kHeadDim];
   __shared__ float red[4];
+  __shared__ float rv[WRITE ? kHeadDim * kHeadDim : 1];
+  __shared__ __attribute__((aligned(16))) StepScratch sc;
   const int g = p.g;
-  stage_matrix256<kHeadDim>(p.r_k + (int64_t)kv * kHeadDim * kHeadDim, rk);
+  if constexpr (WRITE) {
+    stage_matrix256<kHeadDim>(p.r_v + (int64_t)kv * kHeadDim * kHeadDim, rv);
+    stage_matrix256<kHeadDim>(p.r_k + (int64_t)kv * kHeadDim * kHeadDim, rk);
+    __syncthreads();
+    step_writes<NG>(p, b, kv, rk, rv, sc);
+  } else {
+    stage_matrix256<kHeadDim>(p.r_k + (int64_t)kv * kHeadDim * kHeadDim, rk);
+  }
   for (int e = t; e < g * kHeadDim; e += 256)
     qs[e >> 7][e & (kHeadDim - 1)] = bf16_val(p.q[((int64_t)b * p.n_q + kv * g) * kHeadDim + e]);
   __syncthreads();
@@ -987,113 +1117,122 @@ __global__ __launch_bounds__(64) void decode_bf16(DecodeParams p) {
 // ---------------------------------------------------------------------------
 // combine: LSE merge, R_V^T on the INT2 part, normalisation
 // ---------------------------------------------------------------------------
-// One block of 256 threads per (request, KV head).  R_V is staged once in LDS
-// with a row stride of 129 floats, so thread j reading row j at column i hits
-// bank (j + i) % 32: no conflicts.  Split weights are recomputed where used.
+// One block of four wavefronts per (request, KV head); wavefront w merges the
+// query heads w, w + 4, ... of the group, lane i owning output channels i and
+// i + 64, so no step needs a block-wide reduction.  R_V is staged once in LDS
+// with a row stride of 129 floats: lane i reading rows i and i + 64 at column
+// k hits bank (i + k) % 32, no conflicts.
 constexpr int kRvStride = kHeadDim + 1;
 
-__device__ __forceinline__ float block_max256(float x, float* red) {
+__device__ __forceinline__ float wave_max(float x) {
   for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
-  __syncthreads();
-  x = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  __syncthreads();
   return x;
 }
-__device__ __forceinline__ float block_sum256(float x, float* red) {
+__device__ __forceinline__ float wave_sum(float x) {
   for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
-  __syncthreads();
-  x = (red[0] + red[1]) + (red[2] + red[3]);
-  __syncthreads();
   return x;
+}
+__device__ __forceinline__ float lane_value(float x, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+}
+
+// rows [u0, u1) of one chunk of 64 splits, weights held by lanes u of `wt`:
+// acc0 / acc1 += w_u row_u[lane] / row_u[lane + 64]
+__device__ __forceinline__ void weighted_rows(const float* rows, float wt, int u0, int u1, float& acc0,
+                                              float& acc1) {
+  const int lane = threadIdx.x & 63;
+  int u = u0;
+  for (; u + 8 <= u1; u += 8) {
+    float x0[8], x1[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      x0[k] = rows[(u + k) * kPartialStride + 2 + lane];
+      x1[k] = rows[(u + k) * kPartialStride + 2 + 64 + lane];
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float wk = lane_value(wt, u + k);
+      acc0 = fmaf(wk, x0[k], acc0);
+      acc1 = fmaf(wk, x1[k], acc1);
+    }
+  }
+  for (; u < u1; ++u) {
+    const float wk = lane_value(wt, u);
+    acc0 = fmaf(wk, rows[u * kPartialStride + 2 + lane], acc0);
+    acc1 = fmaf(wk, rows[u * kPartialStride + 2 + 64 + lane], acc1);
+  }
 }
 
 __global__ __launch_bounds__(256) void decode_combine(DecodeParams p) {
   __shared__ float rv[kHeadDim * kRvStride];
-  __shared__ float half_sum[3][2][kHeadDim];
-  __shared__ float aint[kHeadDim];
-  __shared__ float wts[256];
-  __shared__ float red[4];
+  __shared__ __attribute__((aligned(16))) float aint[4][kHeadDim];
   const int bk = blockIdx.x;
   const int b = bk / p.n_kv, kv = bk % p.n_kv;
-  const int t = threadIdx.x, j = t & (kHeadDim - 1), hf = t >> 7;
-  const int S = p.splits_int2 + p.splits_bf16;
-  if (p.splits_int2 > 0) stage_matrix256<kRvStride>(p.r_v + (int64_t)kv * kHeadDim * kHeadDim, rv);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int S = p.splits_int2 + p.splits_bf16, SI = p.splits_int2;
+  if (SI > 0) stage_matrix256<kRvStride>(p.r_v + (int64_t)kv * kHeadDim * kHeadDim, rv);
   __syncthreads();
-  for (int h = 0; h < p.g; ++h) {
+  for (int h0 = 0; h0 < p.g; h0 += 4) {  // same trip count in every wavefront
+    const int h = h0 + w;
     const int hq = kv * p.g + h;
-    const float* base = p.partial + ((int64_t)b * p.n_q + hq) * S * kPartialStride;
-    float m = kNegInf;
-    for (int s = t; s < S; s += 256) m = fmaxf(m, base[s * kPartialStride]);
-    const float M = block_max256(m, red);
-    float l = 0.f;
-    if (M != kNegInf)
-      for (int s = t; s < S; s += 256) {
-        const float ms = base[s * kPartialStride];
-        if (ms != kNegInf) l = fmaf(exp2f(ms - M), base[s * kPartialStride + 1], l);
+    float M = kNegInf, L = 0.f, ai0 = 0.f, ai1 = 0.f, ab0 = 0.f, ab1 = 0.f;
+    if (h < p.g) {
+      const float* base = p.partial + ((int64_t)b * p.n_q + hq) * S * kPartialStride;
+      float m = kNegInf;
+      for (int s = lane; s < S; s += 64) m = fmaxf(m, base[s * kPartialStride]);
+      M = wave_max(m);
+      if (M != kNegInf) {
+        for (int c0 = 0; c0 < S; c0 += 64) {
+          const int s = c0 + lane;
+          float wt = 0.f;
+          if (s < S) {
+            const float ms = base[s * kPartialStride];
+            wt = ms == kNegInf ? 0.f : exp2f(ms - M);  // a split without tokens has zero rows
+            L = fmaf(wt, base[s * kPartialStride + 1], L);
+          }
+          const int cn = min(64, S - c0);
+          const int ci = max(0, min(cn, SI - c0));  // INT2 splits of this chunk come first
+          const float* rows = base + (int64_t)c0 * kPartialStride;
+          weighted_rows(rows, wt, 0, ci, ai0, ai1);
+          weighted_rows(rows, wt, ci, cn, ab0, ab1);
+        }
+        L = wave_sum(L);
       }
-    const float L = block_sum256(l, red);
-    // weighted sums of the partial rows: this thread takes channel j of every
-    // other split (half hf), separately for the INT2 and the bf16 splits; the
-    // weights of 256 splits at a time go through LDS so the row loads are
-    // independent of each other
-    float ai = 0.f, ab = 0.f;
-    if (M != kNegInf) {
-      for (int c0 = 0; c0 < S; c0 += 256) {
-        const int cn = min(256, S - c0);
-        if (t < cn) {
-          const float ms = base[(c0 + t) * kPartialStride];
-          wts[t] = ms == kNegInf ? 0.f : exp2f(ms - M);  // a split without tokens has zero rows
+      aint[w][lane] = ai0;
+      aint[w][lane + 64] = ai1;
+    }
+    __syncthreads();
+    if (h < p.g) {
+      // R_V^T on the INT2 part: out_j = sum_k aint_k R_V[j][k]
+      float r0 = 0.f, r1 = 0.f;
+      if (SI > 0) {
+        const float* row0 = rv + lane * kRvStride;
+        const float* row1 = rv + (lane + 64) * kRvStride;
+#pragma unroll 8
+        for (int k = 0; k < kHeadDim; k += 4) {
+          const float4 a = *(const float4*)&aint[w][k];
+          r0 = fmaf(a.x, row0[k], r0);
+          r1 = fmaf(a.x, row1[k], r1);
+          r0 = fmaf(a.y, row0[k + 1], r0);
+          r1 = fmaf(a.y, row1[k + 1], r1);
+          r0 = fmaf(a.z, row0[k + 2], r0);
+          r1 = fmaf(a.z, row1[k + 2], r1);
+          r0 = fmaf(a.w, row0[k + 3], r0);
+          r1 = fmaf(a.w, row1[k + 3], r1);
         }
-        __syncthreads();
-        const int si = max(0, min(cn, p.splits_int2 - c0));  // INT2 splits of this chunk
-        int s = hf;
-        for (; s + 6 < si; s += 8) {
-          float x[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) x[u] = base[(c0 + s + 2 * u) * kPartialStride + 2 + j];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) ai = fmaf(wts[s + 2 * u], x[u], ai);
-        }
-        for (; s < si; s += 2) ai = fmaf(wts[s], base[(c0 + s) * kPartialStride + 2 + j], ai);
-        for (; s + 6 < cn; s += 8) {
-          float x[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) x[u] = base[(c0 + s + 2 * u) * kPartialStride + 2 + j];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) ab = fmaf(wts[s + 2 * u], x[u], ab);
-        }
-        for (; s < cn; s += 2) ab = fmaf(wts[s], base[(c0 + s) * kPartialStride + 2 + j], ab);
-        __syncthreads();
       }
-    }
-    half_sum[0][hf][j] = ai;
-    half_sum[1][hf][j] = ab;
-    __syncthreads();
-    if (hf == 0) aint[j] = half_sum[0][0][j] + half_sum[0][1][j];
-    __syncthreads();
-    // R_V^T on the INT2 part: out_j = sum_i aint_i R_V[j][i], i split over the halves
-    float r = 0.f;
-    if (p.splits_int2 > 0) {
-      const float* row = rv + j * kRvStride + 64 * hf;
-      const float* a = aint + 64 * hf;
-#pragma unroll 16
-      for (int i = 0; i < 64; ++i) r = fmaf(a[i], row[i], r);
-    }
-    half_sum[2][hf][j] = r;
-    __syncthreads();
-    if (hf == 0) {
-      const float abf = half_sum[1][0][j] + half_sum[1][1][j];
-      const float o = (M == kNegInf) ? 0.f : ((half_sum[2][0][j] + half_sum[2][1][j]) + abf) / L;
-      p.out[((int64_t)b * p.n_q + hq) * kHeadDim + j] = o;
+      float* o = p.out + ((int64_t)b * p.n_q + hq) * kHeadDim;
+      const bool empty = M == kNegInf;
+      o[lane] = empty ? 0.f : (r0 + ab0) / L;
+      o[lane + 64] = empty ? 0.f : (r1 + ab1) / L;
     }
     __syncthreads();
   }
 }
 
 template <int NG, int CT>
-hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
+hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop,
+                           const SideStream* side) {
   const int bkn = p.batch * p.n_kv;
   // the event pair brackets the dominant kernel: the INT2 stream when there is
   // one, else the bf16 stream
@@ -1101,14 +1240,19 @@ hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream, hipEvent_t
   auto mark = [&](hipEvent_t ev) { return ev ? hipEventRecord(ev, stream) : hipSuccess; };
   hipError_t e = hipSuccess;
   if (int2) {
-    hipLaunchKernelGGL((decode_prologue<NG, CT>), dim3(bkn), dim3(256), 0, stream, p);
+    if (p.step_slots)
+      hipLaunchKernelGGL((decode_prologue<NG, CT, true>), dim3(bkn), dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((decode_prologue<NG, CT, false>), dim3(bkn), dim3(256), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if (p.splits_bf16 > 0) {
-    if (!int2 && (e = mark(ev_start)) != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_bf16, dim3(bkn * p.splits_bf16), dim3(64), 0, stream, p);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (!int2 && (e = mark(ev_stop)) != hipSuccess) return e;
+  // with an INT2 kernel to hide behind, the bf16 kernel runs on the side
+  // stream: after the prologue (whose writes it reads), beside the INT2 kernel,
+  // joined before the combine
+  const bool fork = int2 && side && p.splits_bf16 > 0;
+  if (fork) {
+    if ((e = hipEventRecord(side->fork, stream)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(side->stream, side->fork, 0)) != hipSuccess) return e;
   }
   if (int2) {
     if ((e = mark(ev_start)) != hipSuccess) return e;
@@ -1116,21 +1260,33 @@ hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream, hipEvent_t
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = mark(ev_stop)) != hipSuccess) return e;
   }
+  if (p.splits_bf16 > 0) {
+    const hipStream_t sb = fork ? side->stream : stream;
+    if (!int2 && (e = mark(ev_start)) != hipSuccess) return e;
+    hipLaunchKernelGGL(decode_bf16, dim3(bkn * p.splits_bf16), dim3(64), 0, sb, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (!int2 && (e = mark(ev_stop)) != hipSuccess) return e;
+  }
+  if (fork) {
+    if ((e = hipEventRecord(side->join, side->stream)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(stream, side->join, 0)) != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(decode_combine, dim3(bkn), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeParams& p, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop,
+                         const SideStream* side) {
   if (p.ng == 4) {
-    if (p.ct == 1) return launch_decode_t<4, 1>(p, stream, ev_start, ev_stop);
-    if (p.ct == 2) return launch_decode_t<4, 2>(p, stream, ev_start, ev_stop);
-    if (p.ct == 3) return launch_decode_t<4, 3>(p, stream, ev_start, ev_stop);
+    if (p.ct == 1) return launch_decode_t<4, 1>(p, stream, ev_start, ev_stop, side);
+    if (p.ct == 2) return launch_decode_t<4, 2>(p, stream, ev_start, ev_stop, side);
+    if (p.ct == 3) return launch_decode_t<4, 3>(p, stream, ev_start, ev_stop, side);
   } else if (p.ng == 2) {
-    if (p.ct == 1) return launch_decode_t<2, 1>(p, stream, ev_start, ev_stop);
-    if (p.ct == 2) return launch_decode_t<2, 2>(p, stream, ev_start, ev_stop);
-    if (p.ct == 3) return launch_decode_t<2, 3>(p, stream, ev_start, ev_stop);
+    if (p.ct == 1) return launch_decode_t<2, 1>(p, stream, ev_start, ev_stop, side);
+    if (p.ct == 2) return launch_decode_t<2, 2>(p, stream, ev_start, ev_stop, side);
+    if (p.ct == 3) return launch_decode_t<2, 3>(p, stream, ev_start, ev_stop, side);
   }
   return hipErrorInvalidValue;
 }

@@ -9,6 +9,9 @@
 #include <cstdio>
 #include <cstring>
 #include <limits>
+#include <atomic>
+#include <map>
+#include <mutex>
 #include <string>
 #include <thread>
 #include <vector>
@@ -613,11 +616,9 @@ oscar_status oscar_plan_decode_step(oscar_pool* pool, oscar_seq* const* seqs, in
     int32_t src = -1, dst = -1;
     oscar_status st = oscar_seq_plan_append(pool, seqs[i], 1, &int2_slots[i], &bf16_slots[i], &src, &dst, &n_age_i);
     if (st) return st;
-    if (n_age_i) {
-      age_src[na] = src;
-      age_dst[na] = dst;
-      ++na;
-    }
+    age_src[i] = n_age_i ? src : -1;
+    age_dst[i] = n_age_i ? dst : -1;
+    na += n_age_i ? 1 : 0;
     ctx_lens[i] = (int32_t)seqs[i]->len;
   }
   *n_age = na;
@@ -770,11 +771,43 @@ size_t oscar_decode_workspace_bytes(const oscar_shape* shape, int32_t batch, int
   return decode_workspace_bytes(batch, shape->n_q_heads, shape->n_kv_heads, ct_of(shape), si + sb);
 }
 
+// Side stream per device for the bf16-region kernel (default priority), with
+// its fork / join events; launches that use it hold the lock so that each
+// record / wait pair belongs to one call.
+static std::atomic<bool> g_overlap{true};
+static std::mutex g_side_mu;
+static std::map<int, SideStream> g_side;
+
+static oscar_status side_stream(SideStream** out) {
+  *out = nullptr;
+  if (!g_overlap) return OSCAR_OK;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(OSCAR_EHIP, "hipGetDevice failed");
+  auto it = g_side.find(dev);
+  if (it == g_side.end()) {
+    SideStream ss{};
+    if (hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess)
+      return fail(OSCAR_EHIP, "side stream creation failed");
+    it = g_side.emplace(dev, ss).first;
+  }
+  *out = &it->second;
+  return OSCAR_OK;
+}
+
+struct StepWrites {
+  const void* k_new;
+  const void* v_new;
+  const int32_t* step_slots;
+};
+
 static oscar_status decode_common(const oscar_shape* shape, const oscar_layer* layer, const oscar_cache* cache,
                                   const void* q, int32_t batch, const int32_t* int2_bt, int32_t max_int2_pages,
                                   const int32_t* bf16_bt, int32_t max_bf16_pages, const int32_t* ctx_lens,
                                   int32_t splits_int2, int32_t splits_bf16, float* out, void* workspace,
-                                  size_t workspace_bytes, void* stream, bool baseline) {
+                                  size_t workspace_bytes, void* stream, bool baseline,
+                                  const StepWrites* writes = nullptr) {
   oscar_status st = check_shape(shape);
   if (st) return st;
   if (batch < 0) return fail(OSCAR_EINVAL, "batch < 0");
@@ -829,13 +862,44 @@ static oscar_status decode_common(const oscar_shape* shape, const oscar_layer* l
   if (workspace_bytes < need) return fail(OSCAR_EINVAL, "workspace %zu bytes < %zu needed", workspace_bytes, need);
   decode_workspace_carve(p, workspace);
   p.out = out;
+  if (writes) {
+    p.step_slots = writes->step_slots;
+    p.k_new = (const uint16_t*)writes->k_new;
+    p.v_new = (const uint16_t*)writes->v_new;
+    p.int2_w = (uint8_t*)cache->int2_pages;
+    p.bf16_w = (uint8_t*)cache->bf16_pages;
+    p.tau_k = layer->tau_k;
+    p.tau_v = layer->tau_v;
+  }
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
   if (g_prof.on) {
     if (hipEventCreate(&ev0) != hipSuccess || hipEventCreate(&ev1) != hipSuccess)
       return fail(OSCAR_EHIP, "hipEventCreate failed");
     g_prof.events.emplace_back(ev0, ev1);
   }
-  return hip_status(launch_decode(p, (hipStream_t)stream, ev0, ev1), "decode launch");
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  SideStream* side = nullptr;
+  if (!baseline && (st = side_stream(&side))) return st;
+  return hip_status(launch_decode(p, (hipStream_t)stream, ev0, ev1, side), "decode launch");
+}
+
+oscar_status oscar_decode_step(const oscar_shape* shape, const oscar_layer* layer, const oscar_cache* cache,
+                               const void* k_new, const void* v_new, const int32_t* step_slots, const void* q,
+                               int32_t batch, const int32_t* int2_bt, int32_t max_int2_pages,
+                               const int32_t* bf16_bt, int32_t max_bf16_pages, const int32_t* ctx_lens,
+                               int32_t splits_int2, int32_t splits_bf16, float* out, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (batch > 0 && (!k_new || !v_new || !step_slots)) return fail(OSCAR_EINVAL, "NULL step input");
+  if (!aligned(k_new, 2) || !aligned(v_new, 2) || !aligned(step_slots, 4))
+    return fail(OSCAR_EINVAL, "step inputs misaligned");
+  const StepWrites w{k_new, v_new, step_slots};
+  return decode_common(shape, layer, cache, q, batch, int2_bt, max_int2_pages, bf16_bt, max_bf16_pages, ctx_lens,
+                       splits_int2, splits_bf16, out, workspace, workspace_bytes, stream, false, &w);
+}
+
+oscar_status oscar_set_overlap(int32_t on) {
+  g_overlap = on != 0;
+  return ok();
 }
 
 oscar_status oscar_decode_attn(const oscar_shape* shape, const oscar_layer* layer, const oscar_cache* cache,

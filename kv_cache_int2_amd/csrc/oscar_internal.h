@@ -59,6 +59,15 @@ struct DecodeParams {
   float* qaux;                // [B*n_kv][1 + 32*ct]: logit factor, 2 Qbar per row, -3 Qbar per row (int bits)
   float* partial;             // [B][Hq][splits][2 + d]: m (log2), l, acc
   float* out;                 // [B][Hq][d]
+  // fused decode-step writes (step_slots null: none), done by the prologue
+  // kernel before the attention kernels read the cache
+  const int32_t* step_slots;  // [4][B]: INT2 slot and bf16 slot of the new token,
+                              // bf16 source and INT2 destination of the token leaving the window
+  const uint16_t* k_new;      // bf16 [B][n_kv][d]: the step's new token
+  const uint16_t* v_new;
+  uint8_t* int2_w;            // writable views of the two storages
+  uint8_t* bf16_w;
+  double tau_k, tau_v;
 };
 
 hipError_t launch_quant_write(const QuantParams& p, int mode, hipStream_t stream);
@@ -67,7 +76,14 @@ hipError_t launch_bf16_write(const uint16_t* k, const uint16_t* v, const int32_t
 hipError_t launch_copy_pages(uint8_t* base, int64_t block_bytes_all_heads, int64_t n_pages, const int32_t* src,
                              const int32_t* dst, int64_t n, hipStream_t stream);
 // ev_start / ev_stop (may be null): recorded on `stream` around the main kernel.
-hipError_t launch_decode(const DecodeParams& p, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop);
+// side (may be null): a second stream on which the bf16-region kernel runs
+// beside the INT2 kernel, forked and joined with the two events `fork`, `join`.
+struct SideStream {
+  hipStream_t stream;
+  hipEvent_t fork, join;
+};
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop,
+                         const SideStream* side);
 
 // Workspace bytes for the decode path (each region 256-byte aligned).
 size_t decode_workspace_bytes(int batch, int n_q, int n_kv, int ct, int splits_total);

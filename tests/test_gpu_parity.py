@@ -343,3 +343,80 @@ def test_full_size_28x100k_sampled():
         _flush(f"long_28x100k request {r}: {len(lps)} INT2 pages x {w.n_kv_heads} heads and the bf16 pages, "
                f"mismatching blocks={mism}")
         assert mism == 0
+
+
+@pytest.mark.parametrize("hq,hkv,group,sink,recent", [(8, 2, 32, 4, 32), (12, 1, 64, 20, 48), (4, 1, 32, 4, 0)])
+def test_fused_decode_step(hq, hkv, group, sink, recent):
+    """oscar_decode_step (writes fused into the decode, bf16 kernel on the side
+    stream) against the separate write calls + oscar_decode_attn in order on one
+    stream: identical cache bytes and bit-identical outputs after every step,
+    through ring age-out, page crossings, sink growth and (recent = 0) new
+    tokens quantised straight to INT2; then the pages bit-exact and the output
+    within tolerance against the oracle."""
+    from kv_cache_int2_amd.torch_cache import to_dev_bits, to_dev_i32
+    w = synth.Workload("fused", 70 + hq + group, hq, hkv, 128, 1, 0, group=group, sink=sink, recent=recent,
+                       outlier_scale=(40.0, 40.0), calib_tokens=512)
+    _flush(f"case fused step hq={hq} hkv={hkv} G={group} sink={sink} recent={recent}")
+    cal = _calibrate(w)
+    sh = K.make_shape(n_q_heads=hq, n_kv_heads=hkv, group=group, sink=sink, recent=recent)
+    lens0 = [0, 3, sink + recent - 2, 200, 1001]
+    n_steps = 40
+    B = len(lens0)
+    caches = [DeviceCache(sh, cal.r_k, cal.r_v, cal.tau_k, cal.tau_v, 600, 64) for _ in range(2)]
+    seqs = [[], []]
+    for r, t in enumerate(lens0):
+        kb, vb = synth.kv_request_bf16(w, r, 0, t)
+        for c in (0, 1):
+            s = caches[c].new_seq()
+            if t:
+                caches[c].append(s, kb, vb)
+            seqs[c].append(s)
+    planners = [K.DecodeStepPlanner(caches[c].pool, seqs[c]) for c in (0, 1)]
+    max_i2 = (max(lens0) + n_steps + 15) // 16
+    max_bf = -(-sink // 16) + recent // 16 + 1
+    si = 3
+    ws = [torch.empty(K.oscar_decode_workspace_bytes(sh, B, si, 1), dtype=torch.uint8, device="cuda")
+          for _ in (0, 1)]
+    outs = [torch.empty((B, hq, 128), dtype=torch.float32, device="cuda") for _ in (0, 1)]
+    try:
+        for st in range(n_steps):
+            kn = np.stack([synth.kv_request_bf16(w, r, lens0[r] + st, lens0[r] + st + 1)[0][0] for r in range(B)])
+            vn = np.stack([synth.kv_request_bf16(w, r, lens0[r] + st, lens0[r] + st + 1)[1][0] for r in range(B)])
+            q = to_dev_bits(np.stack([synth.q_decode_bf16(w, r, st + 1) for r in range(B)]))
+            kd, vd = to_dev_bits(kn), to_dev_bits(vn)
+            res = [planners[c].step() for c in (0, 1)]
+            bufs = [planners[c].buf.copy() for c in (0, 1)]
+            assert np.array_equal(bufs[0], bufs[1]) and res[0] == res[1]
+            d = to_dev_i32(bufs[0])
+            tabs = [caches[c].tables(seqs[c], max_i2, max_bf) for c in (0, 1)]
+            dt = [(to_dev_i32(i2), to_dev_i32(bf), to_dev_i32(ctx)) for i2, bf, ctx in tabs]
+            c0, c1 = caches
+            # separate calls, one stream
+            K.oscar_set_overlap(False)
+            if res[0][0]:
+                K.oscar_requant_from_bf16(sh, c0.layer, c0.cache, d[2], d[3], n=B)
+            if np.any(bufs[0][0] >= 0):
+                K.oscar_quant_write(sh, c0.layer, c0.cache, kd, vd, d[0], n=B)
+            if np.any(bufs[0][1] >= 0):
+                K.oscar_bf16_write(sh, c0.cache, kd, vd, d[1], n=B)
+            K.oscar_decode_attn(sh, c0.layer, c0.cache, q, *dt[0][:2], dt[0][2], outs[0], ws[0], si, 1)
+            # fused step, side stream
+            K.oscar_set_overlap(True)
+            K.oscar_decode_step(sh, c1.layer, c1.cache, kd, vd, d[:4], q, *dt[1][:2], dt[1][2], outs[1], ws[1],
+                                si, 1)
+            torch.cuda.synchronize()
+            assert torch.equal(outs[0], outs[1]), f"step {st}: outputs differ"
+            if st % 8 == 7 or st == n_steps - 1:
+                assert torch.equal(c0.int2, c1.int2), f"step {st}: INT2 storage differs"
+                assert torch.equal(c0.bf16, c1.bf16), f"step {st}: bf16 storage differs"
+    finally:
+        K.oscar_set_overlap(True)
+    _flush(f"fused step: {n_steps} steps identical to the separate calls")
+    out = outs[1].cpu().numpy()
+    qf = np.stack([synth.q_decode_bf16(w, r, n_steps) for r in range(B)])
+    for r in range(B):
+        t = lens0[r] + n_steps
+        kb, vb = synth.kv_request_bf16(w, r, 0, t)
+        store = O.store_request(kb, vb, cal, group, sink, recent)
+        _check_pages(caches[1], seqs[1][r], store, w, f"fused step len={t}")
+        _check_close(out[r], O.decode_attention(qf[r], store, cal, group), f"fused step decode len={t}")
