@@ -4,11 +4,10 @@ One step = one decode step for the whole batch: host region planning
 (oscar_plan_decode_step), then oscar_decode_step: re-quantisation of the
 tokens leaving the recent window and bf16 append of every request's new token
 (fused into the prologue kernel), and mixed-precision paged decode attention
-(prologue, INT2 kernel with the bf16-region kernel beside it on a second
-stream, split-K combine).  --unfused runs the same step as separate write
-calls and in-order kernels.  The cache is resident in HBM before the timed
-region; the inputs of the steps are generated and uploaded beforehand (128
-distinct sets, used in turn).
+(prologue, INT2 kernel, bf16-region kernel, split-K combine).  --unfused runs
+the same step with the writes as separate calls.  The cache is resident in
+HBM before the timed region; the inputs of the steps are generated and
+uploaded beforehand (128 distinct sets, used in turn).
 
 Prints one JSON line.  value = KV tokens attended per second (summed context
 lengths of all requests and steps / wall time of the timed steps).
@@ -182,7 +181,8 @@ def main():
     max_i2 = (T_final + 15) // 16
     max_bf = w.sink // 16 + 1 + w.recent // 16
     si = args.splits or K.oscar_decode_auto_splits(sh, B, max_i2)
-    ws = torch.empty(K.oscar_decode_workspace_bytes(sh, B, si, 1), dtype=torch.uint8, device="cuda")
+    sb_step = 4                                 # bf16 splits, run inside the combine kernel
+    ws = torch.empty(K.oscar_decode_workspace_bytes(sh, B, si, sb_step), dtype=torch.uint8, device="cuda")
     out = torch.empty((B, hq, 128), dtype=torch.float32, device="cuda")
     i2_bt, bf_bt, ctx = dc.tables(seqs, max_i2, max_bf)
     tables = [to_dev_i32(i2_bt), to_dev_i32(bf_bt)]
@@ -204,10 +204,10 @@ def main():
             if np.any(planner.buf[0] >= 0):
                 K.oscar_quant_write(sh, dc.layer, dc.cache, new_k_d[si_], new_v_d[si_], d[0], n=B)
             K.oscar_bf16_write(sh, dc.cache, new_k_d[si_], new_v_d[si_], d[1], n=B)
-            K.oscar_decode_attn(sh, dc.layer, dc.cache, q_d[si_], tables[0], tables[1], d[4], out, ws, si, 1)
+            K.oscar_decode_attn(sh, dc.layer, dc.cache, q_d[si_], tables[0], tables[1], d[4], out, ws, si, sb_step)
         else:
             K.oscar_decode_step(sh, dc.layer, dc.cache, new_k_d[si_], new_v_d[si_], d[:4], q_d[si_], tables[0],
-                                tables[1], d[4], out, ws, si, 1)
+                                tables[1], d[4], out, ws, si, sb_step)
         ctx_hist.append(planner.buf[4].astype(np.int64).copy())
 
     for st in range(args.warmup):

@@ -215,7 +215,8 @@ oscar_status oscar_copy_pages(const oscar_shape* shape, const oscar_cache* cache
  * [batch][max_int2_pages]; bf16_bt int32 [batch][max_bf16_pages]; ctx_lens
  * int32 [batch].  Output (device): out fp32 [batch][n_q_heads][d].
  * splits_int2 / splits_bf16: work items per (request, KV head) for the INT2 and
- * bf16 regions (0 = choose).  workspace: device, >= oscar_decode_workspace_bytes
+ * bf16 regions (0 = choose; up to four bf16 splits run inside the merging
+ * kernel, one per wavefront).  workspace: device, >= oscar_decode_workspace_bytes
  * with the same arguments, 256-byte aligned.  T = 0 gives a zero row. */
 size_t oscar_decode_workspace_bytes(const oscar_shape* shape, int32_t batch, int32_t splits_int2,
                                     int32_t splits_bf16);
@@ -272,13 +273,6 @@ oscar_status oscar_decode_step(const oscar_shape* shape, const oscar_layer* laye
                                const int32_t* bf16_bt, int32_t max_bf16_pages, const int32_t* ctx_lens,
                                int32_t splits_int2, int32_t splits_bf16, float* out, void* workspace,
                                size_t workspace_bytes, void* stream);
-
-/* Whether oscar_decode_attn / oscar_decode_step run the bf16-region kernel on
- * a second stream of the library's (default priority, one per device, created
- * at first use) beside the INT2 kernel (on != 0, the default), or in order on
- * the caller's stream.  The results are the same either way; calls that use
- * the second stream are serialised by a lock while they enqueue. */
-oscar_status oscar_set_overlap(int32_t on);
 
 /* Instrumentation.  While enabled (on != 0), each decode launch made by the
  * calling thread records a pair of HIP events on its stream around the main

@@ -69,7 +69,6 @@ _SIGS = {
     "oscar_decode_step": (C.c_int32, [C.POINTER(Shape), C.POINTER(Layer), C.POINTER(Cache), P, P, P, P,
                                       C.c_int32, P, C.c_int32, P, C.c_int32, P, C.c_int32, C.c_int32, P, P,
                                       C.c_size_t, P]),
-    "oscar_set_overlap": (C.c_int32, [C.c_int32]),
     "oscar_decode_attn_bf16_baseline": (C.c_int32, [C.POINTER(Shape), C.POINTER(Cache), P, C.c_int32, P,
                                                     C.c_int32, P, C.c_int32, P, P, C.c_size_t, P]),
     "oscar_decode_auto_splits": (C.c_int32, [C.POINTER(Shape), C.c_int32, C.c_int32]),
@@ -288,10 +287,6 @@ def oscar_decode_step(shape, layer, cache, k_new, v_new, step_slots, q, int2_bt,
                                    _ptr(step_slots), _ptr(q), batch, _ptr(int2_bt), int2_bt.shape[1], _ptr(bf16_bt),
                                    bf16_bt.shape[1], _ptr(ctx_lens), splits_int2, splits_bf16, _ptr(out),
                                    _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
-
-
-def oscar_set_overlap(on: bool):
-    _check(lib().oscar_set_overlap(1 if on else 0))
 
 
 def oscar_decode_attn_bf16_baseline(shape, cache, q, bf16_bt, ctx_lens, out, workspace, splits=0, stream=None):

@@ -474,7 +474,7 @@ struct Int2Offsets {
 template <int NG>
 __device__ __forceinline__ Int2Offsets int2_offsets() {
   constexpr Int2Layout L{NG};
-  const int lane = threadIdx.x, ln = lane & 15, qd = lane >> 4;
+  const int lane = threadIdx.x & 63, ln = lane & 15, qd = lane >> 4;
   return Int2Offsets{(uint32_t)(L.k_codes() + ln * 32 + 8 * qd), (uint32_t)(L.k_sz() + ln * NG * 4),
                      (uint32_t)(L.v_codes() + qd * kHeadDim + 8 * ln),
                      (uint32_t)(L.v_sz() + ((ln % NG) * kPage + 4 * qd) * 4)};
@@ -543,7 +543,7 @@ __device__ __forceinline__ void int2_issue(const uint8_t* blk0, const uint8_t* b
   constexpr Int2Layout L{NG};
   constexpr int kRest = (L.bytes() - 1024) / 16;
   static_assert(L.bytes() > 1024 && L.bytes() <= 2048 && L.bytes() % 16 == 0, "block staging layout");
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const u32x4 rs = block_rsrc(t ? blk1 : blk0, L.bytes());
@@ -605,7 +605,7 @@ template <int NG, int CT, bool EDGE, class Src>
 __device__ __forceinline__ void int2_pair(const Src& src, int lp0, int p_end, int lo, int hi,
                                           const Int2Const<NG, CT>& K, Int2State<NG, CT>& S, float* p_lds) {
   constexpr int HPL = 4 / NG;
-  const int lane = threadIdx.x, ln = lane & 15, qd = lane >> 4;
+  const int lane = threadIdx.x & 63, ln = lane & 15, qd = lane >> 4;
   // ---- logits ----
   const Int2KData<NG> DK = src.k();
   bool valid[2];
@@ -776,7 +776,7 @@ template <int NG, int CT>
 __device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float* p_lds, uint8_t* stage) {
   constexpr Int2Layout L{NG};
   constexpr int HPL = 4 / NG;
-  const int lane = threadIdx.x, ln = lane & 15, qd = lane >> 4;
+  const int lane = threadIdx.x & 63, ln = lane & 15, qd = lane >> 4;
   const int T = p.ctx_lens[b];
   const int lo = p.sink;
   const int hi = T - p.recent;
@@ -943,7 +943,7 @@ template <bool EDGE>
 __device__ __forceinline__ void bf16_pair(const DecodeParams& p, const uint8_t* blk0, const uint8_t* blk1, int lp0,
                                           int p_end, int n_sink, int ring0, int n_rec, const u32x4 (&bq)[4],
                                           float& m_run, float& l_run, f32x4 (&acc)[8]) {
-  const int lane = threadIdx.x, ln = lane & 15, qd = lane >> 4;
+  const int lane = threadIdx.x & 63, ln = lane & 15, qd = lane >> 4;
   const int a = qd & 1;
   const uint8_t* bk = (ln >> 3) ? blk1 : blk0;
   const int tokA = 8 * ((ln >> 2) & 1) + (ln & 3);
@@ -1026,7 +1026,7 @@ __device__ __forceinline__ void bf16_pair(const DecodeParams& p, const uint8_t* 
 }
 
 __device__ void bf16_item(const DecodeParams& p, int b, int kv, int split) {
-  const int lane = threadIdx.x, ln = lane & 15, qd = lane >> 4;
+  const int lane = threadIdx.x & 63, ln = lane & 15, qd = lane >> 4;
   const int T = p.ctx_lens[b];
   const int n_sink = min(p.sink, T);
   const int ring0 = kPage * ((p.sink + kPage - 1) / kPage);
@@ -1115,14 +1115,19 @@ __global__ __launch_bounds__(64) void decode_bf16(DecodeParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// combine: LSE merge, R_V^T on the INT2 part, normalisation
+// combine: bf16 region (when its splits fit the block), LSE merge, R_V^T on
+// the INT2 part, normalisation
 // ---------------------------------------------------------------------------
-// One block of four wavefronts per (request, KV head); wavefront w merges the
-// query heads w, w + 4, ... of the group, lane i owning output channels i and
-// i + 64, so no step needs a block-wide reduction.  R_V is staged once in LDS
-// with a row stride of 129 floats: lane i reading rows i and i + 64 at column
-// k hits bank (i + k) % 32, no conflicts.
+// One block of four wavefronts per (request, KV head).  With bf16_in_combine,
+// wavefront w first runs bf16 split w (at most four) and leaves its partial
+// beside the INT2 splits' ones.  Then wavefront w merges the query heads w,
+// w + 4, ... of the group, lane i owning output channels i and i + 64, so no
+// step needs a block-wide reduction; the first 32 partial rows of a head are
+// loaded at once, behind the split maxima.  R_V is staged once in LDS with a
+// row stride of 129 floats: lane i reading rows i and i + 64 at column k hits
+// bank (i + k) % 32, no conflicts.
 constexpr int kRvStride = kHeadDim + 1;
+constexpr int kCombineRows = 32;
 
 __device__ __forceinline__ float wave_max(float x) {
   for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
@@ -1171,29 +1176,58 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeParams p) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int S = p.splits_int2 + p.splits_bf16, SI = p.splits_int2;
   if (SI > 0) stage_matrix256<kRvStride>(p.r_v + (int64_t)kv * kHeadDim * kHeadDim, rv);
-  __syncthreads();
+  if (p.bf16_in_combine && w < p.splits_bf16) bf16_item(p, b, kv, SI + w);
+  __syncthreads();  // R_V staged; the bf16 partials written by this block are visible to it
   for (int h0 = 0; h0 < p.g; h0 += 4) {  // same trip count in every wavefront
     const int h = h0 + w;
     const int hq = kv * p.g + h;
     float M = kNegInf, L = 0.f, ai0 = 0.f, ai1 = 0.f, ab0 = 0.f, ab1 = 0.f;
     if (h < p.g) {
       const float* base = p.partial + ((int64_t)b * p.n_q + hq) * S * kPartialStride;
-      float m = kNegInf;
-      for (int s = lane; s < S; s += 64) m = fmaxf(m, base[s * kPartialStride]);
+      // split maxima first, then the first rows, so that the max reduction
+      // waits only for the former
+      const float ms = lane < S ? base[lane * kPartialStride] : kNegInf;
+      const float ls = lane < S ? base[lane * kPartialStride + 1] : 0.f;
+      float m = ms;
+      for (int s = lane + 64; s < S; s += 64) m = fmaxf(m, base[s * kPartialStride]);
+      const int n0 = min(S, kCombineRows);
+      float x0[kCombineRows], x1[kCombineRows];
+#pragma unroll
+      for (int k = 0; k < kCombineRows; ++k) {
+        x0[k] = k < n0 ? base[k * kPartialStride + 2 + lane] : 0.f;
+        x1[k] = k < n0 ? base[k * kPartialStride + 2 + 64 + lane] : 0.f;
+      }
       M = wave_max(m);
       if (M != kNegInf) {
+        // a split without tokens has m = -inf and zero rows: weight 0
+        const float wt0 = ms == kNegInf ? 0.f : exp2f(ms - M);
+        L = wt0 * ls;
+#pragma unroll
+        for (int k = 0; k < kCombineRows; ++k) {
+          const float wk = lane_value(wt0, k);  // 0 past S
+          const float wi = k < SI ? wk : 0.f, wb = k < SI ? 0.f : wk;
+          ai0 = fmaf(wi, x0[k], ai0);
+          ai1 = fmaf(wi, x1[k], ai1);
+          ab0 = fmaf(wb, x0[k], ab0);
+          ab1 = fmaf(wb, x1[k], ab1);
+        }
+        // the rest of the first 64 splits, then further chunks of 64
         for (int c0 = 0; c0 < S; c0 += 64) {
-          const int s = c0 + lane;
-          float wt = 0.f;
-          if (s < S) {
-            const float ms = base[s * kPartialStride];
-            wt = ms == kNegInf ? 0.f : exp2f(ms - M);  // a split without tokens has zero rows
-            L = fmaf(wt, base[s * kPartialStride + 1], L);
+          float wt = wt0;
+          if (c0 > 0) {
+            const int s = c0 + lane;
+            wt = 0.f;
+            if (s < S) {
+              const float mc = base[s * kPartialStride];
+              wt = mc == kNegInf ? 0.f : exp2f(mc - M);
+              L = fmaf(wt, base[s * kPartialStride + 1], L);
+            }
           }
+          const int u0 = c0 == 0 ? n0 : 0;
           const int cn = min(64, S - c0);
-          const int ci = max(0, min(cn, SI - c0));  // INT2 splits of this chunk come first
+          const int ci = max(u0, min(cn, SI - c0));  // INT2 splits come first
           const float* rows = base + (int64_t)c0 * kPartialStride;
-          weighted_rows(rows, wt, 0, ci, ai0, ai1);
+          weighted_rows(rows, wt, u0, ci, ai0, ai1);
           weighted_rows(rows, wt, ci, cn, ab0, ab1);
         }
         L = wave_sum(L);
@@ -1231,11 +1265,13 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeParams p) {
 }
 
 template <int NG, int CT>
-hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop,
-                           const SideStream* side) {
+hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
   const int bkn = p.batch * p.n_kv;
   // the event pair brackets the dominant kernel: the INT2 stream when there is
-  // one, else the bf16 stream
+  // one, else the bf16 stream.  (Running the bf16 kernel on a second stream
+  // beside the INT2 kernel was measured slower: its wavefronts take slots from
+  // the INT2 kernel's full rounds.  Up to four bf16 splits run inside the
+  // combine instead.)
   const bool int2 = p.splits_int2 > 0;
   auto mark = [&](hipEvent_t ev) { return ev ? hipEventRecord(ev, stream) : hipSuccess; };
   hipError_t e = hipSuccess;
@@ -1245,31 +1281,16 @@ hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream, hipEvent_t
     else
       hipLaunchKernelGGL((decode_prologue<NG, CT, false>), dim3(bkn), dim3(256), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
-  // with an INT2 kernel to hide behind, the bf16 kernel runs on the side
-  // stream: after the prologue (whose writes it reads), beside the INT2 kernel,
-  // joined before the combine
-  const bool fork = int2 && side && p.splits_bf16 > 0;
-  if (fork) {
-    if ((e = hipEventRecord(side->fork, stream)) != hipSuccess) return e;
-    if ((e = hipStreamWaitEvent(side->stream, side->fork, 0)) != hipSuccess) return e;
-  }
-  if (int2) {
     if ((e = mark(ev_start)) != hipSuccess) return e;
     hipLaunchKernelGGL((decode_int2<NG, CT>), dim3(bkn * p.splits_int2), dim3(64), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = mark(ev_stop)) != hipSuccess) return e;
   }
-  if (p.splits_bf16 > 0) {
-    const hipStream_t sb = fork ? side->stream : stream;
+  if (p.splits_bf16 > 0 && !p.bf16_in_combine) {
     if (!int2 && (e = mark(ev_start)) != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_bf16, dim3(bkn * p.splits_bf16), dim3(64), 0, sb, p);
+    hipLaunchKernelGGL(decode_bf16, dim3(bkn * p.splits_bf16), dim3(64), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (!int2 && (e = mark(ev_stop)) != hipSuccess) return e;
-  }
-  if (fork) {
-    if ((e = hipEventRecord(side->join, side->stream)) != hipSuccess) return e;
-    if ((e = hipStreamWaitEvent(stream, side->join, 0)) != hipSuccess) return e;
   }
   hipLaunchKernelGGL(decode_combine, dim3(bkn), dim3(256), 0, stream, p);
   return hipGetLastError();
@@ -1277,16 +1298,15 @@ hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream, hipEvent_t
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeParams& p, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop,
-                         const SideStream* side) {
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
   if (p.ng == 4) {
-    if (p.ct == 1) return launch_decode_t<4, 1>(p, stream, ev_start, ev_stop, side);
-    if (p.ct == 2) return launch_decode_t<4, 2>(p, stream, ev_start, ev_stop, side);
-    if (p.ct == 3) return launch_decode_t<4, 3>(p, stream, ev_start, ev_stop, side);
+    if (p.ct == 1) return launch_decode_t<4, 1>(p, stream, ev_start, ev_stop);
+    if (p.ct == 2) return launch_decode_t<4, 2>(p, stream, ev_start, ev_stop);
+    if (p.ct == 3) return launch_decode_t<4, 3>(p, stream, ev_start, ev_stop);
   } else if (p.ng == 2) {
-    if (p.ct == 1) return launch_decode_t<2, 1>(p, stream, ev_start, ev_stop, side);
-    if (p.ct == 2) return launch_decode_t<2, 2>(p, stream, ev_start, ev_stop, side);
-    if (p.ct == 3) return launch_decode_t<2, 3>(p, stream, ev_start, ev_stop, side);
+    if (p.ct == 1) return launch_decode_t<2, 1>(p, stream, ev_start, ev_stop);
+    if (p.ct == 2) return launch_decode_t<2, 2>(p, stream, ev_start, ev_stop);
+    if (p.ct == 3) return launch_decode_t<2, 3>(p, stream, ev_start, ev_stop);
   }
   return hipErrorInvalidValue;
 }

@@ -9,9 +9,6 @@
 #include <cstdio>
 #include <cstring>
 #include <limits>
-#include <atomic>
-#include <map>
-#include <mutex>
 #include <string>
 #include <thread>
 #include <vector>
@@ -771,31 +768,6 @@ size_t oscar_decode_workspace_bytes(const oscar_shape* shape, int32_t batch, int
   return decode_workspace_bytes(batch, shape->n_q_heads, shape->n_kv_heads, ct_of(shape), si + sb);
 }
 
-// Side stream per device for the bf16-region kernel (default priority), with
-// its fork / join events; launches that use it hold the lock so that each
-// record / wait pair belongs to one call.
-static std::atomic<bool> g_overlap{true};
-static std::mutex g_side_mu;
-static std::map<int, SideStream> g_side;
-
-static oscar_status side_stream(SideStream** out) {
-  *out = nullptr;
-  if (!g_overlap) return OSCAR_OK;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return fail(OSCAR_EHIP, "hipGetDevice failed");
-  auto it = g_side.find(dev);
-  if (it == g_side.end()) {
-    SideStream ss{};
-    if (hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking) != hipSuccess ||
-        hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess)
-      return fail(OSCAR_EHIP, "side stream creation failed");
-    it = g_side.emplace(dev, ss).first;
-  }
-  *out = &it->second;
-  return OSCAR_OK;
-}
-
 struct StepWrites {
   const void* k_new;
   const void* v_new;
@@ -852,7 +824,10 @@ static oscar_status decode_common(const oscar_shape* shape, const oscar_layer* l
     p.sink = shape->sink;
     p.recent = shape->recent;
     p.splits_int2 = splits_int2 ? splits_int2 : oscar_decode_auto_splits(shape, batch, max_int2_pages);
-    p.splits_bf16 = splits_bf16 ? splits_bf16 : 1;
+    // up to four bf16 splits run inside the combine kernel (one per wavefront);
+    // the bf16 region is at most sink + recent tokens
+    p.splits_bf16 = splits_bf16 ? splits_bf16 : 4;
+    p.bf16_in_combine = p.splits_bf16 <= 4;
     // P' = p s 2^sp stays below 2^15: s <= 2 tau_v / 3 (rounded to fp16), p <= 1
     const double smax = 2.0 * (double)layer->tau_v / 3.0;
     p.p_scale_exp = 0.f;
@@ -877,10 +852,7 @@ static oscar_status decode_common(const oscar_shape* shape, const oscar_layer* l
       return fail(OSCAR_EHIP, "hipEventCreate failed");
     g_prof.events.emplace_back(ev0, ev1);
   }
-  std::lock_guard<std::mutex> lock(g_side_mu);
-  SideStream* side = nullptr;
-  if (!baseline && (st = side_stream(&side))) return st;
-  return hip_status(launch_decode(p, (hipStream_t)stream, ev0, ev1, side), "decode launch");
+  return hip_status(launch_decode(p, (hipStream_t)stream, ev0, ev1), "decode launch");
 }
 
 oscar_status oscar_decode_step(const oscar_shape* shape, const oscar_layer* layer, const oscar_cache* cache,
@@ -897,10 +869,6 @@ oscar_status oscar_decode_step(const oscar_shape* shape, const oscar_layer* laye
                        splits_int2, splits_bf16, out, workspace, workspace_bytes, stream, false, &w);
 }
 
-oscar_status oscar_set_overlap(int32_t on) {
-  g_overlap = on != 0;
-  return ok();
-}
 
 oscar_status oscar_decode_attn(const oscar_shape* shape, const oscar_layer* layer, const oscar_cache* cache,
                                const void* q, int32_t batch, const int32_t* int2_bt, int32_t max_int2_pages,

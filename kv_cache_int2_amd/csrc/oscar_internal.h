@@ -53,6 +53,7 @@ struct DecodeParams {
   int batch, n_q, n_kv, g, ng, ct;
   int sink, recent;           // region rule (baseline: sink huge, recent 0)
   int splits_int2, splits_bf16;
+  int bf16_in_combine;        // bf16 splits (<= 4) run by the combine kernel's wavefronts
   float p_scale_exp;          // P' is scaled by 2^p_scale_exp before fp16 rounding
   // workspace carve-up
   uint32_t* qb;               // [B*n_kv][ct][3 digits][2 k-steps][64 lanes][4] int8x4 words: digits of 2Q
@@ -76,14 +77,7 @@ hipError_t launch_bf16_write(const uint16_t* k, const uint16_t* v, const int32_t
 hipError_t launch_copy_pages(uint8_t* base, int64_t block_bytes_all_heads, int64_t n_pages, const int32_t* src,
                              const int32_t* dst, int64_t n, hipStream_t stream);
 // ev_start / ev_stop (may be null): recorded on `stream` around the main kernel.
-// side (may be null): a second stream on which the bf16-region kernel runs
-// beside the INT2 kernel, forked and joined with the two events `fork`, `join`.
-struct SideStream {
-  hipStream_t stream;
-  hipEvent_t fork, join;
-};
-hipError_t launch_decode(const DecodeParams& p, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop,
-                         const SideStream* side);
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop);
 
 // Workspace bytes for the decode path (each region 256-byte aligned).
 size_t decode_workspace_bytes(int batch, int n_q, int n_kv, int ct, int splits_total);

@@ -71,7 +71,7 @@ class DeviceCache:
         i2, bf, ctx = tables if tables is not None else self.tables(seqs)
         B = len(seqs)
         si = splits_int2 or K.oscar_decode_auto_splits(self.shape, B, i2.shape[1])
-        sb = splits_bf16 or 1
+        sb = splits_bf16 or 4
         ws = torch.empty(K.oscar_decode_workspace_bytes(self.shape, B, si, sb), dtype=torch.uint8, device="cuda")
         out = torch.empty((B, self.shape.n_q_heads, 128), dtype=torch.float32, device="cuda")
         K.oscar_decode_attn(self.shape, self.layer, self.cache, to_dev_bits(q_bits), to_dev_i32(i2), to_dev_i32(bf),

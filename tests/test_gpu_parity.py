@@ -180,10 +180,11 @@ def test_ragged_batch_gqa_groups(hq, hkv, group):
         _check_pages(dc, seqs[r], stores[r], w, f"ragged len={lens[r]}")
     q = np.stack(qs)
     ref = np.stack([O.decode_attention(q[r], stores[r], cal, group) for r in range(len(lens))])
-    for si in (0, 1, 4):
-        out = dc.decode(seqs, q, splits_int2=si).cpu().numpy()
+    # bf16 splits <= 4 run inside the combine kernel, 5 in their own kernel
+    for si, sb in ((0, 0), (1, 1), (4, 3), (1, 5)):
+        out = dc.decode(seqs, q, splits_int2=si, splits_bf16=sb).cpu().numpy()
         for r in range(len(lens)):
-            _check_close(out[r], ref[r], f"ragged hq={hq} G={group} len={lens[r]} splits={si}")
+            _check_close(out[r], ref[r], f"ragged hq={hq} G={group} len={lens[r]} splits={si}/{sb}")
 
 
 def test_empty_context_gives_zero_rows():
@@ -347,9 +348,8 @@ def test_full_size_28x100k_sampled():
 
 @pytest.mark.parametrize("hq,hkv,group,sink,recent", [(8, 2, 32, 4, 32), (12, 1, 64, 20, 48), (4, 1, 32, 4, 0)])
 def test_fused_decode_step(hq, hkv, group, sink, recent):
-    """oscar_decode_step (writes fused into the decode, bf16 kernel on the side
-    stream) against the separate write calls + oscar_decode_attn in order on one
-    stream: identical cache bytes and bit-identical outputs after every step,
+    """oscar_decode_step (writes fused into the decode's prologue kernel) against
+    the separate write calls + oscar_decode_attn: identical cache bytes and bit-identical outputs after every step,
     through ring age-out, page crossings, sink growth and (recent = 0) new
     tokens quantised straight to INT2; then the pages bit-exact and the output
     within tolerance against the oracle."""
@@ -378,39 +378,34 @@ def test_fused_decode_step(hq, hkv, group, sink, recent):
     ws = [torch.empty(K.oscar_decode_workspace_bytes(sh, B, si, 1), dtype=torch.uint8, device="cuda")
           for _ in (0, 1)]
     outs = [torch.empty((B, hq, 128), dtype=torch.float32, device="cuda") for _ in (0, 1)]
-    try:
-        for st in range(n_steps):
-            kn = np.stack([synth.kv_request_bf16(w, r, lens0[r] + st, lens0[r] + st + 1)[0][0] for r in range(B)])
-            vn = np.stack([synth.kv_request_bf16(w, r, lens0[r] + st, lens0[r] + st + 1)[1][0] for r in range(B)])
-            q = to_dev_bits(np.stack([synth.q_decode_bf16(w, r, st + 1) for r in range(B)]))
-            kd, vd = to_dev_bits(kn), to_dev_bits(vn)
-            res = [planners[c].step() for c in (0, 1)]
-            bufs = [planners[c].buf.copy() for c in (0, 1)]
-            assert np.array_equal(bufs[0], bufs[1]) and res[0] == res[1]
-            d = to_dev_i32(bufs[0])
-            tabs = [caches[c].tables(seqs[c], max_i2, max_bf) for c in (0, 1)]
-            dt = [(to_dev_i32(i2), to_dev_i32(bf), to_dev_i32(ctx)) for i2, bf, ctx in tabs]
-            c0, c1 = caches
-            # separate calls, one stream
-            K.oscar_set_overlap(False)
-            if res[0][0]:
-                K.oscar_requant_from_bf16(sh, c0.layer, c0.cache, d[2], d[3], n=B)
-            if np.any(bufs[0][0] >= 0):
-                K.oscar_quant_write(sh, c0.layer, c0.cache, kd, vd, d[0], n=B)
-            if np.any(bufs[0][1] >= 0):
-                K.oscar_bf16_write(sh, c0.cache, kd, vd, d[1], n=B)
-            K.oscar_decode_attn(sh, c0.layer, c0.cache, q, *dt[0][:2], dt[0][2], outs[0], ws[0], si, 1)
-            # fused step, side stream
-            K.oscar_set_overlap(True)
-            K.oscar_decode_step(sh, c1.layer, c1.cache, kd, vd, d[:4], q, *dt[1][:2], dt[1][2], outs[1], ws[1],
-                                si, 1)
-            torch.cuda.synchronize()
-            assert torch.equal(outs[0], outs[1]), f"step {st}: outputs differ"
-            if st % 8 == 7 or st == n_steps - 1:
-                assert torch.equal(c0.int2, c1.int2), f"step {st}: INT2 storage differs"
-                assert torch.equal(c0.bf16, c1.bf16), f"step {st}: bf16 storage differs"
-    finally:
-        K.oscar_set_overlap(True)
+    for st in range(n_steps):
+        kn = np.stack([synth.kv_request_bf16(w, r, lens0[r] + st, lens0[r] + st + 1)[0][0] for r in range(B)])
+        vn = np.stack([synth.kv_request_bf16(w, r, lens0[r] + st, lens0[r] + st + 1)[1][0] for r in range(B)])
+        q = to_dev_bits(np.stack([synth.q_decode_bf16(w, r, st + 1) for r in range(B)]))
+        kd, vd = to_dev_bits(kn), to_dev_bits(vn)
+        res = [planners[c].step() for c in (0, 1)]
+        bufs = [planners[c].buf.copy() for c in (0, 1)]
+        assert np.array_equal(bufs[0], bufs[1]) and res[0] == res[1]
+        d = to_dev_i32(bufs[0])
+        tabs = [caches[c].tables(seqs[c], max_i2, max_bf) for c in (0, 1)]
+        dt = [(to_dev_i32(i2), to_dev_i32(bf), to_dev_i32(ctx)) for i2, bf, ctx in tabs]
+        c0, c1 = caches
+        # separate calls
+        if res[0][0]:
+            K.oscar_requant_from_bf16(sh, c0.layer, c0.cache, d[2], d[3], n=B)
+        if np.any(bufs[0][0] >= 0):
+            K.oscar_quant_write(sh, c0.layer, c0.cache, kd, vd, d[0], n=B)
+        if np.any(bufs[0][1] >= 0):
+            K.oscar_bf16_write(sh, c0.cache, kd, vd, d[1], n=B)
+        K.oscar_decode_attn(sh, c0.layer, c0.cache, q, *dt[0][:2], dt[0][2], outs[0], ws[0], si, 1)
+        # fused step
+        K.oscar_decode_step(sh, c1.layer, c1.cache, kd, vd, d[:4], q, *dt[1][:2], dt[1][2], outs[1], ws[1],
+                            si, 1)
+        torch.cuda.synchronize()
+        assert torch.equal(outs[0], outs[1]), f"step {st}: outputs differ"
+        if st % 8 == 7 or st == n_steps - 1:
+            assert torch.equal(c0.int2, c1.int2), f"step {st}: INT2 storage differs"
+            assert torch.equal(c0.bf16, c1.bf16), f"step {st}: bf16 storage differs"
     _flush(f"fused step: {n_steps} steps identical to the separate calls")
     out = outs[1].cpu().numpy()
     qf = np.stack([synth.q_decode_bf16(w, r, n_steps) for r in range(B)])
