@@ -25,19 +25,17 @@
 //   three balanced int8 digits.  A = the digits, block-diagonal over channel
 //   groups (row (h, gamma) only sees channels of group gamma), B = the 2-bit
 //   codes as int8 bytes (columns = tokens).  The digit chains feed each other
-//   (acc <- (acc << 8) + sum d c) and the last starts from -3 Qbar, so the
-//   accumulator ends holding, exactly,
-//     C2 = sum_{j in gamma} Q_j (2 c_j - 3),     Qbar = sum_{j in gamma} Q_j,
-//   and  sum_j Q_j (z + c_j s) = (s/2) C2 + (z + 1.5 s) Qbar.  The large, nearly
-//   cancelling terms s C and z Qbar of the direct form are never rounded.
+//   (acc <- (acc << 8) + sum d c), so the accumulator ends holding, exactly,
+//     C = sum_{j in gamma} 2 Q_j c_j   (|C| < 2^29),   Qbar = sum_{j in gamma} Q_j,
+//   and  sum_j 2 Q_j (z + c_j s) = s C + z 2 Qbar, two fp32 products whose
+//   rounding (2^-24 of the larger term) stays far below the logit tolerance.
 // INT2 values on MFMA (v_mfma_f32_16x16x32_f16):
 //   A = P'[(h, gamma), t] = p_ht s_t,gamma 2^sp 4^-r as fp16 hi + lo (about 22
-//   significant bits), B = centred codes (2c - 3) 4^r 2^-24, exact fp16
-//   subnormals built from the packed bytes with one mask and one packed fma.
-//   The accumulator row (h, gamma) is kept for the channels of group gamma.
-//   With the midpoint w = z + 1.5 s the value is w + (2c - 3) s / 2: the VALU
-//   sums p w, the MFMA sums p s (2c - 3), whose signs keep its accumulation
-//   unbiased.
+//   significant bits), B = the codes as exact fp16 subnormals c 4^r 2^-24 cut
+//   from the packed bytes with one mask.  Odd token slots enter as -P' against
+//   3 - c, so the products' signs alternate and the MFMA's accumulation stays
+//   unbiased; the VALU sums p z and the 3 P' of the odd slots.  The
+//   accumulator row (h, gamma) is kept for the channels of group gamma.
 // bf16 tokens use v_mfma_f32_16x16x32_bf16 with the unrotated query (exact
 // products) and P split into bf16 hi + mid + lo.
 #include <hip/hip_runtime.h>
@@ -291,8 +289,8 @@ __device__ void step_writes(const DecodeParams& p, int b, int kv, const float* r
 // prologue: q R_K operands
 // ---------------------------------------------------------------------------
 // Words per (request, KV head): A digits of 2Q ((((ct*3 + digit)*2 + kstep)*64 + lane)*4 + reg),
-// then aux floats [1 + 32*CT]: logit factor 2^-sq / 2, per row 2*Qbar (float),
-// per row -3*Qbar (int32 bits).  WRITE: the decode-step writes come first.
+// then aux floats [1 + 16*CT]: logit factor 2^-sq / 2, per row 2*Qbar (float).
+// WRITE: the decode-step writes come first.
 template <int NG, int CT, bool WRITE>
 __global__ __launch_bounds__(256) void decode_prologue(DecodeParams p) {
   const int bk = blockIdx.x;
@@ -368,7 +366,7 @@ __global__ __launch_bounds__(256) void decode_prologue(DecodeParams p) {
   for (int k = 0; k < 8; ++k)
     if (hf + 2 * k < g) qi[hf + 2 * k][j] = (int)rintf(ldexpf(qt[k], sq));
   __syncthreads();
-  float* aux = p.qaux + (int64_t)bk * (1 + 32 * CT);
+  float* aux = p.qaux + (int64_t)bk * (1 + 16 * CT);
   if (t == 0) aux[0] = ldexpf(0.5f, -sq);
   if (t < 16 * CT) {
     const int h = t / NG, gam = t % NG;
@@ -376,7 +374,6 @@ __global__ __launch_bounds__(256) void decode_prologue(DecodeParams p) {
     if (h < g)
       for (int c = gam * G; c < (gam + 1) * G; ++c) sum += qi[h][c];
     aux[1 + t] = 2.0f * (float)sum;
-    aux[1 + 16 * CT + t] = __builtin_bit_cast(float, -3 * sum);
   }
   uint32_t* qb = p.qb + (int64_t)bk * CT * 3 * 2 * 64 * 4;
   for (int w = t; w < CT * 3 * 2 * 64 * 4; w += 256) {
@@ -406,10 +403,9 @@ __global__ __launch_bounds__(256) void decode_prologue(DecodeParams p) {
 // main kernel: INT2 work item
 //
 // Per iteration one wavefront takes two pages (32 tokens) of one (request, KV
-// head).  Logits: C[(h, gamma), t] = sum_j 2Q_hj c_tj - 3 Qbar on the int8 MFMA
-// with A = digits of 2Q (rows (h, gamma)), B = codes (columns = the 16 tokens
-// of one page); the -3 Qbar enters as the initial accumulator of the low
-// digit.  Lane l then holds, for the head of its row group and token l%16, all
+// head).  Logits: C[(h, gamma), t] = sum_j 2Q_hj c_tj on the int8 MFMA with
+// A = digits of 2Q (rows (h, gamma)), B = codes (columns = the 16 tokens of one
+// page).  Lane l then holds, for the head of its row group and token l%16, all
 // channel groups, so the group sum and the exp need no cross-lane traffic.
 // The running max is lazy: it moves, with a margin, only when a logit passes
 // it (one ballot per pair); only then are row maxima reduced and the
@@ -440,7 +436,6 @@ struct Int2State {
 template <int NG, int CT>
 struct Int2Const {
   u32x4 qa[CT][3][2];  // digits of 2Q: A operand, rows 16ct + ln
-  i32x4 qneg3[CT];     // -3 Qbar of the accumulator rows 16ct + 4qd + r
   float qbar2[CT][4];  // 2 Qbar of those rows
   float kfac, ikfac;   // raw logit -> log2 units, and its inverse (powers of two)
   float lpf;           // log2(pscale 4^-(ln % 4)): P' factor of the token this lane writes
@@ -631,14 +626,12 @@ __device__ __forceinline__ void int2_pair(const Src& src, int lp0, int p_end, in
     }
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
-      // digit chains feed each other: acc <- (acc << 8) + sum d_k c, the low
-      // digit's chain starting from (acc << 8) - 3 Qbar; every partial value is
-      // an exact integer below 2^31 in magnitude
+      // digit chains feed each other: acc <- (acc << 8) + sum d_k c; every
+      // partial value is an exact integer below 2^31 in magnitude
       i32x4 cd = i32x4{0, 0, 0, 0};
 #pragma unroll
       for (int d = 0; d < 3; ++d) {
-        if (d == 1) cd = cd << 8;
-        if (d == 2) cd = (cd << 8) + K.qneg3[ct];
+        if (d > 0) cd = cd << 8;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) cd = mfma_i8(K.qa[ct][d][ks], av[ks], cd);
       }
@@ -648,9 +641,9 @@ __device__ __forceinline__ void int2_pair(const Src& src, int lp0, int p_end, in
 #pragma unroll
         for (int gg = 0; gg < NG; ++gg) {
           const int r = hh * NG + gg;
-          const int c2 = cd[r];  // sum_j 2Q_j c_j - 3 Qbar = sum_j Q_j (2 c_j - 3)
+          const int c2 = cd[r];  // sum_j 2Q_j c_j
           const float sv = half_lo(DK.ksz[t][gg]), zv = half_hi(DK.ksz[t][gg]);
-          x = fmaf(sv, (float)c2, fmaf(fmaf(1.5f, sv, zv), K.qbar2[ct][r], x));
+          x = fmaf(sv, (float)c2, fmaf(zv, K.qbar2[ct][r], x));
         }
         lg[t][ct][hh] = valid[t] ? x : kNegInf;
       }
@@ -797,7 +790,7 @@ __device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float
 #pragma unroll
     for (int kt = 0; kt < 8; ++kt) S.acc[ct][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  const float* aux = p.qaux + (int64_t)bk * (1 + 32 * CT);
+  const float* aux = p.qaux + (int64_t)bk * (1 + 16 * CT);
   const float pscale = exp2f(p.p_scale_exp);
   if (hi > lo && lo >= 0) {
     const int first = lo / kPage, last = (hi - 1) / kPage;
@@ -816,10 +809,7 @@ __device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks) K.qa[ct][d][ks] = qb[((ct * 3 + d) * 2 + ks) * 64 + lane];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          K.qbar2[ct][r] = aux[1 + 16 * ct + 4 * qd + r];
-          K.qneg3[ct][r] = __builtin_bit_cast(int, aux[1 + 16 * CT + 16 * ct + 4 * qd + r]);
-        }
+        for (int r = 0; r < 4; ++r) K.qbar2[ct][r] = aux[1 + 16 * ct + 4 * qd + r];
       }
       K.kfac = aux[0];
       K.ikfac = 1.0f / K.kfac;
@@ -1317,7 +1307,7 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t decode_workspace_bytes(int batch, int n_q, int n_kv, int ct, int splits_total) {
   const size_t bkn = (size_t)batch * n_kv;
-  return align256(bkn * ct * 3 * 2 * 64 * 4 * sizeof(uint32_t)) + align256(bkn * (1 + 32 * ct) * sizeof(float)) +
+  return align256(bkn * ct * 3 * 2 * 64 * 4 * sizeof(uint32_t)) + align256(bkn * (1 + 16 * ct) * sizeof(float)) +
          align256((size_t)batch * n_q * splits_total * kPartialStride * sizeof(float));
 }
 
@@ -1327,7 +1317,7 @@ void decode_workspace_carve(DecodeParams& p, void* ws) {
   p.qb = (uint32_t*)w;
   w += align256(bkn * p.ct * 3 * 2 * 64 * 4 * sizeof(uint32_t));
   p.qaux = (float*)w;
-  w += align256(bkn * (1 + 32 * p.ct) * sizeof(float));
+  w += align256(bkn * (1 + 16 * p.ct) * sizeof(float));
   p.partial = (float*)w;
 }
 

@@ -57,7 +57,7 @@ struct DecodeParams {
   float p_scale_exp;          // P' is scaled by 2^p_scale_exp before fp16 rounding
   // workspace carve-up
   uint32_t* qb;               // [B*n_kv][ct][3 digits][2 k-steps][64 lanes][4] int8x4 words: digits of 2Q
-  float* qaux;                // [B*n_kv][1 + 32*ct]: logit factor, 2 Qbar per row, -3 Qbar per row (int bits)
+  float* qaux;                // [B*n_kv][1 + 16*ct]: logit factor, 2 Qbar per row
   float* partial;             // [B][Hq][splits][2 + d]: m (log2), l, acc
   float* out;                 // [B][Hq][d]
   // fused decode-step writes (step_slots null: none), done by the prologue
