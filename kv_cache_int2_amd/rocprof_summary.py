@@ -1,8 +1,10 @@
 """Summaries of rocprofv3 result databases (SQLite) for the OSCAR kernels.
 
-    python -m kv_cache_int2_amd.rocprof_summary trace DB --command CMD
+    python -m kv_cache_int2_amd.rocprof_summary trace DB --command CMD [--tail NAME:N]
         per-kernel dispatch statistics (count, average / min / max duration),
-        as a short markdown table.
+        as a short markdown table; --tail adds the same statistics over the
+        last N dispatches of the kernel whose name contains NAME (the timed
+        steps of a run, without its warm-up).
 
     python -m kv_cache_int2_amd.rocprof_summary pmc --fetch DB --write DB
         --kernel NAME --copy NAME --copy-bytes N --workload W --source FILE
@@ -44,6 +46,16 @@ def counter_per_dispatch(db: str, counter: str, kernel: str):
     return [v for _, v in con.execute(q, (counter, f"%{kernel}%")).fetchall()]
 
 
+def tail_stats(db: str, kernel: str, n: int):
+    con = sqlite3.connect(db)
+    d = [r[0] for r in con.execute("select duration from kernels where name like ? order by start desc limit ?",
+                                   (f"%{kernel}%", n)).fetchall()]
+    if not d:
+        sys.exit(f"no dispatches of {kernel} in {db}")
+    return dict(calls=len(d), avg_us=sum(d) / len(d) / 1e3, min_us=min(d) / 1e3, max_us=max(d) / 1e3,
+                total_ms=sum(d) / 1e6)
+
+
 def cmd_trace(a):
     rows = kernel_stats(a.db)
     out = [f"# rocprofv3 kernel trace: {a.title}", "", "Command:", "", "```", a.command, "```", "",
@@ -51,6 +63,16 @@ def cmd_trace(a):
     for r in rows:
         out.append(f"| {r['name']} | {r['calls']} | {r['avg_us']:.2f} | {r['min_us']:.2f} | {r['max_us']:.2f} "
                    f"| {r['total_ms']:.3f} |")
+    for spec in a.tail or []:
+        name, n = spec.rsplit(":", 1)
+        r = tail_stats(a.db, name, int(n))
+        out += ["", f"Last {r['calls']} dispatches of {name}:", "",
+                "| kernel | calls | avg us | min us | max us | total ms |", "|---|---:|---:|---:|---:|---:|",
+                f"| {name} (last {r['calls']}) | {r['calls']} | {r['avg_us']:.2f} | {r['min_us']:.2f} "
+                f"| {r['max_us']:.2f} | {r['total_ms']:.3f} |"]
+    if a.notes:
+        with open(a.notes) as f:
+            out += ["", f.read().rstrip()]
     print("\n".join(out))
 
 
@@ -85,6 +107,8 @@ def main(argv=None):
     t.add_argument("db")
     t.add_argument("--command", required=True)
     t.add_argument("--title", default="")
+    t.add_argument("--tail", action="append", help="NAME:N, statistics of the last N dispatches")
+    t.add_argument("--notes", help="text file appended to the summary")
     p = sub.add_parser("pmc")
     for k in ("fetch", "write", "kernel", "copy", "workload", "source", "command"):
         p.add_argument("--" + k, required=True)
