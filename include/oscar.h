@@ -70,7 +70,7 @@ typedef int32_t oscar_status;
 
 /* Shape of one attention layer and of the cache layout.
  * Supported: head_dim 128, page_size 16, group 32 or 64, n_q_heads a multiple
- * of n_kv_heads with n_q_heads / n_kv_heads * (head_dim / group) <= 48,
+ * of n_kv_heads with n_q_heads / n_kv_heads * (head_dim / group) <= 64,
  * sink >= 0, recent >= 0 (recent a multiple of page_size or 0). */
 typedef struct oscar_shape {
   int32_t head_dim;    /* d */

@@ -561,6 +561,13 @@ __device__ __forceinline__ void vm_wait() {
     asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
 }
 
+// Workgroup barrier without a memory fence: a fence would make the staging
+// wavefront drain the loads it keeps in flight.  The staged bytes a barrier
+// publishes are complete by then (the staging wavefront's vm_wait comes
+// first), and every wavefront has consumed the LDS data it read before it
+// arrives; the "memory" clobber keeps LDS accesses on their side.
+__device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
+
 // a pair staged in LDS: each part is read when the pair asks for it
 template <int NG>
 struct Int2Staged {
@@ -767,11 +774,15 @@ __device__ __forceinline__ void int2_pair(const Src& src, int lp0, int p_end, in
   }
 }
 
-template <int NG, int CT>
+// W wavefronts per work item: wavefront w takes the CT row tiles starting at
+// tile w CT, all of them reading the same staged pages.
+template <int NG, int CT, int W>
 __device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float* p_lds, uint8_t* stage) {
   constexpr Int2Layout L{NG};
   constexpr int HPL = 4 / NG;
+  constexpr int kTiles = W * CT;  // row tiles of the (request, KV head)
   const int lane = threadIdx.x & 63, ln = lane & 15, qd = lane >> 4;
+  const int t0 = W > 1 ? (int)(threadIdx.x >> 6) * CT : 0;  // first row tile of this wavefront
   const int T = p.ctx_lens[b];
   const int lo = p.sink;
   const int hi = T - p.recent;
@@ -790,7 +801,7 @@ __device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float
 #pragma unroll
     for (int kt = 0; kt < 8; ++kt) S.acc[ct][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  const float* aux = p.qaux + (int64_t)bk * (1 + 16 * CT);
+  const float* aux = p.qaux + (int64_t)bk * (1 + 16 * kTiles);
   const float pscale = exp2f(p.p_scale_exp);
   if (hi > lo && lo >= 0) {
     const int first = lo / kPage, last = (hi - 1) / kPage;
@@ -801,15 +812,15 @@ __device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float
     const int p_end = min(min(first + n_pages, p_begin + pps), p.max_int2_pages);
     if (p_begin < p_end) {
       Int2Const<NG, CT> K;
-      const u32x4* qb = (const u32x4*)(p.qb + (int64_t)bk * CT * 3 * 2 * 64 * 4);
+      const u32x4* qb = (const u32x4*)(p.qb + (int64_t)bk * kTiles * 3 * 2 * 64 * 4);
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
 #pragma unroll
         for (int d = 0; d < 3; ++d)
 #pragma unroll
-          for (int ks = 0; ks < 2; ++ks) K.qa[ct][d][ks] = qb[((ct * 3 + d) * 2 + ks) * 64 + lane];
+          for (int ks = 0; ks < 2; ++ks) K.qa[ct][d][ks] = qb[(((t0 + ct) * 3 + d) * 2 + ks) * 64 + lane];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) K.qbar2[ct][r] = aux[1 + 16 * ct + 4 * qd + r];
+        for (int r = 0; r < 4; ++r) K.qbar2[ct][r] = aux[1 + 16 * (t0 + ct) + 4 * qd + r];
       }
       K.kfac = aux[0];
       K.ikfac = 1.0f / K.kfac;
@@ -846,38 +857,80 @@ __device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float
       const int main_end = min(p_end, hi / kPage);
       constexpr int kSlot = 2 * L.bytes();
       const uint32_t a0 = lds_address(stage);
-      while (lp0 + 2 <= main_end) {
-        const int c0 = lp0;
-        const int cn = min(64, main_end - c0);
-        const int id = lane < cn ? bt[c0 + lane] : 0;
-        const uint64_t bad = __builtin_amdgcn_ballot_w64(lane < cn && !ok(id));
-        const int lim = bad ? c0 + (int)__builtin_ctzll(bad) : c0 + cn;  // pages [c0, lim) have good ids
-        if (lp0 + 2 > lim) break;
-        // every earlier vector load (operands, ids, edge pages) completes here,
-        // where the compiler sees it, so it adds no wait inside the pair loop
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-        auto page = [&](int l) { return blk(__builtin_amdgcn_readlane(id, l - c0)); };
-        int2_issue<NG>(page(lp0), page(lp0 + 1), a0);
-        if (lp0 + 4 <= lim) int2_issue<NG>(page(lp0 + 2), page(lp0 + 3), a0 + kSlot);
-        int cur = 0;  // slot of the pair at lp0 (wavefront-uniform)
-        for (;;) {
-          // stage the pair two ahead into the slot the previous pair freed,
-          // then wait for this pair's bytes
-          const int nxt = cur == 0 ? 2 : cur - 1;
-          if (lp0 + 6 <= lim) {
-            int2_issue<NG>(page(lp0 + 4), page(lp0 + 5), a0 + nxt * kSlot);
-            vm_wait<8>();
-          } else if (lp0 + 4 <= lim) {
-            vm_wait<4>();
-          } else {
-            vm_wait<0>();
-          }
-          int2_pair<NG, CT, false>(Int2Staged<NG>{stage + cur * kSlot, off}, lp0, p_end, lo, hi, K, S, p_lds);
-          lp0 += 2;
+      if constexpr (W == 1) {
+        while (lp0 + 2 <= main_end) {
+          const int c0 = lp0;
+          const int cn = min(64, main_end - c0);
+          const int id = lane < cn ? bt[c0 + lane] : 0;
+          const uint64_t bad = __builtin_amdgcn_ballot_w64(lane < cn && !ok(id));
+          const int lim = bad ? c0 + (int)__builtin_ctzll(bad) : c0 + cn;  // pages [c0, lim) have good ids
           if (lp0 + 2 > lim) break;
-          cur = cur == 2 ? 0 : cur + 1;
+          // every earlier vector load (operands, ids, edge pages) completes here,
+          // where the compiler sees it, so it adds no wait inside the pair loop
+          __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+          auto page = [&](int l) { return blk(__builtin_amdgcn_readlane(id, l - c0)); };
+          int2_issue<NG>(page(lp0), page(lp0 + 1), a0);
+          if (lp0 + 4 <= lim) int2_issue<NG>(page(lp0 + 2), page(lp0 + 3), a0 + kSlot);
+          int cur = 0;  // slot of the pair at lp0 (wavefront-uniform)
+          for (;;) {
+            // stage the pair two ahead into the slot the previous pair freed,
+            // then wait for this pair's bytes
+            const int nxt = cur == 0 ? 2 : cur - 1;
+            if (lp0 + 6 <= lim) {
+              int2_issue<NG>(page(lp0 + 4), page(lp0 + 5), a0 + nxt * kSlot);
+              vm_wait<8>();
+            } else if (lp0 + 4 <= lim) {
+              vm_wait<4>();
+            } else {
+              vm_wait<0>();
+            }
+            int2_pair<NG, CT, false>(Int2Staged<NG>{stage + cur * kSlot, off}, lp0, p_end, lo, hi, K, S, p_lds);
+            lp0 += 2;
+            if (lp0 + 2 > lim) break;
+            cur = cur == 2 ? 0 : cur + 1;
+          }
+          if (lim < c0 + cn) break;  // a bad id: the rest goes through the masked path
         }
-        if (lim < c0 + cn) break;  // a bad id: the rest goes through the masked path
+      } else {
+        // the W wavefronts share one ring of four slots: wavefront 0 stages
+        // two pairs ahead and waits for its loads; one barrier per pair then
+        // publishes the pair to all and certifies that all have finished the
+        // pair before last, whose slot the next staging load reuses
+        const bool leader = t0 == 0;
+        while (lp0 + 2 <= main_end) {
+          const int c0 = lp0;
+          const int cn = min(64, main_end - c0);
+          const int id = lane < cn ? bt[c0 + lane] : 0;
+          const uint64_t bad = __builtin_amdgcn_ballot_w64(lane < cn && !ok(id));
+          const int lim = bad ? c0 + (int)__builtin_ctzll(bad) : c0 + cn;
+          if (lp0 + 2 > lim) break;
+          __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+          barrier_no_fence();  // every wavefront is done with the slots of the previous chunk
+          auto page = [&](int l) { return blk(__builtin_amdgcn_readlane(id, l - c0)); };
+          if (leader) {
+            int2_issue<NG>(page(lp0), page(lp0 + 1), a0);
+            if (lp0 + 4 <= lim) int2_issue<NG>(page(lp0 + 2), page(lp0 + 3), a0 + kSlot);
+          }
+          int cur = 0;
+          for (;;) {
+            if (leader) {
+              if (lp0 + 6 <= lim) {
+                int2_issue<NG>(page(lp0 + 4), page(lp0 + 5), a0 + ((cur + 2) & 3) * kSlot);
+                vm_wait<8>();
+              } else if (lp0 + 4 <= lim) {
+                vm_wait<4>();
+              } else {
+                vm_wait<0>();
+              }
+            }
+            barrier_no_fence();
+            int2_pair<NG, CT, false>(Int2Staged<NG>{stage + cur * kSlot, off}, lp0, p_end, lo, hi, K, S, p_lds);
+            lp0 += 2;
+            if (lp0 + 2 > lim) break;
+            cur = (cur + 1) & 3;
+          }
+          if (lim < c0 + cn) break;
+        }
       }
       for (; lp0 < p_end; lp0 += 2) edge(lp0);
     }
@@ -898,7 +951,7 @@ __device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float zr = __shfl(z, 4 * qd + r);
-      const int row = 16 * ct + 4 * qd + r;
+      const int row = 16 * (t0 + ct) + 4 * qd + r;
       const int h = row / NG, gam_row = row % NG;
 #pragma unroll
       for (int kt = 0; kt < 8; ++kt) {
@@ -913,7 +966,7 @@ __device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float
     for (int hh = 0; hh < HPL; ++hh) {
       const float lpf = p.p_scale_exp - (float)(2 * (ln & 3));
       const float l = row_sum16(S.l_run[ct][hh] * exp2f(-lpf));
-      const int h = (16 * ct + 4 * qd + hh * NG) / NG;
+      const int h = (16 * (t0 + ct) + 4 * qd + hh * NG) / NG;
       if (ln == 0 && h < p.g) {
         float* dst = p.partial + (((int64_t)b * p.n_q + kv * p.g + h) * Ssp + split) * kPartialStride;
         dst[0] = lpf - S.moff[ct][hh];  // -inf when this split saw no token
@@ -1083,20 +1136,20 @@ __device__ void bf16_item(const DecodeParams& p, int b, int kv, int split) {
   }
 }
 
-// register budget: one row tile fits 4 wavefronts per SIMD (128 VGPRs; LDS
-// 9.5-10 KB per wavefront also fits 16 per compute unit); wider GQA groups
-// need more registers
-template <int NG, int CT>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(CT == 1 ? 4 : (CT == 2 ? 2 : 1), 8))) void
+// CT 16-row tiles per wavefront, W wavefronts per work item (tile_split).  One
+// tile fits 4 wavefronts per SIMD (121 VGPRs); two tiles, which share the
+// unpacked codes, 2.  Wavefronts of one item share the staged pages.  LDS per
+// item: each wavefront's p and the staging ring (three slots for one
+// wavefront, four when shared).
+template <int NG, int CT, int W>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(CT == 1 ? 4 : (CT == 2 ? 2 : 1), 8))) void
 decode_int2(DecodeParams p) {
-  // p of the 16 CT / NG heads a wavefront covers, 2 pages x 16 tokens each;
-  // three staging slots of two blocks
-  __shared__ __attribute__((aligned(16))) float p_lds[(16 * CT / NG) * 32];
-  __shared__ __attribute__((aligned(16))) uint8_t stage[6 * Int2Layout{NG}.bytes()];
+  __shared__ __attribute__((aligned(16))) float p_lds[W][(16 * CT / NG) * 32];
+  __shared__ __attribute__((aligned(16))) uint8_t stage[(W == 1 ? 6 : 8) * Int2Layout{NG}.bytes()];
   const int item = blockIdx.x;
   const int split = item % p.splits_int2;
   const int bk = item / p.splits_int2;
-  int2_item<NG, CT>(p, bk / p.n_kv, bk % p.n_kv, split, p_lds, stage);
+  int2_item<NG, CT, W>(p, bk / p.n_kv, bk % p.n_kv, split, p_lds[W > 1 ? threadIdx.x >> 6 : 0], stage);
 }
 
 __global__ __launch_bounds__(64) void decode_bf16(DecodeParams p) {
@@ -1256,7 +1309,7 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeParams p) {
   }
 }
 
-template <int NG, int CT>
+template <int NG, int CT, int W>
 hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
   const int bkn = p.batch * p.n_kv;
   // the event pair brackets the dominant kernel: the INT2 stream when there is
@@ -1269,12 +1322,12 @@ hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream, hipEvent_t
   hipError_t e = hipSuccess;
   if (int2) {
     if (p.step_slots)
-      hipLaunchKernelGGL((decode_prologue<NG, CT, true>), dim3(bkn), dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((decode_prologue<NG, CT * W, true>), dim3(bkn), dim3(256), 0, stream, p);
     else
-      hipLaunchKernelGGL((decode_prologue<NG, CT, false>), dim3(bkn), dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((decode_prologue<NG, CT * W, false>), dim3(bkn), dim3(256), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = mark(ev_start)) != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_int2<NG, CT>), dim3(bkn * p.splits_int2), dim3(64), 0, stream, p);
+    hipLaunchKernelGGL((decode_int2<NG, CT, W>), dim3(bkn * p.splits_int2), dim3(64 * W), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = mark(ev_stop)) != hipSuccess) return e;
   }
@@ -1291,14 +1344,18 @@ hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream, hipEvent_t
 }  // namespace
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
+  // p.ct = 16-row tiles of a (request, KV head), spread as tile_split says
+  const TileSplit ts = tile_split(p.ct);
+  const int key = ts.ct * 10 + ts.w;
+  if (ts.ct * ts.w != p.ct) return hipErrorInvalidValue;
   if (p.ng == 4) {
-    if (p.ct == 1) return launch_decode_t<4, 1>(p, stream, ev_start, ev_stop);
-    if (p.ct == 2) return launch_decode_t<4, 2>(p, stream, ev_start, ev_stop);
-    if (p.ct == 3) return launch_decode_t<4, 3>(p, stream, ev_start, ev_stop);
+    if (key == 11) return launch_decode_t<4, 1, 1>(p, stream, ev_start, ev_stop);
+    if (key == 21) return launch_decode_t<4, 2, 1>(p, stream, ev_start, ev_stop);
+    if (key == 13) return launch_decode_t<4, 1, 3>(p, stream, ev_start, ev_stop);
+    if (key == 22) return launch_decode_t<4, 2, 2>(p, stream, ev_start, ev_stop);
   } else if (p.ng == 2) {
-    if (p.ct == 1) return launch_decode_t<2, 1>(p, stream, ev_start, ev_stop);
-    if (p.ct == 2) return launch_decode_t<2, 2>(p, stream, ev_start, ev_stop);
-    if (p.ct == 3) return launch_decode_t<2, 3>(p, stream, ev_start, ev_stop);
+    if (key == 11) return launch_decode_t<2, 1, 1>(p, stream, ev_start, ev_stop);
+    if (key == 21) return launch_decode_t<2, 2, 1>(p, stream, ev_start, ev_stop);
   }
   return hipErrorInvalidValue;
 }

@@ -52,7 +52,7 @@ oscar_status check_shape(const oscar_shape* s) {
     return fail(OSCAR_EINVAL, "n_q_heads %d must be a positive multiple of n_kv_heads %d", s->n_q_heads, s->n_kv_heads);
   const int g = s->n_q_heads / s->n_kv_heads;
   if (g > 16) return fail(OSCAR_EUNSUPPORTED, "query heads per KV head %d > 16", g);
-  if (g * (kHeadDim / s->group) > 48) return fail(OSCAR_EUNSUPPORTED, "gqa * groups = %d > 48", g * (kHeadDim / s->group));
+  if (g * (kHeadDim / s->group) > 64) return fail(OSCAR_EUNSUPPORTED, "gqa * groups = %d > 64", g * (kHeadDim / s->group));
   if (s->sink < 0 || s->recent < 0) return fail(OSCAR_EINVAL, "sink/recent must be >= 0");
   if (s->recent % kPage) return fail(OSCAR_EUNSUPPORTED, "recent %d must be a multiple of %d", s->recent, kPage);
   if (s->sink > (1 << 26) || s->recent > (1 << 26)) return fail(OSCAR_EINVAL, "sink/recent too large");
@@ -746,15 +746,15 @@ static int device_cus() {
 
 int32_t oscar_decode_auto_splits(const oscar_shape* shape, int32_t batch, int32_t max_int2_pages) {
   if (check_shape(shape) != OSCAR_OK || batch < 1) return 1;
-  // Work items run in rounds of the wavefronts that fit the device at once
-  // (4 SIMDs per compute unit; 4, 2 or 1 wavefronts per SIMD for 1, 2 or 3
-  // row tiles).  A count just above a whole number of rounds leaves a nearly
+  // Work items run in rounds of the items that fit the device at once (4
+  // SIMDs per compute unit, 4 / ct wavefronts per SIMD, w wavefronts per item:
+  // tile_split).  A count just above a whole number of rounds leaves a nearly
   // empty last round that costs a full item time.  Take the count that fills
   // two whole rounds (some slack for uneven requests, few partial results),
   // within [1, 64] and at least 32 pages per split.
   const int64_t pairs = (int64_t)batch * shape->n_kv_heads;
-  const int ct = ct_of(shape);
-  const int64_t cap = (int64_t)device_cus() * 4 * (ct == 1 ? 4 : (ct == 2 ? 2 : 1));
+  const TileSplit ts = tile_split(ct_of(shape));
+  const int64_t cap = (int64_t)device_cus() * 4 * (4 / ts.ct) / ts.w;
   const int64_t smax = std::max<int64_t>(1, std::min<int64_t>(kAutoMaxSplits, max_int2_pages / 32));
   const int64_t s = 2 * cap / pairs;
   return (int32_t)std::max<int64_t>(1, std::min<int64_t>(s, smax));

@@ -71,6 +71,21 @@ struct DecodeParams {
   double tau_k, tau_v;
 };
 
+// How the 16-row tiles of a (request, KV head) spread over the wavefronts of
+// one INT2 work item: CT tiles per wavefront (they share the unpacked codes,
+// at 4 / CT wavefronts per SIMD), W wavefronts (they share the staged pages).
+struct TileSplit {
+  int ct, w;
+};
+inline TileSplit tile_split(int tiles) {
+  switch (tiles) {
+    case 2: return {2, 1};
+    case 3: return {1, 3};
+    case 4: return {2, 2};
+    default: return {1, 1};
+  }
+}
+
 hipError_t launch_quant_write(const QuantParams& p, int mode, hipStream_t stream);
 hipError_t launch_bf16_write(const uint16_t* k, const uint16_t* v, const int32_t* slots, int64_t n, int n_kv,
                              uint8_t* bf16_pages, int64_t n_pages, hipStream_t stream);

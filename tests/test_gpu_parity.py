@@ -157,7 +157,7 @@ def test_qwen3_8b_layer_32k():
         _check_close(out, ref, f"qwen3_8b_32k decode splits={si}")
 
 
-@pytest.mark.parametrize("hq,hkv,group", [(4, 1, 32), (8, 1, 32), (12, 1, 32), (12, 1, 64), (4, 2, 64), (16, 1, 64)])
+@pytest.mark.parametrize("hq,hkv,group", [(4, 1, 32), (8, 1, 32), (12, 1, 32), (16, 1, 32), (12, 1, 64), (4, 2, 64), (16, 1, 64)])
 def test_ragged_batch_gqa_groups(hq, hkv, group):
     """Mixed lengths (all-bf16, exactly sink+recent, one INT2 token, odd page
     counts) in one batch, for several GQA widths and both group sizes."""
