@@ -127,6 +127,23 @@ oscar_status oscar_calibrate_host(const oscar_shape* shape, int64_t n, const flo
                                   float* r_v_out, double* eig_k_out, double* eig_v_out, float* tau_k_out,
                                   float* tau_v_out);
 
+/* The same calibration with the rotation chosen ([ES] the accuracy paragraph
+ * and the paragraph before "Lo que OSCAR hace diferente"; [IT] 4: the pages'
+ * baselines): OSCAR_ROTATION_OSCAR is oscar_calibrate_host;
+ * OSCAR_ROTATION_IDENTITY is naive INT2, R = I; OSCAR_ROTATION_HADAMARD is the
+ * data-oblivious Hadamard rotation R = H P_br (the composite with U = I).  The
+ * two baselines do not read the covariances (eig outputs, when given, are set
+ * to NaN); tau is the same quantile, taken under the chosen R.  The write and
+ * read kernels take any of them unchanged.  Errors: as oscar_calibrate_host,
+ * and OSCAR_EINVAL for an unknown rotation. */
+#define OSCAR_ROTATION_OSCAR 0
+#define OSCAR_ROTATION_IDENTITY 1
+#define OSCAR_ROTATION_HADAMARD 2
+oscar_status oscar_calibrate_host_rotation(const oscar_shape* shape, int32_t rotation, int64_t n, const float* q,
+                                           const float* k, const float* v, double clip_pct_k, double clip_pct_v,
+                                           float* r_k_out, float* r_v_out, double* eig_k_out, double* eig_v_out,
+                                           float* tau_k_out, float* tau_v_out);
+
 /* ---- Page pools and sequences (host bookkeeping; [IT] 2.2.B paged cache with
  * prefix caching; [ES] serving section) ---- */
 oscar_status oscar_pool_create(const oscar_shape* shape, int64_t n_int2_pages, int64_t n_bf16_pages,

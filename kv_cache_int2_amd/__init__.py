@@ -48,6 +48,8 @@ _SIGS = {
     "oscar_bf16_block_bytes": (C.c_int64, [C.POINTER(Shape)]),
     "oscar_calibrate_host": (C.c_int32, [C.POINTER(Shape), C.c_int64, P, P, P, C.c_double, C.c_double,
                                          P, P, P, P, P, P]),
+    "oscar_calibrate_host_rotation": (C.c_int32, [C.POINTER(Shape), C.c_int32, C.c_int64, P, P, P, C.c_double,
+                                                  C.c_double, P, P, P, P, P, P]),
     "oscar_pool_create": (C.c_int32, [C.POINTER(Shape), C.c_int64, C.c_int64, C.POINTER(P)]),
     "oscar_pool_destroy": (C.c_int32, [P]),
     "oscar_pool_free_pages": (C.c_int32, [P, I64P, I64P]),
@@ -137,9 +139,15 @@ def oscar_bf16_block_bytes(shape: Shape) -> int:
     return int(lib().oscar_bf16_block_bytes(C.byref(shape)))
 
 
-def oscar_calibrate_host(shape: Shape, q, k, v, clip_pct_k=0.96, clip_pct_v=0.92):
+ROTATION_OSCAR, ROTATION_IDENTITY, ROTATION_HADAMARD = 0, 1, 2
+ROTATIONS = {"oscar": ROTATION_OSCAR, "identity": ROTATION_IDENTITY, "hadamard": ROTATION_HADAMARD}
+
+
+def oscar_calibrate_host(shape: Shape, q, k, v, clip_pct_k=0.96, clip_pct_v=0.92, rotation="oscar"):
     """q: float32 numpy [n, Hq, d]; k, v: [n, Hkv, d].  Returns
-    (r_k [Hkv,d,d] f32, r_v, eig_k [Hkv,d] f64, eig_v, tau_k, tau_v)."""
+    (r_k [Hkv,d,d] f32, r_v, eig_k [Hkv,d] f64, eig_v, tau_k, tau_v).
+    rotation: "oscar", or the baselines "identity" / "hadamard"
+    (oscar_calibrate_host_rotation)."""
     import numpy as np
     q = np.ascontiguousarray(q, dtype=np.float32)
     k = np.ascontiguousarray(k, dtype=np.float32)
@@ -150,9 +158,10 @@ def oscar_calibrate_host(shape: Shape, q, k, v, clip_pct_k=0.96, clip_pct_v=0.92
     e_k = np.empty((hkv, d), np.float64)
     e_v = np.empty_like(e_k)
     tk, tv = C.c_float(), C.c_float()
-    _check(lib().oscar_calibrate_host(C.byref(shape), n, q.ctypes.data, k.ctypes.data, v.ctypes.data,
-                                      clip_pct_k, clip_pct_v, r_k.ctypes.data, r_v.ctypes.data,
-                                      e_k.ctypes.data, e_v.ctypes.data, C.addressof(tk), C.addressof(tv)))
+    _check(lib().oscar_calibrate_host_rotation(C.byref(shape), ROTATIONS[rotation], n, q.ctypes.data,
+                                               k.ctypes.data, v.ctypes.data, clip_pct_k, clip_pct_v,
+                                               r_k.ctypes.data, r_v.ctypes.data, e_k.ctypes.data, e_v.ctypes.data,
+                                               C.addressof(tk), C.addressof(tv)))
     return r_k, r_v, e_k, e_v, np.float32(tk.value), np.float32(tv.value)
 
 

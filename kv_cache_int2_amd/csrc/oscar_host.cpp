@@ -284,19 +284,35 @@ int64_t oscar_bf16_block_bytes(const oscar_shape* shape) {
   return kBf16BlockBytes;
 }
 
-oscar_status oscar_calibrate_host(const oscar_shape* shape, int64_t n, const float* q, const float* k,
-                                  const float* v, double clip_pct_k, double clip_pct_v, float* r_k_out,
-                                  float* r_v_out, double* eig_k_out, double* eig_v_out, float* tau_k_out,
-                                  float* tau_v_out) {
+oscar_status oscar_calibrate_host_rotation(const oscar_shape* shape, int32_t rotation, int64_t n, const float* q,
+                                           const float* k, const float* v, double clip_pct_k, double clip_pct_v,
+                                           float* r_k_out, float* r_v_out, double* eig_k_out, double* eig_v_out,
+                                           float* tau_k_out, float* tau_v_out) {
   oscar_status st = check_shape(shape);
   if (st) return st;
+  if (rotation != OSCAR_ROTATION_OSCAR && rotation != OSCAR_ROTATION_IDENTITY && rotation != OSCAR_ROTATION_HADAMARD)
+    return fail(OSCAR_EINVAL, "rotation %d unknown", rotation);
   if (n < 1) return fail(OSCAR_EINVAL, "n = %lld calibration tokens", (long long)n);
   if (!q || !k || !v || !r_k_out || !r_v_out || !tau_k_out || !tau_v_out)
     return fail(OSCAR_EINVAL, "NULL calibration pointer");
   if (!(clip_pct_k > 0.0 && clip_pct_k <= 1.0) || !(clip_pct_v > 0.0 && clip_pct_v <= 1.0))
     return fail(OSCAR_EINVAL, "clip quantiles must lie in (0, 1]");
   const int d = kHeadDim, hkv = shape->n_kv_heads;
-  {
+  if (rotation != OSCAR_ROTATION_OSCAR) {
+    // the pages' baselines: no rotation, or the data-oblivious H P_br (the
+    // composite with U = I); neither reads the covariances
+    std::vector<double> r((size_t)d * d, 0.0), eye((size_t)d * d, 0.0);
+    for (int i = 0; i < d; ++i) eye[(size_t)i * d + i] = 1.0;
+    if (rotation == OSCAR_ROTATION_HADAMARD)
+      composite_rotation(d, eye, r);
+    else
+      r = eye;
+    for (int h = 0; h < hkv; ++h)
+      for (size_t i = 0; i < (size_t)d * d; ++i) r_k_out[(size_t)h * d * d + i] = r_v_out[(size_t)h * d * d + i] = (float)r[i];
+    for (double* e : {eig_k_out, eig_v_out})
+      if (e)
+        for (size_t i = 0; i < (size_t)hkv * d; ++i) e[i] = std::numeric_limits<double>::quiet_NaN();
+  } else {
     std::vector<std::thread> pool;
     const unsigned hw = std::max(1u, std::thread::hardware_concurrency());
     for (int h0 = 0; h0 < hkv; h0 += (int)hw) {
@@ -329,6 +345,14 @@ oscar_status oscar_calibrate_host(const oscar_shape* shape, int64_t n, const flo
     *(which ? tau_v_out : tau_k_out) = (float)tau;
   }
   return ok();
+}
+
+oscar_status oscar_calibrate_host(const oscar_shape* shape, int64_t n, const float* q, const float* k,
+                                  const float* v, double clip_pct_k, double clip_pct_v, float* r_k_out,
+                                  float* r_v_out, double* eig_k_out, double* eig_v_out, float* tau_k_out,
+                                  float* tau_v_out) {
+  return oscar_calibrate_host_rotation(shape, OSCAR_ROTATION_OSCAR, n, q, k, v, clip_pct_k, clip_pct_v, r_k_out,
+                                       r_v_out, eig_k_out, eig_v_out, tau_k_out, tau_v_out);
 }
 
 }  // extern "C"

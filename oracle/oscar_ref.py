@@ -164,30 +164,46 @@ class LayerCalibration:
     tau_v: np.float32
 
 
+ROTATIONS = ("oscar", "identity", "hadamard")
+
+
 def calibrate_layer(q: np.ndarray, k: np.ndarray, v: np.ndarray,
-                    clip_k: float = 0.96, clip_v: float = 0.92) -> LayerCalibration:
+                    clip_k: float = 0.96, clip_v: float = 0.92, rotation: str = "oscar") -> LayerCalibration:
     """Offline calibration of one layer.
     q: [N, Hq, d]; k, v: [N, Hkv, d] calibration activations (fp32 values).
     Per KV head: C_Q and C_S, their eigenbases, R_K = U_Q H P_br and
     R_V = U_S H P_br, stored as fp32.  Per layer: clip thresholds
     ([ES] write path: percentile threshold, typical c_K = 0.96, c_V = 0.92).
     READING: tau is the c-quantile of |x R| over all calibration tokens, KV
-    heads and channels of the layer, computed with the stored fp32 R."""
+    heads and channels of the layer, computed with the stored fp32 R.
+    rotation: "oscar" (the above), or one of the pages' baselines ([ES]
+    accuracy paragraph and the paragraph before "Lo que OSCAR hace
+    diferente"; [IT] 4): "identity", naive INT2 with no rotation (R = I), and
+    "hadamard", the data-oblivious Hadamard rotation (R = H P_br, the
+    composite with U = I).  Neither baseline looks at the covariances; their
+    eig arrays are NaN.  tau is recomputed for the chosen R."""
+    if rotation not in ROTATIONS:
+        raise ValueError(f"rotation must be one of {ROTATIONS}")
     n, hq, d = q.shape
     hkv = k.shape[1]
     g = hq // hkv
     r_k = np.empty((hkv, d, d), dtype=np.float32)
     r_v = np.empty_like(r_k)
-    eig_k = np.empty((hkv, d))
-    eig_v = np.empty((hkv, d))
+    eig_k = np.full((hkv, d), np.nan)
+    eig_v = np.full((hkv, d), np.nan)
     rot_k, rot_v = [], []
     for h in range(hkv):
-        qh = q[:, h * g:(h + 1) * g, :]
-        lam_q, u_q = eig_desc(query_covariance(qh))
-        lam_s, u_s = eig_desc(score_weighted_value_covariance(qh, k[:, h, :], v[:, h, :]))
-        r_k[h] = composite_rotation(u_q).astype(np.float32)
-        r_v[h] = composite_rotation(u_s).astype(np.float32)
-        eig_k[h], eig_v[h] = lam_q, lam_s
+        if rotation == "oscar":
+            qh = q[:, h * g:(h + 1) * g, :]
+            lam_q, u_q = eig_desc(query_covariance(qh))
+            lam_s, u_s = eig_desc(score_weighted_value_covariance(qh, k[:, h, :], v[:, h, :]))
+            r_k[h] = composite_rotation(u_q).astype(np.float32)
+            r_v[h] = composite_rotation(u_s).astype(np.float32)
+            eig_k[h], eig_v[h] = lam_q, lam_s
+        elif rotation == "hadamard":
+            r_k[h] = r_v[h] = composite_rotation(np.eye(d)).astype(np.float32)
+        else:
+            r_k[h] = r_v[h] = np.eye(d, dtype=np.float32)
         rot_k.append(np.abs(k[:, h, :].astype(np.float64) @ r_k[h].astype(np.float64)))
         rot_v.append(np.abs(v[:, h, :].astype(np.float64) @ r_v[h].astype(np.float64)))
     tau_k = np.float32(quantile_linear(np.concatenate(rot_k), clip_k))

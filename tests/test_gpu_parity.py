@@ -299,35 +299,42 @@ def test_bf16_baseline_decode(hq, hkv):
             _check_close(out[r], ref, f"baseline hq={hq} len={lens[r]} splits={sp}")
 
 
-def test_full_size_28x100k_sampled():
-    """The measured workload at full size, in the launch configuration the
-    bench times (whole batch, automatic split count): decode outputs of every
-    query head of two requests, and a spread of their page blocks, against the
-    oracle run on those two requests alone."""
-    w = synth.WORKLOADS["long_28x100k"]
+def _full_size_sampled(w, group, check):
+    """Fill a workload at full size (a shared prefix through a fork, as the
+    bench does), decode the whole batch in the bench's launch configuration
+    (automatic split count), and check the requests in `check`: every query
+    head's output, and a spread of their page blocks, against the oracle run on
+    those requests alone."""
     B, T = w.batch, w.context
-    _flush(f"case long_28x100k: B={B} T={T} Hq={w.n_q_heads} Hkv={w.n_kv_heads} G={w.group}")
+    _flush(f"case {w.name}: B={B} T={T} Hq={w.n_q_heads} Hkv={w.n_kv_heads} G={group}")
     cal = _calibrate(w)
-    sh = K.make_shape(n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads, group=w.group, sink=w.sink,
+    sh = K.make_shape(n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads, group=group, sink=w.sink,
                       recent=w.recent)
     ppr = (T + 15) // 16 + 2
     dc = DeviceCache(sh, cal.r_k, cal.r_v, cal.tau_k, cal.tau_v, B * ppr + 8,
                      B * (w.sink // 16 + 2 + w.recent // 16) + 8)
+    parent, start = None, 0
+    if w.shared_prefix:
+        start = w.shared_prefix
+        kb, vb = synth.kv_request_bf16(w, 0, 0, start)
+        parent = dc.new_seq()
+        _fill(dc, parent, kb, vb, [start])
     seqs = []
     for r in range(B):
-        kb, vb = synth.kv_request_bf16(w, r, 0, T)
-        seq = dc.new_seq()
-        _fill(dc, seq, kb, vb, [16384] * (T // 16384) + [T % 16384])
+        kb, vb = synth.kv_request_bf16(w, r, start, T)
+        seq = dc.fork(parent) if parent is not None else dc.new_seq()
+        n = T - start
+        _fill(dc, seq, kb, vb, [16384] * (n // 16384) + ([n % 16384] if n % 16384 else []))
         seqs.append(seq)
     _flush("filled")
     q = np.stack([synth.q_decode_bf16(w, r, 1) for r in range(B)])
     out = dc.decode(seqs, q).cpu().numpy()
     assert np.all(np.isfinite(out))
     i2, bf, _ = dc.tables(seqs)
-    for r in (0, B - 1):
+    for r in check:
         kb, vb = synth.kv_request_bf16(w, r, 0, T)
-        st = O.store_request(kb, vb, cal, w.group, w.sink, w.recent)
-        _check_close(out[r], O.decode_attention(q[r], st, cal, w.group), f"long_28x100k request {r}")
+        st = O.store_request(kb, vb, cal, group, w.sink, w.recent)
+        _check_close(out[r], O.decode_attention(q[r], st, cal, group), f"{w.name} G={group} request {r}")
         # page blocks: the first INT2 pages, pages spread over the history, the last ones
         n_lp = int(np.count_nonzero(i2[r] >= 0))
         lps = sorted({0, 1, 2, n_lp // 3, n_lp // 2, 2 * n_lp // 3, n_lp - 2, n_lp - 1})
@@ -335,15 +342,36 @@ def test_full_size_28x100k_sampled():
         for lp in lps:
             for h in range(w.n_kv_heads):
                 got = dc.int2_block_bytes_of(int(i2[r, lp]), h)
-                mism += not np.array_equal(got, _expected_int2_block(st, lp, h, w.group))
+                mism += not np.array_equal(got, _expected_int2_block(st, lp, h, group))
             for lpb in range(bf.shape[1]):
                 if bf[r, lpb] >= 0 and lp == lps[0]:
                     for h in range(w.n_kv_heads):
                         got = dc.bf16_block_bytes_of(int(bf[r, lpb]), h)
                         mism += not np.array_equal(got, _expected_bf16_block(st, lpb, h, w.sink, w.recent))
-        _flush(f"long_28x100k request {r}: {len(lps)} INT2 pages x {w.n_kv_heads} heads and the bf16 pages, "
-               f"mismatching blocks={mism}")
+        _flush(f"{w.name} G={group} request {r}: {len(lps)} INT2 pages x {w.n_kv_heads} heads and the bf16 "
+               f"pages, mismatching blocks={mism}")
         assert mism == 0
+
+
+def test_full_size_28x100k_sampled():
+    """The measured workload: 28 requests x 100000 tokens, g = 4."""
+    w = synth.WORKLOADS["long_28x100k"]
+    _full_size_sampled(w, w.group, (0, w.batch - 1))
+
+
+def test_full_size_prefix_64x32k_sampled():
+    """64 requests x 32768 tokens sharing an 8192-token prefix through the block
+    tables, g = 8 (two row tiles on one wavefront)."""
+    w = synth.WORKLOADS["qwen3_32b_prefix"]
+    _full_size_sampled(w, w.group, (0, w.batch - 1))
+
+
+@pytest.mark.parametrize("group", [32, 64])
+def test_full_size_stress_16x128k_sampled(group):
+    """16 requests x 131072 tokens, g = 12, both group sizes (three tiles as
+    three wavefronts at G = 32, two tiles on one wavefront at G = 64)."""
+    w = synth.WORKLOADS["stress_16x128k"]
+    _full_size_sampled(w, group, (w.batch - 1,))
 
 
 @pytest.mark.parametrize("hq,hkv,group,sink,recent", [(8, 2, 32, 4, 32), (12, 1, 64, 20, 48), (4, 1, 32, 4, 0)])
@@ -415,3 +443,34 @@ def test_fused_decode_step(hq, hkv, group, sink, recent):
         store = O.store_request(kb, vb, cal, group, sink, recent)
         _check_pages(caches[1], seqs[1][r], store, w, f"fused step len={t}")
         _check_close(out[r], O.decode_attention(qf[r], store, cal, group), f"fused step decode len={t}")
+
+
+@pytest.mark.parametrize("rotation", ["oscar", "identity", "hadamard"])
+def test_f1_rotation_ablation_through_the_kernels(rotation):
+    """The pages' baselines (naive INT2, Hadamard only) run through the same
+    write and decode kernels as OSCAR: pages bit-exact and outputs within
+    tolerance against the oracle under that rotation; the output error against
+    exact attention over the unquantised cache is reported."""
+    w = synth.WORKLOADS["qwen3_8b_32k"]
+    t = 8192
+    _flush(f"case f1 rotation={rotation}: T={t} Hq=32 Hkv=8 G=32")
+    q, k, v = synth.calib_layer(w)
+    cal = O.calibrate_layer(q, k, v, rotation=rotation)
+    sh = K.make_shape(n_q_heads=32, n_kv_heads=8, group=32, sink=w.sink, recent=w.recent)
+    dc = DeviceCache(sh, cal.r_k, cal.r_v, cal.tau_k, cal.tau_v, 600, 16)
+    kb, vb = synth.kv_request_bf16(w, 0, 0, t)
+    seq = dc.new_seq()
+    _fill(dc, seq, kb, vb, [4096, 4000, 1] + [1] * 95)
+    st = O.store_request(kb, vb, cal, w.group, w.sink, w.recent)
+    _check_pages(dc, seq, st, w, f"f1 {rotation}")
+    kx, vx = O.bf16_to_f64(kb), O.bf16_to_f64(vb)
+    oe = on = 0.0
+    for s in range(4):
+        qb = synth.q_decode_bf16(w, 0, s)
+        out = dc.decode([seq], qb[None]).cpu().numpy()[0].astype(np.float64)
+        _check_close(out, O.decode_attention(qb, st, cal, w.group), f"f1 {rotation} decode {s}")
+        ex = O.attend(O.bf16_to_f64(qb), kx, vx)
+        oe += float(((out - ex) ** 2).sum())
+        on += float((ex ** 2).sum())
+    _flush(f"f1 rotation={rotation}: output error vs unquantised cache rel_l2={math.sqrt(oe / on):.4f} "
+           f"tau_k={float(cal.tau_k):.3f} tau_v={float(cal.tau_v):.3f}")

@@ -112,6 +112,20 @@ def test_calibration_matches_oracle(lib, name):
     assert abs(tk / cal.tau_k - 1) < 1e-6 and abs(tv / cal.tau_v - 1) < 1e-6
 
 
+@pytest.mark.parametrize("rotation", ["identity", "hadamard"])
+def test_calibration_rotation_baselines_match_oracle(lib, rotation):
+    """The pages' baselines (no rotation; H P_br alone) from the host calibration
+    equal the oracle's: the same fixed R, tau under that R, no eigenvalues."""
+    w = synth.WORKLOADS["qwen3_8b_32k"]
+    q, k, v = synth.calib_layer(w, n=512)
+    sh = K.make_shape(n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads, group=w.group)
+    rk, rv, ek, ev, tk, tv = K.oscar_calibrate_host(sh, q, k, v, rotation=rotation)
+    cal = O.calibrate_layer(q, k, v, rotation=rotation)
+    assert np.array_equal(rk, cal.r_k) and np.array_equal(rv, cal.r_v)
+    assert np.all(np.isnan(ek)) and np.all(np.isnan(ev))
+    assert abs(tk / cal.tau_k - 1) < 1e-6 and abs(tv / cal.tau_v - 1) < 1e-6
+
+
 def test_calibration_errors(lib):
     sh = K.make_shape()
     z = np.zeros((4, 1, 128), np.float32)
@@ -119,6 +133,11 @@ def test_calibration_errors(lib):
         K.oscar_calibrate_host(sh, z, z, z, clip_pct_k=0.0)
     with pytest.raises(K.OscarError):
         K.oscar_calibrate_host(sh, z, z, z, clip_pct_v=1.5)
+    r = np.empty((1, 128, 128), np.float32)
+    t = C.c_float()
+    assert K.lib().oscar_calibrate_host_rotation(C.byref(sh), 7, 4, z.ctypes.data, z.ctypes.data, z.ctypes.data,
+                                                 0.96, 0.92, r.ctypes.data, r.ctypes.data, None, None,
+                                                 C.addressof(t), C.addressof(t)) == K.OSCAR_EINVAL
 
 
 # ---------------------------------------------------------------------------
