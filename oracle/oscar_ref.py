@@ -51,6 +51,42 @@ def to_f16(x: np.ndarray) -> np.ndarray:
     return np.asarray(x, dtype=np.float64).astype(np.float16)
 
 
+# 8-bit scale and zero of the lower-metadata history format: the OCP FP8 E4M3
+# encoding (sign, 4 exponent bits with bias 7, 3 mantissa bits; exponent 0 is
+# subnormal; S.1111.111 is NaN; no infinities; largest finite 448).
+E4M3_NAN = np.uint8(0x7F)
+
+
+def e4m3_decode(code: np.ndarray) -> np.ndarray:
+    """FP8 E4M3 codes (uint8) -> exact float64 values."""
+    c = np.asarray(code, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2((e - 7).astype(np.float64)))
+    out = sign * mag
+    return np.where((c & 0x7F) == 0x7F, np.nan, out)
+
+
+_E4M3_POS = e4m3_decode(np.arange(0x7F, dtype=np.uint8))   # codes 0x00..0x7E: 0 .. 448, increasing
+
+
+def to_e4m3(x: np.ndarray) -> np.ndarray:
+    """Round float64 to FP8 E4M3, nearest with ties to the even code, in a
+    single rounding; the sign is kept (so -0.0 -> 0x80).  READING: magnitudes
+    beyond 448 saturate to 448 (the format has no infinity); NaN -> 0x7F."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    i = np.clip(np.searchsorted(_E4M3_POS, a), 1, 0x7E)       # _E4M3_POS[i-1] < a <= _E4M3_POS[i]
+    lo, hi = _E4M3_POS[i - 1], _E4M3_POS[i]
+    pick_hi = (a - lo > hi - a) | ((a - lo == hi - a) & (i % 2 == 0))
+    code = np.where(pick_hi, i, i - 1)
+    code = np.where(a >= 448.0, 0x7E, code)
+    code = np.where(a == 0, 0, code)
+    code = code | np.where(np.signbit(x), 0x80, 0)
+    return np.where(np.isnan(x), E4M3_NAN, code).astype(np.uint8)
+
+
 # ---------------------------------------------------------------------------
 # The fixed parts of the composite rotation  ([ES] "Lo que OSCAR hace
 # diferente": Lemma 1 and the bit-reversal paragraph; [IT] 2.2.A)
@@ -219,17 +255,21 @@ def calibrate_layer(q: np.ndarray, k: np.ndarray, v: np.ndarray,
 F16_NAN = np.float16(np.nan)
 
 
-def quantize(x: np.ndarray, r: np.ndarray, tau: float, group: int):
+def quantize(x: np.ndarray, r: np.ndarray, tau: float, group: int, scale_bits: int = 16):
     """x: [n, d] input values (bf16 values as float64), r: [d, d] (fp32 values),
     tau: clip threshold (fp32 value).  Returns codes uint8 [n, d],
-    scale/zero float16 [n, d/group], and the rotated, clipped fp64 values.
-    Steps (all fp64 until the fp16 rounding of scale and zero):
+    scale/zero [n, d/group] and the rotated, clipped fp64 values.
+    Steps (all fp64 until the rounding of scale and zero):
       x_rot = x R ; clamp to [-tau, tau] ;
       per group: mn, mx ; s = f16((mx - mn) / 3) ; z = f16(mn) ;
       c = clamp(round_half_even((x_rot - z) / s), 0, 3), c = 0 where s == 0.
-    READING: codes are taken against the fp16-rounded s and z, so the
-    encoder and the decoder (z + c s) agree.  A group holding NaN stores
-    s = z = NaN and codes 0."""
+    READING: codes are taken against the rounded s and z, so the encoder and
+    the decoder (z + c s) agree.  A group holding NaN stores s = z = NaN and
+    codes 0.  scale_bits = 16 stores s and z as float16; scale_bits = 8 (the
+    lower-metadata format) as FP8 E4M3 codes (uint8), the same steps with
+    e4m3 rounding in place of f16."""
+    if scale_bits not in (16, 8):
+        raise ValueError("scale_bits must be 16 or 8")
     x = np.asarray(x, dtype=np.float64)
     n, d = x.shape
     ng = d // group
@@ -239,25 +279,36 @@ def quantize(x: np.ndarray, r: np.ndarray, tau: float, group: int):
     xg = xr.reshape(n, ng, group)
     mn = xg.min(axis=2)
     mx = xg.max(axis=2)
-    s = to_f16((mx - mn) / 3.0)
-    z = to_f16(mn)
-    s64 = s.astype(np.float64)[:, :, None]
-    z64 = z.astype(np.float64)[:, :, None]
+    if scale_bits == 16:
+        s = to_f16((mx - mn) / 3.0)
+        z = to_f16(mn)
+    else:
+        s = to_e4m3((mx - mn) / 3.0)
+        z = to_e4m3(mn)
+    s64 = meta_values(s)[:, :, None]
+    z64 = meta_values(z)[:, :, None]
     with np.errstate(divide="ignore", invalid="ignore"):
         tt = (xg - z64) / s64
     c = np.clip(np.rint(tt), 0, 3)
     bad = np.isnan(mn) | np.isnan(mx)
     c = np.where((s64 == 0) | bad[:, :, None], 0, c)
-    s = np.where(bad, F16_NAN, s)
-    z = np.where(bad, F16_NAN, z)
+    nan = F16_NAN if scale_bits == 16 else E4M3_NAN
+    s = np.where(bad, nan, s)
+    z = np.where(bad, nan, z)
     return c.reshape(n, d).astype(np.uint8), s, z, xr
+
+
+def meta_values(m: np.ndarray) -> np.ndarray:
+    """Stored scale or zero -> float64: float16 values, or E4M3 codes (uint8)."""
+    m = np.asarray(m)
+    return e4m3_decode(m) if m.dtype == np.uint8 else m.astype(np.float64)
 
 
 def dequantize(codes: np.ndarray, s: np.ndarray, z: np.ndarray, group: int) -> np.ndarray:
     """Rotated-basis reconstruction z + c s (fp64)."""
     n, d = codes.shape
     c = codes.astype(np.float64).reshape(n, d // group, group)
-    return (z.astype(np.float64)[:, :, None] + c * s.astype(np.float64)[:, :, None]).reshape(n, d)
+    return (meta_values(z)[:, :, None] + c * meta_values(s)[:, :, None]).reshape(n, d)
 
 
 def unrotate(x_rot: np.ndarray, r: np.ndarray) -> np.ndarray:
@@ -335,7 +386,7 @@ class StoredRequest:
 
 
 def store_request(k_bits: np.ndarray, v_bits: np.ndarray, cal: LayerCalibration, group: int,
-                  sink: int, recent: int) -> StoredRequest:
+                  sink: int, recent: int, scale_bits: int = 16) -> StoredRequest:
     """Apply the region rule and the write path to a whole request.
     k_bits, v_bits: [T, Hkv, d] bf16 bit patterns."""
     t, hkv, d = k_bits.shape
@@ -343,14 +394,14 @@ def store_request(k_bits: np.ndarray, v_bits: np.ndarray, cal: LayerCalibration,
     reg = regions(t, sink, recent)
     kc = np.zeros((t, hkv, d), np.uint8)
     vc = np.zeros_like(kc)
-    ks = np.zeros((t, hkv, ng), np.float16)
+    ks = np.zeros((t, hkv, ng), np.float16 if scale_bits == 16 else np.uint8)
     kz, vs, vz = ks.copy(), ks.copy(), ks.copy()
     idx = np.nonzero(reg == REGION_INT2)[0]
     if idx.size:
         for h in range(hkv):
-            c, s, z, _ = quantize(bf16_to_f64(k_bits[idx, h]), cal.r_k[h], cal.tau_k, group)
+            c, s, z, _ = quantize(bf16_to_f64(k_bits[idx, h]), cal.r_k[h], cal.tau_k, group, scale_bits)
             kc[idx, h], ks[idx, h], kz[idx, h] = c, s, z
-            c, s, z, _ = quantize(bf16_to_f64(v_bits[idx, h]), cal.r_v[h], cal.tau_v, group)
+            c, s, z, _ = quantize(bf16_to_f64(v_bits[idx, h]), cal.r_v[h], cal.tau_v, group, scale_bits)
             vc[idx, h], vs[idx, h], vz[idx, h] = c, s, z
     return StoredRequest(reg, k_bits, v_bits, kc, ks, kz, vc, vs, vz)
 
@@ -391,8 +442,8 @@ def decode_attention(q_bits: np.ndarray, st: StoredRequest, cal: LayerCalibratio
 # (channel-major).
 # ---------------------------------------------------------------------------
 
-def int2_block_bytes(d: int, group: int) -> int:
-    return 2 * (PAGE * d // 4 + PAGE * (d // group) * 4)
+def int2_block_bytes(d: int, group: int, scale_bits: int = 16) -> int:
+    return 2 * (PAGE * d // 4 + PAGE * (d // group) * scale_bits // 4)
 
 
 def bf16_block_bytes(d: int) -> int:
@@ -400,13 +451,16 @@ def bf16_block_bytes(d: int) -> int:
 
 
 def _pack_sz(s: np.ndarray, z: np.ndarray, token_major: bool) -> np.ndarray:
-    # s, z: [16, NG] float16 -> bytes of [16][NG][2] (token-major) or [NG][16][2] fp16
-    pair = np.stack([s, z] if token_major else [s.T, z.T], axis=-1).astype(np.float16)
+    # s, z: [16, NG] float16 or E4M3 codes -> bytes of [16][NG][(s, z)]
+    # (token-major) or [NG][16][(s, z)]: a float16 pair, or a byte pair
+    pair = np.stack([s, z] if token_major else [s.T, z.T], axis=-1)
+    pair = pair.astype(np.uint8 if pair.dtype == np.uint8 else np.float16)
     return np.ascontiguousarray(pair).view(np.uint8).ravel()
 
 
 def pack_int2_block(kc, ks, kz, vc, vs, vz) -> np.ndarray:
-    """Codes [16, d] (uint8 0..3), scale/zero [16, NG] float16 -> uint8 block."""
+    """Codes [16, d] (uint8 0..3), scale/zero [16, NG] (float16, or uint8 E4M3
+    codes for the lower-metadata format) -> uint8 block."""
     kc = np.asarray(kc, np.uint8)
     vc = np.asarray(vc, np.uint8)
     t, d = kc.shape
@@ -422,18 +476,19 @@ def pack_int2_block(kc, ks, kz, vc, vs, vz) -> np.ndarray:
                            _pack_sz(vs, vz, False)])
 
 
-def unpack_int2_block(buf: np.ndarray, d: int, group: int):
+def unpack_int2_block(buf: np.ndarray, d: int, group: int, scale_bits: int = 16):
     """Inverse of pack_int2_block."""
     buf = np.asarray(buf, np.uint8)
     ng = d // group
     nc = PAGE * d // 4
-    nsz = PAGE * ng * 4
+    nsz = PAGE * ng * scale_bits // 4
+    mt = np.float16 if scale_bits == 16 else np.uint8
     kb = buf[:nc].reshape(PAGE, d // 4)
     kc = np.zeros((PAGE, d), np.uint8)
     for i in range(4):
         kc[:, i::4] = (kb >> (2 * i)) & 3
     o = nc
-    ksz = buf[o:o + nsz].copy().view(np.float16).reshape(PAGE, ng, 2).transpose(1, 0, 2)
+    ksz = buf[o:o + nsz].copy().view(mt).reshape(PAGE, ng, 2).transpose(1, 0, 2)
     o += nsz
     vb = buf[o:o + nc].reshape(4, d)
     vc = np.zeros((PAGE, d), np.uint8)
@@ -441,7 +496,7 @@ def unpack_int2_block(buf: np.ndarray, d: int, group: int):
         for i in range(4):
             vc[4 * q + i] = (vb[q] >> (2 * i)) & 3
     o += nc
-    vsz = buf[o:o + nsz].copy().view(np.float16).reshape(ng, PAGE, 2)
+    vsz = buf[o:o + nsz].copy().view(mt).reshape(ng, PAGE, 2)
     return kc, ksz[:, :, 0].T, ksz[:, :, 1].T, vc, vsz[:, :, 0].T, vsz[:, :, 1].T
 
 

@@ -609,3 +609,93 @@ def test_f1_naive_int2_is_far_worse_than_either_rotation():
     for r in ("oscar", "hadamard"):
         assert 2 * err[r][0] < err["identity"][0], err
         assert err[r][1] < err["identity"][1], err
+
+
+# ---------------------------------------------------------------------------
+# f3: the lower-metadata history format (8-bit scale and zero, FP8 E4M3), which
+# with G = 64 gives the 2.25 history bits behind the pages' 2.28 / 2.38 bits
+# per element (P8)
+# ---------------------------------------------------------------------------
+
+def test_f3_e4m3_codec_matches_library():
+    """Decode of all 256 codes and nearest-even encode (with the sign of zero,
+    subnormals, every tie between neighbours and saturation at 448) equal
+    torch's float8_e4m3fn conversions."""
+    codes = np.arange(256, dtype=np.uint8)
+    lib = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    ours = O.e4m3_decode(codes)
+    assert np.array_equal(np.isnan(lib), np.isnan(ours))
+    assert np.array_equal(lib[~np.isnan(lib)], ours[~np.isnan(ours)])
+    assert np.array_equal(np.signbit(lib[~np.isnan(lib)]), np.signbit(ours[~np.isnan(ours)]))
+    assert ours[0x38] == 1.0 and ours[0x7E] == 448.0 and ours[0x01] == 2.0 ** -9 and ours[0x08] == 2.0 ** -6
+    pos = ours[:0x7F]
+    mids = (pos[:-1] + pos[1:]) / 2
+    rng = np.random.default_rng(83)
+    x = np.concatenate([rng.uniform(-463, 463, 20000), rng.normal(0, 0.01, 20000), mids, -mids, pos, -pos,
+                        [0.0, -0.0, 2.0 ** -10, -(2.0 ** -10), 3 * 2.0 ** -11, 448.0, 449.0, 463.9]])
+    lib = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.to_e4m3(x), lib)
+    # READING beyond the library's range (it returns NaN past 464): saturate
+    assert list(O.to_e4m3(np.array([464.0, 1e6, -1e6, np.inf]))) == [0x7E, 0x7E, 0xFE, 0x7E]
+    assert O.to_e4m3(np.array([np.nan]))[0] == 0x7F
+
+
+@pytest.mark.parametrize("group", [32, 64])
+def test_f3_fp8_meta_codes_are_nearest_level(group):
+    """With 8-bit metadata: s and z are the E4M3 roundings of (mx - mn)/3 and
+    mn of the clipped rotated group, and each code is the nearest of the four
+    levels z + c s (brute force in Python floats)."""
+    rng = np.random.default_rng(89 + group)
+    d = 128
+    r = _rand_orth(rng, d)
+    x = rng.standard_normal((60, d)) * 3
+    tau = 3.0
+    codes, s, z, _ = O.quantize(x, r, tau, group, scale_bits=8)
+    assert s.dtype == np.uint8 and z.dtype == np.uint8
+    for n in range(x.shape[0]):
+        rot = np.clip(x[n] @ r.astype(np.float64), -tau, tau)
+        for gm in range(d // group):
+            vals = rot[gm * group:(gm + 1) * group]
+            mn, mx = float(vals.min()), float(vals.max())
+            assert s[n, gm] == O.to_e4m3(np.array((mx - mn) / 3.0))
+            assert z[n, gm] == O.to_e4m3(np.array(mn))
+            sv, zv = float(O.e4m3_decode(s[n, gm])), float(O.e4m3_decode(z[n, gm]))
+            for jj, val in enumerate(vals):
+                t = (val - zv) / sv
+                if abs(t - math.floor(t) - 0.5) < 1e-9:
+                    continue
+                best = int(np.argmin([abs(val - (zv + c * sv)) for c in range(4)]))
+                assert codes[n, gm * group + jj] == best
+    # degenerate and NaN groups keep their meaning
+    xd = np.zeros((2, d))
+    xd[1, 0] = np.nan
+    c, s, z, _ = O.quantize(xd, np.eye(d), 10.0, group, scale_bits=8)
+    assert np.all(s[0] == 0) and np.all(c == 0) and np.all(s[1] == 0x7F) and np.all(z[1] == 0x7F)
+
+
+def test_f3_fp8_meta_block_layout_by_hand():
+    """G = 64 with 8-bit metadata: 512 B K codes, K (s, z) byte pairs
+    token-major, 512 B V codes, V (s, z) byte pairs group-major: 1152 B per
+    16 tokens, i.e. 2.25 bits per element."""
+    d, group = 128, 64
+    kc = np.tile(np.arange(d) % 4, (16, 1)).astype(np.uint8)
+    vc = np.zeros((16, d), np.uint8)
+    vc[6, 9] = 1
+    ks = np.full((16, 2), 0x30, np.uint8)
+    kz = np.full((16, 2), 0xB8, np.uint8)       # -1.0
+    ks[7, 1] = 0x44                             # 3.0 at token 7, group 1
+    vs = np.full((16, 2), 0x28, np.uint8)       # 0.25
+    vs[5, 0] = 0x4A                             # 5.0 at token 5, group 0
+    blk = O.pack_int2_block(kc, ks, kz, vc, vs, kz)
+    assert blk.size == O.int2_block_bytes(d, group, 8) == 1152
+    assert blk.size * 8 / (16 * 2 * d) == O.int2_history_bits(group, 8, 8) == 2.25
+    assert O.e4m3_decode(np.uint8(0x44)) == 3.0 and O.e4m3_decode(np.uint8(0x4A)) == 5.0
+    assert np.all(blk[:512] == 0xE4)
+    ksz = blk[512:576]                          # [token][group][(s, z)]
+    assert ksz[(7 * 2 + 1) * 2] == 0x44 and ksz[(7 * 2 + 1) * 2 + 1] == 0xB8
+    vb = blk[576:1088].reshape(4, d)
+    assert vb[1, 9] == 1 << 4 and np.count_nonzero(vb) == 1
+    vsz = blk[1088:1152]                        # [group][token][(s, z)]
+    assert vsz[(0 * 16 + 5) * 2] == 0x4A and np.count_nonzero(vsz[0::2] == 0x28) == 31
+    for a, b in zip(O.unpack_int2_block(blk, d, group, 8), (kc, ks, kz, vc, vs, kz)):
+        assert np.array_equal(a, b)
