@@ -15,6 +15,7 @@ lengths of all requests and steps / wall time of the timed steps).
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -44,6 +45,8 @@ def parse():
                     help="untimed steps first (about a second of decode, so clocks have settled)")
     ap.add_argument("--workload", default="long_28x100k")
     ap.add_argument("--group", type=int, default=0, help="override the workload's INT2 group size")
+    ap.add_argument("--layout", choices=["workload", "pages"], default="workload",
+                    help="pages: the pages' default layout (sink 64, recent 256, G = 64, FP8 scale and zero)")
     ap.add_argument("--splits", type=int, default=0, help="INT2 splits per (request, KV head); 0 = auto")
     ap.add_argument("--unfused", action="store_true",
                     help="separate write calls and in-order kernels instead of the fused decode step")
@@ -58,11 +61,11 @@ def int2_tokens(t, sink, recent):
     return max(0, int(t) - sink - recent)
 
 
-def algorithmic_bytes(ctx, hkv, hq, group, sink, recent):
+def algorithmic_bytes(ctx, hkv, hq, group, sink, recent, mb=4):
     """Bytes the method must move for one decode of the batch: INT2 codes +
-    fp16 scale/zero of history tokens, bf16 K/V of sink/recent tokens, the
-    bf16 query and the fp32 output."""
-    per_int2 = 2 * (128 // 4 + (128 // group) * 4)          # K and V, per token and KV head
+    scale/zero of history tokens, bf16 K/V of sink/recent tokens, the bf16
+    query and the fp32 output."""
+    per_int2 = 2 * (128 // 4 + (128 // group) * mb)         # K and V, per token and KV head
     per_bf16 = 2 * 128 * 2
     tot = 0
     for t in ctx:
@@ -71,11 +74,12 @@ def algorithmic_bytes(ctx, hkv, hq, group, sink, recent):
     return tot + len(ctx) * hq * 128 * (2 + 4)
 
 
-def int2_kernel_bytes(ctx, hkv, group, sink, recent):
+def int2_kernel_bytes(ctx, hkv, group, sink, recent, mb=4):
     """Algorithmic bytes of one launch of the INT2 kernel: 2 x (32 B of codes +
-    (128/G) x 4 B of fp16 scale/zero) per INT2 token and KV head (96 B at G=32,
-    80 B at G=64).  The bf16 tokens belong to the bf16 kernel."""
-    per_int2 = 2 * (128 // 4 + (128 // group) * 4)
+    (128/G) x mb B of scale/zero, mb = 4 for fp16, 2 for FP8) per INT2 token
+    and KV head (96 B at G=32 fp16, 80 B at G=64 fp16, 72 B at G=64 FP8).  The
+    bf16 tokens belong to the bf16 region's work."""
+    per_int2 = 2 * (128 // 4 + (128 // group) * mb)
     return sum(int2_tokens(t, sink, recent) for t in ctx) * hkv * per_int2
 
 
@@ -93,13 +97,20 @@ def main():
     assert torch.cuda.is_available(), "bench needs a GPU"
     torch.cuda.set_device(0)
     w = synth.WORKLOADS[args.workload]
+    scale_bits = 16
+    if args.layout == "pages":
+        w = dataclasses.replace(w, sink=64, recent=256, group=64)
+        scale_bits = 8
     group = args.group or w.group
+    mb = 4 if scale_bits == 16 else 2
     B, hq, hkv = w.batch, w.n_q_heads, w.n_kv_heads
     n_steps = args.warmup + args.steps
     T_final = w.context
     T0 = T_final - n_steps                      # the last timed step attends T_final tokens
-    sh = K.make_shape(n_q_heads=hq, n_kv_heads=hkv, group=group, sink=w.sink, recent=w.recent)
-    log(f"workload {w.name}: B={B} T={T_final} Hq={hq} Hkv={hkv} G={group} sink={w.sink} recent={w.recent}")
+    sh = K.make_shape(n_q_heads=hq, n_kv_heads=hkv, group=group, sink=w.sink, recent=w.recent,
+                      scale_bits=scale_bits)
+    log(f"workload {w.name}: B={B} T={T_final} Hq={hq} Hkv={hkv} G={group} sink={w.sink} recent={w.recent} "
+        f"scale_bits={scale_bits}")
 
     # ---- calibration (offline, host C++) ----
     t = time.time()
@@ -226,8 +237,8 @@ def main():
     tokens = int(sum(c.sum() for c in ctx_hist))
     value = tokens / elapsed
     main_avg_ms = main_ms / max(launches, 1)
-    alg_step = np.mean([algorithmic_bytes(c, hkv, hq, group, w.sink, w.recent) for c in ctx_hist])
-    alg = np.mean([int2_kernel_bytes(c, hkv, group, w.sink, w.recent) for c in ctx_hist])
+    alg_step = np.mean([algorithmic_bytes(c, hkv, hq, group, w.sink, w.recent, mb) for c in ctx_hist])
+    alg = np.mean([int2_kernel_bytes(c, hkv, group, w.sink, w.recent, mb) for c in ctx_hist])
     achieved = alg / (main_avg_ms * 1e-3) / 1e9
     log(f"timed {args.steps} steps in {elapsed * 1e3:.2f} ms: {value / 1e9:.3f} G KV tok/s; "
         f"decode_int2 avg {main_avg_ms * 1e3:.1f} us -> {achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS:.1%} of peak)")
@@ -303,7 +314,7 @@ def main():
         T_s = T_final
         while spent < args.cpu_seconds and n_req < B:
             kb, vb = synth.kv_request_bf16(w, n_req, 0, T_s)
-            st_ = O.store_request(kb, vb, cal, group, w.sink, w.recent)
+            st_ = O.store_request(kb, vb, cal, group, w.sink, w.recent, scale_bits)
             qb = synth.q_decode_bf16(w, n_req)
             c0 = time.perf_counter()
             O.decode_attention(qb, st_, cal, group)
@@ -321,8 +332,12 @@ def main():
         qw_flops = 2 * 2 * 128 * 128 * hkv * qw_tokens
         qw = {"tokens_per_s": qw_tokens / qw_time, "ms_total": round(qw_time * 1e3, 3),
               "fp64_mfma_util": round(qw_flops / qw_time / (FP64_PEAK_TFLOPS * 1e12), 4),
-              "gbs": round(qw_tokens * hkv * (2 * 128 * 2 + 2 * (32 + 4 * 128 // group)) / qw_time / 1e9, 1)}
+              "gbs": round(qw_tokens * hkv * (2 * 128 * 2 + 2 * (32 + (128 // group) * mb)) / qw_time / 1e9, 1)}
 
+    # stored bits per KV element at the final context (bf16 sink/recent + INT2 history)
+    n_i2 = int2_tokens(T_final, w.sink, w.recent)
+    hist_bits = 2.0 + 8 * mb / group           # codes + the (scale, zero) pair per group
+    bits_per_element = (n_i2 * hist_bits + (T_final - n_i2) * 16.0) / T_final
     res = {
         "metric": "INT2 paged decode attention: KV tokens/s + achieved HBM GB/s (% of peak)",
         "value": value,
@@ -338,6 +353,7 @@ def main():
         "data": "synthetic (seeded generator; calibration on synthetic activations)",
         "config": {"workload": w.name, "batch": B, "context": T_final, "n_q_heads": hq, "n_kv_heads": hkv,
                    "head_dim": 128, "group": group, "sink": w.sink, "recent": w.recent, "page_size": 16,
+                   "scale_bits": scale_bits, "bits_per_element": round(bits_per_element, 4),
                    "splits_int2": si, "step": "unfused" if args.unfused else "fused"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,

@@ -80,6 +80,9 @@ typedef struct oscar_shape {
   int32_t sink;        /* S0 ([ES] serving section; 64 there) */
   int32_t recent;      /* W  ([ES] serving section; 256 there) */
   int32_t page_size;   /* tokens per page */
+  int32_t scale_bits;  /* storage of each group's scale and zero: 16 (or 0) two fp16; 8 two FP8 E4M3,
+                          the lower-metadata format (G = 64 gives 2.25 history bits per element:
+                          [ES] accuracy section, 2.28 / 2.38 bits per element) */
 } oscar_shape;
 
 /* Calibration state of one layer ([IT] 2.2.A: fixed rotations and clip

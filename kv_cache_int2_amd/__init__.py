@@ -25,7 +25,8 @@ class OscarError(RuntimeError):
 
 class Shape(C.Structure):
     _fields_ = [("head_dim", C.c_int32), ("n_q_heads", C.c_int32), ("n_kv_heads", C.c_int32),
-                ("group", C.c_int32), ("sink", C.c_int32), ("recent", C.c_int32), ("page_size", C.c_int32)]
+                ("group", C.c_int32), ("sink", C.c_int32), ("recent", C.c_int32), ("page_size", C.c_int32),
+                ("scale_bits", C.c_int32)]
 
 
 class Layer(C.Structure):
@@ -118,8 +119,9 @@ def _stream(stream=None):
     return torch.cuda.current_stream().cuda_stream
 
 
-def make_shape(head_dim=128, n_q_heads=1, n_kv_heads=1, group=32, sink=4, recent=128, page_size=PAGE) -> Shape:
-    return Shape(head_dim, n_q_heads, n_kv_heads, group, sink, recent, page_size)
+def make_shape(head_dim=128, n_q_heads=1, n_kv_heads=1, group=32, sink=4, recent=128, page_size=PAGE,
+               scale_bits=16) -> Shape:
+    return Shape(head_dim, n_q_heads, n_kv_heads, group, sink, recent, page_size, scale_bits)
 
 
 def make_layer(r_k, r_v, tau_k, tau_v) -> Layer:

@@ -42,6 +42,7 @@
 #include <stdint.h>
 
 #include <cmath>
+#include <type_traits>
 
 #include "oscar_internal.h"
 #include "quant_common.h"
@@ -54,6 +55,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x1 __attribute__((ext_vector_type(1)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
@@ -183,11 +185,11 @@ struct StepScratch {
   uint32_t sz[2][4];           // [K/V][group] fp16 scale | zero << 16
 };
 
-template <int NG>
+template <int NG, int MB>
 __device__ __forceinline__ void quantise_and_store(const DecodeParams& p, int kv, int tok, int32_t dst,
                                                    const float* rk, const float* rv, StepScratch& sc) {
   constexpr int G = kHeadDim / NG;
-  constexpr Int2Layout L{NG};
+  constexpr Int2Layout L{NG, MB};
   const int t = threadIdx.x, m = t >> 7, j = t & (kHeadDim - 1);
   const float* R = m ? rv : rk;
   const float* x = sc.x[tok][m];
@@ -212,12 +214,11 @@ __device__ __forceinline__ void quantise_and_store(const DecodeParams& p, int kv
     mx = omx > mx ? omx : mx;
     nan |= __shfl_xor((int)nan, off) != 0;
   }
-  uint16_t sb = 0x7e00u, zb = 0x7e00u;
+  uint32_t pair = nan_sz<MB>();
   uint8_t c = 0;
   if (!nan) {
-    sb = f64_to_f16_bits((mx - mn) / 3.0);
-    zb = f64_to_f16_bits(mn);
-    const double sd = f16_bits_to_f64(sb), zd = f16_bits_to_f64(zb);
+    double sd, zd;
+    pair = encode_sz<MB>((mx - mn) / 3.0, mn, sd, zd);
     if (sd != 0.0) {
       double cd = __builtin_rint((v - zd) / sd);
       cd = cd < 0.0 ? 0.0 : (cd > 3.0 ? 3.0 : cd);
@@ -225,7 +226,7 @@ __device__ __forceinline__ void quantise_and_store(const DecodeParams& p, int kv
     }
   }
   sc.code[m][j] = c;
-  if (j % G == 0) sc.sz[m][j / G] = (uint32_t)sb | ((uint32_t)zb << 16);
+  if (j % G == 0) sc.sz[m][j / G] = pair;
   __syncthreads();
   const int64_t page = dst / kPage;
   const int slot = dst % kPage;
@@ -238,10 +239,10 @@ __device__ __forceinline__ void quantise_and_store(const DecodeParams& p, int kv
     *(uint32_t*)(blk + L.k_codes() + slot * 32 + 4 * t) = w;
   } else if (t >= 16 && t < 16 + NG) {
     const int gm = t - 16;
-    *(uint32_t*)(blk + L.k_sz() + (slot * NG + gm) * 4) = sc.sz[0][gm];  // K: token-major
+    store_sz<MB>(blk + L.k_sz() + (slot * NG + gm) * MB, sc.sz[0][gm]);  // K: token-major
   } else if (t >= 32 && t < 32 + NG) {
     const int gm = t - 32;
-    *(uint32_t*)(blk + L.v_sz() + (gm * kPage + slot) * 4) = sc.sz[1][gm];  // V: group-major
+    store_sz<MB>(blk + L.v_sz() + (gm * kPage + slot) * MB, sc.sz[1][gm]);  // V: group-major
   } else if (t >= 64 && t < 96) {
     // V codes by token quad: byte jc of quad slot/4 holds channel jc, this
     // token at bits 2 (slot % 4); the other three tokens keep their bits
@@ -259,7 +260,7 @@ __device__ __forceinline__ void quantise_and_store(const DecodeParams& p, int kv
   __syncthreads();
 }
 
-template <int NG>
+template <int NG, int MB>
 __device__ void step_writes(const DecodeParams& p, int b, int kv, const float* rk, const float* rv,
                             StepScratch& sc) {
   const int t = threadIdx.x, m = t >> 7, j = t & (kHeadDim - 1);
@@ -281,8 +282,8 @@ __device__ void step_writes(const DecodeParams& p, int b, int kv, const float* r
   if (put_i2) sc.x[1][m][j] = bf16_val(xn);
   __syncthreads();  // the leaving token has been read before its ring slot is reused
   if (put_bf) *bf16_elem(bf_new) = xn;
-  if (age) quantise_and_store<NG>(p, kv, 0, age_dst, rk, rv, sc);
-  if (put_i2) quantise_and_store<NG>(p, kv, 1, i2_new, rk, rv, sc);
+  if (age) quantise_and_store<NG, MB>(p, kv, 0, age_dst, rk, rv, sc);
+  if (put_i2) quantise_and_store<NG, MB>(p, kv, 1, i2_new, rk, rv, sc);
 }
 
 // ---------------------------------------------------------------------------
@@ -291,7 +292,7 @@ __device__ void step_writes(const DecodeParams& p, int b, int kv, const float* r
 // Words per (request, KV head): A digits of 2Q ((((ct*3 + digit)*2 + kstep)*64 + lane)*4 + reg),
 // then aux floats [1 + 16*CT]: logit factor 2^-sq / 2, per row 2*Qbar (float).
 // WRITE: the decode-step writes come first.
-template <int NG, int CT, bool WRITE>
+template <int NG, int MB, int CT, bool WRITE>
 __global__ __launch_bounds__(256) void decode_prologue(DecodeParams p) {
   const int bk = blockIdx.x;
   const int b = bk / p.n_kv, kv = bk % p.n_kv;
@@ -308,7 +309,7 @@ __global__ __launch_bounds__(256) void decode_prologue(DecodeParams p) {
     stage_matrix256<kHeadDim>(p.r_v + (int64_t)kv * kHeadDim * kHeadDim, rv);
     stage_matrix256<kHeadDim>(p.r_k + (int64_t)kv * kHeadDim * kHeadDim, rk);
     __syncthreads();
-    step_writes<NG>(p, b, kv, rk, rv, sc);
+    step_writes<NG, MB>(p, b, kv, rk, rv, sc);
   } else {
     stage_matrix256<kHeadDim>(p.r_k + (int64_t)kv * kHeadDim * kHeadDim, rk);
   }
@@ -466,14 +467,48 @@ struct Int2Offsets {
   uint32_t kc, ksz, vw, vsz;
 };
 
-template <int NG>
+template <int NG, int MB>
 __device__ __forceinline__ Int2Offsets int2_offsets() {
-  constexpr Int2Layout L{NG};
+  constexpr Int2Layout L{NG, MB};
   const int lane = threadIdx.x & 63, ln = lane & 15, qd = lane >> 4;
-  return Int2Offsets{(uint32_t)(L.k_codes() + ln * 32 + 8 * qd), (uint32_t)(L.k_sz() + ln * NG * 4),
+  return Int2Offsets{(uint32_t)(L.k_codes() + ln * 32 + 8 * qd), (uint32_t)(L.k_sz() + ln * NG * MB),
                      (uint32_t)(L.v_codes() + qd * kHeadDim + 8 * ln),
-                     (uint32_t)(L.v_sz() + ((ln % NG) * kPage + 4 * qd) * 4)};
+                     (uint32_t)(L.v_sz() + ((ln % NG) * kPage + 4 * qd) * MB)};
 }
+
+// Stored (scale, zero) pairs -> fp16 pairs, scale in the low half (the form
+// the arithmetic reads).  FP8 E4M3 byte pairs convert exactly: every E4M3
+// value is an fp16 value.
+__device__ __forceinline__ uint32_t e4m3_pair_lo(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+}
+__device__ __forceinline__ uint32_t e4m3_pair_hi(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
+}
+// one token's K pairs, every group: NG stored pairs, raw words of 4 or 2 bytes each
+template <int NG, int MB, class W>
+__device__ __forceinline__ void k_pairs(const W& raw, uint32_t (&ksz)[NG]) {
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    if constexpr (MB == 4)
+      ksz[g] = raw[g];
+    else
+      ksz[g] = (g & 1) ? e4m3_pair_hi(raw[g >> 1]) : e4m3_pair_lo(raw[g >> 1]);
+  }
+}
+// four tokens' V pairs of one group
+template <int MB, class W>
+__device__ __forceinline__ u32x4 v_pairs(const W& raw) {
+  if constexpr (MB == 4)
+    return raw;
+  else
+    return u32x4{e4m3_pair_lo(raw[0]), e4m3_pair_hi(raw[0]), e4m3_pair_lo(raw[1]), e4m3_pair_hi(raw[1])};
+}
+// raw words of a lane's K pairs (NG * MB bytes) and V pairs (4 * MB bytes)
+template <int NG, int MB>
+using KRaw = typename std::conditional<NG * MB == 16, u32x4, typename std::conditional<NG * MB == 8, u32x2, u32x1>::type>::type;
+template <int MB>
+using VRaw = typename std::conditional<MB == 4, u32x4, u32x2>::type;
 
 // Buffer descriptor of one block (gfx9 raw buffer: stride 0, bounds = the
 // block's bytes).  The block address is wavefront-uniform, so the descriptor
@@ -482,26 +517,28 @@ constexpr int kBufferWord3 = 0x00020000;
 // s_waitcnt immediate for vmcnt(0) alone (expcnt and lgkmcnt at their maxima)
 constexpr int kWaitVmcnt0 = 0x0F70;
 
-template <int NG>
+template <class W>
+__device__ __forceinline__ W buffer_load(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  if constexpr (sizeof(W) == 16)
+    return __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+  else if constexpr (sizeof(W) == 8)
+    return __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
+  else
+    return u32x1{__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0)};
+}
+
+template <int NG, int MB>
 __device__ __forceinline__ Int2Data<NG> int2_load(const uint8_t* blk0, const uint8_t* blk1, const Int2Offsets& o) {
-  constexpr Int2Layout L{NG};
+  constexpr Int2Layout L{NG, MB};
   Int2Data<NG> d;
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc((void*)(t ? blk1 : blk0), 0, L.bytes(), kBufferWord3);
     d.kd.kc[t] = __builtin_amdgcn_raw_buffer_load_b64(rs, o.kc, 0, 0);
-    if constexpr (NG == 4) {
-      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, o.ksz, 0, 0);
-#pragma unroll
-      for (int g = 0; g < 4; ++g) d.kd.ksz[t][g] = v[g];
-    } else {
-      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rs, o.ksz, 0, 0);
-      d.kd.ksz[t][0] = v[0];
-      d.kd.ksz[t][1] = v[1];
-    }
+    k_pairs<NG, MB>(buffer_load<KRaw<NG, MB>>(rs, o.ksz), d.kd.ksz[t]);
     d.vd.vw[t] = __builtin_amdgcn_raw_buffer_load_b64(rs, o.vw, 0, 0);
-    d.vd.vsz[t] = __builtin_amdgcn_raw_buffer_load_b128(rs, o.vsz, 0, 0);
+    d.vd.vsz[t] = v_pairs<MB>(buffer_load<VRaw<MB>>(rs, o.vsz));
   }
   return d;
 }
@@ -535,9 +572,9 @@ __device__ __forceinline__ void lds_dma16(const u32x4& rs, uint32_t lds, uint32_
 }
 
 // st: LDS byte address of a two-block slot
-template <int NG>
+template <int NG, int MB>
 __device__ __forceinline__ void int2_issue(const uint8_t* blk0, const uint8_t* blk1, uint32_t st) {
-  constexpr Int2Layout L{NG};
+  constexpr Int2Layout L{NG, MB};
   constexpr int kRest = (L.bytes() - 1024) / 16;
   static_assert(L.bytes() > 1024 && L.bytes() <= 2048 && L.bytes() % 16 == 0, "block staging layout");
   const int lane = threadIdx.x & 63;
@@ -569,37 +606,29 @@ __device__ __forceinline__ void vm_wait() {
 __device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
 
 // a pair staged in LDS: each part is read when the pair asks for it
-template <int NG>
+template <int NG, int MB>
 struct Int2Staged {
   const uint8_t* st;
   Int2Offsets o;
   __device__ __forceinline__ Int2KData<NG> k() const {
-    constexpr Int2Layout L{NG};
+    constexpr Int2Layout L{NG, MB};
     Int2KData<NG> d;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const uint8_t* blk = st + t * L.bytes();
       d.kc[t] = *(const u32x2*)(blk + o.kc);
-      if constexpr (NG == 4) {
-        const u32x4 v = *(const u32x4*)(blk + o.ksz);
-#pragma unroll
-        for (int g = 0; g < 4; ++g) d.ksz[t][g] = v[g];
-      } else {
-        const u32x2 v = *(const u32x2*)(blk + o.ksz);
-        d.ksz[t][0] = v[0];
-        d.ksz[t][1] = v[1];
-      }
+      k_pairs<NG, MB>(*(const KRaw<NG, MB>*)(blk + o.ksz), d.ksz[t]);
     }
     return d;
   }
   __device__ __forceinline__ Int2VData<NG> v() const {
-    constexpr Int2Layout L{NG};
+    constexpr Int2Layout L{NG, MB};
     Int2VData<NG> d;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const uint8_t* blk = st + t * L.bytes();
       d.vw[t] = *(const u32x2*)(blk + o.vw);
-      d.vsz[t] = *(const u32x4*)(blk + o.vsz);
+      d.vsz[t] = v_pairs<MB>(*(const VRaw<MB>*)(blk + o.vsz));
     }
     return d;
   }
@@ -776,9 +805,9 @@ __device__ __forceinline__ void int2_pair(const Src& src, int lp0, int p_end, in
 
 // W wavefronts per work item: wavefront w takes the CT row tiles starting at
 // tile w CT, all of them reading the same staged pages.
-template <int NG, int CT, int W>
+template <int NG, int MB, int CT, int W>
 __device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float* p_lds, uint8_t* stage) {
-  constexpr Int2Layout L{NG};
+  constexpr Int2Layout L{NG, MB};
   constexpr int HPL = 4 / NG;
   constexpr int kTiles = W * CT;  // row tiles of the (request, KV head)
   const int lane = threadIdx.x & 63, ln = lane & 15, qd = lane >> 4;
@@ -829,7 +858,7 @@ __device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float
       const int64_t npg = p.n_int2_pages;
       const uint8_t* base = p.int2_pages;
       const int n_kv = p.n_kv;
-      const Int2Offsets off = int2_offsets<NG>();
+      const Int2Offsets off = int2_offsets<NG, MB>();
       auto blk = [&](int pg) { return base + ((int64_t)pg * n_kv + kv) * (int64_t)L.bytes(); };
       auto ok = [&](int pg) { return pg >= 0 && pg < npg; };
       // masked pair: partial pages at the region edges, odd tails, bad page ids
@@ -841,7 +870,7 @@ __device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float
         if (!ok0) pg0 = 0;
         if (!ok1) pg1 = pg0;
         const int pe = ok0 ? (ok1 ? p_end : lp0 + 1) : lp0;
-        const Int2Data<NG> D = int2_load<NG>(blk(pg0), blk(pg1), off);
+        const Int2Data<NG> D = int2_load<NG, MB>(blk(pg0), blk(pg1), off);
         int2_pair<NG, CT, true>(D, lp0, pe, lo, hi, K, S, p_lds);
       };
       int lp0 = p_begin;
@@ -869,22 +898,22 @@ __device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float
           // where the compiler sees it, so it adds no wait inside the pair loop
           __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
           auto page = [&](int l) { return blk(__builtin_amdgcn_readlane(id, l - c0)); };
-          int2_issue<NG>(page(lp0), page(lp0 + 1), a0);
-          if (lp0 + 4 <= lim) int2_issue<NG>(page(lp0 + 2), page(lp0 + 3), a0 + kSlot);
+          int2_issue<NG, MB>(page(lp0), page(lp0 + 1), a0);
+          if (lp0 + 4 <= lim) int2_issue<NG, MB>(page(lp0 + 2), page(lp0 + 3), a0 + kSlot);
           int cur = 0;  // slot of the pair at lp0 (wavefront-uniform)
           for (;;) {
             // stage the pair two ahead into the slot the previous pair freed,
             // then wait for this pair's bytes
             const int nxt = cur == 0 ? 2 : cur - 1;
             if (lp0 + 6 <= lim) {
-              int2_issue<NG>(page(lp0 + 4), page(lp0 + 5), a0 + nxt * kSlot);
+              int2_issue<NG, MB>(page(lp0 + 4), page(lp0 + 5), a0 + nxt * kSlot);
               vm_wait<8>();
             } else if (lp0 + 4 <= lim) {
               vm_wait<4>();
             } else {
               vm_wait<0>();
             }
-            int2_pair<NG, CT, false>(Int2Staged<NG>{stage + cur * kSlot, off}, lp0, p_end, lo, hi, K, S, p_lds);
+            int2_pair<NG, CT, false>(Int2Staged<NG, MB>{stage + cur * kSlot, off}, lp0, p_end, lo, hi, K, S, p_lds);
             lp0 += 2;
             if (lp0 + 2 > lim) break;
             cur = cur == 2 ? 0 : cur + 1;
@@ -908,14 +937,14 @@ __device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float
           barrier_no_fence();  // every wavefront is done with the slots of the previous chunk
           auto page = [&](int l) { return blk(__builtin_amdgcn_readlane(id, l - c0)); };
           if (leader) {
-            int2_issue<NG>(page(lp0), page(lp0 + 1), a0);
-            if (lp0 + 4 <= lim) int2_issue<NG>(page(lp0 + 2), page(lp0 + 3), a0 + kSlot);
+            int2_issue<NG, MB>(page(lp0), page(lp0 + 1), a0);
+            if (lp0 + 4 <= lim) int2_issue<NG, MB>(page(lp0 + 2), page(lp0 + 3), a0 + kSlot);
           }
           int cur = 0;
           for (;;) {
             if (leader) {
               if (lp0 + 6 <= lim) {
-                int2_issue<NG>(page(lp0 + 4), page(lp0 + 5), a0 + ((cur + 2) & 3) * kSlot);
+                int2_issue<NG, MB>(page(lp0 + 4), page(lp0 + 5), a0 + ((cur + 2) & 3) * kSlot);
                 vm_wait<8>();
               } else if (lp0 + 4 <= lim) {
                 vm_wait<4>();
@@ -924,7 +953,7 @@ __device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float
               }
             }
             barrier_no_fence();
-            int2_pair<NG, CT, false>(Int2Staged<NG>{stage + cur * kSlot, off}, lp0, p_end, lo, hi, K, S, p_lds);
+            int2_pair<NG, CT, false>(Int2Staged<NG, MB>{stage + cur * kSlot, off}, lp0, p_end, lo, hi, K, S, p_lds);
             lp0 += 2;
             if (lp0 + 2 > lim) break;
             cur = (cur + 1) & 3;
@@ -1141,15 +1170,15 @@ __device__ void bf16_item(const DecodeParams& p, int b, int kv, int split) {
 // unpacked codes, 2.  Wavefronts of one item share the staged pages.  LDS per
 // item: each wavefront's p and the staging ring (three slots for one
 // wavefront, four when shared).
-template <int NG, int CT, int W>
+template <int NG, int MB, int CT, int W>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(CT == 1 ? 4 : (CT == 2 ? 2 : 1), 8))) void
 decode_int2(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) float p_lds[W][(16 * CT / NG) * 32];
-  __shared__ __attribute__((aligned(16))) uint8_t stage[(W == 1 ? 6 : 8) * Int2Layout{NG}.bytes()];
+  __shared__ __attribute__((aligned(16))) uint8_t stage[(W == 1 ? 6 : 8) * Int2Layout{NG, MB}.bytes()];
   const int item = blockIdx.x;
   const int split = item % p.splits_int2;
   const int bk = item / p.splits_int2;
-  int2_item<NG, CT, W>(p, bk / p.n_kv, bk % p.n_kv, split, p_lds[W > 1 ? threadIdx.x >> 6 : 0], stage);
+  int2_item<NG, MB, CT, W>(p, bk / p.n_kv, bk % p.n_kv, split, p_lds[W > 1 ? threadIdx.x >> 6 : 0], stage);
 }
 
 __global__ __launch_bounds__(64) void decode_bf16(DecodeParams p) {
@@ -1309,7 +1338,7 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeParams p) {
   }
 }
 
-template <int NG, int CT, int W>
+template <int NG, int MB, int CT, int W>
 hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
   const int bkn = p.batch * p.n_kv;
   // the event pair brackets the dominant kernel: the INT2 stream when there is
@@ -1322,12 +1351,12 @@ hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream, hipEvent_t
   hipError_t e = hipSuccess;
   if (int2) {
     if (p.step_slots)
-      hipLaunchKernelGGL((decode_prologue<NG, CT * W, true>), dim3(bkn), dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((decode_prologue<NG, MB, CT * W, true>), dim3(bkn), dim3(256), 0, stream, p);
     else
-      hipLaunchKernelGGL((decode_prologue<NG, CT * W, false>), dim3(bkn), dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((decode_prologue<NG, MB, CT * W, false>), dim3(bkn), dim3(256), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = mark(ev_start)) != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_int2<NG, CT, W>), dim3(bkn * p.splits_int2), dim3(64 * W), 0, stream, p);
+    hipLaunchKernelGGL((decode_int2<NG, MB, CT, W>), dim3(bkn * p.splits_int2), dim3(64 * W), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = mark(ev_stop)) != hipSuccess) return e;
   }
@@ -1341,22 +1370,29 @@ hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream, hipEvent_t
   return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_decode(const DecodeParams& p, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
+template <int MB>
+hipError_t launch_decode_mb(const DecodeParams& p, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
   // p.ct = 16-row tiles of a (request, KV head), spread as tile_split says
   const TileSplit ts = tile_split(p.ct);
   const int key = ts.ct * 10 + ts.w;
   if (ts.ct * ts.w != p.ct) return hipErrorInvalidValue;
   if (p.ng == 4) {
-    if (key == 11) return launch_decode_t<4, 1, 1>(p, stream, ev_start, ev_stop);
-    if (key == 21) return launch_decode_t<4, 2, 1>(p, stream, ev_start, ev_stop);
-    if (key == 13) return launch_decode_t<4, 1, 3>(p, stream, ev_start, ev_stop);
-    if (key == 22) return launch_decode_t<4, 2, 2>(p, stream, ev_start, ev_stop);
+    if (key == 11) return launch_decode_t<4, MB, 1, 1>(p, stream, ev_start, ev_stop);
+    if (key == 21) return launch_decode_t<4, MB, 2, 1>(p, stream, ev_start, ev_stop);
+    if (key == 13) return launch_decode_t<4, MB, 1, 3>(p, stream, ev_start, ev_stop);
+    if (key == 22) return launch_decode_t<4, MB, 2, 2>(p, stream, ev_start, ev_stop);
   } else if (p.ng == 2) {
-    if (key == 11) return launch_decode_t<2, 1, 1>(p, stream, ev_start, ev_stop);
-    if (key == 21) return launch_decode_t<2, 2, 1>(p, stream, ev_start, ev_stop);
+    if (key == 11) return launch_decode_t<2, MB, 1, 1>(p, stream, ev_start, ev_stop);
+    if (key == 21) return launch_decode_t<2, MB, 2, 1>(p, stream, ev_start, ev_stop);
   }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
+  if (p.mb == 4) return launch_decode_mb<4>(p, stream, ev_start, ev_stop);
+  if (p.mb == 2) return launch_decode_mb<2>(p, stream, ev_start, ev_stop);
   return hipErrorInvalidValue;
 }
 

@@ -56,12 +56,15 @@ oscar_status check_shape(const oscar_shape* s) {
   if (s->sink < 0 || s->recent < 0) return fail(OSCAR_EINVAL, "sink/recent must be >= 0");
   if (s->recent % kPage) return fail(OSCAR_EUNSUPPORTED, "recent %d must be a multiple of %d", s->recent, kPage);
   if (s->sink > (1 << 26) || s->recent > (1 << 26)) return fail(OSCAR_EINVAL, "sink/recent too large");
+  if (s->scale_bits != 0 && s->scale_bits != 16 && s->scale_bits != 8)
+    return fail(OSCAR_EUNSUPPORTED, "scale_bits %d unsupported (16 or 8)", s->scale_bits);
   return OSCAR_OK;
 }
 
 int ng_of(const oscar_shape* s) { return kHeadDim / s->group; }
 int ct_of(const oscar_shape* s) { return (s->n_q_heads / s->n_kv_heads * ng_of(s) + 15) / 16; }
-int64_t int2_block(const oscar_shape* s) { return Int2Layout{ng_of(s)}.bytes(); }
+int mb_of(const oscar_shape* s) { return s->scale_bits == 8 ? 2 : 4; }
+int64_t int2_block(const oscar_shape* s) { return Int2Layout{ng_of(s), mb_of(s)}.bytes(); }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -690,6 +693,7 @@ oscar_status oscar_quant_write(const oscar_shape* shape, const oscar_layer* laye
   p.n = n;
   p.n_kv = shape->n_kv_heads;
   p.group = shape->group;
+  p.mb = mb_of(shape);
   return hip_status(launch_quant_write(p, 0, (hipStream_t)stream), "quant_write launch");
 }
 
@@ -716,6 +720,7 @@ oscar_status oscar_requant_from_bf16(const oscar_shape* shape, const oscar_layer
   p.n = n;
   p.n_kv = shape->n_kv_heads;
   p.group = shape->group;
+  p.mb = mb_of(shape);
   return hip_status(launch_quant_write(p, 1, (hipStream_t)stream), "requant launch");
 }
 
@@ -839,6 +844,7 @@ static oscar_status decode_common(const oscar_shape* shape, const oscar_layer* l
   p.g = p.n_q / p.n_kv;
   p.ng = baseline ? 4 : ng_of(shape);
   p.ct = baseline ? 1 : ct_of(shape);
+  p.mb = mb_of(shape);
   if (baseline) {
     p.sink = 1 << 28;
     p.recent = 0;

@@ -9,14 +9,17 @@ namespace oscar {
 constexpr int kHeadDim = 128;
 constexpr int kPage = 16;
 
-// Byte offsets inside an INT2 (page, KV head) block; ng = head_dim / group.
+// Byte offsets inside an INT2 (page, KV head) block; ng = head_dim / group,
+// mb = bytes of one (scale, zero) pair: 4 (two fp16) or 2 (two FP8 E4M3, the
+// lower-metadata format).
 struct Int2Layout {
   int ng;
+  int mb;
   __host__ __device__ constexpr int k_codes() const { return 0; }
   __host__ __device__ constexpr int k_sz() const { return kPage * kHeadDim / 4; }
-  __host__ __device__ constexpr int v_codes() const { return k_sz() + kPage * ng * 4; }
+  __host__ __device__ constexpr int v_codes() const { return k_sz() + kPage * ng * mb; }
   __host__ __device__ constexpr int v_sz() const { return v_codes() + kPage * kHeadDim / 4; }
-  __host__ __device__ constexpr int bytes() const { return v_sz() + kPage * ng * 4; }
+  __host__ __device__ constexpr int bytes() const { return v_sz() + kPage * ng * mb; }
 };
 constexpr int kBf16BlockBytes = 4 * kPage * kHeadDim;
 
@@ -35,6 +38,7 @@ struct QuantParams {
   int64_t n;
   int n_kv;
   int group;
+  int mb;                     // bytes of a (scale, zero) pair: 4 or 2
 };
 
 struct DecodeParams {
@@ -51,6 +55,7 @@ struct DecodeParams {
   int max_bf16_pages;
   const int32_t* ctx_lens;
   int batch, n_q, n_kv, g, ng, ct;
+  int mb;                     // bytes of a (scale, zero) pair in the INT2 blocks: 4 or 2
   int sink, recent;           // region rule (baseline: sink huge, recent 0)
   int splits_int2, splits_bf16;
   int bf16_in_combine;        // bf16 splits (<= 4) run by the combine kernel's wavefronts

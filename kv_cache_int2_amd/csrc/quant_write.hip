@@ -19,7 +19,8 @@
 // an fp64 rotated value, the same precision a double-precision reference uses.
 // Per group: mn, mx; s = fp16((mx - mn) / 3), z = fp16(mn), one rounding from
 // fp64, nearest-even; code = clamp(rint((x - z) / s), 0, 3) in fp64 (IEEE
-// division, rint = nearest-even).
+// division, rint = nearest-even).  The lower-metadata format (MB = 2) rounds s
+// and z to FP8 E4M3 instead, the same way.
 //
 // Storage (per (page, KV head) block): K codes token-major (a token's 32 bytes
 // are its own) with token-major scale/zero, V codes by token quad [4][128]
@@ -41,10 +42,10 @@ typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __builtin_bit_cast(float, (uint32_t)b << 16); }
 
-template <int MODE, int NG>
+template <int MODE, int NG, int MB>
 __global__ __launch_bounds__(512) void quant_write_kernel(QuantParams p) {
   constexpr int G = kHeadDim / NG;
-  constexpr Int2Layout L{NG};
+  constexpr Int2Layout L{NG, MB};
   constexpr int kTpg = 32 / NG;  // threads per (token, group), 4 channels each
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -125,15 +126,14 @@ __global__ __launch_bounds__(512) void quant_write_kernel(QuantParams p) {
       mx = omx > mx ? omx : mx;
       nan |= __shfl_xor((int)nan, off) != 0;
     }
-    uint16_t sb, zb;
+    uint32_t sz;
     if (nan) {
-      sb = zb = 0x7e00u;
+      sz = nan_sz<MB>();
 #pragma unroll
       for (int e = 0; e < 4; ++e) codes[t][j0 + e] = 0;
     } else {
-      sb = f64_to_f16_bits((mx - mn) / 3.0);
-      zb = f64_to_f16_bits(mn);
-      const double sd = f16_bits_to_f64(sb), zd = f16_bits_to_f64(zb);
+      double sd, zd;
+      sz = encode_sz<MB>((mx - mn) / 3.0, mn, sd, zd);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         double c = 0.0;
@@ -144,7 +144,7 @@ __global__ __launch_bounds__(512) void quant_write_kernel(QuantParams p) {
         codes[t][j0 + e] = (uint8_t)c;
       }
     }
-    if (sub == 0) szs[t][gm] = (uint32_t)sb | ((uint32_t)zb << 16);
+    if (sub == 0) szs[t][gm] = sz;
   }
   __syncthreads();
   if (tid >= 64) return;
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(512) void quant_write_kernel(QuantParams p) {
       const int slot = dst[t] % kPage;
       uint8_t* blk = pages + (page * p.n_kv + kv) * blk_bytes;
       const int idx = isv ? (gm * kPage + slot) : (slot * NG + gm);  // V group-major, K token-major
-      *(uint32_t*)(blk + (isv ? L.v_sz() : L.k_sz()) + idx * 4) = szs[t][gm];
+      store_sz<MB>(blk + (isv ? L.v_sz() : L.k_sz()) + idx * MB, szs[t][gm]);
     }
   }
   if (!isv) {
@@ -246,10 +246,14 @@ __global__ __launch_bounds__(256) void copy_pages_kernel(uint8_t* base, int64_t 
 template <int MODE>
 hipError_t launch_qw(const QuantParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)((p.n + 15) / 16), (unsigned)p.n_kv, 2);
-  if (p.group == 32)
-    hipLaunchKernelGGL((quant_write_kernel<MODE, 4>), grid, dim3(512), 0, stream, p);
+  if (p.group == 32 && p.mb == 4)
+    hipLaunchKernelGGL((quant_write_kernel<MODE, 4, 4>), grid, dim3(512), 0, stream, p);
+  else if (p.group == 32)
+    hipLaunchKernelGGL((quant_write_kernel<MODE, 4, 2>), grid, dim3(512), 0, stream, p);
+  else if (p.mb == 4)
+    hipLaunchKernelGGL((quant_write_kernel<MODE, 2, 4>), grid, dim3(512), 0, stream, p);
   else
-    hipLaunchKernelGGL((quant_write_kernel<MODE, 2>), grid, dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((quant_write_kernel<MODE, 2, 2>), grid, dim3(512), 0, stream, p);
   return hipGetLastError();
 }
 

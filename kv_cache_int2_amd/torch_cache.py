@@ -79,10 +79,14 @@ class DeviceCache:
         return out
 
     def int2_block_bytes_of(self, page: int, head: int) -> np.ndarray:
+        if not (0 <= page < self.cache.n_int2_pages and 0 <= head < self.shape.n_kv_heads):
+            raise IndexError(f"INT2 block ({page}, {head}) outside the pool")
         off = (page * self.shape.n_kv_heads + head) * self.int2_block
         return self.int2[off:off + self.int2_block].cpu().numpy()
 
     def bf16_block_bytes_of(self, page: int, head: int) -> np.ndarray:
+        if not (0 <= page < self.cache.n_bf16_pages and 0 <= head < self.shape.n_kv_heads):
+            raise IndexError(f"bf16 block ({page}, {head}) outside the pool")
         off = (page * self.shape.n_kv_heads + head) * self.bf16_block
         return self.bf16[off:off + self.bf16_block].cpu().numpy()
 

@@ -48,7 +48,7 @@ def _expected_int2_block(st, lp, h, group):
     kc = np.zeros((16, 128), np.uint8)
     vc = np.zeros_like(kc)
     ng = 128 // group
-    ks, kz, vs, vz = (np.zeros((16, ng), np.float16) for _ in range(4))
+    ks, kz, vs, vz = (np.zeros((16, ng), st.k_s.dtype) for _ in range(4))
     for s in range(16):
         p = lp * 16 + s
         if p < t and st.region[p] == O.REGION_INT2:
@@ -157,15 +157,18 @@ def test_qwen3_8b_layer_32k():
         _check_close(out, ref, f"qwen3_8b_32k decode splits={si}")
 
 
-@pytest.mark.parametrize("hq,hkv,group", [(4, 1, 32), (8, 1, 32), (12, 1, 32), (16, 1, 32), (12, 1, 64), (4, 2, 64), (16, 1, 64)])
-def test_ragged_batch_gqa_groups(hq, hkv, group):
+@pytest.mark.parametrize("hq,hkv,group,scale_bits", [(4, 1, 32, 16), (8, 1, 32, 16), (12, 1, 32, 16), (16, 1, 32, 16),
+                                                      (12, 1, 64, 16), (4, 2, 64, 16), (16, 1, 64, 16),
+                                                      (4, 1, 64, 8), (8, 1, 32, 8), (12, 1, 64, 8)])
+def test_ragged_batch_gqa_groups(hq, hkv, group, scale_bits):
     """Mixed lengths (all-bf16, exactly sink+recent, one INT2 token, odd page
-    counts) in one batch, for several GQA widths and both group sizes."""
+    counts) in one batch, for several GQA widths, both group sizes and both
+    scale/zero formats."""
     w = synth.Workload("ragged", 10 + hq + group, hq, hkv, 128, 1, 0, group=group, sink=4, recent=32,
                        outlier_scale=(40.0, 40.0), calib_tokens=512)
-    _flush(f"case ragged hq={hq} hkv={hkv} G={group}")
+    _flush(f"case ragged hq={hq} hkv={hkv} G={group} scale_bits={scale_bits}")
     cal = _calibrate(w)
-    sh = K.make_shape(n_q_heads=hq, n_kv_heads=hkv, group=group, sink=4, recent=32)
+    sh = K.make_shape(n_q_heads=hq, n_kv_heads=hkv, group=group, sink=4, recent=32, scale_bits=scale_bits)
     dc = DeviceCache(sh, cal.r_k, cal.r_v, cal.tau_k, cal.tau_v, 600, 64)
     lens = [1, 5, 36, 37, 53, 100, 515, 1000, 2049, 3001]
     seqs, stores, qs = [], [], []
@@ -174,7 +177,7 @@ def test_ragged_batch_gqa_groups(hq, hkv, group):
         seq = dc.new_seq()
         _fill(dc, seq, kb, vb, [t] if t < 200 else [t - 7] + [1] * 7)
         seqs.append(seq)
-        stores.append(O.store_request(kb, vb, cal, group, 4, 32))
+        stores.append(O.store_request(kb, vb, cal, group, 4, 32, scale_bits))
         qs.append(synth.q_decode_bf16(w, r))
     for r in (0, 6, 9):
         _check_pages(dc, seqs[r], stores[r], w, f"ragged len={lens[r]}")
@@ -203,12 +206,14 @@ def test_empty_context_gives_zero_rows():
     _check_close(out[1], O.decode_attention(q[1], st, cal, 32), "after empty row")
 
 
-def test_quant_write_scattered_slots_and_nan_group():
+@pytest.mark.parametrize("scale_bits", [16, 8])
+def test_quant_write_scattered_slots_and_nan_group(scale_bits):
     """Tokens written in shuffled order into scattered slots (V words merged by
-    atomics across wavefronts) and a NaN input row."""
+    atomics across wavefronts) and a NaN input row, with fp16 and with FP8
+    scale and zero."""
     w = synth.WORKLOADS["qwen3_8b_32k"]
     cal = _calibrate(w)
-    sh = K.make_shape(n_q_heads=32, n_kv_heads=8, group=32, sink=0, recent=0)
+    sh = K.make_shape(n_q_heads=32, n_kv_heads=8, group=32, sink=0, recent=0, scale_bits=scale_bits)
     dc = DeviceCache(sh, cal.r_k, cal.r_v, cal.tau_k, cal.tau_v, 64, 1)
     n = 37 * 16
     kb, vb = synth.kv_request_bf16(w, 3, 0, n)
@@ -224,20 +229,21 @@ def test_quant_write_scattered_slots_and_nan_group():
     for h in (0, 2, 7):
         xk = O.bf16_to_f64(kb[:, h])
         xv = O.bf16_to_f64(vb[:, h])
-        ck, sk, zk, _ = O.quantize(xk, cal.r_k[h], cal.tau_k, 32)
-        cv, sv, zv, _ = O.quantize(xv, cal.r_v[h], cal.tau_v, 32)
+        ck, sk, zk, _ = O.quantize(xk, cal.r_k[h], cal.tau_k, 32, scale_bits)
+        cv, sv, zv, _ = O.quantize(xv, cal.r_v[h], cal.tau_v, 32, scale_bits)
+        bits = np.uint16 if scale_bits == 16 else np.uint8
         for i in range(n):
             page, s = divmod(int(slots[i]), 16)
-            blk = O.unpack_int2_block(pool[page, h], 128, 32)
+            blk = O.unpack_int2_block(pool[page, h], 128, 32, scale_bits)
             assert np.array_equal(blk[0][s], ck[i]), (h, i)
             assert np.array_equal(blk[3][s], cv[i]), (h, i)
             if h == 2 and i == 100:
-                assert np.all(np.isnan(blk[1][s])) and np.all(np.isnan(blk[2][s]))
+                assert np.all(np.isnan(O.meta_values(blk[1][s]))) and np.all(np.isnan(O.meta_values(blk[2][s])))
                 continue
-            assert np.array_equal(blk[1][s].view(np.uint16), sk[i].view(np.uint16))
-            assert np.array_equal(blk[2][s].view(np.uint16), zk[i].view(np.uint16))
-            assert np.array_equal(blk[4][s].view(np.uint16), sv[i].view(np.uint16))
-            assert np.array_equal(blk[5][s].view(np.uint16), zv[i].view(np.uint16))
+            assert np.array_equal(blk[1][s].view(bits), sk[i].view(bits))
+            assert np.array_equal(blk[2][s].view(bits), zk[i].view(bits))
+            assert np.array_equal(blk[4][s].view(bits), sv[i].view(bits))
+            assert np.array_equal(blk[5][s].view(bits), zv[i].view(bits))
 
 
 def test_shared_prefix_fork():
@@ -299,17 +305,18 @@ def test_bf16_baseline_decode(hq, hkv):
             _check_close(out[r], ref, f"baseline hq={hq} len={lens[r]} splits={sp}")
 
 
-def _full_size_sampled(w, group, check):
+def _full_size_sampled(w, group, check, scale_bits=16):
     """Fill a workload at full size (a shared prefix through a fork, as the
     bench does), decode the whole batch in the bench's launch configuration
     (automatic split count), and check the requests in `check`: every query
     head's output, and a spread of their page blocks, against the oracle run on
     those requests alone."""
     B, T = w.batch, w.context
-    _flush(f"case {w.name}: B={B} T={T} Hq={w.n_q_heads} Hkv={w.n_kv_heads} G={group}")
+    _flush(f"case {w.name}: B={B} T={T} Hq={w.n_q_heads} Hkv={w.n_kv_heads} G={group} sink={w.sink} "
+           f"recent={w.recent} scale_bits={scale_bits}")
     cal = _calibrate(w)
     sh = K.make_shape(n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads, group=group, sink=w.sink,
-                      recent=w.recent)
+                      recent=w.recent, scale_bits=scale_bits)
     ppr = (T + 15) // 16 + 2
     dc = DeviceCache(sh, cal.r_k, cal.r_v, cal.tau_k, cal.tau_v, B * ppr + 8,
                      B * (w.sink // 16 + 2 + w.recent // 16) + 8)
@@ -333,21 +340,29 @@ def _full_size_sampled(w, group, check):
     i2, bf, _ = dc.tables(seqs)
     for r in check:
         kb, vb = synth.kv_request_bf16(w, r, 0, T)
-        st = O.store_request(kb, vb, cal, group, w.sink, w.recent)
+        st = O.store_request(kb, vb, cal, group, w.sink, w.recent, scale_bits)
         _check_close(out[r], O.decode_attention(q[r], st, cal, group), f"{w.name} G={group} request {r}")
         # page blocks: the first INT2 pages, pages spread over the history, the last ones
-        n_lp = int(np.count_nonzero(i2[r] >= 0))
-        lps = sorted({0, 1, 2, n_lp // 3, n_lp // 2, 2 * n_lp // 3, n_lp - 2, n_lp - 1})
+        # (logical INT2 pages before the sink's end hold no token and have no block)
+        have = np.nonzero(i2[r] >= 0)[0]
+        n_lp = have.size
+        lps = sorted({int(have[i]) for i in (0, 1, 2, n_lp // 3, n_lp // 2, 2 * n_lp // 3, n_lp - 2, n_lp - 1)})
         mism = 0
+        def differ(kind, lp, h, got, exp):
+            bad = np.nonzero(got != exp)[0]
+            if bad.size:
+                _flush(f"{w.name} request {r}: {kind} page {lp} head {h}: {bad.size} bytes differ at "
+                       f"{bad[:6].tolist()}: got {got[bad[:6]].tolist()} expected {exp[bad[:6]].tolist()}")
+            return int(bad.size > 0)
         for lp in lps:
             for h in range(w.n_kv_heads):
                 got = dc.int2_block_bytes_of(int(i2[r, lp]), h)
-                mism += not np.array_equal(got, _expected_int2_block(st, lp, h, group))
+                mism += differ("INT2", lp, h, got, _expected_int2_block(st, lp, h, group))
             for lpb in range(bf.shape[1]):
                 if bf[r, lpb] >= 0 and lp == lps[0]:
                     for h in range(w.n_kv_heads):
                         got = dc.bf16_block_bytes_of(int(bf[r, lpb]), h)
-                        mism += not np.array_equal(got, _expected_bf16_block(st, lpb, h, w.sink, w.recent))
+                        mism += differ("bf16", lpb, h, got, _expected_bf16_block(st, lpb, h, w.sink, w.recent))
         _flush(f"{w.name} G={group} request {r}: {len(lps)} INT2 pages x {w.n_kv_heads} heads and the bf16 "
                f"pages, mismatching blocks={mism}")
         assert mism == 0
@@ -366,6 +381,14 @@ def test_full_size_prefix_64x32k_sampled():
     _full_size_sampled(w, w.group, (0, w.batch - 1))
 
 
+def test_full_size_28x100k_pages_layout_sampled():
+    """The pages' default layout on the 28 x 100k batch: sink 64, recent 256,
+    G = 64 with FP8 scale and zero (2.25 history bits per element)."""
+    import dataclasses
+    w = dataclasses.replace(synth.WORKLOADS["long_28x100k"], sink=64, recent=256, group=64)
+    _full_size_sampled(w, 64, (0, w.batch - 1), scale_bits=8)
+
+
 @pytest.mark.parametrize("group", [32, 64])
 def test_full_size_stress_16x128k_sampled(group):
     """16 requests x 131072 tokens, g = 12, both group sizes (three tiles as
@@ -374,8 +397,9 @@ def test_full_size_stress_16x128k_sampled(group):
     _full_size_sampled(w, group, (w.batch - 1,))
 
 
-@pytest.mark.parametrize("hq,hkv,group,sink,recent", [(8, 2, 32, 4, 32), (12, 1, 64, 20, 48), (4, 1, 32, 4, 0)])
-def test_fused_decode_step(hq, hkv, group, sink, recent):
+@pytest.mark.parametrize("hq,hkv,group,sink,recent,scale_bits", [(8, 2, 32, 4, 32, 16), (12, 1, 64, 20, 48, 16),
+                                                                   (4, 1, 32, 4, 0, 16), (4, 2, 64, 64, 48, 8)])
+def test_fused_decode_step(hq, hkv, group, sink, recent, scale_bits):
     """oscar_decode_step (writes fused into the decode's prologue kernel) against
     the separate write calls + oscar_decode_attn: identical cache bytes and bit-identical outputs after every step,
     through ring age-out, page crossings, sink growth and (recent = 0) new
@@ -384,9 +408,9 @@ def test_fused_decode_step(hq, hkv, group, sink, recent):
     from kv_cache_int2_amd.torch_cache import to_dev_bits, to_dev_i32
     w = synth.Workload("fused", 70 + hq + group, hq, hkv, 128, 1, 0, group=group, sink=sink, recent=recent,
                        outlier_scale=(40.0, 40.0), calib_tokens=512)
-    _flush(f"case fused step hq={hq} hkv={hkv} G={group} sink={sink} recent={recent}")
+    _flush(f"case fused step hq={hq} hkv={hkv} G={group} sink={sink} recent={recent} scale_bits={scale_bits}")
     cal = _calibrate(w)
-    sh = K.make_shape(n_q_heads=hq, n_kv_heads=hkv, group=group, sink=sink, recent=recent)
+    sh = K.make_shape(n_q_heads=hq, n_kv_heads=hkv, group=group, sink=sink, recent=recent, scale_bits=scale_bits)
     lens0 = [0, 3, sink + recent - 2, 200, 1001]
     n_steps = 40
     B = len(lens0)
@@ -440,7 +464,7 @@ def test_fused_decode_step(hq, hkv, group, sink, recent):
     for r in range(B):
         t = lens0[r] + n_steps
         kb, vb = synth.kv_request_bf16(w, r, 0, t)
-        store = O.store_request(kb, vb, cal, group, sink, recent)
+        store = O.store_request(kb, vb, cal, group, sink, recent, scale_bits)
         _check_pages(caches[1], seqs[1][r], store, w, f"fused step len={t}")
         _check_close(out[r], O.decode_attention(qf[r], store, cal, group), f"fused step decode len={t}")
 
