@@ -426,6 +426,21 @@ def decode_attention(q_bits: np.ndarray, st: StoredRequest, cal: LayerCalibratio
     return attend(bf16_to_f64(q_bits), k, v)
 
 
+def prefill_attention(q_bits: np.ndarray, st: StoredRequest, cal: LayerCalibration, group: int) -> np.ndarray:
+    """Exact fp64 attention of a chunk of C new queries over the mixed cache
+    (chunked prefill, [IT] 2.2.B / [ES] serving section: prefix-cached chunked
+    prefill over the same paged cache).  st holds the request after the
+    chunk's C tokens were written, T positions in all; query c sits at
+    position T - C + c and attends the positions up to and including its own
+    (causal), each in the form the cache holds it.  q_bits: [C, Hq, d] bf16
+    bit patterns; returns [C, Hq, d]."""
+    k, v = represented_kv(st, cal, group)
+    c_n = q_bits.shape[0]
+    t = k.shape[0]
+    return np.stack([attend(bf16_to_f64(q_bits[c]), k[:t - c_n + c + 1], v[:t - c_n + c + 1])
+                     for c in range(c_n)])
+
+
 # ---------------------------------------------------------------------------
 # Storage format of one page (per KV head).  Written out independently here
 # from the format's definition so stored bytes can be compared exactly.

@@ -699,3 +699,60 @@ def test_f3_fp8_meta_block_layout_by_hand():
     assert vsz[(0 * 16 + 5) * 2] == 0x4A and np.count_nonzero(vsz[0::2] == 0x28) == 31
     for a, b in zip(O.unpack_int2_block(blk, d, group, 8), (kc, ks, kz, vc, vs, kz)):
         assert np.array_equal(a, b)
+
+
+# ---------------------------------------------------------------------------
+# f2: chunked-prefill attention over the mixed cache
+# ---------------------------------------------------------------------------
+
+def test_f2_prefill_single_query_is_decode(tiny_cal):
+    """A chunk of one query is a decode step: same result as decode_attention."""
+    w, q, k, v, cal = tiny_cal
+    kb, vb = synth.kv_request_bf16(w, 0, 0, 700)
+    st = O.store_request(kb, vb, cal, 32, w.sink, w.recent)
+    qb = synth.q_decode_bf16(w, 0, 3)
+    assert np.array_equal(O.prefill_attention(qb[None], st, cal, 32)[0], O.decode_attention(qb, st, cal, 32))
+
+
+def test_f2_prefill_all_bf16_is_causal_sdpa():
+    """When every position is bf16 (T <= sink + recent) the chunk's attention
+    is causal scaled-dot-product attention over the bf16 values, bottom-right
+    aligned (the library routine with an explicit mask)."""
+    w = synth.WORKLOADS["tiny"]
+    q, k, v = synth.calib_layer(w, n=256)
+    cal = O.calibrate_layer(q, k, v)
+    t, c_n = 120, 9
+    kb, vb = synth.kv_request_bf16(w, 1, 0, t)
+    st = O.store_request(kb, vb, cal, 32, w.sink, w.recent)
+    assert np.all(st.region != O.REGION_INT2)
+    qb = np.stack([synth.q_decode_bf16(w, 1, s) for s in range(c_n)])
+    ours = O.prefill_attention(qb, st, cal, 32)
+    qt = torch.from_numpy(O.bf16_to_f64(qb)).permute(1, 0, 2)           # [H, C, d]
+    kt = torch.from_numpy(O.bf16_to_f64(kb)).permute(1, 0, 2)           # [Hkv, T, d]
+    vt = torch.from_numpy(O.bf16_to_f64(vb)).permute(1, 0, 2)
+    mask = torch.arange(t)[None, :] <= (t - c_n + torch.arange(c_n))[:, None]
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask).permute(1, 0, 2).numpy()
+    assert np.abs(ours - ref).max() < 1e-12
+
+
+def test_f2_prefill_brute_force_gqa_mixed_cache():
+    """Small GQA case with INT2 history, sink and recent: each query's output
+    recomputed by explicit loops over the positions it may see."""
+    w = synth.Workload("f2", 91, 4, 2, 128, 1, 0, sink=4, recent=32, calib_tokens=256)
+    q, k, v = synth.calib_layer(w)
+    cal = O.calibrate_layer(q, k, v)
+    t, c_n = 150, 6
+    kb, vb = synth.kv_request_bf16(w, 0, 0, t)
+    st = O.store_request(kb, vb, cal, 32, 4, 32)
+    kr, vr = O.represented_kv(st, cal, 32)
+    qb = np.stack([synth.q_decode_bf16(w, 0, s) for s in range(c_n)])
+    ours = O.prefill_attention(qb, st, cal, 32)
+    for c in range(c_n):
+        qf = O.bf16_to_f64(qb[c])
+        for h in range(4):
+            vis = t - c_n + c + 1
+            lg = [sum(qf[h, j] * kr[p, h // 2, j] for j in range(128)) / math.sqrt(128) for p in range(vis)]
+            m = max(lg)
+            wts = [math.exp(x - m) for x in lg]
+            o = [sum(wts[p] * vr[p, h // 2, j] for p in range(vis)) / sum(wts) for j in range(128)]
+            assert np.abs(ours[c, h] - np.array(o)).max() < 1e-10
