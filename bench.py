@@ -48,6 +48,10 @@ def parse():
     ap.add_argument("--layout", choices=["workload", "pages"], default="workload",
                     help="pages: the pages' default layout (sink 64, recent 256, G = 64, FP8 scale and zero)")
     ap.add_argument("--splits", type=int, default=0, help="INT2 splits per (request, KV head); 0 = auto")
+    ap.add_argument("--mode", choices=["decode", "prefill"], default="decode",
+                    help="prefill: time chunked-prefill attention (oscar_prefill_attn) of --chunk queries per "
+                         "request over the filled cache instead of decode steps")
+    ap.add_argument("--chunk", type=int, default=128, help="queries per request in --mode prefill")
     ap.add_argument("--unfused", action="store_true",
                     help="separate write calls and in-order kernels instead of the fused decode step")
     ap.add_argument("--no-baseline", action="store_true", help="skip the bf16 same-kernel baseline")
@@ -81,6 +85,68 @@ def int2_kernel_bytes(ctx, hkv, group, sink, recent, mb=4):
     bf16 tokens belong to the bf16 region's work."""
     per_int2 = 2 * (128 // 4 + (128 // group) * mb)
     return sum(int2_tokens(t, sink, recent) for t in ctx) * hkv * per_int2
+
+
+def run_prefill(args, w, sh, group, scale_bits, mb, cal):
+    """Chunked prefill: every request holds T - C tokens, its C-token chunk is
+    written, then the chunk's queries attend over the mixed cache; the
+    attention launches (oscar_prefill_attn) are timed, the cache unchanged."""
+    import torch
+    import kv_cache_int2_amd as K
+    import synth
+    from kv_cache_int2_amd.torch_cache import DeviceCache, to_dev_bits, to_dev_i32
+    B, hq, hkv, T, C = w.batch, w.n_q_heads, w.n_kv_heads, w.context, args.chunk
+    r_k, r_v, tau_k, tau_v = cal
+    ppr = (T + 15) // 16 + 2
+    dc = DeviceCache(sh, r_k, r_v, tau_k, tau_v, B * ppr + 8, B * (w.sink // 16 + 2 + w.recent // 16) + 8)
+    seqs = []
+    t = time.time()
+    for r in range(B):
+        kb, vb = synth.kv_request_bf16(w, r, 0, T)
+        s = dc.new_seq()
+        for c0 in range(0, T - C, 16384):
+            c1 = min(T - C, c0 + 16384)
+            dc.append(s, kb[c0:c1], vb[c0:c1])
+        dc.append(s, kb[T - C:], vb[T - C:])        # the chunk
+        seqs.append(s)
+    torch.cuda.synchronize()
+    log(f"cache filled in {time.time() - t:.1f}s; chunk of {C} per request written")
+    i2, bf, ctx = dc.tables(seqs)
+    q = to_dev_bits(np.stack([np.stack([synth.q_decode_bf16(w, r, c) for c in range(C)]) for r in range(B)]))
+    ws = torch.empty(K.oscar_prefill_workspace_bytes(sh, B, C), dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, C, hq, 128), dtype=torch.float32, device="cuda")
+    i2d, bfd, ctxd = to_dev_i32(i2), to_dev_i32(bf), to_dev_i32(ctx)
+    for _ in range(args.warmup):
+        K.oscar_prefill_attn(sh, dc.layer, dc.cache, q, i2d, bfd, ctxd, out, ws)
+    torch.cuda.synchronize()
+    K.oscar_profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        K.oscar_prefill_attn(sh, dc.layer, dc.cache, q, i2d, bfd, ctxd, out, ws)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    K.oscar_profile_enable(False)
+    int2_ms, launches = K.oscar_profile_read()
+    assert torch.isfinite(out).all(), "non-finite prefill output"
+    ctx_np = ctx.astype(np.int64)
+    attended = int(sum(int(c) - C + i + 1 for c in ctx_np for i in range(C)))
+    per_call = (t1 - t0) / args.steps
+    int2_us = int2_ms / max(launches, 1) * 1e3
+    int2_bytes = int2_kernel_bytes(ctx_np, hkv, group, w.sink, w.recent, mb)
+    log(f"prefill: {per_call * 1e3:.3f} ms per call, {launches // max(args.steps, 1)} INT2 passes of "
+        f"{int2_us:.1f} us each")
+    res = {
+        "metric": "chunked-prefill attention over the mixed cache: KV tokens attended/s",
+        "value": attended / per_call, "unit": "KV tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": per_call * 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "i8+f16 mfma, f32 acc", "data": "synthetic (seeded generator)",
+        "config": {"workload": w.name, "batch": B, "context": T, "chunk": C, "n_q_heads": hq, "n_kv_heads": hkv,
+                   "group": group, "sink": w.sink, "recent": w.recent, "scale_bits": scale_bits},
+        "int2_pass": {"kernel": "decode_int2", "passes_per_call": launches // max(args.steps, 1),
+                      "us_per_pass": round(int2_us, 2), "int2_bytes_per_pass": int(int2_bytes),
+                      "gbs_per_pass": round(int2_bytes / (int2_us * 1e-6) / 1e9, 1)},
+    }
+    print(json.dumps(res), flush=True)
 
 
 def main():
@@ -117,6 +183,9 @@ def main():
     qc, kc, vc = synth.calib_layer(w)
     r_k, r_v, _, _, tau_k, tau_v = K.oscar_calibrate_host(sh, qc, kc, vc)
     log(f"calibration {time.time() - t:.1f}s tau_k={tau_k:.3f} tau_v={tau_v:.3f}")
+    if args.mode == "prefill":
+        run_prefill(args, w, sh, group, scale_bits, mb, (r_k, r_v, tau_k, tau_v))
+        return
 
     pages_per_req = (T_final + 15) // 16 + 2
     dc = DeviceCache(sh, r_k, r_v, tau_k, tau_v, B * pages_per_req + 8, B * (w.sink // 16 + 2 + w.recent // 16) + 8)

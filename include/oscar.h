@@ -254,6 +254,30 @@ oscar_status oscar_decode_attn_bf16_baseline(const oscar_shape* shape, const osc
                                              const int32_t* ctx_lens, int32_t splits, float* out,
                                              void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- Chunked prefill over the mixed cache ([IT] 2.2.B and [ES] serving
+ * section: prefix-cached chunked prefill reads the same paged INT2 + bf16
+ * cache) ----
+ * Attention of a chunk of C new queries per request: query c of request b sits
+ * at position T - C + c (T = ctx_lens[b], the length after the chunk's tokens
+ * were written with the write calls) and attends every position up to its own,
+ * each in the form the cache holds it (INT2 history through the rotations as in
+ * decode, bf16 sink and recent values).  Inputs (device): q bf16
+ * [batch][C][n_q_heads][d]; block tables and ctx_lens as for oscar_decode_attn.
+ * Output (device): out fp32 [batch][C][n_q_heads][d].  Requires 1 <= C <=
+ * recent (the chunk lies in the bf16 window, so the INT2 history precedes every
+ * query): OSCAR_EUNSUPPORTED otherwise.  The queries run in blocks (16 at
+ * g = 4, G = 32), each block one pass over the history with one wavefront per
+ * 16 (query head, group) rows.  splits as in decode (0 = choose; bf16 splits
+ * default 1).  workspace: >= oscar_prefill_workspace_bytes with the same
+ * batch, C and splits, 256-byte aligned. */
+size_t oscar_prefill_workspace_bytes(const oscar_shape* shape, int32_t batch, int32_t chunk, int32_t splits_int2,
+                                     int32_t splits_bf16);
+oscar_status oscar_prefill_attn(const oscar_shape* shape, const oscar_layer* layer, const oscar_cache* cache,
+                                const void* q, int32_t batch, int32_t chunk, const int32_t* int2_bt,
+                                int32_t max_int2_pages, const int32_t* bf16_bt, int32_t max_bf16_pages,
+                                const int32_t* ctx_lens, int32_t splits_int2, int32_t splits_bf16, float* out,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
 /* Splits chosen when 0 is passed: the count whose work items fill two whole
  * rounds of the wavefronts the device runs at once, at most 64 and at least 32
  * pages per split (deterministic for a given device). */

@@ -72,6 +72,10 @@ _SIGS = {
     "oscar_decode_step": (C.c_int32, [C.POINTER(Shape), C.POINTER(Layer), C.POINTER(Cache), P, P, P, P,
                                       C.c_int32, P, C.c_int32, P, C.c_int32, P, C.c_int32, C.c_int32, P, P,
                                       C.c_size_t, P]),
+    "oscar_prefill_workspace_bytes": (C.c_size_t, [C.POINTER(Shape), C.c_int32, C.c_int32, C.c_int32, C.c_int32]),
+    "oscar_prefill_attn": (C.c_int32, [C.POINTER(Shape), C.POINTER(Layer), C.POINTER(Cache), P, C.c_int32,
+                                       C.c_int32, P, C.c_int32, P, C.c_int32, P, C.c_int32, C.c_int32, P, P,
+                                       C.c_size_t, P]),
     "oscar_decode_attn_bf16_baseline": (C.c_int32, [C.POINTER(Shape), C.POINTER(Cache), P, C.c_int32, P,
                                                     C.c_int32, P, C.c_int32, P, P, C.c_size_t, P]),
     "oscar_decode_auto_splits": (C.c_int32, [C.POINTER(Shape), C.c_int32, C.c_int32]),
@@ -298,6 +302,20 @@ def oscar_decode_step(shape, layer, cache, k_new, v_new, step_slots, q, int2_bt,
                                    _ptr(step_slots), _ptr(q), batch, _ptr(int2_bt), int2_bt.shape[1], _ptr(bf16_bt),
                                    bf16_bt.shape[1], _ptr(ctx_lens), splits_int2, splits_bf16, _ptr(out),
                                    _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def oscar_prefill_workspace_bytes(shape, batch, chunk, splits_int2=0, splits_bf16=0) -> int:
+    return int(lib().oscar_prefill_workspace_bytes(C.byref(shape), batch, chunk, splits_int2, splits_bf16))
+
+
+def oscar_prefill_attn(shape, layer, cache, q, int2_bt, bf16_bt, ctx_lens, out, workspace, splits_int2=0,
+                       splits_bf16=0, stream=None):
+    """q: device bf16 bits [batch, C, Hq, d]; out: fp32 [batch, C, Hq, d]."""
+    batch, chunk = q.shape[0], q.shape[1]
+    _check(lib().oscar_prefill_attn(C.byref(shape), C.byref(layer), C.byref(cache), _ptr(q), batch, chunk,
+                                    _ptr(int2_bt), int2_bt.shape[1], _ptr(bf16_bt), bf16_bt.shape[1],
+                                    _ptr(ctx_lens), splits_int2, splits_bf16, _ptr(out), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def oscar_decode_attn_bf16_baseline(shape, cache, q, bf16_bt, ctx_lens, out, workspace, splits=0, stream=None):

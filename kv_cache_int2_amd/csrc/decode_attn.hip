@@ -147,6 +147,17 @@ __device__ __forceinline__ const uint8_t* block_ptr(const uint8_t* base, int64_t
   return base + ((page * n_kv + kv) * (int64_t)bytes);
 }
 
+// Element offset of the q (and out) row of kernel head hv of KV head kv, and
+// the last position that head's query may attend (its own: the chunk's
+// queries are the request's last positions; in decode, the last one).
+__device__ __forceinline__ int64_t q_row(const DecodeParams& p, int b, int kv, int hv) {
+  const int c = hv / p.g_real, h = hv - c * p.g_real;
+  return (((int64_t)b * p.chunk + p.chunk0 + c) * p.q_heads + kv * p.g_real + h) * kHeadDim;
+}
+__device__ __forceinline__ int q_pos(const DecodeParams& p, int b, int hv) {
+  return p.ctx_lens[b] - p.chunk + p.chunk0 + hv / p.g_real;
+}
+
 // A 128 x 128 fp32 matrix to LDS by a block of 256 threads, row stride
 // `stride` floats: 16 independent 16-byte loads per thread, all issued before
 // the first store.
@@ -286,6 +297,62 @@ __device__ void step_writes(const DecodeParams& p, int b, int kv, const float* r
   if (put_i2) quantise_and_store<NG, MB>(p, kv, 1, i2_new, rk, rv, sc);
 }
 
+// The INT2 kernel's q operands of one (request, KV head), from the fixed-point
+// q~ (qi: [head][channel], g heads) and its scale exponent sq, for `tiles`
+// 16-row tiles (rows (head, group); rows past the g heads get zero digits):
+// aux = [logit factor 2^-sq / 2, 2 Qbar per row], then the int8 digits of 2Q
+// as MFMA A operands, words ((((tile*3 + digit)*2 + kstep)*64 + lane)*4 + reg).
+// Called by all 256 threads after qi is complete.
+template <int NG>
+__device__ __forceinline__ void write_q_operands(const DecodeParams& p, int bk, int tiles, int g,
+                                                 const int (*qi)[kHeadDim], int sq) {
+  constexpr int G = kHeadDim / NG;
+  const int t = threadIdx.x;
+  float* aux = p.qaux + (int64_t)bk * (1 + 16 * tiles);
+  if (t == 0) aux[0] = ldexpf(0.5f, -sq);
+  for (int row = t; row < 16 * tiles; row += 256) {
+    const int h = row / NG, gam = row % NG;
+    int sum = 0;
+    if (h < g)
+      for (int c = gam * G; c < (gam + 1) * G; ++c) sum += qi[h][c];
+    aux[1 + row] = 2.0f * (float)sum;
+  }
+  uint32_t* qb = p.qb + (int64_t)bk * tiles * 3 * 2 * 64 * 4;
+  for (int w = t; w < tiles * 3 * 2 * 64 * 4; w += 256) {
+    const int reg = w & 3, lane = (w >> 2) & 63, ks = (w >> 8) & 1, rest = w >> 9;
+    const int digit = rest % 3, ct = rest / 3;
+    const int ln = lane & 15, qd = lane >> 4;
+    const int col = 16 * ct + ln, h = col / NG, gam = col % NG;
+    uint32_t word = 0;
+    for (int byte = 0; byte < 4; ++byte) {
+      const int ch = 32 * qd + 16 * ks + 4 * byte + reg;
+      int dv = 0;
+      if (h < g && ch / G == gam) {
+        const int q = 2 * qi[h][ch];
+        const int d2 = ((q + 128) & 255) - 128;
+        const int q1 = (q - d2) >> 8;
+        const int d1 = ((q1 + 128) & 255) - 128;
+        const int d0 = (q1 - d1) >> 8;
+        dv = digit == 0 ? d0 : (digit == 1 ? d1 : d2);
+      }
+      word |= (uint32_t)(dv & 0xff) << (8 * byte);
+    }
+    qb[w] = word;
+  }
+}
+
+// the scale exponent sq that brings the largest |q~| (mx) to [2^20, 2^21),
+// so that |2Q| <= 2^22 fits three balanced int8 digits
+__device__ __forceinline__ int q_scale_exponent(float mx) {
+  int sq = 0;
+  if (mx > 0.f && mx < __builtin_huge_valf()) {
+    int e;
+    frexpf(mx, &e);          // mx in [2^(e-1), 2^e)
+    sq = min(21 - e, 100);   // keeps the logit factor 2^-sq / 2 a normal float
+  }
+  return sq;
+}
+
 // ---------------------------------------------------------------------------
 // prologue: q R_K operands
 // ---------------------------------------------------------------------------
@@ -314,7 +381,7 @@ __global__ __launch_bounds__(256) void decode_prologue(DecodeParams p) {
     stage_matrix256<kHeadDim>(p.r_k + (int64_t)kv * kHeadDim * kHeadDim, rk);
   }
   for (int e = t; e < g * kHeadDim; e += 256)
-    qs[e >> 7][e & (kHeadDim - 1)] = bf16_val(p.q[((int64_t)b * p.n_q + kv * g) * kHeadDim + e]);
+    qs[e >> 7][e & (kHeadDim - 1)] = bf16_val(p.q[q_row(p, b, kv, e >> 7) + (e & (kHeadDim - 1))]);
   __syncthreads();
   // q~[h][j]: this thread sums inputs i in [64 hf, 64 hf + 64) for every head
   // (q read four inputs at a time); the halves exchange partial sums through
@@ -355,49 +422,75 @@ __global__ __launch_bounds__(256) void decode_prologue(DecodeParams p) {
   if ((t & 63) == 0) red[t >> 6] = mx;
   __syncthreads();
   mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  // 2^sq brings the largest |q~| to [2^20, 2^21), so |2Q| <= 2^22 fits three
-  // balanced int8 digits
-  int sq = 0;
-  if (mx > 0.f && mx < __builtin_huge_valf()) {
-    int e;
-    frexpf(mx, &e);  // mx in [2^(e-1), 2^e)
-    sq = min(21 - e, 100);  // keeps the logit factor 2^-sq / 2 a normal float
-  }
+  const int sq = q_scale_exponent(mx);
 #pragma unroll
   for (int k = 0; k < 8; ++k)
     if (hf + 2 * k < g) qi[hf + 2 * k][j] = (int)rintf(ldexpf(qt[k], sq));
   __syncthreads();
-  float* aux = p.qaux + (int64_t)bk * (1 + 16 * CT);
-  if (t == 0) aux[0] = ldexpf(0.5f, -sq);
-  if (t < 16 * CT) {
-    const int h = t / NG, gam = t % NG;
-    int sum = 0;
-    if (h < g)
-      for (int c = gam * G; c < (gam + 1) * G; ++c) sum += qi[h][c];
-    aux[1 + t] = 2.0f * (float)sum;
-  }
-  uint32_t* qb = p.qb + (int64_t)bk * CT * 3 * 2 * 64 * 4;
-  for (int w = t; w < CT * 3 * 2 * 64 * 4; w += 256) {
-    const int reg = w & 3, lane = (w >> 2) & 63, ks = (w >> 8) & 1, rest = w >> 9;
-    const int digit = rest % 3, ct = rest / 3;
-    const int ln = lane & 15, qd = lane >> 4;
-    const int col = 16 * ct + ln, h = col / NG, gam = col % NG;
-    uint32_t word = 0;
-    for (int byte = 0; byte < 4; ++byte) {
-      const int ch = 32 * qd + 16 * ks + 4 * byte + reg;
-      int dv = 0;
-      if (h < g && ch / G == gam) {
-        const int q = 2 * qi[h][ch];
-        const int d2 = ((q + 128) & 255) - 128;
-        const int q1 = (q - d2) >> 8;
-        const int d1 = ((q1 + 128) & 255) - 128;
-        const int d0 = (q1 - d1) >> 8;
-        dv = digit == 0 ? d0 : (digit == 1 ? d1 : d2);
+  write_q_operands<NG>(p, bk, CT, g, qi, sq);
+}
+
+// Prologue of a chunked-prefill launch: the same operands for up to 64 kernel
+// heads (queries of the chunk x model heads of the KV head; the host keeps
+// p.g <= 64), the heads taken 16 at a time; one scale exponent for all.
+template <int NG>
+__global__ __launch_bounds__(256) void prefill_prologue(DecodeParams p) {
+  const int bk = blockIdx.x;
+  const int b = bk / p.n_kv, kv = bk % p.n_kv;
+  const int t = threadIdx.x, j = t & (kHeadDim - 1), hf = t >> 7;
+  __shared__ float rk[kHeadDim * kHeadDim];
+  __shared__ float qs[16][kHeadDim];
+  __shared__ float qt[64][kHeadDim];
+  __shared__ int qi[64][kHeadDim];
+  __shared__ float red[4];
+  const int g = p.g;
+  stage_matrix256<kHeadDim>(p.r_k + (int64_t)kv * kHeadDim * kHeadDim, rk);
+  float mx = 0.f;
+  for (int h0 = 0; h0 < g; h0 += 16) {
+    const int gb = min(16, g - h0);
+    __syncthreads();  // R_K staged; the previous block's exchange is read
+    for (int e = t; e < gb * kHeadDim; e += 256)
+      qs[e >> 7][e & (kHeadDim - 1)] = bf16_val(p.q[q_row(p, b, kv, h0 + (e >> 7)) + (e & (kHeadDim - 1))]);
+    __syncthreads();
+    float acc[16];
+#pragma unroll
+    for (int h = 0; h < 16; ++h) acc[h] = 0.f;
+    for (int i = 64 * hf; i < 64 * hf + 64; i += 4) {
+      const float r0 = rk[i * kHeadDim + j], r1 = rk[(i + 1) * kHeadDim + j];
+      const float r2 = rk[(i + 2) * kHeadDim + j], r3 = rk[(i + 3) * kHeadDim + j];
+#pragma unroll
+      for (int h = 0; h < 16; ++h) {
+        if (h < gb) {
+          const float4 q4 = *(const float4*)&qs[h][i];
+          acc[h] = fmaf(q4.w, r3, fmaf(q4.z, r2, fmaf(q4.y, r1, fmaf(q4.x, r0, acc[h]))));
+        }
       }
-      word |= (uint32_t)(dv & 0xff) << (8 * byte);
     }
-    qb[w] = word;
+    __syncthreads();  // qs becomes the exchange of the halves' partial sums
+#pragma unroll
+    for (int h = 0; h < 16; ++h)
+      if (h < gb && (h & 1) != hf) qs[h][j] = acc[h];
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int h = hf + 2 * k;
+      if (h < gb) {
+        const float own = hf ? acc[2 * k + 1] : acc[2 * k];  // hf is uniform per wavefront
+        const float v = (own + qs[h][j]) * kLog2eOverSqrtD;
+        qt[h0 + h][j] = v;
+        mx = fmaxf(mx, fabsf(v));
+      }
+    }
   }
+  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  if ((t & 63) == 0) red[t >> 6] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const int sq = q_scale_exponent(mx);
+  for (int e = t; e < g * kHeadDim; e += 256)
+    qi[e >> 7][e & (kHeadDim - 1)] = (int)rintf(ldexpf(qt[e >> 7][e & (kHeadDim - 1)], sq));
+  __syncthreads();
+  write_q_operands<NG>(p, bk, p.ct, g, qi, sq);
 }
 
 // ---------------------------------------------------------------------------
@@ -1012,11 +1105,20 @@ __device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float
 __device__ __forceinline__ bool bf16_slot_valid(int L, int n_sink, int ring0, int n_rec) {
   return L < n_sink || (L >= ring0 && L < ring0 + n_rec);
 }
+// position held by a valid bf16 logical slot of a request of T positions: a
+// sink slot holds its own position, ring slot r the newest position p < T
+// with p - sink = r modulo the window
+__device__ __forceinline__ int bf16_slot_position(int L, int ring0, int T, int sink, int window) {
+  if (L < ring0) return L;
+  const int r = L - ring0;
+  return T - 1 - (T - 1 - sink - r) % window;
+}
 
+// EDGE: masked pair; its slots must be valid and hold positions <= qpos
 template <bool EDGE>
 __device__ __forceinline__ void bf16_pair(const DecodeParams& p, const uint8_t* blk0, const uint8_t* blk1, int lp0,
-                                          int p_end, int n_sink, int ring0, int n_rec, const u32x4 (&bq)[4],
-                                          float& m_run, float& l_run, f32x4 (&acc)[8]) {
+                                          int p_end, int n_sink, int ring0, int n_rec, int T, int qpos,
+                                          const u32x4 (&bq)[4], float& m_run, float& l_run, f32x4 (&acc)[8]) {
   const int lane = threadIdx.x & 63, ln = lane & 15, qd = lane >> 4;
   const int a = qd & 1;
   const uint8_t* bk = (ln >> 3) ? blk1 : blk0;
@@ -1048,7 +1150,8 @@ __device__ __forceinline__ void bf16_pair(const DecodeParams& p, const uint8_t* 
     for (int r = 0; r < 4; ++r) {
       if constexpr (EDGE) {
         const int L = lp * kPage + 8 * a + 4 * t + r;
-        valid[t][r] = lp < p_end && bf16_slot_valid(L, n_sink, ring0, n_rec);
+        valid[t][r] = lp < p_end && bf16_slot_valid(L, n_sink, ring0, n_rec) &&
+                      bf16_slot_position(L, ring0, T, p.sink, p.recent) <= qpos;
       } else {
         valid[t][r] = true;
       }
@@ -1099,9 +1202,13 @@ __device__ __forceinline__ void bf16_pair(const DecodeParams& p, const uint8_t* 
   }
 }
 
-__device__ void bf16_item(const DecodeParams& p, int b, int kv, int split) {
+// The bf16 region of one (request, KV head) for query c of the launch (its
+// g_real model heads, rows ln < g_real), split `split` of the partials.
+__device__ void bf16_item(const DecodeParams& p, int b, int kv, int split, int c) {
   const int lane = threadIdx.x & 63, ln = lane & 15, qd = lane >> 4;
   const int T = p.ctx_lens[b];
+  const int h0 = c * p.g_real;  // first kernel head of this query
+  const int qpos = q_pos(p, b, h0);
   const int n_sink = min(p.sink, T);
   const int ring0 = kPage * ((p.sink + kPage - 1) / kPage);
   const int n_rec = T > p.sink ? min(p.recent, T - p.sink) : 0;
@@ -1117,8 +1224,8 @@ __device__ void bf16_item(const DecodeParams& p, int b, int kv, int split) {
   const int p_end = min(min(n_logical, p_begin + pps), p.max_bf16_pages);
   if (p_begin < p_end) {
     u32x4 bq[4];
-    const bool hv = ln < p.g;
-    const uint16_t* qrow = p.q + ((int64_t)b * p.n_q + kv * p.g + (hv ? ln : 0)) * kHeadDim;
+    const bool hv = ln < p.g_real;
+    const uint16_t* qrow = p.q + q_row(p, b, kv, h0 + (hv ? ln : 0));
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const u32x4 v = *(const u32x4*)(qrow + 32 * qd + 8 * s);
@@ -1137,13 +1244,14 @@ __device__ void bf16_item(const DecodeParams& p, int b, int kv, int split) {
       const uint8_t* blk0 = block_ptr(p.bf16_pages, pg0, p.n_kv, kv, kBf16BlockBytes);
       const uint8_t* blk1 = block_ptr(p.bf16_pages, pg1, p.n_kv, kv, kBf16BlockBytes);
       const int L0 = lp0 * kPage, L1 = (lp0 + 2) * kPage;
+      // a chunk's queries mask the newer positions: every prefill pair is masked
       const bool interior =
-          has1 && ok0 && ok1 && ((L1 <= n_sink) || (L0 >= ring0 && L1 <= ring0 + n_rec));
+          p.chunk == 1 && has1 && ok0 && ok1 && ((L1 <= n_sink) || (L0 >= ring0 && L1 <= ring0 + n_rec));
       if (interior) {
-        bf16_pair<false>(p, blk0, blk1, lp0, p_end, n_sink, ring0, n_rec, bq, m_run, l_run, acc);
+        bf16_pair<false>(p, blk0, blk1, lp0, p_end, n_sink, ring0, n_rec, T, qpos, bq, m_run, l_run, acc);
       } else {
         const int pe = ok0 ? (ok1 ? p_end : lp0 + 1) : lp0;
-        bf16_pair<true>(p, blk0, blk1, lp0, pe, n_sink, ring0, n_rec, bq, m_run, l_run, acc);
+        bf16_pair<true>(p, blk0, blk1, lp0, pe, n_sink, ring0, n_rec, T, qpos, bq, m_run, l_run, acc);
       }
     }
   }
@@ -1152,14 +1260,14 @@ __device__ void bf16_item(const DecodeParams& p, int b, int kv, int split) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int h = 4 * qd + r;
-    if (h < p.g) {
-      float* dst = p.partial + (((int64_t)b * p.n_q + kv * p.g + h) * S + split) * kPartialStride;
+    if (h < p.g_real) {
+      float* dst = p.partial + (((int64_t)b * p.n_q + kv * p.g + h0 + h) * S + split) * kPartialStride;
 #pragma unroll
       for (int kt = 0; kt < 8; ++kt) dst[2 + 8 * ln + kt] = acc[kt][r];
     }
   }
-  if (qd == 0 && ln < p.g) {
-    float* dst = p.partial + (((int64_t)b * p.n_q + kv * p.g + ln) * S + split) * kPartialStride;
+  if (qd == 0 && ln < p.g_real) {
+    float* dst = p.partial + (((int64_t)b * p.n_q + kv * p.g + h0 + ln) * S + split) * kPartialStride;
     dst[0] = m_run;
     dst[1] = l;
   }
@@ -1181,11 +1289,14 @@ decode_int2(DecodeParams p) {
   int2_item<NG, MB, CT, W>(p, bk / p.n_kv, bk % p.n_kv, split, p_lds[W > 1 ? threadIdx.x >> 6 : 0], stage);
 }
 
+// items: (request, KV head, query of the launch, bf16 split)
 __global__ __launch_bounds__(64) void decode_bf16(DecodeParams p) {
   const int item = blockIdx.x;
+  const int n_c = p.g / p.g_real;
   const int sb = item % p.splits_bf16;
-  const int bk = item / p.splits_bf16;
-  bf16_item(p, bk / p.n_kv, bk % p.n_kv, p.splits_int2 + sb);
+  const int c = (item / p.splits_bf16) % n_c;
+  const int bk = item / p.splits_bf16 / n_c;
+  bf16_item(p, bk / p.n_kv, bk % p.n_kv, p.splits_int2 + sb, c);
 }
 
 // ---------------------------------------------------------------------------
@@ -1250,7 +1361,7 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeParams p) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int S = p.splits_int2 + p.splits_bf16, SI = p.splits_int2;
   if (SI > 0) stage_matrix256<kRvStride>(p.r_v + (int64_t)kv * kHeadDim * kHeadDim, rv);
-  if (p.bf16_in_combine && w < p.splits_bf16) bf16_item(p, b, kv, SI + w);
+  if (p.bf16_in_combine && w < p.splits_bf16) bf16_item(p, b, kv, SI + w, 0);
   __syncthreads();  // R_V staged; the bf16 partials written by this block are visible to it
   for (int h0 = 0; h0 < p.g; h0 += 4) {  // same trip count in every wavefront
     const int h = h0 + w;
@@ -1329,7 +1440,7 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeParams p) {
           r1 = fmaf(a.w, row1[k + 3], r1);
         }
       }
-      float* o = p.out + ((int64_t)b * p.n_q + hq) * kHeadDim;
+      float* o = p.out + q_row(p, b, kv, h);
       const bool empty = M == kNegInf;
       o[lane] = empty ? 0.f : (r0 + ab0) / L;
       o[lane + 64] = empty ? 0.f : (r1 + ab1) / L;
@@ -1362,12 +1473,44 @@ hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream, hipEvent_t
   }
   if (p.splits_bf16 > 0 && !p.bf16_in_combine) {
     if (!int2 && (e = mark(ev_start)) != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_bf16, dim3(bkn * p.splits_bf16), dim3(64), 0, stream, p);
+    hipLaunchKernelGGL(decode_bf16, dim3(bkn * (p.g / p.g_real) * p.splits_bf16), dim3(64), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (!int2 && (e = mark(ev_stop)) != hipSuccess) return e;
   }
   hipLaunchKernelGGL(decode_combine, dim3(bkn), dim3(256), 0, stream, p);
   return hipGetLastError();
+}
+
+// One query block of a chunked prefill: W = p.ct tiles, one wavefront each.
+template <int NG, int MB, int W>
+hipError_t launch_prefill_t(const DecodeParams& p, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
+  const int bkn = p.batch * p.n_kv;
+  auto mark = [&](hipEvent_t ev) { return ev ? hipEventRecord(ev, stream) : hipSuccess; };
+  hipError_t e = hipSuccess;
+  hipLaunchKernelGGL((prefill_prologue<NG>), dim3(bkn), dim3(256), 0, stream, p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = mark(ev_start)) != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_int2<NG, MB, 1, W>), dim3(bkn * p.splits_int2), dim3(64 * W), 0, stream, p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = mark(ev_stop)) != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_bf16, dim3(bkn * (p.g / p.g_real) * p.splits_bf16), dim3(64), 0, stream, p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_combine, dim3(bkn), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int MB>
+hipError_t launch_prefill_mb(const DecodeParams& p, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
+  if (p.ng == 4) {
+    if (p.ct == 4) return launch_prefill_t<4, MB, 4>(p, stream, ev_start, ev_stop);
+    if (p.ct == 8) return launch_prefill_t<4, MB, 8>(p, stream, ev_start, ev_stop);
+    if (p.ct == 16) return launch_prefill_t<4, MB, 16>(p, stream, ev_start, ev_stop);
+  } else if (p.ng == 2) {
+    if (p.ct == 4) return launch_prefill_t<2, MB, 4>(p, stream, ev_start, ev_stop);
+    if (p.ct == 8) return launch_prefill_t<2, MB, 8>(p, stream, ev_start, ev_stop);
+    if (p.ct == 16) return launch_prefill_t<2, MB, 16>(p, stream, ev_start, ev_stop);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <int MB>
@@ -1393,6 +1536,12 @@ hipError_t launch_decode_mb(const DecodeParams& p, hipStream_t stream, hipEvent_
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
   if (p.mb == 4) return launch_decode_mb<4>(p, stream, ev_start, ev_stop);
   if (p.mb == 2) return launch_decode_mb<2>(p, stream, ev_start, ev_stop);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill(const DecodeParams& p, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
+  if (p.mb == 4) return launch_prefill_mb<4>(p, stream, ev_start, ev_stop);
+  if (p.mb == 2) return launch_prefill_mb<2>(p, stream, ev_start, ev_stop);
   return hipErrorInvalidValue;
 }
 

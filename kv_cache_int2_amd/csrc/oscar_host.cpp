@@ -845,6 +845,10 @@ static oscar_status decode_common(const oscar_shape* shape, const oscar_layer* l
   p.ng = baseline ? 4 : ng_of(shape);
   p.ct = baseline ? 1 : ct_of(shape);
   p.mb = mb_of(shape);
+  p.q_heads = p.n_q;
+  p.g_real = p.g;
+  p.chunk = 1;
+  p.chunk0 = 0;
   if (baseline) {
     p.sink = 1 << 28;
     p.recent = 0;
@@ -907,6 +911,108 @@ oscar_status oscar_decode_attn(const oscar_shape* shape, const oscar_layer* laye
                                size_t workspace_bytes, void* stream) {
   return decode_common(shape, layer, cache, q, batch, int2_bt, max_int2_pages, bf16_bt, max_bf16_pages, ctx_lens,
                        splits_int2, splits_bf16, out, workspace, workspace_bytes, stream, false);
+}
+
+// Chunked prefill: queries per launch so that the kernel heads (queries x
+// model heads, at most 64: the prologue's capacity) fill at most 16 tiles of
+// 16 (head, group) rows; tiles per launch rounded up to 4, 8 or 16 wavefronts.
+static int prefill_block(const oscar_shape* shape) {
+  const int g = shape->n_q_heads / shape->n_kv_heads;
+  return std::max(1, std::min(256 / (g * ng_of(shape)), 64 / g));
+}
+static int prefill_tiles(const oscar_shape* shape, int queries) {
+  const int g = shape->n_q_heads / shape->n_kv_heads;
+  const int tiles = (queries * g * ng_of(shape) + 15) / 16;
+  return tiles <= 4 ? 4 : (tiles <= 8 ? 8 : 16);
+}
+static int32_t prefill_auto_splits(const oscar_shape* shape, int32_t batch, int32_t max_int2_pages, int tiles) {
+  // two whole rounds of items of `tiles` wavefronts (4 per SIMD), as in decode
+  const int64_t pairs = (int64_t)batch * shape->n_kv_heads;
+  const int64_t cap = (int64_t)device_cus() * 4 * 4 / tiles;
+  const int64_t smax = std::max<int64_t>(1, std::min<int64_t>(kAutoMaxSplits, max_int2_pages / 32));
+  return (int32_t)std::max<int64_t>(1, std::min<int64_t>(2 * cap / pairs, smax));
+}
+
+size_t oscar_prefill_workspace_bytes(const oscar_shape* shape, int32_t batch, int32_t chunk, int32_t splits_int2,
+                                     int32_t splits_bf16) {
+  if (check_shape(shape) != OSCAR_OK || batch < 0 || chunk < 1 || splits_int2 < 0 || splits_bf16 < 0) return 0;
+  const int qn = std::min<int>(chunk, prefill_block(shape));
+  const int g = shape->n_q_heads / shape->n_kv_heads;
+  const int si = splits_int2 == 0 ? kAutoMaxSplits : splits_int2;
+  const int sb = splits_bf16 == 0 ? 1 : splits_bf16;
+  return decode_workspace_bytes(batch, shape->n_kv_heads * qn * g, shape->n_kv_heads, prefill_tiles(shape, qn),
+                                si + sb);
+}
+
+oscar_status oscar_prefill_attn(const oscar_shape* shape, const oscar_layer* layer, const oscar_cache* cache,
+                                const void* q, int32_t batch, int32_t chunk, const int32_t* int2_bt,
+                                int32_t max_int2_pages, const int32_t* bf16_bt, int32_t max_bf16_pages,
+                                const int32_t* ctx_lens, int32_t splits_int2, int32_t splits_bf16, float* out,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  oscar_status st = check_shape(shape);
+  if (st) return st;
+  if (batch < 0 || chunk < 1) return fail(OSCAR_EINVAL, "batch < 0 or chunk < 1");
+  if (batch == 0) return ok();
+  if (chunk > shape->recent)
+    return fail(OSCAR_EUNSUPPORTED, "chunk %d longer than the recent window %d", chunk, shape->recent);
+  if (!q || !ctx_lens || !out || !workspace) return fail(OSCAR_EINVAL, "NULL argument");
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(workspace, 256))
+    return fail(OSCAR_EINVAL, "q/out must be 16-byte and workspace 256-byte aligned");
+  if ((st = check_layer(layer)) || (st = check_cache(cache, true, true))) return st;
+  if (!int2_bt || max_int2_pages < 1 || !bf16_bt || max_bf16_pages < 1)
+    return fail(OSCAR_EINVAL, "block tables missing");
+  if (splits_int2 < 0 || splits_bf16 < 0 || splits_int2 > 4096 || splits_bf16 > 4096)
+    return fail(OSCAR_EINVAL, "splits out of range");
+  const size_t need = oscar_prefill_workspace_bytes(shape, batch, chunk, splits_int2, splits_bf16);
+  if (workspace_bytes < need) return fail(OSCAR_EINVAL, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  const int g = shape->n_q_heads / shape->n_kv_heads;
+  const int block = prefill_block(shape);
+  for (int c0 = 0; c0 < chunk; c0 += block) {
+    const int qn = std::min(block, chunk - c0);
+    DecodeParams p{};
+    p.int2_pages = (const uint8_t*)cache->int2_pages;
+    p.n_int2_pages = cache->n_int2_pages;
+    p.bf16_pages = (const uint8_t*)cache->bf16_pages;
+    p.n_bf16_pages = cache->n_bf16_pages;
+    p.q = (const uint16_t*)q;
+    p.r_k = layer->r_k;
+    p.r_v = layer->r_v;
+    p.int2_bt = int2_bt;
+    p.max_int2_pages = max_int2_pages;
+    p.bf16_bt = bf16_bt;
+    p.max_bf16_pages = max_bf16_pages;
+    p.ctx_lens = ctx_lens;
+    p.batch = batch;
+    p.n_kv = shape->n_kv_heads;
+    p.g_real = g;
+    p.q_heads = shape->n_q_heads;
+    p.chunk = chunk;
+    p.chunk0 = c0;
+    p.g = qn * g;
+    p.n_q = p.n_kv * p.g;
+    p.ng = ng_of(shape);
+    p.ct = prefill_tiles(shape, qn);
+    p.mb = mb_of(shape);
+    p.sink = shape->sink;
+    p.recent = shape->recent;
+    p.splits_int2 = splits_int2 ? splits_int2 : prefill_auto_splits(shape, batch, max_int2_pages, p.ct);
+    p.splits_bf16 = splits_bf16 ? splits_bf16 : 1;
+    p.bf16_in_combine = 0;
+    const double smax = 2.0 * (double)layer->tau_v / 3.0;
+    p.p_scale_exp = 0.f;
+    if (std::isfinite(smax) && smax > 0)
+      p.p_scale_exp = (float)std::clamp((int)std::floor(std::log2(32768.0 / smax)) - 1, -60, 60);
+    decode_workspace_carve(p, workspace);
+    p.out = out;
+    hipEvent_t ev0 = nullptr, ev1 = nullptr;
+    if (g_prof.on) {
+      if (hipEventCreate(&ev0) != hipSuccess || hipEventCreate(&ev1) != hipSuccess)
+        return fail(OSCAR_EHIP, "hipEventCreate failed");
+      g_prof.events.emplace_back(ev0, ev1);
+    }
+    if ((st = hip_status(launch_prefill(p, (hipStream_t)stream, ev0, ev1), "prefill launch"))) return st;
+  }
+  return ok();
 }
 
 oscar_status oscar_profile_enable(int32_t on) {

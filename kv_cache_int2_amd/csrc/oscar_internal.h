@@ -54,7 +54,15 @@ struct DecodeParams {
   const int32_t* bf16_bt;
   int max_bf16_pages;
   const int32_t* ctx_lens;
+  // Query heads as the kernels see them: g per KV head, n_q = n_kv g.  In
+  // decode these are the model's heads.  In chunked prefill they are virtual:
+  // head hv of KV head kv is query chunk0 + hv / g_real of the chunk, model
+  // head kv g_real + hv % g_real (q_row, q_pos).
   int batch, n_q, n_kv, g, ng, ct;
+  int q_heads;                // query heads of one token in q and out (Hq)
+  int g_real;                 // model query heads per KV head
+  int chunk;                  // queries per request in q and out (1 in decode)
+  int chunk0;                 // first of them handled by this launch
   int mb;                     // bytes of a (scale, zero) pair in the INT2 blocks: 4 or 2
   int sink, recent;           // region rule (baseline: sink huge, recent 0)
   int splits_int2, splits_bf16;
@@ -98,6 +106,8 @@ hipError_t launch_copy_pages(uint8_t* base, int64_t block_bytes_all_heads, int64
                              const int32_t* dst, int64_t n, hipStream_t stream);
 // ev_start / ev_stop (may be null): recorded on `stream` around the main kernel.
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop);
+// One query block of a chunked prefill (p.ct = 4, 8 or 16 tiles, one wavefront each).
+hipError_t launch_prefill(const DecodeParams& p, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop);
 
 // Workspace bytes for the decode path (each region 256-byte aligned).
 size_t decode_workspace_bytes(int batch, int n_q, int n_kv, int ct, int splits_total);

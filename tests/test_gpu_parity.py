@@ -498,3 +498,43 @@ def test_f1_rotation_ablation_through_the_kernels(rotation):
         on += float((ex ** 2).sum())
     _flush(f"f1 rotation={rotation}: output error vs unquantised cache rel_l2={math.sqrt(oe / on):.4f} "
            f"tau_k={float(cal.tau_k):.3f} tau_v={float(cal.tau_v):.3f}")
+
+
+@pytest.mark.parametrize("hq,hkv,group,scale_bits,t0,chunk", [
+    (32, 8, 32, 16, 3000, 16), (4, 1, 32, 16, 700, 37), (8, 2, 64, 8, 5000, 128),
+    (1, 1, 32, 16, 300, 100), (16, 1, 32, 16, 2000, 20), (12, 1, 64, 16, 1500, 7)])
+def test_f2_prefill_attention(hq, hkv, group, scale_bits, t0, chunk):
+    """Chunked prefill over the mixed cache: a chunk of new tokens is written
+    (their entry into the recent window pushes older tokens into INT2), then
+    its queries attend causally; every query head of every chunk query against
+    the oracle.  Requests of different lengths, one made of the chunk alone,
+    several query blocks per launch (g = 4, G = 32: 16 queries a block)."""
+    from kv_cache_int2_amd.torch_cache import to_dev_bits, to_dev_i32
+    w = synth.Workload("prefill", 120 + hq + chunk, hq, hkv, 128, 1, 0, group=group, sink=4, recent=128,
+                       outlier_scale=(20.0, 20.0), calib_tokens=512)
+    _flush(f"case f2 prefill hq={hq} hkv={hkv} G={group} scale_bits={scale_bits} t0={t0} chunk={chunk}")
+    cal = _calibrate(w)
+    sh = K.make_shape(n_q_heads=hq, n_kv_heads=hkv, group=group, sink=4, recent=128, scale_bits=scale_bits)
+    dc = DeviceCache(sh, cal.r_k, cal.r_v, cal.tau_k, cal.tau_v, 1200, 64)
+    starts = [t0, t0 // 3 + 11, 0]
+    seqs = []
+    for r, s0 in enumerate(starts):
+        kb, vb = synth.kv_request_bf16(w, r, 0, s0 + chunk)
+        seq = dc.new_seq()
+        if s0:
+            dc.append(seq, kb[:s0], vb[:s0])
+        dc.append(seq, kb[s0:], vb[s0:])           # the chunk's own tokens
+        seqs.append(seq)
+    i2, bf, ctx = dc.tables(seqs)
+    q = np.stack([np.stack([synth.q_decode_bf16(w, r, c) for c in range(chunk)]) for r in range(len(starts))])
+    B = len(starts)
+    ws = torch.empty(K.oscar_prefill_workspace_bytes(sh, B, chunk), dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, chunk, hq, 128), dtype=torch.float32, device="cuda")
+    K.oscar_prefill_attn(sh, dc.layer, dc.cache, to_dev_bits(q), to_dev_i32(i2), to_dev_i32(bf), to_dev_i32(ctx),
+                         out, ws)
+    got = out.cpu().numpy()
+    for r, s0 in enumerate(starts):
+        kb, vb = synth.kv_request_bf16(w, r, 0, s0 + chunk)
+        st = O.store_request(kb, vb, cal, group, 4, 128, scale_bits)
+        ref = O.prefill_attention(q[r], st, cal, group)
+        _check_close(got[r], ref, f"f2 prefill request {r} T={s0 + chunk} chunk={chunk}")
