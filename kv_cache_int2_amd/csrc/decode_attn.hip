@@ -82,10 +82,6 @@ __device__ __forceinline__ float half_lo(uint32_t w) {
 __device__ __forceinline__ float half_hi(uint32_t w) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
 }
-__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
-         ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
-}
 // fp32 -> bf16 bits, nearest-even (finite inputs)
 __device__ __forceinline__ uint32_t bf16_bits(float x) {
   uint32_t u = __builtin_bit_cast(uint32_t, x);
@@ -364,7 +360,6 @@ __global__ __launch_bounds__(256) void decode_prologue(DecodeParams p) {
   const int bk = blockIdx.x;
   const int b = bk / p.n_kv, kv = bk % p.n_kv;
   const int t = threadIdx.x, j = t & (kHeadDim - 1), hf = t >> 7;
-  constexpr int G = kHeadDim / NG;
   __shared__ float rk[kHeadDim * kHeadDim];
   __shared__ float qs[16][kHeadDim];
   __shared__ int qi[16][kHeadDim];
