@@ -263,9 +263,10 @@ oscar_status oscar_decode_attn_bf16_baseline(const oscar_shape* shape, const osc
  * each in the form the cache holds it (INT2 history through the rotations as in
  * decode, bf16 sink and recent values).  Inputs (device): q bf16
  * [batch][C][n_q_heads][d]; block tables and ctx_lens as for oscar_decode_attn.
- * Output (device): out fp32 [batch][C][n_q_heads][d].  Requires 1 <= C <=
- * recent (the chunk lies in the bf16 window, so the INT2 history precedes every
- * query): OSCAR_EUNSUPPORTED otherwise.  The queries run in blocks (16 at
+ * Output (device): out fp32 [batch][C][n_q_heads][d].  C >= 1 and
+ * ctx_lens[b] >= C.  A chunk longer than the recent window has its older
+ * positions in INT2 like any history: its queries read them in that form,
+ * each query only up to its own position.  The queries run in blocks (16 at
  * g = 4, G = 32), each block one pass over the history with one wavefront per
  * 16 (query head, group) rows.  splits as in decode (0 = choose; bf16 splits
  * default 1).  workspace: >= oscar_prefill_workspace_bytes with the same

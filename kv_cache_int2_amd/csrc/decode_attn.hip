@@ -722,22 +722,34 @@ struct Int2Staged {
   }
 };
 
+// EDGE: a masked pair.  Its tokens must lie in [lo, hi) on pages below
+// p_end, and row head h (16 t0 ... of the wavefront's tiles) sees positions up
+// to qlo + floor(h / g_real), i.e. position qlo + k when k g_real <= h (causal
+// masks of a chunk's queries; in decode every row sees the whole INT2 region).
 template <int NG, int CT, bool EDGE, class Src>
-__device__ __forceinline__ void int2_pair(const Src& src, int lp0, int p_end, int lo, int hi,
-                                          const Int2Const<NG, CT>& K, Int2State<NG, CT>& S, float* p_lds) {
+__device__ __forceinline__ void int2_pair(const Src& src, int lp0, int p_end, int lo, int hi, int qlo, int g_real,
+                                          int t0, const Int2Const<NG, CT>& K, Int2State<NG, CT>& S, float* p_lds) {
   constexpr int HPL = 4 / NG;
   const int lane = threadIdx.x & 63, ln = lane & 15, qd = lane >> 4;
   // ---- logits ----
   const Int2KData<NG> DK = src.k();
-  bool valid[2];
+  bool seen[2][CT][HPL];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    if constexpr (EDGE) {
-      const int pos = (lp0 + t) * kPage + ln;
-      valid[t] = lp0 + t < p_end && pos >= lo && pos < hi;
-    } else {
-      valid[t] = true;
-    }
+    const int pos = (lp0 + t) * kPage + ln;
+    const bool valid = !EDGE || (lp0 + t < p_end && pos >= lo && pos < hi);
+    const int later = __mul24(pos - qlo, g_real);  // |pos - qlo| < 2^17
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int hh = 0; hh < HPL; ++hh) {
+        if constexpr (EDGE) {
+          const int h = (16 / NG) * (t0 + ct) + (4 / NG) * qd + hh;
+          seen[t][ct][hh] = valid && later <= h;
+        } else {
+          seen[t][ct][hh] = true;
+        }
+      }
   }
   float lg[2][CT][HPL];
 #pragma unroll
@@ -769,7 +781,7 @@ __device__ __forceinline__ void int2_pair(const Src& src, int lp0, int p_end, in
           const float sv = half_lo(DK.ksz[t][gg]), zv = half_hi(DK.ksz[t][gg]);
           x = fmaf(sv, (float)c2, fmaf(zv, K.qbar2[ct][r], x));
         }
-        lg[t][ct][hh] = valid[t] ? x : kNegInf;
+        lg[t][ct][hh] = seen[t][ct][hh] ? x : kNegInf;
       }
     }
   }
@@ -818,7 +830,7 @@ __device__ __forceinline__ void int2_pair(const Src& src, int lp0, int p_end, in
 #pragma unroll
       for (int hh = 0; hh < HPL; ++hh) {
         const float e = fast_exp2(fmaf(lg[t][ct][hh], K.kfac, S.moff[ct][hh]));  // p pfac
-        pr[t][ct][hh] = valid[t] ? e : 0.f;
+        pr[t][ct][hh] = seen[t][ct][hh] ? e : 0.f;
         S.l_run[ct][hh] += pr[t][ct][hh];
       }
   }
@@ -844,10 +856,10 @@ __device__ __forceinline__ void int2_pair(const Src& src, int lp0, int p_end, in
       float s0 = half_lo(DV.vsz[0][r]), z0 = half_hi(DV.vsz[0][r]);
       float s1 = half_lo(DV.vsz[1][r]), z1 = half_hi(DV.vsz[1][r]);
       if constexpr (EDGE) {
-        // unwritten slots may hold anything: zero their scale and zero point
-        const int pos0 = lp0 * kPage + 4 * qd + r, pos1 = pos0 + kPage;
-        const bool v0 = lp0 < p_end && pos0 >= lo && pos0 < hi;
-        const bool v1 = lp0 + 1 < p_end && pos1 >= lo && pos1 < hi;
+        // a token this row gives no weight (an unwritten slot, a position its
+        // query does not see) may hold a non-finite pair, and 0 * NaN is NaN:
+        // zero its scale and zero point
+        const bool v0 = pf0[r] != 0.f, v1 = pf1[r] != 0.f;
         s0 = v0 ? s0 : 0.f;
         z0 = v0 ? z0 : 0.f;
         s1 = v1 ? s1 : 0.f;
@@ -899,10 +911,17 @@ __device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float
   constexpr int HPL = 4 / NG;
   constexpr int kTiles = W * CT;  // row tiles of the (request, KV head)
   const int lane = threadIdx.x & 63, ln = lane & 15, qd = lane >> 4;
-  const int t0 = W > 1 ? (int)(threadIdx.x >> 6) * CT : 0;  // first row tile of this wavefront
+  // first row tile of this wavefront (wavefront-uniform: kept in a scalar register)
+  const int t0 = W > 1 ? __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) * CT : 0;
   const int T = p.ctx_lens[b];
+  // the launch's queries sit at positions qlo .. qlo + (g - 1) / g_real (in
+  // decode, T - 1 alone): keys up to qlo are seen by every row, later ones
+  // (a chunk longer than the recent window) only by the rows of later queries
+  const int qlo = T - p.chunk + p.chunk0;
   const int lo = p.sink;
-  const int hi = T - p.recent;
+  const int hi = min(T - p.recent, qlo + (p.g - 1) / p.g_real + 1);
+  const int hi_all = min(hi, qlo + 1);
+  const int g_real = p.g_real;
   const int bk = b * p.n_kv + kv;
   Int2State<NG, CT> S;
 #pragma unroll
@@ -959,19 +978,19 @@ __device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float
         if (!ok1) pg1 = pg0;
         const int pe = ok0 ? (ok1 ? p_end : lp0 + 1) : lp0;
         const Int2Data<NG> D = int2_load<NG, MB>(blk(pg0), blk(pg1), off);
-        int2_pair<NG, CT, true>(D, lp0, pe, lo, hi, K, S, p_lds);
+        int2_pair<NG, CT, true>(D, lp0, pe, lo, hi, qlo, g_real, t0, K, S, p_lds);
       };
       int lp0 = p_begin;
       if (lp0 * kPage < lo) {
         edge(lp0);
         lp0 += 2;
       }
-      // interior pairs (both pages fully inside [lo, hi)), staged in LDS two
+      // interior pairs (both pages fully inside [lo, hi_all)), staged in LDS two
       // pairs ahead in a ring of three slots.  Page ids come 64 at a time, one
       // per lane, and a pair takes its two ids with v_readlane: no memory
       // access and no wait inside the pair loop.  Each chunk ends with its
       // staging loads drained.
-      const int main_end = min(p_end, hi / kPage);
+      const int main_end = min(p_end, hi_all / kPage);
       constexpr int kSlot = 2 * L.bytes();
       const uint32_t a0 = lds_address(stage);
       if constexpr (W == 1) {
@@ -1001,7 +1020,8 @@ __device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float
             } else {
               vm_wait<0>();
             }
-            int2_pair<NG, CT, false>(Int2Staged<NG, MB>{stage + cur * kSlot, off}, lp0, p_end, lo, hi, K, S, p_lds);
+            int2_pair<NG, CT, false>(Int2Staged<NG, MB>{stage + cur * kSlot, off}, lp0, p_end, lo, hi, qlo, g_real, t0,
+                                     K, S, p_lds);
             lp0 += 2;
             if (lp0 + 2 > lim) break;
             cur = cur == 2 ? 0 : cur + 1;
@@ -1041,7 +1061,8 @@ __device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float
               }
             }
             barrier_no_fence();
-            int2_pair<NG, CT, false>(Int2Staged<NG, MB>{stage + cur * kSlot, off}, lp0, p_end, lo, hi, K, S, p_lds);
+            int2_pair<NG, CT, false>(Int2Staged<NG, MB>{stage + cur * kSlot, off}, lp0, p_end, lo, hi, qlo, g_real, t0,
+                                     K, S, p_lds);
             lp0 += 2;
             if (lp0 + 2 > lim) break;
             cur = (cur + 1) & 3;
@@ -1175,6 +1196,18 @@ __device__ __forceinline__ void bf16_pair(const DecodeParams& p, const uint8_t* 
       pr[t][r] = valid[t][r] ? e : 0.f;
       l_run += pr[t][r];
     }
+  if constexpr (EDGE) {
+    // a masked slot may hold a non-finite value (an unwritten slot, a
+    // position the query does not see): zero it, since 0 * NaN is NaN.
+    // Value word w of this lane holds its tokens 8a + 2w and 8a + 2w + 1.
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t keep = (valid[w >> 1][2 * (w & 1)] ? 0x0000ffffu : 0u) |
+                            (valid[w >> 1][2 * (w & 1) + 1] ? 0xffff0000u : 0u);
+#pragma unroll
+      for (int kt = 0; kt < 8; ++kt) vv[kt][w] &= keep;
+    }
+  }
   // A register r: tokens 8a + 2r, 8a + 2r + 1 = tile r/2, rows 2(r%2), 2(r%2)+1.
   // p = hi + mid + lo in bf16 (24 significant bits): bf16 values are not
   // clipped, so a few large unrotated values can dominate the sum.

@@ -953,8 +953,6 @@ oscar_status oscar_prefill_attn(const oscar_shape* shape, const oscar_layer* lay
   if (st) return st;
   if (batch < 0 || chunk < 1) return fail(OSCAR_EINVAL, "batch < 0 or chunk < 1");
   if (batch == 0) return ok();
-  if (chunk > shape->recent)
-    return fail(OSCAR_EUNSUPPORTED, "chunk %d longer than the recent window %d", chunk, shape->recent);
   if (!q || !ctx_lens || !out || !workspace) return fail(OSCAR_EINVAL, "NULL argument");
   if (!aligned(q, 16) || !aligned(out, 16) || !aligned(workspace, 256))
     return fail(OSCAR_EINVAL, "q/out must be 16-byte and workspace 256-byte aligned");

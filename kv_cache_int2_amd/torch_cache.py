@@ -21,13 +21,17 @@ class DeviceCache:
     """One layer's paged cache on the GPU plus its host pool bookkeeping."""
 
     def __init__(self, shape: K.Shape, r_k: np.ndarray, r_v: np.ndarray, tau_k, tau_v, n_int2_pages: int,
-                 n_bf16_pages: int):
+                 n_bf16_pages: int, fill: int = 0):
+        """fill: the byte every page starts with (0xFF makes each unwritten
+        bf16 value and fp16 or FP8 scale/zero a NaN)."""
         self.shape = shape
         self.pool = K.Pool(shape, n_int2_pages, n_bf16_pages)
         ib = K.oscar_int2_block_bytes(shape)
         bb = K.oscar_bf16_block_bytes(shape)
-        self.int2 = torch.zeros(max(n_int2_pages, 1) * shape.n_kv_heads * ib, dtype=torch.uint8, device="cuda")
-        self.bf16 = torch.zeros(max(n_bf16_pages, 1) * shape.n_kv_heads * bb, dtype=torch.uint8, device="cuda")
+        self.int2 = torch.full((max(n_int2_pages, 1) * shape.n_kv_heads * ib,), fill, dtype=torch.uint8,
+                               device="cuda")
+        self.bf16 = torch.full((max(n_bf16_pages, 1) * shape.n_kv_heads * bb,), fill, dtype=torch.uint8,
+                               device="cuda")
         self.cache = K.make_cache(self.int2, n_int2_pages, self.bf16, n_bf16_pages)
         self.r_k = torch.from_numpy(np.ascontiguousarray(r_k, dtype=np.float32)).cuda()
         self.r_v = torch.from_numpy(np.ascontiguousarray(r_v, dtype=np.float32)).cuda()

@@ -190,6 +190,52 @@ def test_ragged_batch_gqa_groups(hq, hkv, group, scale_bits):
             _check_close(out[r], ref[r], f"ragged hq={hq} G={group} len={lens[r]} splits={si}/{sb}")
 
 
+@pytest.mark.parametrize("group,scale_bits", [(32, 16), (64, 8)])
+def test_unwritten_slots_may_hold_nan(group, scale_bits):
+    """Pools that start as all-0xFF bytes (every unwritten bf16 value and
+    scale/zero a NaN): the slots no position owns yet (sink page tail, recent
+    ring not yet full, the INT2 pages at the region edges) must not reach the
+    outputs, in decode and in a chunked prefill longer than the window."""
+    from kv_cache_int2_amd.torch_cache import to_dev_bits, to_dev_i32
+    w = synth.Workload("nanfill", 70 + group, 8, 1, 128, 1, 0, group=group, sink=4, recent=32,
+                       outlier_scale=(20.0, 20.0), calib_tokens=512)
+    _flush(f"case nan-filled pools G={group} scale_bits={scale_bits}")
+    cal = _calibrate(w)
+    sh = K.make_shape(n_q_heads=8, n_kv_heads=1, group=group, sink=4, recent=32, scale_bits=scale_bits)
+    dc = DeviceCache(sh, cal.r_k, cal.r_v, cal.tau_k, cal.tau_v, 400, 64, fill=0xFF)
+    lens = [1, 5, 21, 36, 37, 53, 515, 2049]
+    seqs, stores, kvs = [], [], []
+    for r, t in enumerate(lens):
+        kb, vb = synth.kv_request_bf16(w, r, 0, t)
+        seq = dc.new_seq()
+        _fill(dc, seq, kb, vb, [t] if t < 200 else [t - 7] + [1] * 7)
+        seqs.append(seq)
+        stores.append(O.store_request(kb, vb, cal, group, 4, 32, scale_bits))
+    q = np.stack([synth.q_decode_bf16(w, r) for r in range(len(lens))])
+    ref = np.stack([O.decode_attention(q[r], stores[r], cal, group) for r in range(len(lens))])
+    for si, sb in ((0, 0), (3, 3), (1, 5)):
+        out = dc.decode(seqs, q, splits_int2=si, splits_bf16=sb).cpu().numpy()
+        for r in range(len(lens)):
+            _check_close(out[r], ref[r], f"nan-filled G={group} len={lens[r]} splits={si}/{sb}")
+    # a chunk of 45 new tokens (past the 32-token window) on two of the requests
+    chunk = 45
+    pf = [seqs[4], seqs[6]]
+    qc = np.stack([np.stack([synth.q_decode_bf16(w, 50 + r, c) for c in range(chunk)]) for r in range(2)])
+    pst = []
+    for r, (seq, t) in enumerate(((seqs[4], lens[4]), (seqs[6], lens[6]))):
+        kb, vb = synth.kv_request_bf16(w, 4 if r == 0 else 6, 0, t + chunk)
+        dc.append(seq, kb[t:], vb[t:])
+        pst.append(O.store_request(kb, vb, cal, group, 4, 32, scale_bits))
+    i2, bf, ctx = dc.tables(pf)
+    ws = torch.empty(K.oscar_prefill_workspace_bytes(sh, 2, chunk), dtype=torch.uint8, device="cuda")
+    out = torch.empty((2, chunk, 8, 128), dtype=torch.float32, device="cuda")
+    K.oscar_prefill_attn(sh, dc.layer, dc.cache, to_dev_bits(qc), to_dev_i32(i2), to_dev_i32(bf), to_dev_i32(ctx),
+                         out, ws)
+    got = out.cpu().numpy()
+    for r in range(2):
+        _check_close(got[r], O.prefill_attention(qc[r], pst[r], cal, group), f"nan-filled prefill {r}")
+
+
 def test_empty_context_gives_zero_rows():
     w = synth.WORKLOADS["tiny"]
     cal = _calibrate(w)
@@ -502,13 +548,16 @@ def test_f1_rotation_ablation_through_the_kernels(rotation):
 
 @pytest.mark.parametrize("hq,hkv,group,scale_bits,t0,chunk", [
     (32, 8, 32, 16, 3000, 16), (4, 1, 32, 16, 700, 37), (8, 2, 64, 8, 5000, 128),
-    (1, 1, 32, 16, 300, 100), (16, 1, 32, 16, 2000, 20), (12, 1, 64, 16, 1500, 7)])
+    (1, 1, 32, 16, 300, 100), (16, 1, 32, 16, 2000, 20), (12, 1, 64, 16, 1500, 7),
+    (32, 8, 32, 16, 3000, 300), (8, 2, 64, 8, 500, 1000), (12, 1, 32, 16, 200, 403), (1, 1, 32, 16, 90, 250)])
 def test_f2_prefill_attention(hq, hkv, group, scale_bits, t0, chunk):
     """Chunked prefill over the mixed cache: a chunk of new tokens is written
     (their entry into the recent window pushes older tokens into INT2), then
     its queries attend causally; every query head of every chunk query against
     the oracle.  Requests of different lengths, one made of the chunk alone,
-    several query blocks per launch (g = 4, G = 32: 16 queries a block)."""
+    several query blocks per launch (g = 4, G = 32: 16 queries a block), and
+    chunks longer than the recent window, whose older positions the queries
+    read as INT2 up to their own."""
     from kv_cache_int2_amd.torch_cache import to_dev_bits, to_dev_i32
     w = synth.Workload("prefill", 120 + hq + chunk, hq, hkv, 128, 1, 0, group=group, sink=4, recent=128,
                        outlier_scale=(20.0, 20.0), calib_tokens=512)

@@ -230,13 +230,15 @@ def test_fork_shares_complete_pages_and_copies_open_ones(lib):
 
 
 def test_prefill_argument_checks(lib):
-    """Chunked prefill needs 1 <= chunk <= recent; the workspace size grows with
-    the chunk up to one query block."""
+    """Chunked prefill needs chunk >= 1 and its other arguments (a chunk longer
+    than the recent window is accepted); the workspace size grows with the
+    chunk up to one query block."""
     sh = K.make_shape(n_q_heads=32, n_kv_heads=8, group=32, sink=4, recent=128)
     assert K.lib().oscar_prefill_attn(C.byref(sh), None, None, None, 2, 129, None, 1, None, 1, None, 0, 0, None,
-                                      None, 0, None) == K.OSCAR_EUNSUPPORTED
+                                      None, 0, None) == K.OSCAR_EINVAL
     assert K.lib().oscar_prefill_attn(C.byref(sh), None, None, None, 2, 0, None, 1, None, 1, None, 0, 0, None,
                                       None, 0, None) == K.OSCAR_EINVAL
     a = K.oscar_prefill_workspace_bytes(sh, 28, 1, 8, 1)
     b = K.oscar_prefill_workspace_bytes(sh, 28, 16, 8, 1)
-    assert 0 < a < b == K.oscar_prefill_workspace_bytes(sh, 28, 128, 8, 1)
+    assert 0 < a < b == K.oscar_prefill_workspace_bytes(sh, 28, 128, 8, 1) == K.oscar_prefill_workspace_bytes(
+        sh, 28, 8192, 8, 1)

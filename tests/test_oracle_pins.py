@@ -735,6 +735,32 @@ def test_f2_prefill_all_bf16_is_causal_sdpa():
     assert np.abs(ours - ref).max() < 1e-12
 
 
+def test_f2_prefill_chunk_past_the_window_brute_force():
+    """A chunk longer than the recent window: its older positions were
+    quantised into INT2 when the chunk was written, and each query reads them
+    in that form, only up to its own position.  Queries on both sides of the
+    INT2/bf16 boundary recomputed by explicit loops."""
+    w = synth.Workload("f2", 93, 4, 2, 128, 1, 0, sink=4, recent=32, calib_tokens=256)
+    q, k, v = synth.calib_layer(w)
+    cal = O.calibrate_layer(q, k, v)
+    t, c_n = 150, 60                       # queries at positions 90 .. 149, INT2 below 118
+    kb, vb = synth.kv_request_bf16(w, 1, 0, t)
+    st = O.store_request(kb, vb, cal, 32, 4, 32)
+    assert st.region[t - c_n] == O.REGION_INT2 and st.region[t - 32] != O.REGION_INT2
+    kr, vr = O.represented_kv(st, cal, 32)
+    qb = np.stack([synth.q_decode_bf16(w, 1, s) for s in range(c_n)])
+    ours = O.prefill_attention(qb, st, cal, 32)
+    for c in (0, 7, 27, 28, 59):
+        qf = O.bf16_to_f64(qb[c])
+        vis = t - c_n + c + 1
+        for h in (0, 3):
+            lg = [sum(qf[h, j] * kr[p, h // 2, j] for j in range(128)) / math.sqrt(128) for p in range(vis)]
+            m = max(lg)
+            wts = [math.exp(x - m) for x in lg]
+            o = [sum(wts[p] * vr[p, h // 2, j] for p in range(vis)) / sum(wts) for j in range(128)]
+            assert np.abs(ours[c, h] - np.array(o)).max() < 1e-10
+
+
 def test_f2_prefill_brute_force_gqa_mixed_cache():
     """Small GQA case with INT2 history, sink and recent: each query's output
     recomputed by explicit loops over the positions it may see."""
