@@ -86,7 +86,14 @@ typedef struct oscar_shape {
 } oscar_shape;
 
 /* Calibration state of one layer ([IT] 2.2.A: fixed rotations and clip
- * thresholds).  r_k / r_v: device fp32 [n_kv_heads][d][d]. */
+ * thresholds).  r_k / r_v: device fp32 [n_kv_heads][d][d], 16-byte aligned.
+ * r_v may be NULL when R_V is folded into the model's weights ([ES] serving
+ * section: the value rotation is absorbed offline into the projections): the
+ * V vectors given to the write calls are then already rotated (W_V R_V), the
+ * cache stores them as given (bf16 region) or quantises them unrotated (INT2
+ * history), and the attention output stays in the rotated basis, for an
+ * output projection R_V^T W_O.  This is the same as passing R_V = I, minus
+ * the identity products.  r_k is required. */
 typedef struct oscar_layer {
   const float* r_k;
   const float* r_v;

@@ -198,16 +198,20 @@ __device__ __forceinline__ void quantise_and_store(const DecodeParams& p, int kv
   constexpr int G = kHeadDim / NG;
   constexpr Int2Layout L{NG, MB};
   const int t = threadIdx.x, m = t >> 7, j = t & (kHeadDim - 1);
-  const float* R = m ? rv : rk;
+  const float* R = m ? rv : rk;  // null: V arrives rotated (R_V folded into the V projection)
   const float* x = sc.x[tok][m];
   double acc = 0.0;
+  if (R) {
 #pragma unroll 8
-  for (int i = 0; i < kHeadDim; i += 4) {
-    const float4 x4 = *(const float4*)&x[i];
-    acc = fma((double)x4.x, (double)R[i * kHeadDim + j], acc);
-    acc = fma((double)x4.y, (double)R[(i + 1) * kHeadDim + j], acc);
-    acc = fma((double)x4.z, (double)R[(i + 2) * kHeadDim + j], acc);
-    acc = fma((double)x4.w, (double)R[(i + 3) * kHeadDim + j], acc);
+    for (int i = 0; i < kHeadDim; i += 4) {
+      const float4 x4 = *(const float4*)&x[i];
+      acc = fma((double)x4.x, (double)R[i * kHeadDim + j], acc);
+      acc = fma((double)x4.y, (double)R[(i + 1) * kHeadDim + j], acc);
+      acc = fma((double)x4.z, (double)R[(i + 2) * kHeadDim + j], acc);
+      acc = fma((double)x4.w, (double)R[(i + 3) * kHeadDim + j], acc);
+    }
+  } else {
+    acc = (double)x[j];
   }
   const double tau = m ? p.tau_v : p.tau_k;
   const double v = acc < -tau ? -tau : (acc > tau ? tau : acc);
@@ -368,10 +372,10 @@ __global__ __launch_bounds__(256) void decode_prologue(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) StepScratch sc;
   const int g = p.g;
   if constexpr (WRITE) {
-    stage_matrix256<kHeadDim>(p.r_v + (int64_t)kv * kHeadDim * kHeadDim, rv);
+    if (p.r_v) stage_matrix256<kHeadDim>(p.r_v + (int64_t)kv * kHeadDim * kHeadDim, rv);
     stage_matrix256<kHeadDim>(p.r_k + (int64_t)kv * kHeadDim * kHeadDim, rk);
     __syncthreads();
-    step_writes<NG, MB>(p, b, kv, rk, rv, sc);
+    step_writes<NG, MB>(p, b, kv, rk, p.r_v ? rv : nullptr, sc);
   } else {
     stage_matrix256<kHeadDim>(p.r_k + (int64_t)kv * kHeadDim * kHeadDim, rk);
   }
@@ -1388,7 +1392,10 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeParams p) {
   const int b = bk / p.n_kv, kv = bk % p.n_kv;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int S = p.splits_int2 + p.splits_bf16, SI = p.splits_int2;
-  if (SI > 0) stage_matrix256<kRvStride>(p.r_v + (int64_t)kv * kHeadDim * kHeadDim, rv);
+  // R_V null: the output stays in the rotated basis (R_V^T folded into the
+  // output projection), and so does the bf16 region's V
+  const bool rot = SI > 0 && p.r_v;
+  if (rot) stage_matrix256<kRvStride>(p.r_v + (int64_t)kv * kHeadDim * kHeadDim, rv);
   if (p.bf16_in_combine && w < p.splits_bf16) bf16_item(p, b, kv, SI + w, 0);
   __syncthreads();  // R_V staged; the bf16 partials written by this block are visible to it
   for (int h0 = 0; h0 < p.g; h0 += 4) {  // same trip count in every wavefront
@@ -1452,7 +1459,10 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeParams p) {
     if (h < p.g) {
       // R_V^T on the INT2 part: out_j = sum_k aint_k R_V[j][k]
       float r0 = 0.f, r1 = 0.f;
-      if (SI > 0) {
+      if (!rot) {
+        r0 = aint[w][lane];
+        r1 = aint[w][lane + 64];
+      } else {
         const float* row0 = rv + lane * kRvStride;
         const float* row1 = rv + (lane + 64) * kRvStride;
 #pragma unroll 8

@@ -663,8 +663,9 @@ static oscar_status check_cache(const oscar_cache* c, bool need_int2, bool need_
 }
 
 static oscar_status check_layer(const oscar_layer* l) {
-  if (!l || !l->r_k || !l->r_v) return fail(OSCAR_EINVAL, "layer rotations missing");
-  if (!aligned(l->r_k, 16) || !aligned(l->r_v, 16)) return fail(OSCAR_EINVAL, "rotations must be 16-byte aligned");
+  if (!l || !l->r_k) return fail(OSCAR_EINVAL, "layer rotation R_K missing");
+  if (!aligned(l->r_k, 16) || (l->r_v && !aligned(l->r_v, 16)))
+    return fail(OSCAR_EINVAL, "rotations must be 16-byte aligned");
   if (std::isnan(l->tau_k) || std::isnan(l->tau_v) || l->tau_k < 0 || l->tau_v < 0)
     return fail(OSCAR_EINVAL, "clip thresholds must be >= 0");
   return OSCAR_OK;

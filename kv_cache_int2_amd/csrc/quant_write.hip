@@ -87,18 +87,25 @@ __global__ __launch_bounds__(512) void quant_write_kernel(QuantParams p) {
   // ---- x_rot = X R in fp64 on MFMA: wavefront w owns output columns 16w..16w+15 ----
   // f64 16x16x4 operands: A lane l -> A[l%16][l/16]; B lane l -> B[l/16][l%16];
   // C lane l, element r -> C[4r + l/16][l%16].
-  const float* R = (isv ? p.r_v : p.r_k) + (int64_t)kv * kHeadDim * kHeadDim;
+  // (R_V null: V arrives rotated, its projection having R_V folded in)
+  const float* Rm = isv ? p.r_v : p.r_k;
   const int ln = lane & 15, qd = lane >> 4;
-  float rb[kHeadDim / 4];  // this lane's B values, loaded together
+  if (Rm) {
+    const float* R = Rm + (int64_t)kv * kHeadDim * kHeadDim;
+    float rb[kHeadDim / 4];  // this lane's B values, loaded together
 #pragma unroll
-  for (int ks = 0; ks < kHeadDim / 4; ++ks) rb[ks] = R[(4 * ks + qd) * kHeadDim + 16 * wave + ln];
-  __syncthreads();
-  f64x4 acc = f64x4{0.0, 0.0, 0.0, 0.0};
+    for (int ks = 0; ks < kHeadDim / 4; ++ks) rb[ks] = R[(4 * ks + qd) * kHeadDim + 16 * wave + ln];
+    __syncthreads();
+    f64x4 acc = f64x4{0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-  for (int ks = 0; ks < kHeadDim / 4; ++ks)
-    acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xin[ln][4 * ks + qd], (double)rb[ks], acc, 0, 0, 0);
+    for (int ks = 0; ks < kHeadDim / 4; ++ks)
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xin[ln][4 * ks + qd], (double)rb[ks], acc, 0, 0, 0);
 #pragma unroll
-  for (int r = 0; r < 4; ++r) xr[4 * r + qd][16 * wave + ln] = acc[r];
+    for (int r = 0; r < 4; ++r) xr[4 * r + qd][16 * wave + ln] = acc[r];
+  } else {
+    __syncthreads();
+    for (int idx = tid; idx < 16 * kHeadDim; idx += 512) xr[idx / kHeadDim][idx % kHeadDim] = xin[idx / kHeadDim][idx % kHeadDim];
+  }
   __syncthreads();
   // ---- clip, group statistics, codes: kTpg threads per (token, group) ----
   {

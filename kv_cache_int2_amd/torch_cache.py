@@ -34,7 +34,8 @@ class DeviceCache:
                                device="cuda")
         self.cache = K.make_cache(self.int2, n_int2_pages, self.bf16, n_bf16_pages)
         self.r_k = torch.from_numpy(np.ascontiguousarray(r_k, dtype=np.float32)).cuda()
-        self.r_v = torch.from_numpy(np.ascontiguousarray(r_v, dtype=np.float32)).cuda()
+        # r_v None: V arrives rotated (R_V folded into the model's projections)
+        self.r_v = None if r_v is None else torch.from_numpy(np.ascontiguousarray(r_v, dtype=np.float32)).cuda()
         self.layer = K.make_layer(self.r_k, self.r_v, tau_k, tau_v)
         self.int2_block = ib
         self.bf16_block = bb

@@ -587,3 +587,76 @@ def test_f2_prefill_attention(hq, hkv, group, scale_bits, t0, chunk):
         st = O.store_request(kb, vb, cal, group, 4, 128, scale_bits)
         ref = O.prefill_attention(q[r], st, cal, group)
         _check_close(got[r], ref, f"f2 prefill request {r} T={s0 + chunk} chunk={chunk}")
+
+
+def test_f4_rv_folded_into_the_projections():
+    """R_V folded into the model's projections ([ES] serving section): V
+    arrives as v R_V (bf16) and the layer has r_v = NULL, so the writes quantise
+    it unrotated and the output stays in the rotated basis.  Through the write
+    calls and then fused decode steps: storage and outputs bit-identical to
+    passing R_V = I, pages bit-exact and outputs within tolerance against the
+    oracle with R_V = I on the same folded V, and the output, rotated back,
+    as accurate against exact attention as the unfolded path's."""
+    import dataclasses
+    from kv_cache_int2_amd.torch_cache import to_dev_bits, to_dev_i32
+    hq, hkv, sink, recent = 8, 2, 4, 32
+    w = synth.Workload("fold", 77, hq, hkv, 128, 1, 0, group=32, sink=sink, recent=recent,
+                       outlier_scale=(20.0, 20.0), calib_tokens=512)
+    _flush("case f4 R_V folded")
+    cal = _calibrate(w)
+    eye = np.broadcast_to(np.eye(128, dtype=np.float32), cal.r_v.shape).copy()
+    cal_i = dataclasses.replace(cal, r_v=eye)
+    sh = K.make_shape(n_q_heads=hq, n_kv_heads=hkv, group=32, sink=sink, recent=recent)
+    r_v64 = cal.r_v.astype(np.float64)
+
+    def folded(vb):  # the folded projection's output, rounded to bf16 as a model would
+        return synth.f32_to_bf16_bits(np.einsum("thd,hde->the", O.bf16_to_f64(vb), r_v64).astype(np.float32))
+
+    lens0, n_steps = [3, 37, 600], 24
+    B = len(lens0)
+    caches = [DeviceCache(sh, cal.r_k, rv, cal.tau_k, cal.tau_v, 200, 32) for rv in (None, eye)]
+    seqs = [[], []]
+    for r, t in enumerate(lens0):
+        kb, vb = synth.kv_request_bf16(w, r, 0, t)
+        for c in (0, 1):
+            s = caches[c].new_seq()
+            caches[c].append(s, kb, folded(vb))
+            seqs[c].append(s)
+    planners = [K.DecodeStepPlanner(caches[c].pool, seqs[c]) for c in (0, 1)]
+    max_i2 = (max(lens0) + n_steps + 15) // 16
+    max_bf = -(-sink // 16) + recent // 16 + 1
+    ws = [torch.empty(K.oscar_decode_workspace_bytes(sh, B, 3, 1), dtype=torch.uint8, device="cuda") for _ in (0, 1)]
+    outs = [torch.empty((B, hq, 128), dtype=torch.float32, device="cuda") for _ in (0, 1)]
+    for st in range(n_steps):
+        kn = np.stack([synth.kv_request_bf16(w, r, lens0[r] + st, lens0[r] + st + 1)[0][0] for r in range(B)])
+        vn = np.stack([folded(synth.kv_request_bf16(w, r, lens0[r] + st, lens0[r] + st + 1)[1])[0]
+                       for r in range(B)])
+        q = to_dev_bits(np.stack([synth.q_decode_bf16(w, r, st + 1) for r in range(B)]))
+        kd, vd = to_dev_bits(kn), to_dev_bits(vn)
+        for c in (0, 1):
+            planners[c].step()
+            d = to_dev_i32(planners[c].buf)
+            i2, bf, ctx = caches[c].tables(seqs[c], max_i2, max_bf)
+            K.oscar_decode_step(sh, caches[c].layer, caches[c].cache, kd, vd, d[:4], q, to_dev_i32(i2),
+                                to_dev_i32(bf), to_dev_i32(ctx), outs[c], ws[c], 3, 1)
+        torch.cuda.synchronize()
+        assert torch.equal(outs[0], outs[1]), f"step {st}: r_v NULL and R_V = I differ"
+    assert torch.equal(caches[0].int2, caches[1].int2) and torch.equal(caches[0].bf16, caches[1].bf16)
+    out = outs[0].cpu().numpy()
+    qf = np.stack([synth.q_decode_bf16(w, r, n_steps) for r in range(B)])
+    for r in range(B):
+        t = lens0[r] + n_steps
+        kb, vb = synth.kv_request_bf16(w, r, 0, t)
+        st_f = O.store_request(kb, folded(vb), cal_i, 32, sink, recent)
+        _check_pages(caches[0], seqs[0][r], st_f, w, f"f4 folded len={t}")
+        _check_close(out[r], O.decode_attention(qf[r], st_f, cal_i, 32), f"f4 folded decode len={t}")
+        # rotated back, as accurate as the unfolded cache against exact attention
+        back = np.stack([out[r][h].astype(np.float64) @ r_v64[h // (hq // hkv)].T for h in range(hq)])
+        st_u = O.store_request(kb, vb, cal, 32, sink, recent)
+        ex = O.attend(O.bf16_to_f64(qf[r]), O.bf16_to_f64(kb), O.bf16_to_f64(vb))
+        e_f = np.linalg.norm(back - ex) / np.linalg.norm(ex)
+        e_u = np.linalg.norm(O.decode_attention(qf[r], st_u, cal, 32) - ex) / np.linalg.norm(ex)
+        _flush(f"f4 len={t}: error vs exact attention folded={e_f:.4f} unfolded={e_u:.4f}")
+        # the folded projection's output carries its own bf16 rounding (2^-9 relative): the
+        # only extra error, seen alone when every position is bf16
+        assert e_f <= 1.05 * e_u + 2.0 ** -8, (t, e_f, e_u)

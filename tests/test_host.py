@@ -77,6 +77,20 @@ def test_launch_argument_errors_before_any_gpu_call(lib):
     ok_cache = K.Cache(0x1000, 4, 0x2000, 4)
     assert lib.oscar_quant_write(C.byref(sh), C.byref(nan_layer), C.byref(ok_cache), 0x10, 0x10, 0x10, 1,
                                  None) == K.OSCAR_EINVAL
+    # R_K is required; R_V may be NULL (folded into the model's projections), and when given it
+    # must be aligned.  The layer passes its check when only R_V is missing: the error is the cache's.
+    no_rk = K.Layer(None, 0x2000, 1.0, 1.0)
+    assert lib.oscar_quant_write(C.byref(sh), C.byref(no_rk), C.byref(ok_cache), 0x10, 0x10, 0x10, 1,
+                                 None) == K.OSCAR_EINVAL
+    assert b"R_K" in lib.oscar_last_error()
+    odd_rv = K.Layer(0x1000, 0x2008, 1.0, 1.0)
+    assert lib.oscar_quant_write(C.byref(sh), C.byref(odd_rv), C.byref(ok_cache), 0x10, 0x10, 0x10, 1,
+                                 None) == K.OSCAR_EINVAL
+    assert b"aligned" in lib.oscar_last_error()
+    folded = K.Layer(0x1000, None, 1.0, 1.0)
+    assert lib.oscar_quant_write(C.byref(sh), C.byref(folded), C.byref(bad), 0x10, 0x10, 0x10, 1,
+                                 None) == K.OSCAR_EINVAL
+    assert b"storage" in lib.oscar_last_error()
 
 
 def test_workspace_bytes_monotone(lib):
