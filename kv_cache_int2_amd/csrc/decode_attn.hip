@@ -310,12 +310,19 @@ __device__ __forceinline__ void write_q_operands(const DecodeParams& p, int bk, 
   const int t = threadIdx.x;
   float* aux = p.qaux + (int64_t)bk * (1 + 16 * tiles);
   if (t == 0) aux[0] = ldexpf(0.5f, -sq);
-  for (int row = t; row < 16 * tiles; row += 256) {
+  // 2 Qbar per row (head, group): 16 threads per row, each summing G/16
+  // channels, then a reduction over the 16 lanes
+  for (int e = t; e < 16 * 16 * tiles; e += 256) {
+    const int row = e >> 4, part = e & 15;
     const int h = row / NG, gam = row % NG;
     int sum = 0;
-    if (h < g)
-      for (int c = gam * G; c < (gam + 1) * G; ++c) sum += qi[h][c];
-    aux[1 + row] = 2.0f * (float)sum;
+    if (h < g) {
+#pragma unroll
+      for (int c = 0; c < G / 16; ++c) sum += qi[h][gam * G + part * (G / 16) + c];
+    }
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+    if (part == 0) aux[1 + row] = 2.0f * (float)sum;
   }
   uint32_t* qb = p.qb + (int64_t)bk * tiles * 3 * 2 * 64 * 4;
   for (int w = t; w < tiles * 3 * 2 * 64 * 4; w += 256) {
@@ -338,6 +345,35 @@ __device__ __forceinline__ void write_q_operands(const DecodeParams& p, int bk, 
       word |= (uint32_t)(dv & 0xff) << (8 * byte);
     }
     qb[w] = word;
+  }
+}
+
+// q~ partial sums of GM heads (the rows of qs; rows past the real heads hold
+// zeros) for column j over the inputs [64 hf, 64 hf + 64): eight rows of R_K
+// read at a time, every head in the same straight-line loop body
+template <int GM>
+__device__ __forceinline__ void qrk_partial(const float* rk, const float (*qs)[kHeadDim], int hf, int j,
+                                            float (&acc)[GM]) {
+#pragma unroll
+  for (int h = 0; h < GM; ++h) acc[h] = 0.f;
+  for (int i = 64 * hf; i < 64 * hf + 64; i += 8) {
+    float r[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) r[u] = rk[(i + u) * kHeadDim + j];
+#pragma unroll
+    for (int h = 0; h < GM; ++h) {
+      const float4 qa = *(const float4*)&qs[h][i], qb = *(const float4*)&qs[h][i + 4];
+      float a = acc[h];
+      a = fmaf(qa.x, r[0], a);
+      a = fmaf(qa.y, r[1], a);
+      a = fmaf(qa.z, r[2], a);
+      a = fmaf(qa.w, r[3], a);
+      a = fmaf(qb.x, r[4], a);
+      a = fmaf(qb.y, r[5], a);
+      a = fmaf(qb.z, r[6], a);
+      a = fmaf(qb.w, r[7], a);
+      acc[h] = a;
+    }
   }
 }
 
@@ -379,30 +415,22 @@ __global__ __launch_bounds__(256) void decode_prologue(DecodeParams p) {
   } else {
     stage_matrix256<kHeadDim>(p.r_k + (int64_t)kv * kHeadDim * kHeadDim, rk);
   }
-  for (int e = t; e < g * kHeadDim; e += 256)
-    qs[e >> 7][e & (kHeadDim - 1)] = bf16_val(p.q[q_row(p, b, kv, e >> 7) + (e & (kHeadDim - 1))]);
+  // GM: the most heads a launch of this tile count has (g <= GM); rows g .. GM-1
+  // of qs are zero, so every loop below runs over GM heads without a branch
+  constexpr int GM = (16 * CT / NG) < 16 ? (16 * CT / NG) : 16;
+  for (int e = t; e < GM * kHeadDim; e += 256)
+    qs[e >> 7][e & (kHeadDim - 1)] =
+        (e >> 7) < g ? bf16_val(p.q[q_row(p, b, kv, e >> 7) + (e & (kHeadDim - 1))]) : 0.f;
   __syncthreads();
-  // q~[h][j]: this thread sums inputs i in [64 hf, 64 hf + 64) for every head
-  // (q read four inputs at a time); the halves exchange partial sums through
-  // LDS and each thread keeps the heads h = hf, hf + 2, ...
-  float acc[16];
-#pragma unroll
-  for (int h = 0; h < 16; ++h) acc[h] = 0.f;
-  for (int i = 64 * hf; i < 64 * hf + 64; i += 4) {
-    const float r0 = rk[i * kHeadDim + j], r1 = rk[(i + 1) * kHeadDim + j];
-    const float r2 = rk[(i + 2) * kHeadDim + j], r3 = rk[(i + 3) * kHeadDim + j];
-#pragma unroll
-    for (int h = 0; h < 16; ++h) {
-      if (h < g) {
-        const float4 q4 = *(const float4*)&qs[h][i];
-        acc[h] = fmaf(q4.w, r3, fmaf(q4.z, r2, fmaf(q4.y, r1, fmaf(q4.x, r0, acc[h]))));
-      }
-    }
-  }
+  // q~[h][j]: this thread sums inputs i in [64 hf, 64 hf + 64) for every head;
+  // the halves exchange partial sums through LDS and each thread keeps the
+  // heads h = hf, hf + 2, ...
+  float acc[GM];
+  qrk_partial<GM>(rk, qs, hf, j, acc);
   __syncthreads();  // qs becomes the exchange: each half publishes the heads the other keeps
 #pragma unroll
-  for (int h = 0; h < 16; ++h)
-    if (h < g && (h & 1) != hf) qs[h][j] = acc[h];
+  for (int h = 0; h < GM; ++h)
+    if ((h & 1) != hf) qs[h][j] = acc[h];
   __syncthreads();
   float qt[8];
   float mx = 0.f;
@@ -410,8 +438,8 @@ __global__ __launch_bounds__(256) void decode_prologue(DecodeParams p) {
   for (int k = 0; k < 8; ++k) {
     const int h = hf + 2 * k;
     qt[k] = 0.f;
-    if (h < g) {
-      const float own = hf ? acc[2 * k + 1] : acc[2 * k];  // hf is uniform per wavefront
+    if (2 * k < GM && h < g) {  // GM is even
+      const float own = hf ? acc[2 * k + 1 < GM ? 2 * k + 1 : 0] : acc[2 * k];  // hf is uniform per wavefront
       qt[k] = (own + qs[h][j]) * kLog2eOverSqrtD;
       mx = fmaxf(mx, fabsf(qt[k]));
     }
@@ -448,27 +476,16 @@ __global__ __launch_bounds__(256) void prefill_prologue(DecodeParams p) {
   for (int h0 = 0; h0 < g; h0 += 16) {
     const int gb = min(16, g - h0);
     __syncthreads();  // R_K staged; the previous block's exchange is read
-    for (int e = t; e < gb * kHeadDim; e += 256)
-      qs[e >> 7][e & (kHeadDim - 1)] = bf16_val(p.q[q_row(p, b, kv, h0 + (e >> 7)) + (e & (kHeadDim - 1))]);
+    for (int e = t; e < 16 * kHeadDim; e += 256)
+      qs[e >> 7][e & (kHeadDim - 1)] =
+          (e >> 7) < gb ? bf16_val(p.q[q_row(p, b, kv, h0 + (e >> 7)) + (e & (kHeadDim - 1))]) : 0.f;
     __syncthreads();
     float acc[16];
-#pragma unroll
-    for (int h = 0; h < 16; ++h) acc[h] = 0.f;
-    for (int i = 64 * hf; i < 64 * hf + 64; i += 4) {
-      const float r0 = rk[i * kHeadDim + j], r1 = rk[(i + 1) * kHeadDim + j];
-      const float r2 = rk[(i + 2) * kHeadDim + j], r3 = rk[(i + 3) * kHeadDim + j];
-#pragma unroll
-      for (int h = 0; h < 16; ++h) {
-        if (h < gb) {
-          const float4 q4 = *(const float4*)&qs[h][i];
-          acc[h] = fmaf(q4.w, r3, fmaf(q4.z, r2, fmaf(q4.y, r1, fmaf(q4.x, r0, acc[h]))));
-        }
-      }
-    }
+    qrk_partial<16>(rk, qs, hf, j, acc);
     __syncthreads();  // qs becomes the exchange of the halves' partial sums
 #pragma unroll
     for (int h = 0; h < 16; ++h)
-      if (h < gb && (h & 1) != hf) qs[h][j] = acc[h];
+      if ((h & 1) != hf) qs[h][j] = acc[h];
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
