@@ -743,13 +743,55 @@ struct Int2Staged {
   }
 };
 
+// MFMA B operands from packed codes.  Keys: one 32-bit word of 16 codes
+// (4 per byte, at bits 2i) becomes the four int8 words of 4 codes each.
+__device__ __forceinline__ u32x4 k_operand(uint32_t x) {
+  return u32x4{x & 0x03030303u, (x >> 2) & 0x03030303u, (x >> 4) & 0x03030303u, (x >> 6) & 0x03030303u};
+}
+// Values, channel 8ln + kt: byte kt of this lane's quad, page 0 -> low half,
+// page 1 -> high half; code c at bits 2r of each half is the fp16 subnormal
+// c 2^(2r-24), and odd token slots take 3 - c = c ^ 3 (one and-xor)
+__device__ __forceinline__ u32x4 v_operand(uint32_t lo_src, uint32_t hi_src, int kt) {
+  const uint32_t sel = (uint32_t)(kt & 3) | 0x0c00u | ((uint32_t)(4 + (kt & 3)) << 16) | 0x0c000000u;
+  const uint32_t x = __builtin_amdgcn_perm(hi_src, lo_src, sel);
+  u32x4 bv;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t m = 0x00030003u << (2 * r);
+    bv[r] = (r & 1) ? ((x & m) ^ m) : (x & m);
+  }
+  return bv;
+}
+// The wavefronts of a multi-wavefront item share the operands of a staged
+// pair: 12 units of one u32x4 per lane (units 0-3: key words (page u / 2,
+// k-step u % 2), units 4-11: value channels kt = u - 4), each unpacked by one
+// wavefront into ops[unit][lane].
+constexpr int kOpUnits = 12;
+template <int NG, int MB>
+__device__ __forceinline__ void unpack_unit(const uint8_t* st, const Int2Offsets& o, int u, u32x4* ops) {
+  constexpr Int2Layout L{NG, MB};
+  const int lane = threadIdx.x & 63;
+  u32x4 v;
+  if (u < 4) {
+    v = k_operand((*(const u32x2*)(st + (u >> 1) * L.bytes() + o.kc))[u & 1]);
+  } else {
+    const int kt = u - 4;
+    v = v_operand(*(const uint32_t*)(st + o.vw + 4 * (kt >> 2)), *(const uint32_t*)(st + L.bytes() + o.vw + 4 * (kt >> 2)),
+                  kt);
+  }
+  ops[u * 64 + lane] = v;
+}
+
 // EDGE: a masked pair.  Its tokens must lie in [lo, hi) on pages below
 // p_end, and row head h (16 t0 ... of the wavefront's tiles) sees positions up
 // to qlo + floor(h / g_real), i.e. position qlo + k when k g_real <= h (causal
 // masks of a chunk's queries; in decode every row sees the whole INT2 region).
-template <int NG, int CT, bool EDGE, class Src>
+// SH: the code operands come unpacked from ops (shared by the item's
+// wavefronts), else each lane unpacks its own.
+template <int NG, int CT, bool EDGE, bool SH, class Src>
 __device__ __forceinline__ void int2_pair(const Src& src, int lp0, int p_end, int lo, int hi, int qlo, int g_real,
-                                          int t0, const Int2Const<NG, CT>& K, Int2State<NG, CT>& S, float* p_lds) {
+                                          int t0, const Int2Const<NG, CT>& K, Int2State<NG, CT>& S, float* p_lds,
+                                          const u32x4* ops) {
   constexpr int HPL = 4 / NG;
   const int lane = threadIdx.x & 63, ln = lane & 15, qd = lane >> 4;
   // ---- logits ----
@@ -777,10 +819,7 @@ __device__ __forceinline__ void int2_pair(const Src& src, int lp0, int p_end, in
   for (int t = 0; t < 2; ++t) {
     u32x4 av[2];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const uint32_t x = DK.kc[t][ks];
-      av[ks] = u32x4{x & 0x03030303u, (x >> 2) & 0x03030303u, (x >> 4) & 0x03030303u, (x >> 6) & 0x03030303u};
-    }
+    for (int ks = 0; ks < 2; ++ks) av[ks] = SH ? ops[(2 * t + ks) * 64 + lane] : k_operand(DK.kc[t][ks]);
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
       // digit chains feed each other: acc <- (acc << 8) + sum d_k c; every
@@ -904,18 +943,7 @@ __device__ __forceinline__ void int2_pair(const Src& src, int lp0, int p_end, in
   // ---- values on MFMA ----
 #pragma unroll
   for (int kt = 0; kt < 8; ++kt) {
-    // channel 8ln + kt: byte kt of this lane's quad, page 0 -> low half, page 1 -> high half
-    const uint32_t lo_src = DV.vw[0][kt >> 2], hi_src = DV.vw[1][kt >> 2];
-    const uint32_t sel = (uint32_t)(kt & 3) | 0x0c00u | ((uint32_t)(4 + (kt & 3)) << 16) | 0x0c000000u;
-    const uint32_t x = __builtin_amdgcn_perm(hi_src, lo_src, sel);
-    // code c at bits 2r of each half is the fp16 subnormal c 2^(2r-24); odd
-    // token slots take 3 - c = c ^ 3 (one and-xor)
-    u32x4 bv;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const uint32_t m = 0x00030003u << (2 * r);
-      bv[r] = (r & 1) ? ((x & m) ^ m) : (x & m);
-    }
+    const u32x4 bv = SH ? ops[(4 + kt) * 64 + lane] : v_operand(DV.vw[0][kt >> 2], DV.vw[1][kt >> 2], kt);
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
       S.acc[ct][kt] = mfma_f16(pa[ct][0], bv, S.acc[ct][kt]);
@@ -927,7 +955,8 @@ __device__ __forceinline__ void int2_pair(const Src& src, int lp0, int p_end, in
 // W wavefronts per work item: wavefront w takes the CT row tiles starting at
 // tile w CT, all of them reading the same staged pages.
 template <int NG, int MB, int CT, int W>
-__device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float* p_lds, uint8_t* stage) {
+__device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float* p_lds, uint8_t* stage,
+                          u32x4* ops) {
   constexpr Int2Layout L{NG, MB};
   constexpr int HPL = 4 / NG;
   constexpr int kTiles = W * CT;  // row tiles of the (request, KV head)
@@ -999,7 +1028,7 @@ __device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float
         if (!ok1) pg1 = pg0;
         const int pe = ok0 ? (ok1 ? p_end : lp0 + 1) : lp0;
         const Int2Data<NG> D = int2_load<NG, MB>(blk(pg0), blk(pg1), off);
-        int2_pair<NG, CT, true>(D, lp0, pe, lo, hi, qlo, g_real, t0, K, S, p_lds);
+        int2_pair<NG, CT, true, false>(D, lp0, pe, lo, hi, qlo, g_real, t0, K, S, p_lds, nullptr);
       };
       int lp0 = p_begin;
       if (lp0 * kPage < lo) {
@@ -1041,8 +1070,8 @@ __device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float
             } else {
               vm_wait<0>();
             }
-            int2_pair<NG, CT, false>(Int2Staged<NG, MB>{stage + cur * kSlot, off}, lp0, p_end, lo, hi, qlo, g_real, t0,
-                                     K, S, p_lds);
+            int2_pair<NG, CT, false, false>(Int2Staged<NG, MB>{stage + cur * kSlot, off}, lp0, p_end, lo, hi, qlo,
+                                            g_real, t0, K, S, p_lds, nullptr);
             lp0 += 2;
             if (lp0 + 2 > lim) break;
             cur = cur == 2 ? 0 : cur + 1;
@@ -1055,6 +1084,11 @@ __device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float
         // publishes the pair to all and certifies that all have finished the
         // pair before last, whose slot the next staging load reuses
         const bool leader = t0 == 0;
+        const int wv = t0 / CT;  // this wavefront's index in the item
+        // sharing the unpacked operands costs a second barrier per pair: it
+        // pays with 16 wavefronts per item (a prefill block, 10 % faster) and
+        // lost 18 % with 3 (wide decode groups)
+        constexpr bool kShareOps = W >= 4;
         while (lp0 + 2 <= main_end) {
           const int c0 = lp0;
           const int cn = min(64, main_end - c0);
@@ -1082,8 +1116,15 @@ __device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float
               }
             }
             barrier_no_fence();
-            int2_pair<NG, CT, false>(Int2Staged<NG, MB>{stage + cur * kSlot, off}, lp0, p_end, lo, hi, qlo, g_real, t0,
-                                     K, S, p_lds);
+            if constexpr (kShareOps) {
+              // the code operands: one share per wavefront, published by a
+              // second barrier (every wavefront has finished the previous
+              // pair, whose operands these overwrite, before the first)
+              for (int u = wv; u < kOpUnits; u += W) unpack_unit<NG, MB>(stage + cur * kSlot, off, u, ops);
+              barrier_no_fence();
+            }
+            int2_pair<NG, CT, false, kShareOps>(Int2Staged<NG, MB>{stage + cur * kSlot, off}, lp0, p_end, lo, hi, qlo,
+                                                g_real, t0, K, S, p_lds, ops);
             lp0 += 2;
             if (lp0 + 2 > lim) break;
             cur = (cur + 1) & 3;
@@ -1332,10 +1373,11 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(CT == 1 
 decode_int2(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) float p_lds[W][(16 * CT / NG) * 32];
   __shared__ __attribute__((aligned(16))) uint8_t stage[(W == 1 ? 6 : 8) * Int2Layout{NG, MB}.bytes()];
+  __shared__ u32x4 ops[W >= 4 ? kOpUnits * 64 : 1];  // code operands shared by the wavefronts of an item
   const int item = blockIdx.x;
   const int split = item % p.splits_int2;
   const int bk = item / p.splits_int2;
-  int2_item<NG, MB, CT, W>(p, bk / p.n_kv, bk % p.n_kv, split, p_lds[W > 1 ? threadIdx.x >> 6 : 0], stage);
+  int2_item<NG, MB, CT, W>(p, bk / p.n_kv, bk % p.n_kv, split, p_lds[W > 1 ? threadIdx.x >> 6 : 0], stage, ops);
 }
 
 // items: (request, KV head, query of the launch, bf16 split)
