@@ -291,6 +291,12 @@ oscar_status oscar_prefill_attn(const oscar_shape* shape, const oscar_layer* lay
  * pages per split (deterministic for a given device). */
 int32_t oscar_decode_auto_splits(const oscar_shape* shape, int32_t batch, int32_t max_int2_pages);
 
+/* INT2 splits oscar_prefill_attn chooses when 0 is passed, for a chunk of
+ * `chunk` queries: the fewest whose work items fill their last round of the
+ * device to at least 15/16, else the best-filled count; at most 64 and at
+ * least 32 pages per split.  Returns 1 for an invalid shape or argument. */
+int32_t oscar_prefill_auto_splits(const oscar_shape* shape, int32_t batch, int32_t max_int2_pages, int32_t chunk);
+
 /* One decode step for a batch: grows each of the n sequences by one token
  * (host bookkeeping, as oscar_seq_plan_append with n_new = 1 per sequence).
  * Outputs (host, capacity n each): int2_slots / bf16_slots of the new tokens

@@ -79,6 +79,7 @@ _SIGS = {
     "oscar_decode_attn_bf16_baseline": (C.c_int32, [C.POINTER(Shape), C.POINTER(Cache), P, C.c_int32, P,
                                                     C.c_int32, P, C.c_int32, P, P, C.c_size_t, P]),
     "oscar_decode_auto_splits": (C.c_int32, [C.POINTER(Shape), C.c_int32, C.c_int32]),
+    "oscar_prefill_auto_splits": (C.c_int32, [C.POINTER(Shape), C.c_int32, C.c_int32, C.c_int32]),
     "oscar_plan_decode_step": (C.c_int32, [P, P, C.c_int32, P, P, P, P, P, P, P]),
     "oscar_profile_enable": (C.c_int32, [C.c_int32]),
     "oscar_profile_read": (C.c_int32, [C.POINTER(C.c_double), I64P]),
@@ -282,6 +283,10 @@ def oscar_decode_workspace_bytes(shape, batch, splits_int2=0, splits_bf16=0) -> 
 
 def oscar_decode_auto_splits(shape, batch, max_int2_pages) -> int:
     return int(lib().oscar_decode_auto_splits(C.byref(shape), batch, max_int2_pages))
+
+
+def oscar_prefill_auto_splits(shape, batch, max_int2_pages, chunk) -> int:
+    return int(lib().oscar_prefill_auto_splits(C.byref(shape), batch, max_int2_pages, chunk))
 
 
 def oscar_decode_attn(shape, layer, cache, q, int2_bt, bf16_bt, ctx_lens, out, workspace, splits_int2=0,

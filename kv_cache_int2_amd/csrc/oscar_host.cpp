@@ -927,11 +927,30 @@ static int prefill_tiles(const oscar_shape* shape, int queries) {
   return tiles <= 4 ? 4 : (tiles <= 8 ? 8 : 16);
 }
 static int32_t prefill_auto_splits(const oscar_shape* shape, int32_t batch, int32_t max_int2_pages, int tiles) {
-  // two whole rounds of items of `tiles` wavefronts (4 per SIMD), as in decode
+  // Items of `tiles` wavefronts (4 per SIMD) run in rounds of `cap` items.  A
+  // pass is long, so a part-empty last round costs its whole share: take the
+  // fewest splits whose last round is at least 15/16 full, else the count that
+  // fills it best (28 x 8 pairs on 256 compute units: 8 splits, 7 full rounds).
   const int64_t pairs = (int64_t)batch * shape->n_kv_heads;
-  const int64_t cap = (int64_t)device_cus() * 4 * 4 / tiles;
+  const int64_t cap = std::max<int64_t>(1, (int64_t)device_cus() * 4 * 4 / tiles);
   const int64_t smax = std::max<int64_t>(1, std::min<int64_t>(kAutoMaxSplits, max_int2_pages / 32));
-  return (int32_t)std::max<int64_t>(1, std::min<int64_t>(2 * cap / pairs, smax));
+  int64_t best = 1;
+  double best_fill = 0.0;
+  for (int64_t sp = 1; sp <= smax; ++sp) {
+    const int64_t n = pairs * sp, rounds = (n + cap - 1) / cap;
+    const double fill = (double)n / (double)(rounds * cap);
+    if (fill >= 15.0 / 16.0) return (int32_t)sp;
+    if (fill > best_fill + 1e-12) {
+      best = sp;
+      best_fill = fill;
+    }
+  }
+  return (int32_t)best;
+}
+
+int32_t oscar_prefill_auto_splits(const oscar_shape* shape, int32_t batch, int32_t max_int2_pages, int32_t chunk) {
+  if (check_shape(shape) != OSCAR_OK || batch < 1 || chunk < 1) return 1;
+  return prefill_auto_splits(shape, batch, max_int2_pages, prefill_tiles(shape, std::min(chunk, prefill_block(shape))));
 }
 
 size_t oscar_prefill_workspace_bytes(const oscar_shape* shape, int32_t batch, int32_t chunk, int32_t splits_int2,

@@ -243,6 +243,19 @@ def test_fork_shares_complete_pages_and_copies_open_ones(lib):
     assert pool.free_pages() == (100, 20)
 
 
+def test_prefill_auto_splits_fill_the_last_round(lib):
+    """With 256 compute units (the host default) and 28 x 8 (request, KV head)
+    pairs: a 16-query block is one 16-wavefront item, 256 run at once, and 8
+    splits make exactly 7 full rounds (2 splits would leave the second round a
+    quarter empty); one query is one wavefront, 1024 at once, and 9 splits fill
+    2016 of 2048.  Short requests cap the count at one split per 32 pages."""
+    sh = K.make_shape(n_q_heads=32, n_kv_heads=8, group=32, sink=4, recent=128)
+    assert K.oscar_prefill_auto_splits(sh, 28, 6300, 128) == 8
+    assert K.oscar_prefill_auto_splits(sh, 28, 6300, 1) == 9
+    assert K.oscar_prefill_auto_splits(sh, 3, 100, 128) == 3
+    assert K.oscar_prefill_auto_splits(sh, 0, 100, 128) == 1
+
+
 def test_prefill_argument_checks(lib):
     """Chunked prefill needs chunk >= 1 and its other arguments (a chunk longer
     than the recent window is accepted); the workspace size grows with the
