@@ -777,14 +777,15 @@ static int device_cus() {
 int32_t oscar_decode_auto_splits(const oscar_shape* shape, int32_t batch, int32_t max_int2_pages) {
   if (check_shape(shape) != OSCAR_OK || batch < 1) return 1;
   // Work items run in rounds of the items that fit the device at once (4
-  // SIMDs per compute unit, 4 / ct wavefronts per SIMD, w wavefronts per item:
-  // tile_split).  A count just above a whole number of rounds leaves a nearly
-  // empty last round that costs a full item time.  Take the count that fills
-  // two whole rounds (some slack for uneven requests, few partial results),
-  // within [1, 64] and at least 32 pages per split.
+  // SIMDs per compute unit, 4 / ct wavefronts per SIMD, whole items of w
+  // wavefronts each: tile_split; three-wavefront items fit five to a compute
+  // unit, not 16/3).  A count just above a whole number of rounds leaves a
+  // nearly empty last round that costs a full item time.  Take the count that
+  // fills two whole rounds (some slack for uneven requests, few partial
+  // results), within [1, 64] and at least 32 pages per split.
   const int64_t pairs = (int64_t)batch * shape->n_kv_heads;
   const TileSplit ts = tile_split(ct_of(shape));
-  const int64_t cap = (int64_t)device_cus() * 4 * (4 / ts.ct) / ts.w;
+  const int64_t cap = (int64_t)device_cus() * ((4 * (4 / ts.ct)) / ts.w);
   const int64_t smax = std::max<int64_t>(1, std::min<int64_t>(kAutoMaxSplits, max_int2_pages / 32));
   const int64_t s = 2 * cap / pairs;
   return (int32_t)std::max<int64_t>(1, std::min<int64_t>(s, smax));
