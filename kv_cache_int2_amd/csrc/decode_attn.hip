@@ -1193,23 +1193,39 @@ __device__ __forceinline__ int bf16_slot_position(int L, int ring0, int T, int s
 }
 
 // EDGE: masked pair; its slots must be valid and hold positions <= qpos
-template <bool EDGE>
-__device__ __forceinline__ void bf16_pair(const DecodeParams& p, const uint8_t* blk0, const uint8_t* blk1, int lp0,
-                                          int p_end, int n_sink, int ring0, int n_rec, int T, int qpos,
-                                          const u32x4 (&bq)[4], float& m_run, float& l_run, f32x4 (&acc)[8]) {
+// a pair of bf16 blocks as this lane reads them: K as the logits' A operand
+// (tokens 8 ((ln / 4) % 2) + ln % 4 + 4t of page ln / 8), V as the values' B
+// operand (channel 8 ln + kt, tokens 8 (qd % 2) .. + 7 of page qd / 2)
+struct Bf16PairData {
+  u32x4 ka[2][4];
+  u32x4 vv[8];
+};
+__device__ __forceinline__ Bf16PairData bf16_pair_load(const uint8_t* blk0, const uint8_t* blk1) {
   const int lane = threadIdx.x & 63, ln = lane & 15, qd = lane >> 4;
   const int a = qd & 1;
   const uint8_t* bk = (ln >> 3) ? blk1 : blk0;
   const int tokA = 8 * ((ln >> 2) & 1) + (ln & 3);
-  u32x4 ka[2][4];
+  Bf16PairData d;
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int s = 0; s < 4; ++s) ka[t][s] = *(const u32x4*)(bk + (tokA + 4 * t) * 256 + 64 * qd + 16 * s);
+    for (int s = 0; s < 4; ++s) d.ka[t][s] = *(const u32x4*)(bk + (tokA + 4 * t) * 256 + 64 * qd + 16 * s);
   const uint8_t* bq_ = (qd >> 1) ? blk1 : blk0;
+#pragma unroll
+  for (int kt = 0; kt < 8; ++kt) d.vv[kt] = *(const u32x4*)(bq_ + 4096 + ((8 * ln + kt) * 16 + 8 * a) * 2);
+  return d;
+}
+
+template <bool EDGE>
+__device__ __forceinline__ void bf16_pair(const DecodeParams& p, const Bf16PairData& d, int lp0, int p_end,
+                                          int n_sink, int ring0, int n_rec, int T, int qpos, const u32x4 (&bq)[4],
+                                          float& m_run, float& l_run, f32x4 (&acc)[8]) {
+  const int lane = threadIdx.x & 63, qd = lane >> 4;
+  const int a = qd & 1;
+  const u32x4 (&ka)[2][4] = d.ka;
   u32x4 vv[8];
 #pragma unroll
-  for (int kt = 0; kt < 8; ++kt) vv[kt] = *(const u32x4*)(bq_ + 4096 + ((8 * ln + kt) * 16 + 8 * a) * 2);
+  for (int kt = 0; kt < 8; ++kt) vv[kt] = d.vv[kt];
 
   f32x4 c[2];
 #pragma unroll
@@ -1294,6 +1310,9 @@ __device__ __forceinline__ void bf16_pair(const DecodeParams& p, const uint8_t* 
 
 // The bf16 region of one (request, KV head) for query c of the launch (its
 // g_real model heads, rows ln < g_real), split `split` of the partials.
+// PREFETCH: the next pair's blocks are read before the current pair is
+// computed (for the combine kernel, whose wavefronts have registers to spare).
+template <bool PREFETCH>
 __device__ void bf16_item(const DecodeParams& p, int b, int kv, int split, int c) {
   const int lane = threadIdx.x & 63, ln = lane & 15, qd = lane >> 4;
   const int T = p.ctx_lens[b];
@@ -1323,7 +1342,15 @@ __device__ void bf16_item(const DecodeParams& p, int b, int kv, int split, int c
     }
     const int32_t* bt = p.bf16_bt + (int64_t)b * p.max_bf16_pages;
     const int64_t npg = p.n_bf16_pages;
-    for (int lp0 = p_begin; lp0 < p_end; lp0 += 2) {
+    // the pair at lp0: its blocks (bad ids read page 0 and are masked), its
+    // page limit for the masked path, and whether it needs no mask at all
+    struct PairAt {
+      const uint8_t* blk0;
+      const uint8_t* blk1;
+      int pe;
+      bool interior;
+    };
+    auto pair_at = [&](int lp0) {
       const bool has1 = lp0 + 1 < p_end;
       int pg0 = bt[lp0];
       int pg1 = has1 ? bt[lp0 + 1] : pg0;
@@ -1331,18 +1358,35 @@ __device__ void bf16_item(const DecodeParams& p, int b, int kv, int split, int c
       const bool ok1 = pg1 >= 0 && pg1 < npg;
       if (!ok0) pg0 = 0;
       if (!ok1) pg1 = pg0;
-      const uint8_t* blk0 = block_ptr(p.bf16_pages, pg0, p.n_kv, kv, kBf16BlockBytes);
-      const uint8_t* blk1 = block_ptr(p.bf16_pages, pg1, p.n_kv, kv, kBf16BlockBytes);
       const int L0 = lp0 * kPage, L1 = (lp0 + 2) * kPage;
       // a chunk's queries mask the newer positions: every prefill pair is masked
       const bool interior =
           p.chunk == 1 && has1 && ok0 && ok1 && ((L1 <= n_sink) || (L0 >= ring0 && L1 <= ring0 + n_rec));
-      if (interior) {
-        bf16_pair<false>(p, blk0, blk1, lp0, p_end, n_sink, ring0, n_rec, T, qpos, bq, m_run, l_run, acc);
-      } else {
-        const int pe = ok0 ? (ok1 ? p_end : lp0 + 1) : lp0;
-        bf16_pair<true>(p, blk0, blk1, lp0, pe, n_sink, ring0, n_rec, T, qpos, bq, m_run, l_run, acc);
+      return PairAt{block_ptr(p.bf16_pages, pg0, p.n_kv, kv, kBf16BlockBytes),
+                    block_ptr(p.bf16_pages, pg1, p.n_kv, kv, kBf16BlockBytes), ok0 ? (ok1 ? p_end : lp0 + 1) : lp0,
+                    interior};
+    };
+    PairAt pa = pair_at(p_begin);
+    Bf16PairData cur = bf16_pair_load(pa.blk0, pa.blk1);
+    for (int lp0 = p_begin; lp0 < p_end; lp0 += 2) {
+      const bool more = lp0 + 2 < p_end;
+      PairAt pn = pa;
+      Bf16PairData nxt;
+      if (more) {
+        pn = pair_at(lp0 + 2);
+        if constexpr (PREFETCH) nxt = bf16_pair_load(pn.blk0, pn.blk1);
       }
+      if (pa.interior)
+        bf16_pair<false>(p, cur, lp0, p_end, n_sink, ring0, n_rec, T, qpos, bq, m_run, l_run, acc);
+      else
+        bf16_pair<true>(p, cur, lp0, pa.pe, n_sink, ring0, n_rec, T, qpos, bq, m_run, l_run, acc);
+      if (more) {
+        if constexpr (PREFETCH)
+          cur = nxt;
+        else
+          cur = bf16_pair_load(pn.blk0, pn.blk1);
+      }
+      pa = pn;
     }
   }
   const int S = p.splits_int2 + p.splits_bf16;
@@ -1387,7 +1431,7 @@ __global__ __launch_bounds__(64) void decode_bf16(DecodeParams p) {
   const int sb = item % p.splits_bf16;
   const int c = (item / p.splits_bf16) % n_c;
   const int bk = item / p.splits_bf16 / n_c;
-  bf16_item(p, bk / p.n_kv, bk % p.n_kv, p.splits_int2 + sb, c);
+  bf16_item<false>(p, bk / p.n_kv, bk % p.n_kv, p.splits_int2 + sb, c);
 }
 
 // ---------------------------------------------------------------------------
@@ -1455,7 +1499,7 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeParams p) {
   // output projection), and so does the bf16 region's V
   const bool rot = SI > 0 && p.r_v;
   if (rot) stage_matrix256<kRvStride>(p.r_v + (int64_t)kv * kHeadDim * kHeadDim, rv);
-  if (p.bf16_in_combine && w < p.splits_bf16) bf16_item(p, b, kv, SI + w, 0);
+  if (p.bf16_in_combine && w < p.splits_bf16) bf16_item<true>(p, b, kv, SI + w, 0);
   __syncthreads();  // R_V staged; the bf16 partials written by this block are visible to it
   for (int h0 = 0; h0 < p.g; h0 += 4) {  // same trip count in every wavefront
     const int h = h0 + w;
