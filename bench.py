@@ -4,12 +4,10 @@ One step = one decode step for the whole batch: host region planning
 (oscar_plan_decode_step), then oscar_decode_step: re-quantisation of the
 tokens leaving the recent window and bf16 append of every request's new token
 (fused into the prologue kernel), and mixed-precision paged decode attention
-(prologue, INT2 kernel, split-K combine running the bf16 region first).
---unfused runs the same step with the writes as separate calls.  As in a
-serving loop, the host plans step s + 1 while the GPU runs step s, and the
-step's slot table (5 x batch int32) goes to the device on a copy stream.  The
-cache is resident in HBM before the timed region; the inputs of the steps are
-generated and uploaded beforehand (128 distinct sets, used in turn).
+(prologue, INT2 kernel, split-K combine running the bf16 region first).  --unfused runs
+the same step with the writes as separate calls.  The cache is resident in
+HBM before the timed region; the inputs of the steps are generated and
+uploaded beforehand (128 distinct sets, used in turn).
 
 Prints one JSON line.  value = KV tokens attended per second (summed context
 lengths of all requests and steps / wall time of the timed steps).
@@ -270,49 +268,32 @@ def main():
     tables = [to_dev_i32(i2_bt), to_dev_i32(bf_bt)]
     ctx_hist = []
 
-    # A serving loop plans step s + 1 on the host and sends its slots while the
-    # GPU runs step s: the 5 x B int32 of each step go over a copy stream one
-    # step ahead, and the step waits only for its own copy's event.
-    copy_stream = torch.cuda.Stream()
-    copied = [torch.cuda.Event() for _ in range(4)]
-    n_age_of = {}
-
-    def stage(st):
+    def step(st):
         n_age, changed = planner.step()
-        n_age_of[st] = n_age
         host_small[st].copy_(torch.from_numpy(planner.buf))
-        if changed:                             # block tables grow: rare, and ordered on the compute stream
+        dev_small[st].copy_(host_small[st], non_blocking=True)
+        if changed:
             i2_bt, bf_bt, _ = dc.tables(seqs, max_i2, max_bf)
             tables[0] = to_dev_i32(i2_bt)
             tables[1] = to_dev_i32(bf_bt)
-        with torch.cuda.stream(copy_stream):
-            dev_small[st].copy_(host_small[st], non_blocking=True)
-            copied[st % 4].record(copy_stream)
-        ctx_hist.append(planner.buf[4].astype(np.int64).copy())
-
-    def step(st):
-        torch.cuda.current_stream().wait_event(copied[st % 4])
-        n_age = n_age_of.pop(st)
         d = dev_small[st]
         si_ = st % n_in
         if args.unfused:
             if n_age:
                 K.oscar_requant_from_bf16(sh, dc.layer, dc.cache, d[2], d[3], n=B)
-            if bool((host_small[st][0] >= 0).any()):
+            if np.any(planner.buf[0] >= 0):
                 K.oscar_quant_write(sh, dc.layer, dc.cache, new_k_d[si_], new_v_d[si_], d[0], n=B)
             K.oscar_bf16_write(sh, dc.cache, new_k_d[si_], new_v_d[si_], d[1], n=B)
             K.oscar_decode_attn(sh, dc.layer, dc.cache, q_d[si_], tables[0], tables[1], d[4], out, ws, si, sb_step)
         else:
             K.oscar_decode_step(sh, dc.layer, dc.cache, new_k_d[si_], new_v_d[si_], d[:4], q_d[si_], tables[0],
                                 tables[1], d[4], out, ws, si, sb_step)
-        if st + 1 < n_steps:
-            stage(st + 1)                       # host planning of the next step overlaps this one on the GPU
+        ctx_hist.append(planner.buf[4].astype(np.int64).copy())
 
-    stage(0)
     for st in range(args.warmup):
         step(st)
     torch.cuda.synchronize()
-    del ctx_hist[:args.warmup]                  # the first timed step's entry stays (staged during warm-up)
+    ctx_hist.clear()
     K.oscar_profile_enable(True)
     t0 = time.perf_counter()
     for st in range(args.warmup, n_steps):
