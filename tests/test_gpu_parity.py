@@ -444,20 +444,22 @@ def test_full_size_stress_16x128k_sampled(group):
 
 
 @pytest.mark.parametrize("hq,hkv,group,sink,recent,scale_bits", [(8, 2, 32, 4, 32, 16), (12, 1, 64, 20, 48, 16),
-                                                                   (4, 1, 32, 4, 0, 16), (4, 2, 64, 64, 48, 8)])
+                                                                   (4, 1, 32, 4, 0, 16), (4, 2, 64, 64, 48, 8),
+                                                                   (16, 1, 32, 0, 16, 16), (4, 1, 64, 0, 0, 8)])
 def test_fused_decode_step(hq, hkv, group, sink, recent, scale_bits):
     """oscar_decode_step (writes fused into the decode's prologue kernel) against
     the separate write calls + oscar_decode_attn: identical cache bytes and bit-identical outputs after every step,
     through ring age-out, page crossings, sink growth and (recent = 0) new
-    tokens quantised straight to INT2; then the pages bit-exact and the output
-    within tolerance against the oracle."""
+    tokens quantised straight to INT2, with no sink region (sink = 0) and with
+    every position INT2 (sink = recent = 0); then the pages bit-exact and the
+    output within tolerance against the oracle."""
     from kv_cache_int2_amd.torch_cache import to_dev_bits, to_dev_i32
     w = synth.Workload("fused", 70 + hq + group, hq, hkv, 128, 1, 0, group=group, sink=sink, recent=recent,
                        outlier_scale=(40.0, 40.0), calib_tokens=512)
     _flush(f"case fused step hq={hq} hkv={hkv} G={group} sink={sink} recent={recent} scale_bits={scale_bits}")
     cal = _calibrate(w)
     sh = K.make_shape(n_q_heads=hq, n_kv_heads=hkv, group=group, sink=sink, recent=recent, scale_bits=scale_bits)
-    lens0 = [0, 3, sink + recent - 2, 200, 1001]
+    lens0 = [0, 3, max(sink + recent - 2, 1), 200, 1001]
     n_steps = 40
     B = len(lens0)
     caches = [DeviceCache(sh, cal.r_k, cal.r_v, cal.tau_k, cal.tau_v, 600, 64) for _ in range(2)]
