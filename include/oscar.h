@@ -33,8 +33,12 @@
  * Storage format of one (page, KV head) block, d channels, G channels per
  * group, NG = d / G, page_size = 16 tokens:
  *   INT2 block (2*(4*d + 64*NG) bytes: 1536 for d=128,G=32; 1280 for G=64):
- *     K codes  [16][d/4] bytes, token-major; channel j of token t sits in byte
- *              t*d/4 + j/4 at bits 2*(j%4).
+ *     K codes  [16][d/4] bytes, token-major; byte b of token t is t*d/4 + b,
+ *              and holds four 2-bit fields, field m at bits 2*m.  G = 64:
+ *              field m of byte b is channel 4*b + m.  G = 32: byte
+ *              b = 8*a + 4*w + i holds at field m the channel
+ *              64*w + 32*(m/2) + 8*a + 4*(m%2) + i (every field position of
+ *              the 4-byte word w of quarter a belongs to one group).
  *     K scale/zero  fp16 [16][NG][2] = (s, z) per token and group (token-major).
  *     V codes  [4][d] bytes by token quad: byte q*d + j holds channel j of
  *              tokens 4q..4q+3, token 4q+i at bits 2*i.

@@ -71,6 +71,9 @@ __device__ __forceinline__ i32x4 mfma_i8(u32x4 a, u32x4 b, i32x4 c) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, a), __builtin_bit_cast(i32x4, b), c, 0, 0,
                                                0);
 }
+__device__ __forceinline__ i32x4 mfma_i8_k32(u32x2 a, u32x2 b, i32x4 c) {
+  return __builtin_amdgcn_mfma_i32_16x16x32_i8(__builtin_bit_cast(long, a), __builtin_bit_cast(long, b), c, 0, 0, 0);
+}
 __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
                                                  0, 0, 0);
@@ -243,10 +246,11 @@ __device__ __forceinline__ void quantise_and_store(const DecodeParams& p, int kv
   const int slot = dst % kPage;
   uint8_t* blk = p.int2_w + (page * p.n_kv + kv) * (int64_t)L.bytes();
   if (t < 8) {
-    // K codes, token-major: 16 channels per word, channel 16t + e at bits 2e
+    // K codes, token-major: word t is word t%2 of quarter t/2; bits 2e hold
+    // field e%4 of byte e/4
     uint32_t w = 0u;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) w |= (uint32_t)sc.code[0][16 * t + e] << (2 * e);
+    for (int e = 0; e < 16; ++e) w |= (uint32_t)sc.code[0][k_code_channel<NG>(t >> 1, t & 1, e >> 2, e & 3)] << (2 * e);
     *(uint32_t*)(blk + L.k_codes() + slot * 32 + 4 * t) = w;
   } else if (t >= 16 && t < 16 + NG) {
     const int gm = t - 16;
@@ -301,7 +305,14 @@ __device__ void step_writes(const DecodeParams& p, int b, int kv, const float* r
 // q~ (qi: [head][channel], g heads) and its scale exponent sq, for `tiles`
 // 16-row tiles (rows (head, group); rows past the g heads get zero digits):
 // aux = [logit factor 2^-sq / 2, 2 Qbar per row], then the int8 digits of 2Q
-// as MFMA A operands, words ((((tile*3 + digit)*2 + kstep)*64 + lane)*4 + reg).
+// as MFMA A operands (digit 0 the most significant).
+//  - 32-channel groups: one 16x16x32 MFMA per group, rows (head, digit) of the
+//    tile's four heads (digit 3: zero), words (((tile*4 + group)*64 + lane)*2
+//    + reg); byte i of reg j of lane quad a is channel 8a + 4j + i of the group
+//    (the key fields that (word >> 2m) & 0x03030303 delivers).
+//  - 64-channel groups: digit chains of 16x16x64 MFMAs over rows (head, group),
+//    words ((((tile*3 + digit)*2 + kstep)*64 + lane)*4 + reg), byte i of reg r
+//    of lane quad a in k-step ks is channel 32a + 16ks + 4i + r.
 // Called by all 256 threads after qi is complete.
 template <int NG>
 __device__ __forceinline__ void write_q_operands(const DecodeParams& p, int bk, int tiles, int g,
@@ -325,6 +336,29 @@ __device__ __forceinline__ void write_q_operands(const DecodeParams& p, int bk, 
     if (part == 0) aux[1 + row] = 2.0f * (float)sum;
   }
   uint32_t* qb = p.qb + (int64_t)bk * tiles * 3 * 2 * 64 * 4;
+  // balanced int8 digits of 2Q: 2Q = d0 2^16 + d1 2^8 + d2
+  auto digit_of = [&](int h, int ch, int digit) {
+    const int q = 2 * qi[h][ch];
+    const int d2 = ((q + 128) & 255) - 128;
+    const int q1 = (q - d2) >> 8;
+    const int d1 = ((q1 + 128) & 255) - 128;
+    const int d0 = (q1 - d1) >> 8;
+    return digit == 0 ? d0 : (digit == 1 ? d1 : d2);
+  };
+  if constexpr (NG == 4) {
+    for (int w = t; w < tiles * 4 * 64 * 2; w += 256) {
+      const int j = w & 1, lane = (w >> 1) & 63, gam = (w >> 7) & 3, ct = w >> 9;
+      const int ln = lane & 15, qd = lane >> 4;
+      const int h = 4 * ct + (ln >> 2), digit = ln & 3;
+      uint32_t word = 0;
+      if (h < g && digit < 3) {
+        for (int byte = 0; byte < 4; ++byte)
+          word |= (uint32_t)(digit_of(h, 32 * gam + 8 * qd + 4 * j + byte, digit) & 0xff) << (8 * byte);
+      }
+      qb[w] = word;
+    }
+    return;
+  }
   for (int w = t; w < tiles * 3 * 2 * 64 * 4; w += 256) {
     const int reg = w & 3, lane = (w >> 2) & 63, ks = (w >> 8) & 1, rest = w >> 9;
     const int digit = rest % 3, ct = rest / 3;
@@ -333,15 +367,7 @@ __device__ __forceinline__ void write_q_operands(const DecodeParams& p, int bk, 
     uint32_t word = 0;
     for (int byte = 0; byte < 4; ++byte) {
       const int ch = 32 * qd + 16 * ks + 4 * byte + reg;
-      int dv = 0;
-      if (h < g && ch / G == gam) {
-        const int q = 2 * qi[h][ch];
-        const int d2 = ((q + 128) & 255) - 128;
-        const int q1 = (q - d2) >> 8;
-        const int d1 = ((q1 + 128) & 255) - 128;
-        const int d0 = (q1 - d1) >> 8;
-        dv = digit == 0 ? d0 : (digit == 1 ? d1 : d2);
-      }
+      const int dv = h < g && ch / G == gam ? digit_of(h, ch, digit) : 0;
       word |= (uint32_t)(dv & 0xff) << (8 * byte);
     }
     qb[w] = word;
@@ -392,8 +418,9 @@ __device__ __forceinline__ int q_scale_exponent(float mx) {
 // ---------------------------------------------------------------------------
 // prologue: q R_K operands
 // ---------------------------------------------------------------------------
-// Words per (request, KV head): A digits of 2Q ((((ct*3 + digit)*2 + kstep)*64 + lane)*4 + reg),
-// then aux floats [1 + 16*CT]: logit factor 2^-sq / 2, per row 2*Qbar (float).
+// Words per (request, KV head): A digits of 2Q (write_q_operands gives their
+// order; 1536 words per row tile reserved), then aux floats [1 + 16*CT]: logit
+// factor 2^-sq / 2, per row 2*Qbar (float).
 // WRITE: the decode-step writes come first.
 template <int NG, int MB, int CT, bool WRITE>
 __global__ __launch_bounds__(256) void decode_prologue(DecodeParams p) {
@@ -545,7 +572,11 @@ struct Int2State {
 
 template <int NG, int CT>
 struct Int2Const {
-  u32x4 qa[CT][3][2];  // digits of 2Q: A operand, rows 16ct + ln
+  // digits of 2Q as A operands: 32-channel groups: qg[ct][group], rows
+  // (head 4ct + ln/4, digit ln%4); 64-channel groups: qa[ct][digit][kstep],
+  // rows 16ct + ln = (head, group)
+  u32x2 qg[NG == 4 ? CT : 1][4];
+  u32x4 qa[NG == 4 ? 1 : CT][3][2];
   float qbar2[CT][4];  // 2 Qbar of those rows
   float kfac, ikfac;   // raw logit -> log2 units, and its inverse (powers of two)
   float lpf;           // log2(pscale 4^-(ln % 4)): P' factor of the token this lane writes
@@ -822,14 +853,28 @@ __device__ __forceinline__ void int2_pair(const Src& src, int lp0, int p_end, in
     for (int ks = 0; ks < 2; ++ks) av[ks] = SH ? ops[(2 * t + ks) * 64 + lane] : k_operand(DK.kc[t][ks]);
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
-      // digit chains feed each other: acc <- (acc << 8) + sum d_k c; every
-      // partial value is an exact integer below 2^31 in magnitude
-      i32x4 cd = i32x4{0, 0, 0, 0};
+      // cd[r]: sum_j 2Q_j c_j of row 16ct + 4qd + r = (head, group), token ln;
+      // every partial value is an exact integer below 2^31 in magnitude
+      i32x4 cd;
+      if constexpr (NG == 4) {
+        // one MFMA per group: registers 2(gam%2), +1 of word gam/2 are its
+        // codes; this lane receives the three digit sums of head qd
 #pragma unroll
-      for (int d = 0; d < 3; ++d) {
-        if (d > 0) cd = cd << 8;
+        for (int gam = 0; gam < 4; ++gam) {
+          const u32x4& b4 = av[gam >> 1];
+          const u32x2 bq = (gam & 1) ? u32x2{b4[2], b4[3]} : u32x2{b4[0], b4[1]};
+          const i32x4 ds = mfma_i8_k32(K.qg[ct][gam], bq, i32x4{0, 0, 0, 0});
+          cd[gam] = (((ds[0] << 8) + ds[1]) << 8) + ds[2];
+        }
+      } else {
+        // digit chains feed each other: acc <- (acc << 8) + sum d_k c
+        cd = i32x4{0, 0, 0, 0};
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) cd = mfma_i8(K.qa[ct][d][ks], av[ks], cd);
+        for (int d = 0; d < 3; ++d) {
+          if (d > 0) cd = cd << 8;
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) cd = mfma_i8(K.qa[ct][d][ks], av[ks], cd);
+        }
       }
 #pragma unroll
       for (int hh = 0; hh < HPL; ++hh) {
@@ -998,13 +1043,19 @@ __device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float
     const int p_end = min(min(first + n_pages, p_begin + pps), p.max_int2_pages);
     if (p_begin < p_end) {
       Int2Const<NG, CT> K;
-      const u32x4* qb = (const u32x4*)(p.qb + (int64_t)bk * kTiles * 3 * 2 * 64 * 4);
+      const uint32_t* qb = p.qb + (int64_t)bk * kTiles * 3 * 2 * 64 * 4;
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
+        if constexpr (NG == 4) {
 #pragma unroll
-        for (int d = 0; d < 3; ++d)
+          for (int gi = 0; gi < 4; ++gi) K.qg[ct][gi] = ((const u32x2*)qb)[((t0 + ct) * 4 + gi) * 64 + lane];
+        } else {
 #pragma unroll
-          for (int ks = 0; ks < 2; ++ks) K.qa[ct][d][ks] = qb[(((t0 + ct) * 3 + d) * 2 + ks) * 64 + lane];
+          for (int d = 0; d < 3; ++d)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+              K.qa[ct][d][ks] = ((const u32x4*)qb)[(((t0 + ct) * 3 + d) * 2 + ks) * 64 + lane];
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) K.qbar2[ct][r] = aux[1 + 16 * (t0 + ct) + 4 * qd + r];
       }

@@ -23,6 +23,18 @@ struct Int2Layout {
 };
 constexpr int kBf16BlockBytes = 4 * kPage * kHeadDim;
 
+// K codes: a token's 32 bytes are four 8-byte quarters a (one per lane quad of
+// the attention kernel), each two 32-bit words w; byte i of a word holds four
+// 2-bit fields, field m at bits 2m.  This gives the channel in field m of byte
+// i of word w of quarter a.  With 32-channel groups (ng = 4) field m of a word
+// belongs to group 2w + m/2, so (word >> 2m) & 0x03030303 is four int8 codes
+// of one group: channel 64w + 32(m/2) + 8a + 4(m%2) + i.  With 64-channel
+// groups channels run consecutively, four per byte: 32a + 16w + 4i + m.
+template <int NG>
+__host__ __device__ constexpr int k_code_channel(int a, int w, int i, int m) {
+  return NG == 4 ? 64 * w + 32 * (m >> 1) + 8 * a + 4 * (m & 1) + i : 32 * a + 16 * w + 4 * i + m;
+}
+
 struct QuantParams {
   const uint16_t* k_src;      // dense bf16 [n][n_kv][d]            (mode 0)
   const uint16_t* v_src;
@@ -69,7 +81,7 @@ struct DecodeParams {
   int bf16_in_combine;        // bf16 splits (<= 4) run by the combine kernel's wavefronts
   float p_scale_exp;          // P' is scaled by 2^p_scale_exp before fp16 rounding
   // workspace carve-up
-  uint32_t* qb;               // [B*n_kv][ct][3 digits][2 k-steps][64 lanes][4] int8x4 words: digits of 2Q
+  uint32_t* qb;               // [B*n_kv][ct][1536] int8x4 words: digits of 2Q as MFMA A operands
   float* qaux;                // [B*n_kv][1 + 16*ct]: logit factor, 2 Qbar per row
   float* partial;             // [B][Hq][splits][2 + d]: m (log2), l, acc
   float* out;                 // [B][Hq][d]

@@ -170,7 +170,8 @@ __global__ __launch_bounds__(512) void quant_write_kernel(QuantParams p) {
     }
   }
   if (!isv) {
-    // K codes: lane -> (token lane/4, bytes 8*(lane%4) .. +7)
+    // K codes: lane -> (token lane/4, quarter lane%4: bytes 8*(lane%4) .. +7);
+    // bits 2e of word w hold field e%4 of byte e/4
     const int t = lane >> 2, part = lane & 3;
     if (dst[t] >= 0) {
       const int64_t page = dst[t] / kPage;
@@ -178,7 +179,10 @@ __global__ __launch_bounds__(512) void quant_write_kernel(QuantParams p) {
       uint8_t* blk = pages + (page * p.n_kv + kv) * blk_bytes;
       uint32_t w[2] = {0u, 0u};
 #pragma unroll
-      for (int j = 0; j < 32; ++j) w[j >> 4] |= (uint32_t)codes[t][32 * part + j] << (2 * (j & 15));
+      for (int wi = 0; wi < 2; ++wi)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          w[wi] |= (uint32_t)codes[t][k_code_channel<NG>(part, wi, e >> 2, e & 3)] << (2 * e);
       *(uint2*)(blk + L.k_codes() + slot * 32 + 8 * part) = make_uint2(w[0], w[1]);
     }
   } else {

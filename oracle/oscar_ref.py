@@ -446,8 +446,9 @@ def prefill_attention(q_bits: np.ndarray, st: StoredRequest, cal: LayerCalibrati
 # from the format's definition so stored bytes can be compared exactly.
 #
 # INT2 page block, d channels, NG = d / G groups, 16 tokens:
-#   [0, 16*d/4)          K codes, token-major: token t owns d/4 bytes;
-#                        channel j sits in byte j//4 at bits 2*(j%4).
+#   [0, 16*d/4)          K codes, token-major: token t owns d/4 bytes, each
+#                        byte four 2-bit fields (field m at bits 2*m); which
+#                        channel each field holds is k_code_channel below.
 #   next 16*NG*4 bytes   K scale/zero as fp16 pairs, token-major [16][NG][(s, z)].
 #   next 16*d/4 bytes    V codes, [4][d] bytes by token quad: byte [q][j]
 #                        holds channel j of tokens 4q..4q+3, token 4q+i at
@@ -456,6 +457,23 @@ def prefill_attention(q_bits: np.ndarray, st: StoredRequest, cal: LayerCalibrati
 # BF16 page block: K as [16][d] bf16 (token-major), then V as [d][16] bf16
 # (channel-major).
 # ---------------------------------------------------------------------------
+
+def k_code_channel(d: int, group: int) -> np.ndarray:
+    """Channel held by each 2-bit field of a token's K-code bytes: entry
+    4*b + m is the channel at bits 2*m of byte b.
+
+    d = 128, G = 32: byte b = 8*a + 4*w + i (quarter a, word w, byte i of the
+    word) holds at field m the channel 64*w + 32*(m // 2) + 8*a + 4*(m % 2) + i,
+    so each field position of a word belongs to one group (fields 0, 1 to group
+    2*w, fields 2, 3 to group 2*w + 1).  Otherwise channels run consecutively,
+    channel j in byte j // 4 at field j % 4."""
+    field = np.arange(d)
+    if d == 128 and group == 32:
+        b, m = field // 4, field % 4
+        a, w, i = b // 8, (b // 4) % 2, b % 4
+        return 64 * w + 32 * (m // 2) + 8 * a + 4 * (m % 2) + i
+    return field
+
 
 def int2_block_bytes(d: int, group: int, scale_bits: int = 16) -> int:
     return 2 * (PAGE * d // 4 + PAGE * (d // group) * scale_bits // 4)
@@ -480,9 +498,11 @@ def pack_int2_block(kc, ks, kz, vc, vs, vz) -> np.ndarray:
     vc = np.asarray(vc, np.uint8)
     t, d = kc.shape
     assert t == PAGE
+    ng = np.asarray(ks).shape[1]
+    kf = kc[:, k_code_channel(d, d // ng)]          # field 4*b + m of each token
     kbytes = np.zeros((PAGE, d // 4), np.uint8)
-    for i in range(4):
-        kbytes |= (kc[:, i::4] << (2 * i)).astype(np.uint8)
+    for m in range(4):
+        kbytes |= (kf[:, m::4] << (2 * m)).astype(np.uint8)
     vbytes = np.zeros((4, d), np.uint8)
     for q in range(4):
         for i in range(4):
@@ -499,9 +519,11 @@ def unpack_int2_block(buf: np.ndarray, d: int, group: int, scale_bits: int = 16)
     nsz = PAGE * ng * scale_bits // 4
     mt = np.float16 if scale_bits == 16 else np.uint8
     kb = buf[:nc].reshape(PAGE, d // 4)
+    kf = np.zeros((PAGE, d), np.uint8)
+    for m in range(4):
+        kf[:, m::4] = (kb >> (2 * m)) & 3
     kc = np.zeros((PAGE, d), np.uint8)
-    for i in range(4):
-        kc[:, i::4] = (kb >> (2 * i)) & 3
+    kc[:, k_code_channel(d, group)] = kf
     o = nc
     ksz = buf[o:o + nsz].copy().view(mt).reshape(PAGE, ng, 2).transpose(1, 0, 2)
     o += nsz

@@ -304,7 +304,10 @@ def test_p7_int2_block_layout_by_hand():
     vs[7, 2] = np.float16(5.0)
     blk = O.pack_int2_block(kc, ks, kz, vc, vs, kz)
     assert blk.size == O.int2_block_bytes(d, group) == 1536
-    assert np.all(blk[:512] == 0xE4)                                 # 0b11_10_01_00
+    # G = 32 K fields: byte 8a + 4w + i holds channels = i (mod 4) in all four
+    # fields, so every byte repeats its position mod 4: 0x00, 0x55, 0xAA, 0xFF
+    kb = blk[:512].reshape(16, 32)
+    assert np.all(kb == (np.arange(32) % 4 * 0x55).astype(np.uint8)[None, :])
     ksz = blk[512:768].view(np.float16)                              # K: [token][group][(s, z)]
     assert ksz[(7 * 4 + 2) * 2] == 3.0 and ksz[(7 * 4 + 2) * 2 + 1] == -1.0
     assert np.count_nonzero(ksz[0::2] == 0.5) == 63
@@ -316,6 +319,38 @@ def test_p7_int2_block_layout_by_hand():
     back = O.unpack_int2_block(blk, d, group)
     for a, b in zip(back, (kc, ks, kz, vc, vs, kz)):
         assert np.array_equal(a, b)
+
+
+def test_p7_k_code_fields_by_hand():
+    """G = 32 K-code fields, positions worked out by hand from the word layout
+    (quarter a, word w, byte i, field m -> channel 64w + 32(m//2) + 8a + 4(m%2) + i)."""
+    d, group = 128, 32
+    spots = [  # (token, channel, code, byte, field)
+        (5, 37, 3, 1, 3),      # group 1: w 0, m//2 1; 5 = 8*0 + 4*1 + 1
+        (9, 100, 2, 4, 3),     # group 3: w 1, m//2 1; 4 = 8*0 + 4*1 + 0
+        (0, 10, 1, 10, 0),     # group 0: w 0, m//2 0; 10 = 8*1 + 4*0 + 2
+        (15, 127, 3, 31, 3),   # group 3: w 1, m//2 1; 31 = 8*3 + 4*1 + 3
+        (2, 64, 1, 4, 0),      # group 2: w 1, m//2 0; 0 = 8*0 + 4*0 + 0
+    ]
+    z16 = np.zeros((16, 4), np.float16)
+    for t, ch, c, b, m in spots:
+        kc = np.zeros((16, d), np.uint8)
+        kc[t, ch] = c
+        kb = O.pack_int2_block(kc, z16, z16, np.zeros((16, d), np.uint8), z16, z16)[:512].reshape(16, 32)
+        assert kb[t, b] == c << (2 * m) and np.count_nonzero(kb) == 1
+        assert O.unpack_int2_block(O.pack_int2_block(kc, z16, z16, kc, z16, z16), d, group)[0][t, ch] == c
+    # what the layout is for: shifting a quarter's word right by 2m and masking
+    # each byte's low two bits yields four codes of ONE group, and the two
+    # field pairs of the four quarters cover each group's 32 channels once
+    ch = O.k_code_channel(d, group).reshape(4, 2, 4, 4)  # [quarter a][word w][byte i][field m]
+    for w in range(2):
+        for m in range(4):
+            assert set((ch[:, w, :, m] // group).ravel()) == {2 * w + m // 2}
+        for half in range(2):
+            cover = ch[:, w, :, 2 * half:2 * half + 2].ravel()
+            assert sorted(cover) == list(range(32 * (2 * w + half), 32 * (2 * w + half) + 32))
+    # G = 64 keeps consecutive channels
+    assert np.array_equal(O.k_code_channel(d, 64), np.arange(d))
 
 
 def test_p7_int2_block_roundtrip_all_bytes():
@@ -333,7 +368,7 @@ def test_p7_int2_block_roundtrip_all_bytes():
     blk = np.zeros(1536, np.uint8)
     blk[:256] = allb
     blk[256:512] = allb[::-1]
-    kc = O.unpack_int2_block(blk, 128, 32)[0]
+    kc = O.unpack_int2_block(blk, 128, 64)[0]                          # consecutive fields
     for b in range(256):
         t, j0 = divmod(b, 32)
         assert [int(kc[t, 4 * j0 + i]) for i in range(4)] == [(b >> (2 * i)) & 3 for i in range(4)]
