@@ -305,14 +305,13 @@ __device__ void step_writes(const DecodeParams& p, int b, int kv, const float* r
 // q~ (qi: [head][channel], g heads) and its scale exponent sq, for `tiles`
 // 16-row tiles (rows (head, group); rows past the g heads get zero digits):
 // aux = [logit factor 2^-sq / 2, 2 Qbar per row], then the int8 digits of 2Q
-// as MFMA A operands (digit 0 the most significant).
-//  - 32-channel groups: one 16x16x32 MFMA per group, rows (head, digit) of the
-//    tile's four heads (digit 3: zero), words (((tile*4 + group)*64 + lane)*2
-//    + reg); byte i of reg j of lane quad a is channel 8a + 4j + i of the group
-//    (the key fields that (word >> 2m) & 0x03030303 delivers).
-//  - 64-channel groups: digit chains of 16x16x64 MFMAs over rows (head, group),
-//    words ((((tile*3 + digit)*2 + kstep)*64 + lane)*4 + reg), byte i of reg r
-//    of lane quad a in k-step ks is channel 32a + 16ks + 4i + r.
+// as MFMA A operands (digit 0 the most significant).  A tile of 16/NG heads
+// takes four MFMAs per page, unit u = (head quad hq, group gam), u = hq NG +
+// gam, each with K = the group's G channels and rows (head 4hq + ln/4 of the
+// tile, digit ln%4; digit 3 is zero): words ((tile*4 + u)*64 + lane)*(8/NG) +
+// reg, 8/NG registers per lane (16x16x32 MFMA at G = 32, 16x16x64 at G = 64).
+// Byte i of reg j of lane quad a is channel G gam + (G/4) a + 4j + i: the key
+// fields that (word >> 2m) & 0x03030303 delivers for that group.
 // Called by all 256 threads after qi is complete.
 template <int NG>
 __device__ __forceinline__ void write_q_operands(const DecodeParams& p, int bk, int tiles, int g,
@@ -336,39 +335,24 @@ __device__ __forceinline__ void write_q_operands(const DecodeParams& p, int bk, 
     if (part == 0) aux[1 + row] = 2.0f * (float)sum;
   }
   uint32_t* qb = p.qb + (int64_t)bk * tiles * 3 * 2 * 64 * 4;
-  // balanced int8 digits of 2Q: 2Q = d0 2^16 + d1 2^8 + d2
-  auto digit_of = [&](int h, int ch, int digit) {
-    const int q = 2 * qi[h][ch];
-    const int d2 = ((q + 128) & 255) - 128;
-    const int q1 = (q - d2) >> 8;
-    const int d1 = ((q1 + 128) & 255) - 128;
-    const int d0 = (q1 - d1) >> 8;
-    return digit == 0 ? d0 : (digit == 1 ? d1 : d2);
-  };
-  if constexpr (NG == 4) {
-    for (int w = t; w < tiles * 4 * 64 * 2; w += 256) {
-      const int j = w & 1, lane = (w >> 1) & 63, gam = (w >> 7) & 3, ct = w >> 9;
-      const int ln = lane & 15, qd = lane >> 4;
-      const int h = 4 * ct + (ln >> 2), digit = ln & 3;
-      uint32_t word = 0;
-      if (h < g && digit < 3) {
-        for (int byte = 0; byte < 4; ++byte)
-          word |= (uint32_t)(digit_of(h, 32 * gam + 8 * qd + 4 * j + byte, digit) & 0xff) << (8 * byte);
-      }
-      qb[w] = word;
-    }
-    return;
-  }
-  for (int w = t; w < tiles * 3 * 2 * 64 * 4; w += 256) {
-    const int reg = w & 3, lane = (w >> 2) & 63, ks = (w >> 8) & 1, rest = w >> 9;
-    const int digit = rest % 3, ct = rest / 3;
+  constexpr int kRegs = 8 / NG;
+  for (int w = t; w < tiles * 4 * 64 * kRegs; w += 256) {
+    const int j = w % kRegs, lane = (w / kRegs) & 63, u = (w / (kRegs * 64)) & 3, ct = w / (kRegs * 256);
     const int ln = lane & 15, qd = lane >> 4;
-    const int col = 16 * ct + ln, h = col / NG, gam = col % NG;
+    const int hq = u / NG, gam = u % NG;
+    const int h = (16 / NG) * ct + 4 * hq + (ln >> 2), digit = ln & 3;
     uint32_t word = 0;
-    for (int byte = 0; byte < 4; ++byte) {
-      const int ch = 32 * qd + 16 * ks + 4 * byte + reg;
-      const int dv = h < g && ch / G == gam ? digit_of(h, ch, digit) : 0;
-      word |= (uint32_t)(dv & 0xff) << (8 * byte);
+    if (h < g && digit < 3) {
+      for (int byte = 0; byte < 4; ++byte) {
+        // balanced int8 digits of 2Q: 2Q = d0 2^16 + d1 2^8 + d2
+        const int q = 2 * qi[h][G * gam + (G / 4) * qd + 4 * j + byte];
+        const int d2 = ((q + 128) & 255) - 128;
+        const int q1 = (q - d2) >> 8;
+        const int d1 = ((q1 + 128) & 255) - 128;
+        const int d0 = (q1 - d1) >> 8;
+        const int dv = digit == 0 ? d0 : (digit == 1 ? d1 : d2);
+        word |= (uint32_t)(dv & 0xff) << (8 * byte);
+      }
     }
     qb[w] = word;
   }
@@ -572,11 +556,9 @@ struct Int2State {
 
 template <int NG, int CT>
 struct Int2Const {
-  // digits of 2Q as A operands: 32-channel groups: qg[ct][group], rows
-  // (head 4ct + ln/4, digit ln%4); 64-channel groups: qa[ct][digit][kstep],
-  // rows 16ct + ln = (head, group)
-  u32x2 qg[NG == 4 ? CT : 1][4];
-  u32x4 qa[NG == 4 ? 1 : CT][3][2];
+  // digits of 2Q as A operands of unit u = (head quad u / NG, group u % NG),
+  // rows (head, digit)
+  typename std::conditional<NG == 4, u32x2, u32x4>::type qa[CT][4];
   float qbar2[CT][4];  // 2 Qbar of those rows
   float kfac, ikfac;   // raw logit -> log2 units, and its inverse (powers of two)
   float lpf;           // log2(pscale 4^-(ln % 4)): P' factor of the token this lane writes
@@ -838,7 +820,7 @@ __device__ __forceinline__ void int2_pair(const Src& src, int lp0, int p_end, in
 #pragma unroll
       for (int hh = 0; hh < HPL; ++hh) {
         if constexpr (EDGE) {
-          const int h = (16 / NG) * (t0 + ct) + (4 / NG) * qd + hh;
+          const int h = (16 / NG) * (t0 + ct) + 4 * hh + qd;
           seen[t][ct][hh] = valid && later <= h;
         } else {
           seen[t][ct][hh] = true;
@@ -853,28 +835,24 @@ __device__ __forceinline__ void int2_pair(const Src& src, int lp0, int p_end, in
     for (int ks = 0; ks < 2; ++ks) av[ks] = SH ? ops[(2 * t + ks) * 64 + lane] : k_operand(DK.kc[t][ks]);
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
-      // cd[r]: sum_j 2Q_j c_j of row 16ct + 4qd + r = (head, group), token ln;
-      // every partial value is an exact integer below 2^31 in magnitude
+      // cd[u]: sum_j 2Q_j c_j of head 4hq + qd of the tile and group gam (u =
+      // hq NG + gam), token ln: one MFMA per unit, whose rows (head, digit)
+      // give this lane the three digit sums of that head.  Every partial
+      // value is an exact integer below 2^31 in magnitude.
       i32x4 cd;
-      if constexpr (NG == 4) {
-        // one MFMA per group: registers 2(gam%2), +1 of word gam/2 are its
-        // codes; this lane receives the three digit sums of head qd
 #pragma unroll
-        for (int gam = 0; gam < 4; ++gam) {
+      for (int u = 0; u < 4; ++u) {
+        const int gam = u % NG;
+        i32x4 ds;
+        if constexpr (NG == 4) {
+          // group gam: fields 2(gam%2), +1 of word gam/2
           const u32x4& b4 = av[gam >> 1];
           const u32x2 bq = (gam & 1) ? u32x2{b4[2], b4[3]} : u32x2{b4[0], b4[1]};
-          const i32x4 ds = mfma_i8_k32(K.qg[ct][gam], bq, i32x4{0, 0, 0, 0});
-          cd[gam] = (((ds[0] << 8) + ds[1]) << 8) + ds[2];
+          ds = mfma_i8_k32(K.qa[ct][u], bq, i32x4{0, 0, 0, 0});
+        } else {
+          ds = mfma_i8(K.qa[ct][u], av[gam], i32x4{0, 0, 0, 0});  // group gam: word gam
         }
-      } else {
-        // digit chains feed each other: acc <- (acc << 8) + sum d_k c
-        cd = i32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int d = 0; d < 3; ++d) {
-          if (d > 0) cd = cd << 8;
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks) cd = mfma_i8(K.qa[ct][d][ks], av[ks], cd);
-        }
+        cd[u] = (((ds[0] << 8) + ds[1]) << 8) + ds[2];
       }
 #pragma unroll
       for (int hh = 0; hh < HPL; ++hh) {
@@ -916,16 +894,29 @@ __device__ __forceinline__ void int2_pair(const Src& src, int lp0, int p_end, in
           S.l_run[ct][hh] *= alpha[hh];
         }
       }
+      // value-accumulator row 16ct + 4qd + r belongs to head (4qd + r) / NG of
+      // the tile: at NG = 4 head qd, this lane's own; at NG = 2 head 2qd + r/2,
+      // whose alpha quad (2qd + r/2) % 4 holds as entry (2qd + r/2) / 4
+      float ar[2] = {alpha[0], alpha[0]};
+      if constexpr (HPL == 2) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int hl = 2 * qd + e;
+          const float x0 = __shfl(alpha[0], 16 * (hl & 3)), x1 = __shfl(alpha[1], 16 * (hl & 3));
+          ar[e] = (hl >> 2) ? x1 : x0;
+        }
+      }
 #pragma unroll
       for (int kt = 0; kt < 8; ++kt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) S.acc[ct][kt][r] *= alpha[r / NG];
-      // value-operand row 16ct + ln belongs to head (16ct + ln) / NG, whose
-      // alpha is held by quad ln / 4, entry (ln % 4) / NG
-      float az = __shfl(alpha[0], 16 * (ln >> 2));
+        for (int r = 0; r < 4; ++r) S.acc[ct][kt][r] *= ar[r >> 1];
+      // value-operand row 16ct + ln belongs to head ln / NG of the tile, i.e.
+      // 4hh + qd with qd = (ln / NG) % 4, hh = ln / (4 NG): its alpha is held
+      // by quad qd, entry hh
+      float az = __shfl(alpha[0], 16 * ((ln / NG) & 3));
       if constexpr (HPL == 2) {
-        const float az1 = __shfl(alpha[1], 16 * (ln >> 2));
-        az = ((ln >> 1) & 1) ? az1 : az;
+        const float az1 = __shfl(alpha[1], 16 * ((ln / NG) & 3));
+        az = (ln >> 3) ? az1 : az;
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) S.zz[ct][r] *= az;
@@ -944,7 +935,7 @@ __device__ __forceinline__ void int2_pair(const Src& src, int lp0, int p_end, in
   for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
     for (int hh = 0; hh < HPL; ++hh) {
-      const int h = (16 * ct + 4 * qd + hh * NG) / NG;
+      const int h = (16 / NG) * ct + 4 * hh + qd;
 #pragma unroll
       for (int t = 0; t < 2; ++t) p_lds[(2 * h + t) * kPage + ln] = pr[t][ct][hh];
     }
@@ -1046,18 +1037,13 @@ __device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float
       const uint32_t* qb = p.qb + (int64_t)bk * kTiles * 3 * 2 * 64 * 4;
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
-        if constexpr (NG == 4) {
+        using QA = typename std::conditional<NG == 4, u32x2, u32x4>::type;
 #pragma unroll
-          for (int gi = 0; gi < 4; ++gi) K.qg[ct][gi] = ((const u32x2*)qb)[((t0 + ct) * 4 + gi) * 64 + lane];
-        } else {
+        for (int u = 0; u < 4; ++u) K.qa[ct][u] = ((const QA*)qb)[((t0 + ct) * 4 + u) * 64 + lane];
+        // 2 Qbar of (head 4hh + qd of the tile, group gg), r = hh NG + gg
 #pragma unroll
-          for (int d = 0; d < 3; ++d)
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-              K.qa[ct][d][ks] = ((const u32x4*)qb)[(((t0 + ct) * 3 + d) * 2 + ks) * 64 + lane];
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) K.qbar2[ct][r] = aux[1 + 16 * (t0 + ct) + 4 * qd + r];
+        for (int r = 0; r < 4; ++r)
+          K.qbar2[ct][r] = aux[1 + 16 * (t0 + ct) + NG * (4 * (r / NG) + qd) + r % NG];
       }
       K.kfac = aux[0];
       K.ikfac = 1.0f / K.kfac;
@@ -1217,7 +1203,7 @@ __device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float
     for (int hh = 0; hh < HPL; ++hh) {
       const float lpf = p.p_scale_exp - (float)(2 * (ln & 3));
       const float l = row_sum16(S.l_run[ct][hh] * exp2f(-lpf));
-      const int h = (16 * (t0 + ct) + 4 * qd + hh * NG) / NG;
+      const int h = (16 / NG) * (t0 + ct) + 4 * hh + qd;
       if (ln == 0 && h < p.g) {
         float* dst = p.partial + (((int64_t)b * p.n_q + kv * p.g + h) * Ssp + split) * kPartialStride;
         dst[0] = lpf - S.moff[ct][hh];  // -inf when this split saw no token

@@ -26,13 +26,14 @@ constexpr int kBf16BlockBytes = 4 * kPage * kHeadDim;
 // K codes: a token's 32 bytes are four 8-byte quarters a (one per lane quad of
 // the attention kernel), each two 32-bit words w; byte i of a word holds four
 // 2-bit fields, field m at bits 2m.  This gives the channel in field m of byte
-// i of word w of quarter a.  With 32-channel groups (ng = 4) field m of a word
-// belongs to group 2w + m/2, so (word >> 2m) & 0x03030303 is four int8 codes
-// of one group: channel 64w + 32(m/2) + 8a + 4(m%2) + i.  With 64-channel
-// groups channels run consecutively, four per byte: 32a + 16w + 4i + m.
+// i of word w of quarter a.  Every field position of a word belongs to one
+// group, so (word >> 2m) & 0x03030303 is four int8 codes of one group:
+//   32-channel groups (ng = 4): channel 64w + 32(m/2) + 8a + 4(m%2) + i
+//     (fields 0, 1: group 2w; fields 2, 3: group 2w + 1);
+//   64-channel groups (ng = 2): channel 64w + 16a + 4m + i (word w: group w).
 template <int NG>
 __host__ __device__ constexpr int k_code_channel(int a, int w, int i, int m) {
-  return NG == 4 ? 64 * w + 32 * (m >> 1) + 8 * a + 4 * (m & 1) + i : 32 * a + 16 * w + 4 * i + m;
+  return NG == 4 ? 64 * w + 32 * (m >> 1) + 8 * a + 4 * (m & 1) + i : 64 * w + 16 * a + 4 * m + i;
 }
 
 struct QuantParams {

@@ -462,16 +462,20 @@ def k_code_channel(d: int, group: int) -> np.ndarray:
     """Channel held by each 2-bit field of a token's K-code bytes: entry
     4*b + m is the channel at bits 2*m of byte b.
 
-    d = 128, G = 32: byte b = 8*a + 4*w + i (quarter a, word w, byte i of the
-    word) holds at field m the channel 64*w + 32*(m // 2) + 8*a + 4*(m % 2) + i,
-    so each field position of a word belongs to one group (fields 0, 1 to group
-    2*w, fields 2, 3 to group 2*w + 1).  Otherwise channels run consecutively,
-    channel j in byte j // 4 at field j % 4."""
+    d = 128: byte b = 8*a + 4*w + i is byte i of word w of quarter a, and
+    every field position of a word belongs to one group:
+      G = 32: field m holds channel 64*w + 32*(m // 2) + 8*a + 4*(m % 2) + i
+              (fields 0, 1: group 2*w; fields 2, 3: group 2*w + 1);
+      G = 64: field m holds channel 64*w + 16*a + 4*m + i (word w: group w).
+    Other shapes: channels run consecutively, channel j in byte j // 4 at
+    field j % 4."""
     field = np.arange(d)
+    b, m = field // 4, field % 4
+    a, w, i = b // 8, (b // 4) % 2, b % 4
     if d == 128 and group == 32:
-        b, m = field // 4, field % 4
-        a, w, i = b // 8, (b // 4) % 2, b % 4
         return 64 * w + 32 * (m // 2) + 8 * a + 4 * (m % 2) + i
+    if d == 128 and group == 64:
+        return 64 * w + 16 * a + 4 * m + i
     return field
 
 

@@ -321,18 +321,26 @@ def test_p7_int2_block_layout_by_hand():
         assert np.array_equal(a, b)
 
 
-def test_p7_k_code_fields_by_hand():
-    """G = 32 K-code fields, positions worked out by hand from the word layout
-    (quarter a, word w, byte i, field m -> channel 64w + 32(m//2) + 8a + 4(m%2) + i)."""
-    d, group = 128, 32
-    spots = [  # (token, channel, code, byte, field)
-        (5, 37, 3, 1, 3),      # group 1: w 0, m//2 1; 5 = 8*0 + 4*1 + 1
-        (9, 100, 2, 4, 3),     # group 3: w 1, m//2 1; 4 = 8*0 + 4*1 + 0
-        (0, 10, 1, 10, 0),     # group 0: w 0, m//2 0; 10 = 8*1 + 4*0 + 2
-        (15, 127, 3, 31, 3),   # group 3: w 1, m//2 1; 31 = 8*3 + 4*1 + 3
-        (2, 64, 1, 4, 0),      # group 2: w 1, m//2 0; 0 = 8*0 + 4*0 + 0
-    ]
-    z16 = np.zeros((16, 4), np.float16)
+@pytest.mark.parametrize("group,spots", [
+    # (token, channel, code, byte, field), worked out by hand from the word
+    # layout: byte 8a + 4w + i, field m
+    (32, [(5, 37, 3, 1, 3),      # group 1: w 0, m//2 1; 5 = 8*0 + 4*1 + 1
+          (9, 100, 2, 4, 3),     # group 3: w 1, m//2 1; 4 = 8*0 + 4*1 + 0
+          (0, 10, 1, 10, 0),     # group 0: w 0, m//2 0; 10 = 8*1 + 4*0 + 2
+          (15, 127, 3, 31, 3),   # group 3: w 1, m//2 1; 31 = 8*3 + 4*1 + 3
+          (2, 64, 1, 4, 0)]),    # group 2: w 1, m//2 0; 0 = 0
+    (64, [(5, 37, 3, 17, 1),     # group 0: w 0; 37 = 16*2 + 4*1 + 1
+          (9, 100, 2, 20, 1),    # group 1: w 1; 36 = 16*2 + 4*1 + 0
+          (0, 10, 1, 2, 2),      # group 0: w 0; 10 = 16*0 + 4*2 + 2
+          (15, 127, 3, 31, 3),   # group 1: w 1; 63 = 16*3 + 4*3 + 3
+          (2, 64, 1, 4, 0)]),    # group 1: w 1; 0 = 0
+])
+def test_p7_k_code_fields_by_hand(group, spots):
+    """K-code fields (quarter a, word w, byte i, field m): G = 32 holds channel
+    64w + 32(m//2) + 8a + 4(m%2) + i, G = 64 channel 64w + 16a + 4m + i."""
+    d = 128
+    ng = d // group
+    z16 = np.zeros((16, ng), np.float16)
     for t, ch, c, b, m in spots:
         kc = np.zeros((16, d), np.uint8)
         kc[t, ch] = c
@@ -340,17 +348,18 @@ def test_p7_k_code_fields_by_hand():
         assert kb[t, b] == c << (2 * m) and np.count_nonzero(kb) == 1
         assert O.unpack_int2_block(O.pack_int2_block(kc, z16, z16, kc, z16, z16), d, group)[0][t, ch] == c
     # what the layout is for: shifting a quarter's word right by 2m and masking
-    # each byte's low two bits yields four codes of ONE group, and the two
-    # field pairs of the four quarters cover each group's 32 channels once
+    # each byte's low two bits yields four codes of ONE group; the words w of
+    # the four quarters, at the field positions of one group, cover that
+    # group's channels once
     ch = O.k_code_channel(d, group).reshape(4, 2, 4, 4)  # [quarter a][word w][byte i][field m]
+    per_word = 4 // (ng // 2)                            # field positions per group in a word
     for w in range(2):
         for m in range(4):
-            assert set((ch[:, w, :, m] // group).ravel()) == {2 * w + m // 2}
-        for half in range(2):
-            cover = ch[:, w, :, 2 * half:2 * half + 2].ravel()
-            assert sorted(cover) == list(range(32 * (2 * w + half), 32 * (2 * w + half) + 32))
-    # G = 64 keeps consecutive channels
-    assert np.array_equal(O.k_code_channel(d, 64), np.arange(d))
+            assert set((ch[:, w, :, m] // group).ravel()) == {w * (ng // 2) + m // per_word}
+        for k in range(ng // 2):
+            gam = w * (ng // 2) + k
+            cover = ch[:, w, :, per_word * k:per_word * (k + 1)].ravel()
+            assert sorted(cover) == list(range(group * gam, group * gam + group))
 
 
 def test_p7_int2_block_roundtrip_all_bytes():
@@ -368,10 +377,12 @@ def test_p7_int2_block_roundtrip_all_bytes():
     blk = np.zeros(1536, np.uint8)
     blk[:256] = allb
     blk[256:512] = allb[::-1]
-    kc = O.unpack_int2_block(blk, 128, 64)[0]                          # consecutive fields
-    for b in range(256):
-        t, j0 = divmod(b, 32)
-        assert [int(kc[t, 4 * j0 + i]) for i in range(4)] == [(b >> (2 * i)) & 3 for i in range(4)]
+    for group in (32, 64):
+        kc = O.unpack_int2_block(blk, 128, group)[0]
+        at = O.k_code_channel(128, group)                              # field 4b + m -> channel
+        for b in range(256):
+            t, bb = divmod(b, 32)
+            assert [int(kc[t, at[4 * bb + m]]) for m in range(4)] == [(b >> (2 * m)) & 3 for m in range(4)]
 
 
 def test_bf16_block_layout():
@@ -725,7 +736,8 @@ def test_f3_fp8_meta_block_layout_by_hand():
     assert blk.size == O.int2_block_bytes(d, group, 8) == 1152
     assert blk.size * 8 / (16 * 2 * d) == O.int2_history_bits(group, 8, 8) == 2.25
     assert O.e4m3_decode(np.uint8(0x44)) == 3.0 and O.e4m3_decode(np.uint8(0x4A)) == 5.0
-    assert np.all(blk[:512] == 0xE4)
+    # K fields: byte 8a + 4w + i holds channels = i (mod 4) in all four fields
+    assert np.all(blk[:512].reshape(16, 32) == (np.arange(32) % 4 * 0x55).astype(np.uint8)[None, :])
     ksz = blk[512:576]                          # [token][group][(s, z)]
     assert ksz[(7 * 2 + 1) * 2] == 0x44 and ksz[(7 * 2 + 1) * 2 + 1] == 0xB8
     vb = blk[576:1088].reshape(4, d)
