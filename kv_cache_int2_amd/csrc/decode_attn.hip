@@ -801,7 +801,9 @@ __device__ __forceinline__ void unpack_unit(const uint8_t* st, const Int2Offsets
 // masks of a chunk's queries; in decode every row sees the whole INT2 region).
 // SH: the code operands come unpacked from ops (shared by the item's
 // wavefronts), else each lane unpacks its own.
-template <int NG, int CT, bool EDGE, bool SH, class Src>
+// LQ: head quads of the last tile that hold a real head (the others have zero
+// digits: their logit MFMAs and sums are skipped, their logits taken as 0).
+template <int NG, int CT, bool EDGE, bool SH, int LQ, class Src>
 __device__ __forceinline__ void int2_pair(const Src& src, int lp0, int p_end, int lo, int hi, int qlo, int g_real,
                                           int t0, const Int2Const<NG, CT>& K, Int2State<NG, CT>& S, float* p_lds,
                                           const u32x4* ops) {
@@ -843,6 +845,10 @@ __device__ __forceinline__ void int2_pair(const Src& src, int lp0, int p_end, in
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int gam = u % NG;
+        if (ct == CT - 1 && u / NG >= LQ) {
+          cd[u] = 0;
+          continue;
+        }
         i32x4 ds;
         if constexpr (NG == 4) {
           // group gam: fields 2(gam%2), +1 of word gam/2
@@ -856,6 +862,10 @@ __device__ __forceinline__ void int2_pair(const Src& src, int lp0, int p_end, in
       }
 #pragma unroll
       for (int hh = 0; hh < HPL; ++hh) {
+        if (ct == CT - 1 && hh >= LQ) {
+          lg[t][ct][hh] = seen[t][ct][hh] ? 0.f : kNegInf;
+          continue;
+        }
         float x = 0.f;
 #pragma unroll
         for (int gg = 0; gg < NG; ++gg) {
@@ -989,8 +999,8 @@ __device__ __forceinline__ void int2_pair(const Src& src, int lp0, int p_end, in
 }
 
 // W wavefronts per work item: wavefront w takes the CT row tiles starting at
-// tile w CT, all of them reading the same staged pages.
-template <int NG, int MB, int CT, int W>
+// tile w CT, all of them reading the same staged pages; LQ as for int2_pair.
+template <int NG, int MB, int CT, int W, int LQ>
 __device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float* p_lds, uint8_t* stage,
                           u32x4* ops) {
   constexpr Int2Layout L{NG, MB};
@@ -1065,7 +1075,7 @@ __device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float
         if (!ok1) pg1 = pg0;
         const int pe = ok0 ? (ok1 ? p_end : lp0 + 1) : lp0;
         const Int2Data<NG> D = int2_load<NG, MB>(blk(pg0), blk(pg1), off);
-        int2_pair<NG, CT, true, false>(D, lp0, pe, lo, hi, qlo, g_real, t0, K, S, p_lds, nullptr);
+        int2_pair<NG, CT, true, false, LQ>(D, lp0, pe, lo, hi, qlo, g_real, t0, K, S, p_lds, nullptr);
       };
       int lp0 = p_begin;
       if (lp0 * kPage < lo) {
@@ -1107,7 +1117,7 @@ __device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float
             } else {
               vm_wait<0>();
             }
-            int2_pair<NG, CT, false, false>(Int2Staged<NG, MB>{stage + cur * kSlot, off}, lp0, p_end, lo, hi, qlo,
+            int2_pair<NG, CT, false, false, LQ>(Int2Staged<NG, MB>{stage + cur * kSlot, off}, lp0, p_end, lo, hi, qlo,
                                             g_real, t0, K, S, p_lds, nullptr);
             lp0 += 2;
             if (lp0 + 2 > lim) break;
@@ -1160,7 +1170,7 @@ __device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float
               for (int u = wv; u < kOpUnits; u += W) unpack_unit<NG, MB>(stage + cur * kSlot, off, u, ops);
               barrier_no_fence();
             }
-            int2_pair<NG, CT, false, kShareOps>(Int2Staged<NG, MB>{stage + cur * kSlot, off}, lp0, p_end, lo, hi, qlo,
+            int2_pair<NG, CT, false, kShareOps, LQ>(Int2Staged<NG, MB>{stage + cur * kSlot, off}, lp0, p_end, lo, hi, qlo,
                                                 g_real, t0, K, S, p_lds, ops);
             lp0 += 2;
             if (lp0 + 2 > lim) break;
@@ -1458,7 +1468,18 @@ decode_int2(DecodeParams p) {
   const int item = blockIdx.x;
   const int split = item % p.splits_int2;
   const int bk = item / p.splits_int2;
-  int2_item<NG, MB, CT, W>(p, bk / p.n_kv, bk % p.n_kv, split, p_lds[W > 1 ? threadIdx.x >> 6 : 0], stage, ops);
+  float* pl = p_lds[W > 1 ? threadIdx.x >> 6 : 0];
+  if constexpr (NG == 2) {
+    // a 64-channel-group tile spans two head quads; when the second quad of
+    // this wavefront's last tile holds no head (g % 8 <= 4), the loop skips
+    // its logits (decided once per wavefront: the tile index is uniform)
+    const int last = (W > 1 ? __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) * CT : 0) + CT - 1;
+    if (8 * last + 4 >= p.g) {
+      int2_item<NG, MB, CT, W, 1>(p, bk / p.n_kv, bk % p.n_kv, split, pl, stage, ops);
+      return;
+    }
+  }
+  int2_item<NG, MB, CT, W, 4 / NG>(p, bk / p.n_kv, bk % p.n_kv, split, pl, stage, ops);
 }
 
 // items: (request, KV head, query of the launch, bf16 split)
