@@ -803,12 +803,17 @@ __device__ __forceinline__ void unpack_unit(const uint8_t* st, const Int2Offsets
 // wavefronts), else each lane unpacks its own.
 // LQ: head quads of the last tile that hold a real head (the others have zero
 // digits: their logit MFMAs and sums are skipped, their logits taken as 0).
+// With one tile of 64-channel groups whose second head quad is empty, the
+// value rows 8-15 (that quad's (head, group) rows) carry the lo part of rows
+// 0-7 instead, so each channel tile takes one value MFMA, not two.
 template <int NG, int CT, bool EDGE, bool SH, int LQ, class Src>
 __device__ __forceinline__ void int2_pair(const Src& src, int lp0, int p_end, int lo, int hi, int qlo, int g_real,
                                           int t0, const Int2Const<NG, CT>& K, Int2State<NG, CT>& S, float* p_lds,
                                           const u32x4* ops) {
   constexpr int HPL = 4 / NG;
+  constexpr bool kPackLo = NG == 2 && CT == 1 && LQ == 1;
   const int lane = threadIdx.x & 63, ln = lane & 15, qd = lane >> 4;
+  const int vrow = kPackLo ? (ln & 7) : ln;  // value-operand row this lane serves
   // ---- logits ----
   const Int2KData<NG> DK = src.k();
   bool seen[2][CT][HPL];
@@ -911,7 +916,7 @@ __device__ __forceinline__ void int2_pair(const Src& src, int lp0, int p_end, in
       if constexpr (HPL == 2) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          const int hl = 2 * qd + e;
+          const int hl = 2 * (kPackLo ? (qd & 1) : qd) + e;
           const float x0 = __shfl(alpha[0], 16 * (hl & 3)), x1 = __shfl(alpha[1], 16 * (hl & 3));
           ar[e] = (hl >> 2) ? x1 : x0;
         }
@@ -923,10 +928,10 @@ __device__ __forceinline__ void int2_pair(const Src& src, int lp0, int p_end, in
       // value-operand row 16ct + ln belongs to head ln / NG of the tile, i.e.
       // 4hh + qd with qd = (ln / NG) % 4, hh = ln / (4 NG): its alpha is held
       // by quad qd, entry hh
-      float az = __shfl(alpha[0], 16 * ((ln / NG) & 3));
+      float az = __shfl(alpha[0], 16 * ((vrow / NG) & 3));
       if constexpr (HPL == 2) {
-        const float az1 = __shfl(alpha[1], 16 * ((ln / NG) & 3));
-        az = (ln >> 3) ? az1 : az;
+        const float az1 = __shfl(alpha[1], 16 * ((vrow / NG) & 3));
+        az = (vrow >> 3) ? az1 : az;
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) S.zz[ct][r] *= az;
@@ -954,7 +959,7 @@ __device__ __forceinline__ void int2_pair(const Src& src, int lp0, int p_end, in
   u32x4 pa[CT][2];
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
-    const int h = (16 * ct + ln) / NG;
+    const int h = (16 * ct + vrow) / NG;
     const f32x4 pf0 = *(const f32x4*)(p_lds + (2 * h) * kPage + 4 * qd);
     const f32x4 pf1 = *(const f32x4*)(p_lds + (2 * h + 1) * kPage + 4 * qd);
 #pragma unroll
@@ -976,8 +981,13 @@ __device__ __forceinline__ void int2_pair(const Src& src, int lp0, int p_end, in
       const float x0 = fmaf(pf0[r], sg * s0, 0.f), x1 = fmaf(pf1[r], sg * s1, 0.f);
       // hi = x truncated to fp16, lo = the exact remainder, truncated again
       const f16x2 hv = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(x0, x1));
-      pa[ct][0][r] = __builtin_bit_cast(uint32_t, hv);
-      pa[ct][1][r] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(mix_sub_lo(x0, hv), mix_sub_hi(x1, hv)));
+      const uint32_t lov = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(mix_sub_lo(x0, hv), mix_sub_hi(x1, hv)));
+      if constexpr (kPackLo) {
+        pa[ct][0][r] = ln < 8 ? __builtin_bit_cast(uint32_t, hv) : lov;
+      } else {
+        pa[ct][0][r] = __builtin_bit_cast(uint32_t, hv);
+        pa[ct][1][r] = lov;
+      }
       S.zz[ct][r] = fmaf(pf0[r], z0, S.zz[ct][r]);
       S.zz[ct][r] = fmaf(pf1[r], z1, S.zz[ct][r]);
       if (r & 1) {  // x = -p s pscale 4^-r here
@@ -993,7 +1003,7 @@ __device__ __forceinline__ void int2_pair(const Src& src, int lp0, int p_end, in
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
       S.acc[ct][kt] = mfma_f16(pa[ct][0], bv, S.acc[ct][kt]);
-      S.acc[ct][kt] = mfma_f16(pa[ct][1], bv, S.acc[ct][kt]);
+      if constexpr (!kPackLo) S.acc[ct][kt] = mfma_f16(pa[ct][1], bv, S.acc[ct][kt]);
     }
   }
 }
@@ -1006,6 +1016,7 @@ __device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float
   constexpr Int2Layout L{NG, MB};
   constexpr int HPL = 4 / NG;
   constexpr int kTiles = W * CT;  // row tiles of the (request, KV head)
+  constexpr bool kPackLo = NG == 2 && CT == 1 && LQ == 1;  // as in int2_pair
   const int lane = threadIdx.x & 63, ln = lane & 15, qd = lane >> 4;
   // first row tile of this wavefront (wavefront-uniform: kept in a scalar register)
   const int t0 = W > 1 ? __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) * CT : 0;
@@ -1203,9 +1214,13 @@ __device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float
 #pragma unroll
       for (int kt = 0; kt < 8; ++kt) {
         const int ch = 8 * ln + kt;
+        float a = S.acc[ct][kt][r];
+        // packed lo rows: row 8 + i (lane quads 2, 3) adds onto row i (a
+        // head of the empty quad is >= g, so quads 2, 3 store nothing)
+        if constexpr (kPackLo) a += __shfl(a, lane + 32);
         if (h < p.g && ch / G == gam_row) {
           float* dst = p.partial + (((int64_t)b * p.n_q + kv * p.g + h) * Ssp + split) * kPartialStride;
-          dst[2 + ch] = fmaf(S.acc[ct][kt][r], accscale, zr);
+          dst[2 + ch] = fmaf(a, accscale, zr);
         }
       }
     }
