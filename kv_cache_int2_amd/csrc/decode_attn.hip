@@ -160,15 +160,16 @@ __device__ __forceinline__ int q_pos(const DecodeParams& p, int b, int hv) {
 // A 128 x 128 fp32 matrix to LDS by a block of 256 threads, row stride
 // `stride` floats: 16 independent 16-byte loads per thread, all issued before
 // the first store.
+// t: this thread's index among the 256.
 template <int Stride>
-__device__ __forceinline__ void stage_matrix256(const float* src, float* lds) {
+__device__ __forceinline__ void stage_matrix256(const float* src, float* lds, int t = threadIdx.x) {
   const float4* R = (const float4*)src;
   float4 v[16];
 #pragma unroll
-  for (int k = 0; k < 16; ++k) v[k] = R[threadIdx.x + 256 * k];
+  for (int k = 0; k < 16; ++k) v[k] = R[t + 256 * k];
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
-    const int e = threadIdx.x + 256 * k;
+    const int e = t + 256 * k;
     float* d = lds + (e >> 5) * Stride + 4 * (e & 31);
     d[0] = v[k].x;
     d[1] = v[k].y;
@@ -1511,14 +1512,18 @@ __global__ __launch_bounds__(64) void decode_bf16(DecodeParams p) {
 // combine: bf16 region (when its splits fit the block), LSE merge, R_V^T on
 // the INT2 part, normalisation
 // ---------------------------------------------------------------------------
-// One block of four wavefronts per (request, KV head).  With bf16_in_combine,
-// wavefront w first runs bf16 split w (at most four) and leaves its partial
-// beside the INT2 splits' ones.  Then wavefront w merges the query heads w,
-// w + 4, ... of the group, lane i owning output channels i and i + 64, so no
-// step needs a block-wide reduction; the first 32 partial rows of a head are
-// loaded at once, behind the split maxima.  R_V is staged once in LDS with a
-// row stride of 129 floats: lane i reading rows i and i + 64 at column k hits
-// bank (i + k) % 32, no conflicts.
+// One block of eight wavefronts per (request, KV head), in two sides that run
+// side by side.  Wavefronts 0-3 run the bf16 region (with bf16_in_combine:
+// bf16 split w, at most four, its partial left beside the INT2 splits' ones)
+// while wavefronts 4-7 stage R_V and merge the INT2 splits of query heads
+// 0-3.  After a barrier, wavefront 4 + w applies R_V^T to the INT2 part of
+// head w (then w + 4, ...) and wavefront w merges that head's bf16 splits;
+// the INT2 side hands its part over through LDS and wavefront w combines the
+// two.  Lane i owns output channels i and i + 64, so no step needs a
+// block-wide reduction; the first 32 partial rows of a merge are loaded at
+// once, behind the split maxima.  R_V is staged in LDS with a row stride of
+// 129 floats: lane i reading rows i and i + 64 at column k hits bank
+// (i + k) % 32, no conflicts.
 constexpr int kRvStride = kHeadDim + 1;
 constexpr int kCombineRows = 32;
 
@@ -1561,105 +1566,137 @@ __device__ __forceinline__ void weighted_rows(const float* rows, float wt, int u
   }
 }
 
-__global__ __launch_bounds__(256) void decode_combine(DecodeParams p) {
+// log-sum-exp merge of the partial rows [s0, s1) of one head (base: its first
+// partial row), by one wavefront: M = their largest max, L = sum 2^(m_s - M)
+// l_s, acc = sum 2^(m_s - M) o_s (lane i: channels i and i + 64); M = -inf,
+// L = acc = 0 when no row saw a token
+__device__ void merge_splits(const float* base, int s0, int s1, float& M, float& L, float& a0, float& a1) {
+  const int lane = threadIdx.x & 63;
+  const int n = s1 - s0;
+  M = kNegInf;
+  L = a0 = a1 = 0.f;
+  if (n <= 0) return;
+  base += (int64_t)s0 * kPartialStride;
+  // split maxima first, then the first rows, so that the max reduction waits
+  // only for the former
+  const float ms = lane < n ? base[lane * kPartialStride] : kNegInf;
+  const float ls = lane < n ? base[lane * kPartialStride + 1] : 0.f;
+  float m = ms;
+  for (int s = lane + 64; s < n; s += 64) m = fmaxf(m, base[s * kPartialStride]);
+  const int n0 = min(n, kCombineRows);
+  float x0[kCombineRows], x1[kCombineRows];
+#pragma unroll
+  for (int k = 0; k < kCombineRows; ++k) {
+    x0[k] = k < n0 ? base[k * kPartialStride + 2 + lane] : 0.f;
+    x1[k] = k < n0 ? base[k * kPartialStride + 2 + 64 + lane] : 0.f;
+  }
+  M = wave_max(m);
+  if (M == kNegInf) return;
+  // a split without tokens has m = -inf and zero rows: weight 0
+  const float wt0 = ms == kNegInf ? 0.f : exp2f(ms - M);
+  float l = wt0 * ls;
+#pragma unroll
+  for (int k = 0; k < kCombineRows; ++k) {
+    const float wk = lane_value(wt0, k);  // 0 past n
+    a0 = fmaf(wk, x0[k], a0);
+    a1 = fmaf(wk, x1[k], a1);
+  }
+  // the rest of the first 64 splits, then further chunks of 64
+  for (int c0 = 0; c0 < n; c0 += 64) {
+    float wt = wt0;
+    if (c0 > 0) {
+      const int s = c0 + lane;
+      wt = 0.f;
+      if (s < n) {
+        const float mc = base[s * kPartialStride];
+        wt = mc == kNegInf ? 0.f : exp2f(mc - M);
+        l = fmaf(wt, base[s * kPartialStride + 1], l);
+      }
+    }
+    weighted_rows(base + (int64_t)c0 * kPartialStride, wt, c0 == 0 ? n0 : 0, min(64, n - c0), a0, a1);
+  }
+  L = wave_sum(l);
+}
+
+__global__ __launch_bounds__(512) void decode_combine(DecodeParams p) {
   __shared__ float rv[kHeadDim * kRvStride];
-  __shared__ __attribute__((aligned(16))) float aint[4][kHeadDim];
+  __shared__ __attribute__((aligned(16))) float aint[4][kHeadDim];  // INT2 part before R_V^T
+  __shared__ float xch[4][kHeadDim + 2];                            // INT2 part, its M and L
   const int bk = blockIdx.x;
   const int b = bk / p.n_kv, kv = bk % p.n_kv;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wl = w & 3;
+  const bool int2_side = w >= 4;
   const int S = p.splits_int2 + p.splits_bf16, SI = p.splits_int2;
   // R_V null: the output stays in the rotated basis (R_V^T folded into the
   // output projection), and so does the bf16 region's V
   const bool rot = SI > 0 && p.r_v;
-  if (rot) stage_matrix256<kRvStride>(p.r_v + (int64_t)kv * kHeadDim * kHeadDim, rv);
-  if (p.bf16_in_combine && w < p.splits_bf16) bf16_item<true>(p, b, kv, SI + w, 0);
+  auto base_of = [&](int h) { return p.partial + ((int64_t)b * p.n_q + kv * p.g + h) * S * kPartialStride; };
+  float Mi = kNegInf, Li = 0.f, ai0 = 0.f, ai1 = 0.f;  // INT2 side: head h0 + wl
+  if (int2_side) {
+    if (rot) stage_matrix256<kRvStride>(p.r_v + (int64_t)kv * kHeadDim * kHeadDim, rv, threadIdx.x - 256);
+    if (wl < p.g) merge_splits(base_of(wl), 0, SI, Mi, Li, ai0, ai1);
+  } else if (p.bf16_in_combine && wl < p.splits_bf16) {
+    bf16_item<true>(p, b, kv, SI + wl, 0);
+  }
   __syncthreads();  // R_V staged; the bf16 partials written by this block are visible to it
   for (int h0 = 0; h0 < p.g; h0 += 4) {  // same trip count in every wavefront
-    const int h = h0 + w;
-    const int hq = kv * p.g + h;
-    float M = kNegInf, L = 0.f, ai0 = 0.f, ai1 = 0.f, ab0 = 0.f, ab1 = 0.f;
+    const int h = h0 + wl;
+    float Mb = kNegInf, Lb = 0.f, ab0 = 0.f, ab1 = 0.f;
     if (h < p.g) {
-      const float* base = p.partial + ((int64_t)b * p.n_q + hq) * S * kPartialStride;
-      // split maxima first, then the first rows, so that the max reduction
-      // waits only for the former
-      const float ms = lane < S ? base[lane * kPartialStride] : kNegInf;
-      const float ls = lane < S ? base[lane * kPartialStride + 1] : 0.f;
-      float m = ms;
-      for (int s = lane + 64; s < S; s += 64) m = fmaxf(m, base[s * kPartialStride]);
-      const int n0 = min(S, kCombineRows);
-      float x0[kCombineRows], x1[kCombineRows];
-#pragma unroll
-      for (int k = 0; k < kCombineRows; ++k) {
-        x0[k] = k < n0 ? base[k * kPartialStride + 2 + lane] : 0.f;
-        x1[k] = k < n0 ? base[k * kPartialStride + 2 + 64 + lane] : 0.f;
-      }
-      M = wave_max(m);
-      if (M != kNegInf) {
-        // a split without tokens has m = -inf and zero rows: weight 0
-        const float wt0 = ms == kNegInf ? 0.f : exp2f(ms - M);
-        L = wt0 * ls;
-#pragma unroll
-        for (int k = 0; k < kCombineRows; ++k) {
-          const float wk = lane_value(wt0, k);  // 0 past S
-          const float wi = k < SI ? wk : 0.f, wb = k < SI ? 0.f : wk;
-          ai0 = fmaf(wi, x0[k], ai0);
-          ai1 = fmaf(wi, x1[k], ai1);
-          ab0 = fmaf(wb, x0[k], ab0);
-          ab1 = fmaf(wb, x1[k], ab1);
-        }
-        // the rest of the first 64 splits, then further chunks of 64
-        for (int c0 = 0; c0 < S; c0 += 64) {
-          float wt = wt0;
-          if (c0 > 0) {
-            const int s = c0 + lane;
-            wt = 0.f;
-            if (s < S) {
-              const float mc = base[s * kPartialStride];
-              wt = mc == kNegInf ? 0.f : exp2f(mc - M);
-              L = fmaf(wt, base[s * kPartialStride + 1], L);
-            }
-          }
-          const int u0 = c0 == 0 ? n0 : 0;
-          const int cn = min(64, S - c0);
-          const int ci = max(u0, min(cn, SI - c0));  // INT2 splits come first
-          const float* rows = base + (int64_t)c0 * kPartialStride;
-          weighted_rows(rows, wt, u0, ci, ai0, ai1);
-          weighted_rows(rows, wt, ci, cn, ab0, ab1);
-        }
-        L = wave_sum(L);
-      }
-      aint[w][lane] = ai0;
-      aint[w][lane + 64] = ai1;
-    }
-    __syncthreads();
-    if (h < p.g) {
-      // R_V^T on the INT2 part: out_j = sum_k aint_k R_V[j][k]
-      float r0 = 0.f, r1 = 0.f;
-      if (!rot) {
-        r0 = aint[w][lane];
-        r1 = aint[w][lane + 64];
-      } else {
-        const float* row0 = rv + lane * kRvStride;
-        const float* row1 = rv + (lane + 64) * kRvStride;
+      if (int2_side) {
+        if (h0 > 0) merge_splits(base_of(h), 0, SI, Mi, Li, ai0, ai1);
+        // R_V^T on the INT2 part: out_j = sum_k aint_k R_V[j][k]
+        float r0 = ai0, r1 = ai1;
+        if (rot) {
+          aint[wl][lane] = ai0;
+          aint[wl][lane + 64] = ai1;
+          // the wavefront's own LDS writes, read back by its other lanes (LDS
+          // operations of one wavefront complete in order)
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+          r0 = r1 = 0.f;
+          const float* row0 = rv + lane * kRvStride;
+          const float* row1 = rv + (lane + 64) * kRvStride;
 #pragma unroll 8
-        for (int k = 0; k < kHeadDim; k += 4) {
-          const float4 a = *(const float4*)&aint[w][k];
-          r0 = fmaf(a.x, row0[k], r0);
-          r1 = fmaf(a.x, row1[k], r1);
-          r0 = fmaf(a.y, row0[k + 1], r0);
-          r1 = fmaf(a.y, row1[k + 1], r1);
-          r0 = fmaf(a.z, row0[k + 2], r0);
-          r1 = fmaf(a.z, row1[k + 2], r1);
-          r0 = fmaf(a.w, row0[k + 3], r0);
-          r1 = fmaf(a.w, row1[k + 3], r1);
+          for (int k = 0; k < kHeadDim; k += 4) {
+            const float4 a = *(const float4*)&aint[wl][k];
+            r0 = fmaf(a.x, row0[k], r0);
+            r1 = fmaf(a.x, row1[k], r1);
+            r0 = fmaf(a.y, row0[k + 1], r0);
+            r1 = fmaf(a.y, row1[k + 1], r1);
+            r0 = fmaf(a.z, row0[k + 2], r0);
+            r1 = fmaf(a.z, row1[k + 2], r1);
+            r0 = fmaf(a.w, row0[k + 3], r0);
+            r1 = fmaf(a.w, row1[k + 3], r1);
+          }
         }
+        xch[wl][lane] = r0;
+        xch[wl][lane + 64] = r1;
+        if (lane == 0) {
+          xch[wl][kHeadDim] = Mi;
+          xch[wl][kHeadDim + 1] = Li;
+        }
+      } else {
+        merge_splits(base_of(h), SI, S, Mb, Lb, ab0, ab1);
       }
-      float* o = p.out + q_row(p, b, kv, h);
-      const bool empty = M == kNegInf;
-      o[lane] = empty ? 0.f : (r0 + ab0) / L;
-      o[lane + 64] = empty ? 0.f : (r1 + ab1) / L;
     }
-    __syncthreads();
+    __syncthreads();  // the INT2 part of heads h0 .. h0 + 3 is in xch
+    if (!int2_side && h < p.g) {
+      const float mi = xch[wl][kHeadDim], li = xch[wl][kHeadDim + 1];
+      const float M = fmaxf(mi, Mb);
+      float* o = p.out + q_row(p, b, kv, h);
+      if (M == kNegInf) {  // no token at all
+        o[lane] = 0.f;
+        o[lane + 64] = 0.f;
+      } else {
+        const float wi = mi == kNegInf ? 0.f : exp2f(mi - M), wb = Mb == kNegInf ? 0.f : exp2f(Mb - M);
+        const float L = wi * li + wb * Lb;
+        o[lane] = (wi * xch[wl][lane] + wb * ab0) / L;
+        o[lane + 64] = (wi * xch[wl][lane + 64] + wb * ab1) / L;
+      }
+    }
+    __syncthreads();  // xch is free again
   }
 }
 
@@ -1691,7 +1728,7 @@ hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream, hipEvent_t
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (!int2 && (e = mark(ev_stop)) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(decode_combine, dim3(bkn), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(decode_combine, dim3(bkn), dim3(512), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -1709,7 +1746,7 @@ hipError_t launch_prefill_t(const DecodeParams& p, hipStream_t stream, hipEvent_
   if ((e = mark(ev_stop)) != hipSuccess) return e;
   hipLaunchKernelGGL(decode_bf16, dim3(bkn * (p.g / p.g_real) * p.splits_bf16), dim3(64), 0, stream, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_combine, dim3(bkn), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(decode_combine, dim3(bkn), dim3(512), 0, stream, p);
   return hipGetLastError();
 }
 
