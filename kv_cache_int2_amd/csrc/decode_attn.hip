@@ -19,13 +19,14 @@
 //   decode_combine   per (request, KV head): log-sum-exp merge of the splits,
 //                    R_V^T on the INT2 part, normalisation.
 //
-// INT2 logits on MFMA (v_mfma_i32_16x16x64_i8, exact integer accumulation):
+// INT2 logits on MFMA (int8, exact integer accumulation):
 //   q~ = (q R_K) log2(e)/sqrt(d) is held as the fixed-point integer
 //   Q = rint(q~ 2^sq) (|Q| <= 2^21 per (request, KV head)); 2Q is split into
-//   three balanced int8 digits.  A = the digits, block-diagonal over channel
-//   groups (row (h, gamma) only sees channels of group gamma), B = the 2-bit
-//   codes as int8 bytes (columns = tokens).  The digit chains feed each other
-//   (acc <- (acc << 8) + sum d c), so the accumulator ends holding, exactly,
+//   three balanced int8 digits.  One MFMA per channel group gamma and four
+//   heads (v_mfma_i32_16x16x32_i8 at G = 32, 16x16x64 at G = 64): K = the
+//   group's channels, A = the digits, rows (head, digit), B = the 2-bit codes
+//   as int8 bytes (columns = tokens).  Two shift-adds join a head's digit sums
+//   into, exactly,
 //     C = sum_{j in gamma} 2 Q_j c_j   (|C| < 2^29),   Qbar = sum_{j in gamma} Q_j,
 //   and  sum_j 2 Q_j (z + c_j s) = s C + z 2 Qbar, two fp32 products whose
 //   rounding (2^-24 of the larger term) stays far below the logit tolerance.
@@ -304,7 +305,7 @@ __device__ void step_writes(const DecodeParams& p, int b, int kv, const float* r
 
 // The INT2 kernel's q operands of one (request, KV head), from the fixed-point
 // q~ (qi: [head][channel], g heads) and its scale exponent sq, for `tiles`
-// 16-row tiles (rows (head, group); rows past the g heads get zero digits):
+// 16-row tiles (16/NG heads; heads past the g heads get zero digits):
 // aux = [logit factor 2^-sq / 2, 2 Qbar per row], then the int8 digits of 2Q
 // as MFMA A operands (digit 0 the most significant).  A tile of 16/NG heads
 // takes four MFMAs per page, unit u = (head quad hq, group gam), u = hq NG +
@@ -1471,8 +1472,8 @@ __device__ void bf16_item(const DecodeParams& p, int b, int kv, int split, int c
 }
 
 // CT 16-row tiles per wavefront, W wavefronts per work item (tile_split).  One
-// tile fits 4 wavefronts per SIMD (121 VGPRs); two tiles, which share the
-// unpacked codes, 2.  Wavefronts of one item share the staged pages.  LDS per
+// tile fits 4 wavefronts per SIMD (at most 126 VGPRs); two tiles, which share
+// the unpacked codes, 2.  Wavefronts of one item share the staged pages.  LDS per
 // item: each wavefront's p and the staging ring (three slots for one
 // wavefront, four when shared).
 template <int NG, int MB, int CT, int W>
