@@ -745,6 +745,14 @@ struct Int2Staged {
     }
     return d;
   }
+  // wide tiles: (scale, zero) pairs of group gam, tokens 4qd .. 4qd + 3 of page t
+  __device__ __forceinline__ u32x4 vsz_g(int t, int gam) const {
+    constexpr Int2Layout L{NG, MB};
+    const int qd = (threadIdx.x & 63) >> 4;
+    return v_pairs<MB>(*(const VRaw<MB>*)(st + t * L.bytes() + L.v_sz() + (gam * kPage + 4 * qd) * MB));
+  }
+  // wide tiles: value B operand of channel tile T (channels 16T .. 16T + 15)
+  __device__ __forceinline__ u32x4 v_wide(int T) const;
   __device__ __forceinline__ Int2VData<NG> v() const {
     constexpr Int2Layout L{NG, MB};
     Int2VData<NG> d;
@@ -782,13 +790,28 @@ __device__ __forceinline__ u32x4 v_operand(uint32_t lo_src, uint32_t hi_src, int
 // k-step u % 2), units 4-11: value channels kt = u - 4), each unpacked by one
 // wavefront into ops[unit][lane].
 constexpr int kOpUnits = 12;
+// Wide tiles (16 head rows, see int2_pair) take channel tiles of one group:
+// tile T holds channels 16T + ln, one byte per page at quad qd.
 template <int NG, int MB>
+__device__ __forceinline__ u32x4 v_wide_operand(const uint8_t* st, int T) {
+  constexpr Int2Layout L{NG, MB};
+  const int lane = threadIdx.x & 63, ln = lane & 15, qd = lane >> 4;
+  const int o = L.v_codes() + qd * kHeadDim + 16 * T + ln;
+  return v_operand(st[o], st[L.bytes() + o], 0);
+}
+template <int NG, int MB>
+__device__ __forceinline__ u32x4 Int2Staged<NG, MB>::v_wide(int T) const {
+  return v_wide_operand<NG, MB>(st, T);
+}
+template <int NG, int MB, bool WIDE>
 __device__ __forceinline__ void unpack_unit(const uint8_t* st, const Int2Offsets& o, int u, u32x4* ops) {
   constexpr Int2Layout L{NG, MB};
   const int lane = threadIdx.x & 63;
   u32x4 v;
   if (u < 4) {
     v = k_operand((*(const u32x2*)(st + (u >> 1) * L.bytes() + o.kc))[u & 1]);
+  } else if (WIDE) {
+    v = v_wide_operand<NG, MB>(st, u - 4);
   } else {
     const int kt = u - 4;
     v = v_operand(*(const uint32_t*)(st + o.vw + 4 * (kt >> 2)), *(const uint32_t*)(st + L.bytes() + o.vw + 4 * (kt >> 2)),
@@ -814,6 +837,9 @@ __device__ __forceinline__ void int2_pair(const Src& src, int lp0, int p_end, in
                                           const u32x4* ops) {
   constexpr int HPL = 4 / NG;
   constexpr bool kPackLo = NG == 2 && CT == 1 && LQ == 1;
+  // wide: four tiles (16 heads) at 32-channel groups; the value MFMAs take the
+  // 16 heads as rows against channel tiles of one group each
+  constexpr bool kWide = NG == 4 && CT == 4;
   const int lane = threadIdx.x & 63, ln = lane & 15, qd = lane >> 4;
   const int vrow = kPackLo ? (ln & 7) : ln;  // value-operand row this lane serves
   // ---- logits ----
@@ -914,6 +940,22 @@ __device__ __forceinline__ void int2_pair(const Src& src, int lp0, int p_end, in
       // value-accumulator row 16ct + 4qd + r belongs to head (4qd + r) / NG of
       // the tile: at NG = 4 head qd, this lane's own; at NG = 2 head 2qd + r/2,
       // whose alpha quad (2qd + r/2) % 4 holds as entry (2qd + r/2) / 4
+      if constexpr (kWide) {
+        // accumulator row 4qd + e is head 4qd + e, i.e. head e of tile qd,
+        // whose alpha quad e holds: only the lanes of quad qd == ct change
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float a = __shfl(alpha[0], 16 * e);
+#pragma unroll
+          for (int kt = 0; kt < 8; ++kt) S.acc[0][kt][e] *= qd == ct ? a : 1.f;
+        }
+        // value row ln is head ln: head ln % 4 of tile ln / 4
+        const float az = __shfl(alpha[0], 16 * (ln & 3));
+#pragma unroll
+        for (int gam = 0; gam < 4; ++gam)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) S.zz[gam][r] *= (ln >> 2) == ct ? az : 1.f;
+      } else {
       float ar[2] = {alpha[0], alpha[0]};
       if constexpr (HPL == 2) {
 #pragma unroll
@@ -937,6 +979,7 @@ __device__ __forceinline__ void int2_pair(const Src& src, int lp0, int p_end, in
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) S.zz[ct][r] *= az;
+      }
     }
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -957,6 +1000,49 @@ __device__ __forceinline__ void int2_pair(const Src& src, int lp0, int p_end, in
       for (int t = 0; t < 2; ++t) p_lds[(2 * h + t) * kPage + ln] = pr[t][ct][hh];
     }
   __builtin_amdgcn_wave_barrier();
+  if constexpr (kWide) {
+    // ---- values, wide: A = P'[head ln][token] for one group at a time, B =
+    // channel tiles 2 gam, 2 gam + 1 of that group; rows are the 16 heads ----
+    const f32x4 pf0 = *(const f32x4*)(p_lds + (2 * ln) * kPage + 4 * qd);
+    const f32x4 pf1 = *(const f32x4*)(p_lds + (2 * ln + 1) * kPage + 4 * qd);
+#pragma unroll
+    for (int gam = 0; gam < 4; ++gam) {
+      const u32x4 sz0 = src.vsz_g(0, gam), sz1 = src.vsz_g(1, gam);
+      u32x4 ph, pl;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float s0 = half_lo(sz0[r]), z0 = half_hi(sz0[r]);
+        float s1 = half_lo(sz1[r]), z1 = half_hi(sz1[r]);
+        if constexpr (EDGE) {
+          // as below: a token without weight may hold a non-finite pair
+          const bool v0 = pf0[r] != 0.f, v1 = pf1[r] != 0.f;
+          s0 = v0 ? s0 : 0.f;
+          z0 = v0 ? z0 : 0.f;
+          s1 = v1 ? s1 : 0.f;
+          z1 = v1 ? z1 : 0.f;
+        }
+        const float sg = (r & 1) ? -1.f : 1.f;
+        const float x0 = fmaf(pf0[r], sg * s0, 0.f), x1 = fmaf(pf1[r], sg * s1, 0.f);
+        const f16x2 hv = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(x0, x1));
+        ph[r] = __builtin_bit_cast(uint32_t, hv);
+        pl[r] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(mix_sub_lo(x0, hv), mix_sub_hi(x1, hv)));
+        S.zz[gam][r] = fmaf(pf0[r], z0, S.zz[gam][r]);
+        S.zz[gam][r] = fmaf(pf1[r], z1, S.zz[gam][r]);
+        if (r & 1) {
+          S.zz[gam][r] = fmaf(-3.f, x0, S.zz[gam][r]);
+          S.zz[gam][r] = fmaf(-3.f, x1, S.zz[gam][r]);
+        }
+      }
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const int T = 2 * gam + tt;
+        const u32x4 bv = SH ? ops[(4 + T) * 64 + lane] : src.v_wide(T);
+        S.acc[0][T] = mfma_f16(ph, bv, S.acc[0][T]);
+        S.acc[0][T] = mfma_f16(pl, bv, S.acc[0][T]);
+      }
+    }
+    return;
+  }
   const Int2VData<NG> DV = src.v();
   u32x4 pa[CT][2];
 #pragma unroll
@@ -1012,13 +1098,15 @@ __device__ __forceinline__ void int2_pair(const Src& src, int lp0, int p_end, in
 
 // W wavefronts per work item: wavefront w takes the CT row tiles starting at
 // tile w CT, all of them reading the same staged pages; LQ as for int2_pair.
+// edge_lds: this wavefront's two-block area for masked pairs (wide tiles only).
 template <int NG, int MB, int CT, int W, int LQ>
 __device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float* p_lds, uint8_t* stage,
-                          u32x4* ops) {
+                          u32x4* ops, uint8_t* edge_lds) {
   constexpr Int2Layout L{NG, MB};
   constexpr int HPL = 4 / NG;
   constexpr int kTiles = W * CT;  // row tiles of the (request, KV head)
   constexpr bool kPackLo = NG == 2 && CT == 1 && LQ == 1;  // as in int2_pair
+  constexpr bool kWide = NG == 4 && CT == 4;               // as in int2_pair
   const int lane = threadIdx.x & 63, ln = lane & 15, qd = lane >> 4;
   // first row tile of this wavefront (wavefront-uniform: kept in a scalar register)
   const int t0 = W > 1 ? __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) * CT : 0;
@@ -1087,8 +1175,23 @@ __device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float
         if (!ok0) pg0 = 0;
         if (!ok1) pg1 = pg0;
         const int pe = ok0 ? (ok1 ? p_end : lp0 + 1) : lp0;
-        const Int2Data<NG> D = int2_load<NG, MB>(blk(pg0), blk(pg1), off);
-        int2_pair<NG, CT, true, false, LQ>(D, lp0, pe, lo, hi, qlo, g_real, t0, K, S, p_lds, nullptr);
+        if constexpr (kWide) {
+          // wide tiles read their operands from LDS: the two blocks are copied
+          // into this wavefront's own area (16 bytes per lane and load; the
+          // wavefront's LDS accesses complete in order)
+          constexpr int n16 = L.bytes() / 16;
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const uint4* src = (const uint4*)blk(t ? pg1 : pg0);
+            uint4* dst = (uint4*)(edge_lds + t * L.bytes());
+            for (int c = lane; c < n16; c += 64) dst[c] = src[c];
+          }
+          int2_pair<NG, CT, true, false, LQ>(Int2Staged<NG, MB>{edge_lds, off}, lp0, pe, lo, hi, qlo, g_real, t0, K,
+                                             S, p_lds, nullptr);
+        } else {
+          const Int2Data<NG> D = int2_load<NG, MB>(blk(pg0), blk(pg1), off);
+          int2_pair<NG, CT, true, false, LQ>(D, lp0, pe, lo, hi, qlo, g_real, t0, K, S, p_lds, nullptr);
+        }
       };
       int lp0 = p_begin;
       if (lp0 * kPage < lo) {
@@ -1180,7 +1283,7 @@ __device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float
               // the code operands: one share per wavefront, published by a
               // second barrier (every wavefront has finished the previous
               // pair, whose operands these overwrite, before the first)
-              for (int u = wv; u < kOpUnits; u += W) unpack_unit<NG, MB>(stage + cur * kSlot, off, u, ops);
+              for (int u = wv; u < kOpUnits; u += W) unpack_unit<NG, MB, kWide>(stage + cur * kSlot, off, u, ops);
               barrier_no_fence();
             }
             int2_pair<NG, CT, false, kShareOps, LQ>(Int2Staged<NG, MB>{stage + cur * kSlot, off}, lp0, p_end, lo, hi, qlo,
@@ -1201,8 +1304,31 @@ __device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float
   const float accscale = exp2f(24.f - p.p_scale_exp);
   const float ipscale = 1.0f / pscale;
   constexpr int G = kHeadDim / NG;
+  if constexpr (kWide) {
+    // accumulator T, row 4qd + e: head 4 t0 + 4qd + e, channel 16T + ln; the
+    // zero-point sums of value row (head) ln, group gam, summed over the quads
+    float zg[4];
+#pragma unroll
+    for (int gam = 0; gam < 4; ++gam) {
+      float z = 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) z = fmaf(S.zz[gam][r], (float)(1 << (2 * r)) * ipscale, z);
+      zg[gam] = sum_across_quads(z);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int h = 4 * t0 + 4 * qd + e;
+      float* dst = p.partial + (((int64_t)b * p.n_q + kv * p.g + h) * Ssp + split) * kPartialStride;
+#pragma unroll
+      for (int T = 0; T < 8; ++T) {
+        const float zr = __shfl(zg[T >> 1], 4 * qd + e);
+        if (h < p.g) dst[2 + 16 * T + ln] = fmaf(S.acc[0][T][e], accscale, zr);
+      }
+    }
+  }
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
+    if constexpr (!kWide) {
     // sum p z + 3 sum_odd p s
     float z = 0.f;
 #pragma unroll
@@ -1225,6 +1351,7 @@ __device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float
           dst[2 + ch] = fmaf(a, accscale, zr);
         }
       }
+    }
     }
 #pragma unroll
     for (int hh = 0; hh < HPL; ++hh) {
@@ -1477,26 +1604,29 @@ __device__ void bf16_item(const DecodeParams& p, int b, int kv, int split, int c
 // item: each wavefront's p and the staging ring (three slots for one
 // wavefront, four when shared).
 template <int NG, int MB, int CT, int W>
-__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(CT == 1 ? 4 : (CT == 2 ? 2 : 1), 8))) void
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(CT == 1 ? 4 : (CT == 2 || CT == 4 ? 2 : 1), 8))) void
 decode_int2(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) float p_lds[W][(16 * CT / NG) * 32];
   __shared__ __attribute__((aligned(16))) uint8_t stage[(W == 1 ? 6 : 8) * Int2Layout{NG, MB}.bytes()];
   __shared__ u32x4 ops[W >= 4 ? kOpUnits * 64 : 1];  // code operands shared by the wavefronts of an item
+  constexpr bool kWide = NG == 4 && CT == 4;
+  __shared__ __attribute__((aligned(16))) uint8_t edge_lds[kWide ? W * 2 * Int2Layout{NG, MB}.bytes() : 16];
   const int item = blockIdx.x;
   const int split = item % p.splits_int2;
   const int bk = item / p.splits_int2;
   float* pl = p_lds[W > 1 ? threadIdx.x >> 6 : 0];
+  uint8_t* el = edge_lds + (kWide && W > 1 ? (threadIdx.x >> 6) : 0) * (kWide ? 2 * Int2Layout{NG, MB}.bytes() : 0);
   if constexpr (NG == 2) {
     // a 64-channel-group tile spans two head quads; when the second quad of
     // this wavefront's last tile holds no head (g % 8 <= 4), the loop skips
     // its logits (decided once per wavefront: the tile index is uniform)
     const int last = (W > 1 ? __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) * CT : 0) + CT - 1;
     if (8 * last + 4 >= p.g) {
-      int2_item<NG, MB, CT, W, 1>(p, bk / p.n_kv, bk % p.n_kv, split, pl, stage, ops);
+      int2_item<NG, MB, CT, W, 1>(p, bk / p.n_kv, bk % p.n_kv, split, pl, stage, ops, el);
       return;
     }
   }
-  int2_item<NG, MB, CT, W, 4 / NG>(p, bk / p.n_kv, bk % p.n_kv, split, pl, stage, ops);
+  int2_item<NG, MB, CT, W, 4 / NG>(p, bk / p.n_kv, bk % p.n_kv, split, pl, stage, ops, el);
 }
 
 // items: (request, KV head, query of the launch, bf16 split)
@@ -1742,7 +1872,11 @@ hipError_t launch_prefill_t(const DecodeParams& p, hipStream_t stream, hipEvent_
   hipLaunchKernelGGL((prefill_prologue<NG>), dim3(bkn), dim3(256), 0, stream, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = mark(ev_start)) != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_int2<NG, MB, 1, W>), dim3(bkn * p.splits_int2), dim3(64 * W), 0, stream, p);
+  // 32-channel groups: wide items, four tiles (16 kernel heads) per wavefront
+  if constexpr (NG == 4)
+    hipLaunchKernelGGL((decode_int2<NG, MB, 4, W / 4>), dim3(bkn * p.splits_int2), dim3(16 * W), 0, stream, p);
+  else
+    hipLaunchKernelGGL((decode_int2<NG, MB, 1, W>), dim3(bkn * p.splits_int2), dim3(64 * W), 0, stream, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = mark(ev_stop)) != hipSuccess) return e;
   hipLaunchKernelGGL(decode_bf16, dim3(bkn * (p.g / p.g_real) * p.splits_bf16), dim3(64), 0, stream, p);

@@ -928,12 +928,15 @@ static int prefill_tiles(const oscar_shape* shape, int queries) {
   return tiles <= 4 ? 4 : (tiles <= 8 ? 8 : 16);
 }
 static int32_t prefill_auto_splits(const oscar_shape* shape, int32_t batch, int32_t max_int2_pages, int tiles) {
-  // Items of `tiles` wavefronts (4 per SIMD) run in rounds of `cap` items.  A
-  // pass is long, so a part-empty last round costs its whole share: take the
-  // fewest splits whose last round is at least 15/16 full, else the count that
-  // fills it best (28 x 8 pairs on 256 compute units: 8 splits, 7 full rounds).
+  // Items run in rounds of `cap` items: at 64-channel groups an item is
+  // `tiles` wavefronts (4 per SIMD), at 32-channel groups tiles / 4 wide
+  // wavefronts (four tiles each, 2 per SIMD).  A pass is long, so a part-empty
+  // last round costs its whole share: take the fewest splits whose last round
+  // is at least 15/16 full, else the count that fills it best (28 x 8 pairs on
+  // 256 compute units, G = 32: 9 splits fill 2016 of 4 x 512).
   const int64_t pairs = (int64_t)batch * shape->n_kv_heads;
-  const int64_t cap = std::max<int64_t>(1, (int64_t)device_cus() * 4 * 4 / tiles);
+  const int per_cu = ng_of(shape) == 4 ? 4 * 2 * 4 : 4 * 4;  // tile slots per compute unit
+  const int64_t cap = std::max<int64_t>(1, (int64_t)device_cus() * per_cu / tiles);
   const int64_t smax = std::max<int64_t>(1, std::min<int64_t>(kAutoMaxSplits, max_int2_pages / 32));
   int64_t best = 1;
   double best_fill = 0.0;

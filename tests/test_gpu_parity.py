@@ -551,7 +551,8 @@ def test_f1_rotation_ablation_through_the_kernels(rotation):
 @pytest.mark.parametrize("hq,hkv,group,scale_bits,t0,chunk", [
     (32, 8, 32, 16, 3000, 16), (4, 1, 32, 16, 700, 37), (8, 2, 64, 8, 5000, 128),
     (1, 1, 32, 16, 300, 100), (16, 1, 32, 16, 2000, 20), (12, 1, 64, 16, 1500, 7),
-    (32, 8, 32, 16, 3000, 300), (8, 2, 64, 8, 500, 1000), (12, 1, 32, 16, 200, 403), (1, 1, 32, 16, 90, 250)])
+    (32, 8, 32, 16, 3000, 300), (8, 2, 64, 8, 500, 1000), (12, 1, 32, 16, 200, 403), (1, 1, 32, 16, 90, 250),
+    (4, 1, 32, 16, 500, 3)])
 def test_f2_prefill_attention(hq, hkv, group, scale_bits, t0, chunk):
     """Chunked prefill over the mixed cache: a chunk of new tokens is written
     (their entry into the recent window pushes older tokens into INT2), then

@@ -249,15 +249,19 @@ def test_fork_shares_complete_pages_and_copies_open_ones(lib):
 
 def test_prefill_auto_splits_fill_the_last_round(lib):
     """With 256 compute units (the host default) and 28 x 8 (request, KV head)
-    pairs: a 16-query block is one 16-wavefront item, 256 run at once, and 8
-    splits make exactly 7 full rounds (2 splits would leave the second round a
-    quarter empty); one query is one wavefront, 1024 at once, and 9 splits fill
-    2016 of 2048.  Short requests cap the count at one split per 32 pages."""
+    pairs.  G = 32: a 16-query block (16 tiles) is one item of four wide
+    wavefronts, two per SIMD, so 512 run at once; 9 splits fill 2016 of 2048
+    (8 would leave the fourth round half empty).  One query (4 tiles) is one
+    wide wavefront, 2048 at once: 9 splits again.  G = 64: a 16-query block is
+    8 tiles of 8 heads, one 8-wavefront item at four per SIMD, 512 at once: 9
+    splits.  Short requests cap the count at one split per 32 pages."""
     sh = K.make_shape(n_q_heads=32, n_kv_heads=8, group=32, sink=4, recent=128)
-    assert K.oscar_prefill_auto_splits(sh, 28, 6300, 128) == 8
+    assert K.oscar_prefill_auto_splits(sh, 28, 6300, 128) == 9
     assert K.oscar_prefill_auto_splits(sh, 28, 6300, 1) == 9
     assert K.oscar_prefill_auto_splits(sh, 3, 100, 128) == 3
     assert K.oscar_prefill_auto_splits(sh, 0, 100, 128) == 1
+    sh64 = K.make_shape(n_q_heads=32, n_kv_heads=8, group=64, sink=4, recent=128)
+    assert K.oscar_prefill_auto_splits(sh64, 28, 6300, 128) == 9
 
 
 def test_prefill_argument_checks(lib):
