@@ -827,7 +827,8 @@ __device__ __forceinline__ void unpack_unit(const uint8_t* st, const Int2Offsets
 // SH: the code operands come unpacked from ops (shared by the item's
 // wavefronts), else each lane unpacks its own.
 // LQ: head quads of the last tile that hold a real head (the others have zero
-// digits: their logit MFMAs and sums are skipped, their logits taken as 0).
+// digits: their logit MFMAs and sums are skipped, their logits taken as 0);
+// 0 when the last tile has none.
 // With one tile of 64-channel groups whose second head quad is empty, the
 // value rows 8-15 (that quad's (head, group) rows) carry the lo part of rows
 // 0-7 instead, so each channel tile takes one value MFMA, not two.
@@ -1616,6 +1617,15 @@ decode_int2(DecodeParams p) {
   const int bk = item / p.splits_int2;
   float* pl = p_lds[W > 1 ? threadIdx.x >> 6 : 0];
   uint8_t* el = edge_lds + (kWide && W > 1 ? (threadIdx.x >> 6) : 0) * (kWide ? 2 * Int2Layout{NG, MB}.bytes() : 0);
+  if constexpr (NG == 4 && CT == 4) {
+    // a wide wavefront whose last tile holds no head (12 heads in 16 rows)
+    // skips that tile's logits
+    const int last = (W > 1 ? __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) * CT : 0) + CT - 1;
+    if (4 * last >= p.g) {
+      int2_item<NG, MB, CT, W, 0>(p, bk / p.n_kv, bk % p.n_kv, split, pl, stage, ops, el);
+      return;
+    }
+  }
   if constexpr (NG == 2) {
     // a 64-channel-group tile spans two head quads; when the second quad of
     // this wavefront's last tile holds no head (g % 8 <= 4), the loop skips
@@ -1910,6 +1920,7 @@ hipError_t launch_decode_mb(const DecodeParams& p, hipStream_t stream, hipEvent_
     if (key == 21) return launch_decode_t<4, MB, 2, 1>(p, stream, ev_start, ev_stop);
     if (key == 13) return launch_decode_t<4, MB, 1, 3>(p, stream, ev_start, ev_stop);
     if (key == 22) return launch_decode_t<4, MB, 2, 2>(p, stream, ev_start, ev_stop);
+    if (key == 41) return launch_decode_t<4, MB, 4, 1>(p, stream, ev_start, ev_stop);
   } else if (p.ng == 2) {
     if (key == 11) return launch_decode_t<2, MB, 1, 1>(p, stream, ev_start, ev_stop);
     if (key == 21) return launch_decode_t<2, MB, 2, 1>(p, stream, ev_start, ev_stop);

@@ -62,7 +62,12 @@ oscar_status check_shape(const oscar_shape* s) {
 }
 
 int ng_of(const oscar_shape* s) { return kHeadDim / s->group; }
-int ct_of(const oscar_shape* s) { return (s->n_q_heads / s->n_kv_heads * ng_of(s) + 15) / 16; }
+// 16-row tiles of one (request, KV head) in a decode launch: three at
+// 32-channel groups are padded to four (one wide wavefront, see tile_split)
+int ct_of(const oscar_shape* s) {
+  const int t = (s->n_q_heads / s->n_kv_heads * ng_of(s) + 15) / 16;
+  return ng_of(s) == 4 && t == 3 ? 4 : t;
+}
 int mb_of(const oscar_shape* s) { return s->scale_bits == 8 ? 2 : 4; }
 int64_t int2_block(const oscar_shape* s) { return Int2Layout{ng_of(s), mb_of(s)}.bytes(); }
 
@@ -777,15 +782,15 @@ static int device_cus() {
 int32_t oscar_decode_auto_splits(const oscar_shape* shape, int32_t batch, int32_t max_int2_pages) {
   if (check_shape(shape) != OSCAR_OK || batch < 1) return 1;
   // Work items run in rounds of the items that fit the device at once (4
-  // SIMDs per compute unit, 4 / ct wavefronts per SIMD, whole items of w
-  // wavefronts each: tile_split; three-wavefront items fit five to a compute
-  // unit, not 16/3).  A count just above a whole number of rounds leaves a
+  // SIMDs per compute unit, waves_per_simd(ct) wavefronts per SIMD, whole
+  // items of w wavefronts each: tile_split; three-wavefront items fit five to
+  // a compute unit, not 16/3).  A count just above a whole number of rounds leaves a
   // nearly empty last round that costs a full item time.  Take the count that
   // fills two whole rounds (some slack for uneven requests, few partial
   // results), within [1, 64] and at least 32 pages per split.
   const int64_t pairs = (int64_t)batch * shape->n_kv_heads;
   const TileSplit ts = tile_split(ct_of(shape));
-  const int64_t cap = (int64_t)device_cus() * ((4 * (4 / ts.ct)) / ts.w);
+  const int64_t cap = (int64_t)device_cus() * ((4 * waves_per_simd(ts.ct)) / ts.w);
   const int64_t smax = std::max<int64_t>(1, std::min<int64_t>(kAutoMaxSplits, max_int2_pages / 32));
   const int64_t s = 2 * cap / pairs;
   return (int32_t)std::max<int64_t>(1, std::min<int64_t>(s, smax));

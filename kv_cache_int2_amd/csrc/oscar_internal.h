@@ -103,14 +103,19 @@ struct DecodeParams {
 struct TileSplit {
   int ct, w;
 };
+// Four tiles (at 32-channel groups: 16 heads, three real tiles padded with an
+// empty fourth) go to one wide wavefront, whose value MFMAs take the 16 heads
+// as rows (two wavefronts per SIMD).
 inline TileSplit tile_split(int tiles) {
   switch (tiles) {
     case 2: return {2, 1};
     case 3: return {1, 3};
-    case 4: return {2, 2};
+    case 4: return {4, 1};
     default: return {1, 1};
   }
 }
+// wavefronts per SIMD of an INT2 item whose wavefronts take ct tiles
+inline int waves_per_simd(int ct) { return ct == 1 ? 4 : 2; }
 
 hipError_t launch_quant_write(const QuantParams& p, int mode, hipStream_t stream);
 hipError_t launch_bf16_write(const uint16_t* k, const uint16_t* v, const int32_t* slots, int64_t n, int n_kv,

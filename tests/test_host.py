@@ -105,10 +105,14 @@ def test_workspace_bytes_monotone(lib):
     assert K.oscar_decode_auto_splits(sh, 1, 40000) == 64      # capped
     assert K.oscar_decode_auto_splits(sh, 28, 6300) == 36      # 2 rounds of 4096 wavefronts over 224 (request, head)
     assert K.oscar_decode_auto_splits(sh, 4096, 6300) == 1     # more than two rounds of pairs
-    # 12 query heads per KV head at G = 32: three one-tile wavefronts per item, five items
-    # (15 wavefronts) to a compute unit: 1280 at once, two rounds over 16 x 8 pairs = 20 splits
+    # 12 query heads per KV head at G = 32: three tiles padded to four, one wide wavefront per
+    # item, two per SIMD: 2048 at once, two rounds over 16 x 8 pairs = 32 splits
     wide = K.make_shape(n_q_heads=96, n_kv_heads=8, group=32, sink=4, recent=128)
-    assert K.oscar_decode_auto_splits(wide, 16, 8200) == 20
+    assert K.oscar_decode_auto_splits(wide, 16, 8200) == 32
+    # 8 query heads per KV head: two tiles on one wavefront, two per SIMD: 2048 at once, two
+    # rounds over 64 x 8 pairs = 8 splits
+    mid = K.make_shape(n_q_heads=64, n_kv_heads=8, group=32, sink=4, recent=128)
+    assert K.oscar_decode_auto_splits(mid, 64, 2100) == 8
 
 
 # ---------------------------------------------------------------------------
