@@ -838,9 +838,11 @@ __device__ __forceinline__ void int2_pair(const Src& src, int lp0, int p_end, in
                                           const u32x4* ops) {
   constexpr int HPL = 4 / NG;
   constexpr bool kPackLo = NG == 2 && CT == 1 && LQ == 1;
-  // wide: four tiles (16 heads) at 32-channel groups; the value MFMAs take the
-  // 16 heads as rows against channel tiles of one group each
-  constexpr bool kWide = NG == 4 && CT == 4;
+  // wide: 16 heads per wavefront (four tiles at 32-channel groups, two at
+  // 64); the value MFMAs take the 16 heads as rows against channel tiles of
+  // one group each.  Head h is head h % 4 of quad entry (h / 4) % HPL of tile
+  // h / (4 HPL).
+  constexpr bool kWide = CT * HPL == 4;
   const int lane = threadIdx.x & 63, ln = lane & 15, qd = lane >> 4;
   const int vrow = kPackLo ? (ln & 7) : ln;  // value-operand row this lane serves
   // ---- logits ----
@@ -942,20 +944,29 @@ __device__ __forceinline__ void int2_pair(const Src& src, int lp0, int p_end, in
       // the tile: at NG = 4 head qd, this lane's own; at NG = 2 head 2qd + r/2,
       // whose alpha quad (2qd + r/2) % 4 holds as entry (2qd + r/2) / 4
       if constexpr (kWide) {
-        // accumulator row 4qd + e is head 4qd + e, i.e. head e of tile qd,
-        // whose alpha quad e holds: only the lanes of quad qd == ct change
+        // accumulator row 4qd + e is head 4qd + e: tile qd / HPL, entry
+        // qd % HPL, held by quad e; only the lanes of that tile's quads change
+        const int ehh = HPL == 2 ? (qd & 1) : 0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float a = __shfl(alpha[0], 16 * e);
+          float a = __shfl(alpha[0], 16 * e);
+          if constexpr (HPL == 2) {
+            const float a1 = __shfl(alpha[1], 16 * e);
+            a = ehh ? a1 : a;
+          }
 #pragma unroll
-          for (int kt = 0; kt < 8; ++kt) S.acc[0][kt][e] *= qd == ct ? a : 1.f;
+          for (int kt = 0; kt < 8; ++kt) S.acc[0][kt][e] *= qd / HPL == ct ? a : 1.f;
         }
-        // value row ln is head ln: head ln % 4 of tile ln / 4
-        const float az = __shfl(alpha[0], 16 * (ln & 3));
+        // value row ln is head ln: tile ln / (4 HPL), entry (ln / 4) % HPL, quad ln % 4
+        float az = __shfl(alpha[0], 16 * (ln & 3));
+        if constexpr (HPL == 2) {
+          const float az1 = __shfl(alpha[1], 16 * (ln & 3));
+          az = ((ln >> 2) & 1) ? az1 : az;
+        }
 #pragma unroll
-        for (int gam = 0; gam < 4; ++gam)
+        for (int gam = 0; gam < NG; ++gam)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) S.zz[gam][r] *= (ln >> 2) == ct ? az : 1.f;
+          for (int r = 0; r < 4; ++r) S.zz[gam][r] *= (ln >> 2) / HPL == ct ? az : 1.f;
       } else {
       float ar[2] = {alpha[0], alpha[0]};
       if constexpr (HPL == 2) {
@@ -1003,11 +1014,11 @@ __device__ __forceinline__ void int2_pair(const Src& src, int lp0, int p_end, in
   __builtin_amdgcn_wave_barrier();
   if constexpr (kWide) {
     // ---- values, wide: A = P'[head ln][token] for one group at a time, B =
-    // channel tiles 2 gam, 2 gam + 1 of that group; rows are the 16 heads ----
+    // the group's channel tiles (8 / NG of 16 channels); rows are the 16 heads ----
     const f32x4 pf0 = *(const f32x4*)(p_lds + (2 * ln) * kPage + 4 * qd);
     const f32x4 pf1 = *(const f32x4*)(p_lds + (2 * ln + 1) * kPage + 4 * qd);
 #pragma unroll
-    for (int gam = 0; gam < 4; ++gam) {
+    for (int gam = 0; gam < NG; ++gam) {
       const u32x4 sz0 = src.vsz_g(0, gam), sz1 = src.vsz_g(1, gam);
       u32x4 ph, pl;
 #pragma unroll
@@ -1035,8 +1046,8 @@ __device__ __forceinline__ void int2_pair(const Src& src, int lp0, int p_end, in
         }
       }
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const int T = 2 * gam + tt;
+      for (int tt = 0; tt < 8 / NG; ++tt) {
+        const int T = (8 / NG) * gam + tt;
         const u32x4 bv = SH ? ops[(4 + T) * 64 + lane] : src.v_wide(T);
         S.acc[0][T] = mfma_f16(ph, bv, S.acc[0][T]);
         S.acc[0][T] = mfma_f16(pl, bv, S.acc[0][T]);
@@ -1107,7 +1118,7 @@ __device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float
   constexpr int HPL = 4 / NG;
   constexpr int kTiles = W * CT;  // row tiles of the (request, KV head)
   constexpr bool kPackLo = NG == 2 && CT == 1 && LQ == 1;  // as in int2_pair
-  constexpr bool kWide = NG == 4 && CT == 4;               // as in int2_pair
+  constexpr bool kWide = CT * HPL == 4;                    // as in int2_pair
   const int lane = threadIdx.x & 63, ln = lane & 15, qd = lane >> 4;
   // first row tile of this wavefront (wavefront-uniform: kept in a scalar register)
   const int t0 = W > 1 ? __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) * CT : 0;
@@ -1306,11 +1317,12 @@ __device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float
   const float ipscale = 1.0f / pscale;
   constexpr int G = kHeadDim / NG;
   if constexpr (kWide) {
-    // accumulator T, row 4qd + e: head 4 t0 + 4qd + e, channel 16T + ln; the
-    // zero-point sums of value row (head) ln, group gam, summed over the quads
-    float zg[4];
+    // accumulator T, row 4qd + e: head 4 HPL t0 + 4qd + e, channel 16T + ln
+    // (group T / (8 / NG)); the zero-point sums of value row (head) ln, group
+    // gam, summed over the quads
+    float zg[NG];
 #pragma unroll
-    for (int gam = 0; gam < 4; ++gam) {
+    for (int gam = 0; gam < NG; ++gam) {
       float z = 0.f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) z = fmaf(S.zz[gam][r], (float)(1 << (2 * r)) * ipscale, z);
@@ -1318,11 +1330,11 @@ __device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int h = 4 * t0 + 4 * qd + e;
+      const int h = 4 * HPL * t0 + 4 * qd + e;
       float* dst = p.partial + (((int64_t)b * p.n_q + kv * p.g + h) * Ssp + split) * kPartialStride;
 #pragma unroll
       for (int T = 0; T < 8; ++T) {
-        const float zr = __shfl(zg[T >> 1], 4 * qd + e);
+        const float zr = __shfl(zg[T / (8 / NG)], 4 * qd + e);
         if (h < p.g) dst[2 + 16 * T + ln] = fmaf(S.acc[0][T][e], accscale, zr);
       }
     }
@@ -1610,7 +1622,7 @@ decode_int2(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) float p_lds[W][(16 * CT / NG) * 32];
   __shared__ __attribute__((aligned(16))) uint8_t stage[(W == 1 ? 6 : 8) * Int2Layout{NG, MB}.bytes()];
   __shared__ u32x4 ops[W >= 4 ? kOpUnits * 64 : 1];  // code operands shared by the wavefronts of an item
-  constexpr bool kWide = NG == 4 && CT == 4;
+  constexpr bool kWide = CT * (4 / NG) == 4;
   __shared__ __attribute__((aligned(16))) uint8_t edge_lds[kWide ? W * 2 * Int2Layout{NG, MB}.bytes() : 16];
   const int item = blockIdx.x;
   const int split = item % p.splits_int2;
@@ -1882,11 +1894,12 @@ hipError_t launch_prefill_t(const DecodeParams& p, hipStream_t stream, hipEvent_
   hipLaunchKernelGGL((prefill_prologue<NG>), dim3(bkn), dim3(256), 0, stream, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = mark(ev_start)) != hipSuccess) return e;
-  // 32-channel groups: wide items, four tiles (16 kernel heads) per wavefront
-  if constexpr (NG == 4)
-    hipLaunchKernelGGL((decode_int2<NG, MB, 4, W / 4>), dim3(bkn * p.splits_int2), dim3(16 * W), 0, stream, p);
-  else
-    hipLaunchKernelGGL((decode_int2<NG, MB, 1, W>), dim3(bkn * p.splits_int2), dim3(64 * W), 0, stream, p);
+  // 32-channel groups: wide items, four tiles (16 kernel heads) per
+  // wavefront.  At 64-channel groups one tile per wavefront, four per SIMD,
+  // measured 5 % faster than two-tile wide wavefronts at two per SIMD.
+  constexpr int kCt = NG == 4 ? 4 : 1;
+  hipLaunchKernelGGL((decode_int2<NG, MB, kCt, W / kCt>), dim3(bkn * p.splits_int2), dim3(64 * (W / kCt)), 0, stream,
+                     p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = mark(ev_stop)) != hipSuccess) return e;
   hipLaunchKernelGGL(decode_bf16, dim3(bkn * (p.g / p.g_real) * p.splits_bf16), dim3(64), 0, stream, p);
