@@ -114,8 +114,8 @@ inline TileSplit tile_split(int tiles) {
     default: return {1, 1};
   }
 }
-// wavefronts per SIMD of an INT2 item whose wavefronts take ct tiles
-inline int waves_per_simd(int ct) { return ct == 1 ? 4 : 2; }
+// wavefronts per SIMD of a decode INT2 item whose wavefronts take ct tiles
+inline int waves_per_simd(int ct) { return ct == 1 ? 4 : (ct == 2 ? 3 : 2); }
 
 hipError_t launch_quant_write(const QuantParams& p, int mode, hipStream_t stream);
 hipError_t launch_bf16_write(const uint16_t* k, const uint16_t* v, const int32_t* slots, int64_t n, int n_kv,

@@ -109,10 +109,10 @@ def test_workspace_bytes_monotone(lib):
     # item, two per SIMD: 2048 at once, two rounds over 16 x 8 pairs = 32 splits
     wide = K.make_shape(n_q_heads=96, n_kv_heads=8, group=32, sink=4, recent=128)
     assert K.oscar_decode_auto_splits(wide, 16, 8200) == 32
-    # 8 query heads per KV head: two tiles on one wavefront, two per SIMD: 2048 at once, two
-    # rounds over 64 x 8 pairs = 8 splits
+    # 8 query heads per KV head: two tiles on one wavefront, three per SIMD: 3072 at once, two
+    # rounds over 64 x 8 pairs = 12 splits
     mid = K.make_shape(n_q_heads=64, n_kv_heads=8, group=32, sink=4, recent=128)
-    assert K.oscar_decode_auto_splits(mid, 64, 2100) == 8
+    assert K.oscar_decode_auto_splits(mid, 64, 2100) == 12
 
 
 # ---------------------------------------------------------------------------
