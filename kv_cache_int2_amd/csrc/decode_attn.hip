@@ -803,15 +803,13 @@ template <int NG, int MB>
 __device__ __forceinline__ u32x4 Int2Staged<NG, MB>::v_wide(int T) const {
   return v_wide_operand<NG, MB>(st, T);
 }
-template <int NG, int MB, bool WIDE>
+template <int NG, int MB>
 __device__ __forceinline__ void unpack_unit(const uint8_t* st, const Int2Offsets& o, int u, u32x4* ops) {
   constexpr Int2Layout L{NG, MB};
   const int lane = threadIdx.x & 63;
   u32x4 v;
   if (u < 4) {
     v = k_operand((*(const u32x2*)(st + (u >> 1) * L.bytes() + o.kc))[u & 1]);
-  } else if (WIDE) {
-    v = v_wide_operand<NG, MB>(st, u - 4);
   } else {
     const int kt = u - 4;
     v = v_operand(*(const uint32_t*)(st + o.vw + 4 * (kt >> 2)), *(const uint32_t*)(st + L.bytes() + o.vw + 4 * (kt >> 2)),
@@ -1015,6 +1013,7 @@ __device__ __forceinline__ void int2_pair(const Src& src, int lp0, int p_end, in
   if constexpr (kWide) {
     // ---- values, wide: A = P'[head ln][token] for one group at a time, B =
     // the group's channel tiles (8 / NG of 16 channels); rows are the 16 heads ----
+    static_assert(!SH, "wide wavefronts unpack their own operands");
     const f32x4 pf0 = *(const f32x4*)(p_lds + (2 * ln) * kPage + 4 * qd);
     const f32x4 pf1 = *(const f32x4*)(p_lds + (2 * ln + 1) * kPage + 4 * qd);
 #pragma unroll
@@ -1048,7 +1047,7 @@ __device__ __forceinline__ void int2_pair(const Src& src, int lp0, int p_end, in
 #pragma unroll
       for (int tt = 0; tt < 8 / NG; ++tt) {
         const int T = (8 / NG) * gam + tt;
-        const u32x4 bv = SH ? ops[(4 + T) * 64 + lane] : src.v_wide(T);
+        const u32x4 bv = src.v_wide(T);
         S.acc[0][T] = mfma_f16(ph, bv, S.acc[0][T]);
         S.acc[0][T] = mfma_f16(pl, bv, S.acc[0][T]);
       }
@@ -1261,9 +1260,10 @@ __device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float
         const bool leader = t0 == 0;
         const int wv = t0 / CT;  // this wavefront's index in the item
         // sharing the unpacked operands costs a second barrier per pair: it
-        // pays with 16 wavefronts per item (a prefill block, 10 % faster) and
-        // lost 18 % with 3 (wide decode groups)
-        constexpr bool kShareOps = W >= 4;
+        // pays with 8 or 16 one-tile wavefronts per item (a prefill block, 10 %
+        // faster) and lost 18 % with 3 (12 heads in three tiles) and 7 % with
+        // 4 wide wavefronts
+        constexpr bool kShareOps = W >= 4 && !kWide;
         while (lp0 + 2 <= main_end) {
           const int c0 = lp0;
           const int cn = min(64, main_end - c0);
@@ -1295,7 +1295,7 @@ __device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float
               // the code operands: one share per wavefront, published by a
               // second barrier (every wavefront has finished the previous
               // pair, whose operands these overwrite, before the first)
-              for (int u = wv; u < kOpUnits; u += W) unpack_unit<NG, MB, kWide>(stage + cur * kSlot, off, u, ops);
+              for (int u = wv; u < kOpUnits; u += W) unpack_unit<NG, MB>(stage + cur * kSlot, off, u, ops);
               barrier_no_fence();
             }
             int2_pair<NG, CT, false, kShareOps, LQ>(Int2Staged<NG, MB>{stage + cur * kSlot, off}, lp0, p_end, lo, hi, qlo,
