@@ -785,11 +785,6 @@ __device__ __forceinline__ u32x4 v_operand(uint32_t lo_src, uint32_t hi_src, int
   }
   return bv;
 }
-// The wavefronts of a multi-wavefront item share the operands of a staged
-// pair: 12 units of one u32x4 per lane (units 0-3: key words (page u / 2,
-// k-step u % 2), units 4-11: value channels kt = u - 4), each unpacked by one
-// wavefront into ops[unit][lane].
-constexpr int kOpUnits = 12;
 // Wide tiles (16 head rows, see int2_pair) take channel tiles of one group:
 // tile T holds channels 16T + ln, one byte per page at quad qd.
 template <int NG, int MB>
@@ -803,37 +798,20 @@ template <int NG, int MB>
 __device__ __forceinline__ u32x4 Int2Staged<NG, MB>::v_wide(int T) const {
   return v_wide_operand<NG, MB>(st, T);
 }
-template <int NG, int MB>
-__device__ __forceinline__ void unpack_unit(const uint8_t* st, const Int2Offsets& o, int u, u32x4* ops) {
-  constexpr Int2Layout L{NG, MB};
-  const int lane = threadIdx.x & 63;
-  u32x4 v;
-  if (u < 4) {
-    v = k_operand((*(const u32x2*)(st + (u >> 1) * L.bytes() + o.kc))[u & 1]);
-  } else {
-    const int kt = u - 4;
-    v = v_operand(*(const uint32_t*)(st + o.vw + 4 * (kt >> 2)), *(const uint32_t*)(st + L.bytes() + o.vw + 4 * (kt >> 2)),
-                  kt);
-  }
-  ops[u * 64 + lane] = v;
-}
 
 // EDGE: a masked pair.  Its tokens must lie in [lo, hi) on pages below
 // p_end, and row head h (16 t0 ... of the wavefront's tiles) sees positions up
 // to qlo + floor(h / g_real), i.e. position qlo + k when k g_real <= h (causal
 // masks of a chunk's queries; in decode every row sees the whole INT2 region).
-// SH: the code operands come unpacked from ops (shared by the item's
-// wavefronts), else each lane unpacks its own.
 // LQ: head quads of the last tile that hold a real head (the others have zero
 // digits: their logit MFMAs and sums are skipped, their logits taken as 0);
 // 0 when the last tile has none.
 // With one tile of 64-channel groups whose second head quad is empty, the
 // value rows 8-15 (that quad's (head, group) rows) carry the lo part of rows
 // 0-7 instead, so each channel tile takes one value MFMA, not two.
-template <int NG, int CT, bool EDGE, bool SH, int LQ, class Src>
+template <int NG, int CT, bool EDGE, int LQ, class Src>
 __device__ __forceinline__ void int2_pair(const Src& src, int lp0, int p_end, int lo, int hi, int qlo, int g_real,
-                                          int t0, const Int2Const<NG, CT>& K, Int2State<NG, CT>& S, float* p_lds,
-                                          const u32x4* ops) {
+                                          int t0, const Int2Const<NG, CT>& K, Int2State<NG, CT>& S, float* p_lds) {
   constexpr int HPL = 4 / NG;
   constexpr bool kPackLo = NG == 2 && CT == 1 && LQ == 1;
   // wide: 16 heads per wavefront (four tiles at 32-channel groups, two at
@@ -868,7 +846,7 @@ __device__ __forceinline__ void int2_pair(const Src& src, int lp0, int p_end, in
   for (int t = 0; t < 2; ++t) {
     u32x4 av[2];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) av[ks] = SH ? ops[(2 * t + ks) * 64 + lane] : k_operand(DK.kc[t][ks]);
+    for (int ks = 0; ks < 2; ++ks) av[ks] = k_operand(DK.kc[t][ks]);
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
       // cd[u]: sum_j 2Q_j c_j of head 4hq + qd of the tile and group gam (u =
@@ -1013,7 +991,6 @@ __device__ __forceinline__ void int2_pair(const Src& src, int lp0, int p_end, in
   if constexpr (kWide) {
     // ---- values, wide: A = P'[head ln][token] for one group at a time, B =
     // the group's channel tiles (8 / NG of 16 channels); rows are the 16 heads ----
-    static_assert(!SH, "wide wavefronts unpack their own operands");
     const f32x4 pf0 = *(const f32x4*)(p_lds + (2 * ln) * kPage + 4 * qd);
     const f32x4 pf1 = *(const f32x4*)(p_lds + (2 * ln + 1) * kPage + 4 * qd);
 #pragma unroll
@@ -1098,7 +1075,7 @@ __device__ __forceinline__ void int2_pair(const Src& src, int lp0, int p_end, in
   // ---- values on MFMA ----
 #pragma unroll
   for (int kt = 0; kt < 8; ++kt) {
-    const u32x4 bv = SH ? ops[(4 + kt) * 64 + lane] : v_operand(DV.vw[0][kt >> 2], DV.vw[1][kt >> 2], kt);
+    const u32x4 bv = v_operand(DV.vw[0][kt >> 2], DV.vw[1][kt >> 2], kt);
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
       S.acc[ct][kt] = mfma_f16(pa[ct][0], bv, S.acc[ct][kt]);
@@ -1112,7 +1089,7 @@ __device__ __forceinline__ void int2_pair(const Src& src, int lp0, int p_end, in
 // edge_lds: this wavefront's two-block area for masked pairs (wide tiles only).
 template <int NG, int MB, int CT, int W, int LQ>
 __device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float* p_lds, uint8_t* stage,
-                          u32x4* ops, uint8_t* edge_lds) {
+                          uint8_t* edge_lds) {
   constexpr Int2Layout L{NG, MB};
   constexpr int HPL = 4 / NG;
   constexpr int kTiles = W * CT;  // row tiles of the (request, KV head)
@@ -1197,11 +1174,11 @@ __device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float
             uint4* dst = (uint4*)(edge_lds + t * L.bytes());
             for (int c = lane; c < n16; c += 64) dst[c] = src[c];
           }
-          int2_pair<NG, CT, true, false, LQ>(Int2Staged<NG, MB>{edge_lds, off}, lp0, pe, lo, hi, qlo, g_real, t0, K,
-                                             S, p_lds, nullptr);
+          int2_pair<NG, CT, true, LQ>(Int2Staged<NG, MB>{edge_lds, off}, lp0, pe, lo, hi, qlo, g_real, t0, K,
+                                             S, p_lds);
         } else {
           const Int2Data<NG> D = int2_load<NG, MB>(blk(pg0), blk(pg1), off);
-          int2_pair<NG, CT, true, false, LQ>(D, lp0, pe, lo, hi, qlo, g_real, t0, K, S, p_lds, nullptr);
+          int2_pair<NG, CT, true, LQ>(D, lp0, pe, lo, hi, qlo, g_real, t0, K, S, p_lds);
         }
       };
       int lp0 = p_begin;
@@ -1244,8 +1221,8 @@ __device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float
             } else {
               vm_wait<0>();
             }
-            int2_pair<NG, CT, false, false, LQ>(Int2Staged<NG, MB>{stage + cur * kSlot, off}, lp0, p_end, lo, hi, qlo,
-                                            g_real, t0, K, S, p_lds, nullptr);
+            int2_pair<NG, CT, false, LQ>(Int2Staged<NG, MB>{stage + cur * kSlot, off}, lp0, p_end, lo, hi, qlo,
+                                            g_real, t0, K, S, p_lds);
             lp0 += 2;
             if (lp0 + 2 > lim) break;
             cur = cur == 2 ? 0 : cur + 1;
@@ -1258,12 +1235,9 @@ __device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float
         // publishes the pair to all and certifies that all have finished the
         // pair before last, whose slot the next staging load reuses
         const bool leader = t0 == 0;
-        const int wv = t0 / CT;  // this wavefront's index in the item
-        // sharing the unpacked operands costs a second barrier per pair: it
-        // pays with 8 or 16 one-tile wavefronts per item (a prefill block, 10 %
-        // faster) and lost 18 % with 3 (12 heads in three tiles) and 7 % with
-        // 4 wide wavefronts
-        constexpr bool kShareOps = W >= 4 && !kWide;
+        // (each wavefront unpacks its own code operands: sharing them through
+        // LDS took a second barrier per pair, which cost more than it saved
+        // for 3, 4 wide and 8 one-tile wavefronts)
         while (lp0 + 2 <= main_end) {
           const int c0 = lp0;
           const int cn = min(64, main_end - c0);
@@ -1291,15 +1265,8 @@ __device__ void int2_item(const DecodeParams& p, int b, int kv, int split, float
               }
             }
             barrier_no_fence();
-            if constexpr (kShareOps) {
-              // the code operands: one share per wavefront, published by a
-              // second barrier (every wavefront has finished the previous
-              // pair, whose operands these overwrite, before the first)
-              for (int u = wv; u < kOpUnits; u += W) unpack_unit<NG, MB>(stage + cur * kSlot, off, u, ops);
-              barrier_no_fence();
-            }
-            int2_pair<NG, CT, false, kShareOps, LQ>(Int2Staged<NG, MB>{stage + cur * kSlot, off}, lp0, p_end, lo, hi, qlo,
-                                                g_real, t0, K, S, p_lds, ops);
+            int2_pair<NG, CT, false, LQ>(Int2Staged<NG, MB>{stage + cur * kSlot, off}, lp0, p_end, lo, hi, qlo,
+                                                g_real, t0, K, S, p_lds);
             lp0 += 2;
             if (lp0 + 2 > lim) break;
             cur = (cur + 1) & 3;
@@ -1622,7 +1589,6 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(CT == 1 
 decode_int2(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) float p_lds[W][(16 * CT / NG) * 32];
   __shared__ __attribute__((aligned(16))) uint8_t stage[(W == 1 ? 6 : 8) * Int2Layout{NG, MB}.bytes()];
-  __shared__ u32x4 ops[W >= 4 ? kOpUnits * 64 : 1];  // code operands shared by the wavefronts of an item
   constexpr bool kWide = CT * (4 / NG) == 4;
   __shared__ __attribute__((aligned(16))) uint8_t edge_lds[kWide ? W * 2 * Int2Layout{NG, MB}.bytes() : 16];
   const int item = blockIdx.x;
@@ -1635,7 +1601,7 @@ decode_int2(DecodeParams p) {
     // skips that tile's logits
     const int last = (W > 1 ? __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) * CT : 0) + CT - 1;
     if (4 * last >= p.g) {
-      int2_item<NG, MB, CT, W, 0>(p, bk / p.n_kv, bk % p.n_kv, split, pl, stage, ops, el);
+      int2_item<NG, MB, CT, W, 0>(p, bk / p.n_kv, bk % p.n_kv, split, pl, stage, el);
       return;
     }
   }
@@ -1645,11 +1611,11 @@ decode_int2(DecodeParams p) {
     // its logits (decided once per wavefront: the tile index is uniform)
     const int last = (W > 1 ? __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) * CT : 0) + CT - 1;
     if (8 * last + 4 >= p.g) {
-      int2_item<NG, MB, CT, W, 1>(p, bk / p.n_kv, bk % p.n_kv, split, pl, stage, ops, el);
+      int2_item<NG, MB, CT, W, 1>(p, bk / p.n_kv, bk % p.n_kv, split, pl, stage, el);
       return;
     }
   }
-  int2_item<NG, MB, CT, W, 4 / NG>(p, bk / p.n_kv, bk % p.n_kv, split, pl, stage, ops, el);
+  int2_item<NG, MB, CT, W, 4 / NG>(p, bk / p.n_kv, bk % p.n_kv, split, pl, stage, el);
 }
 
 // items: (request, KV head, query of the launch, bf16 split)
