@@ -99,7 +99,8 @@ struct DecodeParams {
 
 // How the 16-row tiles of a (request, KV head) spread over the wavefronts of
 // one INT2 work item: CT tiles per wavefront (they share the unpacked codes,
-// at 4 / CT wavefronts per SIMD), W wavefronts (they share the staged pages).
+// at waves_per_simd(CT) wavefronts per SIMD), W wavefronts (they share the
+// staged pages).
 struct TileSplit {
   int ct, w;
 };
