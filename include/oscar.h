@@ -102,7 +102,9 @@ typedef struct oscar_layer {
   const float* r_k;
   const float* r_v;
   float tau_k;         /* clip threshold for rotated keys (x_rot clamped to [-tau, tau]) */
-  float tau_v;
+  float tau_v;         /* Both finite and >= 0, and at most 65504 with fp16 scale and
+                          zero (so that neither can overflow); calls taking a layer
+                          return OSCAR_EINVAL otherwise. */
 } oscar_layer;
 
 /* Device storage of one layer (caller-owned; 256-byte aligned). */

@@ -667,12 +667,19 @@ static oscar_status check_cache(const oscar_cache* c, bool need_int2, bool need_
   return OSCAR_OK;
 }
 
-static oscar_status check_layer(const oscar_layer* l) {
+// The clip thresholds must be finite and >= 0.  With fp16 scale and zero they
+// must also be at most 65504, the largest finite fp16: every clipped value then
+// has |x| <= 65504, so z = fp16(mn) and s = fp16((mx - mn) / 3) are finite and
+// every code (x - z) / s is a finite number before its clamp to 0..3.  (FP8
+// scale and zero saturate at 448 instead of overflowing.)
+static oscar_status check_layer(const oscar_layer* l, const oscar_shape* shape) {
   if (!l || !l->r_k) return fail(OSCAR_EINVAL, "layer rotation R_K missing");
   if (!aligned(l->r_k, 16) || (l->r_v && !aligned(l->r_v, 16)))
     return fail(OSCAR_EINVAL, "rotations must be 16-byte aligned");
-  if (std::isnan(l->tau_k) || std::isnan(l->tau_v) || l->tau_k < 0 || l->tau_v < 0)
-    return fail(OSCAR_EINVAL, "clip thresholds must be >= 0");
+  if (!std::isfinite(l->tau_k) || !std::isfinite(l->tau_v) || l->tau_k < 0 || l->tau_v < 0)
+    return fail(OSCAR_EINVAL, "clip thresholds must be finite and >= 0");
+  if (mb_of(shape) == 4 && (l->tau_k > 65504.f || l->tau_v > 65504.f))
+    return fail(OSCAR_EINVAL, "clip thresholds above 65504 would overflow the fp16 scale and zero");
   return OSCAR_OK;
 }
 
@@ -683,7 +690,7 @@ oscar_status oscar_quant_write(const oscar_shape* shape, const oscar_layer* laye
   if (st) return st;
   if (n < 0) return fail(OSCAR_EINVAL, "n < 0");
   if (n == 0) return ok();
-  if ((st = check_layer(layer)) || (st = check_cache(cache, true, false))) return st;
+  if ((st = check_layer(layer, shape)) || (st = check_cache(cache, true, false))) return st;
   if (!k_bf16 || !v_bf16 || !int2_slots) return fail(OSCAR_EINVAL, "NULL input");
   if (n > (1LL << 31) / 16) return fail(OSCAR_EINVAL, "n too large");
   QuantParams p{};
@@ -710,7 +717,7 @@ oscar_status oscar_requant_from_bf16(const oscar_shape* shape, const oscar_layer
   if (st) return st;
   if (n < 0) return fail(OSCAR_EINVAL, "n < 0");
   if (n == 0) return ok();
-  if ((st = check_layer(layer)) || (st = check_cache(cache, true, true))) return st;
+  if ((st = check_layer(layer, shape)) || (st = check_cache(cache, true, true))) return st;
   if (!src_bf16_slots || !dst_int2_slots) return fail(OSCAR_EINVAL, "NULL slot array");
   QuantParams p{};
   p.bf16_pages = (const uint8_t*)cache->bf16_pages;
@@ -825,7 +832,7 @@ static oscar_status decode_common(const oscar_shape* shape, const oscar_layer* l
     return fail(OSCAR_EINVAL, "q/out must be 16-byte and workspace 256-byte aligned");
   if (!bf16_bt || max_bf16_pages < 1) return fail(OSCAR_EINVAL, "bf16 block table missing");
   if (!baseline) {
-    if ((st = check_layer(layer)) || (st = check_cache(cache, true, true))) return st;
+    if ((st = check_layer(layer, shape)) || (st = check_cache(cache, true, true))) return st;
     if (!int2_bt || max_int2_pages < 1) return fail(OSCAR_EINVAL, "INT2 block table missing");
   } else {
     if ((st = check_cache(cache, false, true))) return st;
@@ -985,7 +992,7 @@ oscar_status oscar_prefill_attn(const oscar_shape* shape, const oscar_layer* lay
   if (!q || !ctx_lens || !out || !workspace) return fail(OSCAR_EINVAL, "NULL argument");
   if (!aligned(q, 16) || !aligned(out, 16) || !aligned(workspace, 256))
     return fail(OSCAR_EINVAL, "q/out must be 16-byte and workspace 256-byte aligned");
-  if ((st = check_layer(layer)) || (st = check_cache(cache, true, true))) return st;
+  if ((st = check_layer(layer, shape)) || (st = check_cache(cache, true, true))) return st;
   if (!int2_bt || max_int2_pages < 1 || !bf16_bt || max_bf16_pages < 1)
     return fail(OSCAR_EINVAL, "block tables missing");
   if (splits_int2 < 0 || splits_bf16 < 0 || splits_int2 > 4096 || splits_bf16 > 4096)

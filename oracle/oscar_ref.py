@@ -22,7 +22,9 @@ narrower type (bf16 inputs, fp32 rotations and thresholds, fp16 scale/zero,
 2-bit codes).  Readings of points the pages leave open are marked READING.
 
 Pinned by tests/test_oracle_pins.py (identities, closed forms, brute force,
-special cases reducing to library routines, the pages' printed constants).
+special cases reducing to library routines, the pages' printed constants) and
+tests/test_oracle_pins_calibration.py (the composite rotation's closed form,
+the clip threshold's quantile and pooling, the query heads of a KV head).
 """
 from __future__ import annotations
 

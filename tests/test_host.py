@@ -77,6 +77,19 @@ def test_launch_argument_errors_before_any_gpu_call(lib):
     ok_cache = K.Cache(0x1000, 4, 0x2000, 4)
     assert lib.oscar_quant_write(C.byref(sh), C.byref(nan_layer), C.byref(ok_cache), 0x10, 0x10, 0x10, 1,
                                  None) == K.OSCAR_EINVAL
+    # an infinite threshold, or one past the largest fp16 with fp16 scale and zero, could
+    # overflow s or z; FP8 scale and zero saturate, so 1e5 is accepted there
+    for tk, tv in ((float("inf"), 1.0), (1.0, float("-inf")), (65600.0, 1.0), (1.0, 1e6)):
+        lay_bad = K.Layer(0x1000, 0x2000, tk, tv)
+        assert lib.oscar_quant_write(C.byref(sh), C.byref(lay_bad), C.byref(ok_cache), 0x10, 0x10, 0x10, 1,
+                                     None) == K.OSCAR_EINVAL
+        assert b"thresholds" in lib.oscar_last_error()
+    sh8 = K.make_shape(group=64, scale_bits=8)
+    big = K.Layer(0x1000, 0x2000, 1e5, 1e5)
+    bad_ptr_cache = K.Cache(0x1010, 4, 0x2000, 4)
+    assert lib.oscar_quant_write(C.byref(sh8), C.byref(big), C.byref(bad_ptr_cache), 0x10, 0x10, 0x10, 1,
+                                 None) == K.OSCAR_EINVAL
+    assert b"thresholds" not in lib.oscar_last_error()
     # R_K is required; R_V may be NULL (folded into the model's projections), and when given it
     # must be aligned.  The layer passes its check when only R_V is missing: the error is the cache's.
     no_rk = K.Layer(None, 0x2000, 1.0, 1.0)
