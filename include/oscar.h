@@ -345,6 +345,11 @@ oscar_status oscar_decode_step(const oscar_shape* shape, const oscar_layer* laye
  * count, and clears them. */
 oscar_status oscar_profile_enable(int32_t on);
 oscar_status oscar_profile_read(double* main_ms, int64_t* launches);
+/* The same, and the first cap launches' durations in milliseconds, in launch
+ * order, into the host array ms_each (cap >= 0; ms_each may be NULL when cap
+ * is 0).  All recorded events are released even if timing one fails
+ * (OSCAR_EHIP). */
+oscar_status oscar_profile_read_each(float* ms_each, int64_t cap, double* main_ms, int64_t* launches);
 
 #ifdef __cplusplus
 }

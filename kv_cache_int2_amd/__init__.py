@@ -83,6 +83,7 @@ _SIGS = {
     "oscar_plan_decode_step": (C.c_int32, [P, P, C.c_int32, P, P, P, P, P, P, P]),
     "oscar_profile_enable": (C.c_int32, [C.c_int32]),
     "oscar_profile_read": (C.c_int32, [C.POINTER(C.c_double), I64P]),
+    "oscar_profile_read_each": (C.c_int32, [P, C.c_int64, C.POINTER(C.c_double), I64P]),
 }
 EXPORTED = tuple(_SIGS)
 
@@ -359,3 +360,12 @@ def oscar_profile_read():
     ms, n = C.c_double(), C.c_int64()
     _check(lib().oscar_profile_read(C.byref(ms), C.byref(n)))
     return ms.value, n.value
+
+
+def oscar_profile_read_each(cap: int = 1 << 16):
+    """(total ms, launch count, per-launch ms as a float32 array of the first cap launches)."""
+    import numpy as np
+    each = np.zeros(max(cap, 1), np.float32)
+    ms, n = C.c_double(), C.c_int64()
+    _check(lib().oscar_profile_read_each(each.ctypes.data, cap, C.byref(ms), C.byref(n)))
+    return ms.value, n.value, each[:min(n.value, cap)].copy()

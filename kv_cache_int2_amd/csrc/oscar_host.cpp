@@ -1054,21 +1054,30 @@ oscar_status oscar_profile_enable(int32_t on) {
   return ok();
 }
 
-oscar_status oscar_profile_read(double* main_ms, int64_t* launches) {
-  if (!main_ms || !launches) return fail(OSCAR_EINVAL, "NULL argument");
+oscar_status oscar_profile_read_each(float* ms_each, int64_t cap, double* main_ms, int64_t* launches) {
+  if (!main_ms || !launches || cap < 0 || (cap > 0 && !ms_each)) return fail(OSCAR_EINVAL, "bad argument");
   double total = 0.0;
+  int64_t i = 0;
+  oscar_status st = OSCAR_OK;
   for (auto& pr : g_prof.events) {
     float ms = 0.f;
-    if (hipEventSynchronize(pr.second) != hipSuccess || hipEventElapsedTime(&ms, pr.first, pr.second) != hipSuccess)
-      return fail(OSCAR_EHIP, "event timing failed");
+    if (st == OSCAR_OK &&
+        (hipEventSynchronize(pr.second) != hipSuccess || hipEventElapsedTime(&ms, pr.first, pr.second) != hipSuccess))
+      st = fail(OSCAR_EHIP, "event timing failed");
     total += ms;
+    if (i < cap) ms_each[i] = ms;
+    ++i;
     (void)hipEventDestroy(pr.first);
     (void)hipEventDestroy(pr.second);
   }
   *launches = (int64_t)g_prof.events.size();
   g_prof.events.clear();
   *main_ms = total;
-  return ok();
+  return st ? st : ok();
+}
+
+oscar_status oscar_profile_read(double* main_ms, int64_t* launches) {
+  return oscar_profile_read_each(nullptr, 0, main_ms, launches);
 }
 
 oscar_status oscar_decode_attn_bf16_baseline(const oscar_shape* shape, const oscar_cache* cache, const void* q,
