@@ -259,6 +259,23 @@ oscar_status oscar_decode_attn(const oscar_shape* shape, const oscar_layer* laye
                                int32_t splits_int2, int32_t splits_bf16, float* out, void* workspace,
                                size_t workspace_bytes, void* stream);
 
+/* Allocation-free decode, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): oscar_decode_attn with the same arguments and results, minus the
+ * workspace, which is a device array inside the library (one copy per GPU,
+ * held until the process ends; its size is
+ * oscar_decode_noalloc_max_workspace_bytes(), 64 MiB).  A call that needs more
+ * (oscar_decode_workspace_bytes with the splits it resolves to) returns
+ * OSCAR_EINVAL before enqueueing anything.  The call allocates nothing: the
+ * first call on a device only looks up the array's address there.  Calls that
+ * overlap on one GPU (other streams, other threads) share the array and race;
+ * serialise them.  Nothing in the array needs clearing between calls. */
+oscar_status oscar_decode_attn_noalloc(const oscar_shape* shape, const oscar_layer* layer, const oscar_cache* cache,
+                                       const void* q, int32_t batch, const int32_t* int2_bt, int32_t max_int2_pages,
+                                       const int32_t* bf16_bt, int32_t max_bf16_pages, const int32_t* ctx_lens,
+                                       int32_t splits_int2, int32_t splits_bf16, float* out, void* stream);
+size_t oscar_decode_noalloc_max_workspace_bytes(void);
+
 /* The same decode kernels over an all-bf16 cache (the comparison baseline):
  * position p of request b lives in bf16 logical page p/16 (bf16_bt row b),
  * slot p%16; sink/recent/INT2 regions are not used. */

@@ -76,6 +76,9 @@ _SIGS = {
     "oscar_prefill_attn": (C.c_int32, [C.POINTER(Shape), C.POINTER(Layer), C.POINTER(Cache), P, C.c_int32,
                                        C.c_int32, P, C.c_int32, P, C.c_int32, P, C.c_int32, C.c_int32, P, P,
                                        C.c_size_t, P]),
+    "oscar_decode_attn_noalloc": (C.c_int32, [C.POINTER(Shape), C.POINTER(Layer), C.POINTER(Cache), P, C.c_int32,
+                                              P, C.c_int32, P, C.c_int32, P, C.c_int32, C.c_int32, P, P]),
+    "oscar_decode_noalloc_max_workspace_bytes": (C.c_size_t, []),
     "oscar_decode_attn_bf16_baseline": (C.c_int32, [C.POINTER(Shape), C.POINTER(Cache), P, C.c_int32, P,
                                                     C.c_int32, P, C.c_int32, P, P, C.c_size_t, P]),
     "oscar_decode_auto_splits": (C.c_int32, [C.POINTER(Shape), C.c_int32, C.c_int32]),
@@ -322,6 +325,18 @@ def oscar_prefill_attn(shape, layer, cache, q, int2_bt, bf16_bt, ctx_lens, out, 
                                     _ptr(int2_bt), int2_bt.shape[1], _ptr(bf16_bt), bf16_bt.shape[1],
                                     _ptr(ctx_lens), splits_int2, splits_bf16, _ptr(out), _ptr(workspace),
                                     workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def oscar_decode_attn_noalloc(shape, layer, cache, q, int2_bt, bf16_bt, ctx_lens, out, splits_int2=0, splits_bf16=0,
+                              stream=None):
+    batch = q.shape[0]
+    _check(lib().oscar_decode_attn_noalloc(C.byref(shape), C.byref(layer), C.byref(cache), _ptr(q), batch,
+                                           _ptr(int2_bt), int2_bt.shape[1], _ptr(bf16_bt), bf16_bt.shape[1],
+                                           _ptr(ctx_lens), splits_int2, splits_bf16, _ptr(out), _stream(stream)))
+
+
+def oscar_decode_noalloc_max_workspace_bytes() -> int:
+    return int(lib().oscar_decode_noalloc_max_workspace_bytes())
 
 
 def oscar_decode_attn_bf16_baseline(shape, cache, q, bf16_bt, ctx_lens, out, workspace, splits=0, stream=None):

@@ -43,6 +43,7 @@
 #include <stdint.h>
 
 #include <cmath>
+#include <mutex>
 #include <type_traits>
 
 #include "oscar_internal.h"
@@ -1938,6 +1939,50 @@ void decode_workspace_carve(DecodeParams& p, void* ws) {
   p.qaux = (float*)w;
   w += align256(bkn * (1 + 16 * p.ct) * sizeof(float));
   p.partial = (float*)w;
+}
+
+
+// ---- The allocation-free decode's workspace ----
+// For callers that cannot allocate device memory (code under graph capture,
+// serving loops, harnesses that forbid it): the split-K workspace of
+// oscar_decode_attn_noalloc lives in this array.  Each GPU the library runs on
+// holds its own copy for the life of the process.  In host code the array's
+// name is not a device address: the address is looked up per device with
+// hipGetSymbolAddress and only that address is handed to kernels.  Every byte
+// a launch reads is written earlier in the same launch, so nothing is cleared;
+// calls that overlap on one GPU share the array and race.
+static __device__ __align__(256) uint8_t scratch[kDecodeScratchBytes];
+
+namespace {
+constexpr int kScratchMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kScratchMaxDevices] = {};
+}  // namespace
+
+hipError_t decode_scratch(hipStream_t stream, void** ptr, size_t* bytes) {
+  int dev = -1;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    // look the address up with the stream's device current
+    int cur = -1;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* addr = nullptr;
+    e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t back = hipSetDevice(cur);
+      if (e == hipSuccess) e = back;
+    }
+    if (e != hipSuccess) return e;
+    if (!addr) return hipErrorInvalidSymbol;
+    g_scratch_addr[dev] = addr;
+  }
+  *ptr = g_scratch_addr[dev];
+  *bytes = kDecodeScratchBytes;
+  return hipSuccess;
 }
 
 }  // namespace oscar

@@ -817,18 +817,25 @@ struct StepWrites {
   const int32_t* step_slots;
 };
 
+// The split-K workspace of a decode launch: caller memory, or (use_scratch)
+// the library's own device array, whose address is looked up once per device.
+struct DecodeWorkspace {
+  void* ptr;
+  size_t bytes;
+  bool use_scratch;
+};
+
 static oscar_status decode_common(const oscar_shape* shape, const oscar_layer* layer, const oscar_cache* cache,
                                   const void* q, int32_t batch, const int32_t* int2_bt, int32_t max_int2_pages,
                                   const int32_t* bf16_bt, int32_t max_bf16_pages, const int32_t* ctx_lens,
-                                  int32_t splits_int2, int32_t splits_bf16, float* out, void* workspace,
-                                  size_t workspace_bytes, void* stream, bool baseline,
-                                  const StepWrites* writes = nullptr) {
+                                  int32_t splits_int2, int32_t splits_bf16, float* out, DecodeWorkspace ws,
+                                  void* stream, bool baseline, const StepWrites* writes = nullptr) {
   oscar_status st = check_shape(shape);
   if (st) return st;
   if (batch < 0) return fail(OSCAR_EINVAL, "batch < 0");
   if (batch == 0) return ok();
-  if (!q || !ctx_lens || !out || !workspace) return fail(OSCAR_EINVAL, "NULL argument");
-  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(workspace, 256))
+  if (!q || !ctx_lens || !out || (!ws.use_scratch && !ws.ptr)) return fail(OSCAR_EINVAL, "NULL argument");
+  if (!aligned(q, 16) || !aligned(out, 16) || (!ws.use_scratch && !aligned(ws.ptr, 256)))
     return fail(OSCAR_EINVAL, "q/out must be 16-byte and workspace 256-byte aligned");
   if (!bf16_bt || max_bf16_pages < 1) return fail(OSCAR_EINVAL, "bf16 block table missing");
   if (!baseline) {
@@ -882,8 +889,17 @@ static oscar_status decode_common(const oscar_shape* shape, const oscar_layer* l
     if (std::isfinite(smax) && smax > 0) p.p_scale_exp = (float)std::clamp((int)std::floor(std::log2(32768.0 / smax)) - 1, -60, 60);
   }
   const size_t need = decode_workspace_bytes(batch, p.n_q, p.n_kv, p.ct, p.splits_int2 + p.splits_bf16);
-  if (workspace_bytes < need) return fail(OSCAR_EINVAL, "workspace %zu bytes < %zu needed", workspace_bytes, need);
-  decode_workspace_carve(p, workspace);
+  if (ws.use_scratch) {
+    if (need > kDecodeScratchBytes)
+      return fail(OSCAR_EINVAL,
+                  "this decode needs %zu bytes of split-K workspace, more than the %zu bytes the allocation-free "
+                  "entry point holds: use fewer splits, a smaller batch, or oscar_decode_attn with a workspace",
+                  need, kDecodeScratchBytes);
+    if ((st = hip_status(decode_scratch((hipStream_t)stream, &ws.ptr, &ws.bytes), "scratch address lookup")))
+      return st;
+  }
+  if (ws.bytes < need) return fail(OSCAR_EINVAL, "workspace %zu bytes < %zu needed", ws.bytes, need);
+  decode_workspace_carve(p, ws.ptr);
   p.out = out;
   if (writes) {
     p.step_slots = writes->step_slots;
@@ -895,7 +911,7 @@ static oscar_status decode_common(const oscar_shape* shape, const oscar_layer* l
     p.tau_v = layer->tau_v;
   }
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
-  if (g_prof.on) {
+  if (g_prof.on && !ws.use_scratch) {
     if (hipEventCreate(&ev0) != hipSuccess || hipEventCreate(&ev1) != hipSuccess)
       return fail(OSCAR_EHIP, "hipEventCreate failed");
     g_prof.events.emplace_back(ev0, ev1);
@@ -914,7 +930,8 @@ oscar_status oscar_decode_step(const oscar_shape* shape, const oscar_layer* laye
     return fail(OSCAR_EINVAL, "step inputs misaligned");
   const StepWrites w{k_new, v_new, step_slots};
   return decode_common(shape, layer, cache, q, batch, int2_bt, max_int2_pages, bf16_bt, max_bf16_pages, ctx_lens,
-                       splits_int2, splits_bf16, out, workspace, workspace_bytes, stream, false, &w);
+                       splits_int2, splits_bf16, out, DecodeWorkspace{workspace, workspace_bytes, false}, stream,
+                       false, &w);
 }
 
 
@@ -924,8 +941,19 @@ oscar_status oscar_decode_attn(const oscar_shape* shape, const oscar_layer* laye
                                int32_t splits_int2, int32_t splits_bf16, float* out, void* workspace,
                                size_t workspace_bytes, void* stream) {
   return decode_common(shape, layer, cache, q, batch, int2_bt, max_int2_pages, bf16_bt, max_bf16_pages, ctx_lens,
-                       splits_int2, splits_bf16, out, workspace, workspace_bytes, stream, false);
+                       splits_int2, splits_bf16, out, DecodeWorkspace{workspace, workspace_bytes, false}, stream,
+                       false);
 }
+
+oscar_status oscar_decode_attn_noalloc(const oscar_shape* shape, const oscar_layer* layer, const oscar_cache* cache,
+                                       const void* q, int32_t batch, const int32_t* int2_bt, int32_t max_int2_pages,
+                                       const int32_t* bf16_bt, int32_t max_bf16_pages, const int32_t* ctx_lens,
+                                       int32_t splits_int2, int32_t splits_bf16, float* out, void* stream) {
+  return decode_common(shape, layer, cache, q, batch, int2_bt, max_int2_pages, bf16_bt, max_bf16_pages, ctx_lens,
+                       splits_int2, splits_bf16, out, DecodeWorkspace{nullptr, 0, true}, stream, false);
+}
+
+size_t oscar_decode_noalloc_max_workspace_bytes(void) { return kDecodeScratchBytes; }
 
 // Chunked prefill: queries per launch so that the kernel heads (queries x
 // model heads, at most 64: the prologue's capacity) fill at most 16 tiles of
@@ -1085,7 +1113,7 @@ oscar_status oscar_decode_attn_bf16_baseline(const oscar_shape* shape, const osc
                                              const int32_t* ctx_lens, int32_t splits, float* out, void* workspace,
                                              size_t workspace_bytes, void* stream) {
   return decode_common(shape, nullptr, cache, q, batch, nullptr, 0, bf16_bt, max_bf16_pages, ctx_lens, 0, splits,
-                       out, workspace, workspace_bytes, stream, true);
+                       out, DecodeWorkspace{workspace, workspace_bytes, false}, stream, true);
 }
 
 }  // extern "C"

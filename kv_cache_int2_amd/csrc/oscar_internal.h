@@ -132,4 +132,11 @@ hipError_t launch_prefill(const DecodeParams& p, hipStream_t stream, hipEvent_t 
 size_t decode_workspace_bytes(int batch, int n_q, int n_kv, int ct, int splits_total);
 void decode_workspace_carve(DecodeParams& p, void* ws);
 
+// The allocation-free decode's workspace: a device array of this size in the
+// library (one copy per GPU, held until the process ends).  decode_scratch
+// returns its address on the device of `stream` (the current device for the
+// null stream), looking the address up on the first call per device.
+constexpr size_t kDecodeScratchBytes = size_t(64) << 20;
+hipError_t decode_scratch(hipStream_t stream, void** ptr, size_t* bytes);
+
 }  // namespace oscar
