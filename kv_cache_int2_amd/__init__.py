@@ -11,7 +11,9 @@ import ctypes as C
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "liboscar.so")
+# OSCAR_LIB names another build of the same library (the host-sanitizer
+# build liboscar_san.so is loaded this way by its test).
+LIB_PATH = os.environ.get("OSCAR_LIB") or os.path.join(HERE, "liboscar.so")
 
 OSCAR_OK, OSCAR_EINVAL, OSCAR_ENOMEM, OSCAR_EHIP, OSCAR_EUNSUPPORTED = 0, -1, -2, -3, -4
 PAGE = 16

@@ -37,6 +37,47 @@ def _run(cmd):
     return out
 
 
+SAN_LIB = os.path.join(HERE, "liboscar_san.so")
+# host-only sanitizers: every -fsanitize applies to the host compilation
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-g"]
+
+
+def asan_runtime() -> str:
+    """The shared AddressSanitizer runtime of hipcc's clang (preloaded into
+    the Python process that loads the sanitized library)."""
+    import glob
+    hits = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not hits:
+        raise RuntimeError("clang AddressSanitizer runtime not found")
+    return hits[-1]
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """liboscar_san.so: the host C++ (pool, planner, calibration, argument
+    checks) built with AddressSanitizer and UndefinedBehaviorSanitizer, linked
+    with the regular device objects.  For host tests on the CPU only."""
+    hipcc = _hipcc()
+    if not all(os.path.exists(os.path.join(BUILD, f + ".o")) for f in os.listdir(CSRC) if f.endswith(".hip")):
+        build(verbose)
+    san_dir = os.path.join(BUILD, "san")
+    os.makedirs(san_dir, exist_ok=True)
+    objs = []
+    for f in sorted(os.listdir(CSRC)):
+        if f.endswith(".hip"):
+            objs.append(os.path.join(BUILD, f + ".o"))
+        elif f.endswith(".cpp"):
+            obj = os.path.join(san_dir, f + ".o")
+            out = _run([hipcc, *COMMON, *SAN_FLAGS, "-c", os.path.join(CSRC, f), "-o", obj])
+            if verbose and out.strip():
+                print(out, file=sys.stderr)
+            objs.append(obj)
+    tmp = SAN_LIB + ".tmp"
+    _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *SAN_FLAGS, "-shared-libasan", *objs, "-o", tmp])
+    os.replace(tmp, SAN_LIB)
+    return SAN_LIB
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     hipcc = _hipcc()
@@ -59,4 +100,7 @@ def build(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    if "--sanitize" in sys.argv:
+        print(build_sanitized(verbose=True))
+    else:
+        print(build(verbose=True))
