@@ -58,6 +58,12 @@ def parse():
     ap.add_argument("--chunk", type=int, default=128, help="queries per request in --mode prefill")
     ap.add_argument("--unfused", action="store_true",
                     help="separate write calls and in-order kernels instead of the fused decode step")
+    ap.add_argument("--interleave", action="store_true",
+                    help="each step also runs the workload's chunked-prefill writes (stress 16x128k: 16 chunks of "
+                         "4096 tokens, bf16 in, quant_write) into a separate page pool, on the same stream")
+    ap.add_argument("--cold-flush-mb", type=int, default=0,
+                    help="before every step, overwrite a buffer of this many MB (above the 256 MB MALL: the step "
+                         "reads its cache cold); the step's GPU time is then taken from events around it")
     ap.add_argument("--no-baseline", action="store_true", help="skip the bf16 same-kernel baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -302,6 +308,26 @@ def main():
     tables = [to_dev_i32(i2_bt), to_dev_i32(bf_bt)]
     ctx_hist = []
 
+    # chunked-prefill writes of other requests, interleaved with each step:
+    # inputs resident in HBM, destinations a page pool of their own
+    iw = None
+    if args.interleave:
+        if not w.write_chunks:
+            raise SystemExit(f"workload {w.name} defines no interleaved write chunks")
+        nc, ct = w.write_chunks, w.write_chunk
+        n_w = nc * ct
+        dcw = DeviceCache(sh, r_k, r_v, tau_k, tau_v, n_w // 16 + 1, 1)
+        kw = np.empty((n_w, hkv, 128), np.uint16)
+        vw = np.empty_like(kw)
+        for c in range(nc):
+            kw[c * ct:(c + 1) * ct], vw[c * ct:(c + 1) * ct] = synth.kv_request_bf16(w, 100_000 + c, 0, ct)
+        iw = (nc, ct, dcw, to_dev_bits(kw), to_dev_bits(vw), to_dev_i32(np.arange(n_w, dtype=np.int32)))
+        del kw, vw
+        log(f"interleaved writes: {nc} chunks x {ct} tokens per step")
+    flush = torch.empty(args.cold_flush_mb << 20, dtype=torch.uint8, device="cuda") if args.cold_flush_mb else None
+    step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_steps)]
+    write_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_steps)]
+
     def step(st):
         n_age, changed = planner.step()
         host_small[st].copy_(torch.from_numpy(planner.buf))
@@ -312,6 +338,9 @@ def main():
             tables[1] = to_dev_i32(bf_bt)
         d = dev_small[st]
         si_ = st % n_in
+        if flush is not None:
+            flush.fill_(st & 0xFF)
+        step_ev[st][0].record()
         if args.unfused:
             if n_age:
                 K.oscar_requant_from_bf16(sh, dc.layer, dc.cache, d[2], d[3], n=B)
@@ -322,6 +351,14 @@ def main():
         else:
             K.oscar_decode_step(sh, dc.layer, dc.cache, new_k_d[si_], new_v_d[si_], d[:4], q_d[si_], tables[0],
                                 tables[1], d[4], out, ws, si, sb_step)
+        step_ev[st][1].record()
+        if iw is not None:
+            nc, ct, dcw, kw_d, vw_d, slots_w = iw
+            write_ev[st][0].record()
+            for c in range(nc):
+                K.oscar_quant_write(sh, dcw.layer, dcw.cache, kw_d[c * ct:(c + 1) * ct], vw_d[c * ct:(c + 1) * ct],
+                                    slots_w[c * ct:(c + 1) * ct])
+            write_ev[st][1].record()
         ctx_hist.append(planner.buf[4].astype(np.int64).copy())
 
     # ---- clock settle: read-only decode of the filled cache, untimed, for a fixed wall time ----
@@ -351,13 +388,40 @@ def main():
     main_ms = float(each_ms.sum())
     if warm_ms.size:
         log("warm-up decode_int2 us: " + " ".join(f"{v * 1e3:.0f}" for v in warm_ms[:32]))
+    step_gpu_us = float(np.mean([a.elapsed_time(b) for a, b in step_ev[args.warmup:]])) * 1e3
+    interleaved = None
+    if iw is not None:
+        nc, ct = iw[0], iw[1]
+        n_w = nc * ct
+        wr_us = float(np.mean([a.elapsed_time(b) for a, b in write_ev[args.warmup:]])) * 1e3
+        wr_bytes = n_w * hkv * (2 * 128 * 2 + 2 * (32 + (128 // group) * mb))
+        interleaved = {"chunks": nc, "chunk_tokens": ct, "us_per_step": round(wr_us, 1),
+                       "tokens_per_s": n_w / (wr_us * 1e-6), "bytes_per_step": wr_bytes,
+                       "gbs": round(wr_bytes / (wr_us * 1e-6) / 1e9, 1),
+                       "frac": round(wr_bytes / (wr_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"interleaved writes: {wr_us:.1f} us per step for {n_w} tokens ({interleaved['gbs']} GB/s); "
+            f"decode step on the GPU {step_gpu_us:.1f} us")
     elapsed = t1 - t0
     tokens = int(sum(c.sum() for c in ctx_hist))
     value = tokens / elapsed
+    value_basis = "wall time of the timed steps" + (" (each with its interleaved writes)" if iw is not None else "")
+    if flush is not None:
+        # the wall time holds the cache flushes: count the steps' own GPU time
+        elapsed = step_gpu_us * 1e-6 * args.steps
+        value = tokens / elapsed
+        value_basis = "GPU time of the timed steps (events around each step; the flush before it excluded)"
     main_avg_ms = main_ms / max(launches, 1)
     alg_step = np.mean([algorithmic_bytes(c, hkv, hq, group, w.sink, w.recent, mb) for c in ctx_hist])
     alg = np.mean([int2_kernel_bytes(c, hkv, group, w.sink, w.recent, mb) for c in ctx_hist])
     achieved = alg / (main_avg_ms * 1e-3) / 1e9
+    # shared-prefix batches: the prefix's complete INT2 pages ([sink, prefix - recent)) are one
+    # physical copy read by every request; count them once for the HBM roofline
+    alg_unique = alg
+    if w.shared_prefix:
+        shared_i2 = max(0, w.shared_prefix - w.recent - w.sink)
+        alg_unique = alg - (B - 1) * shared_i2 * hkv * 2 * (32 + (128 // group) * mb)
+        log(f"shared prefix: INT2 bytes per launch {alg:.0f} logical, {alg_unique:.0f} unique "
+            f"({alg_unique / (main_avg_ms * 1e-3) / 1e9 / HBM_PEAK_GBS:.1%} of peak on unique bytes)")
     log(f"timed {args.steps} steps in {elapsed * 1e3:.2f} ms: {value / 1e9:.3f} G KV tok/s; "
         f"decode_int2 avg {main_avg_ms * 1e3:.1f} us -> {achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS:.1%} of peak)")
     log("decode_int2 us per timed step: " + " ".join(f"{v * 1e3:.0f}" for v in each_ms[:64]))
@@ -420,6 +484,29 @@ def main():
         log(f"bf16 baseline: decode_bf16 {b_main * 1e3:.1f} us, {baseline['achieved_gbs']} GB/s; "
             f"INT2/bf16 kernel time ratio {b_main / main_avg_ms:.2f}x")
 
+    # ---- the workload's prefill write chunk timed on its own (quant_write, bf16 in) ----
+    chunk_write = None
+    if w.write_chunk:
+        ct = w.write_chunk
+        dcc = DeviceCache(sh, r_k, r_v, tau_k, tau_v, ct // 16 + 1, 1)
+        kb, vb = synth.kv_request_bf16(w, 200_000, 0, ct)
+        kcd, vcd, scd = to_dev_bits(kb), to_dev_bits(vb), to_dev_i32(np.arange(ct, dtype=np.int32))
+        for _ in range(3):
+            K.oscar_quant_write(sh, dcc.layer, dcc.cache, kcd, vcd, scd)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+        for a, b in evs:
+            a.record()
+            K.oscar_quant_write(sh, dcc.layer, dcc.cache, kcd, vcd, scd)
+            b.record()
+        torch.cuda.synchronize()
+        us = float(np.median([a.elapsed_time(b) for a, b in evs])) * 1e3
+        cbytes = ct * hkv * (2 * 128 * 2 + 2 * (32 + (128 // group) * mb))
+        chunk_write = {"chunk_tokens": ct, "us_median": round(us, 1), "tokens_per_s": ct / (us * 1e-6),
+                       "gbs": round(cbytes / (us * 1e-6) / 1e9, 1),
+                       "frac": round(cbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"write chunk of {ct} tokens on its own: {us:.1f} us median, {chunk_write['gbs']} GB/s")
+        del dcc
+
     # ---- CPU oracle baseline on a bounded sample ----
     cpu = None
     if not args.no_cpu:
@@ -473,16 +560,24 @@ def main():
         "config": {"workload": w.name, "batch": B, "context": T_final, "n_q_heads": hq, "n_kv_heads": hkv,
                    "head_dim": 128, "group": group, "sink": w.sink, "recent": w.recent, "page_size": 16,
                    "scale_bits": scale_bits, "bits_per_element": round(bits_per_element, 4),
-                   "splits_int2": si, "step": "unfused" if args.unfused else "fused"},
+                   "splits_int2": si, "step": "unfused" if args.unfused else "fused",
+                   "interleaved_writes": bool(iw), "cold": bool(flush is not None)},
+        "value_basis": value_basis,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "decode_int2", "kernel_us": round(main_avg_ms * 1e3, 2),
                      "kernel_us_min": round(float(each_ms.min()) * 1e3, 2) if each_ms.size else None,
                      "kernel_us_median": round(float(np.median(each_ms)) * 1e3, 2) if each_ms.size else None,
                      "algorithmic_bytes_per_launch": int(alg),
+                     "algorithmic_bytes_unique_per_launch": int(alg_unique),
+                     "frac_unique": round(alg_unique / (main_avg_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "algorithmic_bytes_per_step": int(alg_step)},
         "cpu_baseline": cpu,
         "settle": settle,
+        "step_gpu_us": round(step_gpu_us, 1),
+        "cold_flush_mb": args.cold_flush_mb,
+        "interleaved_write": interleaved,
+        "write_chunk": chunk_write,
         "bf16_baseline": baseline,
         "quant_write": qw,
     }

@@ -6,6 +6,11 @@
         last N dispatches of the kernel whose name contains NAME (the timed
         steps of a run, without its warm-up).
 
+    python -m kv_cache_int2_amd.rocprof_summary sq DB --kernel NAME [--kernel NAME ...]
+        MFMA utilisation and VALU busy per kernel from one SQ counter pass
+        (SQ_INSTS_VALU, SQ_INSTS_MFMA, SQ_ACTIVE_INST_VALU,
+        SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE).
+
     python -m kv_cache_int2_amd.rocprof_summary pmc --fetch DB --write DB
         --kernel NAME --copy NAME --copy-bytes N --workload W --source FILE
         --algorithmic-bytes N --command CMD
@@ -44,6 +49,45 @@ def counter_per_dispatch(db: str, counter: str, kernel: str):
     q = ("select k.dispatch_id, sum(p.counter_value) from pmc_events p join kernels k "
          "on p.dispatch_id = k.dispatch_id where p.counter_name = ? and k.name like ? group by k.dispatch_id")
     return [v for _, v in con.execute(q, (counter, f"%{kernel}%")).fetchall()]
+
+
+def counter_agg_per_dispatch(db: str, counter: str, kernel: str, agg: str):
+    """Per-dispatch values of a counter over its hardware instances (agg: sum or max)."""
+    con = sqlite3.connect(db)
+    q = (f"select k.dispatch_id, {agg}(p.counter_value) from pmc_events p join kernels k "
+         "on p.dispatch_id = k.dispatch_id where p.counter_name = ? and k.name like ? group by k.dispatch_id")
+    return {d: v for d, v in con.execute(q, (counter, f"%{kernel}%")).fetchall()}
+
+
+SQ_COUNTERS = ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_ACTIVE_INST_VALU", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
+
+
+def sq_stats(db: str, kernel: str, cu_num: int, simd_num: int):
+    """MFMA utilisation and VALU busy of one kernel, averaged over its
+    dispatches, with the tool's own derived-metric formulas:
+      MfmaUtil = 100 sum(SQ_VALU_MFMA_BUSY_CYCLES) / (max(GRBM_GUI_ACTIVE) SIMD_NUM)
+      VALUBusy = 100 sum(SQ_ACTIVE_INST_VALU) / CU_NUM / max(GRBM_GUI_ACTIVE)"""
+    v = {c: counter_agg_per_dispatch(db, c, kernel, "max" if c.startswith("GRBM") else "sum") for c in SQ_COUNTERS}
+    ids = sorted(set.intersection(*(set(x) for x in v.values())))
+    if not ids:
+        sys.exit(f"no SQ counters for {kernel} in {db}")
+    mfma = [100.0 * v["SQ_VALU_MFMA_BUSY_CYCLES"][d] / (v["GRBM_GUI_ACTIVE"][d] * simd_num) for d in ids]
+    valu = [100.0 * v["SQ_ACTIVE_INST_VALU"][d] / cu_num / v["GRBM_GUI_ACTIVE"][d] for d in ids]
+    mean = lambda xs: sum(xs) / len(xs)
+    return dict(dispatches=len(ids), mfma_util_pct=mean(mfma), valu_busy_pct=mean(valu),
+                valu_insts=mean([v["SQ_INSTS_VALU"][d] for d in ids]),
+                mfma_insts=mean([v["SQ_INSTS_MFMA"][d] for d in ids]),
+                gui_active_cycles=mean([v["GRBM_GUI_ACTIVE"][d] for d in ids]))
+
+
+def cmd_sq(a):
+    out = [f"| kernel | dispatches | MFMA util % | VALU busy % | VALU insts | MFMA insts | GUI active cycles |",
+           "|---|---:|---:|---:|---:|---:|---:|"]
+    for k in a.kernel:
+        r = sq_stats(a.db, k, a.cu_num, a.simd_num)
+        out.append(f"| {k} | {r['dispatches']} | {r['mfma_util_pct']:.1f} | {r['valu_busy_pct']:.1f} "
+                   f"| {r['valu_insts']:.4g} | {r['mfma_insts']:.4g} | {r['gui_active_cycles']:.4g} |")
+    print("\n".join(out))
 
 
 def tail_stats(db: str, kernel: str, n: int):
@@ -114,8 +158,13 @@ def main(argv=None):
         p.add_argument("--" + k, required=True)
     p.add_argument("--copy-bytes", type=int, required=True)
     p.add_argument("--algorithmic-bytes", type=int, default=0)
+    q = sub.add_parser("sq")
+    q.add_argument("db")
+    q.add_argument("--kernel", action="append", required=True, help="kernel name substring (repeatable)")
+    q.add_argument("--cu-num", type=int, default=256)
+    q.add_argument("--simd-num", type=int, default=1024)
     a = ap.parse_args(argv)
-    cmd_trace(a) if a.cmd == "trace" else cmd_pmc(a)
+    {"trace": cmd_trace, "pmc": cmd_pmc, "sq": cmd_sq}[a.cmd](a)
 
 
 if __name__ == "__main__":
