@@ -213,8 +213,9 @@ oscar_status oscar_block_tables(const oscar_pool* pool, const oscar_seq* const* 
  *   nearest-even); code = clamp(rint((x_rot - z)/s), 0, 3) (fp64, half-even),
  *   code = 0 where s == 0; a group holding NaN stores s = z = NaN, codes 0;
  * packed into the slot's INT2 block.  Inputs: k_bf16, v_bf16 device bf16
- * [n][n_kv_heads][d]; int2_slots device int32 [n].  Slots must be distinct
- * within one call.  n == 0 is a no-op. */
+ * [n][n_kv_heads][d], contiguous, 16-byte aligned (EINVAL otherwise);
+ * int2_slots device int32 [n].  Slots must be distinct within one call.
+ * n == 0 is a no-op. */
 oscar_status oscar_quant_write(const oscar_shape* shape, const oscar_layer* layer, const oscar_cache* cache,
                                const void* k_bf16, const void* v_bf16, const int32_t* int2_slots, int64_t n,
                                void* stream);

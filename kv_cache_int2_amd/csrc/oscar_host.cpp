@@ -692,6 +692,7 @@ oscar_status oscar_quant_write(const oscar_shape* shape, const oscar_layer* laye
   if (n == 0) return ok();
   if ((st = check_layer(layer, shape)) || (st = check_cache(cache, true, false))) return st;
   if (!k_bf16 || !v_bf16 || !int2_slots) return fail(OSCAR_EINVAL, "NULL input");
+  if (!aligned(k_bf16, 16) || !aligned(v_bf16, 16)) return fail(OSCAR_EINVAL, "inputs must be 16-byte aligned");
   if (n > (1LL << 31) / 16) return fail(OSCAR_EINVAL, "n too large");
   QuantParams p{};
   p.k_src = (const uint16_t*)k_bf16;

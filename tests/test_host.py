@@ -104,6 +104,11 @@ def test_launch_argument_errors_before_any_gpu_call(lib):
     assert lib.oscar_quant_write(C.byref(sh), C.byref(folded), C.byref(bad), 0x10, 0x10, 0x10, 1,
                                  None) == K.OSCAR_EINVAL
     assert b"storage" in lib.oscar_last_error()
+    # K/V rows are read 16 bytes at a time
+    for kp, vp in ((0x18, 0x10), (0x10, 0x12)):
+        assert lib.oscar_quant_write(C.byref(sh), C.byref(good_layer), C.byref(ok_cache), kp, vp, 0x10, 1,
+                                     None) == K.OSCAR_EINVAL
+        assert b"16-byte" in lib.oscar_last_error()
 
 
 def test_workspace_bytes_monotone(lib):
