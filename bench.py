@@ -28,7 +28,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak
-FP64_PEAK_TFLOPS = 78.6        # MI355X fp64 (vector and matrix)
+INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA
+WRITE_DIGIT_PAIRS = 16         # int8 digit-pair products per rotation in the write kernel
 PROFILE_PMC = os.path.join(ROOT, "profiles", "decode_int2_long_28x100k_pmc.json")
 KERNEL_SRC = os.path.join(ROOT, "kv_cache_int2_amd", "csrc", "decode_attn.hip")
 
@@ -484,12 +485,10 @@ def main():
         log(f"bf16 baseline: decode_bf16 {b_main * 1e3:.1f} us, {baseline['achieved_gbs']} GB/s; "
             f"INT2/bf16 kernel time ratio {b_main / main_avg_ms:.2f}x")
 
-    # ---- the workload's prefill write chunk timed on its own (quant_write, bf16 in) ----
-    chunk_write = None
-    if w.write_chunk:
-        ct = w.write_chunk
+    # ---- quant_write timed on its own: the workload's prefill chunk and a 16384-token chunk ----
+    def time_write(ct, seed_req):
         dcc = DeviceCache(sh, r_k, r_v, tau_k, tau_v, ct // 16 + 1, 1)
-        kb, vb = synth.kv_request_bf16(w, 200_000, 0, ct)
+        kb, vb = synth.kv_request_bf16(w, seed_req, 0, ct)
         kcd, vcd, scd = to_dev_bits(kb), to_dev_bits(vb), to_dev_i32(np.arange(ct, dtype=np.int32))
         for _ in range(3):
             K.oscar_quant_write(sh, dcc.layer, dcc.cache, kcd, vcd, scd)
@@ -501,11 +500,22 @@ def main():
         torch.cuda.synchronize()
         us = float(np.median([a.elapsed_time(b) for a, b in evs])) * 1e3
         cbytes = ct * hkv * (2 * 128 * 2 + 2 * (32 + (128 // group) * mb))
-        chunk_write = {"chunk_tokens": ct, "us_median": round(us, 1), "tokens_per_s": ct / (us * 1e-6),
-                       "gbs": round(cbytes / (us * 1e-6) / 1e9, 1),
-                       "frac": round(cbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
-        log(f"write chunk of {ct} tokens on its own: {us:.1f} us median, {chunk_write['gbs']} GB/s")
+        ops = 2.0 * WRITE_DIGIT_PAIRS * 128 * 128 * 2 * hkv * ct
         del dcc
+        return {"chunk_tokens": ct, "us_median": round(us, 1), "tokens_per_s": ct / (us * 1e-6),
+                "gbs": round(cbytes / (us * 1e-6) / 1e9, 1),
+                "frac": round(cbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "int8_mfma_frac": round(ops / (us * 1e-6) / (INT8_PEAK_TOPS * 1e12), 4)}
+
+    chunk_write = None
+    if w.write_chunk:
+        chunk_write = time_write(w.write_chunk, 200_000)
+        log(f"write chunk of {w.write_chunk} tokens on its own: {chunk_write['us_median']} us median, "
+            f"{chunk_write['gbs']} GB/s")
+    write_16k = time_write(16384, 200_001)
+    log(f"write chunk of 16384 tokens on its own: {write_16k['us_median']} us median, "
+        f"{write_16k['tokens_per_s'] / 1e9:.3f} G tok/s, {write_16k['gbs']} GB/s ({write_16k['frac']:.1%} of HBM), "
+        f"int8 MFMA {write_16k['int8_mfma_frac']:.1%} of peak")
 
     # ---- CPU oracle baseline on a bounded sample ----
     cpu = None
@@ -535,9 +545,9 @@ def main():
 
     qw = None
     if qw_tokens:
-        qw_flops = 2 * 2 * 128 * 128 * hkv * qw_tokens
+        qw_ops = 2.0 * WRITE_DIGIT_PAIRS * 128 * 128 * 2 * hkv * qw_tokens
         qw = {"tokens_per_s": qw_tokens / qw_time, "ms_total": round(qw_time * 1e3, 3),
-              "fp64_mfma_util": round(qw_flops / qw_time / (FP64_PEAK_TFLOPS * 1e12), 4),
+              "int8_mfma_frac": round(qw_ops / qw_time / (INT8_PEAK_TOPS * 1e12), 4),
               "gbs": round(qw_tokens * hkv * (2 * 128 * 2 + 2 * (32 + (128 // group) * mb)) / qw_time / 1e9, 1)}
 
     # stored bits per KV element at the final context (bf16 sink/recent + INT2 history)
@@ -578,6 +588,7 @@ def main():
         "cold_flush_mb": args.cold_flush_mb,
         "interleaved_write": interleaved,
         "write_chunk": chunk_write,
+        "write_chunk_16k": write_16k,
         "bf16_baseline": baseline,
         "quant_write": qw,
     }

@@ -205,19 +205,27 @@ struct alignas(16) TokInfo {
   int pad[3];
 };
 
+constexpr int kMaxTilesPerWg = 64;  // bounds the list of tiles sent to the exact path
+
 struct Smem {
-  uint8_t xdig[4][2][4][kTok][16];     // x digits [digit][K half][lane quad][token][16 channels]
-  uint16_t xraw[kTok][kHeadDim];       // bf16 inputs of the tile (exact path)
-  uint8_t codes[kTok][kCodeRow];
-  uint32_t szs[kTok][4];
-  TokInfo tok[kTok];
-  alignas(16) int32_t dst[2][kTok];    // by tile parity: a tile's stores overlap the next tile's loads
-  uint32_t flag[kWaves];               // per wavefront: some decision of the tile not certified
+  // main loop, buffered so that one barrier per tile orders every access
+  uint8_t xdig[2][4][2][4][kTok][16];  // by tile parity: x digits [digit][K half][lane quad][token][16 channels]
+  TokInfo tok[3][kTok];                // by tile mod 3
+  alignas(16) int32_t dst[3][kTok];    // by tile mod 3
+  uint8_t codes[2][kTok][kCodeRow];    // by tile parity; the exact path uses [0]
+  u32x4 rlo[kWaves][2][2][64];         // the residual digit of R: A operand of wavefront w, tile s, half h
+  uint32_t flag[2][kWaves];            // by tile parity, per wavefront: some decision not certified
   double part[kTok][kWaves][2];        // per-wavefront group min/max (64-channel groups)
   uint32_t rbits[4];                   // float bits of the maxima over channels j of sum_i |R_ij - Y_ij 2^-30|,
                                        // sum_i |R_ij - Y_ij 2^-30 - lo_ij 2^-38|, sum_i |R_ij|, and of max |R_ij|
   uint32_t bad_r;                      // some entry of R is non-finite or outside [-1.5, 1.5]
-  double xr[kTok][kHeadDim + 1];       // exact path: rotated values
+  uint32_t fb_n;                       // tiles sent to the exact path, as offsets from the first tile
+  uint16_t fb_list[kMaxTilesPerWg];
+  // the exact path, after the main loop
+  uint16_t xraw[kTok][kHeadDim];       // bf16 inputs of the tile
+  alignas(16) int32_t dst_x[kTok];
+  uint32_t szs[kTok][4];
+  double xr[kTok][kHeadDim + 1];       // rotated values
 };
 
 // ---- the exact path for one tile: x R in fp64 on MFMA, quantiser in fp64 ----
@@ -282,7 +290,7 @@ __device__ __attribute__((noinline)) void exact_tile(Smem& S, const float* R, do
   if (nan) {
     sz = nan_sz<MB>();
 #pragma unroll
-    for (int e = 0; e < 8; ++e) S.codes[t][j0 + e] = 0;
+    for (int e = 0; e < 8; ++e) S.codes[0][t][j0 + e] = 0;
   } else {
     double sd, zd;
     sz = encode_sz<MB>((mx - mn) / 3.0, mn, sd, zd);
@@ -293,13 +301,13 @@ __device__ __attribute__((noinline)) void exact_tile(Smem& S, const float* R, do
         c = __builtin_rint((v[e] - zd) / sd);
         c = c < 0.0 ? 0.0 : (c > 3.0 ? 3.0 : c);
       }
-      S.codes[t][j0 + e] = (uint8_t)c;
+      S.codes[0][t][j0 + e] = (uint8_t)c;
     }
   }
   if (sub == 0) S.szs[t][gm] = sz;
 }
 
-// ---- stores of one tile from LDS (wavefront 0; after the exact path) ----
+// ---- stores of one tile from LDS (wavefront 0; the exact path) ----
 template <int NG, int MB>
 __device__ void store_tile(Smem& S, const int32_t* dst, uint8_t* pages, int64_t n_kv, int kv, int isv, int lane) {
   constexpr Int2Layout L{NG, MB};
@@ -328,7 +336,7 @@ __device__ void store_tile(Smem& S, const int32_t* dst, uint8_t* pages, int64_t 
       for (int wi = 0; wi < 2; ++wi)
 #pragma unroll
         for (int e = 0; e < 16; ++e)
-          w[wi] |= (uint32_t)S.codes[t][k_code_channel<NG>(part, wi, e >> 2, e & 3)] << (2 * e);
+          w[wi] |= (uint32_t)S.codes[0][t][k_code_channel<NG>(part, wi, e >> 2, e & 3)] << (2 * e);
       *(uint2*)(blk + L.k_codes() + slot * 32 + 8 * part) = make_uint2(w[0], w[1]);
     }
   } else {
@@ -364,7 +372,7 @@ __device__ void store_tile(Smem& S, const int32_t* dst, uint8_t* pages, int64_t 
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         mask |= 3u << (8 * c + 2 * i);
-        bits |= (uint32_t)S.codes[t][4 * jd + c] << (8 * c + 2 * i);
+        bits |= (uint32_t)S.codes[0][t][4 * jd + c] << (8 * c + 2 * i);
       }
     }
     flush(key, mask, bits);
@@ -378,26 +386,23 @@ __device__ void store_tile(Smem& S, const int32_t* dst, uint8_t* pages, int64_t 
 // in registers (a quad broadcast), stored whole when the quad's slots are one
 // aligned run, else merged token by token with atomic and/or.  K: a word takes
 // dwords of two wavefronts, so it is packed from the codes in LDS (4 aligned
-// dword reads), wavefront w packing tokens 4w..4w+3.
+// dword reads), wavefront w packing tokens 4w..4w+3.  Slots: sl of token ln,
+// d4 of tokens 4(ln/4) .. +3, sk of token 4w + lane/8.
 template <int NG, int MB>
-__device__ __forceinline__ void store_fast(const Smem& S, const int32_t* dst, const uint32_t cw[2], uint32_t sz,
-                                           uint8_t* pages, int64_t n_kv, int kv, int isv, int lane, int wave) {
+__device__ __forceinline__ void store_fast(const uint8_t (*codes)[kCodeRow], int32_t sl, int4 d4, int32_t sk,
+                                           const uint32_t cw[2], uint32_t sz, uint8_t* pages, int64_t n_kv, int kv,
+                                           int isv, int lane, int wave) {
   constexpr Int2Layout L{NG, MB};
   const int64_t blk_bytes = L.bytes();
   const int ln = lane & 15, qd = lane >> 4;
-  auto block = [&](int32_t sl) { return pages + ((int64_t)(sl / kPage) * n_kv + kv) * blk_bytes; };
-  if (qd == 0 && (NG == 4 || (wave & 1) == 0)) {
-    const int32_t sl = dst[ln];
-    if (sl >= 0) {
-      const int gm = NG == 4 ? wave : (wave >> 1), slot = sl % kPage;
-      store_sz<MB>(block(sl) + (isv ? L.v_sz() + (gm * kPage + slot) * MB : L.k_sz() + (slot * NG + gm) * MB), sz);
-    }
+  auto block = [&](int32_t slot) { return pages + ((int64_t)(slot / kPage) * n_kv + kv) * blk_bytes; };
+  if (qd == 0 && (NG == 4 || (wave & 1) == 0) && sl >= 0) {
+    const int gm = NG == 4 ? wave : (wave >> 1), slot = sl % kPage;
+    store_sz<MB>(block(sl) + (isv ? L.v_sz() + (gm * kPage + slot) * MB : L.k_sz() + (slot * NG + gm) * MB), sz);
   }
   if (isv) {
     const int i4 = ln & 3;
-    const int4 d4 = *(const int4*)&dst[ln & ~3];
     const bool whole = d4.x >= 0 && (d4.x & 3) == 0 && d4.y == d4.x + 1 && d4.z == d4.x + 2 && d4.w == d4.x + 3;
-    const int32_t sl = dst[ln];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int jd = 4 * (2 * wave + s) + qd;  // dword of channels 4jd .. 4jd+3
@@ -416,15 +421,12 @@ __device__ __forceinline__ void store_fast(const Smem& S, const int32_t* dst, co
         atomicOr(word, cw[s] << sh);
       }
     }
-  } else if (lane < 32) {
+  } else if (lane < 32 && sk >= 0) {
     const int t = 4 * wave + (lane >> 3), a = (lane >> 1) & 3, w = lane & 1;
-    const int32_t sl = dst[t];
-    if (sl >= 0) {
-      uint32_t word = 0u;
+    uint32_t word = 0u;
 #pragma unroll
-      for (int m = 0; m < 4; ++m) word |= *(const uint32_t*)&S.codes[t][k_code_channel<NG>(a, w, 0, m)] << (2 * m);
-      *(uint32_t*)(block(sl) + L.k_codes() + (sl % kPage) * 32 + 8 * a + 4 * w) = word;
-    }
+    for (int m = 0; m < 4; ++m) word |= *(const uint32_t*)&codes[t][k_code_channel<NG>(a, w, 0, m)] << (2 * m);
+    *(uint32_t*)(block(sk) + L.k_codes() + (sk % kPage) * 32 + 8 * a + 4 * w) = word;
   }
 }
 
@@ -446,6 +448,7 @@ __global__ __launch_bounds__(kThreads, 2) void quant_write_kernel(QuantParams p,
   const int64_t tile0 = (int64_t)blockIdx.x * tiles_per_wg;
   const int64_t tile1 = tile0 + tiles_per_wg < n_tiles ? tile0 + tiles_per_wg : n_tiles;
   if (tile0 >= tile1) return;
+  const int count = (int)(tile1 - tile0);  // <= kMaxTilesPerWg
   const float* Rm = isv ? p.r_v : p.r_k;  // null: V arrives rotated (R_V folded into its projection)
   const float* R = Rm ? Rm + (int64_t)kv * kHeadDim * kHeadDim : nullptr;
   const double tau = isv ? p.tau_v : p.tau_k;
@@ -454,44 +457,55 @@ __global__ __launch_bounds__(kThreads, 2) void quant_write_kernel(QuantParams p,
   // per-thread role in the loads: token tt, channels 8cc .. 8cc+7
   const int tt = tid >> 4, cc = tid & 15;
   const uint16_t* src = MODE == 0 ? (isv ? p.v_src : p.k_src) : nullptr;
-  // inputs of the next tile, fetched while the current one is processed
-  int32_t nx_slot = -1;
-  uint4 nx = make_uint4(0u, 0u, 0u, 0u);
+  // The inputs of one tile: its token's slot and 8 bf16 (zero and -1 for a
+  // token past the end of the work group's tiles).  Loads are unconditional
+  // (clamped in bounds) so that the tile loop has no branches around them.
+  struct In {
+    int32_t slot;
+    uint4 x;
+    bool valid;
+  };
   auto fetch = [&](int64_t tile) {
+    In in;
     const int64_t tok = tile * kTok + tt;
-    nx_slot = -1;
-    nx = make_uint4(0u, 0u, 0u, 0u);
-    if (tok >= p.n) return;
-    nx_slot = p.dst_slots[tok];
+    in.valid = tile < tile1 && tok < p.n;
+    const int64_t tc = in.valid ? tok : 0;
+    in.slot = p.dst_slots[tc];
     if constexpr (MODE == 0) {
-      nx = *(const uint4*)(src + (tok * p.n_kv + kv) * kHeadDim + 8 * cc);  // in bounds for any slot
+      in.x = *(const uint4*)(src + (tc * p.n_kv + kv) * kHeadDim + 8 * cc);
     } else {
-      const int32_t ss = p.src_slots[tok];
+      const int32_t ss = p.src_slots[tc];
       const int64_t page = ss / kPage;
-      const int slot = ss % kPage;
-      if (ss >= 0 && page < p.n_bf16_pages) {
-        const uint16_t* blk = (const uint16_t*)(p.bf16_pages + (page * p.n_kv + kv) * (int64_t)kBf16BlockBytes);
-        if (!isv) {
-          nx = *(const uint4*)(blk + slot * kHeadDim + 8 * cc);
-        } else {
-          uint32_t w4[4];
+      const bool ok = ss >= 0 && page < p.n_bf16_pages;
+      in.valid = in.valid && ok;
+      const int64_t pc = ok ? page : 0;
+      const int slot = ok ? ss % kPage : 0;
+      const uint16_t* blk = (const uint16_t*)(p.bf16_pages + (pc * p.n_kv + kv) * (int64_t)kBf16BlockBytes);
+      if (!isv) {
+        in.x = *(const uint4*)(blk + slot * kHeadDim + 8 * cc);
+      } else {
+        uint32_t w4[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            w4[e] = (uint32_t)blk[kPage * kHeadDim + (8 * cc + 2 * e) * kPage + slot] |
-                    ((uint32_t)blk[kPage * kHeadDim + (8 * cc + 2 * e + 1) * kPage + slot] << 16);
-          nx = make_uint4(w4[0], w4[1], w4[2], w4[3]);
-        }
+        for (int e = 0; e < 4; ++e)
+          w4[e] = (uint32_t)blk[kPage * kHeadDim + (8 * cc + 2 * e) * kPage + slot] |
+                  ((uint32_t)blk[kPage * kHeadDim + (8 * cc + 2 * e + 1) * kPage + slot] << 16);
+        in.x = make_uint4(w4[0], w4[1], w4[2], w4[3]);
       }
     }
+    return in;
   };
-  fetch(tile0);
+  // the slot a token's codes go to: -1 without a slot or past the INT2 pages
+  auto dst_of = [&](const In& in) {
+    const int32_t d = in.valid ? in.slot : -1;
+    return (d >= 0 && (int64_t)(d / kPage) < p.n_int2_pages) ? d : -1;
+  };
+  In nx = fetch(tile0);
 
   // ---- set-up: this wavefront's R digits in registers (A operands) ----
   // A lane l holds row (output channel) 16T + l%16; its 16 bytes of K half h
   // are input channels 64h + 16(l/16) + 0..15 (the x digits use the same map).
   if (tid < 5) (tid < 4 ? S.rbits[tid] : S.bad_r) = 0u;
   u32x4 ra[2][2][4];  // [tile s][half h][digit b]
-  u32x4 rl[2][2];     // residual digit lo
   float d1[2] = {0.f, 0.f}, d2[2] = {0.f, 0.f}, l1[2] = {0.f, 0.f}, rmax = 0.f;
   bool bad = false;
   float rv[2][2][4][4];  // R[64h + 16qd + 4k4 + e][16(2w+s) + l%16], all loads in flight together
@@ -549,7 +563,7 @@ __global__ __launch_bounds__(kThreads, 2) void quant_write_kernel(QuantParams p,
         ra[s][h][1][k4] = b1;
         ra[s][h][2][k4] = __builtin_amdgcn_perm(q23, q01, 0x05040100u);
         ra[s][h][3][k4] = __builtin_amdgcn_perm(q23, q01, 0x07060302u);
-        rl[s][h][k4] = lo4;
+        S.rlo[wave][s][h][lane][k4] = lo4;
       }
     }
   }
@@ -584,18 +598,13 @@ __global__ __launch_bounds__(kThreads, 2) void quant_write_kernel(QuantParams p,
                     (1.0 + 0x1p-10);
   const double kbr = 0x1p-29 * (double)__builtin_bit_cast(float, S.rbits[3]);
 
-  for (int64_t tile = tile0; tile < tile1; ++tile) {
-    int32_t dslot = nx_slot;
-    const uint4 u = nx;
-    if (tile + 1 < tile1) fetch(tile + 1);
-    if (dslot >= 0 && (int64_t)(dslot / kPage) >= p.n_int2_pages) dslot = -1;
-    const uint32_t wv[4] = {dslot >= 0 ? u.x : 0u, dslot >= 0 ? u.y : 0u, dslot >= 0 ? u.z : 0u,
-                            dslot >= 0 ? u.w : 0u};  // 8 bf16 (pairs)
-    // ---- the tile's inputs, per-token exponent, digits to LDS ----
-    *(uint4*)&S.xraw[tt][8 * cc] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
-    int32_t* const dst = S.dst[tile & 1];
-    if (cc == 0) dst[tt] = dslot;
-    // max |x| of the token (16 consecutive lanes)
+  // ---- stage: a tile's digits, per-token info and slots to LDS buffers ----
+  auto stage = [&](int k, const In& in) {
+    const int32_t dslot = dst_of(in);
+    const uint32_t wv[4] = {dslot >= 0 ? in.x.x : 0u, dslot >= 0 ? in.x.y : 0u, dslot >= 0 ? in.x.z : 0u,
+                            dslot >= 0 ? in.x.w : 0u};  // 8 bf16 (pairs)
+    S.dst[k % 3][tt] = dslot;  // the token's 16 threads write the same value
+    // max |x| of the token (its 16 threads are one lane row)
     uint32_t amax = 0u;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -636,24 +645,22 @@ __global__ __launch_bounds__(kThreads, 2) void quant_write_kernel(QuantParams p,
       // channel i = 8cc + e: K half i / 64, lane quad (i % 64) / 16, byte i % 16
       const int h = cc >> 3, q = (cc & 7) >> 1, off = 8 * (cc & 1);
 #pragma unroll
-      for (int a = 0; a < 4; ++a) *(uint2*)&S.xdig[a][h][q][tt][off] = make_uint2(dg[a][0], dg[a][1]);
+      for (int a = 0; a < 4; ++a) *(uint2*)&S.xdig[k & 1][a][h][q][tt][off] = make_uint2(dg[a][0], dg[a][1]);
     }
     // per-token totals: sum |D0| (< 2^16) and the rounded entries
     const int tot = row_sum_i32(dsum + (inexact << 16));
-    if (cc == 0) {
-      TokInfo ti;
-      ti.c8 = __builtin_ldexp(1.0, E - 50);
-      // an all-zero token is exactly zero
-      ti.bound = amax == 0u ? 0.0
-                            : __builtin_ldexp(ka + (double)(tot >> 16) * kbr + (double)(tot & 0xffff) * kOmit, E);
-      ti.exact = tok_exact ? 1 : 0;
-      ti.pad[0] = ti.pad[1] = ti.pad[2] = 0;
-      S.tok[tt] = ti;
-    }
-    __syncthreads();
+    TokInfo ti;
+    ti.c8 = __builtin_ldexp(1.0, E - 50);
+    // an all-zero token is exactly zero
+    ti.bound = amax == 0u ? 0.0 : __builtin_ldexp(ka + (double)(tot >> 16) * kbr + (double)(tot & 0xffff) * kOmit, E);
+    ti.exact = tok_exact ? 1 : 0;
+    ti.pad[0] = ti.pad[1] = ti.pad[2] = 0;
+    S.tok[k % 3][tt] = ti;  // the token's 16 threads write the same value
+  };
 
-    // ---- digit-pair MFMAs: wavefront w, column tiles s = 0, 1 ----
-    i32x4 acc[2][kClasses];
+  // ---- digit-pair MFMAs of a staged tile: wavefront w, column tiles s = 0, 1 ----
+  i32x4 acc[2][kClasses];
+  auto rotate = [&](int k) {
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
@@ -662,18 +669,38 @@ __global__ __launch_bounds__(kThreads, 2) void quant_write_kernel(QuantParams p,
     for (int h = 0; h < 2; ++h) {
       u32x4 xb[4];
 #pragma unroll
-      for (int a = 0; a < 4; ++a) xb[a] = *(const u32x4*)&S.xdig[a][h][qd][ln][0];
+      for (int a = 0; a < 4; ++a) xb[a] = *(const u32x4*)&S.xdig[k & 1][a][h][qd][ln][0];
 #define OSCAR_MFMA(A, B, C)                                   \
   acc[0][C] = mfma_i8(ra[0][h][B], xb[A], acc[0][C]); \
   acc[1][C] = mfma_i8(ra[1][h][B], xb[A], acc[1][C]);
       OSCAR_PAIRS(OSCAR_MFMA)
 #undef OSCAR_MFMA
-      acc[0][1] = mfma_i8(rl[0][h], xb[3], acc[0][1]);
-      acc[1][1] = mfma_i8(rl[1][h], xb[3], acc[1][1]);
+      acc[0][1] = mfma_i8(S.rlo[wave][0][h][lane], xb[3], acc[0][1]);
+      acc[1][1] = mfma_i8(S.rlo[wave][1][h][lane], xb[3], acc[1][1]);
     }
+  };
 
-    // ---- epilogue: lane (token ln, quad qd), channels 16(2w+s) + 4qd + r ----
-    const TokInfo ti = S.tok[ln];
+  // ---- prologue: tiles 0 and 1 staged, tile 0 rotated ----
+  if (tid == 0) S.fb_n = 0u;
+  {
+    const In in0 = nx;
+    nx = fetch(tile0 + 1);
+    stage(0, in0);
+    const In in1 = nx;
+    nx = fetch(tile0 + 2);
+    stage(1, in1);
+  }
+  __syncthreads();
+  rotate(0);
+  __syncthreads();  // every wavefront has read tile 0's digits before tile 2 replaces them
+
+  for (int k = 0; k < count; ++k) {
+    // ---- A: this tile's per-token info and slots, and its rotated values ----
+    const TokInfo ti = S.tok[k % 3][ln];
+    const int32_t* dk3 = S.dst[k % 3];
+    const int32_t sl = dk3[ln];
+    const int4 d4 = *(const int4*)&dk3[ln & ~3];
+    const int32_t sk = dk3[4 * wave + ((lane >> 3) & 3)];
     // sum_w acc_w 256^w in the unit c8 of the lowest class:
     // (acc5 256 + acc4) 2^32 + (acc3 256 + acc2) 2^16 + (acc1 256 + acc0),
     // each term an int32 (|.| < 2^26.7, 2^30.1, 2^30.8); the inner fma is
@@ -688,6 +715,10 @@ __global__ __launch_bounds__(kThreads, 2) void quant_write_kernel(QuantParams p,
         const int lo = acc[s][1][r] * 256 + acc[s][0][r];
         xw[4 * s + r] = __builtin_fma((double)hi, 0x1p32, __builtin_fma((double)mid, 0x1p16, (double)lo));
       }
+    // ---- B: the next tile's MFMAs run under this tile's epilogue and the staging ----
+    rotate(k + 1);
+
+    // ---- C: epilogue: lane (token ln, quad qd), channels 16(2w+s) + 4qd + r ----
     double mn = xw[0], mx = xw[0];
 #pragma unroll
     for (int e = 1; e < 8; ++e) {
@@ -726,50 +757,71 @@ __global__ __launch_bounds__(kThreads, 2) void quant_write_kernel(QuantParams p,
     const uint32_t zb = mb[0], sb = mb[2];
     bool unsure = zb != mb[1] || sb != mb[3];
     const double sv = meta_value<MB>(sb), zv = meta_value<MB>(zb);
-    uint32_t cw[2] = {0u, 0u};
-    if (sv != 0.0) {
-      // 1 / s: v_rcp_f64 and two Newton steps, relative error below 2^-50
-      double inv_s = __builtin_amdgcn_rcp(sv);
-      inv_s = __builtin_fma(inv_s, __builtin_fma(-sv, inv_s, 1.0), inv_s);
-      inv_s = __builtin_fma(inv_s, __builtin_fma(-sv, inv_s, 1.0), inv_s);
-      // t = (x c8 - z) / s = x (c8 / s) - z / s; against the exact (and the
-      // reference's) t: eb / s, the rounding of z / s, the error of 1 / s over
-      // |t| <= 4 and the rounding of the fma
-      const double ta = c8 * inv_s, tb = -zv * inv_s;
-      const double m = 0.5 - (eb * inv_s * (1.0 + 0x1p-40) + __builtin_fabs(tb) * 0x1p-52 + 0x1p-46);
-      // clip at +-tau, then clamp t to [0, 3]: one clamp of t (monotone steps)
-      const double tlo = __builtin_fmin(__builtin_fmax(__builtin_fma(-tau, inv_s, tb), 0.0), 3.0);
-      const double thi = __builtin_fmin(__builtin_fmax(__builtin_fma(tau, inv_s, tb), 0.0), 3.0);
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        double packed = 0.0;  // c0 + 256 c1 + 65536 c2 + 2^24 c3, exact
-#pragma unroll
-        for (int r = 3; r >= 0; --r) {
-          const double t = __builtin_fmin(__builtin_fmax(__builtin_fma(xw[4 * s + r], ta, tb), tlo), thi);
-          const double c = __builtin_rint(t);
-          unsure |= __builtin_fabs(t - c) > m;
-          packed = __builtin_fma(packed, 256.0, c);
-        }
-        cw[s] = (uint32_t)packed;
-      }
+    // 1 / s: v_rcp_f64 and two Newton steps, relative error below 2^-50 (s = 0:
+    // every code is 0, taken below)
+    const double sd = sv != 0.0 ? sv : 1.0;
+    double inv_s = __builtin_amdgcn_rcp(sd);
+    inv_s = __builtin_fma(inv_s, __builtin_fma(-sd, inv_s, 1.0), inv_s);
+    inv_s = __builtin_fma(inv_s, __builtin_fma(-sd, inv_s, 1.0), inv_s);
+    // t = (x c8 - z) / s = x (c8 / s) - z / s; against the exact (and the
+    // reference's) t: eb / s, the rounding of z / s, the error of 1 / s over
+    // |t| <= 4 and the rounding of the fma
+    const double ta = c8 * inv_s, tb = -zv * inv_s;
+    const double m = 0.5 - (eb * inv_s * (1.0 + 0x1p-40) + __builtin_fabs(tb) * 0x1p-52 + 0x1p-46);
+    // clip at +-tau, then clamp t to [0, 3]: one clamp of t (monotone steps)
+    const double tlo = __builtin_fmin(__builtin_fmax(__builtin_fma(-tau, inv_s, tb), 0.0), 3.0);
+    const double thi = __builtin_fmin(__builtin_fmax(__builtin_fma(tau, inv_s, tb), 0.0), 3.0);
+    // ---- the tile after next staged (inputs fetched one tile earlier); its
+    // independent work fills the latency of the decision chain above ----
+    {
+      const In in = nx;
+      nx = fetch(tile0 + k + 3);
+      stage(k + 2, in);
     }
+    uint32_t cw[2];
+    bool code_unsure = false;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      double packed = 0.0;  // c0 + 256 c1 + 65536 c2 + 2^24 c3, exact
+#pragma unroll
+      for (int r = 3; r >= 0; --r) {
+        const double t = __builtin_fmin(__builtin_fmax(__builtin_fma(xw[4 * s + r], ta, tb), tlo), thi);
+        const double c = __builtin_rint(t);
+        code_unsure |= __builtin_fabs(t - c) > m;
+        packed = __builtin_fma(packed, 256.0, c);
+      }
+      cw[s] = sv != 0.0 ? (uint32_t)packed : 0u;
+    }
+    unsure |= sv != 0.0 && code_unsure;
     // codes of channels 16(2w+s) + 4qd + 0..3, one byte each
 #pragma unroll
-    for (int s = 0; s < 2; ++s) *(uint32_t*)&S.codes[ln][16 * (2 * wave + s) + 4 * qd] = cw[s];
-    // one answer for the whole work group: some decision of the tile not
-    // certified (tokens without a slot are not stored and do not count)
-    const bool wave_unsure = __ballot((unsure && dst[ln] >= 0) || ti.exact || bad_r) != 0;
-    if (lane == 0) S.flag[wave] = wave_unsure ? 1u : 0u;
+    for (int s = 0; s < 2; ++s) *(uint32_t*)&S.codes[k & 1][ln][16 * (2 * wave + s) + 4 * qd] = cw[s];
+    // some decision of the tile not certified (tokens without a slot are not
+    // stored and do not count); every lane writes the wavefront's answer
+    S.flag[k & 1][wave] = __ballot((unsure && sl >= 0) || ti.exact || bad_r) != 0 ? 1u : 0u;
     __syncthreads();
-    const uint4 fl = *(const uint4*)S.flag;
+    const uint4 fl = *(const uint4*)S.flag[k & 1];
     if ((fl.x | fl.y | fl.z | fl.w) != 0u) {
-      exact_tile<NG, MB>(S, R, tau, lane, wave);
-      __syncthreads();
-      if (wave == 0) store_tile<NG, MB>(S, dst, p.int2_pages, p.n_kv, kv, isv, lane);
+      if (tid == 0) S.fb_list[S.fb_n++] = (uint16_t)k;  // redone after the loop
     } else {
-      store_fast<NG, MB>(S, dst, cw, sb | (zb << (4 * MB)), p.int2_pages, p.n_kv, kv, isv, lane, wave);
+      store_fast<NG, MB>(S.codes[k & 1], sl, d4, sk, cw, sb | (zb << (4 * MB)), p.int2_pages, p.n_kv, kv, isv,
+                         lane, wave);
     }
-    // codes and flags are rewritten only after the next tile's first barrier
+  }
+
+  // ---- the exact path for the tiles whose decisions the bound left open ----
+  __syncthreads();
+  const int n_fb = (int)S.fb_n;
+  for (int i = 0; i < n_fb; ++i) {
+    const In in = fetch(tile0 + S.fb_list[i]);
+    const int32_t dslot = dst_of(in);
+    *(uint4*)&S.xraw[tt][8 * cc] = dslot >= 0 ? in.x : make_uint4(0u, 0u, 0u, 0u);
+    if (cc == 0) S.dst_x[tt] = dslot;
+    __syncthreads();
+    exact_tile<NG, MB>(S, R, tau, lane, wave);
+    __syncthreads();
+    if (wave == 0) store_tile<NG, MB>(S, S.dst_x, p.int2_pages, p.n_kv, kv, isv, lane);
+    __syncthreads();
   }
 }
 
@@ -802,14 +854,16 @@ __global__ __launch_bounds__(256) void copy_pages_kernel(uint8_t* base, int64_t 
   for (int64_t w = threadIdx.x; w < page_bytes / 16; w += 256) to[w] = from[w];
 }
 
-// Tiles per work group: about two work groups per compute unit in one round.
+// Tiles per work group: about two work groups per compute unit in one round,
+// at most kMaxTilesPerWg.
 int tiles_per_wg(const QuantParams& p) {
   const int64_t n_tiles = (p.n + kTok - 1) / kTok;
   const int64_t mats = 2 * (int64_t)p.n_kv;
   int64_t wg_per_mat = 512 / mats;
   if (wg_per_mat < 1) wg_per_mat = 1;
   if (wg_per_mat > n_tiles) wg_per_mat = n_tiles;
-  return (int)((n_tiles + wg_per_mat - 1) / wg_per_mat);
+  int64_t tpw = (n_tiles + wg_per_mat - 1) / wg_per_mat;
+  return (int)(tpw < kMaxTilesPerWg ? tpw : kMaxTilesPerWg);  // more work groups beyond that
 }
 
 template <int MODE, int NG, int MB>

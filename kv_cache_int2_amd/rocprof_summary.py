@@ -7,13 +7,13 @@
         steps of a run, without its warm-up).
 
     python -m kv_cache_int2_amd.rocprof_summary sq DB --kernel NAME [--kernel NAME ...]
-        MFMA utilisation and VALU busy per kernel from one SQ counter pass
+        [--tail N]  MFMA utilisation and VALU busy per kernel from one SQ counter pass
         (SQ_INSTS_VALU, SQ_INSTS_MFMA, SQ_ACTIVE_INST_VALU,
         SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE).
 
     python -m kv_cache_int2_amd.rocprof_summary pmc --fetch DB --write DB
         --kernel NAME --copy NAME --copy-bytes N --workload W --source FILE
-        --algorithmic-bytes N --command CMD
+        --algorithmic-bytes N --command CMD [--tail N]
         HBM traffic per launch of one kernel from a FETCH_SIZE pass and a
         WRITE_SIZE pass (KiB per dispatch), each scaled by what the same
         counter reads for a plain copy kernel that moves a known number of
@@ -42,13 +42,16 @@ def kernel_stats(db: str):
             for n, c, a, lo, hi, t in rows]
 
 
-def counter_per_dispatch(db: str, counter: str, kernel: str):
+def counter_per_dispatch(db: str, counter: str, kernel: str, tail: int = 0):
     """Per-dispatch values of a counter for kernels whose name contains `kernel`
-    (summed over the counter's hardware instances)."""
+    (summed over the counter's hardware instances), in dispatch order; tail > 0
+    keeps the last `tail` dispatches."""
     con = sqlite3.connect(db)
     q = ("select k.dispatch_id, sum(p.counter_value) from pmc_events p join kernels k "
-         "on p.dispatch_id = k.dispatch_id where p.counter_name = ? and k.name like ? group by k.dispatch_id")
-    return [v for _, v in con.execute(q, (counter, f"%{kernel}%")).fetchall()]
+         "on p.dispatch_id = k.dispatch_id where p.counter_name = ? and k.name like ? group by k.dispatch_id "
+         "order by k.dispatch_id")
+    vals = [v for _, v in con.execute(q, (counter, f"%{kernel}%")).fetchall()]
+    return vals[-tail:] if tail > 0 else vals
 
 
 def counter_agg_per_dispatch(db: str, counter: str, kernel: str, agg: str):
@@ -62,13 +65,15 @@ def counter_agg_per_dispatch(db: str, counter: str, kernel: str, agg: str):
 SQ_COUNTERS = ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_ACTIVE_INST_VALU", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
 
 
-def sq_stats(db: str, kernel: str, cu_num: int, simd_num: int):
+def sq_stats(db: str, kernel: str, cu_num: int, simd_num: int, tail: int = 0):
     """MFMA utilisation and VALU busy of one kernel, averaged over its
     dispatches, with the tool's own derived-metric formulas:
       MfmaUtil = 100 sum(SQ_VALU_MFMA_BUSY_CYCLES) / (max(GRBM_GUI_ACTIVE) SIMD_NUM)
       VALUBusy = 100 sum(SQ_ACTIVE_INST_VALU) / CU_NUM / max(GRBM_GUI_ACTIVE)"""
     v = {c: counter_agg_per_dispatch(db, c, kernel, "max" if c.startswith("GRBM") else "sum") for c in SQ_COUNTERS}
     ids = sorted(set.intersection(*(set(x) for x in v.values())))
+    if tail > 0:
+        ids = ids[-tail:]
     if not ids:
         sys.exit(f"no SQ counters for {kernel} in {db}")
     mfma = [100.0 * v["SQ_VALU_MFMA_BUSY_CYCLES"][d] / (v["GRBM_GUI_ACTIVE"][d] * simd_num) for d in ids]
@@ -84,7 +89,7 @@ def cmd_sq(a):
     out = [f"| kernel | dispatches | MFMA util % | VALU busy % | VALU insts | MFMA insts | GUI active cycles |",
            "|---|---:|---:|---:|---:|---:|---:|"]
     for k in a.kernel:
-        r = sq_stats(a.db, k, a.cu_num, a.simd_num)
+        r = sq_stats(a.db, k, a.cu_num, a.simd_num, a.tail)
         out.append(f"| {k} | {r['dispatches']} | {r['mfma_util_pct']:.1f} | {r['valu_busy_pct']:.1f} "
                    f"| {r['valu_insts']:.4g} | {r['mfma_insts']:.4g} | {r['gui_active_cycles']:.4g} |")
     print("\n".join(out))
@@ -126,7 +131,7 @@ def cmd_pmc(a):
         res["kernel_source_sha256"] = hashlib.sha256(f.read()).hexdigest()
     total = 0.0
     for counter, db in (("FETCH_SIZE", a.fetch), ("WRITE_SIZE", a.write)):
-        k = counter_per_dispatch(db, counter, a.kernel)
+        k = counter_per_dispatch(db, counter, a.kernel, a.tail)
         c = counter_per_dispatch(db, counter, a.copy)
         if not k or not c:
             sys.exit(f"no {counter} values for {a.kernel} or {a.copy} in {db}")
@@ -158,11 +163,13 @@ def main(argv=None):
         p.add_argument("--" + k, required=True)
     p.add_argument("--copy-bytes", type=int, required=True)
     p.add_argument("--algorithmic-bytes", type=int, default=0)
+    p.add_argument("--tail", type=int, default=0, help="only the kernel's last N dispatches")
     q = sub.add_parser("sq")
     q.add_argument("db")
     q.add_argument("--kernel", action="append", required=True, help="kernel name substring (repeatable)")
     q.add_argument("--cu-num", type=int, default=256)
     q.add_argument("--simd-num", type=int, default=1024)
+    q.add_argument("--tail", type=int, default=0, help="only each kernel's last N dispatches")
     a = ap.parse_args(argv)
     {"trace": cmd_trace, "pmc": cmd_pmc, "sq": cmd_sq}[a.cmd](a)
 
