@@ -663,3 +663,71 @@ def test_f4_rv_folded_into_the_projections():
         # the folded projection's output carries its own bf16 rounding (2^-9 relative): the
         # only extra error, seen alone when every position is bf16
         assert e_f <= 1.05 * e_u + 2.0 ** -8, (t, e_f, e_u)
+
+
+def _bits(vals):
+    """float values exactly representable in bf16 -> bf16 bit patterns"""
+    return synth.f32_to_bf16_bits(np.asarray(vals, np.float32))
+
+
+def _check_written_rows(dc, sh, kb, vb, r_k, r_v, tau_k, tau_v, group, scale_bits, label):
+    pool = dc.int2.cpu().numpy().reshape(dc.int2.numel() // (sh.n_kv_heads * dc.int2_block), sh.n_kv_heads, -1)
+    bits = np.uint16 if scale_bits == 16 else np.uint8
+    n = kb.shape[0]
+    for h in range(sh.n_kv_heads):
+        ck, sk, zk, _ = O.quantize(O.bf16_to_f64(kb[:, h]), r_k[h], tau_k, group, scale_bits)
+        cv, sv, zv, _ = O.quantize(O.bf16_to_f64(vb[:, h]), r_v[h], tau_v, group, scale_bits)
+        bad = 0
+        for i in range(n):
+            page, s = divmod(i, 16)
+            blk = O.unpack_int2_block(pool[page, h], 128, group, scale_bits)
+            ok = (np.array_equal(blk[0][s], ck[i]) and np.array_equal(blk[3][s], cv[i])
+                  and np.array_equal(blk[1][s].view(bits), sk[i].view(bits))
+                  and np.array_equal(blk[2][s].view(bits), zk[i].view(bits))
+                  and np.array_equal(blk[4][s].view(bits), sv[i].view(bits))
+                  and np.array_equal(blk[5][s].view(bits), zv[i].view(bits)))
+            if not ok:
+                bad += 1
+                if bad < 4:
+                    _flush(f"{label}: head {h} token {i} differs")
+        assert bad == 0, (label, h, bad)
+
+
+@pytest.mark.parametrize("scale_bits", [16, 8])
+def test_quant_write_certification_edges(scale_bits):
+    """The write kernel's certified decisions at their edges, with identity
+    rotations (R_K = I, R_V folded) so that the rotated values are the bf16
+    inputs themselves: codes whose t is exactly a half-integer (the exact path
+    breaks the tie half-even), groups with s = 0, values clipped at +-tau,
+    entries far below the token's maximum (rounded in the fixed point, covered
+    by the bound), an all-zero token and a ragged tail; then a rotation with
+    entries outside [-1.5, 1.5], which sends every tile to the exact path."""
+    from kv_cache_int2_amd.torch_cache import to_dev_bits, to_dev_i32
+    w = synth.WORKLOADS["qwen3_8b_32k"]
+    sh = K.make_shape(n_q_heads=4, n_kv_heads=1, group=32, sink=0, recent=0, scale_bits=scale_bits)
+    n = 19 * 16 + 5
+    kb, vb = synth.kv_request_bf16(w, 11, 0, n)
+    kb, vb = np.ascontiguousarray(kb[:, :1]), np.ascontiguousarray(vb[:, :1])
+    rng = np.random.default_rng(5)
+    ties = np.array([0.0, 3.0, 0.5, 1.5, 2.5] * 26)[:128]       # z = 0, s = 1, t on .5 boundaries
+    for x in (kb, vb):
+        x[0] = 0                                                  # all-zero token
+        x[1, 0] = _bits(ties)
+        x[2, 0] = _bits(ties * 0.25 - 0.375)                      # shifted and scaled ties
+        tiny = np.full(128, 2.0 ** -30)
+        tiny[::7] = 2.0 ** -40
+        tiny[3], tiny[64] = 1.0, -0.75
+        x[3, 0] = _bits(tiny)                                     # entries 2^-30, 2^-40 below max 1
+        x[4, 0] = _bits(np.full(128, 0.75))                       # s = 0 in every group
+        x[5, 0] = _bits(np.where(np.arange(128) % 3 == 0, 10.0, -0.3))  # clipped at tau
+        for t in range(6, 40):                                    # random small integers and halves: many ties
+            x[t, 0] = _bits(rng.integers(-6, 7, 128) * 0.5)
+    eye = np.eye(128, dtype=np.float32)[None]
+    for label, r_k, tau in (("identity", eye, 4.0), ("R outside [-1.5, 1.5]", 2.0 * eye, 8.0)):
+        _flush(f"case certification edges: {label}, scale_bits {scale_bits}")
+        dc = DeviceCache(sh, r_k, None, tau, tau, (n + 15) // 16, 1)
+        K.oscar_quant_write(sh, dc.layer, dc.cache, to_dev_bits(kb), to_dev_bits(vb),
+                            to_dev_i32(np.arange(n, dtype=np.int32)))
+        torch.cuda.synchronize()
+        _check_written_rows(dc, sh, kb, vb, r_k.astype(np.float64), eye.astype(np.float64), tau, tau, 32,
+                            scale_bits, label)
