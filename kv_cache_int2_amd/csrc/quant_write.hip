@@ -231,34 +231,47 @@ struct Smem {
 // ---- the exact path for one tile: x R in fp64 on MFMA, quantiser in fp64 ----
 typedef const float __attribute__((address_space(1))) * gfloat_ptr;
 
+// f64 16x16x4 operands: A lane l -> A[l%16][l/16]; B lane l -> B[l/16][l%16];
+// C lane l, element r -> C[4r + l/16][l%16].  Wavefront w: column tiles 2w, 2w+1.
+// The B operands of the lane: R[4ks + l/16][16(2w+s) + l%16].  R is device
+// global memory (read through that address space, so that LDS waits do not
+// wait for these loads as well).
+__device__ __forceinline__ void exact_load_r(const float* R, int lane, int wave, float rb[2][kHeadDim / 4]) {
+  if (!R) return;
+  const gfloat_ptr Rg = (gfloat_ptr)R;
+  const int ln = lane & 15, qd = lane >> 4;
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int ks = 0; ks < kHeadDim / 4; ++ks) rb[s][ks] = Rg[(4 * ks + qd) * kHeadDim + 16 * (2 * wave + s) + ln];
+}
+
 template <int NG, int MB>
-__device__ __attribute__((noinline)) void exact_tile(Smem& S, const float* R, double tau, int lane, int wave) {
+__device__ __forceinline__ void exact_tile(Smem& S, const float* R, const float rb[2][kHeadDim / 4], double tau,
+                                           int lane, int wave) {
   constexpr int G = kHeadDim / NG;
   const int ln = lane & 15, qd = lane >> 4;
-  // f64 16x16x4 operands: A lane l -> A[l%16][l/16]; B lane l -> B[l/16][l%16];
-  // C lane l, element r -> C[4r + l/16][l%16].  Wavefront w: column tiles 2w, 2w+1.
-  // R is device global memory (read through that address space, so that the
-  // LDS waits below do not wait for these loads as well)
-  const gfloat_ptr Rg = (gfloat_ptr)R;
-  for (int s = 0; s < 2; ++s) {
-    const int col = 16 * (2 * wave + s) + ln;
-    f64x4 acc = f64x4{0.0, 0.0, 0.0, 0.0};
-    if (R) {
-      float rb[kHeadDim / 4];
+  if (R) {
+    // per column tile two interleaved accumulation chains (even and odd k steps), added at the end
 #pragma unroll
-      for (int ks = 0; ks < kHeadDim / 4; ++ks) rb[ks] = Rg[(4 * ks + qd) * kHeadDim + col];
-      double xa[kHeadDim / 4];
+    for (int s = 0; s < 2; ++s) {
+      f64x4 acc0 = f64x4{0.0, 0.0, 0.0, 0.0}, acc1 = f64x4{0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-      for (int ks = 0; ks < kHeadDim / 4; ++ks) xa[ks] = (double)bf16_to_f32(S.xraw[ln][4 * ks + qd]);
+      for (int ks = 0; ks < kHeadDim / 4; ks += 2) {
+        acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)bf16_to_f32(S.xraw[ln][4 * ks + qd]), (double)rb[s][ks],
+                                                    acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)bf16_to_f32(S.xraw[ln][4 * ks + 4 + qd]),
+                                                    (double)rb[s][ks + 1], acc1, 0, 0, 0);
+      }
 #pragma unroll
-      for (int ks = 0; ks < kHeadDim / 4; ++ks)
-        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(xa[ks], (double)rb[ks], acc, 0, 0, 0);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) S.xr[4 * r + qd][col] = acc[r];
-    } else {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) S.xr[4 * r + qd][col] = (double)bf16_to_f32(S.xraw[4 * r + qd][col]);
+      for (int r = 0; r < 4; ++r) S.xr[4 * r + qd][16 * (2 * wave + s) + ln] = acc0[r] + acc1[r];
     }
+  } else {
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        S.xr[4 * r + qd][16 * (2 * wave + s) + ln] = (double)bf16_to_f32(S.xraw[4 * r + qd][16 * (2 * wave + s) + ln]);
   }
   __syncthreads();
   // 16 / NG threads per (token, group), 8 channels each
@@ -430,6 +443,81 @@ __device__ __forceinline__ void store_fast(const uint8_t (*codes)[kCodeRow], int
   }
 }
 
+// The inputs of one tile for thread (token tt, channels 8cc .. 8cc+7): the
+// token's INT2 slot and 8 bf16, zero and invalid for a token past `tile_end`
+// or the input.  Loads are unconditional (clamped in bounds), so that the tile
+// loop has no branches around them.
+struct TileIn {
+  int32_t slot;
+  uint4 x;
+  bool valid;
+};
+template <int MODE>
+__device__ __forceinline__ TileIn fetch_tile(const QuantParams& p, const uint16_t* src, int kv, int isv, int64_t tile,
+                                             int64_t tile_end, int tt, int cc) {
+  TileIn in;
+  const int64_t tok = tile * kTok + tt;
+  in.valid = tile < tile_end && tok < p.n;
+  const int64_t tc = in.valid ? tok : 0;
+  in.slot = p.dst_slots[tc];
+  if constexpr (MODE == 0) {
+    in.x = *(const uint4*)(src + (tc * p.n_kv + kv) * kHeadDim + 8 * cc);
+  } else {
+    const int32_t ss = p.src_slots[tc];
+    const int64_t page = ss / kPage;
+    const bool ok = ss >= 0 && page < p.n_bf16_pages;
+    in.valid = in.valid && ok;
+    const int64_t pc = ok ? page : 0;
+    const int slot = ok ? ss % kPage : 0;
+    const uint16_t* blk = (const uint16_t*)(p.bf16_pages + (pc * p.n_kv + kv) * (int64_t)kBf16BlockBytes);
+    if (!isv) {
+      in.x = *(const uint4*)(blk + slot * kHeadDim + 8 * cc);
+    } else {
+      uint32_t w4[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        w4[e] = (uint32_t)blk[kPage * kHeadDim + (8 * cc + 2 * e) * kPage + slot] |
+                ((uint32_t)blk[kPage * kHeadDim + (8 * cc + 2 * e + 1) * kPage + slot] << 16);
+      in.x = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+    }
+  }
+  return in;
+}
+// the slot a token's codes go to: -1 without a slot or past the INT2 pages
+__device__ __forceinline__ int32_t tile_dst(const QuantParams& p, const TileIn& in) {
+  const int32_t d = in.valid ? in.slot : -1;
+  return (d >= 0 && (int64_t)(d / kPage) < p.n_int2_pages) ? d : -1;
+}
+
+// One tile per work group straight on the exact path (fp64 MFMA rotation and
+// fp64 quantiser): for launches of a few tiles per matrix, where setting up
+// the integer digits of R would cost more than the tiles themselves.
+template <int MODE, int NG, int MB>
+__global__ __launch_bounds__(kThreads) void quant_write_direct(QuantParams p) {
+  extern __shared__ __align__(16) uint8_t smem_raw[];
+  Smem& S = *reinterpret_cast<Smem*>(smem_raw);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int64_t tile = blockIdx.x;
+  const int kv = blockIdx.y;
+  const int isv = blockIdx.z;
+  const float* Rm = isv ? p.r_v : p.r_k;
+  const float* R = Rm ? Rm + (int64_t)kv * kHeadDim * kHeadDim : nullptr;
+  const double tau = isv ? p.tau_v : p.tau_k;
+  const int tt = tid >> 4, cc = tid & 15;
+  const uint16_t* src = MODE == 0 ? (isv ? p.v_src : p.k_src) : nullptr;
+  float rb[2][kHeadDim / 4];
+  exact_load_r(R, lane, wave, rb);  // in flight with the inputs
+  const TileIn in = fetch_tile<MODE>(p, src, kv, isv, tile, tile + 1, tt, cc);
+  const int32_t dslot = tile_dst(p, in);
+  *(uint4*)&S.xraw[tt][8 * cc] = dslot >= 0 ? in.x : make_uint4(0u, 0u, 0u, 0u);
+  if (cc == 0) S.dst_x[tt] = dslot;
+  __syncthreads();
+  exact_tile<NG, MB>(S, R, rb, tau, lane, wave);
+  __syncthreads();
+  if (wave == 0) store_tile<NG, MB>(S, S.dst_x, p.int2_pages, p.n_kv, kv, isv, lane);
+}
+
 // Digit pairs (a = x digit, b = R digit) by weight class w = a + b - 1.
 #define OSCAR_PAIRS(X)                                                                                        \
   X(0, 1, 0) X(1, 0, 0) X(0, 2, 1) X(1, 1, 1) X(2, 0, 1) X(0, 3, 2) X(1, 2, 2) X(2, 1, 2) X(3, 0, 2) X(1, 3, 3) \
@@ -457,49 +545,9 @@ __global__ __launch_bounds__(kThreads, 2) void quant_write_kernel(QuantParams p,
   // per-thread role in the loads: token tt, channels 8cc .. 8cc+7
   const int tt = tid >> 4, cc = tid & 15;
   const uint16_t* src = MODE == 0 ? (isv ? p.v_src : p.k_src) : nullptr;
-  // The inputs of one tile: its token's slot and 8 bf16 (zero and -1 for a
-  // token past the end of the work group's tiles).  Loads are unconditional
-  // (clamped in bounds) so that the tile loop has no branches around them.
-  struct In {
-    int32_t slot;
-    uint4 x;
-    bool valid;
-  };
-  auto fetch = [&](int64_t tile) {
-    In in;
-    const int64_t tok = tile * kTok + tt;
-    in.valid = tile < tile1 && tok < p.n;
-    const int64_t tc = in.valid ? tok : 0;
-    in.slot = p.dst_slots[tc];
-    if constexpr (MODE == 0) {
-      in.x = *(const uint4*)(src + (tc * p.n_kv + kv) * kHeadDim + 8 * cc);
-    } else {
-      const int32_t ss = p.src_slots[tc];
-      const int64_t page = ss / kPage;
-      const bool ok = ss >= 0 && page < p.n_bf16_pages;
-      in.valid = in.valid && ok;
-      const int64_t pc = ok ? page : 0;
-      const int slot = ok ? ss % kPage : 0;
-      const uint16_t* blk = (const uint16_t*)(p.bf16_pages + (pc * p.n_kv + kv) * (int64_t)kBf16BlockBytes);
-      if (!isv) {
-        in.x = *(const uint4*)(blk + slot * kHeadDim + 8 * cc);
-      } else {
-        uint32_t w4[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          w4[e] = (uint32_t)blk[kPage * kHeadDim + (8 * cc + 2 * e) * kPage + slot] |
-                  ((uint32_t)blk[kPage * kHeadDim + (8 * cc + 2 * e + 1) * kPage + slot] << 16);
-        in.x = make_uint4(w4[0], w4[1], w4[2], w4[3]);
-      }
-    }
-    return in;
-  };
-  // the slot a token's codes go to: -1 without a slot or past the INT2 pages
-  auto dst_of = [&](const In& in) {
-    const int32_t d = in.valid ? in.slot : -1;
-    return (d >= 0 && (int64_t)(d / kPage) < p.n_int2_pages) ? d : -1;
-  };
-  In nx = fetch(tile0);
+  auto fetch = [&](int64_t tile) { return fetch_tile<MODE>(p, src, kv, isv, tile, tile1, tt, cc); };
+  auto dst_of = [&](const TileIn& in) { return tile_dst(p, in); };
+  TileIn nx = fetch(tile0);
 
   // ---- set-up: this wavefront's R digits in registers (A operands) ----
   // A lane l holds row (output channel) 16T + l%16; its 16 bytes of K half h
@@ -599,7 +647,7 @@ __global__ __launch_bounds__(kThreads, 2) void quant_write_kernel(QuantParams p,
   const double kbr = 0x1p-29 * (double)__builtin_bit_cast(float, S.rbits[3]);
 
   // ---- stage: a tile's digits, per-token info and slots to LDS buffers ----
-  auto stage = [&](int k, const In& in) {
+  auto stage = [&](int k, const TileIn& in) {
     const int32_t dslot = dst_of(in);
     const uint32_t wv[4] = {dslot >= 0 ? in.x.x : 0u, dslot >= 0 ? in.x.y : 0u, dslot >= 0 ? in.x.z : 0u,
                             dslot >= 0 ? in.x.w : 0u};  // 8 bf16 (pairs)
@@ -683,10 +731,10 @@ __global__ __launch_bounds__(kThreads, 2) void quant_write_kernel(QuantParams p,
   // ---- prologue: tiles 0 and 1 staged, tile 0 rotated ----
   if (tid == 0) S.fb_n = 0u;
   {
-    const In in0 = nx;
+    const TileIn in0 = nx;
     nx = fetch(tile0 + 1);
     stage(0, in0);
-    const In in1 = nx;
+    const TileIn in1 = nx;
     nx = fetch(tile0 + 2);
     stage(1, in1);
   }
@@ -774,7 +822,7 @@ __global__ __launch_bounds__(kThreads, 2) void quant_write_kernel(QuantParams p,
     // ---- the tile after next staged (inputs fetched one tile earlier); its
     // independent work fills the latency of the decision chain above ----
     {
-      const In in = nx;
+      const TileIn in = nx;
       nx = fetch(tile0 + k + 3);
       stage(k + 2, in);
     }
@@ -813,12 +861,14 @@ __global__ __launch_bounds__(kThreads, 2) void quant_write_kernel(QuantParams p,
   __syncthreads();
   const int n_fb = (int)S.fb_n;
   for (int i = 0; i < n_fb; ++i) {
-    const In in = fetch(tile0 + S.fb_list[i]);
+    const TileIn in = fetch(tile0 + S.fb_list[i]);
     const int32_t dslot = dst_of(in);
     *(uint4*)&S.xraw[tt][8 * cc] = dslot >= 0 ? in.x : make_uint4(0u, 0u, 0u, 0u);
     if (cc == 0) S.dst_x[tt] = dslot;
     __syncthreads();
-    exact_tile<NG, MB>(S, R, tau, lane, wave);
+    float rb[2][kHeadDim / 4];
+    exact_load_r(R, lane, wave, rb);
+    exact_tile<NG, MB>(S, R, rb, tau, lane, wave);
     __syncthreads();
     if (wave == 0) store_tile<NG, MB>(S, S.dst_x, p.int2_pages, p.n_kv, kv, isv, lane);
     __syncthreads();
@@ -854,6 +904,10 @@ __global__ __launch_bounds__(256) void copy_pages_kernel(uint8_t* base, int64_t 
   for (int64_t w = threadIdx.x; w < page_bytes / 16; w += 256) to[w] = from[w];
 }
 
+// Launches of at most this many 16-token tiles per (KV head, K or V) take the
+// exact path directly.
+constexpr int64_t kDirectMaxTiles = 64;
+
 // Tiles per work group: about two work groups per compute unit in one round,
 // at most kMaxTilesPerWg.
 int tiles_per_wg(const QuantParams& p) {
@@ -868,8 +922,13 @@ int tiles_per_wg(const QuantParams& p) {
 
 template <int MODE, int NG, int MB>
 hipError_t launch_qw_t(const QuantParams& p, hipStream_t stream) {
-  const int tpw = tiles_per_wg(p);
   const int64_t n_tiles = (p.n + kTok - 1) / kTok;
+  if (n_tiles <= kDirectMaxTiles) {
+    hipLaunchKernelGGL((quant_write_direct<MODE, NG, MB>), dim3((unsigned)n_tiles, (unsigned)p.n_kv, 2),
+                       dim3(kThreads), sizeof(Smem), stream, p);
+    return hipGetLastError();
+  }
+  const int tpw = tiles_per_wg(p);
   const dim3 grid((unsigned)((n_tiles + tpw - 1) / tpw), (unsigned)p.n_kv, 2);
   const size_t lds = sizeof(Smem);
   auto kern = quant_write_kernel<MODE, NG, MB>;
