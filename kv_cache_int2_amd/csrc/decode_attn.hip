@@ -408,10 +408,15 @@ __device__ __forceinline__ int q_scale_exponent(float mx) {
 // Words per (request, KV head): A digits of 2Q (write_q_operands gives their
 // order; 1536 words per row tile reserved), then aux floats [1 + 16*CT]: logit
 // factor 2^-sq / 2, per row 2*Qbar (float).
-// WRITE: the decode-step writes come first.
+// WRITE: the decode-step writes come first.  With p.split_writes, the grid is
+// twice B x Hkv: work groups [0, B Hkv) build the q operands and work groups
+// [B Hkv, 2 B Hkv) do the step's writes, side by side (for small batches,
+// where the doubled grid still runs in one round).
 template <int NG, int MB, int CT, bool WRITE>
 __global__ __launch_bounds__(256) void decode_prologue(DecodeParams p) {
-  const int bk = blockIdx.x;
+  const int nbk = p.batch * p.n_kv;
+  const bool writer = WRITE && p.split_writes && (int)blockIdx.x >= nbk;
+  const int bk = writer ? (int)blockIdx.x - nbk : (int)blockIdx.x;
   const int b = bk / p.n_kv, kv = bk % p.n_kv;
   const int t = threadIdx.x, j = t & (kHeadDim - 1), hf = t >> 7;
   __shared__ float rk[kHeadDim * kHeadDim];
@@ -421,11 +426,12 @@ __global__ __launch_bounds__(256) void decode_prologue(DecodeParams p) {
   __shared__ float rv[WRITE ? kHeadDim * kHeadDim : 1];
   __shared__ __attribute__((aligned(16))) StepScratch sc;
   const int g = p.g;
-  if constexpr (WRITE) {
+  if (WRITE && (!p.split_writes || writer)) {
     if (p.r_v) stage_matrix256<kHeadDim>(p.r_v + (int64_t)kv * kHeadDim * kHeadDim, rv);
     stage_matrix256<kHeadDim>(p.r_k + (int64_t)kv * kHeadDim * kHeadDim, rk);
     __syncthreads();
     step_writes<NG, MB>(p, b, kv, rk, p.r_v ? rv : nullptr, sc);
+    if (writer) return;  // uniform per work group
   } else {
     stage_matrix256<kHeadDim>(p.r_k + (int64_t)kv * kHeadDim * kHeadDim, rk);
   }
@@ -1834,7 +1840,8 @@ hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream, hipEvent_t
   hipError_t e = hipSuccess;
   if (int2) {
     if (p.step_slots)
-      hipLaunchKernelGGL((decode_prologue<NG, MB, CT * W, true>), dim3(bkn), dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((decode_prologue<NG, MB, CT * W, true>), dim3(p.split_writes ? 2 * bkn : bkn), dim3(256), 0,
+                         stream, p);
     else
       hipLaunchKernelGGL((decode_prologue<NG, MB, CT * W, false>), dim3(bkn), dim3(256), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;

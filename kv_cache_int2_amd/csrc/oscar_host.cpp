@@ -910,6 +910,10 @@ static oscar_status decode_common(const oscar_shape* shape, const oscar_layer* l
     p.bf16_w = (uint8_t*)cache->bf16_pages;
     p.tau_k = layer->tau_k;
     p.tau_v = layer->tau_v;
+    // The prologue holds R_K and R_V in LDS (one work group per compute unit):
+    // when twice the (request, KV head) count still fits one round, the writes
+    // take work groups of their own beside the q operands.
+    p.split_writes = 2 * (int64_t)p.batch * p.n_kv <= device_cus() ? 1 : 0;
   }
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
   if (g_prof.on && !ws.use_scratch) {

@@ -94,6 +94,7 @@ struct DecodeParams {
   const uint16_t* v_new;
   uint8_t* int2_w;            // writable views of the two storages
   uint8_t* bf16_w;
+  int split_writes;           // the writes in work groups of their own (small batches)
   double tau_k, tau_v;
 };
 
