@@ -17,8 +17,9 @@
         HBM traffic per launch of one kernel from a FETCH_SIZE pass and a
         WRITE_SIZE pass (KiB per dispatch), each scaled by what the same
         counter reads for a plain copy kernel that moves a known number of
-        bytes in each direction.  Prints JSON; the source hash ties the figure
-        to the kernel source it was measured on.
+        bytes in each direction (its largest dispatch: a workload's own page
+        copies are far smaller than the calibration copy).  Prints JSON; the
+        source hash ties the figure to the kernel source it was measured on.
 """
 from __future__ import annotations
 
@@ -135,7 +136,7 @@ def cmd_pmc(a):
         c = counter_per_dispatch(db, counter, a.copy)
         if not k or not c:
             sys.exit(f"no {counter} values for {a.kernel} or {a.copy} in {db}")
-        copy_kib = sum(c) / len(c)
+        copy_kib = max(c)
         factor = a.copy_bytes / (copy_kib * 1024.0)        # true bytes per counted byte
         kern_kib = sum(k) / len(k)
         bytes_ = kern_kib * 1024.0 * factor
