@@ -105,6 +105,16 @@ __device__ __forceinline__ float mix_sub_hi(float x, f16x2 h) {
   return r;
 }
 
+// ((d0 << 8) + d1 << 8) + d2 as two shift-adds (v_lshl_add_u32): the empty asm
+// keeps the compiler from re-associating it into two shifts and an add3.  The
+// shift-adds stay compiler-generated, so the wait states after the MFMA that
+// produced d0..d2 are the compiler's.
+__device__ __forceinline__ int join_digits(int d0, int d1, int d2) {
+  int t = (d0 << 8) + d1;
+  asm("" : "+v"(t));
+  return (t << 8) + d2;
+}
+
 // butterfly sum over the NG lanes of a channel-group set (lanes differ in the low bits)
 template <int NG>
 __device__ __forceinline__ float group_sum(float x) {
@@ -826,6 +836,10 @@ __device__ __forceinline__ void int2_pair(const Src& src, int lp0, int p_end, in
   // one group each.  Head h is head h % 4 of quad entry (h / 4) % HPL of tile
   // h / (4 HPL).
   constexpr bool kWide = CT * HPL == 4;
+  // one-tile bodies issue a page's logit MFMAs together, into accumulators of
+  // their own (no MFMA-to-VALU wait after each); the two-tile bodies, held to
+  // 168 VGPRs, and the wide ones join each unit's sums before the next MFMA
+  constexpr bool kBatchUnits = CT == 1;
   const int lane = threadIdx.x & 63, ln = lane & 15, qd = lane >> 4;
   const int vrow = kPackLo ? (ln & 7) : ln;  // value-operand row this lane serves
   // ---- logits ----
@@ -860,24 +874,43 @@ __device__ __forceinline__ void int2_pair(const Src& src, int lp0, int p_end, in
       // hq NG + gam), token ln: one MFMA per unit, whose rows (head, digit)
       // give this lane the three digit sums of that head.  Every partial
       // value is an exact integer below 2^31 in magnitude.
-      i32x4 cd;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      auto unit_mfma = [&](int u) {
         const int gam = u % NG;
-        if (ct == CT - 1 && u / NG >= LQ) {
-          cd[u] = 0;
-          continue;
-        }
-        i32x4 ds;
         if constexpr (NG == 4) {
           // group gam: fields 2(gam%2), +1 of word gam/2
           const u32x4& b4 = av[gam >> 1];
           const u32x2 bq = (gam & 1) ? u32x2{b4[2], b4[3]} : u32x2{b4[0], b4[1]};
-          ds = mfma_i8_k32(K.qa[ct][u], bq, i32x4{0, 0, 0, 0});
+          return mfma_i8_k32(K.qa[ct][u], bq, i32x4{0, 0, 0, 0});
         } else {
-          ds = mfma_i8(K.qa[ct][u], av[gam], i32x4{0, 0, 0, 0});  // group gam: word gam
+          return mfma_i8(K.qa[ct][u], av[gam], i32x4{0, 0, 0, 0});  // group gam: word gam
         }
-        cd[u] = (((ds[0] << 8) + ds[1]) << 8) + ds[2];
+      };
+      auto skip = [&](int u) { return ct == CT - 1 && u / NG >= LQ; };
+      i32x4 cd;
+      if constexpr (kBatchUnits) {
+        // the unit MFMAs issue together, into accumulators of their own, and
+        // their digit sums are joined after them
+        i32x4 ds[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (!skip(u)) ds[u] = unit_mfma(u);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          // at G = 64 the two-op join takes registers that body does not have
+          const int c = NG == 4 ? join_digits(ds[u][0], ds[u][1], ds[u][2])
+                                : (((ds[u][0] << 8) + ds[u][1]) << 8) + ds[u][2];
+          cd[u] = skip(u) ? 0 : c;
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (skip(u)) {
+            cd[u] = 0;
+            continue;
+          }
+          const i32x4 d = unit_mfma(u);
+          cd[u] = (((d[0] << 8) + d[1]) << 8) + d[2];
+        }
       }
 #pragma unroll
       for (int hh = 0; hh < HPL; ++hh) {
