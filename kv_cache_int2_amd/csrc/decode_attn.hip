@@ -909,7 +909,7 @@ __device__ __forceinline__ void int2_pair(const Src& src, int lp0, int p_end, in
             continue;
           }
           const i32x4 d = unit_mfma(u);
-          cd[u] = (((d[0] << 8) + d[1]) << 8) + d[2];
+          cd[u] = NG == 4 ? join_digits(d[0], d[1], d[2]) : (((d[0] << 8) + d[1]) << 8) + d[2];
         }
       }
 #pragma unroll
