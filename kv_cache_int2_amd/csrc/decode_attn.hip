@@ -1631,9 +1631,22 @@ decode_int2(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t stage[(W == 1 ? 6 : 8) * Int2Layout{NG, MB}.bytes()];
   constexpr bool kWide = CT * (4 / NG) == 4;
   __shared__ __attribute__((aligned(16))) uint8_t edge_lds[kWide ? W * 2 * Int2Layout{NG, MB}.bytes() : 16];
+  // XCD-aware order: blocks go to the eight XCDs in turn (block i to XCD
+  // i % 8).  With a multiple of 8 (request, KV head) pairs every split of pair
+  // bk runs on XCD bk % 8, the XCD of the prologue's and the combine's block
+  // bk, so its q operands and partial rows pass through one L2; in time the
+  // items still come pair by pair, as in the plain order.
   const int item = blockIdx.x;
-  const int split = item % p.splits_int2;
-  const int bk = item / p.splits_int2;
+  const int S = p.splits_int2, bkn = (int)gridDim.x / S;
+  int split, bk;
+  if ((bkn & 7) == 0) {
+    const int j = item >> 3;
+    split = j % S;
+    bk = 8 * (j / S) + (item & 7);
+  } else {
+    split = item % S;
+    bk = item / S;
+  }
   float* pl = p_lds[W > 1 ? threadIdx.x >> 6 : 0];
   uint8_t* el = edge_lds + (kWide && W > 1 ? (threadIdx.x >> 6) : 0) * (kWide ? 2 * Int2Layout{NG, MB}.bytes() : 0);
   if constexpr (NG == 4 && CT == 4) {
