@@ -186,6 +186,14 @@ def run_prefill(args, w, sh, group, scale_bits, mb, cal):
         "int2_pass": {"kernel": "decode_int2", "passes_per_call": launches // max(args.steps, 1),
                       "us_per_pass": round(int2_us, 2), "int2_bytes_per_pass": int(int2_bytes),
                       "gbs_per_pass": round(int2_bytes / (int2_us * 1e-6) / 1e9, 1)},
+        # one pass reads the INT2 history once for 16 queries' rows: its bytes
+        # against HBM; the pass is bound by its VALU and MFMA issue, which the
+        # SQ counters of the profile show
+        "roofline": {"bound": "hbm", "achieved": round(int2_bytes / (int2_us * 1e-6) / 1e9, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(int2_bytes / (int2_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "decode_int2", "kernel_us": round(int2_us, 2),
+                     "algorithmic_bytes_per_launch": int(int2_bytes)},
     }
     print(json.dumps(res), flush=True)
 
