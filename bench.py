@@ -355,10 +355,15 @@ def main():
     step_ev_range = range(args.warmup, n_steps) if timed_step_ev or args.warmup == 0 else range(args.warmup)
     write_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_steps)]
 
+    # up to 64 requests the step's slot table and lengths travel in the prologue's
+    # launch arguments (oscar_decode_step_host_tables): no copy per step
+    host_tables = not args.unfused and B <= 64
+
     def step(st):
         n_age, changed = planner.step()
-        host_small[st].copy_(torch.from_numpy(planner.buf))
-        dev_small[st].copy_(host_small[st], non_blocking=True)
+        if not host_tables:
+            host_small[st].copy_(torch.from_numpy(planner.buf))
+            dev_small[st].copy_(host_small[st], non_blocking=True)
         if changed:
             i2_bt, bf_bt, _ = dc.tables(seqs, max_i2, max_bf)
             k = tab_n[0] % n_tab
@@ -385,6 +390,9 @@ def main():
                 K.oscar_quant_write(sh, dc.layer, dc.cache, new_k_d[si_], new_v_d[si_], d[0], n=B)
             K.oscar_bf16_write(sh, dc.cache, new_k_d[si_], new_v_d[si_], d[1], n=B)
             K.oscar_decode_attn(sh, dc.layer, dc.cache, q_d[si_], tables[0], tables[1], d[4], out, ws, si, sb_step)
+        elif host_tables:
+            K.oscar_decode_step_host_tables(sh, dc.layer, dc.cache, new_k_d[si_], new_v_d[si_], planner.buf[:4],
+                                            q_d[si_], tables[0], tables[1], planner.buf[4], out, ws, si, sb_step)
         else:
             K.oscar_decode_step(sh, dc.layer, dc.cache, new_k_d[si_], new_v_d[si_], d[:4], q_d[si_], tables[0],
                                 tables[1], d[4], out, ws, si, sb_step)
@@ -607,7 +615,7 @@ def main():
         "config": {"workload": w.name, "batch": B, "context": T_final, "n_q_heads": hq, "n_kv_heads": hkv,
                    "head_dim": 128, "group": group, "sink": w.sink, "recent": w.recent, "page_size": 16,
                    "scale_bits": scale_bits, "bits_per_element": round(bits_per_element, 4),
-                   "splits_int2": si, "step": "unfused" if args.unfused else "fused",
+                   "splits_int2": si, "step": "unfused" if args.unfused else ("fused, host tables" if host_tables else "fused"),
                    "interleaved_writes": bool(iw), "cold": bool(flush is not None)},
         "value_basis": value_basis,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

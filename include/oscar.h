@@ -356,6 +356,22 @@ oscar_status oscar_decode_step(const oscar_shape* shape, const oscar_layer* laye
                                int32_t splits_int2, int32_t splits_bf16, float* out, void* workspace,
                                size_t workspace_bytes, void* stream);
 
+/* oscar_decode_step with the step's small tables in host memory ([ES] serving
+ * section, as above): step_slots int32 [4][batch] and ctx_lens int32 [batch]
+ * are read on the host when the call is made and travel to the kernels inside
+ * their launch arguments, so the step needs no copy of them to the device (a
+ * serving loop passes the arrays oscar_plan_decode_step filled).  The caller
+ * may reuse both arrays as soon as the call returns.  batch <= 64
+ * (OSCAR_EINVAL otherwise: use oscar_decode_step).  Every other argument, the
+ * writes and the result are those of oscar_decode_step. */
+oscar_status oscar_decode_step_host_tables(const oscar_shape* shape, const oscar_layer* layer,
+                                           const oscar_cache* cache, const void* k_new, const void* v_new,
+                                           const int32_t* step_slots, const void* q, int32_t batch,
+                                           const int32_t* int2_bt, int32_t max_int2_pages, const int32_t* bf16_bt,
+                                           int32_t max_bf16_pages, const int32_t* ctx_lens, int32_t splits_int2,
+                                           int32_t splits_bf16, float* out, void* workspace, size_t workspace_bytes,
+                                           void* stream);
+
 /* Instrumentation.  While enabled (on != 0), each decode launch made by the
  * calling thread records a pair of HIP events on its stream around the main
  * decode kernel (not the prologue or the combine).  oscar_profile_read waits

@@ -10,6 +10,8 @@ from __future__ import annotations
 import ctypes as C
 import os
 
+import numpy as np
+
 HERE = os.path.dirname(os.path.abspath(__file__))
 # OSCAR_LIB names another build of the same library (the host-sanitizer
 # build liboscar_san.so is loaded this way by its test).
@@ -74,6 +76,9 @@ _SIGS = {
     "oscar_decode_step": (C.c_int32, [C.POINTER(Shape), C.POINTER(Layer), C.POINTER(Cache), P, P, P, P,
                                       C.c_int32, P, C.c_int32, P, C.c_int32, P, C.c_int32, C.c_int32, P, P,
                                       C.c_size_t, P]),
+    "oscar_decode_step_host_tables": (C.c_int32, [C.POINTER(Shape), C.POINTER(Layer), C.POINTER(Cache), P, P, P,
+                                                  P, C.c_int32, P, C.c_int32, P, C.c_int32, P, C.c_int32,
+                                                  C.c_int32, P, P, C.c_size_t, P]),
     "oscar_prefill_workspace_bytes": (C.c_size_t, [C.POINTER(Shape), C.c_int32, C.c_int32, C.c_int32, C.c_int32]),
     "oscar_prefill_attn": (C.c_int32, [C.POINTER(Shape), C.POINTER(Layer), C.POINTER(Cache), P, C.c_int32,
                                        C.c_int32, P, C.c_int32, P, C.c_int32, P, C.c_int32, C.c_int32, P, P,
@@ -313,6 +318,22 @@ def oscar_decode_step(shape, layer, cache, k_new, v_new, step_slots, q, int2_bt,
                                    _ptr(step_slots), _ptr(q), batch, _ptr(int2_bt), int2_bt.shape[1], _ptr(bf16_bt),
                                    bf16_bt.shape[1], _ptr(ctx_lens), splits_int2, splits_bf16, _ptr(out),
                                    _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def oscar_decode_step_host_tables(shape, layer, cache, k_new, v_new, step_slots, q, int2_bt, bf16_bt, ctx_lens,
+                                  out, workspace, splits_int2=0, splits_bf16=0, stream=None):
+    """oscar_decode_step with step_slots int32 [4][batch] and ctx_lens int32
+    [batch] as host numpy arrays (read during the call; batch <= 64)."""
+    batch = q.shape[0]
+    slots = np.ascontiguousarray(step_slots, dtype=np.int32)
+    ctx = np.ascontiguousarray(ctx_lens, dtype=np.int32)
+    if slots.shape != (4, batch) or ctx.shape != (batch,):
+        raise ValueError(f"step_slots must be [4][{batch}] and ctx_lens [{batch}] (got {slots.shape}, {ctx.shape})")
+    _check(lib().oscar_decode_step_host_tables(C.byref(shape), C.byref(layer), C.byref(cache), _ptr(k_new),
+                                               _ptr(v_new), _ptr(slots), _ptr(q), batch, _ptr(int2_bt),
+                                               int2_bt.shape[1], _ptr(bf16_bt), bf16_bt.shape[1], _ptr(ctx),
+                                               splits_int2, splits_bf16, _ptr(out), _ptr(workspace),
+                                               workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def oscar_prefill_workspace_bytes(shape, batch, chunk, splits_int2=0, splits_bf16=0) -> int:

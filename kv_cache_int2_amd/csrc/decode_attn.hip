@@ -288,12 +288,18 @@ __device__ __forceinline__ void quantise_and_store(const DecodeParams& p, int kv
   __syncthreads();
 }
 
+// step slot row r (0-3) of request b: from the launch arguments or from the
+// caller's device array
+__device__ __forceinline__ int32_t step_slot(const DecodeParams& p, const ArgTables& tabs, int r, int b) {
+  return p.arg_tables ? tabs.v[r][b] : p.step_slots[r * p.batch + b];
+}
+
 template <int NG, int MB>
-__device__ void step_writes(const DecodeParams& p, int b, int kv, const float* rk, const float* rv,
-                            StepScratch& sc) {
+__device__ void step_writes(const DecodeParams& p, const ArgTables& tabs, int b, int kv, const float* rk,
+                            const float* rv, StepScratch& sc) {
   const int t = threadIdx.x, m = t >> 7, j = t & (kHeadDim - 1);
-  const int32_t i2_new = p.step_slots[b], bf_new = p.step_slots[p.batch + b];
-  const int32_t age_src = p.step_slots[2 * p.batch + b], age_dst = p.step_slots[3 * p.batch + b];
+  const int32_t i2_new = step_slot(p, tabs, 0, b), bf_new = step_slot(p, tabs, 1, b);
+  const int32_t age_src = step_slot(p, tabs, 2, b), age_dst = step_slot(p, tabs, 3, b);
   const bool age = age_src >= 0 && age_dst >= 0 && age_src / kPage < p.n_bf16_pages &&
                    age_dst / kPage < p.n_int2_pages;
   const bool put_i2 = i2_new >= 0 && i2_new / kPage < p.n_int2_pages;
@@ -422,13 +428,17 @@ __device__ __forceinline__ int q_scale_exponent(float mx) {
 // twice B x Hkv: work groups [0, B Hkv) build the q operands and work groups
 // [B Hkv, 2 B Hkv) do the step's writes, side by side (for small batches,
 // where the doubled grid still runs in one round).
+// tabs: the step tables of oscar_decode_step_host_tables (p.arg_tables); the
+// q-operand block of (b, KV head 0) then copies b's context length to ctx_w,
+// which the later kernels read as ctx_lens.
 template <int NG, int MB, int CT, bool WRITE>
-__global__ __launch_bounds__(256) void decode_prologue(DecodeParams p) {
+__global__ __launch_bounds__(256) void decode_prologue(DecodeParams p, ArgTables tabs) {
   const int nbk = p.batch * p.n_kv;
   const bool writer = WRITE && p.split_writes && (int)blockIdx.x >= nbk;
   const int bk = writer ? (int)blockIdx.x - nbk : (int)blockIdx.x;
   const int b = bk / p.n_kv, kv = bk % p.n_kv;
   const int t = threadIdx.x, j = t & (kHeadDim - 1), hf = t >> 7;
+  if (WRITE && p.arg_tables && !writer && kv == 0 && t == 0) p.ctx_w[b] = tabs.v[4][b];
   __shared__ float rk[kHeadDim * kHeadDim];
   __shared__ float qs[16][kHeadDim];
   __shared__ int qi[16][kHeadDim];
@@ -440,7 +450,7 @@ __global__ __launch_bounds__(256) void decode_prologue(DecodeParams p) {
     if (p.r_v) stage_matrix256<kHeadDim>(p.r_v + (int64_t)kv * kHeadDim * kHeadDim, rv);
     stage_matrix256<kHeadDim>(p.r_k + (int64_t)kv * kHeadDim * kHeadDim, rk);
     __syncthreads();
-    step_writes<NG, MB>(p, b, kv, rk, p.r_v ? rv : nullptr, sc);
+    step_writes<NG, MB>(p, tabs, b, kv, rk, p.r_v ? rv : nullptr, sc);
     if (writer) return;  // uniform per work group
   } else {
     stage_matrix256<kHeadDim>(p.r_k + (int64_t)kv * kHeadDim * kHeadDim, rk);
@@ -1874,7 +1884,8 @@ __global__ __launch_bounds__(512) void decode_combine(DecodeParams p) {
 }
 
 template <int NG, int MB, int CT, int W>
-hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
+hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop,
+                           const ArgTables& tabs) {
   const int bkn = p.batch * p.n_kv;
   // the event pair brackets the dominant kernel: the INT2 stream when there is
   // one, else the bf16 stream.  (Running the bf16 kernel on a second stream
@@ -1885,11 +1896,11 @@ hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream, hipEvent_t
   auto mark = [&](hipEvent_t ev) { return ev ? hipEventRecord(ev, stream) : hipSuccess; };
   hipError_t e = hipSuccess;
   if (int2) {
-    if (p.step_slots)
+    if (p.has_step)
       hipLaunchKernelGGL((decode_prologue<NG, MB, CT * W, true>), dim3(p.split_writes ? 2 * bkn : bkn), dim3(256), 0,
-                         stream, p);
+                         stream, p, tabs);
     else
-      hipLaunchKernelGGL((decode_prologue<NG, MB, CT * W, false>), dim3(bkn), dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((decode_prologue<NG, MB, CT * W, false>), dim3(bkn), dim3(256), 0, stream, p, tabs);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = mark(ev_start)) != hipSuccess) return e;
     hipLaunchKernelGGL((decode_int2<NG, MB, CT, W>), dim3(bkn * p.splits_int2), dim3(64 * W), 0, stream, p);
@@ -1944,29 +1955,33 @@ hipError_t launch_prefill_mb(const DecodeParams& p, hipStream_t stream, hipEvent
 }
 
 template <int MB>
-hipError_t launch_decode_mb(const DecodeParams& p, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
+hipError_t launch_decode_mb(const DecodeParams& p, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop,
+                            const ArgTables& tabs) {
   // p.ct = 16-row tiles of a (request, KV head), spread as tile_split says
   const TileSplit ts = tile_split(p.ct);
   const int key = ts.ct * 10 + ts.w;
   if (ts.ct * ts.w != p.ct) return hipErrorInvalidValue;
   if (p.ng == 4) {
-    if (key == 11) return launch_decode_t<4, MB, 1, 1>(p, stream, ev_start, ev_stop);
-    if (key == 21) return launch_decode_t<4, MB, 2, 1>(p, stream, ev_start, ev_stop);
-    if (key == 13) return launch_decode_t<4, MB, 1, 3>(p, stream, ev_start, ev_stop);
-    if (key == 22) return launch_decode_t<4, MB, 2, 2>(p, stream, ev_start, ev_stop);
-    if (key == 41) return launch_decode_t<4, MB, 4, 1>(p, stream, ev_start, ev_stop);
+    if (key == 11) return launch_decode_t<4, MB, 1, 1>(p, stream, ev_start, ev_stop, tabs);
+    if (key == 21) return launch_decode_t<4, MB, 2, 1>(p, stream, ev_start, ev_stop, tabs);
+    if (key == 13) return launch_decode_t<4, MB, 1, 3>(p, stream, ev_start, ev_stop, tabs);
+    if (key == 22) return launch_decode_t<4, MB, 2, 2>(p, stream, ev_start, ev_stop, tabs);
+    if (key == 41) return launch_decode_t<4, MB, 4, 1>(p, stream, ev_start, ev_stop, tabs);
   } else if (p.ng == 2) {
-    if (key == 11) return launch_decode_t<2, MB, 1, 1>(p, stream, ev_start, ev_stop);
-    if (key == 21) return launch_decode_t<2, MB, 2, 1>(p, stream, ev_start, ev_stop);
+    if (key == 11) return launch_decode_t<2, MB, 1, 1>(p, stream, ev_start, ev_stop, tabs);
+    if (key == 21) return launch_decode_t<2, MB, 2, 1>(p, stream, ev_start, ev_stop, tabs);
   }
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeParams& p, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
-  if (p.mb == 4) return launch_decode_mb<4>(p, stream, ev_start, ev_stop);
-  if (p.mb == 2) return launch_decode_mb<2>(p, stream, ev_start, ev_stop);
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop,
+                         const ArgTables* tabs) {
+  static const ArgTables kNoTables{};
+  const ArgTables& t = tabs ? *tabs : kNoTables;
+  if (p.mb == 4) return launch_decode_mb<4>(p, stream, ev_start, ev_stop, t);
+  if (p.mb == 2) return launch_decode_mb<2>(p, stream, ev_start, ev_stop, t);
   return hipErrorInvalidValue;
 }
 
@@ -1981,7 +1996,8 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 size_t decode_workspace_bytes(int batch, int n_q, int n_kv, int ct, int splits_total) {
   const size_t bkn = (size_t)batch * n_kv;
   return align256(bkn * ct * 3 * 2 * 64 * 4 * sizeof(uint32_t)) + align256(bkn * (1 + 16 * ct) * sizeof(float)) +
-         align256((size_t)batch * n_q * splits_total * kPartialStride * sizeof(float));
+         align256((size_t)batch * n_q * splits_total * kPartialStride * sizeof(float)) +
+         align256((size_t)batch * sizeof(int32_t));
 }
 
 void decode_workspace_carve(DecodeParams& p, void* ws) {
@@ -1992,6 +2008,8 @@ void decode_workspace_carve(DecodeParams& p, void* ws) {
   p.qaux = (float*)w;
   w += align256(bkn * (1 + 16 * p.ct) * sizeof(float));
   p.partial = (float*)w;
+  w += align256((size_t)p.batch * p.n_q * (p.splits_int2 + p.splits_bf16) * kPartialStride * sizeof(float));
+  p.ctx_w = (int32_t*)w;
 }
 
 

@@ -816,6 +816,7 @@ struct StepWrites {
   const void* k_new;
   const void* v_new;
   const int32_t* step_slots;
+  bool host_tables;  // step_slots and ctx_lens in host memory: copied into the launch arguments
 };
 
 // The split-K workspace of a decode launch: caller memory, or (use_scratch)
@@ -902,8 +903,21 @@ static oscar_status decode_common(const oscar_shape* shape, const oscar_layer* l
   if (ws.bytes < need) return fail(OSCAR_EINVAL, "workspace %zu bytes < %zu needed", ws.bytes, need);
   decode_workspace_carve(p, ws.ptr);
   p.out = out;
+  ArgTables tabs{};
   if (writes) {
+    p.has_step = 1;
     p.step_slots = writes->step_slots;
+    if (writes->host_tables) {
+      // the host arrays go into the prologue's launch arguments; the prologue
+      // copies the lengths to the workspace, where the later kernels read them
+      for (int r = 0; r < 4; ++r)
+        std::copy(writes->step_slots + (int64_t)r * batch, writes->step_slots + (int64_t)(r + 1) * batch,
+                  tabs.v[r]);
+      std::copy(ctx_lens, ctx_lens + batch, tabs.v[4]);
+      p.arg_tables = 1;
+      p.step_slots = nullptr;
+      p.ctx_lens = p.ctx_w;
+    }
     p.k_new = (const uint16_t*)writes->k_new;
     p.v_new = (const uint16_t*)writes->v_new;
     p.int2_w = (uint8_t*)cache->int2_pages;
@@ -921,7 +935,7 @@ static oscar_status decode_common(const oscar_shape* shape, const oscar_layer* l
       return fail(OSCAR_EHIP, "hipEventCreate failed");
     g_prof.events.emplace_back(ev0, ev1);
   }
-  return hip_status(launch_decode(p, (hipStream_t)stream, ev0, ev1), "decode launch");
+  return hip_status(launch_decode(p, (hipStream_t)stream, ev0, ev1, p.arg_tables ? &tabs : nullptr), "decode launch");
 }
 
 oscar_status oscar_decode_step(const oscar_shape* shape, const oscar_layer* layer, const oscar_cache* cache,
@@ -933,7 +947,26 @@ oscar_status oscar_decode_step(const oscar_shape* shape, const oscar_layer* laye
   if (batch > 0 && (!k_new || !v_new || !step_slots)) return fail(OSCAR_EINVAL, "NULL step input");
   if (!aligned(k_new, 2) || !aligned(v_new, 2) || !aligned(step_slots, 4))
     return fail(OSCAR_EINVAL, "step inputs misaligned");
-  const StepWrites w{k_new, v_new, step_slots};
+  const StepWrites w{k_new, v_new, step_slots, false};
+  return decode_common(shape, layer, cache, q, batch, int2_bt, max_int2_pages, bf16_bt, max_bf16_pages, ctx_lens,
+                       splits_int2, splits_bf16, out, DecodeWorkspace{workspace, workspace_bytes, false}, stream,
+                       false, &w);
+}
+
+oscar_status oscar_decode_step_host_tables(const oscar_shape* shape, const oscar_layer* layer,
+                                           const oscar_cache* cache, const void* k_new, const void* v_new,
+                                           const int32_t* step_slots, const void* q, int32_t batch,
+                                           const int32_t* int2_bt, int32_t max_int2_pages, const int32_t* bf16_bt,
+                                           int32_t max_bf16_pages, const int32_t* ctx_lens, int32_t splits_int2,
+                                           int32_t splits_bf16, float* out, void* workspace, size_t workspace_bytes,
+                                           void* stream) {
+  if (batch > kArgBatch)
+    return fail(OSCAR_EINVAL, "batch %d > %d: the step tables of oscar_decode_step_host_tables travel in the "
+                              "launch arguments; use oscar_decode_step with device tables",
+                batch, kArgBatch);
+  if (batch > 0 && (!k_new || !v_new || !step_slots || !ctx_lens)) return fail(OSCAR_EINVAL, "NULL step input");
+  if (!aligned(k_new, 2) || !aligned(v_new, 2)) return fail(OSCAR_EINVAL, "step inputs misaligned");
+  const StepWrites w{k_new, v_new, step_slots, true};
   return decode_common(shape, layer, cache, q, batch, int2_bt, max_int2_pages, bf16_bt, max_bf16_pages, ctx_lens,
                        splits_int2, splits_bf16, out, DecodeWorkspace{workspace, workspace_bytes, false}, stream,
                        false, &w);

@@ -54,6 +54,13 @@ struct QuantParams {
   int mb;                     // bytes of a (scale, zero) pair: 4 or 2
 };
 
+// Step tables carried in the prologue's launch arguments: rows 0-3 the step's
+// slots, row 4 the context lengths, each of kArgBatch entries.
+constexpr int kArgBatch = 64;
+struct ArgTables {
+  int32_t v[5][kArgBatch];
+};
+
 struct DecodeParams {
   const uint8_t* int2_pages;
   int64_t n_int2_pages;
@@ -96,6 +103,13 @@ struct DecodeParams {
   uint8_t* bf16_w;
   int split_writes;           // the writes in work groups of their own (small batches)
   double tau_k, tau_v;
+  int has_step;               // the step's writes run (step_slots, or the argument tables)
+  // oscar_decode_step_host_tables: the step's [4][B] slots and ctx_lens, given
+  // in host memory, travel in the prologue's launch arguments (ArgTables, B <=
+  // kArgBatch); step_slots is then null, and the prologue copies the lengths
+  // to ctx_w, a workspace array that ctx_lens names for the later kernels
+  int arg_tables;
+  int32_t* ctx_w;
 };
 
 // How the 16-row tiles of a (request, KV head) spread over the wavefronts of
@@ -125,7 +139,8 @@ hipError_t launch_bf16_write(const uint16_t* k, const uint16_t* v, const int32_t
 hipError_t launch_copy_pages(uint8_t* base, int64_t block_bytes_all_heads, int64_t n_pages, const int32_t* src,
                              const int32_t* dst, int64_t n, hipStream_t stream);
 // ev_start / ev_stop (may be null): recorded on `stream` around the main kernel.
-hipError_t launch_decode(const DecodeParams& p, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop);
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop,
+                         const ArgTables* tabs = nullptr);
 // One query block of a chunked prefill (p.ct = 4, 8 or 16 tiles, one wavefront each).
 hipError_t launch_prefill(const DecodeParams& p, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop);
 

@@ -451,8 +451,10 @@ def test_fused_decode_step(hq, hkv, group, sink, recent, scale_bits):
     the separate write calls + oscar_decode_attn: identical cache bytes and bit-identical outputs after every step,
     through ring age-out, page crossings, sink growth and (recent = 0) new
     tokens quantised straight to INT2, with no sink region (sink = 0) and with
-    every position INT2 (sink = recent = 0); then the pages bit-exact and the
-    output within tolerance against the oracle."""
+    every position INT2 (sink = recent = 0); oscar_decode_step_host_tables (the
+    step tables in host memory, carried in the launch arguments) identical to
+    oscar_decode_step at every step; then the pages bit-exact and the output
+    within tolerance against the oracle."""
     from kv_cache_int2_amd.torch_cache import to_dev_bits, to_dev_i32
     w = synth.Workload("fused", 70 + hq + group, hq, hkv, 128, 1, 0, group=group, sink=sink, recent=recent,
                        outlier_scale=(40.0, 40.0), calib_tokens=512)
@@ -462,34 +464,34 @@ def test_fused_decode_step(hq, hkv, group, sink, recent, scale_bits):
     lens0 = [0, 3, max(sink + recent - 2, 1), 200, 1001]
     n_steps = 40
     B = len(lens0)
-    caches = [DeviceCache(sh, cal.r_k, cal.r_v, cal.tau_k, cal.tau_v, 600, 64) for _ in range(2)]
-    seqs = [[], []]
+    caches = [DeviceCache(sh, cal.r_k, cal.r_v, cal.tau_k, cal.tau_v, 600, 64) for _ in range(3)]
+    seqs = [[], [], []]
     for r, t in enumerate(lens0):
         kb, vb = synth.kv_request_bf16(w, r, 0, t)
-        for c in (0, 1):
+        for c in (0, 1, 2):
             s = caches[c].new_seq()
             if t:
                 caches[c].append(s, kb, vb)
             seqs[c].append(s)
-    planners = [K.DecodeStepPlanner(caches[c].pool, seqs[c]) for c in (0, 1)]
+    planners = [K.DecodeStepPlanner(caches[c].pool, seqs[c]) for c in (0, 1, 2)]
     max_i2 = (max(lens0) + n_steps + 15) // 16
     max_bf = -(-sink // 16) + recent // 16 + 1
     si = 3
     ws = [torch.empty(K.oscar_decode_workspace_bytes(sh, B, si, 1), dtype=torch.uint8, device="cuda")
-          for _ in (0, 1)]
-    outs = [torch.empty((B, hq, 128), dtype=torch.float32, device="cuda") for _ in (0, 1)]
+          for _ in (0, 1, 2)]
+    outs = [torch.empty((B, hq, 128), dtype=torch.float32, device="cuda") for _ in (0, 1, 2)]
     for st in range(n_steps):
         kn = np.stack([synth.kv_request_bf16(w, r, lens0[r] + st, lens0[r] + st + 1)[0][0] for r in range(B)])
         vn = np.stack([synth.kv_request_bf16(w, r, lens0[r] + st, lens0[r] + st + 1)[1][0] for r in range(B)])
         q = to_dev_bits(np.stack([synth.q_decode_bf16(w, r, st + 1) for r in range(B)]))
         kd, vd = to_dev_bits(kn), to_dev_bits(vn)
-        res = [planners[c].step() for c in (0, 1)]
-        bufs = [planners[c].buf.copy() for c in (0, 1)]
-        assert np.array_equal(bufs[0], bufs[1]) and res[0] == res[1]
+        res = [planners[c].step() for c in (0, 1, 2)]
+        bufs = [planners[c].buf.copy() for c in (0, 1, 2)]
+        assert np.array_equal(bufs[0], bufs[1]) and np.array_equal(bufs[0], bufs[2]) and res[0] == res[1] == res[2]
         d = to_dev_i32(bufs[0])
-        tabs = [caches[c].tables(seqs[c], max_i2, max_bf) for c in (0, 1)]
+        tabs = [caches[c].tables(seqs[c], max_i2, max_bf) for c in (0, 1, 2)]
         dt = [(to_dev_i32(i2), to_dev_i32(bf), to_dev_i32(ctx)) for i2, bf, ctx in tabs]
-        c0, c1 = caches
+        c0, c1 = caches[0], caches[1]
         # separate calls
         if res[0][0]:
             K.oscar_requant_from_bf16(sh, c0.layer, c0.cache, d[2], d[3], n=B)
@@ -501,11 +503,20 @@ def test_fused_decode_step(hq, hkv, group, sink, recent, scale_bits):
         # fused step
         K.oscar_decode_step(sh, c1.layer, c1.cache, kd, vd, d[:4], q, *dt[1][:2], dt[1][2], outs[1], ws[1],
                             si, 1)
+        # fused step, tables from host memory (the array is overwritten right
+        # after the call: the launch arguments hold their own copy)
+        host_tab = bufs[2].copy()
+        K.oscar_decode_step_host_tables(sh, caches[2].layer, caches[2].cache, kd, vd, host_tab[:4], q, *dt[2][:2],
+                                        host_tab[4], outs[2], ws[2], si, 1)
+        host_tab[:] = -7
         torch.cuda.synchronize()
         assert torch.equal(outs[0], outs[1]), f"step {st}: outputs differ"
+        assert torch.equal(outs[1], outs[2]), f"step {st}: host-table step differs"
         if st % 8 == 7 or st == n_steps - 1:
             assert torch.equal(c0.int2, c1.int2), f"step {st}: INT2 storage differs"
             assert torch.equal(c0.bf16, c1.bf16), f"step {st}: bf16 storage differs"
+            assert torch.equal(c1.int2, caches[2].int2) and torch.equal(c1.bf16, caches[2].bf16), \
+                f"step {st}: host-table step storage differs"
     _flush(f"fused step: {n_steps} steps identical to the separate calls")
     out = outs[1].cpu().numpy()
     qf = np.stack([synth.q_decode_bf16(w, r, n_steps) for r in range(B)])

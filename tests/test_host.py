@@ -109,6 +109,20 @@ def test_launch_argument_errors_before_any_gpu_call(lib):
         assert lib.oscar_quant_write(C.byref(sh), C.byref(good_layer), C.byref(ok_cache), kp, vp, 0x10, 1,
                                      None) == K.OSCAR_EINVAL
         assert b"16-byte" in lib.oscar_last_error()
+    # the host-table step carries its tables in the launch arguments: at most 64
+    # requests, and its host arrays are required
+    slots = np.full((4, 65), -1, np.int32)
+    ctx = np.ones(65, np.int32)
+    assert lib.oscar_decode_step_host_tables(C.byref(sh), C.byref(good_layer), C.byref(ok_cache), 0x10, 0x10,
+                                             slots.ctypes.data, 0x10, 65, 0x10, 1, 0x10, 1, ctx.ctypes.data, 0, 0,
+                                             0x10, 0x100, 1 << 20, None) == K.OSCAR_EINVAL
+    assert b"launch arguments" in lib.oscar_last_error()
+    assert lib.oscar_decode_step_host_tables(C.byref(sh), C.byref(good_layer), C.byref(ok_cache), 0x10, 0x10,
+                                             None, 0x10, 2, 0x10, 1, 0x10, 1, ctx.ctypes.data, 0, 0, 0x10, 0x100,
+                                             1 << 20, None) == K.OSCAR_EINVAL
+    assert lib.oscar_decode_step_host_tables(C.byref(sh), C.byref(good_layer), C.byref(ok_cache), 0x10, 0x10,
+                                             slots.ctypes.data, 0x10, 0, 0x10, 1, 0x10, 1, ctx.ctypes.data, 0, 0,
+                                             0x10, 0x100, 1 << 20, None) == K.OSCAR_OK
 
 
 def test_workspace_bytes_monotone(lib):
