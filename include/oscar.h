@@ -311,8 +311,8 @@ oscar_status oscar_prefill_attn(const oscar_shape* shape, const oscar_layer* lay
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* Splits chosen when 0 is passed: the count whose work items fill two whole
- * rounds of the wavefronts the device runs at once, at most 64 and at least 32
- * pages per split (deterministic for a given device). */
+ * rounds of the wavefronts the device runs at once, at most 128 and at least
+ * 16 pages per split (deterministic for a given device). */
 int32_t oscar_decode_auto_splits(const oscar_shape* shape, int32_t batch, int32_t max_int2_pages);
 
 /* INT2 splits oscar_prefill_attn chooses when 0 is passed, for a chunk of

@@ -134,7 +134,8 @@ def test_tiny_write_pages_and_decode():
     out = dc.decode([seq], q).cpu().numpy()
     ref = O.decode_attention(q[0], st, cal, w.group)[None]
     _check_close(out, ref, "tiny decode")
-    for si in (1, 3, 7, 64):
+    # 200 splits: more splits than some pages hold tokens for (empty partials)
+    for si in (1, 3, 7, 64, 200):
         out = dc.decode([seq], q, splits_int2=si).cpu().numpy()
         _check_close(out, ref, f"tiny decode splits={si}")
 
@@ -152,7 +153,9 @@ def test_qwen3_8b_layer_32k():
     _check_pages(dc, seq, st, w, "qwen3_8b_32k")
     q = synth.q_decode_bf16(w, 0)[None]
     ref = O.decode_attention(q[0], st, cal, w.group)[None]
-    for si in (0, 5, 16):
+    # past 64 splits the combine merges chunks of 64 partial rows in groups of
+    # 16: 100 (a partial group), 128 (two chunks), 130 (a third chunk of two)
+    for si in (0, 5, 16, 100, 128, 130):
         out = dc.decode([seq], q, splits_int2=si).cpu().numpy()
         _check_close(out, ref, f"qwen3_8b_32k decode splits={si}")
 

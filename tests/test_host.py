@@ -132,9 +132,10 @@ def test_workspace_bytes_monotone(lib):
     assert 0 < a < b and a % 256 == 0
     assert K.oscar_decode_workspace_bytes(sh, 28, 0, 0) >= b
     s = K.oscar_decode_auto_splits(sh, 28, 6300)
-    assert 1 <= s <= 64
-    assert K.oscar_decode_auto_splits(sh, 1, 64) == 2          # at least 32 pages per split
-    assert K.oscar_decode_auto_splits(sh, 1, 40000) == 64      # capped
+    assert 1 <= s <= 128
+    assert K.oscar_decode_auto_splits(sh, 1, 64) == 4          # at least 16 pages per split
+    assert K.oscar_decode_auto_splits(sh, 1, 2048) == 128      # one 32K-token request: 128 splits
+    assert K.oscar_decode_auto_splits(sh, 1, 40000) == 128     # capped
     assert K.oscar_decode_auto_splits(sh, 28, 6300) == 36      # 2 rounds of 4096 wavefronts over 224 (request, head)
     assert K.oscar_decode_auto_splits(sh, 4096, 6300) == 1     # more than two rounds of pairs
     # 12 query heads per KV head at G = 32: three tiles padded to four, one wide wavefront per
