@@ -1838,21 +1838,38 @@ __global__ __launch_bounds__(512) void decode_combine(DecodeParams p) {
           __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
           __builtin_amdgcn_wave_barrier();
           __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+          // 32 k at a time: every LDS read of a batch is issued before its
+          // FMAs (one LDS latency per batch, not one per read), two
+          // accumulators per output
+          float r0b = 0.f, r1b = 0.f;
           r0 = r1 = 0.f;
           const float* row0 = rv + lane * kRvStride;
           const float* row1 = rv + (lane + 64) * kRvStride;
-#pragma unroll 8
-          for (int k = 0; k < kHeadDim; k += 4) {
-            const float4 a = *(const float4*)&aint[wl][k];
-            r0 = fmaf(a.x, row0[k], r0);
-            r1 = fmaf(a.x, row1[k], r1);
-            r0 = fmaf(a.y, row0[k + 1], r0);
-            r1 = fmaf(a.y, row1[k + 1], r1);
-            r0 = fmaf(a.z, row0[k + 2], r0);
-            r1 = fmaf(a.z, row1[k + 2], r1);
-            r0 = fmaf(a.w, row0[k + 3], r0);
-            r1 = fmaf(a.w, row1[k + 3], r1);
+#pragma unroll
+          for (int k0 = 0; k0 < kHeadDim; k0 += 32) {
+            float4 a[8];
+            float x0[32], x1[32];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) a[i] = *(const float4*)&aint[wl][k0 + 4 * i];
+#pragma unroll
+            for (int i = 0; i < 32; ++i) {
+              x0[i] = row0[k0 + i];
+              x1[i] = row1[k0 + i];
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              r0 = fmaf(a[i].x, x0[4 * i], r0);
+              r1 = fmaf(a[i].x, x1[4 * i], r1);
+              r0b = fmaf(a[i].y, x0[4 * i + 1], r0b);
+              r1b = fmaf(a[i].y, x1[4 * i + 1], r1b);
+              r0 = fmaf(a[i].z, x0[4 * i + 2], r0);
+              r1 = fmaf(a[i].z, x1[4 * i + 2], r1);
+              r0b = fmaf(a[i].w, x0[4 * i + 3], r0b);
+              r1b = fmaf(a[i].w, x1[4 * i + 3], r1b);
+            }
           }
+          r0 += r0b;
+          r1 += r1b;
         }
         xch[wl][lane] = r0;
         xch[wl][lane + 64] = r1;
