@@ -1563,8 +1563,17 @@ __device__ void bf16_item(const DecodeParams& p, int b, int kv, int split, int c
     }
     const int32_t* bt = p.bf16_bt + (int64_t)b * p.max_bf16_pages;
     const int64_t npg = p.n_bf16_pages;
+    // the split's page ids, 64 at a time, one per lane (one load beside the q
+    // loads, not one dependent load per pair): lane i holds page id_base + i
+    int id_base = p_begin;
+    auto load_ids = [&](int base) {
+      const int lp = base + lane;
+      return lp < p_end ? bt[lp] : -1;
+    };
+    int ids = load_ids(id_base);
     // the pair at lp0: its blocks (bad ids read page 0 and are masked), its
     // page limit for the masked path, and whether it needs no mask at all
+    // (lp0 - id_base is even and below 64: both pages are in `ids`)
     struct PairAt {
       const uint8_t* blk0;
       const uint8_t* blk1;
@@ -1573,8 +1582,8 @@ __device__ void bf16_item(const DecodeParams& p, int b, int kv, int split, int c
     };
     auto pair_at = [&](int lp0) {
       const bool has1 = lp0 + 1 < p_end;
-      int pg0 = bt[lp0];
-      int pg1 = has1 ? bt[lp0 + 1] : pg0;
+      int pg0 = __builtin_amdgcn_readlane(ids, lp0 - id_base);
+      int pg1 = has1 ? __builtin_amdgcn_readlane(ids, lp0 + 1 - id_base) : pg0;
       const bool ok0 = pg0 >= 0 && pg0 < npg;
       const bool ok1 = pg1 >= 0 && pg1 < npg;
       if (!ok0) pg0 = 0;
@@ -1594,6 +1603,10 @@ __device__ void bf16_item(const DecodeParams& p, int b, int kv, int split, int c
       PairAt pn = pa;
       Bf16PairData nxt;
       if (more) {
+        if (lp0 + 2 >= id_base + 64) {  // the next 64 page ids
+          id_base += 64;
+          ids = load_ids(id_base);
+        }
         pn = pair_at(lp0 + 2);
         if constexpr (PREFETCH) nxt = bf16_pair_load(pn.blk0, pn.blk1);
       }
