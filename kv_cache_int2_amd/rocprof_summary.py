@@ -7,9 +7,10 @@
         steps of a run, without its warm-up).
 
     python -m kv_cache_int2_amd.rocprof_summary sq DB --kernel NAME [--kernel NAME ...]
-        [--tail N]  MFMA utilisation and VALU busy per kernel from one SQ counter pass
-        (SQ_INSTS_VALU, SQ_INSTS_MFMA, SQ_ACTIVE_INST_VALU,
-        SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE).
+        [--tail N] [--skip-last M]  MFMA utilisation and VALU busy per kernel from one
+        SQ counter pass (SQ_INSTS_VALU, SQ_INSTS_MFMA, SQ_ACTIVE_INST_VALU,
+        SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE); --skip-last drops each kernel's
+        last M dispatches before --tail takes its last N.
 
     python -m kv_cache_int2_amd.rocprof_summary pmc --fetch DB --write DB
         --kernel NAME --copy NAME --copy-bytes N --workload W --source FILE
@@ -66,13 +67,15 @@ def counter_agg_per_dispatch(db: str, counter: str, kernel: str, agg: str):
 SQ_COUNTERS = ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_ACTIVE_INST_VALU", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
 
 
-def sq_stats(db: str, kernel: str, cu_num: int, simd_num: int, tail: int = 0):
+def sq_stats(db: str, kernel: str, cu_num: int, simd_num: int, tail: int = 0, skip_last: int = 0):
     """MFMA utilisation and VALU busy of one kernel, averaged over its
     dispatches, with the tool's own derived-metric formulas:
       MfmaUtil = 100 sum(SQ_VALU_MFMA_BUSY_CYCLES) / (max(GRBM_GUI_ACTIVE) SIMD_NUM)
       VALUBusy = 100 sum(SQ_ACTIVE_INST_VALU) / CU_NUM / max(GRBM_GUI_ACTIVE)"""
     v = {c: counter_agg_per_dispatch(db, c, kernel, "max" if c.startswith("GRBM") else "sum") for c in SQ_COUNTERS}
     ids = sorted(set.intersection(*(set(x) for x in v.values())))
+    if skip_last > 0:
+        ids = ids[:-skip_last]
     if tail > 0:
         ids = ids[-tail:]
     if not ids:
@@ -90,7 +93,7 @@ def cmd_sq(a):
     out = [f"| kernel | dispatches | MFMA util % | VALU busy % | VALU insts | MFMA insts | GUI active cycles |",
            "|---|---:|---:|---:|---:|---:|---:|"]
     for k in a.kernel:
-        r = sq_stats(a.db, k, a.cu_num, a.simd_num, a.tail)
+        r = sq_stats(a.db, k, a.cu_num, a.simd_num, a.tail, a.skip_last)
         out.append(f"| {k} | {r['dispatches']} | {r['mfma_util_pct']:.1f} | {r['valu_busy_pct']:.1f} "
                    f"| {r['valu_insts']:.4g} | {r['mfma_insts']:.4g} | {r['gui_active_cycles']:.4g} |")
     print("\n".join(out))
@@ -171,6 +174,7 @@ def main(argv=None):
     q.add_argument("--cu-num", type=int, default=256)
     q.add_argument("--simd-num", type=int, default=1024)
     q.add_argument("--tail", type=int, default=0, help="only each kernel's last N dispatches")
+    q.add_argument("--skip-last", type=int, default=0, help="leave out each kernel's last M dispatches first")
     a = ap.parse_args(argv)
     {"trace": cmd_trace, "pmc": cmd_pmc, "sq": cmd_sq}[a.cmd](a)
 
