@@ -169,6 +169,72 @@ __device__ __forceinline__ int q_pos(const DecodeParams& p, int b, int hv) {
   return p.ctx_lens[b] - p.chunk + p.chunk0 + hv / p.g_real;
 }
 
+// Lane exchanges without LDS (a wavefront is four rows of 16 lanes): every
+// lane takes the value n lanes around its row (DPP row rotate), or, from
+// v_permlane16/32_swap with both operands x, the values of the two rows it is
+// paired with (rows (0,1) and (2,3); rows (0,2) and (1,3)).
+__device__ __forceinline__ uint32_t lane_ror(uint32_t x, int n) {
+  switch (n) {
+    case 1: return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x121, 0xf, 0xf, false);
+    case 2: return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x122, 0xf, 0xf, false);
+    case 4: return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x124, 0xf, 0xf, false);
+    default: return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x128, 0xf, 0xf, false);
+  }
+}
+__device__ __forceinline__ double ror_f64(double v, int n) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint64_t r = (uint64_t)lane_ror((uint32_t)u, n) | ((uint64_t)lane_ror((uint32_t)(u >> 32), n) << 32);
+  return __builtin_bit_cast(double, r);
+}
+template <bool ROWS32>
+__device__ __forceinline__ void row_pair_f64(double v, double& a, double& b) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const auto lo = ROWS32 ? __builtin_amdgcn_permlane32_swap((uint32_t)u, (uint32_t)u, false, false)
+                         : __builtin_amdgcn_permlane16_swap((uint32_t)u, (uint32_t)u, false, false);
+  const auto hi = ROWS32 ? __builtin_amdgcn_permlane32_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false, false)
+                         : __builtin_amdgcn_permlane16_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false, false);
+  a = __builtin_bit_cast(double, (uint64_t)lo[0] | ((uint64_t)hi[0] << 32));
+  b = __builtin_bit_cast(double, (uint64_t)lo[1] | ((uint64_t)hi[1] << 32));
+}
+// minimum and maximum of a double over the G (32 or 64) consecutive lanes of
+// each group, in every lane: rows first (rotations by 1, 2, 4, 8), then row
+// pairs.  Comparisons keep the current value against a NaN (a group holding
+// NaN is flagged apart).
+template <int G>
+__device__ __forceinline__ void group_minmax_f64(double& mn, double& mx) {
+#pragma unroll
+  for (int n = 1; n < 16; n <<= 1) {
+    const double a = ror_f64(mn, n), b = ror_f64(mx, n);
+    mn = a < mn ? a : mn;
+    mx = b > mx ? b : mx;
+  }
+  double a, b;
+  row_pair_f64<false>(mn, a, b);
+  mn = a < b ? a : b;
+  row_pair_f64<false>(mx, a, b);
+  mx = a > b ? a : b;
+  if constexpr (G == 64) {
+    row_pair_f64<true>(mn, a, b);
+    mn = a < b ? a : b;
+    row_pair_f64<true>(mx, a, b);
+    mx = a > b ? a : b;
+  }
+}
+// maximum of a non-negative float over the whole wavefront, in every lane
+__device__ __forceinline__ float wave_max_nonneg(float x) {
+  uint32_t u = __builtin_bit_cast(uint32_t, x);  // non-negative floats order as their bit patterns
+#pragma unroll
+  for (int n = 1; n < 16; n <<= 1) {
+    const uint32_t y = lane_ror(u, n);
+    u = y > u ? y : u;
+  }
+  auto p16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  u = p16[0] > p16[1] ? p16[0] : p16[1];
+  auto p32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  u = p32[0] > p32[1] ? p32[0] : p32[1];
+  return __builtin_bit_cast(float, u);
+}
+
 // A 128 x 128 fp32 matrix to LDS by a block of 256 threads, row stride
 // `stride` floats: 16 independent 16-byte loads per thread, all issued before
 // the first store.
@@ -232,15 +298,10 @@ __device__ __forceinline__ void quantise_and_store(const DecodeParams& p, int kv
   const double tau = m ? p.tau_v : p.tau_k;
   const double v = acc < -tau ? -tau : (acc > tau ? tau : acc);
   double mn = v, mx = v;
-  bool nan = v != v;
   // the G channels of a group are consecutive lanes of one wavefront
-#pragma unroll
-  for (int off = 1; off < G; off <<= 1) {
-    const double omn = __shfl_xor(mn, off), omx = __shfl_xor(mx, off);
-    mn = omn < mn ? omn : mn;
-    mx = omx > mx ? omx : mx;
-    nan |= __shfl_xor((int)nan, off) != 0;
-  }
+  group_minmax_f64<G>(mn, mx);
+  const uint64_t nan_lanes = __builtin_amdgcn_ballot_w64(v != v);
+  const bool nan = G == 64 ? nan_lanes != 0 : ((nan_lanes >> (threadIdx.x & 32)) & 0xffffffffull) != 0;
   uint32_t pair = nan_sz<MB>();
   uint8_t c = 0;
   if (!nan) {
@@ -485,7 +546,7 @@ __global__ __launch_bounds__(256) void decode_prologue(DecodeParams p, ArgTables
     }
   }
 
-  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  mx = wave_max_nonneg(mx);
   if ((t & 63) == 0) red[t >> 6] = mx;
   __syncthreads();
   mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
