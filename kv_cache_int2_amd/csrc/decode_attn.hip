@@ -171,8 +171,20 @@ __device__ __forceinline__ int q_pos(const DecodeParams& p, int b, int hv) {
 
 // Lane exchanges without LDS (a wavefront is four rows of 16 lanes): every
 // lane takes the value n lanes around its row (DPP row rotate), or, from
-// v_permlane16/32_swap with both operands x, the values of the two rows it is
-// paired with (rows (0,1) and (2,3); rows (0,2) and (1,3)).
+// v_permlane16/32_swap with x in both registers, the values of the two rows it
+// is paired with (rows (0,1) and (2,3); rows (0,2) and (1,3)).
+// The swaps are written in asm: the compiler's builtins for them have handed
+// back the first register for both results.  The s_nop 1 before gives the two
+// wait states a swap needs after a VALU write of its operands; the one after
+// gives the two a DPP read of a result needs (the compiler does not count an
+// asm block as a VALU write).
+template <bool ROWS32>
+__device__ __forceinline__ void swap_rows(uint32_t& a, uint32_t& b) {
+  if constexpr (ROWS32)
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  else
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
 __device__ __forceinline__ uint32_t lane_ror(uint32_t x, int n) {
   switch (n) {
     case 1: return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x121, 0xf, 0xf, false);
@@ -189,12 +201,11 @@ __device__ __forceinline__ double ror_f64(double v, int n) {
 template <bool ROWS32>
 __device__ __forceinline__ void row_pair_f64(double v, double& a, double& b) {
   const uint64_t u = __builtin_bit_cast(uint64_t, v);
-  const auto lo = ROWS32 ? __builtin_amdgcn_permlane32_swap((uint32_t)u, (uint32_t)u, false, false)
-                         : __builtin_amdgcn_permlane16_swap((uint32_t)u, (uint32_t)u, false, false);
-  const auto hi = ROWS32 ? __builtin_amdgcn_permlane32_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false, false)
-                         : __builtin_amdgcn_permlane16_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false, false);
-  a = __builtin_bit_cast(double, (uint64_t)lo[0] | ((uint64_t)hi[0] << 32));
-  b = __builtin_bit_cast(double, (uint64_t)lo[1] | ((uint64_t)hi[1] << 32));
+  uint32_t l0 = (uint32_t)u, l1 = l0, h0 = (uint32_t)(u >> 32), h1 = h0;
+  swap_rows<ROWS32>(l0, l1);
+  swap_rows<ROWS32>(h0, h1);
+  a = __builtin_bit_cast(double, (uint64_t)l0 | ((uint64_t)h0 << 32));
+  b = __builtin_bit_cast(double, (uint64_t)l1 | ((uint64_t)h1 << 32));
 }
 // minimum and maximum of a double over the G (32 or 64) consecutive lanes of
 // each group, in every lane: rows first (rotations by 1, 2, 4, 8), then row
@@ -228,10 +239,12 @@ __device__ __forceinline__ float wave_max_nonneg(float x) {
     const uint32_t y = lane_ror(u, n);
     u = y > u ? y : u;
   }
-  auto p16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  u = p16[0] > p16[1] ? p16[0] : p16[1];
-  auto p32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  u = p32[0] > p32[1] ? p32[0] : p32[1];
+  uint32_t v = u;
+  swap_rows<false>(u, v);
+  u = v > u ? v : u;
+  v = u;
+  swap_rows<true>(u, v);
+  u = v > u ? v : u;
   return __builtin_bit_cast(float, u);
 }
 
@@ -1784,13 +1797,27 @@ __global__ __launch_bounds__(64) void decode_bf16(DecodeParams p) {
 constexpr int kRvStride = kHeadDim + 1;
 constexpr int kCombineRows = 32;
 
+// maximum / sum over the wavefront, in every lane: rows by DPP rotations, then
+// the row pairs by permlane swaps (no LDS round trips)
 __device__ __forceinline__ float wave_max(float x) {
-  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
-  return x;
+#pragma unroll
+  for (int n = 1; n < 16; n <<= 1) x = fmaxf(x, __builtin_bit_cast(float, lane_ror(__builtin_bit_cast(uint32_t, x), n)));
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  swap_rows<false>(a, b);
+  x = fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+  a = b = __builtin_bit_cast(uint32_t, x);
+  swap_rows<true>(a, b);
+  return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
 }
 __device__ __forceinline__ float wave_sum(float x) {
-  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
-  return x;
+#pragma unroll
+  for (int n = 1; n < 16; n <<= 1) x += __builtin_bit_cast(float, lane_ror(__builtin_bit_cast(uint32_t, x), n));
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  swap_rows<false>(a, b);
+  x = __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+  a = b = __builtin_bit_cast(uint32_t, x);
+  swap_rows<true>(a, b);
+  return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
 }
 __device__ __forceinline__ float lane_value(float x, int l) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));

@@ -121,19 +121,26 @@ __device__ __forceinline__ int row_sum_i32(int x) {
   for (int n = 1; n < 16; n <<= 1) x += (int)dpp_ror((uint32_t)x, n);
   return x;
 }
-// v_permlane16_swap / v_permlane32_swap with both operands x: the pair
+// v_permlane16_swap / v_permlane32_swap with x in both registers: the pair
 // (first, second) holds, for each lane, the values of the two rows it is
 // paired with: rows (0,1) and (2,3) for 16, rows (0,2) and (1,3) for 32.
+// Written in asm: the compiler's builtins for them have handed back the first
+// register for both results.  The s_nop 1 before gives the two wait states a
+// swap needs after a VALU write of its operands; the one after gives the two a
+// DPP read of a result needs (the compiler does not count an asm block as a
+// VALU write).
 struct RowPair {
   uint32_t a, b;
 };
 __device__ __forceinline__ RowPair swap16(uint32_t x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-  return RowPair{r[0], r[1]};
+  RowPair r{x, x};
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(r.a), "+v"(r.b));
+  return r;
 }
 __device__ __forceinline__ RowPair swap32(uint32_t x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-  return RowPair{r[0], r[1]};
+  RowPair r{x, x};
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(r.a), "+v"(r.b));
+  return r;
 }
 __device__ __forceinline__ double f64_of(uint32_t lo, uint32_t hi) {
   return __builtin_bit_cast(double, (uint64_t)lo | ((uint64_t)hi << 32));
