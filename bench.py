@@ -53,6 +53,11 @@ def parse():
     ap.add_argument("--layout", choices=["workload", "pages"], default="workload",
                     help="pages: the pages' default layout (sink 64, recent 256, G = 64, FP8 scale and zero)")
     ap.add_argument("--splits", type=int, default=0, help="INT2 splits per (request, KV head); 0 = auto")
+    ap.add_argument("--batch", type=int, default=0, help="override the workload's batch (requests)")
+    ap.add_argument("--decode-form", choices=["auto", "standard", "small"], default="auto",
+                    help="decode launch form (oscar_decode_set_small_grid): auto, standard (one combine work "
+                         "group per (request, KV head)), small (bf16 splits inside the INT2 kernel's grid, one "
+                         "combine work group per query head, where one wavefront holds an item's tiles)")
     ap.add_argument("--mode", choices=["decode", "prefill"], default="decode",
                     help="prefill: time chunked-prefill attention (oscar_prefill_attn) of --chunk queries per "
                          "request over the filled cache instead of decode steps")
@@ -216,6 +221,9 @@ def main():
     if args.layout == "pages":
         w = dataclasses.replace(w, sink=64, recent=256, group=64)
         scale_bits = 8
+    if args.batch:
+        w = dataclasses.replace(w, batch=args.batch)
+    K.oscar_decode_set_small_grid({"auto": 0, "standard": 1, "small": 2}[args.decode_form])
     group = args.group or w.group
     mb = 4 if scale_bits == 16 else 2
     B, hq, hkv = w.batch, w.n_q_heads, w.n_kv_heads
@@ -616,7 +624,8 @@ def main():
                    "head_dim": 128, "group": group, "sink": w.sink, "recent": w.recent, "page_size": 16,
                    "scale_bits": scale_bits, "bits_per_element": round(bits_per_element, 4),
                    "splits_int2": si, "step": "unfused" if args.unfused else ("fused, host tables" if host_tables else "fused"),
-                   "interleaved_writes": bool(iw), "cold": bool(flush is not None)},
+                   "interleaved_writes": bool(iw), "cold": bool(flush is not None),
+                   "decode_form": args.decode_form},
         "value_basis": value_basis,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,

@@ -312,8 +312,25 @@ oscar_status oscar_prefill_attn(const oscar_shape* shape, const oscar_layer* lay
 
 /* Splits chosen when 0 is passed: the count whose work items fill two whole
  * rounds of the wavefronts the device runs at once, at most 128 and at least
- * 16 pages per split (deterministic for a given device). */
+ * 16 pages per split (deterministic for a given device and small-grid mode).
+ * Where the small-grid form applies (oscar_decode_set_small_grid not 1, one
+ * wavefront per work item), the count is lowered to the one whose INT2 items
+ * and four bf16 splits fit two wavefronts per SIMD, if that leaves at least 24
+ * splits. */
 int32_t oscar_decode_auto_splits(const oscar_shape* shape, int32_t batch, int32_t max_int2_pages);
+
+/* Form of the decode launches ([IT] 2.2.B split-K decode with a log-sum-exp
+ * combine; the form changes only the work split, not what is computed).  On a
+ * small grid (one request, say) the bf16 sink/recent splits run as extra
+ * items of the INT2 kernel's launch, and the combine takes one work group per
+ * (request, KV head, query head) instead of one per (request, KV head).
+ * mode 0 (the default): that form when the INT2 items and the bf16 splits fit
+ * two wavefronts per SIMD and one wavefront holds a work item's tiles; 1:
+ * never; 2: whenever one wavefront holds a work item's tiles.  Process-wide
+ * (every later decode and decode-step call, any thread); returns the previous
+ * mode, or -1 (mode unchanged) for a mode outside 0..2.  Results of the two
+ * forms differ only in fp32 summation order. */
+int32_t oscar_decode_set_small_grid(int32_t mode);
 
 /* INT2 splits oscar_prefill_attn chooses when 0 is passed, for a chunk of
  * `chunk` queries: the fewest whose work items fill their last round of the

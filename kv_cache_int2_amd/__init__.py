@@ -89,6 +89,7 @@ _SIGS = {
     "oscar_decode_attn_bf16_baseline": (C.c_int32, [C.POINTER(Shape), C.POINTER(Cache), P, C.c_int32, P,
                                                     C.c_int32, P, C.c_int32, P, P, C.c_size_t, P]),
     "oscar_decode_auto_splits": (C.c_int32, [C.POINTER(Shape), C.c_int32, C.c_int32]),
+    "oscar_decode_set_small_grid": (C.c_int32, [C.c_int32]),
     "oscar_prefill_auto_splits": (C.c_int32, [C.POINTER(Shape), C.c_int32, C.c_int32, C.c_int32]),
     "oscar_plan_decode_step": (C.c_int32, [P, P, C.c_int32, P, P, P, P, P, P, P]),
     "oscar_profile_enable": (C.c_int32, [C.c_int32]),
@@ -294,6 +295,10 @@ def oscar_decode_workspace_bytes(shape, batch, splits_int2=0, splits_bf16=0) -> 
 
 def oscar_decode_auto_splits(shape, batch, max_int2_pages) -> int:
     return int(lib().oscar_decode_auto_splits(C.byref(shape), batch, max_int2_pages))
+
+
+def oscar_decode_set_small_grid(mode: int) -> int:
+    return int(lib().oscar_decode_set_small_grid(mode))
 
 
 def oscar_prefill_auto_splits(shape, batch, max_int2_pages, chunk) -> int:

@@ -1721,8 +1721,12 @@ __device__ void bf16_item(const DecodeParams& p, int b, int kv, int split, int c
 // few spilled registers: measured 8 % faster than 2 without them); four 2.  Wavefronts of one item share the staged pages.  LDS per
 // item: each wavefront's p and the staging ring (three slots for one
 // wavefront, four when shared).
-template <int NG, int MB, int CT, int W>
-__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(CT == 1 ? 4 : (CT == 2 && W == 1 ? 3 : (CT == 2 || CT == 4 ? 2 : 1)), 8))) void
+// BX (small grids, W = 1): the grid's last batch n_kv splits_bf16 work groups
+// run the bf16 region, one split each (its pairs not prefetched), beside the
+// INT2 items.  The kernel then holds the bf16 item's registers (208 VGPRs):
+// two wavefronts per SIMD, all that a grid this form is chosen for needs.
+template <int NG, int MB, int CT, int W, bool BX = false>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(BX ? 2 : (CT == 1 ? 4 : (CT == 2 && W == 1 ? 3 : (CT == 2 || CT == 4 ? 2 : 1))), 8))) void
 decode_int2(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) float p_lds[W][(16 * CT / NG) * 32];
   __shared__ __attribute__((aligned(16))) uint8_t stage[(W == 1 ? 6 : 8) * Int2Layout{NG, MB}.bytes()];
@@ -1734,7 +1738,15 @@ decode_int2(DecodeParams p) {
   // bk, so its q operands and partial rows pass through one L2; in time the
   // items still come pair by pair, as in the plain order.
   const int item = blockIdx.x;
-  const int S = p.splits_int2, bkn = (int)gridDim.x / S;
+  const int S = p.splits_int2, bkn = p.batch * p.n_kv;
+  if constexpr (BX) {
+    static_assert(W == 1, "bf16 items are one wavefront");
+    if (item >= bkn * S) {
+      const int e = item - bkn * S, pair = e / p.splits_bf16;
+      bf16_item<false>(p, pair / p.n_kv, pair % p.n_kv, S + e % p.splits_bf16, 0);
+      return;
+    }
+  }
   int split, bk;
   if ((bkn & 7) == 0) {
     const int j = item >> 3;
@@ -2001,6 +2013,140 @@ __global__ __launch_bounds__(512) void decode_combine(DecodeParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// combine on small grids: one work group per (request, KV head, query head)
+// ---------------------------------------------------------------------------
+// With one request (say) the form above runs eight work groups, each a chain
+// of dependent loads.  Here the bf16 splits have run inside the INT2 kernel's
+// grid, and each query head takes a work group of nine wavefronts: wavefront w
+// < 8 merges the INT2 splits [w SI / 8, (w + 1) SI / 8) of the head (16 rows at
+// 128 splits: one batch of loads), R_V's loads in flight meanwhile and its LDS
+// stores after; wavefront 8 merges the bf16 splits.  The eight INT2 parts are
+// joined in LDS, and R_V^T is spread over the eight wavefronts: output channel
+// 16 w + lane / 4, a quarter of k per lane, summed over the lane quad.
+constexpr int kHeadMergeWaves = 8;
+
+__global__ __launch_bounds__(64 * (kHeadMergeWaves + 1)) void decode_combine_head(DecodeParams p) {
+  __shared__ float rv[kHeadDim * kRvStride];
+  __shared__ float part[kHeadMergeWaves][kHeadDim + 2];  // each INT2 range: rows, M, L
+  __shared__ float bpart[kHeadDim + 2];                  // the bf16 splits: rows, M, L
+  __shared__ float ajoin[kHeadDim];                      // the joined INT2 part
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  // XCD-aware order, as in the INT2 kernel: the work groups of pair bk run on
+  // XCD bk % 8, where that pair's partial rows were written
+  const int bkn = p.batch * p.n_kv, g = p.g, item = blockIdx.x;
+  int bk, h;
+  if ((bkn & 7) == 0) {
+    const int j = item >> 3;
+    h = j % g;
+    bk = 8 * (j / g) + (item & 7);
+  } else {
+    h = item % g;
+    bk = item / g;
+  }
+  const int b = bk / p.n_kv, kv = bk % p.n_kv;
+  const int S = p.splits_int2 + p.splits_bf16, SI = p.splits_int2;
+  const bool rot = SI > 0 && p.r_v;
+  const float* base = p.partial + ((int64_t)b * p.n_q + kv * g + h) * S * kPartialStride;
+  float M, L, a0, a1;
+  if (w < kHeadMergeWaves) {
+    constexpr int kT = 64 * kHeadMergeWaves, kPer = kHeadDim * kHeadDim / 4 / kT;
+    float4 rvv[kPer];
+    const float4* R = (const float4*)(p.r_v + (int64_t)kv * kHeadDim * kHeadDim);
+    if (rot) {
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) rvv[k] = R[threadIdx.x + kT * k];
+    }
+    merge_splits(base, (int)((int64_t)w * SI / kHeadMergeWaves), (int)((int64_t)(w + 1) * SI / kHeadMergeWaves), M,
+                 L, a0, a1);
+    part[w][lane] = a0;
+    part[w][lane + 64] = a1;
+    if (lane == 0) {
+      part[w][kHeadDim] = M;
+      part[w][kHeadDim + 1] = L;
+    }
+    if (rot) {
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) {
+        const int e = threadIdx.x + kT * k;
+        float* d = rv + (e >> 5) * kRvStride + 4 * (e & 31);
+        d[0] = rvv[k].x;
+        d[1] = rvv[k].y;
+        d[2] = rvv[k].z;
+        d[3] = rvv[k].w;
+      }
+    }
+  } else {
+    merge_splits(base, SI, S, M, L, a0, a1);
+    bpart[lane] = a0;
+    bpart[lane + 64] = a1;
+    if (lane == 0) {
+      bpart[kHeadDim] = M;
+      bpart[kHeadDim + 1] = L;
+    }
+  }
+  __syncthreads();  // the nine parts and R_V are in LDS
+  // join the INT2 ranges: mi their largest max, each weighted by 2^(M_w - mi)
+  // (0 for a range without tokens)
+  float mi = kNegInf;
+#pragma unroll
+  for (int r = 0; r < kHeadMergeWaves; ++r) mi = fmaxf(mi, part[r][kHeadDim]);
+  float wts[kHeadMergeWaves], li = 0.f;
+#pragma unroll
+  for (int r = 0; r < kHeadMergeWaves; ++r) {
+    const float mr = part[r][kHeadDim];
+    wts[r] = mr == kNegInf ? 0.f : exp2f(mr - mi);
+    li = fmaf(wts[r], part[r][kHeadDim + 1], li);
+  }
+  if (w < kHeadMergeWaves && lane < kHeadDim / kHeadMergeWaves) {
+    const int k = (kHeadDim / kHeadMergeWaves) * w + lane;
+    float a = 0.f;
+#pragma unroll
+    for (int r = 0; r < kHeadMergeWaves; ++r) a = fmaf(wts[r], part[r][k], a);
+    ajoin[k] = a;
+  }
+  __syncthreads();  // the joined INT2 part is in LDS
+  if (w >= kHeadMergeWaves) return;
+  const int j = (kHeadDim / kHeadMergeWaves) * w + (lane >> 2), kq = lane & 3;
+  float r;
+  if (rot) {
+    // out_j = sum_k a_k R_V[j][k]: lane quarter kq of k, read from k offset
+    // 8 kq on (the 32 lanes of a half-wavefront then hit 32 distinct banks)
+    const float* row = rv + j * kRvStride + 32 * kq;
+    const float* av = ajoin + 32 * kq;
+    float x[32], y[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const int kk = (i + 8 * kq) & 31;
+      x[i] = row[kk];
+      y[i] = av[kk];
+    }
+    float r0 = 0.f, r1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; i += 2) {
+      r0 = fmaf(y[i], x[i], r0);
+      r1 = fmaf(y[i + 1], x[i + 1], r1);
+    }
+    r = r0 + r1;
+    // sum over the lane quad (DPP quad permutations [1,0,3,2] and [2,3,0,1])
+    r += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, r), 0xb1, 0xf, 0xf, false));
+    r += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, r), 0x4e, 0xf, 0xf, false));
+  } else {
+    r = ajoin[j];
+  }
+  if (kq == 0) {
+    const float mb = bpart[kHeadDim], lb = bpart[kHeadDim + 1];
+    const float Mx = fmaxf(mi, mb);
+    float* o = p.out + q_row(p, b, kv, h);
+    if (Mx == kNegInf) {  // no token at all
+      o[j] = 0.f;
+    } else {
+      const float wi = mi == kNegInf ? 0.f : exp2f(mi - Mx), wb = mb == kNegInf ? 0.f : exp2f(mb - Mx);
+      o[j] = (wi * r + wb * bpart[j]) / (wi * li + wb * lb);
+    }
+  }
+}
+
 template <int NG, int MB, int CT, int W>
 hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop,
                            const ArgTables& tabs) {
@@ -2011,6 +2157,8 @@ hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream, hipEvent_t
   // the INT2 kernel's full rounds.  Up to four bf16 splits run inside the
   // combine instead.)
   const bool int2 = p.splits_int2 > 0;
+  // the small-grid form: one-wavefront INT2 items only
+  if (p.small_grid && (W != 1 || !int2 || p.splits_bf16 < 1)) return hipErrorInvalidValue;
   auto mark = [&](hipEvent_t ev) { return ev ? hipEventRecord(ev, stream) : hipSuccess; };
   hipError_t e = hipSuccess;
   if (int2) {
@@ -2021,6 +2169,16 @@ hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream, hipEvent_t
       hipLaunchKernelGGL((decode_prologue<NG, MB, CT * W, false>), dim3(bkn), dim3(256), 0, stream, p, tabs);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = mark(ev_start)) != hipSuccess) return e;
+    if constexpr (W == 1) {
+      if (p.small_grid) {
+        hipLaunchKernelGGL((decode_int2<NG, MB, CT, 1, true>), dim3(bkn * (p.splits_int2 + p.splits_bf16)), dim3(64),
+                           0, stream, p);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if ((e = mark(ev_stop)) != hipSuccess) return e;
+        hipLaunchKernelGGL(decode_combine_head, dim3(bkn * p.g), dim3(64 * (kHeadMergeWaves + 1)), 0, stream, p);
+        return hipGetLastError();
+      }
+    }
     hipLaunchKernelGGL((decode_int2<NG, MB, CT, W>), dim3(bkn * p.splits_int2), dim3(64 * W), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = mark(ev_stop)) != hipSuccess) return e;

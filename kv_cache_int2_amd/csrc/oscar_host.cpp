@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -788,7 +789,25 @@ static int device_cus() {
   return cached;
 }
 
-int32_t oscar_decode_auto_splits(const oscar_shape* shape, int32_t batch, int32_t max_int2_pages) {
+// 0 automatic, 1 never, 2 wherever the tile split allows (oscar_decode_set_small_grid)
+static std::atomic<int> g_small_grid_mode{0};
+
+int32_t oscar_decode_set_small_grid(int32_t mode) {
+  if (mode < 0 || mode > 2) return -1;
+  return g_small_grid_mode.exchange(mode);
+}
+
+// The small-grid form's INT2 kernel holds the bf16 item's registers: two
+// wavefronts per SIMD.  Its grid (INT2 items and bf16 splits) must fit that.
+static int64_t small_grid_waves() { return 8 * (int64_t)device_cus(); }
+// fewest splits worth lowering the count to for that form (32K-token requests,
+// 8 KV heads: 8 requests at 28 splits 64.5 against 72.5 us a step in the
+// standard form at 128; 16 requests at 12 splits 115.5 against 103.8 at 64)
+static const int kSmallGridMinSplits = 24;
+
+// Automatic split count for a decode with sb bf16 splits (sb < 0: the
+// all-bf16 baseline, whose splits never take the small-grid form).
+static int32_t decode_auto_splits(const oscar_shape* shape, int32_t batch, int32_t max_int2_pages, int sb) {
   if (check_shape(shape) != OSCAR_OK || batch < 1) return 1;
   // Work items run in rounds of the items that fit the device at once (4
   // SIMDs per compute unit, waves_per_simd(ct) wavefronts per SIMD, whole
@@ -798,14 +817,27 @@ int32_t oscar_decode_auto_splits(const oscar_shape* shape, int32_t batch, int32_
   // fills two whole rounds (some slack for uneven requests, few partial
   // results), within [1, 128] and at least 16 pages per split.  Small batches
   // reach the bounds: at one request of 32K tokens (8 KV heads) 128 splits
-  // measured fastest (64: 43.5 us a step, 128: 40.0, 256: 44.6, the combine's
-  // merge growing with the split count).
+  // measured fastest in the standard form (64: 43.5 us a step, 128: 40.0,
+  // 256: 44.6, the combine's merge growing with the split count).
   const int64_t pairs = (int64_t)batch * shape->n_kv_heads;
   const TileSplit ts = tile_split(ct_of(shape));
   const int64_t cap = (int64_t)device_cus() * ((4 * waves_per_simd(ts.ct)) / ts.w);
   const int64_t smax = std::max<int64_t>(1, std::min<int64_t>(kAutoMaxSplitsDecode, max_int2_pages / 16));
-  const int64_t s = 2 * cap / pairs;
-  return (int32_t)std::max<int64_t>(1, std::min<int64_t>(s, smax));
+  int64_t s = std::max<int64_t>(1, std::min<int64_t>(2 * cap / pairs, smax));
+  // Small grids (oscar_decode_set_small_grid not 1, one-wavefront items): the
+  // count that fits the small-grid form's two wavefronts per SIMD, when that
+  // leaves at least kSmallGridMinSplits (2, 4 and 8 requests of 32K tokens at
+  // 8 KV heads: 124, 60 and 28 splits, 11-15 % shorter steps than the standard
+  // form at 128)
+  if (sb >= 0 && g_small_grid_mode.load() != 1 && ts.w == 1) {
+    const int64_t fit = small_grid_waves() / pairs - sb;
+    if (fit >= kSmallGridMinSplits) s = std::min(s, fit);
+  }
+  return (int32_t)s;
+}
+
+int32_t oscar_decode_auto_splits(const oscar_shape* shape, int32_t batch, int32_t max_int2_pages) {
+  return decode_auto_splits(shape, batch, max_int2_pages, 4);
 }
 
 size_t oscar_decode_workspace_bytes(const oscar_shape* shape, int32_t batch, int32_t splits_int2,
@@ -880,15 +912,24 @@ static oscar_status decode_common(const oscar_shape* shape, const oscar_layer* l
     p.sink = 1 << 28;
     p.recent = 0;
     p.splits_int2 = 0;
-    p.splits_bf16 = splits_bf16 ? splits_bf16 : oscar_decode_auto_splits(shape, batch, max_bf16_pages);
+    p.splits_bf16 = splits_bf16 ? splits_bf16 : decode_auto_splits(shape, batch, max_bf16_pages, -1);
   } else {
     p.sink = shape->sink;
     p.recent = shape->recent;
-    p.splits_int2 = splits_int2 ? splits_int2 : oscar_decode_auto_splits(shape, batch, max_int2_pages);
     // up to four bf16 splits run inside the combine kernel (one per wavefront);
     // the bf16 region is at most sink + recent tokens
     p.splits_bf16 = splits_bf16 ? splits_bf16 : 4;
     p.bf16_in_combine = p.splits_bf16 <= 4;
+    p.splits_int2 = splits_int2 ? splits_int2 : decode_auto_splits(shape, batch, max_int2_pages, p.splits_bf16);
+    // Small grids: the bf16 splits join the INT2 kernel's launch and the
+    // combine takes a work group per query head (one request: the standard
+    // form runs eight work groups of dependent loads on 256 compute units).
+    // The INT2 kernel then holds the bf16 item's registers (two wavefronts per
+    // SIMD), so its grid must fit that; its items must be one wavefront.
+    const int mode = g_small_grid_mode.load();
+    const int64_t waves = (int64_t)batch * p.n_kv * (p.splits_int2 + p.splits_bf16);
+    p.small_grid = batch > 0 && tile_split(p.ct).w == 1 && mode != 1 && (mode == 2 || waves <= small_grid_waves());
+    if (p.small_grid) p.bf16_in_combine = 0;
     // P' = p s 2^sp stays below 2^15: s <= 2 tau_v / 3 (rounded to fp16), p <= 1
     const double smax = 2.0 * (double)layer->tau_v / 3.0;
     p.p_scale_exp = 0.f;

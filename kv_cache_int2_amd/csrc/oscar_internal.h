@@ -87,6 +87,9 @@ struct DecodeParams {
   int sink, recent;           // region rule (baseline: sink huge, recent 0)
   int splits_int2, splits_bf16;
   int bf16_in_combine;        // bf16 splits (<= 4) run by the combine kernel's wavefronts
+  // small grids: the bf16 splits run as extra items of the INT2 kernel's grid,
+  // and the combine takes one work group per (request, KV head, query head)
+  int small_grid;
   float p_scale_exp;          // P' is scaled by 2^p_scale_exp before fp16 rounding
   // workspace carve-up
   uint32_t* qb;               // [B*n_kv][ct][1536] int8x4 words: digits of 2Q as MFMA A operands

@@ -22,6 +22,23 @@ pytestmark = pytest.mark.gpu
 
 MAX_ABS, REL_L2 = 2e-3, 1e-3
 
+# decode launch forms (oscar_decode_set_small_grid): 1 one combine work group per
+# (request, KV head); 2 the small-grid form (bf16 splits inside the INT2
+# kernel's grid, one combine work group per query head) wherever it applies
+FORMS = ((1, "standard"), (2, "small-grid"))
+
+
+class _decode_form:
+    def __init__(self, mode):
+        self.mode = mode
+
+    def __enter__(self):
+        self.prev = K.oscar_decode_set_small_grid(self.mode)
+        assert self.prev in (0, 1, 2)
+
+    def __exit__(self, *exc):
+        K.oscar_decode_set_small_grid(self.prev)
+
 
 def _flush(msg):
     print(msg, flush=True)
@@ -134,10 +151,13 @@ def test_tiny_write_pages_and_decode():
     out = dc.decode([seq], q).cpu().numpy()
     ref = O.decode_attention(q[0], st, cal, w.group)[None]
     _check_close(out, ref, "tiny decode")
-    # 200 splits: more splits than some pages hold tokens for (empty partials)
-    for si in (1, 3, 7, 64, 200):
-        out = dc.decode([seq], q, splits_int2=si).cpu().numpy()
-        _check_close(out, ref, f"tiny decode splits={si}")
+    # 200 splits: more splits than some pages hold tokens for (empty partials);
+    # fewer than 8 splits leave some of the small-grid combine's merge ranges empty
+    for mode, form in FORMS:
+        with _decode_form(mode):
+            for si in (1, 3, 7, 64, 200):
+                out = dc.decode([seq], q, splits_int2=si).cpu().numpy()
+                _check_close(out, ref, f"tiny decode {form} splits={si}")
 
 
 def test_qwen3_8b_layer_32k():
@@ -155,9 +175,11 @@ def test_qwen3_8b_layer_32k():
     ref = O.decode_attention(q[0], st, cal, w.group)[None]
     # past 64 splits the combine merges chunks of 64 partial rows in groups of
     # 16: 100 (a partial group), 128 (two chunks), 130 (a third chunk of two)
-    for si in (0, 5, 16, 100, 128, 130):
-        out = dc.decode([seq], q, splits_int2=si).cpu().numpy()
-        _check_close(out, ref, f"qwen3_8b_32k decode splits={si}")
+    for mode, form in FORMS:
+        with _decode_form(mode):
+            for si in (0, 5, 16, 100, 128, 130, 256):
+                out = dc.decode([seq], q, splits_int2=si).cpu().numpy()
+                _check_close(out, ref, f"qwen3_8b_32k decode {form} splits={si}")
 
 
 @pytest.mark.parametrize("hq,hkv,group,scale_bits", [(4, 1, 32, 16), (8, 1, 32, 16), (12, 1, 32, 16), (16, 1, 32, 16),
@@ -187,10 +209,13 @@ def test_ragged_batch_gqa_groups(hq, hkv, group, scale_bits):
     q = np.stack(qs)
     ref = np.stack([O.decode_attention(q[r], stores[r], cal, group) for r in range(len(lens))])
     # bf16 splits <= 4 run inside the combine kernel, 5 in their own kernel
-    for si, sb in ((0, 0), (1, 1), (4, 3), (1, 5)):
-        out = dc.decode(seqs, q, splits_int2=si, splits_bf16=sb).cpu().numpy()
-        for r in range(len(lens)):
-            _check_close(out[r], ref[r], f"ragged hq={hq} G={group} len={lens[r]} splits={si}/{sb}")
+    # (the small-grid form: all inside the INT2 kernel's grid)
+    for mode, form in FORMS:
+        with _decode_form(mode):
+            for si, sb in ((0, 0), (1, 1), (4, 3), (1, 5)):
+                out = dc.decode(seqs, q, splits_int2=si, splits_bf16=sb).cpu().numpy()
+                for r in range(len(lens)):
+                    _check_close(out[r], ref[r], f"ragged {form} hq={hq} G={group} len={lens[r]} splits={si}/{sb}")
 
 
 @pytest.mark.parametrize("group,scale_bits", [(32, 16), (64, 8)])
@@ -216,10 +241,12 @@ def test_unwritten_slots_may_hold_nan(group, scale_bits):
         stores.append(O.store_request(kb, vb, cal, group, 4, 32, scale_bits))
     q = np.stack([synth.q_decode_bf16(w, r) for r in range(len(lens))])
     ref = np.stack([O.decode_attention(q[r], stores[r], cal, group) for r in range(len(lens))])
-    for si, sb in ((0, 0), (3, 3), (1, 5)):
-        out = dc.decode(seqs, q, splits_int2=si, splits_bf16=sb).cpu().numpy()
-        for r in range(len(lens)):
-            _check_close(out[r], ref[r], f"nan-filled G={group} len={lens[r]} splits={si}/{sb}")
+    for mode, form in FORMS:
+        with _decode_form(mode):
+            for si, sb in ((0, 0), (3, 3), (1, 5)):
+                out = dc.decode(seqs, q, splits_int2=si, splits_bf16=sb).cpu().numpy()
+                for r in range(len(lens)):
+                    _check_close(out[r], ref[r], f"nan-filled {form} G={group} len={lens[r]} splits={si}/{sb}")
     # a chunk of 45 new tokens (past the 32-token window) on two of the requests
     chunk = 45
     pf = [seqs[4], seqs[6]]
@@ -249,10 +276,12 @@ def test_empty_context_gives_zero_rows():
     kb, vb = synth.kv_request_bf16(w, 0, 0, 200)
     dc.append(full, kb, vb)
     q = np.stack([synth.q_decode_bf16(w, 0), synth.q_decode_bf16(w, 1)])
-    out = dc.decode([empty, full], q).cpu().numpy()
-    assert np.all(out[0] == 0)
     st = O.store_request(kb, vb, cal, 32, w.sink, w.recent)
-    _check_close(out[1], O.decode_attention(q[1], st, cal, 32), "after empty row")
+    for mode, form in FORMS:
+        with _decode_form(mode):
+            out = dc.decode([empty, full], q).cpu().numpy()
+        assert np.all(out[0] == 0), form
+        _check_close(out[1], O.decode_attention(q[1], st, cal, 32), f"after empty row ({form})")
 
 
 @pytest.mark.parametrize("scale_bits", [16, 8])
@@ -495,23 +524,26 @@ def test_fused_decode_step(hq, hkv, group, sink, recent, scale_bits):
         tabs = [caches[c].tables(seqs[c], max_i2, max_bf) for c in (0, 1, 2)]
         dt = [(to_dev_i32(i2), to_dev_i32(bf), to_dev_i32(ctx)) for i2, bf, ctx in tabs]
         c0, c1 = caches[0], caches[1]
-        # separate calls
-        if res[0][0]:
-            K.oscar_requant_from_bf16(sh, c0.layer, c0.cache, d[2], d[3], n=B)
-        if np.any(bufs[0][0] >= 0):
-            K.oscar_quant_write(sh, c0.layer, c0.cache, kd, vd, d[0], n=B)
-        if np.any(bufs[0][1] >= 0):
-            K.oscar_bf16_write(sh, c0.cache, kd, vd, d[1], n=B)
-        K.oscar_decode_attn(sh, c0.layer, c0.cache, q, *dt[0][:2], dt[0][2], outs[0], ws[0], si, 1)
-        # fused step
-        K.oscar_decode_step(sh, c1.layer, c1.cache, kd, vd, d[:4], q, *dt[1][:2], dt[1][2], outs[1], ws[1],
-                            si, 1)
-        # fused step, tables from host memory (the array is overwritten right
-        # after the call: the launch arguments hold their own copy)
-        host_tab = bufs[2].copy()
-        K.oscar_decode_step_host_tables(sh, caches[2].layer, caches[2].cache, kd, vd, host_tab[:4], q, *dt[2][:2],
-                                        host_tab[4], outs[2], ws[2], si, 1)
-        host_tab[:] = -7
+        # both launch forms, alternating by step (the three calls of one step
+        # take the same form)
+        with _decode_form(FORMS[st % 2][0]):
+            # separate calls
+            if res[0][0]:
+                K.oscar_requant_from_bf16(sh, c0.layer, c0.cache, d[2], d[3], n=B)
+            if np.any(bufs[0][0] >= 0):
+                K.oscar_quant_write(sh, c0.layer, c0.cache, kd, vd, d[0], n=B)
+            if np.any(bufs[0][1] >= 0):
+                K.oscar_bf16_write(sh, c0.cache, kd, vd, d[1], n=B)
+            K.oscar_decode_attn(sh, c0.layer, c0.cache, q, *dt[0][:2], dt[0][2], outs[0], ws[0], si, 1)
+            # fused step
+            K.oscar_decode_step(sh, c1.layer, c1.cache, kd, vd, d[:4], q, *dt[1][:2], dt[1][2], outs[1], ws[1],
+                                si, 1)
+            # fused step, tables from host memory (the array is overwritten right
+            # after the call: the launch arguments hold their own copy)
+            host_tab = bufs[2].copy()
+            K.oscar_decode_step_host_tables(sh, caches[2].layer, caches[2].cache, kd, vd, host_tab[:4], q, *dt[2][:2],
+                                            host_tab[4], outs[2], ws[2], si, 1)
+            host_tab[:] = -7
         torch.cuda.synchronize()
         assert torch.equal(outs[0], outs[1]), f"step {st}: outputs differ"
         assert torch.equal(outs[1], outs[2]), f"step {st}: host-table step differs"

@@ -148,6 +148,30 @@ def test_workspace_bytes_monotone(lib):
     assert K.oscar_decode_auto_splits(mid, 64, 2100) == 12
 
 
+def test_auto_splits_fit_the_small_grid_form(lib):
+    """With the small-grid form allowed (mode 0 or 2) and one-wavefront items,
+    the automatic count fits the INT2 items and four bf16 splits into two
+    wavefronts per SIMD (2048 on 256 compute units) when that leaves at least
+    24 splits; with the form off (mode 1) it is the two-round count."""
+    sh = K.make_shape(n_q_heads=32, n_kv_heads=8, group=32, sink=4, recent=128)
+    prev = K.oscar_decode_set_small_grid(0)
+    try:
+        for mode in (0, 2):
+            K.oscar_decode_set_small_grid(mode)
+            assert K.oscar_decode_auto_splits(sh, 1, 2048) == 128    # 8 x 132 = 1056 wavefronts fit
+            assert K.oscar_decode_auto_splits(sh, 2, 2048) == 124    # 16 x (124 + 4) = 2048
+            assert K.oscar_decode_auto_splits(sh, 4, 2048) == 60
+            assert K.oscar_decode_auto_splits(sh, 8, 2048) == 28
+            assert K.oscar_decode_auto_splits(sh, 9, 2048) == 24     # 2048 // 72 - 4
+            assert K.oscar_decode_auto_splits(sh, 10, 2048) == 102   # 21 would be too few: two rounds
+            assert K.oscar_decode_auto_splits(sh, 28, 6300) == 36
+        K.oscar_decode_set_small_grid(1)
+        assert K.oscar_decode_auto_splits(sh, 2, 2048) == 128
+        assert K.oscar_decode_auto_splits(sh, 8, 2048) == 128
+    finally:
+        K.oscar_decode_set_small_grid(prev)
+
+
 # ---------------------------------------------------------------------------
 # calibration vs oracle
 # ---------------------------------------------------------------------------
@@ -299,6 +323,21 @@ def test_prefill_auto_splits_fill_the_last_round(lib):
     assert K.oscar_prefill_auto_splits(sh, 0, 100, 128) == 1
     sh64 = K.make_shape(n_q_heads=32, n_kv_heads=8, group=64, sink=4, recent=128)
     assert K.oscar_prefill_auto_splits(sh64, 28, 6300, 128) == 9
+
+
+def test_decode_form_setter(lib):
+    """oscar_decode_set_small_grid: returns the previous mode, rejects modes
+    outside 0..2 with -1 and leaves the mode unchanged."""
+    prev = K.oscar_decode_set_small_grid(2)
+    try:
+        assert prev in (0, 1, 2)
+        assert K.oscar_decode_set_small_grid(1) == 2
+        assert K.oscar_decode_set_small_grid(3) == -1
+        assert K.oscar_decode_set_small_grid(-1) == -1
+        assert K.oscar_decode_set_small_grid(0) == 1
+        assert K.oscar_decode_set_small_grid(0) == 0
+    finally:
+        K.oscar_decode_set_small_grid(prev)
 
 
 def test_prefill_argument_checks(lib):
