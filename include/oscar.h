@@ -393,12 +393,13 @@ oscar_status oscar_decode_step_host_tables(const oscar_shape* shape, const oscar
  * calling thread records a pair of HIP events on its stream around the main
  * decode kernel (not the prologue or the combine).  oscar_profile_read waits
  * for the recorded events, returns the summed milliseconds and the launch
- * count, and clears them. */
+ * count, and clears the record (disabling first keeps it readable).  The
+ * event pairs are created once per thread and reused after each read. */
 oscar_status oscar_profile_enable(int32_t on);
 oscar_status oscar_profile_read(double* main_ms, int64_t* launches);
 /* The same, and the first cap launches' durations in milliseconds, in launch
  * order, into the host array ms_each (cap >= 0; ms_each may be NULL when cap
- * is 0).  All recorded events are released even if timing one fails
+ * is 0).  The record is cleared even if timing one launch fails
  * (OSCAR_EHIP). */
 oscar_status oscar_profile_read_each(float* ms_each, int64_t cap, double* main_ms, int64_t* launches);
 

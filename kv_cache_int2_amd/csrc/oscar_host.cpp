@@ -12,6 +12,7 @@
 #include <limits>
 #include <string>
 #include <thread>
+#include <tuple>
 #include <vector>
 
 #include "oscar.h"
@@ -23,9 +24,27 @@ namespace {
 
 thread_local std::string g_err;
 
+// Event pairs around the main kernel of each launch while profiling is on.
+// They are created once and reused after each read (an event created per
+// launch cost the host several microseconds a step, which at one request
+// shows in the step time), and live as long as the thread.
 struct ProfileState {
   bool on = false;
-  std::vector<std::pair<hipEvent_t, hipEvent_t>> events;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> pool;
+  size_t used = 0;  // pool[0, used): recorded since the last read
+  // the next pair (nullptr, nullptr after an error)
+  std::pair<hipEvent_t, hipEvent_t> acquire() {
+    if (used == pool.size()) {
+      hipEvent_t a = nullptr, b = nullptr;
+      if (hipEventCreate(&a) != hipSuccess) return {nullptr, nullptr};
+      if (hipEventCreate(&b) != hipSuccess) {
+        (void)hipEventDestroy(a);
+        return {nullptr, nullptr};
+      }
+      pool.emplace_back(a, b);
+    }
+    return pool[used++];
+  }
 };
 thread_local ProfileState g_prof;
 
@@ -976,9 +995,8 @@ static oscar_status decode_common(const oscar_shape* shape, const oscar_layer* l
   }
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
   if (g_prof.on && !ws.use_scratch) {
-    if (hipEventCreate(&ev0) != hipSuccess || hipEventCreate(&ev1) != hipSuccess)
-      return fail(OSCAR_EHIP, "hipEventCreate failed");
-    g_prof.events.emplace_back(ev0, ev1);
+    std::tie(ev0, ev1) = g_prof.acquire();
+    if (!ev0) return fail(OSCAR_EHIP, "hipEventCreate failed");
   }
   return hip_status(launch_decode(p, (hipStream_t)stream, ev0, ev1, p.arg_tables ? &tabs : nullptr), "decode launch");
 }
@@ -1151,9 +1169,8 @@ oscar_status oscar_prefill_attn(const oscar_shape* shape, const oscar_layer* lay
     p.out = out;
     hipEvent_t ev0 = nullptr, ev1 = nullptr;
     if (g_prof.on) {
-      if (hipEventCreate(&ev0) != hipSuccess || hipEventCreate(&ev1) != hipSuccess)
-        return fail(OSCAR_EHIP, "hipEventCreate failed");
-      g_prof.events.emplace_back(ev0, ev1);
+      std::tie(ev0, ev1) = g_prof.acquire();
+      if (!ev0) return fail(OSCAR_EHIP, "hipEventCreate failed");
     }
     if ((st = hip_status(launch_prefill(p, (hipStream_t)stream, ev0, ev1), "prefill launch"))) return st;
   }
@@ -1161,7 +1178,7 @@ oscar_status oscar_prefill_attn(const oscar_shape* shape, const oscar_layer* lay
 }
 
 oscar_status oscar_profile_enable(int32_t on) {
-  g_prof.on = on != 0;
+  g_prof.on = on != 0;  // launches recorded so far stay readable
   return ok();
 }
 
@@ -1170,7 +1187,8 @@ oscar_status oscar_profile_read_each(float* ms_each, int64_t cap, double* main_m
   double total = 0.0;
   int64_t i = 0;
   oscar_status st = OSCAR_OK;
-  for (auto& pr : g_prof.events) {
+  for (size_t k = 0; k < g_prof.used; ++k) {
+    const auto& pr = g_prof.pool[k];
     float ms = 0.f;
     if (st == OSCAR_OK &&
         (hipEventSynchronize(pr.second) != hipSuccess || hipEventElapsedTime(&ms, pr.first, pr.second) != hipSuccess))
@@ -1178,11 +1196,9 @@ oscar_status oscar_profile_read_each(float* ms_each, int64_t cap, double* main_m
     total += ms;
     if (i < cap) ms_each[i] = ms;
     ++i;
-    (void)hipEventDestroy(pr.first);
-    (void)hipEventDestroy(pr.second);
   }
-  *launches = (int64_t)g_prof.events.size();
-  g_prof.events.clear();
+  *launches = (int64_t)g_prof.used;
+  g_prof.used = 0;  // the pairs are reused by the next launches
   *main_ms = total;
   return st ? st : ok();
 }
