@@ -15,6 +15,7 @@ lengths of all requests and steps / wall time of the timed steps).
 from __future__ import annotations
 
 import argparse
+import ctypes as C
 import dataclasses
 import hashlib
 import json
@@ -367,6 +368,16 @@ def main():
     # launch arguments (oscar_decode_step_host_tables): no copy per step
     host_tables = not args.unfused and B <= 64
 
+    # the host-table step's pointer arguments, marshalled once: the binding's
+    # per-call conversions (about 4 us) would set the pace of a one-request step
+    step_fn = K.lib().oscar_decode_step_host_tables
+    step_args = {"slots": planner.buf.ctypes.data, "ctx": planner.buf.ctypes.data + 4 * planner.buf.shape[1] * 4,
+                 "head": (C.byref(sh), C.byref(dc.layer), C.byref(dc.cache)),
+                 "io": [(new_k_d[i].data_ptr(), new_v_d[i].data_ptr(), q_d[i].data_ptr()) for i in range(n_in)],
+                 "tail": (out.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(),
+                          torch.cuda.current_stream().cuda_stream),
+                 "tables": None}
+
     def step(st):
         n_age, changed = planner.step()
         if not host_tables:
@@ -384,6 +395,7 @@ def main():
             tab_ev[k] = torch.cuda.Event()
             tab_ev[k].record()
             tables[0], tables[1] = tab_dev[k]
+            step_args["tables"] = None
         d = dev_small[st]
         si_ = st % n_in
         if flush is not None:
@@ -399,8 +411,16 @@ def main():
             K.oscar_bf16_write(sh, dc.cache, new_k_d[si_], new_v_d[si_], d[1], n=B)
             K.oscar_decode_attn(sh, dc.layer, dc.cache, q_d[si_], tables[0], tables[1], d[4], out, ws, si, sb_step)
         elif host_tables:
-            K.oscar_decode_step_host_tables(sh, dc.layer, dc.cache, new_k_d[si_], new_v_d[si_], planner.buf[:4],
-                                            q_d[si_], tables[0], tables[1], planner.buf[4], out, ws, si, sb_step)
+            # oscar_decode_step_host_tables(shape, layer, cache, k_new, v_new, step_slots, q, batch, int2_bt,
+            # max_int2_pages, bf16_bt, max_bf16_pages, ctx_lens, splits_int2, splits_bf16, out, workspace,
+            # workspace_bytes, stream), as the binding's wrapper passes them
+            if step_args["tables"] is None:
+                step_args["tables"] = (tables[0].data_ptr(), tables[0].shape[1], tables[1].data_ptr(),
+                                       tables[1].shape[1])
+            kp, vp, qp = step_args["io"][si_]
+            i2p, i2n, bfp, bfn = step_args["tables"]
+            K._check(step_fn(*step_args["head"], kp, vp, step_args["slots"], qp, B, i2p, i2n, bfp, bfn,
+                             step_args["ctx"], si, sb_step, *step_args["tail"]))
         else:
             K.oscar_decode_step(sh, dc.layer, dc.cache, new_k_d[si_], new_v_d[si_], d[:4], q_d[si_], tables[0],
                                 tables[1], d[4], out, ws, si, sb_step)
@@ -430,6 +450,7 @@ def main():
     t0 = time.perf_counter()
     for st in range(args.warmup, n_steps):
         step(st)
+    t_issued = time.perf_counter()  # the host has queued every step; near t1 means the host sets the pace
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     K.oscar_profile_enable(False)
@@ -639,6 +660,7 @@ def main():
         "cpu_baseline": cpu,
         "settle": settle,
         "step_gpu_us": round(step_gpu_us, 1),
+        "host_issue_us_per_step": round((t_issued - t0) / args.steps * 1e6, 2),
         "step_gpu_us_over": "timed steps" if step_ev_range.start == args.warmup else "warm-up steps",
         "cold_flush_mb": args.cold_flush_mb,
         "interleaved_write": interleaved,

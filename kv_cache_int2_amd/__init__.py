@@ -386,12 +386,14 @@ class DecodeStepPlanner:
         self.buf = np.zeros((5, max(self.n, 1)), np.int32)   # int2, bf16, age_src, age_dst, ctx
         self.n_age = C.c_int32()
         self.changed = C.c_int32()
+        # the arguments never change (buf is reused): marshalled once
+        b = self.buf
+        self._fn = lib().oscar_plan_decode_step
+        self._args = (self.pool.handle, self.arr, self.n, b[0].ctypes.data, b[1].ctypes.data, b[2].ctypes.data,
+                      b[3].ctypes.data, C.byref(self.n_age), b[4].ctypes.data, C.byref(self.changed))
 
     def step(self):
-        b = self.buf
-        _check(lib().oscar_plan_decode_step(self.pool.handle, self.arr, self.n, b[0].ctypes.data, b[1].ctypes.data,
-                                            b[2].ctypes.data, b[3].ctypes.data, C.byref(self.n_age),
-                                            b[4].ctypes.data, C.byref(self.changed)))
+        _check(self._fn(*self._args))
         return self.n_age.value, bool(self.changed.value)
 
 

@@ -288,64 +288,70 @@ struct StepScratch {
 };
 
 template <int NG, int MB>
+// wm: the matrix this work group writes (0 K, 1 V), -1 both; the threads of
+// the other matrix (whole wavefronts) skip the arithmetic and the stores.
 __device__ __forceinline__ void quantise_and_store(const DecodeParams& p, int kv, int tok, int32_t dst,
-                                                   const float* rk, const float* rv, StepScratch& sc) {
+                                                   const float* rk, const float* rv, StepScratch& sc, int wm) {
   constexpr int G = kHeadDim / NG;
   constexpr Int2Layout L{NG, MB};
   const int t = threadIdx.x, m = t >> 7, j = t & (kHeadDim - 1);
+  const bool mine = wm < 0 || m == wm;  // uniform per wavefront
   const float* R = m ? rv : rk;  // null: V arrives rotated (R_V folded into the V projection)
   const float* x = sc.x[tok][m];
   double acc = 0.0;
-  if (R) {
+  if (mine) {
+    if (R) {
 #pragma unroll 8
-    for (int i = 0; i < kHeadDim; i += 4) {
-      const float4 x4 = *(const float4*)&x[i];
-      acc = fma((double)x4.x, (double)R[i * kHeadDim + j], acc);
-      acc = fma((double)x4.y, (double)R[(i + 1) * kHeadDim + j], acc);
-      acc = fma((double)x4.z, (double)R[(i + 2) * kHeadDim + j], acc);
-      acc = fma((double)x4.w, (double)R[(i + 3) * kHeadDim + j], acc);
+      for (int i = 0; i < kHeadDim; i += 4) {
+        const float4 x4 = *(const float4*)&x[i];
+        acc = fma((double)x4.x, (double)R[i * kHeadDim + j], acc);
+        acc = fma((double)x4.y, (double)R[(i + 1) * kHeadDim + j], acc);
+        acc = fma((double)x4.z, (double)R[(i + 2) * kHeadDim + j], acc);
+        acc = fma((double)x4.w, (double)R[(i + 3) * kHeadDim + j], acc);
+      }
+    } else {
+      acc = (double)x[j];
     }
-  } else {
-    acc = (double)x[j];
-  }
-  const double tau = m ? p.tau_v : p.tau_k;
-  const double v = acc < -tau ? -tau : (acc > tau ? tau : acc);
-  double mn = v, mx = v;
-  // the G channels of a group are consecutive lanes of one wavefront
-  group_minmax_f64<G>(mn, mx);
-  const uint64_t nan_lanes = __builtin_amdgcn_ballot_w64(v != v);
-  const bool nan = G == 64 ? nan_lanes != 0 : ((nan_lanes >> (threadIdx.x & 32)) & 0xffffffffull) != 0;
-  uint32_t pair = nan_sz<MB>();
-  uint8_t c = 0;
-  if (!nan) {
-    double sd, zd;
-    pair = encode_sz<MB>((mx - mn) / 3.0, mn, sd, zd);
-    if (sd != 0.0) {
-      double cd = __builtin_rint((v - zd) / sd);
-      cd = cd < 0.0 ? 0.0 : (cd > 3.0 ? 3.0 : cd);
-      c = (uint8_t)cd;
+    const double tau = m ? p.tau_v : p.tau_k;
+    const double v = acc < -tau ? -tau : (acc > tau ? tau : acc);
+    double mn = v, mx = v;
+    // the G channels of a group are consecutive lanes of one wavefront
+    group_minmax_f64<G>(mn, mx);
+    const uint64_t nan_lanes = __builtin_amdgcn_ballot_w64(v != v);
+    const bool nan = G == 64 ? nan_lanes != 0 : ((nan_lanes >> (threadIdx.x & 32)) & 0xffffffffull) != 0;
+    uint32_t pair = nan_sz<MB>();
+    uint8_t c = 0;
+    if (!nan) {
+      double sd, zd;
+      pair = encode_sz<MB>((mx - mn) / 3.0, mn, sd, zd);
+      if (sd != 0.0) {
+        double cd = __builtin_rint((v - zd) / sd);
+        cd = cd < 0.0 ? 0.0 : (cd > 3.0 ? 3.0 : cd);
+        c = (uint8_t)cd;
+      }
     }
+    sc.code[m][j] = c;
+    if (j % G == 0) sc.sz[m][j / G] = pair;
   }
-  sc.code[m][j] = c;
-  if (j % G == 0) sc.sz[m][j / G] = pair;
   __syncthreads();
   const int64_t page = dst / kPage;
   const int slot = dst % kPage;
   uint8_t* blk = p.int2_w + (page * p.n_kv + kv) * (int64_t)L.bytes();
-  if (t < 8) {
+  const bool do_k = wm != 1, do_v = wm != 0;
+  if (do_k && t < 8) {
     // K codes, token-major: word t is word t%2 of quarter t/2; bits 2e hold
     // field e%4 of byte e/4
     uint32_t w = 0u;
 #pragma unroll
     for (int e = 0; e < 16; ++e) w |= (uint32_t)sc.code[0][k_code_channel<NG>(t >> 1, t & 1, e >> 2, e & 3)] << (2 * e);
     *(uint32_t*)(blk + L.k_codes() + slot * 32 + 4 * t) = w;
-  } else if (t >= 16 && t < 16 + NG) {
+  } else if (do_k && t >= 16 && t < 16 + NG) {
     const int gm = t - 16;
     store_sz<MB>(blk + L.k_sz() + (slot * NG + gm) * MB, sc.sz[0][gm]);  // K: token-major
-  } else if (t >= 32 && t < 32 + NG) {
+  } else if (do_v && t >= 32 && t < 32 + NG) {
     const int gm = t - 32;
     store_sz<MB>(blk + L.v_sz() + (gm * kPage + slot) * MB, sc.sz[1][gm]);  // V: group-major
-  } else if (t >= 64 && t < 96) {
+  } else if (do_v && t >= 64 && t < 96) {
     // V codes by token quad: byte jc of quad slot/4 holds channel jc, this
     // token at bits 2 (slot % 4); the other three tokens keep their bits
     const int jd = t - 64, sh = 2 * (slot & 3);
@@ -368,10 +374,12 @@ __device__ __forceinline__ int32_t step_slot(const DecodeParams& p, const ArgTab
   return p.arg_tables ? tabs.v[r][b] : p.step_slots[r * p.batch + b];
 }
 
+// wm: as for quantise_and_store (0 K, 1 V, -1 both)
 template <int NG, int MB>
 __device__ void step_writes(const DecodeParams& p, const ArgTables& tabs, int b, int kv, const float* rk,
-                            const float* rv, StepScratch& sc) {
+                            const float* rv, StepScratch& sc, int wm) {
   const int t = threadIdx.x, m = t >> 7, j = t & (kHeadDim - 1);
+  const bool mine = wm < 0 || m == wm;
   const int32_t i2_new = step_slot(p, tabs, 0, b), bf_new = step_slot(p, tabs, 1, b);
   const int32_t age_src = step_slot(p, tabs, 2, b), age_dst = step_slot(p, tabs, 3, b);
   const bool age = age_src >= 0 && age_dst >= 0 && age_src / kPage < p.n_bf16_pages &&
@@ -386,12 +394,12 @@ __device__ void step_writes(const DecodeParams& p, const ArgTables& tabs, int b,
     const int sl = slot_id % kPage;
     return m ? blk + kPage * kHeadDim + j * kPage + sl : blk + sl * kHeadDim + j;
   };
-  if (age) sc.x[0][m][j] = bf16_val(*bf16_elem(age_src));
-  if (put_i2) sc.x[1][m][j] = bf16_val(xn);
+  if (age && mine) sc.x[0][m][j] = bf16_val(*bf16_elem(age_src));
+  if (put_i2 && mine) sc.x[1][m][j] = bf16_val(xn);
   __syncthreads();  // the leaving token has been read before its ring slot is reused
-  if (put_bf) *bf16_elem(bf_new) = xn;
-  if (age) quantise_and_store<NG, MB>(p, kv, 0, age_dst, rk, rv, sc);
-  if (put_i2) quantise_and_store<NG, MB>(p, kv, 1, i2_new, rk, rv, sc);
+  if (put_bf && mine) *bf16_elem(bf_new) = xn;
+  if (age) quantise_and_store<NG, MB>(p, kv, 0, age_dst, rk, rv, sc, wm);
+  if (put_i2) quantise_and_store<NG, MB>(p, kv, 1, i2_new, rk, rv, sc, wm);
 }
 
 // The INT2 kernel's q operands of one (request, KV head), from the fixed-point
@@ -498,10 +506,12 @@ __device__ __forceinline__ int q_scale_exponent(float mx) {
 // Words per (request, KV head): A digits of 2Q (write_q_operands gives their
 // order; 1536 words per row tile reserved), then aux floats [1 + 16*CT]: logit
 // factor 2^-sq / 2, per row 2*Qbar (float).
-// WRITE: the decode-step writes come first.  With p.split_writes, the grid is
-// twice B x Hkv: work groups [0, B Hkv) build the q operands and work groups
-// [B Hkv, 2 B Hkv) do the step's writes, side by side (for small batches,
-// where the doubled grid still runs in one round).
+// WRITE: the decode-step writes come first.  With p.split_writes = 1 the grid
+// is twice B x Hkv: work groups [0, B Hkv) build the q operands and work
+// groups [B Hkv, 2 B Hkv) do the step's writes, side by side (for small
+// batches, where the doubled grid still runs in one round); with 2 it is
+// three times B x Hkv, writer 2 bk + m doing matrix m (K, V) of pair bk and
+// staging only its own R.
 // tabs: the step tables of oscar_decode_step_host_tables (p.arg_tables); the
 // q-operand block of (b, KV head 0) then copies b's context length to ctx_w,
 // which the later kernels read as ctx_lens.
@@ -509,7 +519,9 @@ template <int NG, int MB, int CT, bool WRITE>
 __global__ __launch_bounds__(256) void decode_prologue(DecodeParams p, ArgTables tabs) {
   const int nbk = p.batch * p.n_kv;
   const bool writer = WRITE && p.split_writes && (int)blockIdx.x >= nbk;
-  const int bk = writer ? (int)blockIdx.x - nbk : (int)blockIdx.x;
+  const int wi = (int)blockIdx.x - nbk;
+  const int bk = writer ? (p.split_writes == 2 ? wi >> 1 : wi) : (int)blockIdx.x;
+  const int wm = writer && p.split_writes == 2 ? (wi & 1) : -1;  // the writer's matrix, -1: both
   const int b = bk / p.n_kv, kv = bk % p.n_kv;
   const int t = threadIdx.x, j = t & (kHeadDim - 1), hf = t >> 7;
   if (WRITE && p.arg_tables && !writer && kv == 0 && t == 0) p.ctx_w[b] = tabs.v[4][b];
@@ -521,10 +533,10 @@ __global__ __launch_bounds__(256) void decode_prologue(DecodeParams p, ArgTables
   __shared__ __attribute__((aligned(16))) StepScratch sc;
   const int g = p.g;
   if (WRITE && (!p.split_writes || writer)) {
-    if (p.r_v) stage_matrix256<kHeadDim>(p.r_v + (int64_t)kv * kHeadDim * kHeadDim, rv);
-    stage_matrix256<kHeadDim>(p.r_k + (int64_t)kv * kHeadDim * kHeadDim, rk);
+    if (p.r_v && wm != 0) stage_matrix256<kHeadDim>(p.r_v + (int64_t)kv * kHeadDim * kHeadDim, rv);
+    if (wm != 1) stage_matrix256<kHeadDim>(p.r_k + (int64_t)kv * kHeadDim * kHeadDim, rk);
     __syncthreads();
-    step_writes<NG, MB>(p, tabs, b, kv, rk, p.r_v ? rv : nullptr, sc);
+    step_writes<NG, MB>(p, tabs, b, kv, rk, p.r_v ? rv : nullptr, sc, wm);
     if (writer) return;  // uniform per work group
   } else {
     stage_matrix256<kHeadDim>(p.r_k + (int64_t)kv * kHeadDim * kHeadDim, rk);
@@ -2163,7 +2175,7 @@ hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream, hipEvent_t
   hipError_t e = hipSuccess;
   if (int2) {
     if (p.has_step)
-      hipLaunchKernelGGL((decode_prologue<NG, MB, CT * W, true>), dim3(p.split_writes ? 2 * bkn : bkn), dim3(256), 0,
+      hipLaunchKernelGGL((decode_prologue<NG, MB, CT * W, true>), dim3((1 + p.split_writes) * bkn), dim3(256), 0,
                          stream, p, tabs);
     else
       hipLaunchKernelGGL((decode_prologue<NG, MB, CT * W, false>), dim3(bkn), dim3(256), 0, stream, p, tabs);

@@ -990,8 +990,10 @@ static oscar_status decode_common(const oscar_shape* shape, const oscar_layer* l
     p.tau_v = layer->tau_v;
     // The prologue holds R_K and R_V in LDS (one work group per compute unit):
     // when twice the (request, KV head) count still fits one round, the writes
-    // take work groups of their own beside the q operands.
-    p.split_writes = 2 * (int64_t)p.batch * p.n_kv <= device_cus() ? 1 : 0;
+    // take work groups of their own beside the q operands; when three times
+    // does, one per matrix (K, V), each staging only its own R.
+    const int64_t pairs = (int64_t)p.batch * p.n_kv;
+    p.split_writes = 3 * pairs <= device_cus() ? 2 : (2 * pairs <= device_cus() ? 1 : 0);
   }
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
   if (g_prof.on && !ws.use_scratch) {

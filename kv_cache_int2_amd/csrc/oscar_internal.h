@@ -104,7 +104,7 @@ struct DecodeParams {
   const uint16_t* v_new;
   uint8_t* int2_w;            // writable views of the two storages
   uint8_t* bf16_w;
-  int split_writes;           // the writes in work groups of their own (small batches)
+  int split_writes;           // the writes in work groups of their own (small batches): 1 per pair, 2 per matrix
   double tau_k, tau_v;
   int has_step;               // the step's writes run (step_slots, or the argument tables)
   // oscar_decode_step_host_tables: the step's [4][B] slots and ctx_lens, given

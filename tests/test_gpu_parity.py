@@ -475,10 +475,14 @@ def test_full_size_stress_16x128k_sampled(group):
     _full_size_sampled(w, group, (w.batch - 1,))
 
 
-@pytest.mark.parametrize("hq,hkv,group,sink,recent,scale_bits", [(8, 2, 32, 4, 32, 16), (12, 1, 64, 20, 48, 16),
-                                                                   (4, 1, 32, 4, 0, 16), (4, 2, 64, 64, 48, 8),
-                                                                   (16, 1, 32, 0, 16, 16), (4, 1, 64, 0, 0, 8)])
-def test_fused_decode_step(hq, hkv, group, sink, recent, scale_bits):
+@pytest.mark.parametrize("hq,hkv,group,sink,recent,scale_bits,reps", [
+    (8, 2, 32, 4, 32, 16, 1), (12, 1, 64, 20, 48, 16, 1), (4, 1, 32, 4, 0, 16, 1), (4, 2, 64, 64, 48, 8, 1),
+    (16, 1, 32, 0, 16, 16, 1), (4, 1, 64, 0, 0, 8, 1),
+    # 8 KV heads x 15 and 25 requests: the prologue's step writes in one work
+    # group per (request, KV head) (120 pairs) and inside the q-operand work
+    # groups (200 pairs); the cases above run one writer per K and V matrix
+    (32, 8, 32, 4, 32, 16, 3), (32, 8, 32, 4, 32, 16, 5)])
+def test_fused_decode_step(hq, hkv, group, sink, recent, scale_bits, reps):
     """oscar_decode_step (writes fused into the decode's prologue kernel) against
     the separate write calls + oscar_decode_attn: identical cache bytes and bit-identical outputs after every step,
     through ring age-out, page crossings, sink growth and (recent = 0) new
@@ -490,13 +494,14 @@ def test_fused_decode_step(hq, hkv, group, sink, recent, scale_bits):
     from kv_cache_int2_amd.torch_cache import to_dev_bits, to_dev_i32
     w = synth.Workload("fused", 70 + hq + group, hq, hkv, 128, 1, 0, group=group, sink=sink, recent=recent,
                        outlier_scale=(40.0, 40.0), calib_tokens=512)
-    _flush(f"case fused step hq={hq} hkv={hkv} G={group} sink={sink} recent={recent} scale_bits={scale_bits}")
+    _flush(f"case fused step hq={hq} hkv={hkv} G={group} sink={sink} recent={recent} scale_bits={scale_bits} "
+           f"batch={5 * reps}")
     cal = _calibrate(w)
     sh = K.make_shape(n_q_heads=hq, n_kv_heads=hkv, group=group, sink=sink, recent=recent, scale_bits=scale_bits)
-    lens0 = [0, 3, max(sink + recent - 2, 1), 200, 1001]
-    n_steps = 40
+    lens0 = [0, 3, max(sink + recent - 2, 1), 200, 1001] * reps
+    n_steps = 40 if reps == 1 else 20
     B = len(lens0)
-    caches = [DeviceCache(sh, cal.r_k, cal.r_v, cal.tau_k, cal.tau_v, 600, 64) for _ in range(3)]
+    caches = [DeviceCache(sh, cal.r_k, cal.r_v, cal.tau_k, cal.tau_v, 600 * reps, 64 * reps) for _ in range(3)]
     seqs = [[], [], []]
     for r, t in enumerate(lens0):
         kb, vb = synth.kv_request_bf16(w, r, 0, t)
