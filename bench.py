@@ -663,7 +663,10 @@ def main():
                      "algorithmic_bytes_per_launch": int(alg),
                      "algorithmic_bytes_unique_per_launch": int(alg_unique),
                      "frac_unique": round(alg_unique / (main_avg_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                     "algorithmic_bytes_per_step": int(alg_step)},
+                     "algorithmic_bytes_per_step": int(alg_step),
+                     # the KV tokens of a step over this kernel's own time (value counts the
+                     # whole step: the prologue with its writes, the combine, the boundaries)
+                     "kernel_kv_tokens_per_s": tokens / args.steps / (main_avg_ms * 1e-3)},
         "cpu_baseline": cpu,
         "settle": settle,
         "step_gpu_us": round(step_gpu_us, 1),
