@@ -55,6 +55,7 @@ def parse():
                     help="pages: the pages' default layout (sink 64, recent 256, G = 64, FP8 scale and zero)")
     ap.add_argument("--splits", type=int, default=0, help="INT2 splits per (request, KV head); 0 = auto")
     ap.add_argument("--batch", type=int, default=0, help="override the workload's batch (requests)")
+    ap.add_argument("--context", type=int, default=0, help="override the workload's context length (tokens)")
     ap.add_argument("--decode-form", choices=["auto", "standard", "small"], default="auto",
                     help="decode launch form (oscar_decode_set_small_grid): auto, standard (one combine work "
                          "group per (request, KV head)), small (bf16 splits inside the INT2 kernel's grid, one "
@@ -227,6 +228,8 @@ def main():
         scale_bits = 8
     if args.batch:
         w = dataclasses.replace(w, batch=args.batch)
+    if args.context:
+        w = dataclasses.replace(w, context=args.context)
     K.oscar_decode_set_small_grid({"auto": 0, "standard": 1, "small": 2}[args.decode_form])
     group = args.group or w.group
     mb = 4 if scale_bits == 16 else 2
