@@ -251,7 +251,8 @@ oscar_status oscar_copy_pages(const oscar_shape* shape, const oscar_cache* cache
  * splits_int2 / splits_bf16: work items per (request, KV head) for the INT2 and
  * bf16 regions (0 = choose; up to four bf16 splits run inside the merging
  * kernel, one per wavefront).  workspace: device, >= oscar_decode_workspace_bytes
- * with the same arguments, 256-byte aligned.  T = 0 gives a zero row. */
+ * with the same arguments (for 0 it sizes the most the automatic count can take
+ * in the current small-grid mode), 256-byte aligned.  T = 0 gives a zero row. */
 size_t oscar_decode_workspace_bytes(const oscar_shape* shape, int32_t batch, int32_t splits_int2,
                                     int32_t splits_bf16);
 oscar_status oscar_decode_attn(const oscar_shape* shape, const oscar_layer* layer, const oscar_cache* cache,
@@ -314,9 +315,9 @@ oscar_status oscar_prefill_attn(const oscar_shape* shape, const oscar_layer* lay
  * rounds of the wavefronts the device runs at once, at most 128 and at least
  * 16 pages per split (deterministic for a given device and small-grid mode).
  * Where the small-grid form applies (oscar_decode_set_small_grid not 1, one
- * wavefront per work item), the count is lowered to the one whose INT2 items
- * and four bf16 splits fit two wavefronts per SIMD, if that leaves at least 24
- * splits. */
+ * wavefront per work item) and the count whose INT2 items and four bf16 splits
+ * fit two wavefronts per SIMD is at least 24, the count is that fit at most,
+ * and the whole fit (past 128) when each of its splits keeps 24 pages. */
 int32_t oscar_decode_auto_splits(const oscar_shape* shape, int32_t batch, int32_t max_int2_pages);
 
 /* Form of the decode launches ([IT] 2.2.B split-K decode with a log-sum-exp

@@ -823,6 +823,12 @@ static int64_t small_grid_waves() { return 8 * (int64_t)device_cus(); }
 // 8 KV heads: 8 requests at 28 splits 64.5 against 72.5 us a step in the
 // standard form at 128; 16 requests at 12 splits 115.5 against 103.8 at 64)
 static const int kSmallGridMinSplits = 24;
+// Long requests take the whole fit (every SIMD two wavefronts) when each of
+// its splits keeps this many pages (one request of 100K tokens, 8 KV heads:
+// 252 splits of 24.8 pages, 39.0 against 42.5 us a step at 128).  A count
+// between the two leaves some SIMDs one wavefront and others two, and the
+// latter end the launch (64K tokens: 170 splits 36.1 against 35.3 us at 128).
+static const int kSmallGridPagesPerSplit = 24;
 
 // Automatic split count for a decode with sb bf16 splits (sb < 0: the
 // all-bf16 baseline, whose splits never take the small-grid form).
@@ -847,12 +853,27 @@ static int32_t decode_auto_splits(const oscar_shape* shape, int32_t batch, int32
   // count that fits the small-grid form's two wavefronts per SIMD, when that
   // leaves at least kSmallGridMinSplits (2, 4 and 8 requests of 32K tokens at
   // 8 KV heads: 124, 60 and 28 splits, 11-15 % shorter steps than the standard
-  // form at 128)
+  // form at 128); long requests take the whole fit, past 128, when each of its
+  // splits keeps kSmallGridPagesPerSplit pages
   if (sb >= 0 && g_small_grid_mode.load() != 1 && ts.w == 1) {
     const int64_t fit = small_grid_waves() / pairs - sb;
-    if (fit >= kSmallGridMinSplits) s = std::min(s, fit);
+    if (fit >= kSmallGridMinSplits) {
+      s = std::min(s, fit);
+      if (max_int2_pages / fit >= kSmallGridPagesPerSplit) s = fit;
+    }
   }
   return (int32_t)s;
+}
+
+// The most INT2 splits the automatic count can take for this batch (at least
+// one bf16 split beside them).
+static int64_t decode_auto_splits_max(const oscar_shape* shape, int32_t batch) {
+  int64_t m = kAutoMaxSplitsDecode;
+  if (check_shape(shape) == OSCAR_OK && g_small_grid_mode.load() != 1 && tile_split(ct_of(shape)).w == 1) {
+    const int64_t pairs = (int64_t)std::max<int32_t>(batch, 1) * shape->n_kv_heads;
+    m = std::max<int64_t>(m, small_grid_waves() / pairs - 1);
+  }
+  return m;
 }
 
 int32_t oscar_decode_auto_splits(const oscar_shape* shape, int32_t batch, int32_t max_int2_pages) {
@@ -862,9 +883,9 @@ int32_t oscar_decode_auto_splits(const oscar_shape* shape, int32_t batch, int32_
 size_t oscar_decode_workspace_bytes(const oscar_shape* shape, int32_t batch, int32_t splits_int2,
                                     int32_t splits_bf16) {
   if (check_shape(shape) != OSCAR_OK || batch < 0 || splits_int2 < 0 || splits_bf16 < 0) return 0;
-  const int si = splits_int2 == 0 ? kAutoMaxSplitsDecode : splits_int2;
+  const int64_t si = splits_int2 == 0 ? decode_auto_splits_max(shape, batch) : splits_int2;
   const int sb = splits_bf16 == 0 ? kAutoMaxSplitsDecode : splits_bf16;
-  return decode_workspace_bytes(batch, shape->n_q_heads, shape->n_kv_heads, ct_of(shape), si + sb);
+  return decode_workspace_bytes(batch, shape->n_q_heads, shape->n_kv_heads, ct_of(shape), (int)(si + sb));
 }
 
 struct StepWrites {

@@ -135,7 +135,12 @@ def test_workspace_bytes_monotone(lib):
     assert 1 <= s <= 128
     assert K.oscar_decode_auto_splits(sh, 1, 64) == 4          # at least 16 pages per split
     assert K.oscar_decode_auto_splits(sh, 1, 2048) == 128      # one 32K-token request: 128 splits
-    assert K.oscar_decode_auto_splits(sh, 1, 40000) == 128     # capped
+    assert K.oscar_decode_auto_splits(sh, 1, 40000) == 252     # the small-grid form's fit for 8 pairs
+    prev = K.oscar_decode_set_small_grid(1)
+    try:
+        assert K.oscar_decode_auto_splits(sh, 1, 40000) == 128  # capped in the standard form
+    finally:
+        K.oscar_decode_set_small_grid(prev)
     assert K.oscar_decode_auto_splits(sh, 28, 6300) == 36      # 2 rounds of 4096 wavefronts over 224 (request, head)
     assert K.oscar_decode_auto_splits(sh, 4096, 6300) == 1     # more than two rounds of pairs
     # 12 query heads per KV head at G = 32: three tiles padded to four, one wide wavefront per
@@ -165,9 +170,16 @@ def test_auto_splits_fit_the_small_grid_form(lib):
             assert K.oscar_decode_auto_splits(sh, 9, 2048) == 24     # 2048 // 72 - 4
             assert K.oscar_decode_auto_splits(sh, 10, 2048) == 102   # 21 would be too few: two rounds
             assert K.oscar_decode_auto_splits(sh, 28, 6300) == 36
+            # long requests: the whole fit (2048 // 8 - 4) when each of its splits keeps 24 pages
+            assert K.oscar_decode_auto_splits(sh, 1, 6250) == 252    # 100K tokens: 24.8 pages a split
+            assert K.oscar_decode_auto_splits(sh, 1, 4096) == 128    # 64K tokens: 16.3 at the fit
+            assert K.oscar_decode_auto_splits(sh, 2, 6250) == 124    # the fit
+            # the workspace for splits 0 covers the largest automatic count (8 pairs: 2048 // 8 - 1)
+            assert K.oscar_decode_workspace_bytes(sh, 1, 0, 4) >= K.oscar_decode_workspace_bytes(sh, 1, 255, 4)
         K.oscar_decode_set_small_grid(1)
         assert K.oscar_decode_auto_splits(sh, 2, 2048) == 128
         assert K.oscar_decode_auto_splits(sh, 8, 2048) == 128
+        assert K.oscar_decode_auto_splits(sh, 1, 6250) == 128
     finally:
         K.oscar_decode_set_small_grid(prev)
 
