@@ -105,6 +105,10 @@ typedef struct oscar_layer {
   float tau_v;         /* Both finite and >= 0, and at most 65504 with fp16 scale and
                           zero (so that neither can overflow); calls taking a layer
                           return OSCAR_EINVAL otherwise. */
+  const void* r_prep;  /* NULL, or device memory written by oscar_layer_prepare for
+                          this r_k / r_v (256-byte aligned): the write calls then
+                          load R's integer digits instead of deriving them in every
+                          work group.  Prepare again after changing r_k or r_v. */
 } oscar_layer;
 
 /* Device storage of one layer (caller-owned; 256-byte aligned). */
@@ -225,6 +229,17 @@ oscar_status oscar_quant_write(const oscar_shape* shape, const oscar_layer* laye
 oscar_status oscar_requant_from_bf16(const oscar_shape* shape, const oscar_layer* layer,
                                      const oscar_cache* cache, const int32_t* src_bf16_slots,
                                      const int32_t* dst_int2_slots, int64_t n, void* stream);
+
+/* R's integer digits for the write calls, prepared once per layer ([IT] 2.2.A:
+ * R is fixed offline, so what the write path derives from it is too).  prep:
+ * device, >= oscar_layer_prep_bytes(shape) bytes, 256-byte aligned, written on
+ * `stream` (r_k / r_v of `layer`, NULL r_v meaning the identity); its contents
+ * are the same as each write work group would derive.  Set layer->r_prep to it
+ * for the write calls that follow on that stream.  OSCAR_EINVAL on a bad shape
+ * or layer, a NULL, misaligned or short prep, before anything is enqueued. */
+size_t oscar_layer_prep_bytes(const oscar_shape* shape);
+oscar_status oscar_layer_prepare(const oscar_shape* shape, const oscar_layer* layer, void* prep, size_t prep_bytes,
+                                 void* stream);
 
 /* Copy bf16 K/V (unrotated) of tokens with bf16_slots[i] >= 0 into bf16 blocks
  * (sink and recent tokens).  k_bf16, v_bf16: device [n][n_kv_heads][d]. */

@@ -34,7 +34,8 @@ class Shape(C.Structure):
 
 
 class Layer(C.Structure):
-    _fields_ = [("r_k", C.c_void_p), ("r_v", C.c_void_p), ("tau_k", C.c_float), ("tau_v", C.c_float)]
+    _fields_ = [("r_k", C.c_void_p), ("r_v", C.c_void_p), ("tau_k", C.c_float), ("tau_v", C.c_float),
+                ("r_prep", C.c_void_p)]
 
 
 class Cache(C.Structure):
@@ -89,6 +90,8 @@ _SIGS = {
     "oscar_decode_attn_bf16_baseline": (C.c_int32, [C.POINTER(Shape), C.POINTER(Cache), P, C.c_int32, P,
                                                     C.c_int32, P, C.c_int32, P, P, C.c_size_t, P]),
     "oscar_decode_auto_splits": (C.c_int32, [C.POINTER(Shape), C.c_int32, C.c_int32]),
+    "oscar_layer_prep_bytes": (C.c_size_t, [C.POINTER(Shape)]),
+    "oscar_layer_prepare": (C.c_int32, [C.POINTER(Shape), C.POINTER(Layer), P, C.c_size_t, P]),
     "oscar_decode_set_small_grid": (C.c_int32, [C.c_int32]),
     "oscar_prefill_auto_splits": (C.c_int32, [C.POINTER(Shape), C.c_int32, C.c_int32, C.c_int32]),
     "oscar_plan_decode_step": (C.c_int32, [P, P, C.c_int32, P, P, P, P, P, P, P]),
@@ -141,9 +144,20 @@ def make_shape(head_dim=128, n_q_heads=1, n_kv_heads=1, group=32, sink=4, recent
     return Shape(head_dim, n_q_heads, n_kv_heads, group, sink, recent, page_size, scale_bits)
 
 
-def make_layer(r_k, r_v, tau_k, tau_v) -> Layer:
-    """r_k, r_v: device fp32 tensors [n_kv, d, d] (kept alive by the caller)."""
-    return Layer(_ptr(r_k), _ptr(r_v), float(tau_k), float(tau_v))
+def make_layer(r_k, r_v, tau_k, tau_v, r_prep=None) -> Layer:
+    """r_k, r_v: device fp32 tensors [n_kv, d, d]; r_prep: the prepared digits
+    (oscar_layer_prepare) or None (all kept alive by the caller)."""
+    return Layer(_ptr(r_k), _ptr(r_v), float(tau_k), float(tau_v), _ptr(r_prep))
+
+
+def oscar_layer_prep_bytes(shape) -> int:
+    return int(lib().oscar_layer_prep_bytes(C.byref(shape)))
+
+
+def oscar_layer_prepare(shape, layer, prep, stream=None):
+    """prep: device uint8 tensor of at least oscar_layer_prep_bytes(shape) bytes."""
+    _check(lib().oscar_layer_prepare(C.byref(shape), C.byref(layer), _ptr(prep), prep.numel() * prep.element_size(),
+                                     _stream(stream)))
 
 
 def make_cache(int2_pages=None, n_int2_pages=0, bf16_pages=None, n_bf16_pages=0) -> Cache:

@@ -696,6 +696,7 @@ static oscar_status check_layer(const oscar_layer* l, const oscar_shape* shape) 
   if (!l || !l->r_k) return fail(OSCAR_EINVAL, "layer rotation R_K missing");
   if (!aligned(l->r_k, 16) || (l->r_v && !aligned(l->r_v, 16)))
     return fail(OSCAR_EINVAL, "rotations must be 16-byte aligned");
+  if (l->r_prep && !aligned(l->r_prep, 256)) return fail(OSCAR_EINVAL, "prepared digits must be 256-byte aligned");
   if (!std::isfinite(l->tau_k) || !std::isfinite(l->tau_v) || l->tau_k < 0 || l->tau_v < 0)
     return fail(OSCAR_EINVAL, "clip thresholds must be finite and >= 0");
   if (mb_of(shape) == 4 && (l->tau_k > 65504.f || l->tau_v > 65504.f))
@@ -728,7 +729,25 @@ oscar_status oscar_quant_write(const oscar_shape* shape, const oscar_layer* laye
   p.n_kv = shape->n_kv_heads;
   p.group = shape->group;
   p.mb = mb_of(shape);
+  p.r_prep = (const uint8_t*)layer->r_prep;
   return hip_status(launch_quant_write(p, 0, (hipStream_t)stream), "quant_write launch");
+}
+
+size_t oscar_layer_prep_bytes(const oscar_shape* shape) {
+  if (check_shape(shape) != OSCAR_OK) return 0;
+  return (size_t)shape->n_kv_heads * 2 * kRPrepBytes;
+}
+
+oscar_status oscar_layer_prepare(const oscar_shape* shape, const oscar_layer* layer, void* prep, size_t prep_bytes,
+                                 void* stream) {
+  oscar_status st = check_shape(shape);
+  if (st) return st;
+  if ((st = check_layer(layer, shape))) return st;
+  if (!prep || !aligned(prep, 256)) return fail(OSCAR_EINVAL, "prep must be a 256-byte aligned device buffer");
+  if (prep_bytes < oscar_layer_prep_bytes(shape))
+    return fail(OSCAR_EINVAL, "prep %zu bytes < %zu needed", prep_bytes, oscar_layer_prep_bytes(shape));
+  return hip_status(launch_prepare_r(layer->r_k, layer->r_v, shape->n_kv_heads, (uint8_t*)prep, (hipStream_t)stream),
+                    "prepare launch");
 }
 
 oscar_status oscar_requant_from_bf16(const oscar_shape* shape, const oscar_layer* layer, const oscar_cache* cache,
@@ -755,6 +774,7 @@ oscar_status oscar_requant_from_bf16(const oscar_shape* shape, const oscar_layer
   p.n_kv = shape->n_kv_heads;
   p.group = shape->group;
   p.mb = mb_of(shape);
+  p.r_prep = (const uint8_t*)layer->r_prep;
   return hip_status(launch_quant_write(p, 1, (hipStream_t)stream), "requant launch");
 }
 

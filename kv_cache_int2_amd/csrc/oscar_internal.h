@@ -52,7 +52,16 @@ struct QuantParams {
   int n_kv;
   int group;
   int mb;                     // bytes of a (scale, zero) pair: 4 or 2
+  const uint8_t* r_prep;      // R's digits prepared per matrix (oscar_layer_prepare), or null
 };
+
+// R's digits prepared for the write kernel, per (KV head, K or V) matrix: the
+// four base-256 digits as MFMA A operands (4 wavefronts x 64 lanes x 16
+// u32x4), the residual digit (4 x 64 x 4 u32x4), the bound's five words,
+// padded to 256 bytes.
+constexpr size_t kRPrepRaBytes = size_t(4) * 2 * 2 * 4 * 64 * 16;
+constexpr size_t kRPrepLoBytes = size_t(4) * 2 * 2 * 64 * 16;
+constexpr size_t kRPrepBytes = kRPrepRaBytes + kRPrepLoBytes + 256;
 
 // Step tables carried in the prologue's launch arguments: rows 0-3 the step's
 // slots, row 4 the context lengths, each of kArgBatch entries.
@@ -137,6 +146,8 @@ inline TileSplit tile_split(int tiles) {
 inline int waves_per_simd(int ct) { return ct == 1 ? 4 : (ct == 2 ? 3 : 2); }
 
 hipError_t launch_quant_write(const QuantParams& p, int mode, hipStream_t stream);
+// R's digits for every (KV head, K or V) matrix into prep (n_kv 2 kRPrepBytes)
+hipError_t launch_prepare_r(const float* r_k, const float* r_v, int n_kv, uint8_t* prep, hipStream_t stream);
 hipError_t launch_bf16_write(const uint16_t* k, const uint16_t* v, const int32_t* slots, int64_t n, int n_kv,
                              uint8_t* bf16_pages, int64_t n_pages, hipStream_t stream);
 hipError_t launch_copy_pages(uint8_t* base, int64_t block_bytes_all_heads, int64_t n_pages, const int32_t* src,

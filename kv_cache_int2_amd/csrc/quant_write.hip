@@ -531,38 +531,25 @@ __global__ __launch_bounds__(kThreads) void quant_write_direct(QuantParams p) {
       X(2, 2, 3) X(3, 1, 3) X(2, 3, 4) X(3, 2, 4) X(3, 3, 5)
 // the residual digit of R against the top X digit: weight 2^24 2^-38 = 256^2 2^-30, class 1
 
-template <int MODE, int NG, int MB>
-__global__ __launch_bounds__(kThreads, 2) void quant_write_kernel(QuantParams p, int tiles_per_wg) {
-  extern __shared__ __align__(16) uint8_t smem_raw[];
-  Smem& S = *reinterpret_cast<Smem*>(smem_raw);
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int kv = blockIdx.y;
-  const int isv = blockIdx.z;
-  const int64_t n_tiles = (p.n + kTok - 1) / kTok;
-  const int64_t tile0 = (int64_t)blockIdx.x * tiles_per_wg;
-  const int64_t tile1 = tile0 + tiles_per_wg < n_tiles ? tile0 + tiles_per_wg : n_tiles;
-  if (tile0 >= tile1) return;
-  const int count = (int)(tile1 - tile0);  // <= kMaxTilesPerWg
-  const float* Rm = isv ? p.r_v : p.r_k;  // null: V arrives rotated (R_V folded into its projection)
-  const float* R = Rm ? Rm + (int64_t)kv * kHeadDim * kHeadDim : nullptr;
-  const double tau = isv ? p.tau_v : p.tau_k;
+// ---- R's integer digits (A operands of the digit MFMAs) ----
+// Lane l of wavefront w holds output channel 16(2w + s) + l%16; its 16 bytes
+// of K half h are input channels 64h + 16(l/16) + 0..15 (the x digits use the
+// same map).  Y = rint(R 2^30) as four balanced base-256 digits (ra[s][h][b],
+// b = 0 the lowest), the residual lo = rint((R - Y 2^-30) 2^38) as one more
+// digit (rlo[s][h]), and per lane the column terms of the error bound.  R
+// null: the identity (V arriving rotated).
+struct RBoundPart {
+  float d1[2], d2[2], l1[2], rmax;
+  bool bad;  // an entry non-finite or outside [-1.5, 1.5]
+};
+
+// store_lo(s, h, k4, word): the residual digits of four input channels, as
+// soon as they are formed (the write kernel puts them straight into LDS).
+template <class StoreLo>
+__device__ __forceinline__ void r_digits(const float* R, int lane, int wave, u32x4 (&ra)[2][2][4], StoreLo store_lo,
+                                         RBoundPart& part) {
   const int ln = lane & 15, qd = lane >> 4;
-
-  // per-thread role in the loads: token tt, channels 8cc .. 8cc+7
-  const int tt = tid >> 4, cc = tid & 15;
-  const uint16_t* src = MODE == 0 ? (isv ? p.v_src : p.k_src) : nullptr;
-  auto fetch = [&](int64_t tile) { return fetch_tile<MODE>(p, src, kv, isv, tile, tile1, tt, cc); };
-  auto dst_of = [&](const TileIn& in) { return tile_dst(p, in); };
-  TileIn nx = fetch(tile0);
-
-  // ---- set-up: this wavefront's R digits in registers (A operands) ----
-  // A lane l holds row (output channel) 16T + l%16; its 16 bytes of K half h
-  // are input channels 64h + 16(l/16) + 0..15 (the x digits use the same map).
-  if (tid < 5) (tid < 4 ? S.rbits[tid] : S.bad_r) = 0u;
-  u32x4 ra[2][2][4];  // [tile s][half h][digit b]
-  float d1[2] = {0.f, 0.f}, d2[2] = {0.f, 0.f}, l1[2] = {0.f, 0.f}, rmax = 0.f;
-  bool bad = false;
+  part = RBoundPart{{0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}, 0.f, false};
   float rv[2][2][4][4];  // R[64h + 16qd + 4k4 + e][16(2w+s) + l%16], all loads in flight together
   if (R) {
 #pragma unroll
@@ -596,16 +583,16 @@ __global__ __launch_bounds__(kThreads, 2) void quant_write_kernel(QuantParams p,
         for (int e = 0; e < 4; ++e) {
           const float r0 = rv[s][h][k4][e];
           const bool ok = __builtin_fabsf(r0) <= 1.5f;  // false for NaN and infinities
-          bad |= !ok;
+          part.bad |= !ok;
           const float r = ok ? r0 : 0.0f;
           const float ys = __builtin_rintf(r * 1073741824.0f);  // R 2^30, exact scaling
           // R - Y 2^-30 is exact in fp32 (both on a grid at most 24 bits below |R - Y 2^-30| <= 2^-31)
           const float dr = r - ys * 0x1p-30f;
           const float lf = __builtin_fminf(__builtin_fmaxf(__builtin_rintf(dr * 0x1p38f), -127.f), 127.f);
-          d1[s] += __builtin_fabsf(dr);
-          d2[s] += __builtin_fabsf(dr - lf * 0x1p-38f);
-          l1[s] += __builtin_fabsf(r);
-          rmax = __builtin_fmaxf(rmax, __builtin_fabsf(r));
+          part.d1[s] += __builtin_fabsf(dr);
+          part.d2[s] += __builtin_fabsf(dr - lf * 0x1p-38f);
+          part.l1[s] += __builtin_fabsf(r);
+          part.rmax = __builtin_fmaxf(part.rmax, __builtin_fabsf(r));
           const int y = (int)ys;  // |y| <= 1.5 2^30
           dgt[e] = (uint32_t)(y + 0x808080) ^ 0x808080u;  // bytes: balanced digits e0, e1, e2 and the top digit
           lo4 |= ((uint32_t)(int)lf & 0xffu) << (8 * e);
@@ -618,30 +605,129 @@ __global__ __launch_bounds__(kThreads, 2) void quant_write_kernel(QuantParams p,
         ra[s][h][1][k4] = b1;
         ra[s][h][2][k4] = __builtin_amdgcn_perm(q23, q01, 0x05040100u);
         ra[s][h][3][k4] = __builtin_amdgcn_perm(q23, q01, 0x07060302u);
-        S.rlo[wave][s][h][lane][k4] = lo4;
+        store_lo(s, h, k4, lo4);
       }
     }
   }
-  // column sums over the four lane quads, then maxima over the work group
+}
+
+// The bound's terms over the whole matrix: column sums over the four lane
+// quads, then maxima over the work group into rbits[0..3] (float bits of
+// max_j sum_i |R_ij - Y_ij 2^-30|, max_j sum_i |R_ij - Y_ij 2^-30 - lo_ij
+// 2^-38|, max_j sum_i |R_ij|, max |R_ij|) and bad.  rbits and bad are LDS,
+// cleared and behind a barrier before the call.
+__device__ __forceinline__ void r_bound_reduce(RBoundPart part, int lane, uint32_t* rbits, uint32_t* bad) {
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
-    d1[s] += __shfl_xor(d1[s], 16);
-    d1[s] += __shfl_xor(d1[s], 32);
-    d2[s] += __shfl_xor(d2[s], 16);
-    d2[s] += __shfl_xor(d2[s], 32);
-    l1[s] += __shfl_xor(l1[s], 16);
-    l1[s] += __shfl_xor(l1[s], 32);
+    part.d1[s] += __shfl_xor(part.d1[s], 16);
+    part.d1[s] += __shfl_xor(part.d1[s], 32);
+    part.d2[s] += __shfl_xor(part.d2[s], 16);
+    part.d2[s] += __shfl_xor(part.d2[s], 32);
+    part.l1[s] += __shfl_xor(part.l1[s], 16);
+    part.l1[s] += __shfl_xor(part.l1[s], 32);
   }
-  __syncthreads();  // flags cleared
-  if (bad) atomicOr(&S.bad_r, 1u);
-  if (qd == 0) {
+  if (part.bad) atomicOr(bad, 1u);
+  if ((lane >> 4) == 0) {
     // non-negative floats order as their bit patterns
-    atomicMax(&S.rbits[0], __builtin_bit_cast(uint32_t, __builtin_fmaxf(d1[0], d1[1])));
-    atomicMax(&S.rbits[1], __builtin_bit_cast(uint32_t, __builtin_fmaxf(d2[0], d2[1])));
-    atomicMax(&S.rbits[2], __builtin_bit_cast(uint32_t, __builtin_fmaxf(l1[0], l1[1])));
+    atomicMax(&rbits[0], __builtin_bit_cast(uint32_t, __builtin_fmaxf(part.d1[0], part.d1[1])));
+    atomicMax(&rbits[1], __builtin_bit_cast(uint32_t, __builtin_fmaxf(part.d2[0], part.d2[1])));
+    atomicMax(&rbits[2], __builtin_bit_cast(uint32_t, __builtin_fmaxf(part.l1[0], part.l1[1])));
   }
-  atomicMax(&S.rbits[3], __builtin_bit_cast(uint32_t, rmax));
+  atomicMax(&rbits[3], __builtin_bit_cast(uint32_t, part.rmax));
+}
+
+// Prepared digits of one matrix (kRPrepBytes): ra as u32x4 [wave][s][h][b][lane],
+// then rlo as u32x4 [wave][s][h][lane], then rbits[4] and bad (5 words).
+__device__ __forceinline__ int r_prep_ra_index(int wave, int s, int h, int b, int lane) {
+  return (((wave * 2 + s) * 2 + h) * 4 + b) * 64 + lane;
+}
+__device__ __forceinline__ int r_prep_lo_index(int wave, int s, int h, int lane) {
+  return ((wave * 2 + s) * 2 + h) * 64 + lane;
+}
+
+// One work group per (KV head, K or V): the prepared digits of that matrix.
+__global__ __launch_bounds__(kThreads) void prepare_r_kernel(const float* r_k, const float* r_v, uint8_t* prep) {
+  __shared__ uint32_t rbits[4], bad;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int kv = blockIdx.x, isv = blockIdx.y;
+  const float* Rm = isv ? r_v : r_k;
+  const float* R = Rm ? Rm + (int64_t)kv * kHeadDim * kHeadDim : nullptr;
+  if (tid < 5) (tid < 4 ? rbits[tid] : bad) = 0u;
+  u32x4 ra[2][2][4], rlo[2][2];
+  RBoundPart part;
+  r_digits(R, lane, wave, ra, [&](int s, int h, int k4, uint32_t w) { rlo[s][h][k4] = w; }, part);
+  uint8_t* base = prep + (int64_t)(kv * 2 + isv) * kRPrepBytes;
+  u32x4* g_ra = (u32x4*)base;
+  u32x4* g_lo = (u32x4*)(base + kRPrepRaBytes);
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) g_ra[r_prep_ra_index(wave, s, h, b, lane)] = ra[s][h][b];
+      g_lo[r_prep_lo_index(wave, s, h, lane)] = rlo[s][h];
+    }
+  __syncthreads();  // flags cleared
+  r_bound_reduce(part, lane, rbits, &bad);
   __syncthreads();
+  // the five words, then zeros to the end of the 256-byte tail
+  if (tid < 64) ((uint32_t*)(base + kRPrepRaBytes + kRPrepLoBytes))[tid] = tid < 4 ? rbits[tid] : (tid == 4 ? bad : 0u);
+}
+
+// PREP: R's digits come prepared (p.r_prep); a separate instantiation, so the
+// one that derives them keeps its own register allocation.
+template <int MODE, int NG, int MB, bool PREP>
+__global__ __launch_bounds__(kThreads, 2) void quant_write_kernel(QuantParams p, int tiles_per_wg) {
+  extern __shared__ __align__(16) uint8_t smem_raw[];
+  Smem& S = *reinterpret_cast<Smem*>(smem_raw);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int kv = blockIdx.y;
+  const int isv = blockIdx.z;
+  const int64_t n_tiles = (p.n + kTok - 1) / kTok;
+  const int64_t tile0 = (int64_t)blockIdx.x * tiles_per_wg;
+  const int64_t tile1 = tile0 + tiles_per_wg < n_tiles ? tile0 + tiles_per_wg : n_tiles;
+  if (tile0 >= tile1) return;
+  const int count = (int)(tile1 - tile0);  // <= kMaxTilesPerWg
+  const float* Rm = isv ? p.r_v : p.r_k;  // null: V arrives rotated (R_V folded into its projection)
+  const float* R = Rm ? Rm + (int64_t)kv * kHeadDim * kHeadDim : nullptr;
+  const double tau = isv ? p.tau_v : p.tau_k;
+  const int ln = lane & 15, qd = lane >> 4;
+
+  // per-thread role in the loads: token tt, channels 8cc .. 8cc+7
+  const int tt = tid >> 4, cc = tid & 15;
+  const uint16_t* src = MODE == 0 ? (isv ? p.v_src : p.k_src) : nullptr;
+  auto fetch = [&](int64_t tile) { return fetch_tile<MODE>(p, src, kv, isv, tile, tile1, tt, cc); };
+  auto dst_of = [&](const TileIn& in) { return tile_dst(p, in); };
+  TileIn nx = fetch(tile0);
+
+  // ---- set-up: this wavefront's R digits in registers (A operands), the
+  // residual digit in LDS, the bound's terms over the matrix: prepared once
+  // per layer (oscar_layer_prepare), or computed here ----
+  u32x4 ra[2][2][4];  // [tile s][half h][digit b]
+  if constexpr (PREP) {
+    const uint8_t* base = p.r_prep + (int64_t)(kv * 2 + isv) * kRPrepBytes;
+    const u32x4* g_ra = (const u32x4*)base;
+    const u32x4* g_lo = (const u32x4*)(base + kRPrepRaBytes);
+    const uint32_t* g_c = (const uint32_t*)(base + kRPrepRaBytes + kRPrepLoBytes);
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) ra[s][h][b] = g_ra[r_prep_ra_index(wave, s, h, b, lane)];
+        S.rlo[wave][s][h][lane] = g_lo[r_prep_lo_index(wave, s, h, lane)];
+      }
+    if (tid < 5) (tid < 4 ? S.rbits[tid] : S.bad_r) = g_c[tid];
+    __syncthreads();
+  } else {
+    if (tid < 5) (tid < 4 ? S.rbits[tid] : S.bad_r) = 0u;
+    RBoundPart part;
+    r_digits(R, lane, wave, ra, [&](int s, int h, int k4, uint32_t w) { S.rlo[wave][s][h][lane][k4] = w; }, part);
+    __syncthreads();  // flags cleared
+    r_bound_reduce(part, lane, S.rbits, &S.bad_r);
+    __syncthreads();
+  }
   const bool bad_r = S.bad_r != 0u;
   // per-token bound = 2^E (ka + n_rounded kbr + sum |D0| kOmit), with
   // |X - 2^24 D3| <= 128 (1 + 256 + 65536) = 8421504, and 2^-44 >= 2^-45 +
@@ -938,7 +1024,7 @@ hipError_t launch_qw_t(const QuantParams& p, hipStream_t stream) {
   const int tpw = tiles_per_wg(p);
   const dim3 grid((unsigned)((n_tiles + tpw - 1) / tpw), (unsigned)p.n_kv, 2);
   const size_t lds = sizeof(Smem);
-  auto kern = quant_write_kernel<MODE, NG, MB>;
+  auto kern = p.r_prep ? quant_write_kernel<MODE, NG, MB, true> : quant_write_kernel<MODE, NG, MB, false>;
   hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, stream, p, tpw);
   return hipGetLastError();
 }
@@ -952,6 +1038,11 @@ hipError_t launch_qw(const QuantParams& p, hipStream_t stream) {
 }
 
 }  // namespace
+
+hipError_t launch_prepare_r(const float* r_k, const float* r_v, int n_kv, uint8_t* prep, hipStream_t stream) {
+  hipLaunchKernelGGL(prepare_r_kernel, dim3((unsigned)n_kv, 2), dim3(kThreads), 0, stream, r_k, r_v, prep);
+  return hipGetLastError();
+}
 
 hipError_t launch_quant_write(const QuantParams& p, int mode, hipStream_t stream) {
   if (p.n == 0) return hipSuccess;

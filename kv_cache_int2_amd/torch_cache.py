@@ -21,9 +21,11 @@ class DeviceCache:
     """One layer's paged cache on the GPU plus its host pool bookkeeping."""
 
     def __init__(self, shape: K.Shape, r_k: np.ndarray, r_v: np.ndarray, tau_k, tau_v, n_int2_pages: int,
-                 n_bf16_pages: int, fill: int = 0):
+                 n_bf16_pages: int, fill: int = 0, prepare: bool = True):
         """fill: the byte every page starts with (0xFF makes each unwritten
-        bf16 value and fp16 or FP8 scale/zero a NaN)."""
+        bf16 value and fp16 or FP8 scale/zero a NaN).  prepare: R's digits
+        prepared once for the write calls (oscar_layer_prepare), else derived
+        in every write work group."""
         self.shape = shape
         self.pool = K.Pool(shape, n_int2_pages, n_bf16_pages)
         ib = K.oscar_int2_block_bytes(shape)
@@ -37,6 +39,11 @@ class DeviceCache:
         # r_v None: V arrives rotated (R_V folded into the model's projections)
         self.r_v = None if r_v is None else torch.from_numpy(np.ascontiguousarray(r_v, dtype=np.float32)).cuda()
         self.layer = K.make_layer(self.r_k, self.r_v, tau_k, tau_v)
+        self.r_prep = None
+        if prepare:
+            self.r_prep = torch.empty(K.oscar_layer_prep_bytes(shape), dtype=torch.uint8, device="cuda")
+            K.oscar_layer_prepare(shape, self.layer, self.r_prep)
+            self.layer = K.make_layer(self.r_k, self.r_v, tau_k, tau_v, self.r_prep)
         self.int2_block = ib
         self.bf16_block = bb
 

@@ -745,7 +745,8 @@ def _check_written_rows(dc, sh, kb, vb, r_k, r_v, tau_k, tau_v, group, scale_bit
 
 
 @pytest.mark.parametrize("scale_bits", [16, 8])
-def test_quant_write_certification_edges(scale_bits):
+@pytest.mark.parametrize("prepare", [True, False], ids=["prepared-digits", "derived-digits"])
+def test_quant_write_certification_edges(scale_bits, prepare):
     """The write kernel's certified decisions at their edges, with identity
     rotations (R_K = I, R_V folded) so that the rotated values are the bf16
     inputs themselves: codes whose t is exactly a half-integer (the exact path
@@ -776,9 +777,40 @@ def test_quant_write_certification_edges(scale_bits):
     eye = np.eye(128, dtype=np.float32)[None]
     for label, r_k, tau in (("identity", eye, 4.0), ("R outside [-1.5, 1.5]", 2.0 * eye, 8.0)):
         _flush(f"case certification edges: {label}, scale_bits {scale_bits}")
-        dc = DeviceCache(sh, r_k, None, tau, tau, (n + 15) // 16, 1)
+        dc = DeviceCache(sh, r_k, None, tau, tau, (n + 15) // 16, 1, prepare=prepare)
         K.oscar_quant_write(sh, dc.layer, dc.cache, to_dev_bits(kb), to_dev_bits(vb),
                             to_dev_i32(np.arange(n, dtype=np.int32)))
         torch.cuda.synchronize()
         _check_written_rows(dc, sh, kb, vb, r_k.astype(np.float64), eye.astype(np.float64), tau, tau, 32,
                             scale_bits, label)
+
+
+@pytest.mark.parametrize("group,scale_bits", [(32, 16), (64, 8)])
+def test_prepared_digits_match_derived(group, scale_bits):
+    """R's digits prepared once per layer (oscar_layer_prepare) against the
+    ones every write work group derives: identical INT2 bytes for the same
+    writes (a 16384-token chunk and a 4096-token one, x40 outliers, the
+    calibrated rotations, and R_V folded), and the prepared buffer itself
+    identical across two preparations."""
+    from kv_cache_int2_amd.torch_cache import to_dev_bits, to_dev_i32
+    w = synth.Workload("prep", 90 + group, 96, 8, 128, 1, 0, group=group, sink=4, recent=128,
+                       outlier_scale=(40.0, 40.0), calib_tokens=1024)
+    cal = _calibrate(w)
+    sh = K.make_shape(n_q_heads=96, n_kv_heads=8, group=group, sink=4, recent=128, scale_bits=scale_bits)
+    n = 16384 + 4096
+    kb, vb = synth.kv_request_bf16(w, 3, 0, n)
+    for r_v in (cal.r_v, None):
+        label = "R_V folded" if r_v is None else "calibrated"
+        _flush(f"case prepared digits G={group} scale_bits={scale_bits} {label}")
+        caches = [DeviceCache(sh, cal.r_k, r_v, cal.tau_k, cal.tau_v, n // 16 + 1, 1, prepare=pr)
+                  for pr in (True, False)]
+        again = torch.empty_like(caches[0].r_prep)
+        K.oscar_layer_prepare(sh, caches[0].layer, again)
+        for dc in caches:
+            for a, b in ((0, 16384), (16384, n)):   # a 16384-token call and a 4096-token one
+                K.oscar_quant_write(sh, dc.layer, dc.cache, to_dev_bits(kb[a:b]), to_dev_bits(vb[a:b]),
+                                    to_dev_i32(np.arange(a, b, dtype=np.int32)))
+        torch.cuda.synchronize()
+        assert torch.equal(caches[0].r_prep, again), label
+        assert torch.equal(caches[0].int2, caches[1].int2), label
+

@@ -109,6 +109,18 @@ def test_launch_argument_errors_before_any_gpu_call(lib):
         assert lib.oscar_quant_write(C.byref(sh), C.byref(good_layer), C.byref(ok_cache), kp, vp, 0x10, 1,
                                      None) == K.OSCAR_EINVAL
         assert b"16-byte" in lib.oscar_last_error()
+    # R's prepared digits: n_kv x 2 matrices of 82176 bytes; the buffer must be
+    # given, 256-byte aligned and large enough, and a layer's r_prep aligned
+    assert K.oscar_layer_prep_bytes(sh) == sh.n_kv_heads * 2 * 82176
+    assert K.oscar_layer_prep_bytes(K.make_shape(n_kv_heads=8, n_q_heads=32)) == 16 * 82176
+    need = K.oscar_layer_prep_bytes(sh)
+    for prep, nbytes in ((None, need), (0x1010, need), (0x1000, need - 1)):
+        assert lib.oscar_layer_prepare(C.byref(sh), C.byref(good_layer), prep, nbytes, None) == K.OSCAR_EINVAL
+    assert lib.oscar_layer_prepare(C.byref(sh), C.byref(no_rk), 0x1000, need, None) == K.OSCAR_EINVAL
+    odd_prep = K.Layer(0x1000, 0x2000, 1.0, 1.0, 0x3010)
+    assert lib.oscar_quant_write(C.byref(sh), C.byref(odd_prep), C.byref(ok_cache), 0x10, 0x10, 0x10, 1,
+                                 None) == K.OSCAR_EINVAL
+    assert b"prepared" in lib.oscar_last_error()
     # the host-table step carries its tables in the launch arguments: at most 64
     # requests, and its host arrays are required
     slots = np.full((4, 65), -1, np.int32)
