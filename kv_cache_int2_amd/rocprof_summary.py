@@ -1,10 +1,11 @@
 """Summaries of rocprofv3 result databases (SQLite) for the OSCAR kernels.
 
-    python -m kv_cache_int2_amd.rocprof_summary trace DB --command CMD [--tail NAME:N]
+    python -m kv_cache_int2_amd.rocprof_summary trace DB --command CMD [--tail NAME:N[:M]]
         per-kernel dispatch statistics (count, average / min / max duration),
         as a short markdown table; --tail adds the same statistics over the
         last N dispatches of the kernel whose name contains NAME (the timed
-        steps of a run, without its warm-up).
+        steps of a run, without its warm-up), after leaving out its last M
+        (dispatches that follow the timed steps).
 
     python -m kv_cache_int2_amd.rocprof_summary sq DB --kernel NAME [--kernel NAME ...]
         [--tail N] [--skip-last M]  MFMA utilisation and VALU busy per kernel from one
@@ -99,10 +100,10 @@ def cmd_sq(a):
     print("\n".join(out))
 
 
-def tail_stats(db: str, kernel: str, n: int):
+def tail_stats(db: str, kernel: str, n: int, skip_last: int = 0):
     con = sqlite3.connect(db)
-    d = [r[0] for r in con.execute("select duration from kernels where name like ? order by start desc limit ?",
-                                   (f"%{kernel}%", n)).fetchall()]
+    d = [r[0] for r in con.execute("select duration from kernels where name like ? order by start desc "
+                                   "limit ? offset ?", (f"%{kernel}%", n, skip_last)).fetchall()]
     if not d:
         sys.exit(f"no dispatches of {kernel} in {db}")
     return dict(calls=len(d), avg_us=sum(d) / len(d) / 1e3, min_us=min(d) / 1e3, max_us=max(d) / 1e3,
@@ -117,9 +118,12 @@ def cmd_trace(a):
         out.append(f"| {r['name']} | {r['calls']} | {r['avg_us']:.2f} | {r['min_us']:.2f} | {r['max_us']:.2f} "
                    f"| {r['total_ms']:.3f} |")
     for spec in a.tail or []:
-        name, n = spec.rsplit(":", 1)
-        r = tail_stats(a.db, name, int(n))
-        out += ["", f"Last {r['calls']} dispatches of {name}:", "",
+        parts = spec.split(":")
+        name, n = parts[0], int(parts[1])
+        skip = int(parts[2]) if len(parts) > 2 else 0
+        r = tail_stats(a.db, name, n, skip)
+        before = f" before its last {skip}" if skip else ""
+        out += ["", f"Last {r['calls']} dispatches of {name}{before}:", "",
                 "| kernel | calls | avg us | min us | max us | total ms |", "|---|---:|---:|---:|---:|---:|",
                 f"| {name} (last {r['calls']}) | {r['calls']} | {r['avg_us']:.2f} | {r['min_us']:.2f} "
                 f"| {r['max_us']:.2f} | {r['total_ms']:.3f} |"]
@@ -160,7 +164,8 @@ def main(argv=None):
     t.add_argument("db")
     t.add_argument("--command", required=True)
     t.add_argument("--title", default="")
-    t.add_argument("--tail", action="append", help="NAME:N, statistics of the last N dispatches")
+    t.add_argument("--tail", action="append", help="NAME:N[:M], statistics of the last N dispatches "
+                   "after leaving out the last M")
     t.add_argument("--notes", help="text file appended to the summary")
     p = sub.add_parser("pmc")
     for k in ("fetch", "write", "kernel", "copy", "workload", "source", "command"):
